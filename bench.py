@@ -1,0 +1,211 @@
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+the BlockMask build (classify, compact, schedule) followed by the forward.
+Inputs are generated once and stay resident in HBM. Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+FLOP accounting: 4 * D flops per allowed (q, kv) pair and (b, h) (2D for
+q.k, 2D for p.v); softmax and score_mod arithmetic are not counted. The
+allowed-pair count comes from the mask's per-row intervals (closed form).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+import workloads as W
+
+BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+F32_PEAK_TFLOPS = 157.3     # MI355X fp32 (vector / matrix)
+HBM_PEAK_GBS = 8000.0
+
+
+def allowed_pairs_per_head(w: W.Workload, doc_lengths=None) -> int:
+    """Allowed (q, kv) pairs of one (b, h), from the per-row allowed intervals."""
+    q = np.arange(w.Q_LEN, dtype=np.int64)
+    kv_max = w.KV_LEN - 1
+    if w.mask == "noop":
+        return w.Q_LEN * w.KV_LEN
+    if w.mask == "causal":
+        return int(np.clip(np.minimum(q, kv_max) + 1, 0, None).sum())
+    if w.mask == "sliding_sink":
+        hi = np.minimum(q, kv_max)
+        lo1 = np.maximum(0, q - w.window + 1)
+        n1 = np.clip(hi - lo1 + 1, 0, None)
+        hi2 = np.minimum(np.minimum(w.sinks - 1, q), kv_max)
+        n2 = np.clip(hi2 + 1, 0, None)
+        ov = np.clip(np.minimum(hi, hi2) - lo1 + 1, 0, None)
+        return int((n1 + n2 - ov).sum())
+    if w.mask == "document_causal":
+        lens = np.asarray(doc_lengths, dtype=np.int64)
+        return int((lens * (lens + 1) // 2).sum())
+    raise ValueError(w.mask)
+
+
+def algorithmic_bytes(w: W.Workload, nqb: int, nkb: int) -> int:
+    """Bytes a forward must move at least once: q, k, v, out, lse and the
+    BlockMask it reads."""
+    es = 4 if w.dtype == "f32" else 2
+    q = w.B * w.Hq * w.Q_LEN * w.D * es
+    kv = 2 * w.B * w.Hkv * w.KV_LEN * w.D * es
+    out = q
+    lse = w.B * w.Hq * w.Q_LEN * 4
+    bm = 4 * (2 * nqb + 2 * nqb * nkb + nqb)
+    return q + kv + out + lse + bm
+
+
+def cpu_baseline(w: W.Workload, inp: W.Inputs, budget_s: float = 20.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same
+    workload: whole (b, h) heads, as many as fit the time budget."""
+    import oracle  # noqa: E402  (CPU-baseline leg only)
+    cores = len(os.sched_getaffinity(0))
+    mask, score = oracle.for_workload(w, inp)
+    pairs = allowed_pairs_per_head(w, inp.doc_lengths)
+    done, t0 = 0, time.perf_counter()
+    heads = []
+    for b in range(w.B):
+        for h in range(w.Hq):
+            oracle.attention(inp.q, inp.k, inp.v, mask, score, w.scale, batches=[b], heads=[h])
+            done += 1
+            heads.append((b, h))
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * pairs * done
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hq} (b, h) heads, all {w.Q_LEN} query rows each, "
+                      f"fp64 NumPy, {dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=W.DENSE_CAUSAL_GQA.name, choices=sorted(W.BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the forward shards by "
+              "(batch, KV head) with no exchange, so no multi-GPU figure is measured here.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import block_sparse_masked_amd as fa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    fa.load_library()
+    w = W.BY_NAME[args.workload]
+    inp = W.generate(w)
+    dev = torch.device("cuda:0")
+    tdtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(inp.q).to(tdtype).to(dev)
+    k = torch.from_numpy(inp.k).to(tdtype).to(dev)
+    v = torch.from_numpy(inp.v).to(tdtype).to(dev)
+    doc = torch.from_numpy(inp.doc_ids).to(dev) if inp.doc_ids is not None else None
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        bm = fa.create_block_mask(w.mask, 1, 1, w.Q_LEN, w.KV_LEN, 128, window=w.window,
+                                  num_sinks=w.sinks, doc_ids=doc, device=dev, stream=stream)
+        fa.flex_attention(q, k, v, bm, score=w.score, softcap=w.softcap, scale=w.scale,
+                          out=out, lse=lse, stream=stream)
+        return bm
+
+    for _ in range(args.warmup):
+        bm = step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps; events around the build and the forward of each
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        bm = fa.create_block_mask(w.mask, 1, 1, w.Q_LEN, w.KV_LEN, 128, window=w.window,
+                                  num_sinks=w.sinks, doc_ids=doc, device=dev, stream=stream)
+        ev[i][1].record(stream)
+        fa.flex_attention(q, k, v, bm, score=w.score, softcap=w.softcap, scale=w.scale,
+                          out=out, lse=lse, stream=stream)
+        ev[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    build_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    fwd_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
+
+    pairs = allowed_pairs_per_head(w, inp.doc_lengths)
+    eff_flops = 4.0 * w.D * pairs * w.B * w.Hq
+    dense_flops = 4.0 * w.D * w.Q_LEN * w.KV_LEN * w.B * w.Hq
+    nonempty = int(bm.kv_num_blocks.sum().item() + bm.full_kv_num_blocks.sum().item())
+    visited_flops = 4.0 * w.D * 128 * 128 * nonempty * w.B * w.Hq
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
+    fwd_avg = float(np.mean(fwd_ms))
+    value = eff_flops / (ms_step * 1e-3) / 1e12
+    fwd_tflops = eff_flops / (fwd_avg * 1e-3) / 1e12
+    nqb, nkb = bm.num_q_blocks, bm.num_kv_blocks
+
+    rec = {
+        "metric": "effective TFLOP/s (unmasked FLOPs) flex-attn fwd bf16; % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Q_LEN": w.Q_LEN,
+                   "KV_LEN": w.KV_LEN, "D": w.D, "mask": w.mask, "score": w.score,
+                   "seed": w.seed, "block": 128, "parallelism": "single-gpu"},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "fwd_ms_avg": round(fwd_avg, 4),
+        "fwd_ms_min": round(float(np.min(fwd_ms)), 4),
+        "build_ms_avg": round(float(np.mean(build_ms)), 4),
+        "fwd_effective_tflops": round(fwd_tflops, 2),
+        "dense_equivalent_tflops": round(dense_flops / (fwd_avg * 1e-3) / 1e12, 2),
+        "visited_tile_tflops": round(visited_flops / (fwd_avg * 1e-3) / 1e12, 2),
+        "unmasked_fraction": round(pairs / (w.Q_LEN * w.KV_LEN), 4),
+        "tile_sparsity_pct": round(100.0 * (1 - nonempty / (nqb * nkb)), 2),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
+            "achieved": round(fwd_tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tflops / peak, 4),
+            "traffic": None,
+            "algorithmic_bytes": algorithmic_bytes(w, nqb, nkb),
+        },
+    }
+    if inp.doc_lengths is not None:
+        rec["config"]["doc_lengths"] = [int(x) for x in inp.doc_lengths]
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,257 @@
+"""MI355X (gfx950) FlexAttention-style block-sparse attention forward.
+
+A thin ctypes binding over ``libflexattn.so`` (C ABI in ``include/flexattn.h``).
+Python only marshals arguments: every step of the BlockMask build and the
+forward runs in the library's HIP kernels. PyTorch provides device memory and
+the current stream. There is no CPU fallback: without the built library on a
+GPU machine, every call raises.
+
+    bm = create_block_mask("causal", B=1, H=1, Q_LEN=4096, KV_LEN=4096)
+    out, lse = flex_attention(q, k, v, bm, score="softcap_alibi", softcap=50.0)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "BlockMask", "FlexAttnError", "MASK_KINDS", "SCORE_KINDS", "create_block_mask",
+    "flex_attention", "library_path", "load_library", "block_mask_sizes", "version",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libflexattn.so")
+
+MASK_KINDS = {"noop": 0, "causal": 1, "sliding_sink": 2, "document_causal": 3}
+SCORE_KINDS = {"none": 0, "alibi": 1, "softcap": 2, "softcap_alibi": 3}
+_F32, _BF16 = 0, 1
+_OK, _INVALID, _UNSUPPORTED, _HIP = 0, 1, 2, 3
+
+
+class FlexAttnError(RuntimeError):
+    """A launch or runtime failure reported by the library."""
+
+
+class _MaskParams(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("num_sinks", ctypes.c_int32),
+                ("doc_ids", ctypes.c_void_p), ("doc_batch", ctypes.c_int32),
+                ("doc_len", ctypes.c_int32)]
+
+
+class _ScoreParams(ctypes.Structure):
+    _fields_ = [("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p)]
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int),
+                ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("stride", ctypes.c_int64 * 4)]
+
+
+class _BlockMask(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Q_LEN", ctypes.c_int32),
+                ("KV_LEN", ctypes.c_int32), ("BLOCK_SIZE", ctypes.c_int32),
+                ("num_q_blocks", ctypes.c_int32), ("num_kv_blocks", ctypes.c_int32),
+                ("kv_num_blocks", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p),
+                ("full_kv_num_blocks", ctypes.c_void_p), ("full_kv_indices", ctypes.c_void_p),
+                ("schedule", ctypes.c_void_p), ("mask_kind", ctypes.c_int),
+                ("mask_params", _MaskParams)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load ``libflexattn.so`` (built in-tree by ``block_sparse_masked_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m block_sparse_masked_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.flexattn_last_error.restype = ctypes.c_char_p
+    lib.flexattn_version.restype = ctypes.c_char_p
+    lib.flexattn_block_mask_sizes.restype = ctypes.c_int
+    lib.flexattn_block_mask_sizes.argtypes = [ctypes.c_int32] * 5 + [
+        ctypes.POINTER(ctypes.c_size_t)] * 3
+    lib.flexattn_create_block_mask.restype = ctypes.c_int
+    lib.flexattn_create_block_mask.argtypes = [
+        ctypes.c_int, ctypes.POINTER(_MaskParams), ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_BlockMask),
+        ctypes.c_void_p]
+    lib.flexattn_fwd.restype = ctypes.c_int
+    lib.flexattn_fwd.argtypes = [
+        ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+        ctypes.POINTER(_BlockMask), ctypes.c_int, ctypes.POINTER(_ScoreParams), ctypes.c_float,
+        ctypes.POINTER(_Tensor), ctypes.c_void_p, ctypes.c_void_p]
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load_library().flexattn_version().decode()
+
+
+def _check(status: int, what: str):
+    if status == _OK:
+        return
+    msg = load_library().flexattn_last_error().decode() or what
+    if status == _INVALID:
+        raise ValueError(msg)
+    if status == _UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise FlexAttnError(msg)
+
+
+def _stream_handle(device: torch.device, stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def block_mask_sizes(B: int, H: int, Q_LEN: int, KV_LEN: int, block: int = 128):
+    """(num_elems, idx_elems, sched_elems) of the BlockMask buffers."""
+    lib = load_library()
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.flexattn_block_mask_sizes(B, H, Q_LEN, KV_LEN, block, ctypes.byref(a),
+                                         ctypes.byref(b), ctypes.byref(c)),
+           "flexattn_block_mask_sizes")
+    return a.value, b.value, c.value
+
+
+@dataclass
+class BlockMask:
+    """Device BlockMask tensors plus the C struct that points at them."""
+
+    kind: str
+    B: int
+    H: int
+    Q_LEN: int
+    KV_LEN: int
+    BLOCK_SIZE: int
+    kv_num_blocks: torch.Tensor       # int32 [B, H, NQB]
+    kv_indices: torch.Tensor          # int32 [B, H, NQB, NKB]
+    full_kv_num_blocks: torch.Tensor  # int32 [B, H, NQB]
+    full_kv_indices: torch.Tensor     # int32 [B, H, NQB, NKB]
+    schedule: torch.Tensor            # int32 [B*H*NQB]
+    doc_ids: Optional[torch.Tensor]
+    _c: _BlockMask
+
+    @property
+    def num_q_blocks(self) -> int:
+        return self.kv_num_blocks.shape[-1]
+
+    @property
+    def num_kv_blocks(self) -> int:
+        return self.kv_indices.shape[-1]
+
+    def numel(self) -> int:
+        """Dense element count of the mask (sparsity ignored)."""
+        return self.B * self.H * self.Q_LEN * self.KV_LEN
+
+    def sparsity(self) -> float:
+        """Percentage of tiles that are not computed (reads the counts back)."""
+        nonempty = int(self.kv_num_blocks.sum().item()) + int(self.full_kv_num_blocks.sum().item())
+        total = self.B * self.H * self.num_q_blocks * self.num_kv_blocks
+        return 100.0 * (1.0 - nonempty / total)
+
+
+def create_block_mask(kind: str, B: int, H: int, Q_LEN: int, KV_LEN: int, block: int = 128,
+                      window: int = 0, num_sinks: int = 0,
+                      doc_ids: Optional[torch.Tensor] = None,
+                      device="cuda", stream=None) -> BlockMask:
+    """Build the BlockMask of a mask kind on the GPU (the library's builder
+    kernels). B and H may be 1 to broadcast over batch / query heads."""
+    lib = load_library()
+    if kind not in MASK_KINDS:
+        raise NotImplementedError(f"mask kind {kind!r} is not one of {sorted(MASK_KINDS)}")
+    device = torch.device(device)
+    n_num, n_idx, n_sched = block_mask_sizes(B, H, Q_LEN, KV_LEN, block)
+    nqb = -(-Q_LEN // block)
+    nkb = -(-KV_LEN // block)
+    kv_num = torch.empty((B, H, nqb), dtype=torch.int32, device=device)
+    kv_idx = torch.empty((B, H, nqb, nkb), dtype=torch.int32, device=device)
+    full_num = torch.empty((B, H, nqb), dtype=torch.int32, device=device)
+    full_idx = torch.empty((B, H, nqb, nkb), dtype=torch.int32, device=device)
+    sched = torch.empty((n_sched,), dtype=torch.int32, device=device)
+    assert kv_num.numel() == n_num and kv_idx.numel() == n_idx
+    mp = _MaskParams(window, num_sinks, None, 0, 0)
+    if kind == "document_causal":
+        if doc_ids is None:
+            raise ValueError("document_causal needs doc_ids")
+        doc_ids = doc_ids.to(device=device, dtype=torch.int32)
+        if doc_ids.dim() == 1:
+            doc_ids = doc_ids.unsqueeze(0)
+        doc_ids = doc_ids.contiguous()
+        mp.doc_ids = doc_ids.data_ptr()
+        mp.doc_batch = doc_ids.shape[0]
+        mp.doc_len = doc_ids.shape[1]
+    c = _BlockMask()
+    c.kv_num_blocks = kv_num.data_ptr()
+    c.kv_indices = kv_idx.data_ptr()
+    c.full_kv_num_blocks = full_num.data_ptr()
+    c.full_kv_indices = full_idx.data_ptr()
+    c.schedule = sched.data_ptr()
+    st = lib.flexattn_create_block_mask(MASK_KINDS[kind], ctypes.byref(mp), B, H, Q_LEN, KV_LEN,
+                                        block, ctypes.byref(c), _stream_handle(device, stream))
+    _check(st, "flexattn_create_block_mask")
+    return BlockMask(kind, B, H, Q_LEN, KV_LEN, block, kv_num, kv_idx, full_num, full_idx, sched,
+                     doc_ids, c)
+
+
+def _tensor(t: torch.Tensor, name: str) -> _Tensor:
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, H, L, D]")
+    if t.dtype == torch.float32:
+        dt = _F32
+    elif t.dtype == torch.bfloat16:
+        dt = _BF16
+    else:
+        raise NotImplementedError(f"{name} dtype {t.dtype} is not float32 or bfloat16")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    st = (ctypes.c_int64 * 4)(*t.stride())
+    return _Tensor(t.data_ptr(), dt, *t.shape, st)
+
+
+def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask,
+                   score: str = "none", softcap: float = 0.0,
+                   alibi_slopes: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   stream=None):
+    """Block-sparse attention forward. q [B,Hq,M,D]; k, v [B,Hkv,N,D].
+
+    Returns (out [B,Hq,M,D] in q's dtype, lse [B,Hq,M] float32)."""
+    lib = load_library()
+    if score not in SCORE_KINDS:
+        raise NotImplementedError(f"score kind {score!r} is not one of {sorted(SCORE_KINDS)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, Hq, M]")
+    sp = _ScoreParams(float(softcap), None)
+    if alibi_slopes is not None:
+        alibi_slopes = alibi_slopes.to(device=q.device, dtype=torch.float32).contiguous()
+        sp.alibi_slopes = alibi_slopes.data_ptr()
+    tq, tk, tv, to = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v"), _tensor(out, "out")
+    st = lib.flexattn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
+                          ctypes.byref(block_mask._c), SCORE_KINDS[score], ctypes.byref(sp),
+                          float(scale), ctypes.byref(to), ctypes.c_void_p(lse.data_ptr()),
+                          _stream_handle(q.device, stream))
+    _check(st, "flexattn_fwd")
+    return out, lse

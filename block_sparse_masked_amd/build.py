@@ -1,0 +1,84 @@
+"""Build the gfx950 shared library ``libflexattn.so`` in-tree with hipcc.
+
+Usage: ``python -m block_sparse_masked_amd.build [--jobs N] [--debug]``.
+Every HIP source is compiled for gfx950 only, with packed-FP32 instruction
+selection disabled (plain fp32 VALU code only).
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libflexattn.so")
+
+SOURCES = ["api.cpp", "block_mask.hip", "fwd_bf16.hip", "fwd_f32.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libflexattn.so)")
+
+
+def common_flags(debug: bool):
+    flags = ["-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", CSRC, "-I", INCLUDE,
+             "-Wall", "-Wno-unused-function",
+             # plain fp32 VALU code: no packed-fp32 instruction selection
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    flags += ["-O1", "-g"] if debug else ["-O3"]
+    return flags
+
+
+def compile_one(src: str, debug: bool, extra) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") or src.endswith(".cpp") else []
+    cmd = [hipcc()] + common_flags(debug) + list(extra) + lang + ["-c", os.path.join(CSRC, src),
+                                                                   "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
+                    if "packed-fp32-ops" not in line)
+    if res.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{out}")
+    if out.strip():
+        sys.stderr.write(out + "\n")
+    return obj
+
+
+def build(jobs: int = 4, debug: bool = False, extra=()) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(lambda s: compile_one(s, debug, extra), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--jobs", type=int, default=4)
+    ap.add_argument("--debug", action="store_true")
+    ap.add_argument("--save-temps", action="store_true",
+                    help="keep the gfx950 assembly of our own kernels under _build/")
+    args = ap.parse_args(argv)
+    extra = []
+    if args.save_temps:
+        extra = ["-save-temps=obj"]
+    print(build(args.jobs, args.debug, extra))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,302 @@
+// C ABI of the block-sparse attention library: host-side argument checks,
+// then dispatch to the gfx950 kernels on the caller's stream. Every check
+// runs before any HIP call, so invalid calls return without touching the
+// device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/flexattn.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+flexattn_status fail(flexattn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+flexattn_status ok() {
+  g_last_error.clear();
+  return FLEXATTN_OK;
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validate mask kind + params; fill the kernel-side view.
+flexattn_status check_mask(flexattn_mask_kind kind, const flexattn_mask_params* p, int B_build,
+                           int Q_LEN, int KV_LEN, fa::MaskParams* out, int* doc_len,
+                           const char* who) {
+  out->window = 0;
+  out->sinks = 0;
+  out->doc = nullptr;
+  out->doc_bstride = 0;
+  *doc_len = 0;
+  if ((int)kind < FLEXATTN_MASK_NOOP || (int)kind > FLEXATTN_MASK_DOCUMENT_CAUSAL)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: mask_kind %d is not one of the supported kinds", who,
+                (int)kind);
+  if (kind == FLEXATTN_MASK_SLIDING_SINK) {
+    if (!p) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: SLIDING_SINK needs params", who);
+    if (p->window < 1)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: SLIDING_SINK window must be >= 1 (got %d)", who,
+                  p->window);
+    if (p->num_sinks < 0)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: SLIDING_SINK num_sinks must be >= 0 (got %d)",
+                  who, p->num_sinks);
+    out->window = p->window;
+    out->sinks = p->num_sinks;
+  }
+  if (kind == FLEXATTN_MASK_DOCUMENT_CAUSAL) {
+    if (!p) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: DOCUMENT_CAUSAL needs params", who);
+    if (!p->doc_ids) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: doc_ids is NULL", who);
+    const int need = Q_LEN > KV_LEN ? Q_LEN : KV_LEN;
+    if (p->doc_len < need)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: doc_len %d < max(Q_LEN, KV_LEN) = %d", who,
+                  p->doc_len, need);
+    if (p->doc_batch != 1 && p->doc_batch != B_build)
+      return fail(FLEXATTN_ERR_INVALID_ARG,
+                  "%s: doc_batch must be 1 or the batch size %d (got %d)", who, B_build,
+                  p->doc_batch);
+    out->doc = p->doc_ids;
+    out->doc_bstride = p->doc_batch > 1 ? (long long)p->doc_len : 0;
+    *doc_len = p->doc_len;
+  }
+  return FLEXATTN_OK;
+}
+
+flexattn_status check_tensor(const flexattn_tensor* t, const char* name) {
+  if (!t) return fail(FLEXATTN_ERR_INVALID_ARG, "flexattn_fwd: %s is NULL", name);
+  if (!t->data) return fail(FLEXATTN_ERR_INVALID_ARG, "flexattn_fwd: %s->data is NULL", name);
+  if (t->dtype != FLEXATTN_F32 && t->dtype != FLEXATTN_BF16)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "flexattn_fwd: %s dtype %d is not F32 or BF16", name,
+                (int)t->dtype);
+  if (t->B < 1 || t->H < 1 || t->L < 1 || t->D < 1)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "flexattn_fwd: %s has a non-positive extent", name);
+  if (t->stride[3] != 1)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "flexattn_fwd: %s rows must be contiguous (stride[3]=1)",
+                name);
+  const int es = t->dtype == FLEXATTN_F32 ? 4 : 2;
+  if (!aligned16(t->data))
+    return fail(FLEXATTN_ERR_INVALID_ARG, "flexattn_fwd: %s->data is not 16-byte aligned", name);
+  for (int i = 0; i < 3; ++i) {
+    if (t->stride[i] < 0 || (t->stride[i] * es) % 16 != 0)
+      return fail(FLEXATTN_ERR_INVALID_ARG,
+                  "flexattn_fwd: %s stride[%d]=%lld is negative or not a multiple of 16 bytes",
+                  name, i, (long long)t->stride[i]);
+  }
+  return FLEXATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flexattn_last_error(void) { return g_last_error.c_str(); }
+
+const char* flexattn_version(void) { return "flexattn-gfx950 0.1.0"; }
+
+flexattn_status flexattn_block_mask_sizes(int32_t B, int32_t H, int32_t Q_LEN, int32_t KV_LEN,
+                                          int32_t block, size_t* num_elems, size_t* idx_elems,
+                                          size_t* sched_elems) {
+  if (!num_elems || !idx_elems || !sched_elems)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "flexattn_block_mask_sizes: NULL output pointer");
+  if (B < 1 || H < 1 || Q_LEN < 1 || KV_LEN < 1)
+    return fail(FLEXATTN_ERR_INVALID_ARG,
+                "flexattn_block_mask_sizes: B, H, Q_LEN, KV_LEN must be >= 1 (got %d %d %d %d)", B,
+                H, Q_LEN, KV_LEN);
+  if (block != fa::kBlock)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "flexattn_block_mask_sizes: block must be 128 (got %d)",
+                block);
+  const size_t rows = (size_t)B * H * ceil_div(Q_LEN, block);
+  *num_elems = rows;
+  *idx_elems = rows * (size_t)ceil_div(KV_LEN, block);
+  *sched_elems = rows;
+  return ok();
+}
+
+flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
+                                           const flexattn_mask_params* params, int32_t B,
+                                           int32_t H, int32_t Q_LEN, int32_t KV_LEN,
+                                           int32_t block, flexattn_block_mask* bm, void* stream) {
+  static const char* who = "flexattn_create_block_mask";
+  if (!bm) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: bm is NULL", who);
+  if (B < 1 || H < 1 || Q_LEN < 1 || KV_LEN < 1)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: B, H, Q_LEN, KV_LEN must be >= 1 (got %d %d %d %d)",
+                who, B, H, Q_LEN, KV_LEN);
+  if (block != fa::kBlock)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: block must be 128 (got %d)", who, block);
+  const int nkb = ceil_div(KV_LEN, block);
+  if (nkb > fa::max_build_kv_blocks())
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: KV_LEN %d exceeds the builder limit of %d tiles",
+                who, KV_LEN, fa::max_build_kv_blocks());
+  if ((long long)B * H * ceil_div(Q_LEN, block) > 0x7fffffffLL / (nkb > 0 ? nkb : 1))
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: index tensor too large", who);
+  if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices ||
+      !bm->schedule)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: a BlockMask buffer pointer is NULL", who);
+  fa::MaskParams mp;
+  int doc_len = 0;
+  flexattn_status st = check_mask(kind, params, B, Q_LEN, KV_LEN, &mp, &doc_len, who);
+  if (st != FLEXATTN_OK) return st;
+
+  bm->B = B;
+  bm->H = H;
+  bm->Q_LEN = Q_LEN;
+  bm->KV_LEN = KV_LEN;
+  bm->BLOCK_SIZE = block;
+  bm->num_q_blocks = ceil_div(Q_LEN, block);
+  bm->num_kv_blocks = nkb;
+  bm->mask_kind = kind;
+  if (params) {
+    bm->mask_params = *params;
+  } else {
+    bm->mask_params = flexattn_mask_params{0, 0, nullptr, 0, 0};
+  }
+
+  fa::BuildLaunch L;
+  L.kind = (int)kind;
+  L.mp = mp;
+  L.doc_len = doc_len;
+  L.Bm = B;
+  L.Hm = H;
+  L.Q_LEN = Q_LEN;
+  L.KV_LEN = KV_LEN;
+  L.NQB = bm->num_q_blocks;
+  L.NKB = nkb;
+  L.kv_num = bm->kv_num_blocks;
+  L.kv_idx = bm->kv_indices;
+  L.full_num = bm->full_kv_num_blocks;
+  L.full_idx = bm->full_kv_indices;
+  L.schedule = bm->schedule;
+  hipError_t e = fa::launch_build(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(FLEXATTN_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
+                             const flexattn_tensor* v, const flexattn_block_mask* bm,
+                             flexattn_score_kind score_kind, const flexattn_score_params* params,
+                             float scale, flexattn_tensor* out, float* lse, void* stream) {
+  static const char* who = "flexattn_fwd";
+  flexattn_status st;
+  if ((st = check_tensor(q, "q")) != FLEXATTN_OK) return st;
+  if ((st = check_tensor(k, "k")) != FLEXATTN_OK) return st;
+  if ((st = check_tensor(v, "v")) != FLEXATTN_OK) return st;
+  if ((st = check_tensor(out, "out")) != FLEXATTN_OK) return st;
+  if (!lse) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: lse is NULL", who);
+  if (!bm) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: bm is NULL", who);
+  if (k->dtype != q->dtype || v->dtype != q->dtype || out->dtype != q->dtype)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: q, k, v and out must share one dtype", who);
+  if (q->D != 64 && q->D != 128)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: head dim %d is not 64 or 128", who, q->D);
+  if (k->D != q->D || v->D != q->D || out->D != q->D)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: q, k, v, out head dims differ", who);
+  if (k->B != q->B || v->B != q->B || out->B != q->B)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: batch sizes differ", who);
+  if (k->H != v->H || out->H != q->H)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: head counts of k/v or q/out differ", who);
+  if (q->H % k->H != 0)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", who, q->H,
+                k->H);
+  if (k->L != v->L) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: k and v lengths differ", who);
+  if (out->L != q->L) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: out and q lengths differ", who);
+  if (!(std::isfinite(scale)))
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: scale is not finite", who);
+  // BlockMask consistency
+  if (bm->BLOCK_SIZE != fa::kBlock)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: BlockMask BLOCK_SIZE must be 128 (got %d)", who,
+                bm->BLOCK_SIZE);
+  if (bm->Q_LEN != q->L || bm->KV_LEN != k->L)
+    return fail(FLEXATTN_ERR_INVALID_ARG,
+                "%s: BlockMask built for Q_LEN=%d KV_LEN=%d, tensors have %d and %d", who,
+                bm->Q_LEN, bm->KV_LEN, q->L, k->L);
+  if (bm->num_q_blocks != ceil_div(q->L, fa::kBlock) ||
+      bm->num_kv_blocks != ceil_div(k->L, fa::kBlock))
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: BlockMask tile counts do not match its lengths",
+                who);
+  if (!(bm->B == 1 || bm->B == q->B) || !(bm->H == 1 || bm->H == q->H))
+    return fail(FLEXATTN_ERR_INVALID_ARG,
+                "%s: BlockMask extents (B=%d, H=%d) must be 1 or match q (B=%d, H=%d)", who, bm->B,
+                bm->H, q->B, q->H);
+  if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices ||
+      !bm->schedule)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: a BlockMask buffer pointer is NULL", who);
+  fa::MaskParams mp;
+  int doc_len = 0;
+  if ((st = check_mask(bm->mask_kind, &bm->mask_params, q->B, q->L, k->L, &mp, &doc_len, who)) !=
+      FLEXATTN_OK)
+    return st;
+  if (bm->mask_kind == FLEXATTN_MASK_DOCUMENT_CAUSAL && bm->mask_params.doc_batch > 1 &&
+      bm->B != q->B)
+    return fail(FLEXATTN_ERR_INVALID_ARG,
+                "%s: per-batch doc_ids need a BlockMask built per batch (B=%d)", who, q->B);
+  if ((long long)q->B * q->H * bm->num_q_blocks > 0x7fffffffLL)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: too many query tiles for one launch", who);
+  if ((int)score_kind < FLEXATTN_SCORE_NONE || (int)score_kind > FLEXATTN_SCORE_SOFTCAP_ALIBI)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: score_kind %d is not a supported kind", who,
+                (int)score_kind);
+  float softcap = 0.0f;
+  const float* slopes = nullptr;
+  if (score_kind == FLEXATTN_SCORE_SOFTCAP || score_kind == FLEXATTN_SCORE_SOFTCAP_ALIBI) {
+    if (!params || !(params->softcap > 0.0f) || !std::isfinite(params->softcap))
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: softcap must be a finite value > 0", who);
+    softcap = params->softcap;
+  }
+  if (score_kind == FLEXATTN_SCORE_ALIBI || score_kind == FLEXATTN_SCORE_SOFTCAP_ALIBI)
+    slopes = params ? params->alibi_slopes : nullptr;
+
+  fa::FwdLaunch L;
+  L.q = q->data;
+  L.k = k->data;
+  L.v = v->data;
+  L.o = out->data;
+  L.lse = lse;
+  for (int i = 0; i < 3; ++i) {
+    L.sq[i] = q->stride[i];
+    L.sk[i] = k->stride[i];
+    L.sv[i] = v->stride[i];
+    L.so[i] = out->stride[i];
+  }
+  L.B = q->B;
+  L.Hq = q->H;
+  L.Hkv = k->H;
+  L.Q_LEN = q->L;
+  L.KV_LEN = k->L;
+  L.D = q->D;
+  L.mask_kind = (int)bm->mask_kind;
+  L.mp = mp;
+  L.score_kind = (int)score_kind;
+  L.softcap = softcap;
+  L.slopes = slopes;
+  L.scale = scale;
+  L.bm.kv_num = bm->kv_num_blocks;
+  L.bm.kv_idx = bm->kv_indices;
+  L.bm.full_num = bm->full_kv_num_blocks;
+  L.bm.full_idx = bm->full_kv_indices;
+  L.bm.schedule = bm->schedule;
+  L.bm.Bm = bm->B;
+  L.bm.Hm = bm->H;
+  L.bm.NQB = bm->num_q_blocks;
+  L.bm.NKB = bm->num_kv_blocks;
+  hipError_t e = (q->dtype == FLEXATTN_BF16)
+                     ? fa::launch_fwd_bf16(L, static_cast<hipStream_t>(stream))
+                     : fa::launch_fwd_f32(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(FLEXATTN_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,352 @@
+// BlockMask builder for gfx950: classify every 128x128 tile of the element
+// mask as empty / partial / full, write the ascending per-row tile lists,
+// then order the rows by tile count for the forward's work schedule.
+//
+// Follows page "tensorplay.nn.attention API", section create_block_mask
+// (separate_full_blocks=True) and section BlockMask ("Basics": a tile is
+// skipped only when all its elements are masked; "Details" item 2: full tiles
+// listed apart; the row-compressed count + index-list format).
+//
+// Counting. For the enumerated mask kinds the allowed keys of one query row
+// form at most two intervals, so the allowed count of a row inside a KV tile
+// is O(1) arithmetic and a tile's count is a sum over its 128 rows:
+//   NOOP          [0, KV_LEN)
+//   CAUSAL        [0, q]
+//   SLIDING_SINK  [q - window + 1, q]  union  [0, min(sinks - 1, q)]
+//   DOCUMENT      [start of q's run of equal ids, q]  -- valid when the ids
+//                 never decrease (each document one contiguous run, the packed
+//                 layout); otherwise every element is compared.
+// The counts are exact, so the classification equals a per-element
+// evaluation of the mask.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace fa {
+
+namespace {
+
+constexpr int kRowThreads = kBlock;  // one thread per query row of a tile
+
+struct BuildArgs {
+  int kind;
+  MaskParams mp;
+  int doc_len;
+  int Bm, Hm, Q_LEN, KV_LEN, NQB, NKB;
+  int* kv_num;
+  int* kv_idx;
+  int* full_num;
+  int* full_idx;
+};
+
+__device__ __forceinline__ int clamp_len(int lo, int hi) { return hi >= lo ? hi - lo + 1 : 0; }
+
+// Wave-wide sum (64 lanes) with cross-lane shuffles.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Inclusive prefix sum over the 128 threads of the block (2 waves).
+__device__ __forceinline__ int block_incl_scan128(int v, int* lds2) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) lds2[wave] = v;
+  __syncthreads();
+  if (wave == 1) v += lds2[0];
+  __syncthreads();
+  return v;
+}
+
+// Inclusive max-scan over the 128 threads (2 waves).
+__device__ __forceinline__ int block_incl_max128(int v, int* lds2) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int u = __shfl_up(v, off, 64);
+    if (lane >= off) v = max(v, u);
+  }
+  if (lane == 63) lds2[wave] = v;
+  __syncthreads();
+  if (wave == 1) v = max(v, lds2[0]);
+  __syncthreads();
+  return v;
+}
+
+// Does doc[0..n) never decrease? Block-wide answer.
+__device__ bool doc_is_sorted(const int* doc, int n) {
+  int bad = 0;
+  for (int i = threadIdx.x; i + 1 < n; i += blockDim.x) bad |= (doc[i] > doc[i + 1]);
+  return __syncthreads_or(bad) == 0;
+}
+
+// First index of the run containing position q0 in a non-decreasing doc row:
+// the smallest i with doc[i] == doc[q0]. Two rounds of a 128-way parallel
+// search over [0, q0].
+__device__ int run_start_of(const int* doc, int q0, int* lds) {
+  const int t = threadIdx.x;
+  const int key = doc[q0];
+  // Round 1: coarse grid of 128 probes over [0, q0].
+  const int step = (q0 + kRowThreads) / kRowThreads;  // >= 1, covers [0, q0]
+  int p = t * step;
+  int hit = (p <= q0 && doc[p] < key) ? t : -1;  // last probe strictly before the run
+  hit = block_incl_max128(hit, lds);
+  if (t == kRowThreads - 1) lds[2] = hit;  // inclusive scan: thread 127 holds the max
+  __syncthreads();
+  const int lastp = lds[2];
+  __syncthreads();
+  if (lastp < 0) return 0;  // probe 0 (position 0) already holds the key
+  int lo, hi;
+  lo = lastp * step + 1;             // first candidate after the last "before" probe
+  hi = min(q0, lo + step - 1);        // the run starts within [lo, hi]
+  // Round 2: positions lo + t*r covering [lo, hi] with r = ceil(len/128).
+  const int len = hi - lo + 1;
+  const int r = (len + kRowThreads - 1) / kRowThreads;
+  int first = 0x7fffffff;
+  for (int i = 0; i < r; ++i) {
+    int pos = lo + t * r + i;
+    if (pos <= hi && doc[pos] == key) first = min(first, pos);
+  }
+  // block min via negated max-scan
+  int neg = block_incl_max128(-first, lds);
+  if (threadIdx.x == 127) lds[2] = -neg;
+  __syncthreads();
+  int res = lds[2];
+  __syncthreads();
+  return res;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
+  extern __shared__ int smem[];  // [2][NKB] per-wave partial counts, then class flags
+  __shared__ int scratch[4];
+  const int row = blockIdx.x;  // (bm * Hm + hm) * NQB + qb
+  const int qb = row % a.NQB;
+  const int bm = row / (a.NQB * a.Hm);
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int q = qb * kBlock + t;
+  const bool qvalid = q < a.Q_LEN;
+  const int NKB = a.NKB;
+  int* wsum = smem;  // [2][NKB]
+
+  // Per-row allowed intervals: I1 = [lo1, hi1], I2 = [lo2, hi2] (may be empty).
+  int lo1 = 0, hi1 = -1, lo2 = 0, hi2 = -1;
+  bool brute = false;
+  const int* doc = nullptr;
+  if constexpr (KIND == MASK_DOCUMENT) {
+    doc = a.mp.doc + (long long)bm * a.mp.doc_bstride;
+    const int n = max(a.Q_LEN, a.KV_LEN);
+    const bool sorted = doc_is_sorted(doc, n);
+    if (sorted) {
+      const int q0 = qb * kBlock;
+      const int s0 = run_start_of(doc, q0, scratch);
+      // run boundaries inside this tile, then the latest boundary <= q
+      int bnd = (qvalid && q > q0 && doc[q] != doc[q - 1]) ? q : -1;
+      bnd = block_incl_max128(bnd, scratch);
+      const int start = bnd >= 0 ? bnd : s0;
+      lo1 = start;
+      hi1 = q;
+    } else {
+      brute = true;
+    }
+  } else if constexpr (KIND == MASK_NOOP) {
+    lo1 = 0;
+    hi1 = a.KV_LEN - 1;
+  } else if constexpr (KIND == MASK_CAUSAL) {
+    lo1 = 0;
+    hi1 = q;
+  } else {  // SLIDING_SINK
+    lo1 = max(0, q - a.mp.window + 1);
+    hi1 = q;
+    lo2 = 0;
+    hi2 = min(a.mp.sinks - 1, q);
+  }
+  hi1 = min(hi1, a.KV_LEN - 1);
+  hi2 = min(hi2, a.KV_LEN - 1);
+
+  for (int j = 0; j < NKB; ++j) {
+    const int c0 = j * kBlock;
+    const int c1 = min(c0 + kBlock - 1, a.KV_LEN - 1);
+    int cnt = 0;
+    if (qvalid) {
+      if constexpr (KIND == MASK_DOCUMENT) {
+        if (brute) {
+          const int dq = doc[q];
+          const int e = min(c1, q);
+          for (int kv = c0; kv <= e; ++kv) cnt += (doc[kv] == dq);
+        } else {
+          cnt = clamp_len(max(lo1, c0), min(hi1, c1));
+        }
+      } else {
+        cnt = clamp_len(max(lo1, c0), min(hi1, c1));
+        if constexpr (KIND == MASK_SLIDING_SINK) {
+          // |I1 u I2| = |I1| + |I2| - |I1 n I2|, each clipped to the tile
+          cnt += clamp_len(max(lo2, c0), min(hi2, c1));
+          cnt -= clamp_len(max(max(lo1, lo2), c0), min(min(hi1, hi2), c1));
+        }
+      }
+    }
+    cnt = wave_sum(cnt);
+    if (lane == 0) wsum[wave * NKB + j] = cnt;
+  }
+  __syncthreads();
+
+  // Classify and compact in chunks of 128 tiles, keeping ascending order.
+  const long long base = (long long)row * NKB;
+  int np_total = 0, nf_total = 0;
+  for (int j0 = 0; j0 < NKB; j0 += kRowThreads) {
+    const int j = j0 + t;
+    int isP = 0, isF = 0;
+    if (j < NKB) {
+      const int tot = wsum[j] + wsum[NKB + j];
+      isF = (tot == kBlock * kBlock);
+      isP = (tot > 0 && !isF);
+    }
+    const int incP = block_incl_scan128(isP, scratch);
+    const int incF = block_incl_scan128(isF, scratch);
+    if (isP) a.kv_idx[base + np_total + incP - 1] = j;
+    if (isF) a.full_idx[base + nf_total + incF - 1] = j;
+    // totals of this chunk live in the last thread
+    if (t == kRowThreads - 1) {
+      scratch[2] = incP;
+      scratch[3] = incF;
+    }
+    __syncthreads();
+    np_total += scratch[2];
+    nf_total += scratch[3];
+    __syncthreads();
+  }
+  // zero the unused tails
+  for (int j = t; j < NKB; j += kRowThreads) {
+    if (j >= np_total) a.kv_idx[base + j] = 0;
+    if (j >= nf_total) a.full_idx[base + j] = 0;
+  }
+  if (t == 0) {
+    a.kv_num[row] = np_total;
+    a.full_num[row] = nf_total;
+  }
+}
+
+// Stable ordering of rows by descending tile count (ties: ascending row id),
+// one workgroup: histogram, suffix offsets, then a stable scatter in chunks.
+constexpr int kSchedThreads = 1024;
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int* kv_num,
+                                                                 const int* full_num, int n,
+                                                                 int nbins, int* schedule) {
+  extern __shared__ int sm[];
+  int* hist = sm;             // [nbins]  -> suffix offsets
+  int* running = sm + nbins;  // [nbins]
+  __shared__ int keys[kSchedThreads];
+  __shared__ int part[kSchedThreads];
+  const int t = threadIdx.x;
+  for (int c = t; c < nbins; c += kSchedThreads) {
+    hist[c] = 0;
+    running[c] = 0;
+  }
+  __syncthreads();
+  for (int i = t; i < n; i += kSchedThreads) atomicAdd(&hist[kv_num[i] + full_num[i]], 1);
+  __syncthreads();
+  // offsets for descending keys: off[c] = sum_{c' > c} hist[c'].
+  // Each thread owns a contiguous segment of bins, scanned from the top.
+  const int seg = (nbins + kSchedThreads - 1) / kSchedThreads;
+  const int hi_bin = nbins - 1 - t * seg;  // segment covers bins (hi_bin - seg, hi_bin]
+  int local = 0;
+  for (int s = 0; s < seg; ++s) {
+    const int c = hi_bin - s;
+    if (c >= 0) local += hist[c];
+  }
+  part[t] = local;
+  __syncthreads();
+  // exclusive prefix over segments (segment order = descending bins)
+  if (t == 0) {
+    int acc = 0;
+    for (int i = 0; i < kSchedThreads; ++i) {
+      const int v = part[i];
+      part[i] = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  int acc = part[t];
+  for (int s = 0; s < seg; ++s) {
+    const int c = hi_bin - s;
+    if (c >= 0) {
+      const int h = hist[c];
+      hist[c] = acc;  // becomes the offset of bin c
+      acc += h;
+    }
+  }
+  __syncthreads();
+  for (int base = 0; base < n; base += kSchedThreads) {
+    const int i = base + t;
+    const int key = (i < n) ? kv_num[i] + full_num[i] : -1;
+    keys[t] = key;
+    __syncthreads();
+    if (i < n) {
+      int rank = 0;
+      for (int u = 0; u < t; ++u) rank += (keys[u] == key);
+      schedule[hist[key] + running[key] + rank] = i;
+    }
+    __syncthreads();
+    if (i < n) atomicAdd(&running[key], 1);
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+int max_build_kv_blocks() {
+  // [2][NKB] ints of dynamic LDS for the classify kernel, two int arrays of
+  // NKB+1 bins for the schedule kernel; stay well inside 64 KiB.
+  return 4096;
+}
+
+hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
+  BuildArgs a;
+  a.kind = L.kind;
+  a.mp = L.mp;
+  a.doc_len = L.doc_len;
+  a.Bm = L.Bm;
+  a.Hm = L.Hm;
+  a.Q_LEN = L.Q_LEN;
+  a.KV_LEN = L.KV_LEN;
+  a.NQB = L.NQB;
+  a.NKB = L.NKB;
+  a.kv_num = L.kv_num;
+  a.kv_idx = L.kv_idx;
+  a.full_num = L.full_num;
+  a.full_idx = L.full_idx;
+  const int rows = L.Bm * L.Hm * L.NQB;
+  const size_t lds = sizeof(int) * 2 * (size_t)L.NKB;
+  switch (L.kind) {
+    case MASK_NOOP:
+      classify_kernel<MASK_NOOP><<<rows, kRowThreads, lds, stream>>>(a);
+      break;
+    case MASK_CAUSAL:
+      classify_kernel<MASK_CAUSAL><<<rows, kRowThreads, lds, stream>>>(a);
+      break;
+    case MASK_SLIDING_SINK:
+      classify_kernel<MASK_SLIDING_SINK><<<rows, kRowThreads, lds, stream>>>(a);
+      break;
+    default:
+      classify_kernel<MASK_DOCUMENT><<<rows, kRowThreads, lds, stream>>>(a);
+      break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nbins = L.NKB + 1;
+  schedule_kernel<<<1, kSchedThreads, sizeof(int) * 2 * (size_t)nbins, stream>>>(
+      L.kv_num, L.full_num, rows, nbins, L.schedule);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,102 @@
+// Shared device-side definitions for the gfx950 block-sparse attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+constexpr int kBlock = 128;  // BlockMask tile edge (queries and keys)
+
+// Kinds, mirrored from the C header's enums (kept numeric so kernels can be
+// templated on them).
+enum MaskKind : int { MASK_NOOP = 0, MASK_CAUSAL = 1, MASK_SLIDING_SINK = 2, MASK_DOCUMENT = 3 };
+enum ScoreKind : int { SCORE_NONE = 0, SCORE_ALIBI = 1, SCORE_SOFTCAP = 2, SCORE_SOFTCAP_ALIBI = 3 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Mask parameters as the kernels see them. `doc` already points at batch
+// row 0; `doc_bstride` is 0 when one document row is shared by all batches.
+struct MaskParams {
+  int window;
+  int sinks;
+  const int* doc;
+  long long doc_bstride;
+};
+
+// The BlockMask as the forward reads it.
+struct BlockMaskView {
+  const int* kv_num;    // [Bm][Hm][NQB]
+  const int* kv_idx;    // [Bm][Hm][NQB][NKB]
+  const int* full_num;  // [Bm][Hm][NQB]
+  const int* full_idx;  // [Bm][Hm][NQB][NKB]
+  const int* schedule;  // [Bm*Hm*NQB]
+  int Bm, Hm, NQB, NKB;
+};
+
+// Element mask of each kind: allowed(b, q, kv) for in-range indices.
+template <int KIND>
+struct Mask;
+
+template <>
+struct Mask<MASK_NOOP> {
+  __device__ __forceinline__ static bool allowed(const MaskParams&, const int*, int, int) {
+    return true;
+  }
+};
+
+template <>
+struct Mask<MASK_CAUSAL> {
+  __device__ __forceinline__ static bool allowed(const MaskParams&, const int*, int q, int kv) {
+    return kv <= q;
+  }
+};
+
+template <>
+struct Mask<MASK_SLIDING_SINK> {
+  __device__ __forceinline__ static bool allowed(const MaskParams& p, const int*, int q, int kv) {
+    return kv <= q && ((q - kv) < p.window || kv < p.sinks);
+  }
+};
+
+template <>
+struct Mask<MASK_DOCUMENT> {
+  // doc: this batch's document id row.
+  __device__ __forceinline__ static bool allowed(const MaskParams&, const int* doc, int q, int kv) {
+    return kv <= q && doc[q] == doc[kv];
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Score modification in the base-2 domain. `s` is the raw dot product q.k;
+// the result is log2(e) * score_mod(scale * s), so exp2 of it is exp of the
+// modified score.
+//   c_scale  = scale * log2(e)
+//   c_cap    = 2 * scale * log2(e) / softcap       (tanh argument, doubled)
+//   cap2     = softcap * log2(e)
+//   slope2   = m_h * log2(e)
+template <int SCORE>
+struct ScoreMod {
+  __device__ __forceinline__ static float apply(float s, float c_scale, float c_cap, float cap2,
+                                                float slope2, float dist) {
+    float x;
+    if constexpr (SCORE == SCORE_SOFTCAP || SCORE == SCORE_SOFTCAP_ALIBI) {
+      // softcap * tanh(y) with tanh(y) = 1 - 2 / (exp(2y) + 1)
+      float e = fast_exp2(s * c_cap);
+      float r = fast_rcp(e + 1.0f);
+      x = fmaf(r, -2.0f * cap2, cap2);
+    } else {
+      x = s * c_scale;
+    }
+    if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI) {
+      x = fmaf(slope2, dist, x);
+    }
+    return x;
+  }
+};
+
+}  // namespace fa

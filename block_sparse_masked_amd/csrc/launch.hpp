@@ -1,0 +1,48 @@
+// Internal launch interface between the C ABI layer and the HIP kernels.
+// Everything here has been validated by the caller (api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace fa {
+
+struct BuildLaunch {
+  int kind;
+  MaskParams mp;
+  int doc_len;
+  int Bm, Hm, Q_LEN, KV_LEN, NQB, NKB;
+  int* kv_num;
+  int* kv_idx;
+  int* full_num;
+  int* full_idx;
+  int* schedule;
+};
+
+hipError_t launch_build(const BuildLaunch& L, hipStream_t stream);
+int max_build_kv_blocks();
+
+struct FwdLaunch {
+  // element strides for b, h, l (d is contiguous)
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  long long sq[3], sk[3], sv[3], so[3];
+  int B, Hq, Hkv, Q_LEN, KV_LEN, D;
+  int mask_kind;
+  MaskParams mp;
+  int score_kind;
+  float softcap;
+  const float* slopes;  // device [Hq] or nullptr
+  float scale;
+  BlockMaskView bm;
+};
+
+hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdLaunch& L, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,219 @@
+/*
+ * flexattn.h - C ABI of the MI355X (gfx950) FlexAttention-style block-sparse
+ * attention forward: a BlockMask builder and a tiled block-sparse forward.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named "device" are HIP device pointers; everything else is host.
+ * - The caller owns and allocates every buffer (inputs, outputs and the
+ *   BlockMask index tensors, sized with flexattn_block_mask_sizes). The
+ *   library allocates no device memory, keeps no state between calls and
+ *   never frees caller memory.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   All device work is enqueued on it asynchronously: no host
+ *   synchronisation and no device-to-host copy, so the calls can be captured
+ *   in a HIP graph.
+ * - Every argument is checked on the host before any HIP call. A bad
+ *   argument returns FLEXATTN_ERR_INVALID_ARG (bad pointer, shape, stride,
+ *   alignment) or FLEXATTN_ERR_UNSUPPORTED (a dtype, head dim, block size or
+ *   kind outside the supported set) and sets a thread-local message read by
+ *   flexattn_last_error(); nothing is launched. A failed launch returns
+ *   FLEXATTN_ERR_HIP. No C++ exception crosses this boundary.
+ * - Index tensors are int32; layouts are row-major (C order).
+ */
+#ifndef FLEXATTN_H
+#define FLEXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLEXATTN_OK = 0,
+  FLEXATTN_ERR_INVALID_ARG = 1,
+  FLEXATTN_ERR_UNSUPPORTED = 2,
+  FLEXATTN_ERR_HIP = 3
+} flexattn_status;
+
+/*
+ * mask_mod kinds: a fixed, enumerated set of element masks
+ * allowed(b, h, q_idx, kv_idx) -> bool, true = the pair may attend
+ * (page "tensorplay.nn.attention API", section create_block_mask, the
+ * mask_mod parameter and the causal_mask example; noop_mask; and_masks and
+ * or_masks compose the sliding-window kind).
+ *   NOOP             every pair.
+ *   CAUSAL           kv_idx <= q_idx.
+ *   SLIDING_SINK     kv_idx <= q_idx AND (q_idx - kv_idx < window OR
+ *                    kv_idx < num_sinks): a sliding window plus StreamingLLM
+ *                    sink tokens (page "transformerlab", section "Attention
+ *                    variants", rows local_flex and sink).
+ *   DOCUMENT_CAUSAL  doc[q_idx] == doc[kv_idx] AND kv_idx <= q_idx: causal
+ *                    attention inside each packed document, the
+ *                    block-diagonal mask of page "Attention Backends"
+ *                    (section "Why care about Attention Kernels?").
+ */
+typedef enum {
+  FLEXATTN_MASK_NOOP = 0,
+  FLEXATTN_MASK_CAUSAL = 1,
+  FLEXATTN_MASK_SLIDING_SINK = 2,
+  FLEXATTN_MASK_DOCUMENT_CAUSAL = 3
+} flexattn_mask_kind;
+
+typedef struct {
+  int32_t window;          /* SLIDING_SINK: >= 1                                  */
+  int32_t num_sinks;       /* SLIDING_SINK: >= 0                                  */
+  const int32_t* doc_ids;  /* DOCUMENT_CAUSAL: device int32 [doc_batch][doc_len];
+                              read through both q_idx and kv_idx; any id values */
+  int32_t doc_batch;       /* DOCUMENT_CAUSAL: 1 (shared by all batches) or B     */
+  int32_t doc_len;         /* DOCUMENT_CAUSAL: >= max(Q_LEN, KV_LEN)              */
+} flexattn_mask_params;
+
+/*
+ * score_mod kinds: s is the scaled score scale * (q . k); the modified score
+ * replaces it before the softmax (page "attention-gym: examples, masks and
+ * kernels for FlexAttention", section "A gallery that grew into a toolkit").
+ *   NONE            s.
+ *   ALIBI           s + m_h * (kv_idx - q_idx) (page "transformerlab",
+ *                   section "Attention variants", row alibi).
+ *   SOFTCAP         softcap * tanh(s / softcap) (page "Attention Backends",
+ *                   tanh soft-capping).
+ *   SOFTCAP_ALIBI   softcap * tanh(s / softcap) + m_h * (kv_idx - q_idx).
+ * m_h is alibi_slopes[h] for query head h, or 2^(-8 (h + 1) / Hq) when
+ * alibi_slopes is NULL.
+ */
+typedef enum {
+  FLEXATTN_SCORE_NONE = 0,
+  FLEXATTN_SCORE_ALIBI = 1,
+  FLEXATTN_SCORE_SOFTCAP = 2,
+  FLEXATTN_SCORE_SOFTCAP_ALIBI = 3
+} flexattn_score_kind;
+
+typedef struct {
+  float softcap;              /* SOFTCAP kinds: > 0, finite                */
+  const float* alibi_slopes;  /* ALIBI kinds: device float [Hq], or NULL   */
+} flexattn_score_params;
+
+typedef enum { FLEXATTN_F32 = 0, FLEXATTN_BF16 = 1 } flexattn_dtype;
+
+/*
+ * A 4-D attention tensor [B][H][L][D] in device memory. stride[] are element
+ * strides of the B, H, L and D dimensions; stride[3] must be 1 (rows
+ * contiguous), each row must start 16-byte aligned (data and the other
+ * strides times the element size are multiples of 16 bytes).
+ */
+typedef struct {
+  void* data;
+  flexattn_dtype dtype;
+  int32_t B, H, L, D;
+  int64_t stride[4];
+} flexattn_tensor;
+
+/*
+ * BlockMask (page "tensorplay.nn.attention API", section BlockMask): the
+ * element mask reduced to BLOCK_SIZE x BLOCK_SIZE tiles. A tile is empty when
+ * every element in it is masked and is then never computed ("Basics"); a tile
+ * is full when all BLOCK_SIZE^2 elements exist and are allowed, so the kernel
+ * skips mask_mod on it ("Details", item 2); other non-empty tiles are partial.
+ * For each (b, h, q row-tile) the partial tiles are listed in (kv_num_blocks,
+ * kv_indices) and the full ones in (full_kv_num_blocks, full_kv_indices):
+ * a count plus the KV tile positions, ascending, the unused tail set to 0.
+ * Out-of-range elements of a tail tile count as masked, so a tail tile is
+ * never full.
+ *
+ * Fields (all index tensors are caller-allocated device int32 buffers):
+ *   B, H                 extents of the index tensors over batch and query
+ *                        heads; 1 broadcasts over that dimension.
+ *   Q_LEN, KV_LEN        sequence lengths; BLOCK_SIZE = 128.
+ *   num_q_blocks (NQB)   ceil(Q_LEN / BLOCK_SIZE); num_kv_blocks (NKB) likewise.
+ *   kv_num_blocks        [B][H][NQB]
+ *   kv_indices           [B][H][NQB][NKB]
+ *   full_kv_num_blocks   [B][H][NQB]
+ *   full_kv_indices      [B][H][NQB][NKB]
+ *   schedule             [B*H*NQB]: row ids (b*H + h)*NQB + qb ordered by
+ *                        descending tile count (partial + full), ties by
+ *                        ascending row id; the forward visits rows in this
+ *                        order (longest first) for load balance.
+ *   mask_kind, mask_params  the mask_mod the partial tiles are evaluated with.
+ * A caller may fill the struct from its own index lists (the from_kv_blocks
+ * use); their contents are then trusted as given.
+ */
+typedef struct {
+  int32_t B, H;
+  int32_t Q_LEN, KV_LEN, BLOCK_SIZE;
+  int32_t num_q_blocks, num_kv_blocks;
+  int32_t* kv_num_blocks;
+  int32_t* kv_indices;
+  int32_t* full_kv_num_blocks;
+  int32_t* full_kv_indices;
+  int32_t* schedule;
+  flexattn_mask_kind mask_kind;
+  flexattn_mask_params mask_params;
+} flexattn_block_mask;
+
+/*
+ * Element counts of the BlockMask buffers for a build at (B, H, Q_LEN,
+ * KV_LEN, block): num_elems for each of kv_num_blocks / full_kv_num_blocks,
+ * idx_elems for each of kv_indices / full_kv_indices, sched_elems for
+ * schedule. Host only. Output pointers must be non-NULL.
+ */
+flexattn_status flexattn_block_mask_sizes(int32_t B, int32_t H, int32_t Q_LEN, int32_t KV_LEN,
+                                          int32_t block, size_t* num_elems, size_t* idx_elems,
+                                          size_t* sched_elems);
+
+/*
+ * create_block_mask (page "tensorplay.nn.attention API", section
+ * create_block_mask, with separate_full_blocks=True): evaluates the mask_mod
+ * of `kind` over every (b, h, q_idx, kv_idx), classifies each tile and writes
+ * the four index tensors plus the schedule into the buffers `bm` points to.
+ * B and H give the extents to build (1 = one build broadcast over that
+ * dimension; the enumerated kinds do not depend on b or h except through
+ * per-batch doc_ids). On input the caller sets bm->kv_num_blocks,
+ * kv_indices, full_kv_num_blocks, full_kv_indices and schedule; the call
+ * fills every other field. block must be 128. Asynchronous on `stream`.
+ */
+flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
+                                           const flexattn_mask_params* params, int32_t B,
+                                           int32_t H, int32_t Q_LEN, int32_t KV_LEN,
+                                           int32_t block, flexattn_block_mask* bm, void* stream);
+
+/*
+ * The block-sparse attention forward (page "tensorplay.nn.attention API",
+ * BlockMask "Details" item 1: the forward reduces along the KV dimension
+ * using the per-row tile lists; item 2: mask_mod is skipped on full tiles;
+ * page "FlagAttention", section "Operator overview": q [B,Hq,M,D], k/v
+ * [B,Hkv,N,D], MQA/GQA). For every query row it visits only the listed KV
+ * tiles, computes s = scale * q.k, applies the score_mod, applies the
+ * mask_mod on partial tiles only, and accumulates the softmax-weighted sum of
+ * V online, never materialising the score matrix.
+ *   q     [B][Hq][Q_LEN][D]; k, v [B][Hkv][KV_LEN][D]; same dtype (F32 or
+ *         BF16); D in {64, 128}; Hq a multiple of Hkv; query head h reads KV
+ *         head h / (Hq / Hkv).
+ *   bm    a BlockMask with bm->Q_LEN == Q_LEN, bm->KV_LEN == KV_LEN,
+ *         bm->B in {1, B}, bm->H in {1, Hq}, BLOCK_SIZE 128.
+ *   out   [B][Hq][Q_LEN][D], same dtype as q (written).
+ *   lse   device float [B][Hq][Q_LEN], contiguous (written): natural-log
+ *         log-sum-exp of the modified, masked scores of each row.
+ * A row with no allowed key gets out = 0 and lse = -inf. bf16 inputs are
+ * contracted on bf16 MFMA with fp32 accumulation (softmax probabilities are
+ * rounded to bf16 for the P.V product); fp32 inputs are computed in fp32
+ * throughout. Asynchronous on `stream`.
+ */
+flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
+                             const flexattn_tensor* v, const flexattn_block_mask* bm,
+                             flexattn_score_kind score_kind, const flexattn_score_params* params,
+                             float scale, flexattn_tensor* out, float* lse, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). Host only. */
+const char* flexattn_last_error(void);
+
+/* Library version string. Host only. */
+const char* flexattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLEXATTN_H */

@@ -1,0 +1,164 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_masked_amd as lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names += re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\**\s*(flexattn_[a-z_]+)\s*\(",
+                                text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return lib.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("flexattn_create_block_mask", "flexattn_fwd", "flexattn_block_mask_sizes",
+                     "flexattn_last_error", "flexattn_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_last_error(L):
+    assert lib.version().startswith("flexattn-gfx950")
+    assert isinstance(L.flexattn_last_error(), bytes)
+
+
+def test_block_mask_sizes(L):
+    assert lib.block_mask_sizes(4, 16, 4096, 4096) == (4 * 16 * 32, 4 * 16 * 32 * 32, 4 * 16 * 32)
+    assert lib.block_mask_sizes(1, 1, 300, 129) == (3, 3 * 2, 3)
+    with pytest.raises(NotImplementedError, match="block must be 128"):
+        lib.block_mask_sizes(1, 1, 256, 256, 64)
+    with pytest.raises(ValueError, match="must be >= 1"):
+        lib.block_mask_sizes(0, 1, 256, 256)
+
+
+def _bm_struct(ptr=16):
+    c = lib._BlockMask()
+    for f in ("kv_num_blocks", "kv_indices", "full_kv_num_blocks", "full_kv_indices", "schedule"):
+        setattr(c, f, ptr)
+    return c
+
+
+def _create(L, kind, params, B=1, H=1, Q=256, K=256, block=128, bm=None):
+    bm = _bm_struct() if bm is None else bm
+    p = ctypes.byref(params) if params is not None else None
+    return L.flexattn_create_block_mask(kind, p, B, H, Q, K, block, ctypes.byref(bm), None)
+
+
+def test_create_block_mask_rejects_bad_arguments(L):
+    mp = lib._MaskParams(0, 0, None, 0, 0)
+    assert _create(L, 9, mp) == lib._UNSUPPORTED
+    assert b"mask_kind" in L.flexattn_last_error()
+    assert _create(L, 1, mp, block=64) == lib._UNSUPPORTED
+    assert _create(L, 1, mp, Q=0) == lib._INVALID
+    assert _create(L, 1, mp, bm=_bm_struct(ptr=0)) == lib._INVALID
+    assert L.flexattn_create_block_mask(1, None, 1, 1, 256, 256, 128, None, None) == lib._INVALID
+    # sliding window needs window >= 1 and sinks >= 0
+    assert _create(L, 2, lib._MaskParams(0, 0, None, 0, 0)) == lib._INVALID
+    assert b"window" in L.flexattn_last_error()
+    assert _create(L, 2, lib._MaskParams(4, -1, None, 0, 0)) == lib._INVALID
+    assert _create(L, 2, None) == lib._INVALID
+    # documents need ids, a long enough row and a valid batch count
+    assert _create(L, 3, lib._MaskParams(0, 0, None, 1, 256)) == lib._INVALID
+    assert _create(L, 3, lib._MaskParams(0, 0, 64, 1, 100)) == lib._INVALID
+    assert b"doc_len" in L.flexattn_last_error()
+    assert _create(L, 3, lib._MaskParams(0, 0, 64, 3, 256), B=2) == lib._INVALID
+    # builder limit on KV length
+    assert _create(L, 1, mp, K=128 * 5000) == lib._UNSUPPORTED
+
+
+def _tensor(dtype=1, B=1, H=2, L_=256, D=64, data=4096, strides=None):
+    if strides is None:
+        strides = (H * L_ * D, L_ * D, D, 1)
+    return lib._Tensor(data, dtype, B, H, L_, D, (ctypes.c_int64 * 4)(*strides))
+
+
+def _good_bm():
+    c = _bm_struct(ptr=4096)
+    c.B, c.H, c.Q_LEN, c.KV_LEN, c.BLOCK_SIZE = 1, 1, 256, 256, 128
+    c.num_q_blocks, c.num_kv_blocks = 2, 2
+    c.mask_kind = 1
+    return c
+
+
+def _fwd(L, q=None, k=None, v=None, o=None, bm=None, score=0, sp=None, scale=0.125, lse=4096):
+    q = _tensor() if q is None else q
+    k = _tensor() if k is None else k
+    v = _tensor() if v is None else v
+    o = _tensor() if o is None else o
+    bm = _good_bm() if bm is None else bm
+    sp = lib._ScoreParams(0.0, None) if sp is None else sp
+    return L.flexattn_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(bm),
+                          score, ctypes.byref(sp), scale, ctypes.byref(o),
+                          ctypes.c_void_p(lse), None)
+
+
+@pytest.mark.parametrize("case,expect,msg", [
+    (dict(q=_tensor(data=0)), lib._INVALID, b"q->data is NULL"),
+    (dict(k=_tensor(dtype=7)), lib._UNSUPPORTED, b"dtype"),
+    (dict(q=_tensor(D=96), k=_tensor(D=96), v=_tensor(D=96), o=_tensor(D=96)),
+     lib._UNSUPPORTED, b"head dim"),
+    (dict(v=_tensor(D=128)), lib._INVALID, b"head dims differ"),
+    (dict(k=_tensor(H=3), v=_tensor(H=3)), lib._INVALID, b"multiple"),
+    (dict(k=_tensor(dtype=0)), lib._INVALID, b"one dtype"),
+    (dict(q=_tensor(strides=(2 * 256 * 64, 256 * 64, 64, 2))), lib._INVALID, b"contiguous"),
+    (dict(q=_tensor(strides=(2 * 256 * 64, 256 * 64, 60, 1))), lib._INVALID, b"16 bytes"),
+    (dict(q=_tensor(data=4098)), lib._INVALID, b"aligned"),
+    (dict(lse=0), lib._INVALID, b"lse"),
+    (dict(scale=float("nan")), lib._INVALID, b"scale"),
+    (dict(score=9), lib._UNSUPPORTED, b"score_kind"),
+    (dict(score=2, sp=lib._ScoreParams(0.0, None)), lib._INVALID, b"softcap"),
+    (dict(score=3, sp=lib._ScoreParams(float("inf"), None)), lib._INVALID, b"softcap"),
+])
+def test_fwd_rejects_bad_arguments(L, case, expect, msg):
+    assert _fwd(L, **case) == expect
+    assert msg in L.flexattn_last_error()
+
+
+def test_fwd_rejects_mismatched_block_mask(L):
+    bm = _good_bm()
+    bm.Q_LEN = 512
+    assert _fwd(L, bm=bm) == lib._INVALID
+    bm = _good_bm()
+    bm.BLOCK_SIZE = 64
+    assert _fwd(L, bm=bm) == lib._UNSUPPORTED
+    bm = _good_bm()
+    bm.H = 3
+    assert _fwd(L, bm=bm) == lib._INVALID
+    bm = _good_bm()
+    bm.num_kv_blocks = 5
+    assert _fwd(L, bm=bm) == lib._INVALID
+    bm = _good_bm()
+    bm.schedule = 0
+    assert _fwd(L, bm=bm) == lib._INVALID
+
+
+def test_python_wrapper_maps_errors():
+    import torch
+    with pytest.raises(NotImplementedError):
+        lib.create_block_mask("prefix_lm", 1, 1, 128, 128, device="cpu")
+    q = torch.zeros(1, 1, 128, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        lib._tensor(q, "q")
+    with pytest.raises(NotImplementedError):
+        lib._tensor(q.half(), "q")

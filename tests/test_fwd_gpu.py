@@ -1,0 +1,185 @@
+"""GPU forward vs the fp64 oracle, element by element, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_masked_amd as m
+    m.load_library()
+    return m
+
+
+def tiny(dtype, D, mask, score, B=2, Hq=4, Hkv=2, Q_LEN=300, KV_LEN=300, seed=0, **kw):
+    return W.Workload(f"tiny_{dtype}_{D}_{mask}_{score}", B=B, Hq=Hq, Hkv=Hkv, Q_LEN=Q_LEN,
+                      KV_LEN=KV_LEN, D=D, dtype=dtype, seed=seed, mask=mask,
+                      window=kw.get("window", 100), sinks=kw.get("sinks", 3),
+                      doc_seed=kw.get("doc_seed", 77), doc_len_range=kw.get("doc_len_range", (20, 150)),
+                      score=score, softcap=kw.get("softcap", 20.0),
+                      value_scale=kw.get("value_scale", 1.0))
+
+
+def check_full(lib, w, B_mask=1, H_mask=1):
+    inp = W.generate(w)
+    bm = G.build_gpu_mask(lib, w, inp, B_mask, H_mask)
+    o, lse, _ = G.run_gpu(lib, w, inp, bm)
+    o_ref, lse_ref = G.oracle_rows(w, inp)
+    res = G.compare(w, o, lse, o_ref, lse_ref)
+    assert res["ok"], G.summary(res)
+    return res
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal"])
+@pytest.mark.parametrize("score", ["none", "alibi", "softcap", "softcap_alibi"])
+def test_fwd_tiny_grid(lib, dtype, D, mask, score):
+    """Every dtype x head dim x mask x score kind, with GQA, 3 query tiles and a
+    ragged tail (300 = 2*128 + 44). bf16 softcap cases scale the inputs by 2
+    (cap 20); fp32 cases keep unit-variance inputs, where the 1e-5 bound is
+    stated, and use cap 2 so tanh is far from linear."""
+    if dtype == "f32":
+        w = tiny(dtype, D, mask, score, softcap=2.0)
+    else:
+        w = tiny(dtype, D, mask, score, value_scale=2.0 if "softcap" in score else 1.0)
+    check_full(lib, w)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("q_len,kv_len", [(1, 1), (1, 200), (200, 1), (129, 257), (257, 129),
+                                          (128, 128), (513, 200)])
+def test_fwd_ragged_lengths(lib, dtype, q_len, kv_len):
+    check_full(lib, tiny(dtype, 64, "causal", "none", Q_LEN=q_len, KV_LEN=kv_len, B=1, Hq=2))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fwd_mqa_and_per_head_mask(lib, dtype):
+    """One KV head for eight query heads; BlockMask built per (b, h)."""
+    w = tiny(dtype, 128, "sliding_sink", "alibi", B=2, Hq=8, Hkv=1, Q_LEN=260, KV_LEN=260)
+    check_full(lib, w, B_mask=2, H_mask=8)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fwd_empty_rows(lib, dtype):
+    """Rows with no allowed key (window 8, no sinks, queries past the keys):
+    O = 0 and LSE = -inf."""
+    w = tiny(dtype, 64, "sliding_sink", "none", B=1, Hq=2, Hkv=2, Q_LEN=300, KV_LEN=140,
+             window=8, sinks=0)
+    res = check_full(lib, w)
+    assert res["dead_rows"] > 0 and res["dead_ok"]
+
+
+def test_fwd_document_not_sorted(lib):
+    """Document ids that are not contiguous runs (the general definition)."""
+    w = tiny("bf16", 64, "document_causal", "none", B=1, Hq=2, Hkv=1, Q_LEN=400, KV_LEN=400)
+    inp = W.generate(w)
+    inp.doc_ids = np.random.default_rng(3).integers(0, 4, size=400).astype(np.int32)
+    o, lse, _ = G.run_gpu(lib, w, inp)
+    o_ref, lse_ref = G.oracle_rows(w, inp)
+    res = G.compare(w, o, lse, o_ref, lse_ref)
+    assert res["ok"], G.summary(res)
+
+
+def test_fwd_explicit_slopes_and_strided_q(lib):
+    """Caller-given ALiBi slopes, and q / out as views of [B, L, H, D] memory."""
+    w = tiny("bf16", 128, "causal", "alibi", B=2, Hq=4, Hkv=2, Q_LEN=256, KV_LEN=256)
+    inp = W.generate(w)
+    slopes = np.array([0.3, 0.05, 0.0, 1.5], dtype=np.float32)
+    qd = G.to_device(inp.q.transpose(0, 2, 1, 3), "bf16").transpose(1, 2)  # strided view
+    assert not qd.is_contiguous()
+    k = G.to_device(inp.k, "bf16")
+    v = G.to_device(inp.v, "bf16")
+    bm = lib.create_block_mask("causal", 1, 1, 256, 256)
+    out = torch.empty((2, 256, 4, 128), dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    o, lse = lib.flex_attention(qd, k, v, bm, score="alibi",
+                                alibi_slopes=torch.from_numpy(slopes), out=out)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, oracle.causal_mask,
+                                      oracle.alibi_score(slopes.astype(np.float64)), w.scale)
+    res = G.compare(w, o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    assert res["ok"], G.summary(res)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fwd_invariants(lib, dtype):
+    """V = 1 gives O = 1 (rows sum to 1); causal row 0 returns V[0]; window 1
+    without sinks returns V row by row."""
+    B, H, L, D = 1, 2, 256, 64
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((B, H, L, D)).astype(np.float32)
+    k = rng.standard_normal((B, H, L, D)).astype(np.float32)
+    v = rng.standard_normal((B, H, L, D)).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = W.round_to_bf16(q), W.round_to_bf16(k), W.round_to_bf16(v)
+    qd, kd, vd = (G.to_device(x, dtype) for x in (q, k, v))
+    ones = torch.ones_like(vd)
+    bm = lib.create_block_mask("causal", 1, 1, L, L)
+    o1, _ = lib.flex_attention(qd, kd, ones, bm)
+    o, lse = lib.flex_attention(qd, kd, vd, bm)
+    bm1 = lib.create_block_mask("sliding_sink", 1, 1, L, L, window=1, num_sinks=0)
+    ow, lsew = lib.flex_attention(qd, kd, vd, bm1)
+    torch.cuda.synchronize()
+    # V = 1: the P.V product uses bf16-rounded probabilities, the sum uses fp32
+    tol_ones = 1e-6 if dtype == "f32" else 1e-2
+    assert torch.allclose(o1.float(), torch.ones_like(o1.float()), atol=tol_ones, rtol=0)
+    # a single allowed key has probability exactly 1: O is that V row exactly
+    assert torch.equal(o[:, :, 0].float(), vd[:, :, 0].float())
+    assert torch.equal(ow.float(), vd.float())
+    diag = (q.astype(np.float64) * k.astype(np.float64)).sum(-1) / math.sqrt(D)
+    np.testing.assert_allclose(lsew.cpu().numpy(), diag, atol=1e-5)
+
+
+def test_fwd_deterministic(lib):
+    w = W.DENSE_CAUSAL_GQA.with_(B=1, Q_LEN=1024, KV_LEN=1024)
+    inp = W.generate(w)
+    bm = G.build_gpu_mask(lib, w, inp)
+    q, k, v = (G.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    o1, l1 = lib.flex_attention(q, k, v, bm)
+    o2, l2 = lib.flex_attention(q, k, v, bm)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_tiny_causal_workload_full(lib):
+    """The tiny fp32 causal workload, every output element."""
+    res = check_full(lib, W.TINY_CAUSAL)
+    assert res["o_max_abs"] <= 1e-5 and res["lse_max_abs"] <= 1e-5
+
+
+def _sample_rows(L, rng, n=96):
+    fixed = [0, 1, 2, 127, 128, 129, 255, 256, L // 2, L - 129, L - 128, L - 2, L - 1]
+    rnd = rng.choice(L, size=n, replace=False)
+    return np.unique(np.concatenate([fixed, rnd]))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("w", W.WORKLOADS[1:], ids=[w.name for w in W.WORKLOADS[1:]])
+def test_full_workload_sampled(lib, w):
+    """Full-size workloads in the bench's launch configuration: every row of
+    the first and last (b, h), and sampled rows of four more (b, h) pairs."""
+    inp = W.generate(w)
+    o, lse, _ = G.run_gpu(lib, w, inp)
+    rng = np.random.default_rng(2024)
+    results = []
+    pairs = [(0, 0), (w.B - 1, w.Hq - 1)]
+    for b, h in pairs:
+        o_ref, lse_ref = G.oracle_rows(w, inp, batches=[b], heads=[h])
+        results.append(G.compare(w, o, lse, o_ref, lse_ref))
+    extra = {(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(4)}
+    for b, h in sorted(extra):
+        rows = _sample_rows(w.Q_LEN, rng)
+        o_ref, lse_ref = G.oracle_rows(w, inp, batches=[b], heads=[h], rows=rows)
+        results.append(G.compare(w, o, lse, o_ref, lse_ref))
+    for r in results:
+        assert r["ok"], (w.name, G.summary(r))

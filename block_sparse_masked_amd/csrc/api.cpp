@@ -258,6 +258,9 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
   if (score_kind == FLEXATTN_SCORE_ALIBI || score_kind == FLEXATTN_SCORE_SOFTCAP_ALIBI)
     slopes = params ? params->alibi_slopes : nullptr;
 
+  if (q->dtype == FLEXATTN_BF16 && fa::fwd_bf16_lds_bytes(q->D, bm->num_kv_blocks) > fa::kMaxLdsBytes)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: KV_LEN %d needs more LDS than a workgroup has", who,
+                k->L);
   fa::FwdLaunch L;
   L.q = q->data;
   L.k = k->data;
@@ -278,6 +281,7 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
   L.D = q->D;
   L.mask_kind = (int)bm->mask_kind;
   L.mp = mp;
+  L.doc_len = doc_len;
   L.score_kind = (int)score_kind;
   L.softcap = softcap;
   L.slopes = slopes;

@@ -35,6 +35,7 @@ struct FwdLaunch {
   int B, Hq, Hkv, Q_LEN, KV_LEN, D;
   int mask_kind;
   MaskParams mp;
+  int doc_len;
   int score_kind;
   float softcap;
   const float* slopes;  // device [Hq] or nullptr
@@ -43,6 +44,8 @@ struct FwdLaunch {
 };
 
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream);
+int fwd_bf16_lds_bytes(int D, int NKB);  // dynamic LDS of the bf16 forward
+constexpr int kMaxLdsBytes = 160 * 1024;
 hipError_t launch_fwd_f32(const FwdLaunch& L, hipStream_t stream);
 
 }  // namespace fa

@@ -162,3 +162,13 @@ def test_python_wrapper_maps_errors():
         lib._tensor(q, "q")
     with pytest.raises(NotImplementedError):
         lib._tensor(q.half(), "q")
+
+
+def test_library_has_no_undefined_internal_symbols():
+    """Every kernel the dispatcher launches has its host stub in the library
+    (a missing stub only shows up when the library is loaded)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", lib.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    bad = [line for line in out.splitlines() if "_ZN2fa" in line]
+    assert not bad, bad[:5]

@@ -33,6 +33,8 @@
 // lazily: O and the row sum are rescaled only when a row's max grows by more
 // than 2^8 (exp2 units), which leaves the result unchanged (any reference
 // point gives the same normalised sums) while skipping most rescales.
+#include <type_traits>
+
 #include "common.hpp"
 #include "fwd_common.hpp"
 #include "launch.hpp"
@@ -77,18 +79,67 @@ __device__ __forceinline__ int swz(int row, int col) {
   }
 }
 
-// V tile swizzle: a transposed read takes 4 consecutive rows x 32 bytes per
-// 16-lane group; XOR-ing the chunk with 2*(row%4) puts those 8 half-chunks in
-// distinct banks.
-__device__ __forceinline__ int swz_v(int row, int col) { return col ^ ((row & 3) << 1); }
+// V tile swizzle for the transposed reads: two 16-lane groups read the same
+// 4 consecutive rows at chunk pairs c, c+1 and c+2, c+3 (c = 4 * d-block).
+// XOR-ing with 4*(row%4) (D = 128: 16 chunks per 256-byte row) or with
+// 4*((row/2)%2) (D = 64: 8 chunks per 128-byte row, two rows per bank sweep)
+// gives those 16 half-chunk pairs distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_v(int row, int col) {
+  if constexpr (D == 128) {
+    return col ^ ((row & 3) << 2);
+  } else {
+    return col ^ (((row >> 1) & 1) << 2);
+  }
+}
 
-// Direct global->LDS loads of one [128][D] bf16 tile through a buffer
-// resource. Each wave-wide load fills one contiguous KiB of LDS (lane l
-// writes bytes [16 l, 16 l + 16)), so each lane fetches the global chunk
-// whose swizzled home is that slot; its byte offset inside the tile is fixed
-// and computed once. Per tile only the resource base moves, and its size ends
-// at the last key row, so rows past kv_len read as zero (their scores are
-// masked: a tile crossing kv_len always takes the masked path).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for raw loads: base, no stride, `bytes` in range (loads past
+// it read as zero).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
+  const unsigned long long p = reinterpret_cast<unsigned long long>(base);
+  i32x4 r;
+  r[0] = (int)(unsigned)p;
+  r[1] = (int)(unsigned)(p >> 32) & 0xffff;
+  r[2] = bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(unsigned long long)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Direct global->LDS loads (16 and 4 bytes per lane). Written as one asm
+// block with its M0 setup and no register results: the LDS they fill is a
+// buffer no instruction reads until after the explicit vmcnt(0) + barrier
+// that ends the tile, so the compiler need not (and does not) wait for them.
+__device__ __forceinline__ i32x4 uniform4(i32x4 v) {
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(v[0]);
+  r[1] = __builtin_amdgcn_readfirstlane(v[1]);
+  r[2] = __builtin_amdgcn_readfirstlane(v[2]);
+  r[3] = __builtin_amdgcn_readfirstlane(v[3]);
+  return r;
+}
+
+__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               : : "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
+__device__ __forceinline__ void dma4(i32x4 rsrc, unsigned lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               : : "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// Direct global->LDS loads of one [128][D] bf16 tile. Each wave-wide load
+// fills one contiguous KiB of LDS (lane l writes bytes [16 l, 16 l + 16)),
+// so each lane fetches the global chunk whose swizzled home is that slot; its
+// byte offset inside the tile is fixed and computed once. Per tile only the
+// resource base moves, and its range ends at the last key row, so rows past
+// kv_len read as zero (their scores are masked: a tile crossing kv_len always
+// takes the masked path).
 template <int D, bool IS_V>
 struct TileLoader {
   static constexpr int CPR = D / 8;
@@ -103,7 +154,7 @@ struct TileLoader {
 #pragma unroll
     for (int i = 0; i < KB_PER_WAVE; ++i) {
       const int row = (wave * KB_PER_WAVE + i) * ROWS_PER_KB + r_in;
-      const int col = IS_V ? swz_v(row, pch) : swz<D>(row, pch);
+      const int col = IS_V ? swz_v<D>(row, pch) : swz<D>(row, pch);
       voff[i] = (int)(row * stride * 2) + col * 16;
     }
     lds_off = wave * KB_PER_WAVE * 512;
@@ -111,19 +162,12 @@ struct TileLoader {
 
   __device__ __forceinline__ void issue(u16* lds, const u16* g, long long stride, int kv0,
                                         int kv_len) const {
-    // (device pass only: the host pass of this compiler drops the kernel
-    // stubs of functions that name the buffer-resource type)
-#if defined(__HIP_DEVICE_COMPILE__)
     const long long bytes = (long long)(kv_len - kv0) * stride * 2;
-    const int nrec = bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes;
-    __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(g + (long long)kv0 * stride), (short)0, nrec,
-                                          0x00020000);
+    const i32x4 rsrc = uniform4(make_rsrc(g + (long long)kv0 * stride,
+                                          bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes));
+    const unsigned base = __builtin_amdgcn_readfirstlane(lds_addr(lds + lds_off));
 #pragma unroll
-    for (int i = 0; i < KB_PER_WAVE; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(lds + lds_off + i * 512), 16, voff[i],
-                                               0, 0, 0);
-#endif
+    for (int i = 0; i < KB_PER_WAVE; ++i) dma16(rsrc, base + 1024 * i, voff[i]);
   }
 };
 
@@ -155,11 +199,12 @@ struct Lane {
   __device__ void init_offsets() {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) kofs[ks] = l32 * D + swz<D>(l32, 2 * ks + hh) * 8;
-    const int row = 4 * hh + (vi >> 2);  // + 16*ks + 8*half: multiples of 4 leave row % 4 alone
+    // + 16*ks + 8*half: multiples of 4 leave row % 4 and (row / 2) % 2 alone
+    const int row = 4 * hh + (vi >> 2);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int d = 32 * db + 16 * vg + 4 * (vi & 3);
-      vofs[db] = row * D + swz_v(row, d >> 3) * 8 + (d & 7);
+      vofs[db] = row * D + swz_v<D>(row, d >> 3) * 8 + (d & 7);
     }
   }
 };
@@ -201,125 +246,134 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
-// O^T += V^T . P^T for one tile (32 MFMAs). The V^T fragment (lane row
-// d = 32*db + lane%32, slot t <-> key 16*ks + 8*(t/4) + 4*hh + t%4, the key
-// order of pf) comes from the row-major V tile with two transposing reads: in
-// each 16-lane group lane j supplies the 8-byte piece (row j/4, columns
+// V^T operand fragment for P.V MFMA (k-step ks, d-block db): lane row
+// d = 32*db + lane%32, slot t <-> key 16*ks + 8*(t/4) + 4*hh + t%4 (the key
+// order of pf), read from the row-major V tile with two transposing reads:
+// in each 16-lane group lane j supplies the 8-byte piece (row j/4, columns
 // 4*(j%4)..+3) of a 4-key x 16-d block and receives column j of that block.
+template <int D>
+__device__ __forceinline__ bf16x8 v_frag(const u16* sV, const Lane<D>& ln, int ks, int db) {
+  bf16x4 part[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const u16* src = sV + ln.vofs[db] + (16 * ks + 8 * ht) * D;
+    part[ht] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4*)(src));
+  }
+  return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// K operand fragment for S MFMA (k-step ks, key block blk): rows
+// 32*blk + lane%32 keep row % 16 (and (row/2) % 8), so one offset per k-step.
+template <int D>
+__device__ __forceinline__ bf16x8 k_frag(const u16* sK, const Lane<D>& ln, int ks, int blk) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(sK + ln.kofs[ks] + 32 * blk * D));
+}
+
+// O^T += V^T . P^T for one tile, no other work (the last tile).
 template <int D>
 __device__ __forceinline__ void pv(f32x16 (&o)[D / 32], const bf16x8 (&pf)[8], const u16* sV,
                                    const Lane<D>& ln) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
+  for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      bf16x4 part[2];
-#pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        const u16* src = sV + ln.vofs[db] + (16 * ks + 8 * ht) * D;
-        part[ht] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4*)(src));
-      }
-      const bf16x8 vf = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
-    }
-  }
-  // keep O in the accumulation registers (one workgroup per CU: 512
-  // registers per lane, the score and probability registers stay in VGPRs)
-#if defined(__HIP_DEVICE_COMPILE__)
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) asm volatile("" : "+a"(o[db]));
-#endif
+    for (int db = 0; db < D / 32; ++db)
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D>(sV, ln, ks, db), pf[ks], o[db],
+                                                      0, 0, 0);
 }
 
-// Score modification of tile kv0 in place (base-2 logits) and the lane's max.
-// Without a score_mod the raw scores stay in place: scale > 0, so the max of
-// the raw scores times scale*log2(e) is the logit max, and the scale is
-// folded into the exponent's FMA.
-template <int D, int SCORE>
-__device__ __forceinline__ float logits(f32x16 (&s)[4], int kv0, const FwdArgs& a,
-                                        const Lane<D>& ln) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if constexpr (SCORE != SCORE_NONE) {
-        const int key = kv0 + 32 * blk + 8 * (r >> 2) + 4 * ln.hh + (r & 3);
-        s[blk][r] = ScoreMod<SCORE>::apply(s[blk][r], a.c_scale, a.c_cap, a.cap2, ln.slope2,
-                                           (float)(key - ln.q));
-      }
-      mx = fmaxf(mx, s[blk][r]);
-    }
-  }
-  return mx;
+// Key offset (within the tile, without 4*hh) of result register r of block blk.
+__device__ __forceinline__ constexpr int key_off(int blk, int r) {
+  return 32 * blk + 8 * (r >> 2) + (r & 3);
 }
 
-// mask_mod on a partial tile (and the key bound), in place; returns the new
-// max. For the document mask the tile's 128 key document ids are in LDS.
+// Per-tile mask limits: key offset c (see key_off) is allowed when c <= hi,
+// and for the sliding window also c > win_lo or c < sink_hi; for documents
+// the key's id (LDS) must equal the query row's.
+struct MaskLimits {
+  int hi, win_lo, sink_hi;
+};
+
 template <int D, int MASK>
-__device__ __forceinline__ float apply_mask(f32x16 (&s)[4], int kv0, const int* tile_doc,
-                                            const FwdArgs& a, const Lane<D>& ln) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      int4 dk = make_int4(0, 0, 0, 0);
-      if constexpr (MASK == MASK_DOCUMENT)
-        dk = *reinterpret_cast<const int4*>(tile_doc + 32 * blk + 8 * g + 4 * ln.hh);
-      const int dks[4] = {dk.x, dk.y, dk.z, dk.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * g + j;
-        const int key = kv0 + 32 * blk + 8 * g + 4 * ln.hh + j;
-        bool ok = key < a.KV_LEN;
-        if constexpr (MASK == MASK_DOCUMENT) {
-          ok = ok && key <= ln.qc && dks[j] == ln.dq;
-        } else {
-          ok = ok && Mask<MASK>::allowed(a.mp, nullptr, ln.qc, key);
-        }
-        s[blk][r] = ok ? s[blk][r] : -INFINITY;
-        mx = fmaxf(mx, s[blk][r]);
-      }
-    }
-  }
-  return mx;
+__device__ __forceinline__ MaskLimits mask_limits(int kv0, const FwdArgs& a, const Lane<D>& ln) {
+  const int base = kv0 + 4 * ln.hh;
+  MaskLimits m;
+  m.hi = a.KV_LEN - 1 - base;
+  if constexpr (MASK != MASK_NOOP) m.hi = min(m.hi, ln.qc - base);
+  m.win_lo = ln.qc - base - a.mp.window;
+  m.sink_hi = a.mp.sinks - base;
+  return m;
 }
 
-// One tile of the pipeline:
-//   phase 1: O += V[j-1] . P[j-1] interleaved with the logits and row max
-//            of S[j] (for j = 0, P is zero and the V buffer is zero-filled);
-//   lazy rescale of O and l when a row max moved up by more than 2^8;
-//   phase 2: S[j+1] = K[j+1] . Q^T interleaved with exp, row sum and the
-//            bf16 conversion of S[j] into P[j].
-template <int D, int MASK, int SCORE>
-__device__ __forceinline__ void step(f32x16 (&s)[4], f32x16 (&s_next)[4], f32x16 (&o)[D / 32],
+// Phase-1 element work: y = score_mod(x), masked on partial tiles; returns y.
+template <int D, int MASK, int SCORE, bool MASKED>
+__device__ __forceinline__ float elem_logit(float x, int blk, int r, int kv0, const MaskLimits& ml,
+                                            const int* tile_doc, const FwdArgs& a,
+                                            const Lane<D>& ln) {
+  float y = x;
+  if constexpr (SCORE != SCORE_NONE) {
+    const int key = kv0 + key_off(blk, r) + 4 * ln.hh;
+    y = ScoreMod<SCORE>::apply(x, a.c_scale, a.c_cap, a.cap2, ln.slope2, (float)(key - ln.q));
+  }
+  if constexpr (MASKED) {
+    const int c = key_off(blk, r);
+    bool ok = c <= ml.hi;
+    if constexpr (MASK == MASK_SLIDING_SINK) ok = ok && (c > ml.win_lo || c < ml.sink_hi);
+    if constexpr (MASK == MASK_DOCUMENT) ok = ok && tile_doc[c + 4 * ln.hh] == ln.dq;
+    y = ok ? y : -INFINITY;
+  }
+  return y;
+}
+
+// Fragment prefetch distance (in MFMAs) and ring size.
+constexpr int kDist = 4;
+constexpr int kRing = kDist + 1;
+
+// One tile of the pipeline, in program order (each group fenced):
+//   phase 1: O += V[j-1] . P[j-1]; per MFMA a share of Y = logits(X) and the
+//            row max (X holds S[j], written by the previous phase 2);
+//   lazy rescale of O and l when a row max rose by more than 2^8;
+//   phase 2: X = S[j+1] = K[j+1] . Q^T; per MFMA a share of P = exp2(Y - m)
+//            (row sum, bf16 pack).
+template <int D, int MASK, int SCORE, bool MASKED>
+__device__ __forceinline__ void step(f32x16 (&X)[4], f32x16 (&Y)[4], f32x16 (&o)[D / 32],
                                      bf16x8 (&pf)[8], float& m_ref, float& l,
                                      const bf16x8 (&qf)[D / 16], const u16* sK_next,
-                                     const u16* sV_prev, int kv0, bool masked,
-                                     const int* tile_doc, const FwdArgs& a, const Lane<D>& ln) {
+                                     const u16* sV_prev, int kv0, const int* tile_doc,
+                                     const FwdArgs& a, const Lane<D>& ln) {
   constexpr int DB = D / 32;
-  constexpr int NMFMA_PV = 8 * DB;
-  constexpr int NMFMA_S = 4 * (D / 16);
-  // phase 1: P.V of the previous tile || logits and max of this tile
-  pv<D>(o, pf, sV_prev, ln);
-  float mx = logits<D, SCORE>(s, kv0, a, ln);
-  // transposed V reads run two MFMAs ahead of their products
-  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
+  constexpr int KS = D / 16;
+  constexpr int NPV = 8 * DB;       // P.V MFMAs per tile
+  constexpr int NS = 4 * KS;        // S MFMAs per tile
+  constexpr int E1 = 64 / NPV;      // elements per phase-1 group
+  constexpr int E2 = 64 / NS;       // elements per phase-2 group
+  const MaskLimits ml = mask_limits<D, MASK>(kv0, a, ln);
+
+  // ---- phase 1
+  bf16x8 vr[kRing];
 #pragma unroll
-  for (int i = 0; i < NMFMA_PV; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    if (i + 2 < NMFMA_PV) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgValu, SCORE == SCORE_NONE ? 2 : 6, 0);
+  for (int i = 0; i < kDist; ++i) vr[i] = v_frag<D>(sV_prev, ln, i / DB, i % DB);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    if (i + kDist < NPV)
+      vr[(i + kDist) % kRing] = v_frag<D>(sV_prev, ln, (i + kDist) / DB, (i + kDist) % DB);
+    o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % kRing], pf[i / DB], o[i % DB], 0,
+                                                        0, 0);
+#pragma unroll
+    for (int e = i * E1; e < (i + 1) * E1; ++e) {
+      const int blk = e >> 4, r = e & 15;
+      Y[blk][r] = elem_logit<D, MASK, SCORE, MASKED>(X[blk][r], blk, r, kv0, ml, tile_doc, a, ln);
+      mx = fmaxf(mx, Y[blk][r]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  if (masked) mx = apply_mask<D, MASK>(s, kv0, tile_doc, a, ln);
   mx = pair_max(mx);
   if constexpr (SCORE == SCORE_NONE) mx *= a.c_scale;
 
-  // lazy rescale when some row's max exceeds its reference by 2^8
+  // ---- lazy rescale (a real branch: rare)
   if (__any(mx > m_ref + kRescaleSlack)) {
+    asm volatile("");
     const float m_new = fmaxf(m_ref, mx);
     const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_ref - m_new);
     l *= alpha;
@@ -332,34 +386,33 @@ __device__ __forceinline__ void step(f32x16 (&s)[4], f32x16 (&s_next)[4], f32x16
   const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
   __builtin_amdgcn_sched_barrier(0);
 
-  // phase 2: S of the next tile || exponentials, row sum, bf16 P
-  compute_s<D>(s_next, sK_next, qf, ln);
+  // ---- phase 2
+  bf16x8 kr[kRing];
+#pragma unroll
+  for (int i = 0; i < kDist; ++i) kr[i] = k_frag<D>(sK_next, ln, i / 4, i % 4);
   float rs = 0.0f;
+  const f32x16 zero = {};
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
+  for (int i = 0; i < NS; ++i) {
+    if (i + kDist < NS) kr[(i + kDist) % kRing] = k_frag<D>(sK_next, ln, (i + kDist) / 4, (i + kDist) % 4);
+    const int blk = i % 4;
+    X[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % kRing], qf[i / 4],
+                                                     i < 4 ? zero : X[blk], 0, 0, 0);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float x = s[ks >> 1][8 * (ks & 1) + t];
+    for (int e = i * E2; e < (i + 1) * E2; ++e) {
+      const float y = Y[e >> 4][e & 15];
       float p;
       if constexpr (SCORE == SCORE_NONE) {
-        p = fast_exp2(fmaf(x, a.c_scale, -m_use));
+        p = fast_exp2(fmaf(y, a.c_scale, -m_use));
       } else {
-        p = fast_exp2(x - m_use);
+        p = fast_exp2(y - m_use);
       }
       rs += p;
-      pf[ks][t] = (__bf16)p;
+      pf[e >> 3][e & 7] = (__bf16)p;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
   l += rs;
-  // K fragment reads run two MFMAs ahead of their products
-  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 1);
-#pragma unroll
-  for (int i = 0; i < NMFMA_S; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 1);
-    if (i + 2 < NMFMA_S) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(kSgValu, 224 / NMFMA_S, 1);
-  }
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D, int MASK, int SCORE>
@@ -389,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const Item it = decode_item(x, a.bm, a.B, a.Hq);
   const int b = it.b, h = it.h;
   const int hk = h / a.G;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Lane<D> ln;
   ln.lane = threadIdx.x & 63;
   ln.l32 = ln.lane & 31;
@@ -424,17 +477,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // document ids of a tile's keys -> docbuf[i] (rows past KV_LEN read as 0)
   auto issue_doc = [&](int* dst, int kv0) {
     if constexpr (MASK == MASK_DOCUMENT) {
-#if defined(__HIP_DEVICE_COMPILE__)
       if (wave == 0) {
         const int nrec = 4 * (min(a.KV_LEN, a.doc_len) - kv0);
-        __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(doc_row + kv0), (short)0, nrec > 0 ? nrec : 0, 0x00020000);
+        const i32x4 rsrc = uniform4(make_rsrc(doc_row + kv0, nrec > 0 ? nrec : 0));
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(dst + 64 * c), 4,
-                                                   4 * ln.lane + 256 * c, 0, 0, 0);
+          dma4(rsrc, __builtin_amdgcn_readfirstlane(lds_addr(dst + 64 * c)), 4 * ln.lane + 256 * c);
       }
-#endif
     }
   };
 
@@ -476,25 +525,28 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     // buffer j%2 (it held V[j-2]) and K[j+2] into K buffer j%2 (it held K[j]).
     // The next tile's S is always computed; on the last tile it reads a stale
     // buffer and is discarded (hidden under that tile's softmax).
-    // even tiles: load into the *0 buffers, read K1 / V1; odd tiles: the
-    // other way round (two tiles per trip so every buffer is fixed)
-    auto stage = [&](int j, f32x16(&cur)[4], f32x16(&nxt)[4], u16* kw, u16* vw, const u16* kr,
-                     const u16* vr, int* dw, const int* dr) {
+    // tile j reads K[(j+1) % 2], V[(j+1) % 2] (holding K[j+1], V[j-1]) and
+    // fills K[j % 2], V[j % 2] with K[j+2], V[j]. Full tiles (no mask code)
+    // then partial tiles; a full tile crossing KV_LEN, which the builder
+    // never lists, is masked on the partial path's key bound.
+    auto stage = [&](int j, auto masked_tag) {
+      constexpr bool M = decltype(masked_tag)::value;
       const int kv_next = tile_kv0(j + 1 < n ? j + 1 : j);
       const int kv_after = tile_kv0(j + 2 < n ? j + 2 : j);
-      vload.issue(vw, vbase, a.sv2, kv0, a.KV_LEN);
-      if (j + 2 < n) kload.issue(kw, kbase, a.sk2, kv_after, a.KV_LEN);
-      if (j + 1 < n) issue_doc(dw, kv_next);
-      const bool masked = (j >= nfull) || (kv0 + kBlock > a.KV_LEN);
-      step<D, MASK, SCORE>(cur, nxt, o, pf, m_ref, l, qf, kr, vr, kv0, masked, dr, a, ln);
+      const bool odd = j & 1;
+      vload.issue(odd ? sV1 : sV0, vbase, a.sv2, kv0, a.KV_LEN);
+      if (j + 2 < n) kload.issue(odd ? sK1 : sK0, kbase, a.sk2, kv_after, a.KV_LEN);
+      if (j + 1 < n) issue_doc(odd ? docbuf : docbuf + 128, kv_next);
+      step<D, MASK, SCORE, M>(s, s2, o, pf, m_ref, l, qf, odd ? sK0 : sK1, odd ? sV0 : sV1, kv0,
+                              odd ? docbuf + 128 : docbuf, a, ln);
       kv0 = kv_next;
       wait_loads_and_sync();
     };
-    for (int j = 0; j < n; j += 2) {
-      stage(j, s, s2, sK0, sV0, sK1, sV1, docbuf + 128, docbuf);
-      if (j + 1 >= n) break;
-      stage(j + 1, s2, s, sK1, sV1, sK0, sV0, docbuf, docbuf + 128);
-    }
+    // full tiles that end inside KV_LEN take the unmasked path
+    const int nfull_fast = (nfull > 0 && tile_kv0(nfull - 1) + kBlock > a.KV_LEN) ? nfull - 1 : nfull;
+    int j = 0;
+    for (; j < nfull_fast; ++j) stage(j, std::false_type{});
+    for (; j < n; ++j) stage(j, std::true_type{});
     const u16* vlast = ((n - 1) & 1) ? sV1 : sV0;
     // the last tile's P . V
     pv<D>(o, pf, vlast, ln);

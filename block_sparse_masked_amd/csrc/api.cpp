@@ -261,6 +261,11 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
   if (q->dtype == FLEXATTN_BF16 && fa::fwd_bf16_lds_bytes(q->D, bm->num_kv_blocks) > fa::kMaxLdsBytes)
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: KV_LEN %d needs more LDS than a workgroup has", who,
                 k->L);
+  // the bf16 kernel addresses a block of up to 128 key rows with 32-bit offsets
+  if (q->dtype == FLEXATTN_BF16 &&
+      (k->stride[2] > fa::kMaxBf16RowStride || v->stride[2] > fa::kMaxBf16RowStride))
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: k/v row stride above %lld elements", who,
+                (long long)fa::kMaxBf16RowStride);
   fa::FwdLaunch L;
   L.q = q->data;
   L.k = k->data;

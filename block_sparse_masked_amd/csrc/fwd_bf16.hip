@@ -9,12 +9,13 @@
 // h / (Hq / Hkv) (page "FlagAttention", section "Operator overview").
 //
 // Work decomposition: one workgroup of 4 waves per (b, h, 128-row query
-// tile); wave w owns query rows [32w, 32w + 32). Both products use
-// v_mfma_f32_32x32x16_bf16:
-//   S^T = K . Q^T    (A = K tile from LDS, B = Q^T held in registers)
+// tile); wave w owns query rows [32w, 32w + 32). Two workgroups share a CU,
+// so each SIMD runs two waves and one wave's softmax (vector ALUs) overlaps
+// the other's matrix products. Both products use v_mfma_f32_32x32x16_bf16:
+//   S^T = K . Q^T    (A = K rows from LDS, B = Q^T held in registers)
 //   O^T += V^T . P^T (A = V^T read transposed from LDS, B = P^T in registers)
 // The MFMA result's lane index is the query column, so each lane holds the
-// scores of one query row (half of the tile's keys); the row max needs one
+// scores of one query row (half of a step's keys); the row max needs one
 // exchange with lane ^ 32, the P^T operand is the converted score registers
 // and the O^T accumulator is rescaled per lane.
 //
@@ -23,12 +24,10 @@
 // lane l holds k = 8*(l/32) + t for both A and B, so the key order inside the
 // P.V contraction follows the S result layout directly.
 //
-// Pipeline per KV tile j (K and V double-buffered in LDS, filled with direct
-// global->LDS loads):
-//   issue loads of V[j+1] and K[j+2]
-//   S[j+1] = K[j+1] . Q^T on the matrix cores, overlapped with the softmax of
-//   S[j] on the vector ALUs; then O += V[j] . P[j]
-//   wait for the loads, barrier
+// KV is walked in steps of NK = 8192 / D keys (64 for D = 128, 128 for D = 64;
+// a step's K or V block is 16 KiB), each BlockMask tile in 128 / NK steps.
+// K and V of step g + 1 are loaded straight from global memory into LDS
+// (double-buffered) while step g computes; one barrier per step.
 // Full tiles take a path with no mask code. The running max is applied
 // lazily: O and the row sum are rescaled only when a row's max grows by more
 // than 2^8 (exp2 units), which leaves the result unchanged (any reference
@@ -46,11 +45,28 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 constexpr int kThreads = 256;
+constexpr int kWgPerCu = 2;
 constexpr float kRescaleSlack = 8.0f;  // exp2 units: p <= 256 between rescales
+constexpr int kStepBytes = 16384;      // one K (or V) step block in LDS
+
+// internal score kind: plain scaled score with the scale applied before the
+// row max (needed when scale < 0; SCORE_NONE folds the scale into exp2)
+constexpr int SCORE_SCALED = 4;
+
+template <int D>
+struct Geom {
+  static constexpr int NK = kStepBytes / (2 * D);  // keys per step
+  static constexpr int SPT = kBlock / NK;          // steps per BlockMask tile
+  static constexpr int NB = NK / 32;               // 32-key blocks per step
+  static constexpr int NE = NB * 16;               // scores per lane per step
+  static constexpr int PKS = NK / 16;              // P.V k-steps per step
+  static constexpr int KS = D / 16;                // S k-steps
+  static constexpr int DB = D / 32;                // O d-blocks
+};
 
 struct FwdArgs {
   const u16* q;
@@ -58,7 +74,8 @@ struct FwdArgs {
   const u16* v;
   u16* o;
   float* lse;
-  long long sq0, sq1, sq2, sk0, sk1, sk2, sv0, sv1, sv2, so0, so1, so2;
+  long long sq0, sq1, sq2, sk0, sk1, sv0, sv1, so0, so1, so2;
+  int sk2, sv2;  // key-row strides (elements, < 2^22)
   int B, Hq, Hkv, G, Q_LEN, KV_LEN;
   int xcd_round;  // > 0: items per schedule round, remapped so KV groups share an XCD
   int doc_len;
@@ -68,8 +85,8 @@ struct FwdArgs {
   BlockMaskView bm;
 };
 
-// 16-byte chunk swizzle of a K tile [128][D] in LDS: the 16 rows a
-// 16-lane phase of a fragment read touches land in distinct banks.
+// 16-byte chunk swizzle of a K block [NK][D] in LDS: the 16 rows a 16-lane
+// phase of a fragment read touches land in distinct banks.
 template <int D>
 __device__ __forceinline__ int swz(int row, int col) {
   if constexpr (D == 128) {
@@ -79,7 +96,7 @@ __device__ __forceinline__ int swz(int row, int col) {
   }
 }
 
-// V tile swizzle for the transposed reads: two 16-lane groups read the same
+// V block swizzle for the transposed reads: two 16-lane groups read the same
 // 4 consecutive rows at chunk pairs c, c+1 and c+2, c+3 (c = 4 * d-block).
 // XOR-ing with 4*(row%4) (D = 128: 16 chunks per 256-byte row) or with
 // 4*((row/2)%2) (D = 64: 8 chunks per 128-byte row, two rows per bank sweep)
@@ -93,37 +110,25 @@ __device__ __forceinline__ int swz_v(int row, int col) {
   }
 }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource for raw loads: base, no stride, `bytes` in range (loads past
-// it read as zero).
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
-  const unsigned long long p = reinterpret_cast<unsigned long long>(base);
-  i32x4 r;
-  r[0] = (int)(unsigned)p;
-  r[1] = (int)(unsigned)(p >> 32) & 0xffff;
-  r[2] = bytes;
-  r[3] = 0x00020000;
-  return r;
-}
-
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(unsigned long long)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Buffer resource for raw loads: 64-bit base, no stride, `bytes` in range
+// (loads past it read as zero). Built from wave-uniform values.
+__device__ __forceinline__ i32x4 make_rsrc(unsigned long long base, unsigned bytes) {
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)base);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(base >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
 }
 
 // Direct global->LDS loads (16 and 4 bytes per lane). Written as one asm
 // block with its M0 setup and no register results: the LDS they fill is a
 // buffer no instruction reads until after the explicit vmcnt(0) + barrier
-// that ends the tile, so the compiler need not (and does not) wait for them.
-__device__ __forceinline__ i32x4 uniform4(i32x4 v) {
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane(v[0]);
-  r[1] = __builtin_amdgcn_readfirstlane(v[1]);
-  r[2] = __builtin_amdgcn_readfirstlane(v[2]);
-  r[3] = __builtin_amdgcn_readfirstlane(v[3]);
-  return r;
-}
-
+// that ends the step, so the compiler need not (and does not) wait for them.
 __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                : : "s"(lds), "v"(voff), "s"(rsrc) : "memory");
@@ -133,41 +138,45 @@ __device__ __forceinline__ void dma4(i32x4 rsrc, unsigned lds, int voff) {
                : : "s"(lds), "v"(voff), "s"(rsrc) : "memory");
 }
 
-// Direct global->LDS loads of one [128][D] bf16 tile. Each wave-wide load
-// fills one contiguous KiB of LDS (lane l writes bytes [16 l, 16 l + 16)),
-// so each lane fetches the global chunk whose swizzled home is that slot; its
-// byte offset inside the tile is fixed and computed once. Per tile only the
-// resource base moves, and its range ends at the last key row, so rows past
-// kv_len read as zero (their scores are masked: a tile crossing kv_len always
-// takes the masked path).
+// Loads of one [NK][D] step block of K or V. Each wave-wide load fills one
+// contiguous KiB of LDS (lane l writes bytes [16 l, 16 l + 16)), so each lane
+// fetches the global chunk whose swizzled home is that slot; its byte offset
+// from the block's first row is fixed and computed once. Per step only the
+// resource moves; its range ends at KV_LEN, so rows past it read as zero
+// (their scores are masked: a tile crossing KV_LEN takes the masked path).
 template <int D, bool IS_V>
-struct TileLoader {
-  static constexpr int CPR = D / 8;
+struct BlockLoader {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int ROWS_PER_KB = 1024 / (2 * D);
-  static constexpr int KB_PER_WAVE = (kBlock / ROWS_PER_KB) / 4;
+  static constexpr int KB_PER_WAVE = kStepBytes / 1024 / 4;
+  static constexpr int NK = Geom<D>::NK;
   int voff[KB_PER_WAVE];
-  int lds_off;  // element offset of this wave's first KiB inside a tile
+  unsigned long long base;  // byte address of key row 0 of this (b, kv head)
+  unsigned row_bytes;
+  unsigned lds0;            // LDS byte address of this wave's first KiB, buffer 0
 
-  __device__ void init(int wave, int lane, long long stride) {
+  __device__ void init(const u16* g, int stride, int wave, int lane, const u16* lds_buf0) {
+    base = reinterpret_cast<unsigned long long>(g);
+    row_bytes = 2u * (unsigned)stride;
     const int r_in = lane / CPR;
     const int pch = lane % CPR;
 #pragma unroll
     for (int i = 0; i < KB_PER_WAVE; ++i) {
       const int row = (wave * KB_PER_WAVE + i) * ROWS_PER_KB + r_in;
       const int col = IS_V ? swz_v<D>(row, pch) : swz<D>(row, pch);
-      voff[i] = (int)(row * stride * 2) + col * 16;
+      voff[i] = row * (int)row_bytes + col * 16;
     }
-    lds_off = wave * KB_PER_WAVE * 512;
+    lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_buf0) + wave * KB_PER_WAVE * 1024);
   }
 
-  __device__ __forceinline__ void issue(u16* lds, const u16* g, long long stride, int kv0,
-                                        int kv_len) const {
-    const long long bytes = (long long)(kv_len - kv0) * stride * 2;
-    const i32x4 rsrc = uniform4(make_rsrc(g + (long long)kv0 * stride,
-                                          bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes));
-    const unsigned base = __builtin_amdgcn_readfirstlane(lds_addr(lds + lds_off));
+  // loads of keys [kv0, kv0 + NK) into buffer `buf` (its LDS is lds0 + buf * 2 * kStepBytes
+  // when the two buffers of K (or V) are laid out [buf][K|V])
+  __device__ __forceinline__ void issue(int kv0, int kv_len, unsigned lds_buf) const {
+    const int rows = min(kv_len - kv0, NK);
+    const i32x4 rsrc = make_rsrc(base + (unsigned long long)kv0 * row_bytes,
+                                 rows > 0 ? (unsigned)rows * row_bytes : 0u);
 #pragma unroll
-    for (int i = 0; i < KB_PER_WAVE; ++i) dma16(rsrc, base + 1024 * i, voff[i]);
+    for (int i = 0; i < KB_PER_WAVE; ++i) dma16(rsrc, lds_buf + 1024 * i, voff[i]);
   }
 };
 
@@ -192,7 +201,7 @@ struct Lane {
   int lane, l32, hh, vg, vi;
   int q, qc;
   float slope2;
-  int dq;  // document id of this lane's query row (document mask)
+  int dq;            // document id of this lane's query row (document mask)
   int kofs[D / 16];  // K fragment (row l32 of block 0, k-step ks)
   int vofs[D / 32];  // V transposed-read piece (k-step 0, half 0, d-block db)
 
@@ -209,36 +218,6 @@ struct Lane {
   }
 };
 
-// S^T = K . Q^T for the four 32-key blocks of a tile.
-template <int D>
-__device__ __forceinline__ void compute_s(f32x16 (&s)[4], const u16* sK, const bf16x8 (&qf)[D / 16],
-                                          const Lane<D>& ln) {
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[blk][r] = 0.0f;
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      // rows 32*blk + l32: block offsets keep row % 16 (and (row/2) % 8)
-      const bf16x8 af =
-          as_bf16x8(*reinterpret_cast<const uint4*>(sK + ln.kofs[ks] + 32 * blk * D));
-      s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], s[blk], 0, 0, 0);
-    }
-  }
-  // scores feed the vector ALUs: keep them in VGPRs
-#if defined(__HIP_DEVICE_COMPILE__)
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk) asm volatile("" : "+v"(s[blk]));
-#endif
-}
-
-// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgValu = 0x0002;
-constexpr int kSgMfma = 0x0008;
-constexpr int kSgDsRead = 0x0100;
-
 // Row max across the two lanes that hold one query row (lane, lane ^ 32).
 __device__ __forceinline__ float pair_max(float x) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
@@ -248,7 +227,7 @@ __device__ __forceinline__ float pair_max(float x) {
 
 // V^T operand fragment for P.V MFMA (k-step ks, d-block db): lane row
 // d = 32*db + lane%32, slot t <-> key 16*ks + 8*(t/4) + 4*hh + t%4 (the key
-// order of pf), read from the row-major V tile with two transposing reads:
+// order of pf), read from the row-major V block with two transposing reads:
 // in each 16-lane group lane j supplies the 8-byte piece (row j/4, columns
 // 4*(j%4)..+3) of a 4-key x 16-d block and receives column j of that block.
 template <int D>
@@ -270,24 +249,12 @@ __device__ __forceinline__ bf16x8 k_frag(const u16* sK, const Lane<D>& ln, int k
   return as_bf16x8(*reinterpret_cast<const uint4*>(sK + ln.kofs[ks] + 32 * blk * D));
 }
 
-// O^T += V^T . P^T for one tile, no other work (the last tile).
-template <int D>
-__device__ __forceinline__ void pv(f32x16 (&o)[D / 32], const bf16x8 (&pf)[8], const u16* sV,
-                                   const Lane<D>& ln) {
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D>(sV, ln, ks, db), pf[ks], o[db],
-                                                      0, 0, 0);
-}
-
-// Key offset (within the tile, without 4*hh) of result register r of block blk.
+// Key offset (within the step, without 4*hh) of result register r of block blk.
 __device__ __forceinline__ constexpr int key_off(int blk, int r) {
   return 32 * blk + 8 * (r >> 2) + (r & 3);
 }
 
-// Per-tile mask limits: key offset c (see key_off) is allowed when c <= hi,
+// Per-step mask limits: key offset c (see key_off) is allowed when c <= hi,
 // and for the sliding window also c > win_lo or c < sink_hi; for documents
 // the key's id (LDS) must equal the query row's.
 struct MaskLimits {
@@ -305,13 +272,16 @@ __device__ __forceinline__ MaskLimits mask_limits(int kv0, const FwdArgs& a, con
   return m;
 }
 
-// Phase-1 element work: y = score_mod(x), masked on partial tiles; returns y.
+// Logit of one score: y = score_mod(x) in base-2 units (raw x for
+// SCORE_NONE, scaled later), -inf where masked on partial tiles.
 template <int D, int MASK, int SCORE, bool MASKED>
 __device__ __forceinline__ float elem_logit(float x, int blk, int r, int kv0, const MaskLimits& ml,
-                                            const int* tile_doc, const FwdArgs& a,
+                                            const int* step_doc, const FwdArgs& a,
                                             const Lane<D>& ln) {
   float y = x;
-  if constexpr (SCORE != SCORE_NONE) {
+  if constexpr (SCORE == SCORE_SCALED) {
+    y = x * a.c_scale;
+  } else if constexpr (SCORE != SCORE_NONE) {
     const int key = kv0 + key_off(blk, r) + 4 * ln.hh;
     y = ScoreMod<SCORE>::apply(x, a.c_scale, a.c_cap, a.cap2, ln.slope2, (float)(key - ln.q));
   }
@@ -319,116 +289,94 @@ __device__ __forceinline__ float elem_logit(float x, int blk, int r, int kv0, co
     const int c = key_off(blk, r);
     bool ok = c <= ml.hi;
     if constexpr (MASK == MASK_SLIDING_SINK) ok = ok && (c > ml.win_lo || c < ml.sink_hi);
-    if constexpr (MASK == MASK_DOCUMENT) ok = ok && tile_doc[c + 4 * ln.hh] == ln.dq;
+    if constexpr (MASK == MASK_DOCUMENT) ok = ok && step_doc[c + 4 * ln.hh] == ln.dq;
     y = ok ? y : -INFINITY;
   }
   return y;
 }
 
-// Fragment prefetch distance (in MFMAs) and ring size.
-constexpr int kDist = 4;
-constexpr int kRing = kDist + 1;
-
-// One tile of the pipeline, in program order (each group fenced):
-//   phase 1: O += V[j-1] . P[j-1]; per MFMA a share of Y = logits(X) and the
-//            row max (X holds S[j], written by the previous phase 2);
-//   lazy rescale of O and l when a row max rose by more than 2^8;
-//   phase 2: X = S[j+1] = K[j+1] . Q^T; per MFMA a share of P = exp2(Y - m)
-//            (row sum, bf16 pack).
+// One KV step: S = K . Q^T, online softmax, O += V . P.
 template <int D, int MASK, int SCORE, bool MASKED>
-__device__ __forceinline__ void step(f32x16 (&X)[4], f32x16 (&Y)[4], f32x16 (&o)[D / 32],
-                                     bf16x8 (&pf)[8], float& m_ref, float& l,
-                                     const bf16x8 (&qf)[D / 16], const u16* sK_next,
-                                     const u16* sV_prev, int kv0, const int* tile_doc,
-                                     const FwdArgs& a, const Lane<D>& ln) {
-  constexpr int DB = D / 32;
-  constexpr int KS = D / 16;
-  constexpr int NPV = 8 * DB;       // P.V MFMAs per tile
-  constexpr int NS = 4 * KS;        // S MFMAs per tile
-  constexpr int E1 = 64 / NPV;      // elements per phase-1 group
-  constexpr int E2 = 64 / NS;       // elements per phase-2 group
-  const MaskLimits ml = mask_limits<D, MASK>(kv0, a, ln);
-
-  // ---- phase 1
-  bf16x8 vr[kRing];
+__device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l,
+                                     const bf16x8 (&qf)[D / 16], const u16* sK, const u16* sV,
+                                     int kv0, const int* step_doc, const FwdArgs& a,
+                                     const Lane<D>& ln) {
+  using G = Geom<D>;
+  f32x16 s[G::NB];
 #pragma unroll
-  for (int i = 0; i < kDist; ++i) vr[i] = v_frag<D>(sV_prev, ln, i / DB, i % DB);
+  for (int b = 0; b < G::NB; ++b) s[b] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks)
+#pragma unroll
+    for (int b = 0; b < G::NB; ++b)
+      s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(sK, ln, ks, b), qf[ks], s[b], 0,
+                                                     0, 0);
+
+  const MaskLimits ml = mask_limits<D, MASK>(kv0, a, ln);
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < NPV; ++i) {
-    if (i + kDist < NPV)
-      vr[(i + kDist) % kRing] = v_frag<D>(sV_prev, ln, (i + kDist) / DB, (i + kDist) % DB);
-    o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % kRing], pf[i / DB], o[i % DB], 0,
-                                                        0, 0);
+  for (int b = 0; b < G::NB; ++b)
 #pragma unroll
-    for (int e = i * E1; e < (i + 1) * E1; ++e) {
-      const int blk = e >> 4, r = e & 15;
-      Y[blk][r] = elem_logit<D, MASK, SCORE, MASKED>(X[blk][r], blk, r, kv0, ml, tile_doc, a, ln);
-      mx = fmaxf(mx, Y[blk][r]);
+    for (int r = 0; r < 16; ++r) {
+      s[b][r] = elem_logit<D, MASK, SCORE, MASKED>(s[b][r], b, r, kv0, ml, step_doc, a, ln);
+      mx = fmaxf(mx, s[b][r]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
   mx = pair_max(mx);
-  if constexpr (SCORE == SCORE_NONE) mx *= a.c_scale;
+  if constexpr (SCORE == SCORE_NONE) mx *= a.c_scale;  // c_scale > 0 here
 
-  // ---- lazy rescale (a real branch: rare)
+  // lazy rescale (a real branch: rare)
   if (__any(mx > m_ref + kRescaleSlack)) {
     asm volatile("");
     const float m_new = fmaxf(m_ref, mx);
     const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_ref - m_new);
     l *= alpha;
 #pragma unroll
-    for (int i = 0; i < DB; ++i)
+    for (int i = 0; i < G::DB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
     m_ref = m_new;
   }
   const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
-  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- phase 2
-  bf16x8 kr[kRing];
-#pragma unroll
-  for (int i = 0; i < kDist; ++i) kr[i] = k_frag<D>(sK_next, ln, i / 4, i % 4);
+  bf16x8 pf[G::PKS];
   float rs = 0.0f;
-  const f32x16 zero = {};
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    if (i + kDist < NS) kr[(i + kDist) % kRing] = k_frag<D>(sK_next, ln, (i + kDist) / 4, (i + kDist) % 4);
-    const int blk = i % 4;
-    X[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % kRing], qf[i / 4],
-                                                     i < 4 ? zero : X[blk], 0, 0, 0);
-#pragma unroll
-    for (int e = i * E2; e < (i + 1) * E2; ++e) {
-      const float y = Y[e >> 4][e & 15];
-      float p;
-      if constexpr (SCORE == SCORE_NONE) {
-        p = fast_exp2(fmaf(y, a.c_scale, -m_use));
-      } else {
-        p = fast_exp2(y - m_use);
-      }
-      rs += p;
-      pf[e >> 3][e & 7] = (__bf16)p;
+  for (int e = 0; e < G::NE; ++e) {
+    const float y = s[e >> 4][e & 15];
+    float p;
+    if constexpr (SCORE == SCORE_NONE) {
+      p = fast_exp2(fmaf(y, a.c_scale, -m_use));
+    } else {
+      p = fast_exp2(y - m_use);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    rs += p;
+    pf[e >> 3][e & 7] = (__bf16)p;
   }
   l += rs;
+
+#pragma unroll
+  for (int ks = 0; ks < G::PKS; ++ks)
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D>(sV, ln, ks, db), pf[ks], o[db], 0,
+                                                      0, 0);
 }
 
 template <int D, int MASK, int SCORE>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
-  constexpr int KSTEPS = D / 16;
-  constexpr int DBLK = D / 32;
-  constexpr int TILE = kBlock * D;  // elements of one K or V tile
-  // LDS: K and V tiles double-buffered as separate arrays (so the compiler
-  // can tell the buffer being filled from the one being read and does not
-  // wait for in-flight loads before LDS reads), two 128-entry document-id
-  // buffers, and the item's tile list (NKB ints, dynamic)
-  __shared__ __attribute__((aligned(16))) u16 sK0[TILE];
-  __shared__ __attribute__((aligned(16))) u16 sK1[TILE];
-  __shared__ __attribute__((aligned(16))) u16 sV0[TILE];
-  __shared__ __attribute__((aligned(16))) u16 sV1[TILE];
-  __shared__ __attribute__((aligned(16))) int docbuf[2 * 128];
+__global__ __launch_bounds__(kThreads, kWgPerCu) void fwd_bf16_kernel(FwdArgs a) {
+  using G = Geom<D>;
+  constexpr int NK = G::NK;
+  constexpr int SPT = G::SPT;
+  constexpr int STEP_ELEMS = kStepBytes / 2;
+  // LDS: K and V step blocks double-buffered (separate arrays, so the
+  // compiler can tell the buffer being filled from the one being read and does
+  // not wait for in-flight loads before LDS reads), two document-id buffers,
+  // and the item's tile list (NKB ints, dynamic)
+  __shared__ __attribute__((aligned(16))) u16 sK0[STEP_ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 sK1[STEP_ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 sV0[STEP_ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 sV1[STEP_ELEMS];
+  __shared__ __attribute__((aligned(16))) int docbuf[(MASK == MASK_DOCUMENT) ? 2 * NK : 1];
   extern __shared__ __attribute__((aligned(16))) int tlist[];
 
   // dispatch order -> item; rounds of equal tile count are remapped so the
@@ -459,12 +407,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
     ln.slope2 = alibi_slope(a.slopes, h, a.Hq) * kLog2e;
 
-  const u16* kbase = a.k + b * a.sk0 + hk * a.sk1;
-  const u16* vbase = a.v + b * a.sv0 + hk * a.sv1;
-  TileLoader<D, false> kload;
-  TileLoader<D, true> vload;
-  kload.init(wave, ln.lane, a.sk2);
-  vload.init(wave, ln.lane, a.sv2);
+  BlockLoader<D, false> kload;
+  BlockLoader<D, true> vload;
+  kload.init(a.k + b * a.sk0 + hk * a.sk1, a.sk2, wave, ln.lane, sK0);
+  vload.init(a.v + b * a.sv0 + hk * a.sv1, a.sv2, wave, ln.lane, sV0);
+  const unsigned k_lds[2] = {kload.lds0, kload.lds0 + (lds_addr(sK1) - lds_addr(sK0))};
+  const unsigned v_lds[2] = {vload.lds0, vload.lds0 + (lds_addr(sV1) - lds_addr(sV0))};
+
   const long long lrow = (long long)it.mrow * a.bm.NKB;
   // counts are clamped to the list length so a malformed BlockMask cannot
   // index past the staged list
@@ -473,23 +422,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // the item's tiles, full then partial, staged in LDS once
   for (int t = threadIdx.x; t < n; t += kThreads)
     tlist[t] = t < nfull ? a.bm.full_idx[lrow + t] : a.bm.kv_idx[lrow + (t - nfull)];
-  auto tile_kv0 = [&](int t) { return kBlock * __builtin_amdgcn_readfirstlane(tlist[t]); };
-  // document ids of a tile's keys -> docbuf[i] (rows past KV_LEN read as 0)
-  auto issue_doc = [&](int* dst, int kv0) {
+  // document ids of a step's keys -> docbuf (rows past KV_LEN read as 0)
+  auto issue_doc = [&](int buf, int kv0) {
     if constexpr (MASK == MASK_DOCUMENT) {
       if (wave == 0) {
-        const int nrec = 4 * (min(a.KV_LEN, a.doc_len) - kv0);
-        const i32x4 rsrc = uniform4(make_rsrc(doc_row + kv0, nrec > 0 ? nrec : 0));
+        const int rows = min(a.KV_LEN, a.doc_len) - kv0;
+        const i32x4 rsrc = make_rsrc(reinterpret_cast<unsigned long long>(doc_row + kv0),
+                                     rows > 0 ? 4u * (unsigned)rows : 0u);
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          dma4(rsrc, __builtin_amdgcn_readfirstlane(lds_addr(dst + 64 * c)), 4 * ln.lane + 256 * c);
+        for (int c = 0; c < NK / 64; ++c)
+          dma4(rsrc, __builtin_amdgcn_readfirstlane(lds_addr(docbuf + buf * NK + 64 * c)),
+               4 * ln.lane + 256 * c);
       }
     }
   };
 
-  f32x16 o[DBLK];
+  f32x16 o[G::DB];
 #pragma unroll
-  for (int i = 0; i < DBLK; ++i)
+  for (int i = 0; i < G::DB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
   float m_ref = -INFINITY;
@@ -497,59 +447,64 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   __syncthreads();  // tile list visible
   if (n > 0) {
-    // prologue: K[0] -> K buffer 0, K[1] -> K buffer 1, Q^T fragments; S[0]
+    // tile indices are clamped into [0, NKB): a malformed BlockMask computes
+    // garbage but never reads outside the KV tensors
+    auto tile_kv0 = [&](int t) {
+      const int idx = __builtin_amdgcn_readfirstlane(tlist[t]);
+      return kBlock * min(max(idx, 0), a.bm.NKB - 1);
+    };
+    // prologue: step 0 -> buffer 0, Q^T fragments
     int kv0 = tile_kv0(0);
-    issue_doc(docbuf, kv0);
-    kload.issue(sK0, kbase, a.sk2, kv0, a.KV_LEN);
-    if (n > 1) kload.issue(sK1, kbase, a.sk2, tile_kv0(1), a.KV_LEN);
-    bf16x8 qf[KSTEPS];
+    issue_doc(0, kv0);
+    kload.issue(kv0, a.KV_LEN, k_lds[0]);
+    vload.issue(kv0, a.KV_LEN, v_lds[0]);
+    bf16x8 qf[G::KS];
     {
       const u16* qrow = a.q + b * a.sq0 + h * a.sq1 + (long long)ln.qc * a.sq2;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
+      for (int ks = 0; ks < G::KS; ++ks)
         qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * ln.hh));
     }
-    // V buffer 1 is read by the first tile's (empty) P.V: zero it, P = 0
-    for (int i = threadIdx.x; i < TILE / 8; i += kThreads)
-      reinterpret_cast<uint4*>(sV1)[i] = make_uint4(0, 0, 0, 0);
     wait_loads_and_sync();
-    f32x16 s[4], s2[4];
-    bf16x8 pf[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) pf[ks][t] = (__bf16)0.0f;
-    compute_s<D>(s, sK0, qf, ln);
 
-    // Tile j: at entry, K[j+1] and V[j-1] are resident; issue V[j] into V
-    // buffer j%2 (it held V[j-2]) and K[j+2] into K buffer j%2 (it held K[j]).
-    // The next tile's S is always computed; on the last tile it reads a stale
-    // buffer and is discarded (hidden under that tile's softmax).
-    // tile j reads K[(j+1) % 2], V[(j+1) % 2] (holding K[j+1], V[j-1]) and
-    // fills K[j % 2], V[j % 2] with K[j+2], V[j]. Full tiles (no mask code)
-    // then partial tiles; a full tile crossing KV_LEN, which the builder
-    // never lists, is masked on the partial path's key bound.
-    auto stage = [&](int j, auto masked_tag) {
-      constexpr bool M = decltype(masked_tag)::value;
-      const int kv_next = tile_kv0(j + 1 < n ? j + 1 : j);
-      const int kv_after = tile_kv0(j + 2 < n ? j + 2 : j);
-      const bool odd = j & 1;
-      vload.issue(odd ? sV1 : sV0, vbase, a.sv2, kv0, a.KV_LEN);
-      if (j + 2 < n) kload.issue(odd ? sK1 : sK0, kbase, a.sk2, kv_after, a.KV_LEN);
-      if (j + 1 < n) issue_doc(odd ? docbuf : docbuf + 128, kv_next);
-      step<D, MASK, SCORE, M>(s, s2, o, pf, m_ref, l, qf, odd ? sK0 : sK1, odd ? sV0 : sV1, kv0,
-                              odd ? docbuf + 128 : docbuf, a, ln);
-      kv0 = kv_next;
-      wait_loads_and_sync();
+    // Step g (global step counter over all tiles) reads buffer g % 2; at its
+    // start it issues the loads of step g + 1 into the other buffer (read by
+    // step g - 1, which every wave finished before the last barrier).
+    int g = 0;
+    int t_next = 1;
+    int kv_tile_next = n > 1 ? tile_kv0(1) : 0;
+    auto run_tile = [&](auto masked_tag) {
+#pragma unroll
+      for (int sub = 0; sub < SPT; ++sub) {
+        constexpr bool M = decltype(masked_tag)::value;
+        const bool last_sub = sub == SPT - 1;
+        const bool has_next = !last_sub || t_next < n;
+        const int kv_nxt = last_sub ? kv_tile_next : kv0 + NK;
+        // buffer of this step: with two steps per tile the parity is the
+        // sub-step (every tile starts on buffer 0)
+        const int cur = (SPT == 2) ? sub : (g & 1);
+        const int nb = cur ^ 1;
+        if (has_next) {
+          issue_doc(nb, kv_nxt);
+          kload.issue(kv_nxt, a.KV_LEN, k_lds[nb]);
+          vload.issue(kv_nxt, a.KV_LEN, v_lds[nb]);
+        }
+        step<D, MASK, SCORE, M>(o, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
+                                (MASK == MASK_DOCUMENT) ? docbuf + cur * NK : nullptr, a, ln);
+        kv0 = kv_nxt;
+        ++g;
+        wait_loads_and_sync();
+      }
+      ++t_next;
+      kv_tile_next = t_next < n ? tile_kv0(t_next) : 0;
     };
-    // full tiles that end inside KV_LEN take the unmasked path
-    const int nfull_fast = (nfull > 0 && tile_kv0(nfull - 1) + kBlock > a.KV_LEN) ? nfull - 1 : nfull;
+    // full tiles that end inside KV_LEN take the unmasked path; a full tile
+    // crossing KV_LEN (never listed by the builder) is masked on the key bound
+    const int nfull_fast =
+        (nfull > 0 && tile_kv0(nfull - 1) + kBlock > a.KV_LEN) ? nfull - 1 : nfull;
     int j = 0;
-    for (; j < nfull_fast; ++j) stage(j, std::false_type{});
-    for (; j < n; ++j) stage(j, std::true_type{});
-    const u16* vlast = ((n - 1) & 1) ? sV1 : sV0;
-    // the last tile's P . V
-    pv<D>(o, pf, vlast, ln);
+    for (; j < nfull_fast; ++j) run_tile(std::false_type{});
+    for (; j < n; ++j) run_tile(std::true_type{});
   }
 
   // epilogue: O = O_acc / l, LSE = ln(sum) + max
@@ -558,13 +513,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   if (qvalid) {
     u16* orow = a.o + b * a.so0 + h * a.so1 + (long long)ln.q * a.so2;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
+    for (int db = 0; db < G::DB; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int gq = 0; gq < 4; ++gq) {
         bf16x4 pk;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pk[j] = (__bf16)(o[db][4 * g + j] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * ln.hh) = pk;
+        for (int j = 0; j < 4; ++j) pk[j] = (__bf16)(o[db][4 * gq + j] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * gq + 4 * ln.hh) = pk;
       }
     }
     if (ln.hh == 0) {
@@ -598,8 +553,10 @@ hipError_t dispatch_score(const FwdArgs& args, int score, int grid, hipStream_t 
       return launch_one<D, MASK, SCORE_ALIBI>(args, grid, stream);
     case SCORE_SOFTCAP:
       return launch_one<D, MASK, SCORE_SOFTCAP>(args, grid, stream);
-    default:
+    case SCORE_SOFTCAP_ALIBI:
       return launch_one<D, MASK, SCORE_SOFTCAP_ALIBI>(args, grid, stream);
+    default:
+      return launch_one<D, MASK, SCORE_SCALED>(args, grid, stream);
   }
 }
 
@@ -620,7 +577,8 @@ hipError_t dispatch_mask(const FwdArgs& args, int mask, int score, int grid, hip
 }  // namespace
 
 int fwd_bf16_lds_bytes(int D, int NKB) {
-  return 4 * kBlock * D * 2 + 4 * ((NKB + 3) & ~3) + 2 * 128 * 4;
+  (void)D;
+  return 4 * kStepBytes + 4 * ((NKB + 3) & ~3) + 2 * 128 * 4;
 }
 
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream) {
@@ -631,8 +589,8 @@ hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream) {
   a.o = static_cast<u16*>(L.o);
   a.lse = L.lse;
   a.sq0 = L.sq[0]; a.sq1 = L.sq[1]; a.sq2 = L.sq[2];
-  a.sk0 = L.sk[0]; a.sk1 = L.sk[1]; a.sk2 = L.sk[2];
-  a.sv0 = L.sv[0]; a.sv1 = L.sv[1]; a.sv2 = L.sv[2];
+  a.sk0 = L.sk[0]; a.sk1 = L.sk[1]; a.sk2 = (int)L.sk[2];
+  a.sv0 = L.sv[0]; a.sv1 = L.sv[1]; a.sv2 = (int)L.sv[2];
   a.so0 = L.so[0]; a.so1 = L.so[1]; a.so2 = L.so[2];
   a.B = L.B;
   a.Hq = L.Hq;
@@ -654,8 +612,10 @@ hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream) {
   a.xcd_round = (L.bm.Bm == 1 && L.bm.Hm == 1 && R % 8 == 0 && (R / 8) % a.G == 0) ? R : 0;
   const int grid = L.B * L.Hq * L.bm.NQB;
   if (grid == 0) return hipSuccess;
-  if (L.D == 128) return dispatch_mask<128>(a, L.mask_kind, L.score_kind, grid, stream);
-  return dispatch_mask<64>(a, L.mask_kind, L.score_kind, grid, stream);
+  // the unscaled fast path takes the row max before scaling: scale must be > 0
+  const int score = (L.score_kind == SCORE_NONE && !(L.scale > 0.0f)) ? SCORE_SCALED : L.score_kind;
+  if (L.D == 128) return dispatch_mask<128>(a, L.mask_kind, score, grid, stream);
+  return dispatch_mask<64>(a, L.mask_kind, score, grid, stream);
 }
 
 }  // namespace fa

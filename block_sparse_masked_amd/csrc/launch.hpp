@@ -46,6 +46,7 @@ struct FwdLaunch {
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream);
 int fwd_bf16_lds_bytes(int D, int NKB);  // dynamic LDS of the bf16 forward
 constexpr int kMaxLdsBytes = 160 * 1024;
+constexpr long long kMaxBf16RowStride = 1ll << 22;  // k/v row stride limit of the bf16 forward
 hipError_t launch_fwd_f32(const FwdLaunch& L, hipStream_t stream);
 
 }  // namespace fa

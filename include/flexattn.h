@@ -199,7 +199,10 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
  * A row with no allowed key gets out = 0 and lse = -inf. bf16 inputs are
  * contracted on bf16 MFMA with fp32 accumulation (softmax probabilities are
  * rounded to bf16 for the P.V product); fp32 inputs are computed in fp32
- * throughout. Asynchronous on `stream`.
+ * throughout. BF16 limits (FLEXATTN_ERR_UNSUPPORTED beyond them): k and v
+ * row strides (stride[2]) at most 2^22 elements, and the per-row tile list
+ * (num_kv_blocks ints) must fit in LDS beside the K/V staging buffers.
+ * Asynchronous on `stream`.
  */
 flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
                              const flexattn_tensor* v, const flexattn_block_mask* bm,

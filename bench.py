@@ -4,7 +4,10 @@ One step = one pass of the whole path over one batch of synthetic input:
 the BlockMask build (classify, compact, schedule) followed by the forward.
 Inputs are generated once and stay resident in HBM. Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1] [--settle-ms T]
+
+Before the W warmup steps, untimed steps run for T ms of wall time so the
+GPU clock has settled (it climbs over the first tens of ms of load).
 
 FLOP accounting: 4 * D flops per allowed (q, kv) pair and (b, h) (2D for
 q.k, 2D for p.v); softmax and score_mod arithmetic are not counted. The
@@ -89,11 +92,13 @@ def cpu_baseline(w: W.Workload, inp: W.Inputs, budget_s: float = 20.0):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=W.DENSE_CAUSAL_GQA.name, choices=sorted(W.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps for this long before the warmup steps (clock settling)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the forward shards by "
@@ -127,6 +132,16 @@ def main(argv=None):
                           out=out, lse=lse, stream=stream)
         return bm
 
+    # Clock settling (untimed): the GPU raises its clock over the first tens
+    # of milliseconds of sustained load, so run steps for at least
+    # --settle-ms of wall time before the warmup steps.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step()
+        settle_steps += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         bm = step()
     torch.cuda.synchronize()
@@ -180,6 +195,7 @@ def main(argv=None):
                    "KV_LEN": w.KV_LEN, "D": w.D, "mask": w.mask, "score": w.score,
                    "seed": w.seed, "block": 128, "parallelism": "single-gpu"},
         "pct_of_peak": round(100.0 * value / peak, 2),
+        "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "fwd_ms_avg": round(fwd_avg, 4),
         "fwd_ms_min": round(float(np.min(fwd_ms)), 4),
         "build_ms_avg": round(float(np.mean(build_ms)), 4),

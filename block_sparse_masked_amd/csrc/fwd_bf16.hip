@@ -32,6 +32,8 @@
 // lazily: O and the row sum are rescaled only when a row's max grows by more
 // than 2^8 (exp2 units), which leaves the result unchanged (any reference
 // point gives the same normalised sums) while skipping most rescales.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "common.hpp"
@@ -48,8 +50,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 
-constexpr int kThreads = 256;
-constexpr int kWgPerCu = 2;
+constexpr int kWavesPerHead = 4;  // 4 x 32 query rows = one 128-row query tile
 constexpr float kRescaleSlack = 8.0f;  // exp2 units: p <= 256 between rescales
 constexpr int kStepBytes = 16384;      // one K (or V) step block in LDS
 
@@ -129,13 +130,19 @@ __device__ __forceinline__ i32x4 make_rsrc(unsigned long long base, unsigned byt
 // block with its M0 setup and no register results: the LDS they fill is a
 // buffer no instruction reads until after the explicit vmcnt(0) + barrier
 // that ends the step, so the compiler need not (and does not) wait for them.
+// No memory clobber: the asm stays ordered against the barriers and waits
+// (all have side effects), while the LDS reads of the other buffer may be
+// scheduled around it. Each load takes the CU's vector-memory path for a few
+// cycles, so the step spreads them between its matrix instructions.
+// The LDS address is wave-uniform by construction; readfirstlane states that
+// to the compiler so the asm operand is always a scalar register.
 __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               : : "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+               : : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "m0");
 }
 __device__ __forceinline__ void dma4(i32x4 rsrc, unsigned lds, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               : : "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+               : : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "m0");
 }
 
 // Loads of one [NK][D] step block of K or V. Each wave-wide load fills one
@@ -144,11 +151,11 @@ __device__ __forceinline__ void dma4(i32x4 rsrc, unsigned lds, int voff) {
 // from the block's first row is fixed and computed once. Per step only the
 // resource moves; its range ends at KV_LEN, so rows past it read as zero
 // (their scores are masked: a tile crossing KV_LEN takes the masked path).
-template <int D, bool IS_V>
+template <int D, bool IS_V, int WAVES>
 struct BlockLoader {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int ROWS_PER_KB = 1024 / (2 * D);
-  static constexpr int KB_PER_WAVE = kStepBytes / 1024 / 4;
+  static constexpr int KB_PER_WAVE = kStepBytes / 1024 / WAVES;
   static constexpr int NK = Geom<D>::NK;
   int voff[KB_PER_WAVE];
   unsigned long long base;  // byte address of key row 0 of this (b, kv head)
@@ -171,6 +178,14 @@ struct BlockLoader {
 
   // loads of keys [kv0, kv0 + NK) into buffer `buf` (its LDS is lds0 + buf * 2 * kStepBytes
   // when the two buffers of K (or V) are laid out [buf][K|V])
+  __device__ __forceinline__ i32x4 plan(int kv0, int kv_len) const {
+    const int rows = min(kv_len - kv0, NK);
+    return make_rsrc(base + (unsigned long long)kv0 * row_bytes,
+                     rows > 0 ? (unsigned)rows * row_bytes : 0u);
+  }
+  __device__ __forceinline__ void issue_one(i32x4 rsrc, unsigned lds_buf, int i) const {
+    dma16(rsrc, lds_buf + 1024 * i, voff[i]);
+  }
   __device__ __forceinline__ void issue(int kv0, int kv_len, unsigned lds_buf) const {
     const int rows = min(kv_len - kv0, NK);
     const i32x4 rsrc = make_rsrc(base + (unsigned long long)kv0 * row_bytes,
@@ -295,12 +310,13 @@ __device__ __forceinline__ float elem_logit(float x, int blk, int r, int kv0, co
   return y;
 }
 
-// One KV step: S = K . Q^T, online softmax, O += V . P.
-template <int D, int MASK, int SCORE, bool MASKED>
+// One KV step: S = K . Q^T, online softmax, O += V . P. `dma(i)` issues the
+// i-th of the NDMA loads of the next step (called between S products).
+template <int D, int MASK, int SCORE, bool MASKED, int NDMA, typename DMA>
 __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l,
                                      const bf16x8 (&qf)[D / 16], const u16* sK, const u16* sV,
                                      int kv0, const int* step_doc, const FwdArgs& a,
-                                     const Lane<D>& ln) {
+                                     const Lane<D>& ln, DMA&& dma) {
   using G = Geom<D>;
   f32x16 s[G::NB];
 #pragma unroll
@@ -309,8 +325,15 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
   for (int ks = 0; ks < G::KS; ++ks)
 #pragma unroll
     for (int b = 0; b < G::NB; ++b)
+    {
       s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(sK, ln, ks, b), qf[ks], s[b], 0,
                                                      0, 0);
+      // the next step's loads, spread over the S products
+      constexpr int NS = G::KS * G::NB;
+      static_assert(NS % NDMA == 0, "loads spread evenly");
+      const int i = ks * G::NB + b;
+      if (i % (NS / NDMA) == 0) dma(i / (NS / NDMA));
+    }
 
   const MaskLimits ml = mask_limits<D, MASK>(kv0, a, ln);
   float mx = -INFINITY;
@@ -362,9 +385,14 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
                                                       0, 0);
 }
 
-template <int D, int MASK, int SCORE>
-__global__ __launch_bounds__(kThreads, kWgPerCu) void fwd_bf16_kernel(FwdArgs a) {
+// HEADS query heads that share one KV head (and one BlockMask row) per
+// workgroup: 4 * HEADS waves read the same K/V step blocks, so HEADS = 2
+// halves the global->LDS traffic per flop. Two waves per SIMD either way.
+template <int D, int MASK, int SCORE, int HEADS>
+__global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf16_kernel(FwdArgs a) {
   using G = Geom<D>;
+  constexpr int WAVES = kWavesPerHead * HEADS;
+  constexpr int THREADS = 64 * WAVES;
   constexpr int NK = G::NK;
   constexpr int SPT = G::SPT;
   constexpr int STEP_ELEMS = kStepBytes / 2;
@@ -387,17 +415,18 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void fwd_bf16_kernel(FwdArgs a)
     const int r = x / R, u = x - r * R;
     x = r * R + (u & 7) * (R >> 3) + (u >> 3);
   }
-  const Item it = decode_item(x, a.bm, a.B, a.Hq);
-  const int b = it.b, h = it.h;
-  const int hk = h / a.G;
+  // with HEADS = 2 the item's head index counts head pairs (2p, 2p + 1)
+  const Item it = decode_item(x, a.bm, a.B, a.Hq / HEADS);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = it.b, h = it.h * HEADS + wave / kWavesPerHead;
+  const int hk = (it.h * HEADS) / a.G;
   Lane<D> ln;
   ln.lane = threadIdx.x & 63;
   ln.l32 = ln.lane & 31;
   ln.hh = ln.lane >> 5;
   ln.vg = (ln.lane >> 4) & 1;
   ln.vi = ln.lane & 15;
-  ln.q = it.qb * kBlock + wave * 32 + ln.l32;
+  ln.q = it.qb * kBlock + (wave % kWavesPerHead) * 32 + ln.l32;
   const bool qvalid = ln.q < a.Q_LEN;
   ln.qc = qvalid ? ln.q : a.Q_LEN - 1;
   const int* doc_row = (MASK == MASK_DOCUMENT) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
@@ -407,8 +436,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void fwd_bf16_kernel(FwdArgs a)
   if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
     ln.slope2 = alibi_slope(a.slopes, h, a.Hq) * kLog2e;
 
-  BlockLoader<D, false> kload;
-  BlockLoader<D, true> vload;
+  BlockLoader<D, false, WAVES> kload;
+  BlockLoader<D, true, WAVES> vload;
   kload.init(a.k + b * a.sk0 + hk * a.sk1, a.sk2, wave, ln.lane, sK0);
   vload.init(a.v + b * a.sv0 + hk * a.sv1, a.sv2, wave, ln.lane, sV0);
   const unsigned k_lds[2] = {kload.lds0, kload.lds0 + (lds_addr(sK1) - lds_addr(sK0))};
@@ -420,7 +449,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void fwd_bf16_kernel(FwdArgs a)
   const int nfull = min(a.bm.full_num[it.mrow], a.bm.NKB);
   const int n = min(nfull + a.bm.kv_num[it.mrow], a.bm.NKB);
   // the item's tiles, full then partial, staged in LDS once
-  for (int t = threadIdx.x; t < n; t += kThreads)
+  for (int t = threadIdx.x; t < n; t += THREADS)
     tlist[t] = t < nfull ? a.bm.full_idx[lrow + t] : a.bm.kv_idx[lrow + (t - nfull)];
   // document ids of a step's keys -> docbuf (rows past KV_LEN read as 0)
   auto issue_doc = [&](int buf, int kv0) {
@@ -484,13 +513,18 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void fwd_bf16_kernel(FwdArgs a)
         // sub-step (every tile starts on buffer 0)
         const int cur = (SPT == 2) ? sub : (g & 1);
         const int nb = cur ^ 1;
-        if (has_next) {
-          issue_doc(nb, kv_nxt);
-          kload.issue(kv_nxt, a.KV_LEN, k_lds[nb]);
-          vload.issue(kv_nxt, a.KV_LEN, v_lds[nb]);
-        }
-        step<D, MASK, SCORE, M>(o, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
-                                (MASK == MASK_DOCUMENT) ? docbuf + cur * NK : nullptr, a, ln);
+        if (has_next) issue_doc(nb, kv_nxt);
+        // without a next step the loads get an empty range (they fetch
+        // nothing; buffer nb was last read before the previous barrier)
+        constexpr int KPW = decltype(kload)::KB_PER_WAVE;
+        const i32x4 krs = kload.plan(has_next ? kv_nxt : a.KV_LEN, a.KV_LEN);
+        const i32x4 vrs = vload.plan(has_next ? kv_nxt : a.KV_LEN, a.KV_LEN);
+        auto dma = [&](int i) {
+          if (i < KPW) kload.issue_one(krs, k_lds[nb], i);
+          else vload.issue_one(vrs, v_lds[nb], i - KPW);
+        };
+        step<D, MASK, SCORE, M, 2 * KPW>(o, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
+                                (MASK == MASK_DOCUMENT) ? docbuf + cur * NK : nullptr, a, ln, dma);
         kv0 = kv_nxt;
         ++g;
         wait_loads_and_sync();
@@ -529,49 +563,56 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void fwd_bf16_kernel(FwdArgs a)
   }
 }
 
-template <int D, int MASK, int SCORE>
+template <int D, int MASK, int SCORE, int HEADS>
 hipError_t launch_one(const FwdArgs& args, int grid, hipStream_t stream) {
   const int lds = 4 * ((args.bm.NKB + 3) & ~3);
   static int attr_bytes = 0;
   if (lds > attr_bytes) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&fwd_bf16_kernel<D, MASK, SCORE>),
+        reinterpret_cast<const void*>(&fwd_bf16_kernel<D, MASK, SCORE, HEADS>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_bytes = lds;
   }
-  fwd_bf16_kernel<D, MASK, SCORE><<<grid, kThreads, lds, stream>>>(args);
+  fwd_bf16_kernel<D, MASK, SCORE, HEADS><<<grid, 64 * kWavesPerHead * HEADS, lds, stream>>>(args);
   return hipGetLastError();
 }
 
-template <int D, int MASK>
+template <int D, int MASK, int HEADS>
 hipError_t dispatch_score(const FwdArgs& args, int score, int grid, hipStream_t stream) {
   switch (score) {
     case SCORE_NONE:
-      return launch_one<D, MASK, SCORE_NONE>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_NONE, HEADS>(args, grid, stream);
     case SCORE_ALIBI:
-      return launch_one<D, MASK, SCORE_ALIBI>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_ALIBI, HEADS>(args, grid, stream);
     case SCORE_SOFTCAP:
-      return launch_one<D, MASK, SCORE_SOFTCAP>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_SOFTCAP, HEADS>(args, grid, stream);
     case SCORE_SOFTCAP_ALIBI:
-      return launch_one<D, MASK, SCORE_SOFTCAP_ALIBI>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_SOFTCAP_ALIBI, HEADS>(args, grid, stream);
     default:
-      return launch_one<D, MASK, SCORE_SCALED>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_SCALED, HEADS>(args, grid, stream);
+  }
+}
+
+template <int D, int HEADS>
+hipError_t dispatch_mask(const FwdArgs& args, int mask, int score, int grid, hipStream_t stream) {
+  switch (mask) {
+    case MASK_NOOP:
+      return dispatch_score<D, MASK_NOOP, HEADS>(args, score, grid, stream);
+    case MASK_CAUSAL:
+      return dispatch_score<D, MASK_CAUSAL, HEADS>(args, score, grid, stream);
+    case MASK_SLIDING_SINK:
+      return dispatch_score<D, MASK_SLIDING_SINK, HEADS>(args, score, grid, stream);
+    default:
+      return dispatch_score<D, MASK_DOCUMENT, HEADS>(args, score, grid, stream);
   }
 }
 
 template <int D>
-hipError_t dispatch_mask(const FwdArgs& args, int mask, int score, int grid, hipStream_t stream) {
-  switch (mask) {
-    case MASK_NOOP:
-      return dispatch_score<D, MASK_NOOP>(args, score, grid, stream);
-    case MASK_CAUSAL:
-      return dispatch_score<D, MASK_CAUSAL>(args, score, grid, stream);
-    case MASK_SLIDING_SINK:
-      return dispatch_score<D, MASK_SLIDING_SINK>(args, score, grid, stream);
-    default:
-      return dispatch_score<D, MASK_DOCUMENT>(args, score, grid, stream);
-  }
+hipError_t dispatch_heads(const FwdArgs& args, int heads, int mask, int score, int grid,
+                          hipStream_t stream) {
+  if (heads == 2) return dispatch_mask<D, 2>(args, mask, score, grid, stream);
+  return dispatch_mask<D, 1>(args, mask, score, grid, stream);
 }
 
 }  // namespace
@@ -605,17 +646,28 @@ hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream) {
   a.cap2 = L.softcap * kLog2e;
   a.slopes = L.slopes;
   a.bm = L.bm;
+  // Two query heads per workgroup are possible when they share a KV head and
+  // a BlockMask row (mask broadcast over heads, even GQA group); one head per
+  // workgroup is the default, FLEXATTN_BF16_HEADS=2 selects the pairs (only
+  // where they apply).
+  const bool pair_ok = L.bm.Hm == 1 && a.G % 2 == 0;
+  int heads = 1;  // measured: two 4-wave workgroups per CU beat one 8-wave one
+  if (const char* env = getenv("FLEXATTN_BF16_HEADS")) {
+    if (env[0] == '1') heads = 1;
+    if (env[0] == '2' && pair_ok) heads = 2;
+  }
   // XCD-aware order: with the mask broadcast over batch and heads every
-  // schedule round holds the B*Hq rows of one query tile; split each round
-  // into 8 contiguous chunks of whole KV groups, one per XCD.
-  const int R = L.B * L.Hq;
-  a.xcd_round = (L.bm.Bm == 1 && L.bm.Hm == 1 && R % 8 == 0 && (R / 8) % a.G == 0) ? R : 0;
-  const int grid = L.B * L.Hq * L.bm.NQB;
+  // schedule round holds the B*Hq/heads items of one query tile; split each
+  // round into 8 contiguous chunks of whole KV groups, one per XCD.
+  const int R = L.B * L.Hq / heads;
+  const int g_items = a.G / heads;  // items per KV group
+  a.xcd_round = (L.bm.Bm == 1 && L.bm.Hm == 1 && R % 8 == 0 && (R / 8) % g_items == 0) ? R : 0;
+  const int grid = R * L.bm.NQB;
   if (grid == 0) return hipSuccess;
   // the unscaled fast path takes the row max before scaling: scale must be > 0
   const int score = (L.score_kind == SCORE_NONE && !(L.scale > 0.0f)) ? SCORE_SCALED : L.score_kind;
-  if (L.D == 128) return dispatch_mask<128>(a, L.mask_kind, score, grid, stream);
-  return dispatch_mask<64>(a, L.mask_kind, score, grid, stream);
+  if (L.D == 128) return dispatch_heads<128>(a, heads, L.mask_kind, score, grid, stream);
+  return dispatch_heads<64>(a, heads, L.mask_kind, score, grid, stream);
 }
 
 }  // namespace fa

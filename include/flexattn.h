@@ -202,6 +202,12 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
  * throughout. BF16 limits (FLEXATTN_ERR_UNSUPPORTED beyond them): k and v
  * row strides (stride[2]) at most 2^22 elements, and the per-row tile list
  * (num_kv_blocks ints) must fit in LDS beside the K/V staging buffers.
+ * Work split (bf16): one query head per workgroup by default; the
+ * environment variable FLEXATTN_BF16_HEADS=2 (read at each call) puts the
+ * two query heads of one KV group in one workgroup (halving K/V loads)
+ * where the BlockMask is broadcast over heads and the GQA group size is
+ * even; =1 forces the default. Results do not depend on it beyond
+ * floating-point summation order.
  * Asynchronous on `stream`.
  */
 flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,

@@ -129,6 +129,10 @@ def _fwd(L, q=None, k=None, v=None, o=None, bm=None, score=0, sp=None, scale=0.1
     (dict(score=9), lib._UNSUPPORTED, b"score_kind"),
     (dict(score=2, sp=lib._ScoreParams(0.0, None)), lib._INVALID, b"softcap"),
     (dict(score=3, sp=lib._ScoreParams(float("inf"), None)), lib._INVALID, b"softcap"),
+    # bf16 k/v rows more than 2^22 elements apart (a [B][L][H][D] view with H*D > 2^22)
+    (dict(k=_tensor(strides=(256 * (1 << 22 + 3), 64, (1 << 22) + 64, 1)),
+          v=_tensor(strides=(256 * (1 << 22 + 3), 64, (1 << 22) + 64, 1))),
+     lib._UNSUPPORTED, b"row stride"),
 ])
 def test_fwd_rejects_bad_arguments(L, case, expect, msg):
     assert _fwd(L, **case) == expect

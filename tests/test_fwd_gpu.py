@@ -44,11 +44,17 @@ def check_full(lib, w, B_mask=1, H_mask=1):
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal"])
 @pytest.mark.parametrize("score", ["none", "alibi", "softcap", "softcap_alibi"])
-def test_fwd_tiny_grid(lib, dtype, D, mask, score):
+@pytest.mark.parametrize("heads", ["auto", "2"])
+def test_fwd_tiny_grid(lib, dtype, D, mask, score, heads, monkeypatch):
     """Every dtype x head dim x mask x score kind, with GQA, 3 query tiles and a
     ragged tail (300 = 2*128 + 44). bf16 softcap cases scale the inputs by 2
     (cap 20); fp32 cases keep unit-variance inputs, where the 1e-5 bound is
-    stated, and use cap 2 so tanh is far from linear."""
+    stated, and use cap 2 so tanh is far from linear. heads="2" runs the bf16
+    kernel with the two query heads of a KV group in one workgroup."""
+    if heads == "2":
+        if dtype == "f32":
+            pytest.skip("the head-pair workgroup is a bf16 kernel variant")
+        monkeypatch.setenv("FLEXATTN_BF16_HEADS", "2")
     if dtype == "f32":
         w = tiny(dtype, D, mask, score, softcap=2.0)
     else:
@@ -57,10 +63,28 @@ def test_fwd_tiny_grid(lib, dtype, D, mask, score):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [-0.125, 0.0])
+@pytest.mark.parametrize("mask", ["causal", "sliding_sink"])
+def test_fwd_nonpositive_scale(lib, dtype, scale, mask):
+    """scale <= 0 is a plain multiplier on q.k (page "tensorplay.nn.attention
+    API", flex_attention's scale argument); the bf16 fast path takes the row
+    max before scaling, so these scales go through the scaled-score path."""
+    w = tiny(dtype, 128, mask, "none", B=1, Hq=2, Hkv=1)
+    w = w.with_(extra={"scale": scale})
+    check_full(lib, w)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("q_len,kv_len", [(1, 1), (1, 200), (200, 1), (129, 257), (257, 129),
                                           (128, 128), (513, 200)])
 def test_fwd_ragged_lengths(lib, dtype, q_len, kv_len):
     check_full(lib, tiny(dtype, 64, "causal", "none", Q_LEN=q_len, KV_LEN=kv_len, B=1, Hq=2))
+
+
+@pytest.mark.parametrize("q_len,kv_len", [(1, 200), (200, 1), (129, 257), (513, 200)])
+def test_fwd_ragged_lengths_head_pairs(lib, q_len, kv_len, monkeypatch):
+    monkeypatch.setenv("FLEXATTN_BF16_HEADS", "2")
+    check_full(lib, tiny("bf16", 128, "causal", "none", Q_LEN=q_len, KV_LEN=kv_len, B=2, Hq=4))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -58,8 +58,8 @@ class Workload:
 
     @property
     def scale(self) -> float:
-        # 1/sqrt(D) for every workload.
-        return float(1.0 / np.sqrt(self.D))
+        # 1/sqrt(D) unless a test sets extra["scale"].
+        return float(self.extra.get("scale", 1.0 / np.sqrt(self.D)))
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)

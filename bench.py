@@ -99,6 +99,9 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed steps for this long before the warmup steps (clock settling)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 5 plain device copies of MIB MiB "
+                         "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the forward shards by "
@@ -112,6 +115,15 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+        return 0
     fa.load_library()
     w = W.BY_NAME[args.workload]
     inp = W.generate(w)

@@ -243,7 +243,8 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
       bm->B != q->B)
     return fail(FLEXATTN_ERR_INVALID_ARG,
                 "%s: per-batch doc_ids need a BlockMask built per batch (B=%d)", who, q->B);
-  if ((long long)q->B * q->H * bm->num_q_blocks > 0x7fffffffLL)
+  // the fp32 kernel launches four workgroups per query tile
+  if ((long long)q->B * q->H * bm->num_q_blocks * 4 > 0x7fffffffLL)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: too many query tiles for one launch", who);
   if ((int)score_kind < FLEXATTN_SCORE_NONE || (int)score_kind > FLEXATTN_SCORE_SOFTCAP_ALIBI)
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: score_kind %d is not a supported kind", who,

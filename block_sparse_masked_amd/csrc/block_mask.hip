@@ -31,6 +31,7 @@ struct BuildArgs {
   int kind;
   MaskParams mp;
   int doc_len;
+  const int* sorted_flags;  // document kind: per-chunk sortedness (schedule buffer)
   int Bm, Hm, Q_LEN, KV_LEN, NQB, NKB;
   int* kv_num;
   int* kv_idx;
@@ -79,13 +80,6 @@ __device__ __forceinline__ int block_incl_max128(int v, int* lds2) {
   return v;
 }
 
-// Does doc[0..n) never decrease? Block-wide answer.
-__device__ bool doc_is_sorted(const int* doc, int n) {
-  int bad = 0;
-  for (int i = threadIdx.x; i + 1 < n; i += blockDim.x) bad |= (doc[i] > doc[i + 1]);
-  return __syncthreads_or(bad) == 0;
-}
-
 // First index of the run containing position q0 in a non-decreasing doc row:
 // the smallest i with doc[i] == doc[q0]. Two rounds of a 128-way parallel
 // search over [0, q0].
@@ -122,32 +116,70 @@ __device__ int run_start_of(const int* doc, int q0, int* lds) {
   return res;
 }
 
+// Sortedness of the document ids, in NQB chunks per document row: workgroup
+// (r, c) checks that doc row r never decreases across positions
+// [c * chunk, (c + 1) * chunk] and writes 1 (sorted) or 0 to flags[r * NQB + c].
+// The flags live in the schedule buffer, which the schedule kernel overwrites
+// after the classify kernel has read them.
+__global__ __launch_bounds__(256) void doc_sorted_kernel(const int* doc, long long bstride, int n,
+                                                         int chunk, int nqb, int* flags) {
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int* row = doc + r * bstride;
+  const int lo = c * chunk;
+  const int hi = min(n - 1, lo + chunk);  // last pair checked: (hi - 1, hi)
+  int bad = 0;
+  for (int i = lo + threadIdx.x; i < hi; i += 256) bad |= (row[i] > row[i + 1]);
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) flags[r * nqb + c] = bad ? 0 : 1;
+}
+
+// Adds the allowed count of the key interval [lo, hi] of one query row to the
+// per-tile totals: the two end tiles directly, the tiles in between (every
+// key allowed) through the difference array `dif` (prefix-summed later).
+__device__ __forceinline__ void add_interval(int* tot, int* dif, int lo, int hi, int sign) {
+  if (hi < lo) return;
+  const int jl = lo / kBlock, jh = hi / kBlock;
+  if (jl == jh) {
+    atomicAdd(&tot[jl], sign * (hi - lo + 1));
+    return;
+  }
+  atomicAdd(&tot[jl], sign * ((jl + 1) * kBlock - lo));
+  atomicAdd(&tot[jh], sign * (hi - jh * kBlock + 1));
+  if (jh > jl + 1) {
+    atomicAdd(&dif[jl + 1], sign * kBlock);
+    atomicAdd(&dif[jh], -sign * kBlock);
+  }
+}
+
 template <int KIND>
 __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
-  extern __shared__ int smem[];  // [2][NKB] per-wave partial counts, then class flags
+  extern __shared__ int smem[];  // tot[NKB], dif[NKB + 1]
   __shared__ int scratch[4];
   const int row = blockIdx.x;  // (bm * Hm + hm) * NQB + qb
   const int qb = row % a.NQB;
   const int bm = row / (a.NQB * a.Hm);
   const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
   const int q = qb * kBlock + t;
   const bool qvalid = q < a.Q_LEN;
   const int NKB = a.NKB;
-  int* wsum = smem;  // [2][NKB]
+  int* tot = smem;
+  int* dif = smem + NKB;
+  for (int j = t; j < 2 * NKB + 1; j += kRowThreads) smem[j] = 0;
 
   // Per-row allowed intervals: I1 = [lo1, hi1], I2 = [lo2, hi2] (may be empty).
   int lo1 = 0, hi1 = -1, lo2 = 0, hi2 = -1;
   bool brute = false;
   const int* doc = nullptr;
   if constexpr (KIND == MASK_DOCUMENT) {
-    doc = a.mp.doc + (long long)bm * a.mp.doc_bstride;
-    const int n = max(a.Q_LEN, a.KV_LEN);
-    const bool sorted = doc_is_sorted(doc, n);
+    const int drow = a.mp.doc_bstride > 0 ? bm : 0;
+    doc = a.mp.doc + (long long)drow * a.mp.doc_bstride;
+    // sorted unless a chunk flag of this document row says otherwise
+    int bad = 0;
+    for (int c = t; c < a.NQB; c += kRowThreads) bad |= (a.sorted_flags[drow * a.NQB + c] == 0);
+    const bool sorted = __syncthreads_or(bad) == 0;
     if (sorted) {
       const int q0 = qb * kBlock;
-      const int s0 = run_start_of(doc, q0, scratch);
+      const int s0 = run_start_of(doc, min(q0, a.doc_len - 1), scratch);
       // run boundaries inside this tile, then the latest boundary <= q
       int bnd = (qvalid && q > q0 && doc[q] != doc[q - 1]) ? q : -1;
       bnd = block_incl_max128(bnd, scratch);
@@ -171,55 +203,56 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
   }
   hi1 = min(hi1, a.KV_LEN - 1);
   hi2 = min(hi2, a.KV_LEN - 1);
+  __syncthreads();  // totals zeroed
 
-  for (int j = 0; j < NKB; ++j) {
-    const int c0 = j * kBlock;
-    const int c1 = min(c0 + kBlock - 1, a.KV_LEN - 1);
-    int cnt = 0;
-    if (qvalid) {
-      if constexpr (KIND == MASK_DOCUMENT) {
-        if (brute) {
-          const int dq = doc[q];
-          const int e = min(c1, q);
-          for (int kv = c0; kv <= e; ++kv) cnt += (doc[kv] == dq);
-        } else {
-          cnt = clamp_len(max(lo1, c0), min(hi1, c1));
-        }
-      } else {
-        cnt = clamp_len(max(lo1, c0), min(hi1, c1));
-        if constexpr (KIND == MASK_SLIDING_SINK) {
-          // |I1 u I2| = |I1| + |I2| - |I1 n I2|, each clipped to the tile
-          cnt += clamp_len(max(lo2, c0), min(hi2, c1));
-          cnt -= clamp_len(max(max(lo1, lo2), c0), min(min(hi1, hi2), c1));
-        }
+  if (qvalid) {
+    if (KIND == MASK_DOCUMENT && brute) {
+      // unsorted ids: compare every key <= q with this row's id
+      const int dq = doc[q];
+      const int e = min(q, a.KV_LEN - 1);
+      for (int j = 0; j * kBlock <= e; ++j) {
+        int cnt = 0;
+        const int c1 = min(j * kBlock + kBlock - 1, e);
+        for (int kv = j * kBlock; kv <= c1; ++kv) cnt += (doc[kv] == dq);
+        if (cnt) atomicAdd(&tot[j], cnt);
+      }
+    } else {
+      add_interval(tot, dif, lo1, hi1, 1);
+      if constexpr (KIND == MASK_SLIDING_SINK) {
+        // |I1 u I2| = |I1| + |I2| - |I1 n I2|
+        add_interval(tot, dif, lo2, hi2, 1);
+        add_interval(tot, dif, max(lo1, lo2), min(hi1, hi2), -1);
       }
     }
-    cnt = wave_sum(cnt);
-    if (lane == 0) wsum[wave * NKB + j] = cnt;
   }
   __syncthreads();
 
-  // Classify and compact in chunks of 128 tiles, keeping ascending order.
+  // Totals (difference array prefix-summed in chunks of 128 tiles), then
+  // classify and compact, keeping ascending order.
   const long long base = (long long)row * NKB;
-  int np_total = 0, nf_total = 0;
+  int np_total = 0, nf_total = 0, run = 0;
   for (int j0 = 0; j0 < NKB; j0 += kRowThreads) {
     const int j = j0 + t;
+    const int d = j < NKB ? dif[j] : 0;
+    const int incD = block_incl_scan128(d, scratch);
     int isP = 0, isF = 0;
     if (j < NKB) {
-      const int tot = wsum[j] + wsum[NKB + j];
-      isF = (tot == kBlock * kBlock);
-      isP = (tot > 0 && !isF);
+      const int cnt = tot[j] + run + incD;
+      isF = (cnt == kBlock * kBlock);
+      isP = (cnt > 0 && !isF);
     }
     const int incP = block_incl_scan128(isP, scratch);
     const int incF = block_incl_scan128(isF, scratch);
     if (isP) a.kv_idx[base + np_total + incP - 1] = j;
     if (isF) a.full_idx[base + nf_total + incF - 1] = j;
-    // totals of this chunk live in the last thread
+    // chunk totals live in the last thread
     if (t == kRowThreads - 1) {
+      scratch[0] = incD;
       scratch[2] = incP;
       scratch[3] = incF;
     }
     __syncthreads();
+    run += scratch[0];
     np_total += scratch[2];
     nf_total += scratch[3];
     __syncthreads();
@@ -236,17 +269,44 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
 }
 
 // Stable ordering of rows by descending tile count (ties: ascending row id),
-// one workgroup: histogram, suffix offsets, then a stable scatter in chunks.
+// one workgroup: histogram, suffix offsets (block scan), then a stable
+// scatter in chunks of 1024 rows.
 constexpr int kSchedThreads = 1024;
+
+// Exclusive prefix sum over the 1024 threads of the block.
+__device__ __forceinline__ int block_excl_scan1024(int v, int* lds16) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(x, off, 64);
+    if (lane >= off) x += u;
+  }
+  if (lane == 63) lds16[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? lds16[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int u = __shfl_up(w, off, 64);
+      if (lane >= off) w += u;
+    }
+    if (lane < 16) lds16[lane] = w;  // inclusive wave totals
+  }
+  __syncthreads();
+  const int before = wave > 0 ? lds16[wave - 1] : 0;
+  __syncthreads();
+  return before + x - v;
+}
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int* kv_num,
                                                                  const int* full_num, int n,
                                                                  int nbins, int* schedule) {
   extern __shared__ int sm[];
-  int* hist = sm;             // [nbins]  -> suffix offsets
+  int* hist = sm;             // [nbins]  -> bin offsets
   int* running = sm + nbins;  // [nbins]
-  __shared__ int keys[kSchedThreads];
-  __shared__ int part[kSchedThreads];
+  __shared__ __attribute__((aligned(16))) int keys[kSchedThreads];
+  __shared__ int wtot[16];
   const int t = threadIdx.x;
   for (int c = t; c < nbins; c += kSchedThreads) {
     hist[c] = 0;
@@ -255,30 +315,18 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int* kv_n
   __syncthreads();
   for (int i = t; i < n; i += kSchedThreads) atomicAdd(&hist[kv_num[i] + full_num[i]], 1);
   __syncthreads();
-  // offsets for descending keys: off[c] = sum_{c' > c} hist[c'].
-  // Each thread owns a contiguous segment of bins, scanned from the top.
+  // offsets for descending keys: off[c] = sum_{c' > c} hist[c']. Thread t owns
+  // the contiguous bins (hi_bin - seg, hi_bin], scanned from the top.
   const int seg = (nbins + kSchedThreads - 1) / kSchedThreads;
-  const int hi_bin = nbins - 1 - t * seg;  // segment covers bins (hi_bin - seg, hi_bin]
+  const int hi_bin = nbins - 1 - t * seg;
   int local = 0;
-  for (int s = 0; s < seg; ++s) {
-    const int c = hi_bin - s;
+  for (int s2 = 0; s2 < seg; ++s2) {
+    const int c = hi_bin - s2;
     if (c >= 0) local += hist[c];
   }
-  part[t] = local;
-  __syncthreads();
-  // exclusive prefix over segments (segment order = descending bins)
-  if (t == 0) {
-    int acc = 0;
-    for (int i = 0; i < kSchedThreads; ++i) {
-      const int v = part[i];
-      part[i] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
-  int acc = part[t];
-  for (int s = 0; s < seg; ++s) {
-    const int c = hi_bin - s;
+  int acc = block_excl_scan1024(local, wtot);
+  for (int s2 = 0; s2 < seg; ++s2) {
+    const int c = hi_bin - s2;
     if (c >= 0) {
       const int h = hist[c];
       hist[c] = acc;  // becomes the offset of bin c
@@ -292,8 +340,14 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int* kv_n
     keys[t] = key;
     __syncthreads();
     if (i < n) {
+      // equal keys earlier in this chunk, four at a time
       int rank = 0;
-      for (int u = 0; u < t; ++u) rank += (keys[u] == key);
+      const int4* k4 = reinterpret_cast<const int4*>(keys);
+      for (int u = 0; u < t / 4; ++u) {
+        const int4 kk = k4[u];
+        rank += (kk.x == key) + (kk.y == key) + (kk.z == key) + (kk.w == key);
+      }
+      for (int u = t & ~3; u < t; ++u) rank += (keys[u] == key);
       schedule[hist[key] + running[key] + rank] = i;
     }
     __syncthreads();
@@ -305,7 +359,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int* kv_n
 }  // namespace
 
 int max_build_kv_blocks() {
-  // [2][NKB] ints of dynamic LDS for the classify kernel, two int arrays of
+  // 2*NKB+1 ints of dynamic LDS for the classify kernel, two int arrays of
   // NKB+1 bins for the schedule kernel; stay well inside 64 KiB.
   return 4096;
 }
@@ -315,6 +369,7 @@ hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
   a.kind = L.kind;
   a.mp = L.mp;
   a.doc_len = L.doc_len;
+  a.sorted_flags = L.schedule;
   a.Bm = L.Bm;
   a.Hm = L.Hm;
   a.Q_LEN = L.Q_LEN;
@@ -326,7 +381,7 @@ hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
   a.full_num = L.full_num;
   a.full_idx = L.full_idx;
   const int rows = L.Bm * L.Hm * L.NQB;
-  const size_t lds = sizeof(int) * 2 * (size_t)L.NKB;
+  const size_t lds = sizeof(int) * (2 * (size_t)L.NKB + 1);
   switch (L.kind) {
     case MASK_NOOP:
       classify_kernel<MASK_NOOP><<<rows, kRowThreads, lds, stream>>>(a);
@@ -337,9 +392,18 @@ hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
     case MASK_SLIDING_SINK:
       classify_kernel<MASK_SLIDING_SINK><<<rows, kRowThreads, lds, stream>>>(a);
       break;
-    default:
+    default: {
+      // sortedness flags of each document row (1 or Bm rows) in NQB chunks
+      const int drows = L.mp.doc_bstride > 0 ? L.Bm : 1;
+      const int n = L.Q_LEN > L.KV_LEN ? L.Q_LEN : L.KV_LEN;
+      const int chunk = (n + L.NQB - 1) / L.NQB;
+      doc_sorted_kernel<<<dim3(L.NQB, drows), 256, 0, stream>>>(L.mp.doc, L.mp.doc_bstride, n,
+                                                               chunk, L.NQB, L.schedule);
+      hipError_t e0 = hipGetLastError();
+      if (e0 != hipSuccess) return e0;
       classify_kernel<MASK_DOCUMENT><<<rows, kRowThreads, lds, stream>>>(a);
       break;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -445,9 +445,12 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
 
   const long long lrow = (long long)it.mrow * a.bm.NKB;
   // counts are clamped to the list length so a malformed BlockMask cannot
-  // index past the staged list
-  const int nfull = min(a.bm.full_num[it.mrow], a.bm.NKB);
-  const int n = min(nfull + a.bm.kv_num[it.mrow], a.bm.NKB);
+  // index past the staged list; the first entry of each list is read with
+  // the counts, so the first step's loads need not wait for the staging
+  const int nfull = __builtin_amdgcn_readfirstlane(min(a.bm.full_num[it.mrow], a.bm.NKB));
+  const int n = __builtin_amdgcn_readfirstlane(min(nfull + a.bm.kv_num[it.mrow], a.bm.NKB));
+  const int first_full = a.bm.full_idx[lrow];
+  const int first_part = a.bm.kv_idx[lrow];
   // the item's tiles, full then partial, staged in LDS once
   for (int t = threadIdx.x; t < n; t += THREADS)
     tlist[t] = t < nfull ? a.bm.full_idx[lrow + t] : a.bm.kv_idx[lrow + (t - nfull)];
@@ -474,16 +477,14 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
   float m_ref = -INFINITY;
   float l = 0.0f;
 
-  __syncthreads();  // tile list visible
   if (n > 0) {
     // tile indices are clamped into [0, NKB): a malformed BlockMask computes
     // garbage but never reads outside the KV tensors
-    auto tile_kv0 = [&](int t) {
-      const int idx = __builtin_amdgcn_readfirstlane(tlist[t]);
-      return kBlock * min(max(idx, 0), a.bm.NKB - 1);
-    };
-    // prologue: step 0 -> buffer 0, Q^T fragments
-    int kv0 = tile_kv0(0);
+    auto clamp_kv0 = [&](int idx) { return kBlock * min(max(idx, 0), a.bm.NKB - 1); };
+    auto tile_kv0 = [&](int t) { return clamp_kv0(__builtin_amdgcn_readfirstlane(tlist[t])); };
+    // prologue: step 0 -> buffer 0, Q^T fragments; then the tile list is
+    // visible (barrier in wait_loads_and_sync)
+    int kv0 = clamp_kv0(__builtin_amdgcn_readfirstlane(nfull > 0 ? first_full : first_part));
     issue_doc(0, kv0);
     kload.issue(kv0, a.KV_LEN, k_lds[0]);
     vload.issue(kv0, a.KV_LEN, v_lds[0]);

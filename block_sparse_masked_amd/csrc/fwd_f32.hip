@@ -4,8 +4,10 @@
 // Same method as the bf16 forward (page "tensorplay.nn.attention API",
 // BlockMask "Details" items 1-2: per-row tile lists, mask_mod only on partial
 // tiles; online softmax over KV tiles), with plain fp32 FMA on the vector
-// ALUs, in natural-log units with accurate tanh / exp / log. One workgroup of 256 threads per (b, h, 128-row query tile); each
-// query row is shared by a pair of threads that split the head dimension.
+// ALUs, in natural-log units with accurate tanh / exp / log. One workgroup
+// of 128 threads per 32 query rows of a (b, h, 128-row query tile) -- four
+// workgroups per tile, so small problems still spread over many CUs; each
+// query row is shared by four threads that split the head dimension.
 #include "common.hpp"
 #include "fwd_common.hpp"
 #include "launch.hpp"
@@ -14,7 +16,10 @@ namespace fa {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kTpr = 4;                        // threads per query row
+constexpr int kRowsPerWg = 32;                 // query rows per workgroup
+constexpr int kThreads = kTpr * kRowsPerWg;
+constexpr int kWgPerTile = kBlock / kRowsPerWg;
 constexpr int kChunk = 16;  // keys per online-softmax update
 constexpr int kSub = 64;    // keys staged in LDS at a time (half a tile)
 
@@ -27,6 +32,14 @@ __device__ __forceinline__ float score_natural(float s, float scale, float cap, 
   if constexpr (SCORE == SCORE_SOFTCAP || SCORE == SCORE_SOFTCAP_ALIBI) t = cap * tanhf(t / cap);
   if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI) t = fmaf(slope, dist, t);
   return t;
+}
+
+// Sum over the four lanes of a quad (the threads of one query row), with DPP
+// quad permutations: xor 1, then xor 2.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+  return x;
 }
 
 struct F32Args {
@@ -62,15 +75,15 @@ __device__ __forceinline__ void load_tile_f32(float* lds, const float* g, long l
 
 template <int D, int MASK, int SCORE>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
-  constexpr int HD = D / 2;  // dims per thread
+  constexpr int HD = D / kTpr;  // dims per thread
   extern __shared__ float smem_f32[];
   float* sK = smem_f32;
   float* sV = smem_f32 + kSub * D;
 
-  const Item it = decode_item(blockIdx.x, a.bm, a.B, a.Hq);
+  const Item it = decode_item(blockIdx.x / kWgPerTile, a.bm, a.B, a.Hq);
   const int b = it.b, h = it.h, hk = h / a.G;
-  const int half = threadIdx.x & 1;
-  const int q = it.qb * kBlock + (threadIdx.x >> 1);
+  const int half = threadIdx.x % kTpr;  // this thread's quarter of the head dimension
+  const int q = it.qb * kBlock + (blockIdx.x % kWgPerTile) * kRowsPerWg + threadIdx.x / kTpr;
   const bool qvalid = q < a.Q_LEN;
   const int qc = qvalid ? q : a.Q_LEN - 1;
 
@@ -114,11 +127,17 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
       float x[kChunk];
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
-        const float* krow = sK + (c0 + j) * D + half * HD;
+        const float4* krow = reinterpret_cast<const float4*>(sK + (c0 + j) * D + half * HD);
         float part = 0.0f;
 #pragma unroll
-        for (int d = 0; d < HD; ++d) part = fmaf(qv[d], krow[d], part);
-        const float sdot = part + __shfl_xor(part, 1, 64);
+        for (int d4 = 0; d4 < HD / 4; ++d4) {
+          const float4 kk = krow[d4];
+          part = fmaf(qv[4 * d4], kk.x, part);
+          part = fmaf(qv[4 * d4 + 1], kk.y, part);
+          part = fmaf(qv[4 * d4 + 2], kk.z, part);
+          part = fmaf(qv[4 * d4 + 3], kk.w, part);
+        }
+        const float sdot = quad_sum(part);
         const int key = kv0 + c0 + j;
         float xv = score_natural<SCORE>(sdot, a.scale, a.softcap, slope, (float)(key - q));
         if (do_mask) {
@@ -141,9 +160,15 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
       for (int j = 0; j < kChunk; ++j) {
         const float p = expf(x[j] - m_use);
         l += p;
-        const float* vrow = sV + (c0 + j) * D + half * HD;
+        const float4* vrow = reinterpret_cast<const float4*>(sV + (c0 + j) * D + half * HD);
 #pragma unroll
-        for (int d = 0; d < HD; ++d) acc[d] = fmaf(p, vrow[d], acc[d]);
+        for (int d4 = 0; d4 < HD / 4; ++d4) {
+          const float4 vv = vrow[d4];
+          acc[4 * d4] = fmaf(p, vv.x, acc[4 * d4]);
+          acc[4 * d4 + 1] = fmaf(p, vv.y, acc[4 * d4 + 1]);
+          acc[4 * d4 + 2] = fmaf(p, vv.z, acc[4 * d4 + 2]);
+          acc[4 * d4 + 3] = fmaf(p, vv.w, acc[4 * d4 + 3]);
+        }
       }
       m = m_new;
     }
@@ -223,7 +248,7 @@ hipError_t launch_fwd_f32(const FwdLaunch& L, hipStream_t stream) {
   a.softcap = L.softcap;
   a.slopes = L.slopes;
   a.bm = L.bm;
-  const int grid = L.B * L.Hq * L.bm.NQB;
+  const int grid = L.B * L.Hq * L.bm.NQB * kWgPerTile;
   if (grid == 0) return hipSuccess;
   if (L.D == 128) return f32_dispatch_mask<128>(a, L.mask_kind, L.score_kind, grid, stream);
   return f32_dispatch_mask<64>(a, L.mask_kind, L.score_kind, grid, stream);

@@ -64,6 +64,34 @@ def algorithmic_bytes(w: W.Workload, nqb: int, nkb: int) -> int:
     return q + kv + out + lse + bm
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("fwd_bf16.hip", "common.hpp", "fwd_common.hpp")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per forward launch from the committed FETCH_SIZE/WRITE_SIZE
+    counter summary of this workload, or None when there is none or the
+    kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(HERE, "profiles", f"fwd_bf16_kernel.{workload}.counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    for name in KERNEL_SOURCES:
+        src = os.path.join(HERE, "block_sparse_masked_amd", "csrc", name)
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if fields.get(f"source_sha256_{name}") != digest:
+            return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w: W.Workload, inp: W.Inputs, budget_s: float = 20.0):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workload: whole (b, h) heads, as many as fit the time budget."""
@@ -223,7 +251,8 @@ def main(argv=None):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(fwd_tflops / peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name) if w.dtype == "bf16" else None,
+            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes": algorithmic_bytes(w, nqb, nkb),
         },
     }

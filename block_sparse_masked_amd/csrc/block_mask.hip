@@ -86,7 +86,7 @@ __device__ __forceinline__ int block_incl_max128(int v, int* lds2) {
 __device__ int run_start_of(const int* doc, int q0, int* lds) {
   const int t = threadIdx.x;
   const int key = doc[q0];
-  // Round 1: coarse grid of 128 probes over [0, q0].
+  // First pass: coarse grid of 128 probes over [0, q0].
   const int step = (q0 + kRowThreads) / kRowThreads;  // >= 1, covers [0, q0]
   int p = t * step;
   int hit = (p <= q0 && doc[p] < key) ? t : -1;  // last probe strictly before the run
@@ -99,7 +99,7 @@ __device__ int run_start_of(const int* doc, int q0, int* lds) {
   int lo, hi;
   lo = lastp * step + 1;             // first candidate after the last "before" probe
   hi = min(q0, lo + step - 1);        // the run starts within [lo, hi]
-  // Round 2: positions lo + t*r covering [lo, hi] with r = ceil(len/128).
+  // Second pass: positions lo + t*r covering [lo, hi] with r = ceil(len/128).
   const int len = hi - lo + 1;
   const int r = (len + kRowThreads - 1) / kRowThreads;
   int first = 0x7fffffff;

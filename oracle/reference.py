@@ -30,7 +30,7 @@ It is written to be checked by eye against the pages, not to be fast:
   (layout ``q [B,Hq,M,D]``, ``k/v [B,Hkv,N,D]``), and page "transformerlab",
   sections "Adding a new attention variant" and "Decode / KV cache".
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 the score passed to score_mod already carries the ``scale`` factor; softcap is
 ``c * tanh(s / c)`` applied before the ALiBi bias; a query row with no allowed
 key yields O = 0 and LSE = -inf; LSE is the natural-log log-sum-exp; KV tile

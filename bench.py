@@ -127,6 +127,9 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed steps for this long before the warmup steps (clock settling)")
+    ap.add_argument("--ablation-steps", type=int, default=20,
+                    help="after the timed steps, time this many forwards on a BlockMask built "
+                         "with separate_full_blocks=False (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB "
                          "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -207,6 +210,32 @@ def main(argv=None):
     build_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
     fwd_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
 
+    # Full-tile ablation (after the timed region, not part of `value`): the
+    # same forward on a BlockMask built with separate_full_blocks=False, so
+    # mask_mod runs on every tile (page "tensorplay.nn.attention API",
+    # BlockMask "Details": skipping the mask on full tiles is the speed-up).
+    ablation = None
+    if args.ablation_steps > 0:
+        bm_all = fa.create_block_mask(w.mask, 1, 1, w.Q_LEN, w.KV_LEN, 128, window=w.window,
+                                      num_sinks=w.sinks, doc_ids=doc, device=dev, stream=stream,
+                                      separate_full_blocks=False)
+        for _ in range(3):
+            fa.flex_attention(q, k, v, bm_all, score=w.score, softcap=w.softcap, scale=w.scale,
+                              out=out, lse=lse, stream=stream)
+        ev_a = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                for _ in range(args.ablation_steps)]
+        for i in range(args.ablation_steps):
+            ev_a[i][0].record(stream)
+            fa.flex_attention(q, k, v, bm_all, score=w.score, softcap=w.softcap, scale=w.scale,
+                              out=out, lse=lse, stream=stream)
+            ev_a[i][1].record(stream)
+        torch.cuda.synchronize()
+        all_partial_ms = float(np.median([a.elapsed_time(b) for a, b in ev_a]))
+        ablation = {"fwd_ms_median_all_partial": round(all_partial_ms, 4),
+                    "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
+                    "speedup_from_full_tiles": round(all_partial_ms / float(np.median(fwd_ms)), 4),
+                    "calls": args.ablation_steps}
+
     pairs = allowed_pairs_per_head(w, inp.doc_lengths)
     eff_flops = 4.0 * w.D * pairs * w.B * w.Hq
     dense_flops = 4.0 * w.D * w.Q_LEN * w.KV_LEN * w.B * w.Hq
@@ -238,6 +267,7 @@ def main(argv=None):
         "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "fwd_ms_avg": round(fwd_avg, 4),
         "fwd_ms_min": round(float(np.min(fwd_ms)), 4),
+        "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
         "build_ms_avg": round(float(np.mean(build_ms)), 4),
         "fwd_effective_tflops": round(fwd_tflops, 2),
         "dense_equivalent_tflops": round(dense_flops / (fwd_avg * 1e-3) / 1e12, 2),
@@ -256,6 +286,8 @@ def main(argv=None):
             "algorithmic_bytes": algorithmic_bytes(w, nqb, nkb),
         },
     }
+    if ablation is not None:
+        rec["full_tile_ablation"] = ablation
     if inp.doc_lengths is not None:
         rec["config"]["doc_lengths"] = [int(x) for x in inp.doc_lengths]
     if not args.no_cpu_baseline:

@@ -88,8 +88,8 @@ def load_library():
     lib.flexattn_create_block_mask.restype = ctypes.c_int
     lib.flexattn_create_block_mask.argtypes = [
         ctypes.c_int, ctypes.POINTER(_MaskParams), ctypes.c_int32, ctypes.c_int32,
-        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_BlockMask),
-        ctypes.c_void_p]
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.POINTER(_BlockMask), ctypes.c_void_p]
     lib.flexattn_fwd.restype = ctypes.c_int
     lib.flexattn_fwd.argtypes = [
         ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
@@ -170,9 +170,11 @@ class BlockMask:
 def create_block_mask(kind: str, B: int, H: int, Q_LEN: int, KV_LEN: int, block: int = 128,
                       window: int = 0, num_sinks: int = 0,
                       doc_ids: Optional[torch.Tensor] = None,
-                      device="cuda", stream=None) -> BlockMask:
+                      device="cuda", stream=None, separate_full_blocks: bool = True) -> BlockMask:
     """Build the BlockMask of a mask kind on the GPU (the library's builder
-    kernels). B and H may be 1 to broadcast over batch / query heads."""
+    kernels). B and H may be 1 to broadcast over batch / query heads.
+    separate_full_blocks=False lists every non-empty tile as partial, so the
+    forward applies the mask on every tile."""
     lib = load_library()
     if kind not in MASK_KINDS:
         raise NotImplementedError(f"mask kind {kind!r} is not one of {sorted(MASK_KINDS)}")
@@ -204,7 +206,8 @@ def create_block_mask(kind: str, B: int, H: int, Q_LEN: int, KV_LEN: int, block:
     c.full_kv_indices = full_idx.data_ptr()
     c.schedule = sched.data_ptr()
     st = lib.flexattn_create_block_mask(MASK_KINDS[kind], ctypes.byref(mp), B, H, Q_LEN, KV_LEN,
-                                        block, ctypes.byref(c), _stream_handle(device, stream))
+                                        block, int(bool(separate_full_blocks)), ctypes.byref(c),
+                                        _stream_handle(device, stream))
     _check(st, "flexattn_create_block_mask")
     return BlockMask(kind, B, H, Q_LEN, KV_LEN, block, kv_num, kv_idx, full_num, full_idx, sched,
                      doc_ids, c)

@@ -129,7 +129,8 @@ flexattn_status flexattn_block_mask_sizes(int32_t B, int32_t H, int32_t Q_LEN, i
 flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
                                            const flexattn_mask_params* params, int32_t B,
                                            int32_t H, int32_t Q_LEN, int32_t KV_LEN,
-                                           int32_t block, flexattn_block_mask* bm, void* stream) {
+                                           int32_t block, int32_t separate_full_blocks,
+                                           flexattn_block_mask* bm, void* stream) {
   static const char* who = "flexattn_create_block_mask";
   if (!bm) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: bm is NULL", who);
   if (B < 1 || H < 1 || Q_LEN < 1 || KV_LEN < 1)
@@ -180,6 +181,7 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
   L.full_num = bm->full_kv_num_blocks;
   L.full_idx = bm->full_kv_indices;
   L.schedule = bm->schedule;
+  L.separate_full = separate_full_blocks != 0;
   hipError_t e = fa::launch_build(L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(FLEXATTN_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));

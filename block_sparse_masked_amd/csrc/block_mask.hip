@@ -37,6 +37,7 @@ struct BuildArgs {
   int* kv_idx;
   int* full_num;
   int* full_idx;
+  int separate_full;  // 0: full tiles are listed with the partial ones
 };
 
 __device__ __forceinline__ int clamp_len(int lo, int hi) { return hi >= lo ? hi - lo + 1 : 0; }
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
     int isP = 0, isF = 0;
     if (j < NKB) {
       const int cnt = tot[j] + run + incD;
-      isF = (cnt == kBlock * kBlock);
+      isF = a.separate_full && (cnt == kBlock * kBlock);
       isP = (cnt > 0 && !isF);
     }
     const int incP = block_incl_scan128(isP, scratch);
@@ -380,6 +381,7 @@ hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
   a.kv_idx = L.kv_idx;
   a.full_num = L.full_num;
   a.full_idx = L.full_idx;
+  a.separate_full = L.separate_full;
   const int rows = L.Bm * L.Hm * L.NQB;
   const size_t lds = sizeof(int) * (2 * (size_t)L.NKB + 1);
   switch (L.kind) {

@@ -19,6 +19,7 @@ struct BuildLaunch {
   int* full_num;
   int* full_idx;
   int* schedule;
+  int separate_full;  // 0: every non-empty tile is listed as partial
 };
 
 hipError_t launch_build(const BuildLaunch& L, hipStream_t stream);

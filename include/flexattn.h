@@ -165,9 +165,13 @@ flexattn_status flexattn_block_mask_sizes(int32_t B, int32_t H, int32_t Q_LEN, i
 
 /*
  * create_block_mask (page "tensorplay.nn.attention API", section
- * create_block_mask, with separate_full_blocks=True): evaluates the mask_mod
- * of `kind` over every (b, h, q_idx, kv_idx), classifies each tile and writes
- * the four index tensors plus the schedule into the buffers `bm` points to.
+ * create_block_mask): evaluates the mask_mod of `kind` over every
+ * (b, h, q_idx, kv_idx), classifies each tile and writes the four index
+ * tensors plus the schedule into the buffers `bm` points to.
+ * separate_full_blocks != 0 lists full tiles apart from partial ones, so the
+ * forward skips mask_mod on them; 0 lists every non-empty tile as partial
+ * (full counts 0, full lists all 0) and mask_mod then runs on every tile, as
+ * that page's create_block_mask parameter of the same name describes.
  * B and H give the extents to build (1 = one build broadcast over that
  * dimension; the enumerated kinds do not depend on b or h except through
  * per-batch doc_ids). On input the caller sets bm->kv_num_blocks,
@@ -177,7 +181,8 @@ flexattn_status flexattn_block_mask_sizes(int32_t B, int32_t H, int32_t Q_LEN, i
 flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
                                            const flexattn_mask_params* params, int32_t B,
                                            int32_t H, int32_t Q_LEN, int32_t KV_LEN,
-                                           int32_t block, flexattn_block_mask* bm, void* stream);
+                                           int32_t block, int32_t separate_full_blocks,
+                                           flexattn_block_mask* bm, void* stream);
 
 /*
  * The block-sparse attention forward (page "tensorplay.nn.attention API",

@@ -229,14 +229,16 @@ def classify_tiles(counts: np.ndarray, q_len: int, kv_len: int, block: int):
 
 
 def create_block_mask(mask_mod: MaskMod, B: int, H: int, Q_LEN: int, KV_LEN: int,
-                      BLOCK_SIZE: int = 128) -> BlockMask:
+                      BLOCK_SIZE: int = 128, separate_full_blocks: bool = True) -> BlockMask:
     """Reduce the element mask to block x block tiles and list them.
 
     For each (b, h, q-tile) the element mask rows of that tile are evaluated
     over every key, allowed elements are counted per KV tile, and the tile is
-    empty (count 0), full (count block^2) or partial. Partial tiles go to
-    ``kv_*`` and full tiles to ``full_kv_*`` (separate_full_blocks=True), each
-    as a count plus an ascending index list.
+    empty (count 0), full (count block^2) or partial. With
+    separate_full_blocks=True partial tiles go to ``kv_*`` and full tiles to
+    ``full_kv_*``, each as a count plus an ascending index list; with False
+    every non-empty tile is listed in ``kv_*`` and ``full_kv_*`` is empty
+    (page "tensorplay.nn.attention API", create_block_mask parameters).
     """
     blk = int(BLOCK_SIZE)
     nqb = -(-Q_LEN // blk)
@@ -253,6 +255,8 @@ def create_block_mask(mask_mod: MaskMod, B: int, H: int, Q_LEN: int, KV_LEN: int
                 padded[:KV_LEN] = per_col
                 counts[b, h, i] = padded.reshape(nkb, blk).sum(axis=1)
     cls = classify_tiles(counts, Q_LEN, KV_LEN, blk)
+    if not separate_full_blocks:
+        cls = np.where(cls == 0, 0, 1).astype(np.int8)
     kv_num = np.zeros((B, H, nqb), dtype=np.int32)
     kv_ind = np.zeros((B, H, nqb, nkb), dtype=np.int32)
     full_num = np.zeros((B, H, nqb), dtype=np.int32)

@@ -19,12 +19,14 @@ def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     return t.to(device)
 
 
-def build_gpu_mask(lib, w: W.Workload, inputs: W.Inputs, B_mask=1, H_mask=1):
+def build_gpu_mask(lib, w: W.Workload, inputs: W.Inputs, B_mask=1, H_mask=1,
+                   separate_full_blocks=True):
     doc = None
     if w.mask == "document_causal":
         doc = torch.from_numpy(inputs.doc_ids.astype(np.int32))
     return lib.create_block_mask(w.mask, B_mask, H_mask, w.Q_LEN, w.KV_LEN, 128,
-                                 window=w.window, num_sinks=w.sinks, doc_ids=doc)
+                                 window=w.window, num_sinks=w.sinks, doc_ids=doc,
+                                 separate_full_blocks=separate_full_blocks)
 
 
 def run_gpu(lib, w: W.Workload, inputs: W.Inputs, bm=None):

@@ -62,7 +62,7 @@ def _bm_struct(ptr=16):
 def _create(L, kind, params, B=1, H=1, Q=256, K=256, block=128, bm=None):
     bm = _bm_struct() if bm is None else bm
     p = ctypes.byref(params) if params is not None else None
-    return L.flexattn_create_block_mask(kind, p, B, H, Q, K, block, ctypes.byref(bm), None)
+    return L.flexattn_create_block_mask(kind, p, B, H, Q, K, block, 1, ctypes.byref(bm), None)
 
 
 def test_create_block_mask_rejects_bad_arguments(L):
@@ -72,7 +72,7 @@ def test_create_block_mask_rejects_bad_arguments(L):
     assert _create(L, 1, mp, block=64) == lib._UNSUPPORTED
     assert _create(L, 1, mp, Q=0) == lib._INVALID
     assert _create(L, 1, mp, bm=_bm_struct(ptr=0)) == lib._INVALID
-    assert L.flexattn_create_block_mask(1, None, 1, 1, 256, 256, 128, None, None) == lib._INVALID
+    assert L.flexattn_create_block_mask(1, None, 1, 1, 256, 256, 128, 1, None, None) == lib._INVALID
     # sliding window needs window >= 1 and sinks >= 0
     assert _create(L, 2, lib._MaskParams(0, 0, None, 0, 0)) == lib._INVALID
     assert b"window" in L.flexattn_last_error()

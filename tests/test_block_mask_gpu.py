@@ -59,6 +59,29 @@ def test_builder_tiny_grid(lib, q_len, kv_len, kind, window, sinks):
     check(bm, ref)
 
 
+@pytest.mark.parametrize("q_len,kv_len", [(1, 1), (129, 129), (300, 255), (512, 512), (700, 1)])
+@pytest.mark.parametrize("kind,window,sinks", [
+    ("noop", 0, 0), ("causal", 0, 0), ("sliding_sink", 200, 130), ("document_causal", 0, 0)])
+def test_builder_unseparated(lib, q_len, kv_len, kind, window, sinks):
+    """separate_full_blocks=False: every non-empty tile in the partial lists,
+    bit-exact against the oracle built the same way."""
+    doc = doc_for(max(q_len, kv_len), seed=q_len * 5 + kv_len) if kind == "document_causal" else None
+    ref = oracle.create_block_mask(oracle.mask_mod_for(kind, window, sinks, doc), 1, 1,
+                                   q_len, kv_len, 128, separate_full_blocks=False)
+    bm = lib.create_block_mask(kind, 1, 1, q_len, kv_len, 128, window=window, num_sinks=sinks,
+                               doc_ids=None if doc is None else torch.from_numpy(doc),
+                               separate_full_blocks=False)
+    check(bm, ref)
+
+
+def test_builder_unseparated_full_workload(lib):
+    """The dense causal workload's mask (32 x 32 tiles) without full tiles."""
+    ref = oracle.create_block_mask(oracle.causal_mask, 1, 1, 4096, 4096, 128,
+                                   separate_full_blocks=False)
+    bm = lib.create_block_mask("causal", 1, 1, 4096, 4096, 128, separate_full_blocks=False)
+    check(bm, ref)
+
+
 def test_builder_batched_heads_broadcast(lib):
     """B=2, H=3 build of a (b, h)-independent mask equals the oracle's full build."""
     ref = oracle.create_block_mask(oracle.sliding_sink_mask(150, 3), 2, 3, 600, 600, 128)

@@ -63,6 +63,22 @@ def test_fwd_tiny_grid(lib, dtype, D, mask, score, heads, monkeypatch):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal"])
+def test_fwd_unseparated_mask(lib, dtype, mask):
+    """A BlockMask built with separate_full_blocks=False (mask_mod on every
+    tile) gives the same attention as the oracle."""
+    w = tiny(dtype, 128, mask, "softcap_alibi" if dtype == "bf16" else "alibi", Q_LEN=520,
+             KV_LEN=520, value_scale=2.0 if dtype == "bf16" else 1.0)
+    inp = W.generate(w)
+    bm = G.build_gpu_mask(lib, w, inp, separate_full_blocks=False)
+    assert int(bm.full_kv_num_blocks.sum().item()) == 0
+    o, lse, _ = G.run_gpu(lib, w, inp, bm)
+    o_ref, lse_ref = G.oracle_rows(w, inp)
+    res = G.compare(w, o, lse, o_ref, lse_ref)
+    assert res["ok"], G.summary(res)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("scale", [-0.125, 0.0])
 @pytest.mark.parametrize("mask", ["causal", "sliding_sink"])
 def test_fwd_nonpositive_scale(lib, dtype, scale, mask):

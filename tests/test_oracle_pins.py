@@ -50,6 +50,26 @@ def test_block_mask_brute_force(kind, q_len, kv_len):
     assert pins.block_mask_matches(bm, pins.lists_from_classes(cls))
 
 
+@pytest.mark.parametrize("kind", list(SCALAR_MASKS))
+@pytest.mark.parametrize("q_len,kv_len", [(16, 16), (17, 33), (77, 50), (100, 100)])
+def test_block_mask_unseparated_brute_force(kind, q_len, kv_len):
+    """separate_full_blocks=False (page "tensorplay.nn.attention API",
+    create_block_mask parameters): every non-empty tile of the per-element
+    loop is listed as partial, in ascending order, and no tile as full."""
+    blk = 16
+    L = max(q_len, kv_len)
+    doc = W.document_ids([5, 1, 20, 13, 61])[:L]
+    scalar = SCALAR_MASKS[kind](doc)
+    bm = oracle.create_block_mask(_oracle_mask(kind, doc), 1, 1, q_len, kv_len, blk,
+                                  separate_full_blocks=False)
+    cls = pins.brute_force_tiles(scalar, 1, 1, q_len, kv_len, blk)
+    merged = np.where(cls == 0, 0, 1)
+    assert pins.block_mask_matches(bm, pins.lists_from_classes(merged))
+    assert int(bm.full_kv_num_blocks.sum()) == 0 and not bm.full_kv_indices.any()
+    split = oracle.create_block_mask(_oracle_mask(kind, doc), 1, 1, q_len, kv_len, blk)
+    assert np.array_equal(bm.to_dense(), split.to_dense())
+
+
 def test_block_mask_brute_force_batched_heads():
     """(b, h)-dependent mask_mod: each (b, h) gets its own lists."""
     def mod(b, h, q, kv):

@@ -25,6 +25,12 @@ from .reference import (  # noqa: F401
     unmasked_pairs,
     window_mask,
 )
+from .backward import (  # noqa: F401
+    attention_backward,
+    score_grad_for,
+    softcap_grad,
+    transpose_block_mask,
+)
 
 
 def mask_mod_for(kind: str, window: int = 0, sinks: int = 0, doc_ids=None):

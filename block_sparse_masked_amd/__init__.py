@@ -21,7 +21,8 @@ import torch
 
 __all__ = [
     "BlockMask", "FlexAttnError", "MASK_KINDS", "SCORE_KINDS", "create_block_mask",
-    "flex_attention", "library_path", "load_library", "block_mask_sizes", "version",
+    "flex_attention", "flex_attention_backward", "library_path", "load_library",
+    "block_mask_sizes", "version",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -60,7 +61,9 @@ class _BlockMask(ctypes.Structure):
                 ("kv_num_blocks", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p),
                 ("full_kv_num_blocks", ctypes.c_void_p), ("full_kv_indices", ctypes.c_void_p),
                 ("schedule", ctypes.c_void_p), ("mask_kind", ctypes.c_int),
-                ("mask_params", _MaskParams)]
+                ("mask_params", _MaskParams),
+                ("q_num_blocks", ctypes.c_void_p), ("q_indices", ctypes.c_void_p),
+                ("full_q_num_blocks", ctypes.c_void_p), ("full_q_indices", ctypes.c_void_p)]
 
 
 _lib = None
@@ -90,6 +93,13 @@ def load_library():
         ctypes.c_int, ctypes.POINTER(_MaskParams), ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.POINTER(_BlockMask), ctypes.c_void_p]
+    lib.flexattn_bwd.restype = ctypes.c_int
+    lib.flexattn_bwd.argtypes = [
+        ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+        ctypes.c_void_p, ctypes.POINTER(_Tensor),
+        ctypes.POINTER(_BlockMask), ctypes.c_int, ctypes.POINTER(_ScoreParams), ctypes.c_float,
+        ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+        ctypes.c_void_p, ctypes.c_void_p]
     lib.flexattn_fwd.restype = ctypes.c_int
     lib.flexattn_fwd.argtypes = [
         ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
@@ -147,6 +157,11 @@ class BlockMask:
     schedule: torch.Tensor            # int32 [B*H*NQB]
     doc_ids: Optional[torch.Tensor]
     _c: _BlockMask
+    # per-KV-tile query lists for the backward (built on request)
+    q_num_blocks: Optional[torch.Tensor] = None       # int32 [B, H, NKB]
+    q_indices: Optional[torch.Tensor] = None          # int32 [B, H, NKB, NQB]
+    full_q_num_blocks: Optional[torch.Tensor] = None  # int32 [B, H, NKB]
+    full_q_indices: Optional[torch.Tensor] = None     # int32 [B, H, NKB, NQB]
 
     @property
     def num_q_blocks(self) -> int:
@@ -170,11 +185,14 @@ class BlockMask:
 def create_block_mask(kind: str, B: int, H: int, Q_LEN: int, KV_LEN: int, block: int = 128,
                       window: int = 0, num_sinks: int = 0,
                       doc_ids: Optional[torch.Tensor] = None,
-                      device="cuda", stream=None, separate_full_blocks: bool = True) -> BlockMask:
+                      device="cuda", stream=None, separate_full_blocks: bool = True,
+                      backward_lists: bool = False) -> BlockMask:
     """Build the BlockMask of a mask kind on the GPU (the library's builder
     kernels). B and H may be 1 to broadcast over batch / query heads.
     separate_full_blocks=False lists every non-empty tile as partial, so the
-    forward applies the mask on every tile."""
+    forward applies the mask on every tile. backward_lists=True also builds
+    the per-KV-tile query lists (q_num_blocks, q_indices, full_q_*) that
+    flex_attention_backward needs."""
     lib = load_library()
     if kind not in MASK_KINDS:
         raise NotImplementedError(f"mask kind {kind!r} is not one of {sorted(MASK_KINDS)}")
@@ -205,12 +223,20 @@ def create_block_mask(kind: str, B: int, H: int, Q_LEN: int, KV_LEN: int, block:
     c.full_kv_num_blocks = full_num.data_ptr()
     c.full_kv_indices = full_idx.data_ptr()
     c.schedule = sched.data_ptr()
+    qlists = [None] * 4
+    if backward_lists:
+        qlists = [torch.empty((B, H, nkb), dtype=torch.int32, device=device),
+                  torch.empty((B, H, nkb, nqb), dtype=torch.int32, device=device),
+                  torch.empty((B, H, nkb), dtype=torch.int32, device=device),
+                  torch.empty((B, H, nkb, nqb), dtype=torch.int32, device=device)]
+        c.q_num_blocks, c.q_indices, c.full_q_num_blocks, c.full_q_indices = (
+            t.data_ptr() for t in qlists)
     st = lib.flexattn_create_block_mask(MASK_KINDS[kind], ctypes.byref(mp), B, H, Q_LEN, KV_LEN,
                                         block, int(bool(separate_full_blocks)), ctypes.byref(c),
                                         _stream_handle(device, stream))
     _check(st, "flexattn_create_block_mask")
     return BlockMask(kind, B, H, Q_LEN, KV_LEN, block, kv_num, kv_idx, full_num, full_idx, sched,
-                     doc_ids, c)
+                     doc_ids, c, *qlists)
 
 
 def _tensor(t: torch.Tensor, name: str) -> _Tensor:
@@ -258,3 +284,46 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask
                           _stream_handle(q.device, stream))
     _check(st, "flexattn_fwd")
     return out, lse
+
+
+def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            lse: torch.Tensor, d_out: torch.Tensor,
+                            block_mask: BlockMask, score: str = "none", softcap: float = 0.0,
+                            alibi_slopes: Optional[torch.Tensor] = None,
+                            scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
+                            dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients (dq, dk, dv) of flex_attention's output for the upstream
+    gradient d_out. bf16 tensors; lse is the forward's and the BlockMask must
+    carry the backward lists (create_block_mask(..., backward_lists=True)).
+    dk / dv sum the query heads of each KV head."""
+    lib = load_library()
+    if score not in SCORE_KINDS:
+        raise NotImplementedError(f"score kind {score!r} is not one of {sorted(SCORE_KINDS)}")
+    if block_mask.q_num_blocks is None:
+        raise ValueError("the BlockMask has no backward lists: build it with backward_lists=True")
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, Hq, M]")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if workspace.dtype != torch.float32 or workspace.numel() < q.shape[0] * q.shape[1] * q.shape[2]:
+        raise ValueError("workspace must be float32 with at least B * Hq * M elements")
+    sp = _ScoreParams(float(softcap), None)
+    if alibi_slopes is not None:
+        alibi_slopes = alibi_slopes.to(device=q.device, dtype=torch.float32).contiguous()
+        sp.alibi_slopes = alibi_slopes.data_ptr()
+    t = {n: _tensor(x, n) for n, x in (("q", q), ("k", k), ("v", v), ("d_out", d_out),
+                                       ("dq", dq), ("dk", dk), ("dv", dv))}
+    st = lib.flexattn_bwd(ctypes.byref(t["q"]), ctypes.byref(t["k"]), ctypes.byref(t["v"]),
+                          ctypes.c_void_p(lse.data_ptr()),
+                          ctypes.byref(t["d_out"]), ctypes.byref(block_mask._c),
+                          SCORE_KINDS[score], ctypes.byref(sp), float(scale),
+                          ctypes.byref(t["dq"]), ctypes.byref(t["dk"]), ctypes.byref(t["dv"]),
+                          ctypes.c_void_p(workspace.data_ptr()), _stream_handle(q.device, stream))
+    _check(st, "flexattn_bwd")
+    return dq, dk, dv

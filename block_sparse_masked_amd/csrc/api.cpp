@@ -76,25 +76,26 @@ flexattn_status check_mask(flexattn_mask_kind kind, const flexattn_mask_params* 
   return FLEXATTN_OK;
 }
 
-flexattn_status check_tensor(const flexattn_tensor* t, const char* name) {
-  if (!t) return fail(FLEXATTN_ERR_INVALID_ARG, "flexattn_fwd: %s is NULL", name);
-  if (!t->data) return fail(FLEXATTN_ERR_INVALID_ARG, "flexattn_fwd: %s->data is NULL", name);
+flexattn_status check_tensor(const flexattn_tensor* t, const char* name,
+                             const char* who = "flexattn_fwd") {
+  if (!t) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: %s is NULL", who, name);
+  if (!t->data) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: %s->data is NULL", who, name);
   if (t->dtype != FLEXATTN_F32 && t->dtype != FLEXATTN_BF16)
-    return fail(FLEXATTN_ERR_UNSUPPORTED, "flexattn_fwd: %s dtype %d is not F32 or BF16", name,
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: %s dtype %d is not F32 or BF16", who, name,
                 (int)t->dtype);
   if (t->B < 1 || t->H < 1 || t->L < 1 || t->D < 1)
-    return fail(FLEXATTN_ERR_INVALID_ARG, "flexattn_fwd: %s has a non-positive extent", name);
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: %s has a non-positive extent", who, name);
   if (t->stride[3] != 1)
-    return fail(FLEXATTN_ERR_INVALID_ARG, "flexattn_fwd: %s rows must be contiguous (stride[3]=1)",
-                name);
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: %s rows must be contiguous (stride[3]=1)",
+                who, name);
   const int es = t->dtype == FLEXATTN_F32 ? 4 : 2;
   if (!aligned16(t->data))
-    return fail(FLEXATTN_ERR_INVALID_ARG, "flexattn_fwd: %s->data is not 16-byte aligned", name);
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: %s->data is not 16-byte aligned", who, name);
   for (int i = 0; i < 3; ++i) {
     if (t->stride[i] < 0 || (t->stride[i] * es) % 16 != 0)
       return fail(FLEXATTN_ERR_INVALID_ARG,
-                  "flexattn_fwd: %s stride[%d]=%lld is negative or not a multiple of 16 bytes",
-                  name, i, (long long)t->stride[i]);
+                  "%s: %s stride[%d]=%lld is negative or not a multiple of 16 bytes",
+                  who, name, i, (long long)t->stride[i]);
   }
   return FLEXATTN_OK;
 }
@@ -147,6 +148,10 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
   if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices ||
       !bm->schedule)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: a BlockMask buffer pointer is NULL", who);
+  if (bm->q_num_blocks && bm->q_indices && bm->full_q_num_blocks && bm->full_q_indices &&
+      (long long)B * H > 65535)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: B*H=%lld above 65535 for the q_* lists", who,
+                (long long)B * H);
   fa::MaskParams mp;
   int doc_len = 0;
   flexattn_status st = check_mask(kind, params, B, Q_LEN, KV_LEN, &mp, &doc_len, who);
@@ -182,6 +187,12 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
   L.full_idx = bm->full_kv_indices;
   L.schedule = bm->schedule;
   L.separate_full = separate_full_blocks != 0;
+  const bool with_q = bm->q_num_blocks && bm->q_indices && bm->full_q_num_blocks &&
+                      bm->full_q_indices;
+  L.q_num = with_q ? bm->q_num_blocks : nullptr;
+  L.q_idx = with_q ? bm->q_indices : nullptr;
+  L.full_q_num = with_q ? bm->full_q_num_blocks : nullptr;
+  L.full_q_idx = with_q ? bm->full_q_indices : nullptr;
   hipError_t e = fa::launch_build(L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(FLEXATTN_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
@@ -306,6 +317,137 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
   hipError_t e = (q->dtype == FLEXATTN_BF16)
                      ? fa::launch_fwd_bf16(L, static_cast<hipStream_t>(stream))
                      : fa::launch_fwd_f32(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(FLEXATTN_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+flexattn_status flexattn_bwd(const flexattn_tensor* q, const flexattn_tensor* k,
+                             const flexattn_tensor* v, const float* lse,
+                             const flexattn_tensor* d_out,
+                             const flexattn_block_mask* bm, flexattn_score_kind score_kind,
+                             const flexattn_score_params* params, float scale,
+                             flexattn_tensor* dq, flexattn_tensor* dk, flexattn_tensor* dv,
+                             float* workspace, void* stream) {
+  static const char* who = "flexattn_bwd";
+  flexattn_status st;
+  const flexattn_tensor* all[7] = {q, k, v, d_out, dq, dk, dv};
+  const char* names[7] = {"q", "k", "v", "d_out", "dq", "dk", "dv"};
+  for (int i = 0; i < 7; ++i)
+    if ((st = check_tensor(all[i], names[i], who)) != FLEXATTN_OK) return st;
+  for (int i = 0; i < 7; ++i)
+    if (all[i]->dtype != FLEXATTN_BF16)
+      return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: %s must be BF16 (the backward is bf16 only)",
+                  who, names[i]);
+  if (!lse) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: lse is NULL", who);
+  if (!workspace) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: workspace is NULL", who);
+  if (!bm) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: bm is NULL", who);
+  if (q->D != 64 && q->D != 128)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: head dim %d is not 64 or 128", who, q->D);
+  for (int i = 1; i < 7; ++i)
+    if (all[i]->D != q->D || all[i]->B != q->B)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: %s batch or head dim differs from q", who,
+                  names[i]);
+  const flexattn_tensor* qlike[2] = {d_out, dq};
+  for (int i = 0; i < 2; ++i)
+    if (qlike[i]->H != q->H || qlike[i]->L != q->L)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: d_out and dq must be shaped like q", who);
+  const flexattn_tensor* kvlike[3] = {v, dk, dv};
+  for (int i = 0; i < 3; ++i)
+    if (kvlike[i]->H != k->H || kvlike[i]->L != k->L)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: v, dk and dv must be shaped like k", who);
+  if (q->H % k->H != 0)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", who, q->H,
+                k->H);
+  if (!std::isfinite(scale)) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: scale is not finite", who);
+  if (bm->BLOCK_SIZE != fa::kBlock)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: BlockMask BLOCK_SIZE must be 128 (got %d)", who,
+                bm->BLOCK_SIZE);
+  if (bm->Q_LEN != q->L || bm->KV_LEN != k->L ||
+      bm->num_q_blocks != ceil_div(q->L, fa::kBlock) ||
+      bm->num_kv_blocks != ceil_div(k->L, fa::kBlock))
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: BlockMask lengths do not match the tensors", who);
+  if (!(bm->B == 1 || bm->B == q->B) || !(bm->H == 1 || bm->H == q->H))
+    return fail(FLEXATTN_ERR_INVALID_ARG,
+                "%s: BlockMask extents (B=%d, H=%d) must be 1 or match q (B=%d, H=%d)", who, bm->B,
+                bm->H, q->B, q->H);
+  if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices ||
+      !bm->schedule)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: a BlockMask buffer pointer is NULL", who);
+  if (!bm->q_num_blocks || !bm->q_indices || !bm->full_q_num_blocks || !bm->full_q_indices)
+    return fail(FLEXATTN_ERR_INVALID_ARG,
+                "%s: the BlockMask has no q_* lists (build it with the q_* buffers set)", who);
+  fa::MaskParams mp;
+  int doc_len = 0;
+  if ((st = check_mask(bm->mask_kind, &bm->mask_params, q->B, q->L, k->L, &mp, &doc_len, who)) !=
+      FLEXATTN_OK)
+    return st;
+  if (bm->mask_kind == FLEXATTN_MASK_DOCUMENT_CAUSAL && bm->mask_params.doc_batch > 1 &&
+      bm->B != q->B)
+    return fail(FLEXATTN_ERR_INVALID_ARG,
+                "%s: per-batch doc_ids need a BlockMask built per batch (B=%d)", who, q->B);
+  if ((long long)q->B * q->H * bm->num_q_blocks > 0x7fffffffLL ||
+      (long long)q->B * k->H * bm->num_kv_blocks > 0x7fffffffLL ||
+      (long long)q->B * q->H * q->L > 0x7fffffffLL)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: too many tiles or rows for one launch", who);
+  if ((int)score_kind < FLEXATTN_SCORE_NONE || (int)score_kind > FLEXATTN_SCORE_SOFTCAP_ALIBI)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: score_kind %d is not a supported kind", who,
+                (int)score_kind);
+  float softcap = 0.0f;
+  const float* slopes = nullptr;
+  if (score_kind == FLEXATTN_SCORE_SOFTCAP || score_kind == FLEXATTN_SCORE_SOFTCAP_ALIBI) {
+    if (!params || !(params->softcap > 0.0f) || !std::isfinite(params->softcap))
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: softcap must be a finite value > 0", who);
+    softcap = params->softcap;
+  }
+  if (score_kind == FLEXATTN_SCORE_ALIBI || score_kind == FLEXATTN_SCORE_SOFTCAP_ALIBI)
+    slopes = params ? params->alibi_slopes : nullptr;
+
+  fa::BwdLaunch L;
+  L.q = q->data;
+  L.k = k->data;
+  L.v = v->data;
+  L.dout = d_out->data;
+  L.lse = lse;
+  L.delta = workspace;
+  L.dq = dq->data;
+  L.dk = dk->data;
+  L.dv = dv->data;
+  for (int i = 0; i < 3; ++i) {
+    L.sq[i] = q->stride[i];
+    L.sk[i] = k->stride[i];
+    L.sv[i] = v->stride[i];
+    L.sdo[i] = d_out->stride[i];
+    L.sdq[i] = dq->stride[i];
+    L.sdk[i] = dk->stride[i];
+    L.sdv[i] = dv->stride[i];
+  }
+  L.B = q->B;
+  L.Hq = q->H;
+  L.Hkv = k->H;
+  L.Q_LEN = q->L;
+  L.KV_LEN = k->L;
+  L.D = q->D;
+  L.mask_kind = (int)bm->mask_kind;
+  L.mp = mp;
+  L.score_kind = (int)score_kind;
+  L.softcap = softcap;
+  L.slopes = slopes;
+  L.scale = scale;
+  L.bm.kv_num = bm->kv_num_blocks;
+  L.bm.kv_idx = bm->kv_indices;
+  L.bm.full_num = bm->full_kv_num_blocks;
+  L.bm.full_idx = bm->full_kv_indices;
+  L.bm.schedule = bm->schedule;
+  L.bm.Bm = bm->B;
+  L.bm.Hm = bm->H;
+  L.bm.NQB = bm->num_q_blocks;
+  L.bm.NKB = bm->num_kv_blocks;
+  L.q_num = bm->q_num_blocks;
+  L.q_idx = bm->q_indices;
+  L.full_q_num = bm->full_q_num_blocks;
+  L.full_q_idx = bm->full_q_indices;
+  hipError_t e = fa::launch_bwd_bf16(L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(FLEXATTN_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();

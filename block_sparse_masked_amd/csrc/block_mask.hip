@@ -357,6 +357,45 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int* kv_n
   }
 }
 
+// Backward lists ("Details", items 3 and 4): for BlockMask row group bh and
+// KV tile j, the query tiles whose partial (full) list holds j, ascending.
+// One thread per (bh, j) walks the NQB rows and binary-searches j in each
+// row's ascending lists.
+__device__ __forceinline__ bool sorted_contains(const int* list, int n, int j) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int v = list[mid];
+    if (v == j) return true;
+    if (v < j) lo = mid + 1;
+    else hi = mid;
+  }
+  return false;
+}
+
+__global__ __launch_bounds__(64) void transpose_kernel(const int* kv_num, const int* kv_idx,
+                                                       const int* full_num, const int* full_idx,
+                                                       int NQB, int NKB, int* q_num, int* q_idx,
+                                                       int* fq_num, int* fq_idx) {
+  const int bh = blockIdx.y;
+  const int j = blockIdx.x * 64 + threadIdx.x;
+  if (j >= NKB) return;
+  const long long rows = (long long)bh * NQB;
+  const long long out = ((long long)bh * NKB + j) * NQB;
+  int np = 0, nf = 0;
+  for (int i = 0; i < NQB; ++i) {
+    const long long r = rows + i;
+    const int cp = min(max(kv_num[r], 0), NKB);
+    const int cf = min(max(full_num[r], 0), NKB);
+    if (sorted_contains(kv_idx + r * NKB, cp, j)) q_idx[out + np++] = i;
+    if (sorted_contains(full_idx + r * NKB, cf, j)) fq_idx[out + nf++] = i;
+  }
+  for (int t = np; t < NQB; ++t) q_idx[out + t] = 0;
+  for (int t = nf; t < NQB; ++t) fq_idx[out + t] = 0;
+  q_num[(long long)bh * NKB + j] = np;
+  fq_num[(long long)bh * NKB + j] = nf;
+}
+
 }  // namespace
 
 int max_build_kv_blocks() {
@@ -412,6 +451,13 @@ hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
   const int nbins = L.NKB + 1;
   schedule_kernel<<<1, kSchedThreads, sizeof(int) * 2 * (size_t)nbins, stream>>>(
       L.kv_num, L.full_num, rows, nbins, L.schedule);
+  if (L.q_num) {
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    transpose_kernel<<<dim3((L.NKB + 63) / 64, L.Bm * L.Hm), 64, 0, stream>>>(
+        L.kv_num, L.kv_idx, L.full_num, L.full_idx, L.NQB, L.NKB, L.q_num, L.q_idx,
+        L.full_q_num, L.full_q_idx);
+  }
   return hipGetLastError();
 }
 

@@ -20,6 +20,11 @@ struct BuildLaunch {
   int* full_idx;
   int* schedule;
   int separate_full;  // 0: every non-empty tile is listed as partial
+  // optional per-KV-tile query lists for the backward (all four or none)
+  int* q_num;
+  int* q_idx;
+  int* full_q_num;
+  int* full_q_idx;
 };
 
 hipError_t launch_build(const BuildLaunch& L, hipStream_t stream);
@@ -49,5 +54,33 @@ int fwd_bf16_lds_bytes(int D, int NKB);  // dynamic LDS of the bf16 forward
 constexpr int kMaxLdsBytes = 160 * 1024;
 constexpr long long kMaxBf16RowStride = 1ll << 22;  // k/v row stride limit of the bf16 forward
 hipError_t launch_fwd_f32(const FwdLaunch& L, hipStream_t stream);
+
+struct BwdLaunch {
+  // element strides for b, h, l (d is contiguous)
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;
+  float* delta;  // workspace [B][Hq][Q_LEN]
+  void* dq;
+  void* dk;
+  void* dv;
+  long long sq[3], sk[3], sv[3], sdo[3], sdq[3], sdk[3], sdv[3];
+  int B, Hq, Hkv, Q_LEN, KV_LEN, D;
+  int mask_kind;
+  MaskParams mp;
+  int score_kind;
+  float softcap;
+  const float* slopes;
+  float scale;
+  BlockMaskView bm;
+  const int* q_num;
+  const int* q_idx;
+  const int* full_q_num;
+  const int* full_q_idx;
+};
+
+hipError_t launch_bwd_bf16(const BwdLaunch& L, hipStream_t stream);
 
 }  // namespace fa

@@ -137,6 +137,14 @@ typedef struct {
  *                        ascending row id; the forward visits rows in this
  *                        order (longest first) for load balance.
  *   mask_kind, mask_params  the mask_mod the partial tiles are evaluated with.
+ *   q_num_blocks, q_indices, full_q_num_blocks, full_q_indices
+ *                        optional lists for the backward ("Details", items 3
+ *                        and 4): for each (b, h, KV tile) the query tiles whose
+ *                        tile is partial (resp. full), ascending, tail 0;
+ *                        [B][H][NKB] counts and [B][H][NKB][NQB] indices.
+ *                        flexattn_create_block_mask fills them when all four
+ *                        pointers are non-NULL; NULL leaves them unbuilt (the
+ *                        forward never reads them, flexattn_bwd needs them).
  * A caller may fill the struct from its own index lists (the from_kv_blocks
  * use); their contents are then trusted as given.
  */
@@ -151,6 +159,10 @@ typedef struct {
   int32_t* schedule;
   flexattn_mask_kind mask_kind;
   flexattn_mask_params mask_params;
+  int32_t* q_num_blocks;
+  int32_t* q_indices;
+  int32_t* full_q_num_blocks;
+  int32_t* full_q_indices;
 } flexattn_block_mask;
 
 /*
@@ -219,6 +231,36 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
                              const flexattn_tensor* v, const flexattn_block_mask* bm,
                              flexattn_score_kind score_kind, const flexattn_score_params* params,
                              float scale, flexattn_tensor* out, float* lse, void* stream);
+
+/*
+ * Backward of flexattn_fwd: the gradients of the forward's output with
+ * respect to q, k and v for an upstream gradient d_out (page
+ * "tensorplay.nn.attention API", section BlockMask, "Details": dQ walks each
+ * query tile's KV tiles from items 1 and 2; dK and dV walk each KV tile's
+ * query tiles from items 3 and 4, so `bm` must carry q_num_blocks,
+ * q_indices, full_q_num_blocks and full_q_indices). mask_mod runs on partial
+ * tiles only, as in the forward.
+ *   q, k, v, score_kind, params, scale: exactly as given to flexattn_fwd.
+ *   lse   the forward's LSE, device float [B][Hq][Q_LEN], contiguous.
+ *   d_out dL/dO, shaped like the forward's output [B][Hq][Q_LEN][D].
+ *   dq    written: dL/dq, shaped like q.
+ *   dk,dv written: dL/dk, dL/dv [B][Hkv][KV_LEN][D]; each sums the query heads
+ *         of its GQA group (in a fixed order: the result is deterministic).
+ *   workspace  device float [B * Hq * Q_LEN], caller-allocated and
+ *         overwritten with Delta_i = sum_j P_ij dP_ij, which equals dO_i . O_i
+ *         but is formed from fp32 P and dP, so the forward's output is not an
+ *         input.
+ * All tensors are BF16 with D in {64, 128} (UNSUPPORTED otherwise); strides
+ * and alignment as for flexattn_fwd. Rows with no allowed key (LSE = -inf)
+ * get dq = 0. Asynchronous on `stream`; no host synchronisation.
+ */
+flexattn_status flexattn_bwd(const flexattn_tensor* q, const flexattn_tensor* k,
+                             const flexattn_tensor* v, const float* lse,
+                             const flexattn_tensor* d_out,
+                             const flexattn_block_mask* bm, flexattn_score_kind score_kind,
+                             const flexattn_score_params* params, float scale,
+                             flexattn_tensor* dq, flexattn_tensor* dk, flexattn_tensor* dv,
+                             float* workspace, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). Host only. */
 const char* flexattn_last_error(void);

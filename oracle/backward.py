@@ -66,11 +66,13 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, d_out: np.nd
                        scale: Optional[float] = None,
                        batches: Optional[Sequence[int]] = None,
                        heads: Optional[Sequence[int]] = None,
+                       rows: Optional[Sequence[int]] = None,
                        row_chunk: int = 1024):
     """dQ [B, Hq, M, D], dK [B, Hkv, N, D], dV [B, Hkv, N, Dv] in fp64.
 
-    Only the selected batches / query heads contribute (dQ rows of other
-    heads stay NaN; dK / dV collect only the selected heads)."""
+    Only the selected batches / query heads / query rows contribute (dQ rows
+    not selected stay NaN; dK / dV collect only the selected rows, so they
+    are the full gradients only when every row of a head is selected)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -88,12 +90,13 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, d_out: np.nd
     dv = np.zeros(v.shape)
     batches = range(B) if batches is None else batches
     heads = range(Hq) if heads is None else heads
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
     kv_idx = np.arange(N, dtype=np.int64)[None, :]
     for b in batches:
         for h in heads:
             hk = h // group
-            for c in range(0, M, row_chunk):
-                r = np.arange(c, min(c + row_chunk, M), dtype=np.int64)
+            for c in range(0, len(rows), row_chunk):
+                r = rows[c:c + row_chunk]
                 q_idx = r[:, None]
                 s = scale * (q[b, h, r] @ k[b, hk].T)
                 s_mod = score_mod(s, b, h, q_idx, kv_idx) if score_mod is not None else s

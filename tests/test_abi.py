@@ -28,8 +28,8 @@ def L():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("flexattn_create_block_mask", "flexattn_fwd", "flexattn_block_mask_sizes",
-                     "flexattn_last_error", "flexattn_version"):
+    for required in ("flexattn_create_block_mask", "flexattn_fwd", "flexattn_bwd",
+                     "flexattn_block_mask_sizes", "flexattn_last_error", "flexattn_version"):
         assert required in names
 
 
@@ -176,3 +176,38 @@ def test_library_has_no_undefined_internal_symbols():
                          capture_output=True, text=True, check=True).stdout
     bad = [line for line in out.splitlines() if "_ZN2fa" in line]
     assert not bad, bad[:5]
+
+
+def _bwd(L, tensors, bm, lse=16, ws=16, score=0):
+    t = [ctypes.byref(x) if x is not None else None for x in tensors]
+    sp = lib._ScoreParams(0.0, None)
+    return L.flexattn_bwd(t[0], t[1], t[2], ctypes.c_void_p(lse), t[3], ctypes.byref(bm),
+                          score, ctypes.byref(sp), 0.125, t[4], t[5], t[6],
+                          ctypes.c_void_p(ws), None)
+
+
+def test_bwd_rejects_bad_arguments(L):
+    """Host-side checks of the backward (no launch happens)."""
+    def tens(dtype=1, H=2, Lq=256, D=128):
+        st = (H * Lq * D, Lq * D, D, 1)
+        return lib._Tensor(16, dtype, 1, H, Lq, D, (ctypes.c_int64 * 4)(*st))
+    bm = _bm_struct()
+    bm.B, bm.H, bm.Q_LEN, bm.KV_LEN, bm.BLOCK_SIZE = 1, 1, 256, 256, 128
+    bm.num_q_blocks, bm.num_kv_blocks, bm.mask_kind = 2, 2, 1
+    good = [tens() for _ in range(7)]
+    # no backward lists
+    assert _bwd(L, good, bm) == lib._INVALID
+    assert b"q_*" in L.flexattn_last_error()
+    bm.q_num_blocks = bm.q_indices = bm.full_q_num_blocks = bm.full_q_indices = 16
+    # fp32 tensors are not supported by the backward
+    f32 = [tens(dtype=0) for _ in range(7)]
+    assert _bwd(L, f32, bm) == lib._UNSUPPORTED
+    assert b"BF16" in L.flexattn_last_error()
+    # head dim, NULL workspace, NULL tensor, mismatched shapes
+    assert _bwd(L, [tens(D=96) for _ in range(7)], bm) == lib._UNSUPPORTED
+    assert _bwd(L, good, bm, ws=0) == lib._INVALID
+    assert _bwd(L, [None] + good[1:], bm) == lib._INVALID
+    bad = list(good)
+    bad[4] = tens(Lq=128)
+    assert _bwd(L, bad, bm) == lib._INVALID
+    assert b"shaped like q" in L.flexattn_last_error()

@@ -1,0 +1,222 @@
+"""GPU backward vs the fp64 oracle, element by element, through the C ABI.
+
+Tolerance (bf16 inputs, bf16 gradients), per element of a gradient row g
+(a query row of dQ, a key row of dK / dV):
+    |g_gpu - g_ref| <= BWD_ROW_RMS * rms(row of g_ref) + BWD_RTOL * |g_ref|
+                       + BWD_FLOOR * rms(g_ref) + BWD_ABS.
+The kernels round dS and P to bf16 (relative error up to 2^-8) before their
+matrix products and round each gradient to bf16 (up to 2^-8); Delta and
+dP - Delta are formed in fp32. The product errors are sums over the row's
+terms, so they scale with that row's magnitude, not the tensor's: rows that
+attend to few keys (early causal rows) have gradients many times the
+tensor's RMS. A CPU simulation of these roundings on the tiny grid stays
+under 1.5% of the row RMS; the bound allows 4% of the row RMS, 2% of the
+element for the output rounding, 0.1% of the tensor RMS for rows whose
+reference is nearly zero, and 1e-5 for gradients that are exactly zero in
+the reference (a row with a single allowed key).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+BWD_ROW_RMS = 0.04
+BWD_RTOL = 0.02
+BWD_FLOOR = 1e-3
+BWD_ABS = 1e-5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_masked_amd as m
+    m.load_library()
+    return m
+
+
+def tiny(D, mask, score, B=2, Hq=4, Hkv=2, Q_LEN=300, KV_LEN=300, seed=0, **kw):
+    return W.Workload(f"bwd_{D}_{mask}_{score}", B=B, Hq=Hq, Hkv=Hkv, Q_LEN=Q_LEN,
+                      KV_LEN=KV_LEN, D=D, dtype="bf16", seed=seed, mask=mask,
+                      window=kw.get("window", 100), sinks=kw.get("sinks", 3),
+                      doc_seed=kw.get("doc_seed", 77),
+                      doc_len_range=kw.get("doc_len_range", (20, 150)), score=score,
+                      softcap=kw.get("softcap", 20.0), value_scale=kw.get("value_scale", 1.0))
+
+
+def mask_of(lib, w, inp, B_mask=1, H_mask=1, separate_full_blocks=True):
+    doc = torch.from_numpy(inp.doc_ids.astype(np.int32)) if w.mask == "document_causal" else None
+    return lib.create_block_mask(w.mask, B_mask, H_mask, w.Q_LEN, w.KV_LEN, 128, window=w.window,
+                                 num_sinks=w.sinks, doc_ids=doc, backward_lists=True,
+                                 separate_full_blocks=separate_full_blocks)
+
+
+def run_bwd(lib, w, inp, d_out, bm):
+    q = G.to_device(inp.q, "bf16")
+    k = G.to_device(inp.k, "bf16")
+    v = G.to_device(inp.v, "bf16")
+    g = G.to_device(d_out, "bf16")
+    out, lse = lib.flex_attention(q, k, v, bm, score=w.score, softcap=w.softcap, scale=w.scale)
+    dq, dk, dv = lib.flex_attention_backward(q, k, v, lse, g, bm, score=w.score,
+                                             softcap=w.softcap, scale=w.scale)
+    torch.cuda.synchronize()
+    return [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+
+
+def oracle_bwd(w, inp, d_out, **sel):
+    mask, score = oracle.for_workload(w, inp)
+    grad = oracle.score_grad_for(w.score, w.softcap)
+    return oracle.attention_backward(inp.q, inp.k, inp.v, d_out, mask, score, grad, w.scale, **sel)
+
+
+def check(got, ref, name):
+    """Apply the bound above to the rows the reference computed; returns the
+    largest error over its bound."""
+    rows = ~np.isnan(ref).any(axis=-1)
+    g, r = got[rows], ref[rows]
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    if not r.size:
+        return 0.0
+    rms_all = float(np.sqrt(np.mean(r * r)))
+    rms_row = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
+    err = np.abs(g - r)
+    bound = BWD_ROW_RMS * rms_row + BWD_RTOL * np.abs(r) + BWD_FLOOR * rms_all + BWD_ABS
+    ratio = err / bound
+    worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    assert np.all(err <= bound), (f"{name}: err/bound {ratio[worst]:.3g} at {worst}: err "
+                                  f"{err[worst]:.4g}, ref {r[worst]:.4g}, row rms "
+                                  f"{float(rms_row[worst[:-1]][0]):.4g}, tensor rms {rms_all:.4g}")
+    return float(ratio.max())
+
+
+def full_check(lib, w, B_mask=1, H_mask=1, separate_full_blocks=True):
+    inp = W.generate(w)
+    d_out = W.generate_upstream(w)
+    bm = mask_of(lib, w, inp, B_mask, H_mask, separate_full_blocks)
+    got = run_bwd(lib, w, inp, d_out, bm)
+    ref = oracle_bwd(w, inp, d_out)
+    return [check(g, r, n) for g, r, n in zip(got, ref, ("dq", "dk", "dv"))]
+
+
+# ------------------------------------------------------------ backward lists
+
+@pytest.mark.parametrize("q_len,kv_len", [(1, 1), (129, 129), (300, 255), (255, 300), (512, 512),
+                                          (700, 1), (1, 700)])
+@pytest.mark.parametrize("kind,window,sinks", [
+    ("noop", 0, 0), ("causal", 0, 0), ("sliding_sink", 200, 130), ("document_causal", 0, 0)])
+def test_backward_lists_bit_exact(lib, q_len, kv_len, kind, window, sinks):
+    """q_num_blocks / q_indices / full_q_* equal the oracle's transpose."""
+    rng = np.random.default_rng(q_len * 31 + kv_len)
+    L = max(q_len, kv_len)
+    doc = None
+    if kind == "document_causal":
+        lens = []
+        while sum(lens) < L:
+            lens.append(int(rng.integers(1, 150)))
+        doc = W.document_ids(lens)[:L]
+    ref = oracle.create_block_mask(oracle.mask_mod_for(kind, window, sinks, doc), 1, 1, q_len,
+                                   kv_len, 128)
+    exp = oracle.transpose_block_mask(ref)
+    bm = lib.create_block_mask(kind, 1, 1, q_len, kv_len, 128, window=window, num_sinks=sinks,
+                               doc_ids=None if doc is None else torch.from_numpy(doc),
+                               backward_lists=True)
+    torch.cuda.synchronize()
+    got = [bm.q_num_blocks, bm.q_indices, bm.full_q_num_blocks, bm.full_q_indices]
+    for name, g, e in zip(("q_num", "q_idx", "full_q_num", "full_q_idx"), got, exp):
+        assert np.array_equal(g.cpu().numpy(), e), name
+
+
+def test_backward_lists_full_workload(lib):
+    """The dense causal workload's lists (32 x 32 tiles)."""
+    ref = oracle.create_block_mask(oracle.causal_mask, 1, 1, 4096, 4096, 128)
+    exp = oracle.transpose_block_mask(ref)
+    bm = lib.create_block_mask("causal", 1, 1, 4096, 4096, 128, backward_lists=True)
+    torch.cuda.synchronize()
+    for g, e in zip((bm.q_num_blocks, bm.q_indices, bm.full_q_num_blocks, bm.full_q_indices), exp):
+        assert np.array_equal(g.cpu().numpy(), e)
+
+
+# ------------------------------------------------------------------ gradients
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal"])
+@pytest.mark.parametrize("score", ["none", "alibi", "softcap", "softcap_alibi"])
+def test_bwd_tiny_grid(lib, D, mask, score):
+    """Every head dim x mask x score kind, GQA (2 query heads per KV head),
+    3 query and KV tiles with a ragged tail (300 = 2*128 + 44)."""
+    w = tiny(D, mask, score, value_scale=2.0 if "softcap" in score else 1.0)
+    full_check(lib, w)
+
+
+@pytest.mark.parametrize("q_len,kv_len", [(1, 1), (1, 200), (200, 1), (129, 257), (257, 129),
+                                          (128, 128), (513, 200)])
+def test_bwd_ragged_lengths(lib, q_len, kv_len):
+    """Lengths that are not multiples of the tile, Q_LEN != KV_LEN (rows with
+    no key under causal when Q_LEN > KV_LEN... and tail tiles on both axes)."""
+    w = tiny(128, "causal", "none", B=1, Hq=2, Hkv=1, Q_LEN=q_len, KV_LEN=kv_len)
+    full_check(lib, w)
+
+
+def test_bwd_empty_rows(lib):
+    """Sliding window without sinks and Q_LEN > KV_LEN + window: query rows
+    with no allowed key (LSE = -inf) get dQ = 0 and add nothing."""
+    w = tiny(128, "sliding_sink", "none", B=1, Hq=2, Hkv=1, Q_LEN=400, KV_LEN=150, window=60,
+             sinks=0)
+    full_check(lib, w)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 1), (8, 2)])
+def test_bwd_head_groupings(lib, Hq, Hkv):
+    """MHA, MQA and GQA with 4 heads per group: dK / dV sum the group."""
+    w = tiny(64, "causal", "alibi", B=1, Hq=Hq, Hkv=Hkv, Q_LEN=260, KV_LEN=260)
+    full_check(lib, w)
+
+
+def test_bwd_per_head_mask_rows(lib):
+    """A BlockMask built per (b, h) (B and H not broadcast) gives the same
+    gradients."""
+    w = tiny(128, "sliding_sink", "softcap", B=2, Hq=4, Hkv=2, Q_LEN=384, KV_LEN=384,
+             value_scale=2.0)
+    full_check(lib, w, B_mask=2, H_mask=4)
+
+
+def test_bwd_unseparated_mask(lib):
+    """separate_full_blocks=False: every tile listed as partial, mask on all."""
+    w = tiny(128, "causal", "softcap_alibi", Q_LEN=384, KV_LEN=384, value_scale=2.0)
+    full_check(lib, w, separate_full_blocks=False)
+
+
+def test_bwd_dense_causal_full_size_sampled(lib):
+    """The dense causal workload at full size (B=4, Hq=16, Hkv=4, L=4096,
+    D=128): dQ rows checked against the oracle on a sample of (b, h, rows)
+    (dQ of a row needs only that row), dK / dV of one KV head checked in full
+    against the oracle over its four query heads restricted to b = 0."""
+    w = W.DENSE_CAUSAL_GQA
+    inp = W.generate(w)
+    d_out = W.generate_upstream(w)
+    bm = mask_of(lib, w, inp)
+    dq, dk, dv = run_bwd(lib, w, inp, d_out, bm)
+    rows = np.array([0, 1, 127, 128, 2047, 3000, 4095])
+    for b, h in ((0, 0), (1, 5), (3, 15)):
+        ref_dq, _, _ = oracle_bwd(w, inp, d_out, batches=[b], heads=[h], rows=rows)
+        check(dq[b, h, rows], ref_dq[b, h, rows], f"dq[{b},{h}]")
+    _, ref_dk, ref_dv = oracle_bwd(w, inp, d_out, batches=[0], heads=[4, 5, 6, 7])
+    check(dk[0, 1], ref_dk[0, 1], "dk[0,1]")
+    check(dv[0, 1], ref_dv[0, 1], "dv[0,1]")
+
+
+def test_bwd_deterministic(lib):
+    """Two backward calls give bit-identical gradients (no atomics)."""
+    w = tiny(128, "document_causal", "alibi", Q_LEN=520, KV_LEN=520)
+    inp = W.generate(w)
+    d_out = W.generate_upstream(w)
+    bm = mask_of(lib, w, inp)
+    a = run_bwd(lib, w, inp, d_out, bm)
+    b = run_bwd(lib, w, inp, d_out, bm)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)

@@ -168,6 +168,15 @@ def generate(w: Workload) -> Inputs:
     return Inputs(q, k, v, doc_ids, doc_lengths)
 
 
+def generate_upstream(w: Workload) -> np.ndarray:
+    """Upstream gradient dO for the backward: standard normal, shaped like
+    the output [B, Hq, Q_LEN, D], from its own stream (seed + 7919) so the
+    forward's inputs do not change; rounded to bf16 for bf16 workloads."""
+    rng = np.random.default_rng(w.seed + 7919)
+    g = rng.standard_normal((w.B, w.Hq, w.Q_LEN, w.D), dtype=np.float32)
+    return round_to_bf16(g) if w.dtype == "bf16" else g
+
+
 def small(w: Workload, **kw) -> Workload:
     """A reduced copy of a workload (same kinds and dtype), for quick checks."""
     return w.with_(**kw)

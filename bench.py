@@ -130,6 +130,9 @@ def main(argv=None):
     ap.add_argument("--ablation-steps", type=int, default=20,
                     help="after the timed steps, time this many forwards on a BlockMask built "
                          "with separate_full_blocks=False (0 = skip)")
+    ap.add_argument("--backward-steps", type=int, default=10,
+                    help="after the forward, time this many backward calls (bf16 workloads; "
+                         "0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB "
                          "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -236,6 +239,35 @@ def main(argv=None):
                     "speedup_from_full_tiles": round(all_partial_ms / float(np.median(fwd_ms)), 4),
                     "calls": args.ablation_steps}
 
+    # Backward (after the forward's timed region, not part of `value`): one
+    # flexattn_bwd call per step on the same inputs with a seeded upstream
+    # gradient; the mask carries the backward lists.
+    backward = None
+    if args.backward_steps > 0 and w.dtype == "bf16":
+        bm_b = fa.create_block_mask(w.mask, 1, 1, w.Q_LEN, w.KV_LEN, 128, window=w.window,
+                                    num_sinks=w.sinks, doc_ids=doc, device=dev, stream=stream,
+                                    backward_lists=True)
+        g = torch.from_numpy(W.generate_upstream(w)).to(tdtype).to(dev)
+        fa.flex_attention(q, k, v, bm_b, score=w.score, softcap=w.softcap, scale=w.scale,
+                          out=out, lse=lse, stream=stream)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        for _ in range(2):
+            fa.flex_attention_backward(q, k, v, lse, g, bm_b, score=w.score, softcap=w.softcap,
+                                       scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws,
+                                       stream=stream)
+        ev_b = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                for _ in range(args.backward_steps)]
+        for i in range(args.backward_steps):
+            ev_b[i][0].record(stream)
+            fa.flex_attention_backward(q, k, v, lse, g, bm_b, score=w.score, softcap=w.softcap,
+                                       scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws,
+                                       stream=stream)
+            ev_b[i][1].record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = float(np.median([a.elapsed_time(b) for a, b in ev_b]))
+        backward = {"ms_median": round(bwd_ms, 4), "calls": args.backward_steps}
+
     pairs = allowed_pairs_per_head(w, inp.doc_lengths)
     eff_flops = 4.0 * w.D * pairs * w.B * w.Hq
     dense_flops = 4.0 * w.D * w.Q_LEN * w.KV_LEN * w.B * w.Hq
@@ -288,6 +320,19 @@ def main(argv=None):
     }
     if ablation is not None:
         rec["full_tile_ablation"] = ablation
+    if backward is not None:
+        # algorithmic work: five products of 2*D flops per allowed pair (S,
+        # dP, dV, dK, dQ); the kernels execute nine (S and dP three times:
+        # Delta pass, dQ walk, dK/dV walk)
+        alg = 10.0 * w.D * pairs * w.B * w.Hq
+        done = 18.0 * w.D * pairs * w.B * w.Hq
+        t = backward["ms_median"] * 1e-3
+        backward.update({
+            "effective_tflops": round(alg / t / 1e12, 2),
+            "executed_tflops": round(done / t / 1e12, 2),
+            "frac_of_peak": round(alg / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "flop_convention": "10*D per allowed (q, kv) pair and (b, h); executed 18*D"})
+        rec["backward"] = backward
     if inp.doc_lengths is not None:
         rec["config"]["doc_lengths"] = [int(x) for x in inp.doc_lengths]
     if not args.no_cpu_baseline:

@@ -303,8 +303,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   __shared__ int sdoc[kBlock];
 
   const int NKB = a.bm.NKB, NQB = a.bm.NQB;
-  const int kb = blockIdx.x % NKB;
-  const int bh = blockIdx.x / NKB;
+  // KV-tile-major order: every (b, KV head) of tile 0 first, then tile 1, ...
+  // Under causal-like masks the early KV tiles have the longest query lists,
+  // so the launch runs longest first (one workgroup per CU at this size).
+  const int nbh = a.B * a.Hkv;
+  const int kb = blockIdx.x / nbh;
+  const int bh = blockIdx.x - kb * nbh;
   const int hk = bh % a.Hkv, b = bh / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;

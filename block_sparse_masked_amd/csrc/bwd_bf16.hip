@@ -101,18 +101,39 @@ __device__ __forceinline__ bf16x8 tr_frag(const u16* blk, int lane, int ks, int 
 }
 
 // Rows [r0, r0 + 128) of a [len][D] bf16 matrix (row stride `ld` elements)
-// into a padded LDS block; rows at or past `len` are zero.
-template <int D>
+// into a padded LDS block; rows at or past `len` are zero. Branch-free (the
+// row is clamped and the value zeroed) so each thread's loads are issued
+// back to back, NB at a time, before any of them is waited for.
+template <int D, int NB>
 __device__ __forceinline__ void stage_rows(u16* lds, const u16* g, long long ld, int r0, int len,
                                            int tid) {
   constexpr int CH = D / 8;  // 16-byte chunks per row
   constexpr int LDR = D + kPad;
-#pragma unroll 4
-  for (int c = tid; c < kBlock * CH; c += kThreads) {
-    const int r = c / CH, ch = c - (c / CH) * CH;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (r0 + r < len) val = *reinterpret_cast<const uint4*>(g + (long long)(r0 + r) * ld + ch * 8);
-    *reinterpret_cast<uint4*>(lds + r * LDR + ch * 8) = val;
+  constexpr int PER = kBlock * CH / kThreads;  // chunks per thread
+  constexpr int BATCH = PER < NB ? PER : NB;
+  static_assert(PER % BATCH == 0, "whole batches");
+#pragma unroll 1
+  for (int b0 = 0; b0 < PER; b0 += BATCH) {
+    uint4 val[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int c = tid + (b0 + i) * kThreads;
+      const int r = c / CH, ch = c % CH;
+      const int rr = min(r0 + r, len - 1);
+      val[i] = *reinterpret_cast<const uint4*>(g + (long long)rr * ld + ch * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int c = tid + (b0 + i) * kThreads;
+      const int r = c / CH, ch = c % CH;
+      const bool in = r0 + r < len;
+      uint4 w = val[i];
+      w.x = in ? w.x : 0u;
+      w.y = in ? w.y : 0u;
+      w.z = in ? w.z : 0u;
+      w.w = in ? w.w : 0u;
+      *reinterpret_cast<uint4*>(lds + r * LDR + ch * 8) = w;
+    }
   }
 }
 
@@ -254,8 +275,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
                        NKB - 1);
     const int kv0 = kb * kBlock;
     __syncthreads();  // the previous tile's reads are done
-    stage_rows<D>(sK, kbase, a.sk[2], kv0, a.KV_LEN, tid);
-    stage_rows<D>(sV, vbase, a.sv[2], kv0, a.KV_LEN, tid);
+    stage_rows<D, 2>(sK, kbase, a.sk[2], kv0, a.KV_LEN, tid);
+    stage_rows<D, 2>(sV, vbase, a.sv[2], kv0, a.KV_LEN, tid);
     if constexpr (MASK == MASK_DOCUMENT) {
       for (int i = tid; i < kBlock; i += kThreads)
         sdoc[i] = (kv0 + i < a.KV_LEN) ? doc_row[kv0 + i] : -1;
@@ -401,8 +422,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
                          NQB - 1);
       const int q0 = qb * kBlock;
       __syncthreads();  // the previous tile's reads are done
-      stage_rows<D>(sQ, qbase, a.sq[2], q0, a.Q_LEN, tid);
-      stage_rows<D>(sG, gbase, a.sdo[2], q0, a.Q_LEN, tid);
+      stage_rows<D, 4>(sQ, qbase, a.sq[2], q0, a.Q_LEN, tid);
+      stage_rows<D, 4>(sG, gbase, a.sdo[2], q0, a.Q_LEN, tid);
       for (int i = tid; i < kBlock; i += kThreads) {
         const bool in = q0 + i < a.Q_LEN;
         slse[i] = in ? lse_base2(a.lse[lbase + q0 + i]) : INFINITY;

@@ -357,83 +357,146 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     accv[i] = f32x16{};
   }
 
-  for (int gi = 0; gi < a.G; ++gi) {
-    const int h = hk * a.G + gi;
-    const int bmi = a.bm.Bm == 1 ? 0 : b;
-    const int hm = a.bm.Hm == 1 ? 0 : h;
-    const long long mrow = ((long long)bmi * a.bm.Hm + hm) * NKB + kb;
-    const int nfull = min(max(a.fq_num[mrow], 0), NQB);
-    const int npart = min(max(a.q_num[mrow], 0), NQB);
-    float slope2 = 0.0f;
-    if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
-      slope2 = alibi_slope(a.slopes, h, a.Hq) * kLog2e;
+  // The walk: for each query head of the group, its full then partial query
+  // tiles of this KV tile; heads with empty lists are skipped.
+  struct Pos {
+    int gi, t, nfull, npart;
+    long long mrow;
+  };
+  auto first_from = [&](int gi) __attribute__((always_inline)) {
+    Pos p{gi, 0, 0, 0, 0};
+    for (; p.gi < a.G; ++p.gi) {
+      const int h = hk * a.G + p.gi;
+      const int bmi = a.bm.Bm == 1 ? 0 : b;
+      const int hm = a.bm.Hm == 1 ? 0 : h;
+      p.mrow = ((long long)bmi * a.bm.Hm + hm) * NKB + kb;
+      p.nfull = min(max(a.fq_num[p.mrow], 0), NQB);
+      p.npart = min(max(a.q_num[p.mrow], 0), NQB);
+      if (p.nfull + p.npart > 0) break;
+    }
+    return p;
+  };
+  auto next_pos = [&](Pos p) __attribute__((always_inline)) {
+    if (p.t + 1 < p.nfull + p.npart) {
+      ++p.t;
+      return p;
+    }
+    return first_from(p.gi + 1);
+  };
+  auto tile_q0 = [&](const Pos& p) __attribute__((always_inline)) {
+    const bool full = p.t < p.nfull;
+    const int qb = full ? a.fq_idx[p.mrow * NQB + p.t] : a.q_idx[p.mrow * NQB + p.t - p.nfull];
+    return min(max(qb, 0), NQB - 1) * kBlock;
+  };
+
+  // The next tile's Q / dO rows (and LSE, Delta, document ids) are loaded
+  // into registers while the current tile computes, then written to LDS.
+  constexpr int CH = D / 8;                    // 16-byte chunks per row
+  constexpr int PER = kBlock * CH / kThreads;  // chunks per thread
+  uint4 pq[PER], pg[PER];
+  float pl = 0.0f, pd = 0.0f;
+  int pdoc = 0;
+  auto fetch = [&](const Pos& p) __attribute__((always_inline)) {
+    const int h = hk * a.G + p.gi;
+    const int q0 = tile_q0(p);
     const u16* qbase = a.q + b * a.sq[0] + h * a.sq[1];
     const u16* gbase = a.dout + b * a.sdo[0] + h * a.sdo[1];
-    const long long lbase = ((long long)b * a.Hq + h) * a.Q_LEN;
-
-    auto tile = [&](int q0, auto masked_tag) __attribute__((always_inline)) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
-#pragma unroll 1
-      for (int qs = 0; qs < kBlock / 32; ++qs) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-        const u16* qrow = sQ + (32 * qs + l32) * LDR + 8 * hh;
-        const u16* grow = sG + (32 * qs + l32) * LDR + 8 * hh;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(qrow + 16 * ks), kf[ks], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(grow + 16 * ks), vf[ks], dp, 0, 0,
-                                                       0);
-        }
-        bf16x8 pf[2], dsf[2];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int ql0 = 32 * qs + 8 * g4 + 4 * hh;
-          const float4 l4 = *reinterpret_cast<const float4*>(slse + ql0);
-          const float4 d4 = *reinterpret_cast<const float4*>(sdel + ql0);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * g4 + j;
-            const int ql = ql0 + j;
-            float x, dm;
-            logit_and_slope<MASK, SCORE, MASKED>(s[r], q0 + ql, kv,
-                                                 (MASK == MASK_DOCUMENT) ? sdoc[ql] : 0, dkv_id,
-                                                 slope2, a, x, dm);
-            const float p = fast_exp2(x - lv[j]);
-            pf[r >> 3][r & 7] = (__bf16)p;
-            dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl[j]) * dm);
-          }
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                tr_frag<LDR>(sG, lane, 2 * qs + k2, db), pf[k2], accv[db], 0, 0, 0);
-            acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                tr_frag<LDR>(sQ, lane, 2 * qs + k2, db), dsf[k2], acck[db], 0, 0, 0);
-          }
-      }
-    };
-
-    for (int t = 0; t < nfull + npart; ++t) {
-      const bool full = t < nfull;
-      const int qb = min(max(full ? a.fq_idx[mrow * NQB + t] : a.q_idx[mrow * NQB + t - nfull], 0),
-                         NQB - 1);
-      const int q0 = qb * kBlock;
-      __syncthreads();  // the previous tile's reads are done
-      stage_rows<D, 4>(sQ, qbase, a.sq[2], q0, a.Q_LEN, tid);
-      stage_rows<D, 4>(sG, gbase, a.sdo[2], q0, a.Q_LEN, tid);
-      for (int i = tid; i < kBlock; i += kThreads) {
-        const bool in = q0 + i < a.Q_LEN;
-        slse[i] = in ? lse_base2(a.lse[lbase + q0 + i]) : INFINITY;
-        sdel[i] = in ? a.delta[lbase + q0 + i] : 0.0f;
-        if constexpr (MASK == MASK_DOCUMENT) sdoc[i] = in ? doc_row[q0 + i] : -2;
-      }
-      __syncthreads();
-      if (full && q0 + kBlock <= a.Q_LEN) tile(q0, std::false_type{});
-      else tile(q0, std::true_type{});
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * kThreads;
+      const int rr = min(q0 + c / CH, a.Q_LEN - 1);
+      pq[i] = *reinterpret_cast<const uint4*>(qbase + (long long)rr * a.sq[2] + (c % CH) * 8);
+      pg[i] = *reinterpret_cast<const uint4*>(gbase + (long long)rr * a.sdo[2] + (c % CH) * 8);
     }
+    if (tid < kBlock) {
+      const long long lrow = ((long long)b * a.Hq + h) * a.Q_LEN + min(q0 + tid, a.Q_LEN - 1);
+      pl = a.lse[lrow];
+      pd = a.delta[lrow];
+      if constexpr (MASK == MASK_DOCUMENT) pdoc = doc_row[min(q0 + tid, a.Q_LEN - 1)];
+    }
+  };
+  auto commit = [&](int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * kThreads;
+      const int r = c / CH;
+      const bool in = q0 + r < a.Q_LEN;
+      uint4 wq = pq[i], wg = pg[i];
+      wq.x = in ? wq.x : 0u; wq.y = in ? wq.y : 0u; wq.z = in ? wq.z : 0u; wq.w = in ? wq.w : 0u;
+      wg.x = in ? wg.x : 0u; wg.y = in ? wg.y : 0u; wg.z = in ? wg.z : 0u; wg.w = in ? wg.w : 0u;
+      *reinterpret_cast<uint4*>(sQ + r * LDR + (c % CH) * 8) = wq;
+      *reinterpret_cast<uint4*>(sG + r * LDR + (c % CH) * 8) = wg;
+    }
+    if (tid < kBlock) {
+      const bool in = q0 + tid < a.Q_LEN;
+      slse[tid] = in ? lse_base2(pl) : INFINITY;
+      sdel[tid] = in ? pd : 0.0f;
+      if constexpr (MASK == MASK_DOCUMENT) sdoc[tid] = in ? pdoc : -2;
+    }
+  };
+
+  auto tile = [&](int q0, float slope2, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+#pragma unroll 1
+    for (int qs = 0; qs < kBlock / 32; ++qs) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const u16* qrow = sQ + (32 * qs + l32) * LDR + 8 * hh;
+      const u16* grow = sG + (32 * qs + l32) * LDR + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(qrow + 16 * ks), kf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(grow + 16 * ks), vf[ks], dp, 0, 0,
+                                                     0);
+      }
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int ql0 = 32 * qs + 8 * g4 + 4 * hh;
+        const float4 l4 = *reinterpret_cast<const float4*>(slse + ql0);
+        const float4 d4 = *reinterpret_cast<const float4*>(sdel + ql0);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g4 + j;
+          const int ql = ql0 + j;
+          float x, dm;
+          logit_and_slope<MASK, SCORE, MASKED>(s[r], q0 + ql, kv,
+                                               (MASK == MASK_DOCUMENT) ? sdoc[ql] : 0, dkv_id,
+                                               slope2, a, x, dm);
+          const float p = fast_exp2(x - lv[j]);
+          pf[r >> 3][r & 7] = (__bf16)p;
+          dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl[j]) * dm);
+        }
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_frag<LDR>(sG, lane, 2 * qs + k2, db), pf[k2], accv[db], 0, 0, 0);
+          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_frag<LDR>(sQ, lane, 2 * qs + k2, db), dsf[k2], acck[db], 0, 0, 0);
+        }
+    }
+  };
+
+
+  Pos cur = first_from(0);
+  if (cur.gi < a.G) fetch(cur);
+  while (cur.gi < a.G) {
+    const int q0 = tile_q0(cur);
+    const bool full = cur.t < cur.nfull;
+    float slope2 = 0.0f;
+    if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
+      slope2 = alibi_slope(a.slopes, hk * a.G + cur.gi, a.Hq) * kLog2e;
+    __syncthreads();  // the previous tile's reads are done
+    commit(q0);
+    __syncthreads();
+    const Pos nxt = next_pos(cur);
+    if (nxt.gi < a.G) fetch(nxt);
+    if (full && q0 + kBlock <= a.Q_LEN) tile(q0, slope2, std::false_type{});
+    else tile(q0, slope2, std::true_type{});
+    cur = nxt;
   }
 
   if (kvalid) {

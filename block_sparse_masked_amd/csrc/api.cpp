@@ -149,8 +149,8 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
       !bm->schedule)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: a BlockMask buffer pointer is NULL", who);
   if (bm->q_num_blocks && bm->q_indices && bm->full_q_num_blocks && bm->full_q_indices &&
-      (long long)B * H > 65535)
-    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: B*H=%lld above 65535 for the q_* lists", who,
+      (long long)B * H > 0x7fffffffLL)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: B*H=%lld too large for the q_* lists", who,
                 (long long)B * H);
   fa::MaskParams mp;
   int doc_len = 0;

@@ -359,8 +359,13 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int* kv_n
 
 // Backward lists ("Details", items 3 and 4): for BlockMask row group bh and
 // KV tile j, the query tiles whose partial (full) list holds j, ascending.
-// One thread per (bh, j) walks the NQB rows and binary-searches j in each
-// row's ascending lists.
+// One workgroup per row group: the rows' lists are scattered into a class
+// grid in LDS (one byte per tile, transposed: [NKB][NQB]), then each thread
+// compacts one KV tile's column. Groups whose grid does not fit fall back to
+// one thread per KV tile binary-searching every row's ascending lists.
+constexpr int kTransposeThreads = 256;
+constexpr int kTransposeLdsBytes = 48 * 1024;
+
 __device__ __forceinline__ bool sorted_contains(const int* list, int n, int j) {
   int lo = 0, hi = n;
   while (lo < hi) {
@@ -373,27 +378,54 @@ __device__ __forceinline__ bool sorted_contains(const int* list, int n, int j) {
   return false;
 }
 
-__global__ __launch_bounds__(64) void transpose_kernel(const int* kv_num, const int* kv_idx,
-                                                       const int* full_num, const int* full_idx,
-                                                       int NQB, int NKB, int* q_num, int* q_idx,
-                                                       int* fq_num, int* fq_idx) {
-  const int bh = blockIdx.y;
-  const int j = blockIdx.x * 64 + threadIdx.x;
-  if (j >= NKB) return;
+__global__ __launch_bounds__(kTransposeThreads) void transpose_kernel(
+    const int* kv_num, const int* kv_idx, const int* full_num, const int* full_idx, int NQB,
+    int NKB, int* q_num, int* q_idx, int* fq_num, int* fq_idx) {
+  __shared__ unsigned char cls[kTransposeLdsBytes];  // [NKB][NQB]: 0 empty, 1 partial, 2 full
+  const int bh = blockIdx.x;
+  const int t = threadIdx.x;
   const long long rows = (long long)bh * NQB;
-  const long long out = ((long long)bh * NKB + j) * NQB;
-  int np = 0, nf = 0;
-  for (int i = 0; i < NQB; ++i) {
-    const long long r = rows + i;
-    const int cp = min(max(kv_num[r], 0), NKB);
-    const int cf = min(max(full_num[r], 0), NKB);
-    if (sorted_contains(kv_idx + r * NKB, cp, j)) q_idx[out + np++] = i;
-    if (sorted_contains(full_idx + r * NKB, cf, j)) fq_idx[out + nf++] = i;
+  const bool in_lds = (long long)NQB * NKB <= kTransposeLdsBytes;
+  if (in_lds) {
+    for (int e = t; e < NQB * NKB; e += kTransposeThreads) cls[e] = 0;
+    __syncthreads();
+    // scatter: (row i, list slot u) pairs spread over the threads
+    for (long long e = t; e < (long long)NQB * NKB; e += kTransposeThreads) {
+      const int i = (int)(e / NKB), u = (int)(e % NKB);
+      const long long r = rows + i;
+      const int cp = min(max(kv_num[r], 0), NKB);
+      const int cf = min(max(full_num[r], 0), NKB);
+      if (u < cp) {
+        const int j = kv_idx[r * NKB + u];
+        if (j >= 0 && j < NKB) cls[j * NQB + i] = 1;
+      }
+      if (u < cf) {
+        const int j = full_idx[r * NKB + u];
+        if (j >= 0 && j < NKB) cls[j * NQB + i] = 2;
+      }
+    }
+    __syncthreads();
   }
-  for (int t = np; t < NQB; ++t) q_idx[out + t] = 0;
-  for (int t = nf; t < NQB; ++t) fq_idx[out + t] = 0;
-  q_num[(long long)bh * NKB + j] = np;
-  fq_num[(long long)bh * NKB + j] = nf;
+  for (int j = t; j < NKB; j += kTransposeThreads) {
+    const long long out = ((long long)bh * NKB + j) * NQB;
+    int np = 0, nf = 0;
+    for (int i = 0; i < NQB; ++i) {
+      int c;
+      if (in_lds) {
+        c = cls[j * NQB + i];
+      } else {
+        const long long r = rows + i;
+        c = sorted_contains(full_idx + r * NKB, min(max(full_num[r], 0), NKB), j) ? 2
+            : sorted_contains(kv_idx + r * NKB, min(max(kv_num[r], 0), NKB), j) ? 1 : 0;
+      }
+      if (c == 1) q_idx[out + np++] = i;
+      if (c == 2) fq_idx[out + nf++] = i;
+    }
+    for (int u = np; u < NQB; ++u) q_idx[out + u] = 0;
+    for (int u = nf; u < NQB; ++u) fq_idx[out + u] = 0;
+    q_num[(long long)bh * NKB + j] = np;
+    fq_num[(long long)bh * NKB + j] = nf;
+  }
 }
 
 }  // namespace
@@ -454,7 +486,7 @@ hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
   if (L.q_num) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    transpose_kernel<<<dim3((L.NKB + 63) / 64, L.Bm * L.Hm), 64, 0, stream>>>(
+    transpose_kernel<<<L.Bm * L.Hm, kTransposeThreads, 0, stream>>>(
         L.kv_num, L.kv_idx, L.full_num, L.full_idx, L.NQB, L.NKB, L.q_num, L.q_idx,
         L.full_q_num, L.full_q_idx);
   }

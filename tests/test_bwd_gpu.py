@@ -131,6 +131,18 @@ def test_backward_lists_bit_exact(lib, q_len, kv_len, kind, window, sinks):
         assert np.array_equal(g.cpu().numpy(), e), name
 
 
+@pytest.mark.parametrize("kind", ["noop", "causal"])
+def test_backward_lists_large_grid(lib, kind):
+    """13 x 4096 tiles: more than the LDS class grid holds, so the builder
+    takes its per-KV-tile search path."""
+    ref = oracle.create_block_mask(oracle.mask_mod_for(kind), 1, 1, 1664, 524288, 128)
+    exp = oracle.transpose_block_mask(ref)
+    bm = lib.create_block_mask(kind, 1, 1, 1664, 524288, 128, backward_lists=True)
+    torch.cuda.synchronize()
+    for g, e in zip((bm.q_num_blocks, bm.q_indices, bm.full_q_num_blocks, bm.full_q_indices), exp):
+        assert np.array_equal(g.cpu().numpy(), e)
+
+
 def test_backward_lists_full_workload(lib):
     """The dense causal workload's lists (32 x 32 tiles)."""
     ref = oracle.create_block_mask(oracle.causal_mask, 1, 1, 4096, 4096, 128)
@@ -220,3 +232,69 @@ def test_bwd_deterministic(lib):
     b = run_bwd(lib, w, inp, d_out, bm)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_bwd_explicit_slopes_and_strided_tensors(lib):
+    """Caller-given ALiBi slopes; q, d_out and dq as views of [B, L, H, D]
+    memory (strided), k as a strided view too."""
+    w = tiny(128, "causal", "alibi", B=2, Hq=4, Hkv=2, Q_LEN=256, KV_LEN=256)
+    inp = W.generate(w)
+    g = W.generate_upstream(w)
+    slopes = np.array([0.3, 0.05, 0.0, 1.5], dtype=np.float32)
+    st = lambda x: G.to_device(x.transpose(0, 2, 1, 3), "bf16").transpose(1, 2)  # noqa: E731
+    q, k, gd = st(inp.q), st(inp.k), st(g)
+    assert not q.is_contiguous() and not k.is_contiguous()
+    v = G.to_device(inp.v, "bf16")
+    sl = torch.from_numpy(slopes)
+    bm = mask_of(lib, w, inp)
+    out, lse = lib.flex_attention(q, k, v, bm, score="alibi", alibi_slopes=sl)
+    dq_buf = torch.empty((2, 256, 4, 128), dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    dq, dk, dv = lib.flex_attention_backward(q, k, v, lse, gd, bm, score="alibi", alibi_slopes=sl,
+                                             dq=dq_buf)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(inp.q, inp.k, inp.v, g, oracle.causal_mask,
+                                    oracle.alibi_score(slopes.astype(np.float64)), None, w.scale)
+    for t, r, n in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+        check(t.float().cpu().numpy().astype(np.float64), r, n)
+
+
+@pytest.mark.parametrize("score", ["none", "softcap"])
+def test_bwd_negative_scale(lib, score):
+    """scale < 0 is a plain multiplier on q.k, as in the forward."""
+    w = tiny(128, "sliding_sink", score, B=1, Hq=2, Hkv=1, Q_LEN=300, KV_LEN=300,
+             softcap=5.0).with_(extra={"scale": -0.1})
+    full_check(lib, w)
+
+
+def test_bwd_per_batch_documents(lib):
+    """Per-batch document ids with a BlockMask built per batch."""
+    w = tiny(64, "document_causal", "none", B=2, Hq=2, Hkv=1, Q_LEN=400, KV_LEN=400)
+    inp = W.generate(w)
+    rng = np.random.default_rng(21)
+    docs = []
+    for _ in range(2):
+        lens = []
+        while sum(lens) < 400:
+            lens.append(int(rng.integers(10, 120)))
+        docs.append(W.document_ids(lens)[:400])
+    both = np.stack(docs).astype(np.int32)
+    g = W.generate_upstream(w)
+    bm = lib.create_block_mask("document_causal", 2, 1, 400, 400, 128,
+                               doc_ids=torch.from_numpy(both), backward_lists=True)
+    q, k, v = (G.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    out, lse = lib.flex_attention(q, k, v, bm)
+    dq, dk, dv = lib.flex_attention_backward(q, k, v, lse, G.to_device(g, "bf16"), bm)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(inp.q, inp.k, inp.v, g, oracle.document_causal_mask(both),
+                                    None, None, w.scale)
+    for t, r, n in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+        check(t.float().cpu().numpy().astype(np.float64), r, n)
+
+
+@pytest.mark.parametrize("q_len,kv_len", [(300, 700), (700, 300)])
+def test_bwd_sliding_sinks_unequal_lengths(lib, q_len, kv_len):
+    """Sliding window + sinks with Q_LEN != KV_LEN (tail tiles on both axes,
+    rows beyond the keys, keys beyond the queries)."""
+    w = tiny(128, "sliding_sink", "softcap_alibi", B=1, Hq=4, Hkv=1, Q_LEN=q_len, KV_LEN=kv_len,
+             window=150, sinks=5, value_scale=2.0)
+    full_check(lib, w)

@@ -21,7 +21,8 @@ import torch
 
 __all__ = [
     "BlockMask", "FlexAttnError", "MASK_KINDS", "SCORE_KINDS", "create_block_mask",
-    "flex_attention", "flex_attention_backward", "library_path", "load_library",
+    "flex_attention", "flex_attention_backward", "block_mask_from_kv_blocks", "library_path",
+    "load_library",
     "block_mask_sizes", "version",
 ]
 
@@ -93,6 +94,9 @@ def load_library():
         ctypes.c_int, ctypes.POINTER(_MaskParams), ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.POINTER(_BlockMask), ctypes.c_void_p]
+    lib.flexattn_block_mask_from_kv_blocks.restype = ctypes.c_int
+    lib.flexattn_block_mask_from_kv_blocks.argtypes = [ctypes.POINTER(_BlockMask), ctypes.c_void_p,
+                                                       ctypes.c_void_p]
     lib.flexattn_bwd.restype = ctypes.c_int
     lib.flexattn_bwd.argtypes = [
         ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
@@ -162,6 +166,7 @@ class BlockMask:
     q_indices: Optional[torch.Tensor] = None          # int32 [B, H, NKB, NQB]
     full_q_num_blocks: Optional[torch.Tensor] = None  # int32 [B, H, NKB]
     full_q_indices: Optional[torch.Tensor] = None     # int32 [B, H, NKB, NQB]
+    status: Optional[torch.Tensor] = None             # int32 [1]: from_kv_blocks check flags
 
     @property
     def num_q_blocks(self) -> int:
@@ -327,3 +332,82 @@ def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           ctypes.c_void_p(workspace.data_ptr()), _stream_handle(q.device, stream))
     _check(st, "flexattn_bwd")
     return dq, dk, dv
+
+
+FROM_KV_BLOCKS_FLAGS = {1: "a count outside [0, NKB]", 2: "an index outside [0, NKB)",
+                        4: "a list that is not strictly ascending",
+                        8: "a tile in both the partial and the full list of a row",
+                        16: "a full tile that crosses Q_LEN or KV_LEN"}
+
+
+def block_mask_from_kv_blocks(kv_num_blocks: torch.Tensor, kv_indices: torch.Tensor,
+                              full_kv_num_blocks: Optional[torch.Tensor] = None,
+                              full_kv_indices: Optional[torch.Tensor] = None,
+                              Q_LEN: Optional[int] = None, KV_LEN: Optional[int] = None,
+                              kind: str = "noop", window: int = 0, num_sinks: int = 0,
+                              doc_ids: Optional[torch.Tensor] = None,
+                              backward_lists: bool = False, validate: bool = True,
+                              stream=None) -> BlockMask:
+    """A BlockMask from caller-given tile lists (BlockMask.from_kv_blocks):
+    kv_num_blocks [B, H, NQB] and kv_indices [B, H, NQB, NKB] list the
+    partial tiles (evaluated with the mask `kind`; "noop" makes them dense),
+    the optional full_* lists the tiles computed without the mask. The GPU
+    computes the schedule (and the backward lists) and checks the lists;
+    with validate=True the check is read back (a synchronisation) and bad
+    lists raise RuntimeError."""
+    lib = load_library()
+    if kind not in MASK_KINDS:
+        raise NotImplementedError(f"mask kind {kind!r} is not one of {sorted(MASK_KINDS)}")
+    if kv_num_blocks.dim() != 3 or kv_indices.dim() != 4:
+        raise RuntimeError("kv_num_blocks must be [B, H, NQB] and kv_indices [B, H, NQB, NKB]")
+    device = kv_indices.device
+    B, H, nqb, nkb = kv_indices.shape
+    if tuple(kv_num_blocks.shape) != (B, H, nqb):
+        raise RuntimeError("kv_num_blocks and kv_indices disagree on [B, H, NQB]")
+    Q_LEN = nqb * 128 if Q_LEN is None else Q_LEN
+    KV_LEN = nkb * 128 if KV_LEN is None else KV_LEN
+    as_i32 = lambda t: t.to(device=device, dtype=torch.int32).contiguous()  # noqa: E731
+    kv_num, kv_idx = as_i32(kv_num_blocks), as_i32(kv_indices)
+    if full_kv_num_blocks is None:
+        full_num = torch.zeros_like(kv_num)
+        full_idx = torch.zeros_like(kv_idx)
+    else:
+        full_num, full_idx = as_i32(full_kv_num_blocks), as_i32(full_kv_indices)
+        if full_num.shape != kv_num.shape or full_idx.shape != kv_idx.shape:
+            raise RuntimeError("full_* lists must have the shapes of the partial lists")
+    sched = torch.empty((B * H * nqb,), dtype=torch.int32, device=device)
+    status = torch.empty((1,), dtype=torch.int32, device=device)
+    c = _BlockMask()
+    c.B, c.H, c.Q_LEN, c.KV_LEN, c.BLOCK_SIZE = B, H, Q_LEN, KV_LEN, 128
+    c.num_q_blocks, c.num_kv_blocks = -(-Q_LEN // 128), -(-KV_LEN // 128)
+    c.kv_num_blocks, c.kv_indices = kv_num.data_ptr(), kv_idx.data_ptr()
+    c.full_kv_num_blocks, c.full_kv_indices = full_num.data_ptr(), full_idx.data_ptr()
+    c.schedule = sched.data_ptr()
+    c.mask_kind = MASK_KINDS[kind]
+    mp = _MaskParams(window, num_sinks, None, 0, 0)
+    if kind == "document_causal":
+        if doc_ids is None:
+            raise ValueError("document_causal needs doc_ids")
+        doc_ids = doc_ids.to(device=device, dtype=torch.int32)
+        doc_ids = (doc_ids.unsqueeze(0) if doc_ids.dim() == 1 else doc_ids).contiguous()
+        mp.doc_ids, mp.doc_batch, mp.doc_len = doc_ids.data_ptr(), doc_ids.shape[0], doc_ids.shape[1]
+    c.mask_params = mp
+    qlists = [None] * 4
+    if backward_lists:
+        qlists = [torch.empty((B, H, nkb), dtype=torch.int32, device=device),
+                  torch.empty((B, H, nkb, nqb), dtype=torch.int32, device=device),
+                  torch.empty((B, H, nkb), dtype=torch.int32, device=device),
+                  torch.empty((B, H, nkb, nqb), dtype=torch.int32, device=device)]
+        c.q_num_blocks, c.q_indices, c.full_q_num_blocks, c.full_q_indices = (
+            t.data_ptr() for t in qlists)
+    st = lib.flexattn_block_mask_from_kv_blocks(ctypes.byref(c), ctypes.c_void_p(status.data_ptr()),
+                                                _stream_handle(device, stream))
+    _check(st, "flexattn_block_mask_from_kv_blocks")
+    bm = BlockMask(kind, B, H, Q_LEN, KV_LEN, 128, kv_num, kv_idx, full_num, full_idx, sched,
+                   doc_ids, c, *qlists, status=status)
+    if validate:
+        flags = int(status.item())
+        if flags:
+            reasons = [text for bit, text in FROM_KV_BLOCKS_FLAGS.items() if flags & bit]
+            raise RuntimeError("invalid kv block lists: " + "; ".join(reasons))
+    return bm

@@ -199,6 +199,62 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
   return ok();
 }
 
+flexattn_status flexattn_block_mask_from_kv_blocks(flexattn_block_mask* bm, int32_t* status,
+                                                   void* stream) {
+  static const char* who = "flexattn_block_mask_from_kv_blocks";
+  if (!bm) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: bm is NULL", who);
+  if (!status) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: status is NULL", who);
+  if (bm->B < 1 || bm->H < 1 || bm->Q_LEN < 1 || bm->KV_LEN < 1)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: B, H, Q_LEN, KV_LEN must be >= 1", who);
+  if (bm->BLOCK_SIZE != fa::kBlock)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: BLOCK_SIZE must be 128 (got %d)", who,
+                bm->BLOCK_SIZE);
+  const int nqb = ceil_div(bm->Q_LEN, fa::kBlock), nkb = ceil_div(bm->KV_LEN, fa::kBlock);
+  if (bm->num_q_blocks != nqb || bm->num_kv_blocks != nkb)
+    return fail(FLEXATTN_ERR_INVALID_ARG,
+                "%s: num_q_blocks / num_kv_blocks must be %d / %d for these lengths", who, nqb,
+                nkb);
+  if (nkb > fa::max_build_kv_blocks())
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: KV_LEN %d exceeds the builder limit of %d tiles",
+                who, bm->KV_LEN, fa::max_build_kv_blocks());
+  if ((long long)bm->B * bm->H * nqb > 0x7fffffffLL / (nkb > 0 ? nkb : 1))
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: index tensor too large", who);
+  if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices ||
+      !bm->schedule)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: a BlockMask buffer pointer is NULL", who);
+  fa::MaskParams mp;
+  int doc_len = 0;
+  flexattn_status st =
+      check_mask(bm->mask_kind, &bm->mask_params, bm->B, bm->Q_LEN, bm->KV_LEN, &mp, &doc_len, who);
+  if (st != FLEXATTN_OK) return st;
+  fa::BuildLaunch L;
+  L.kind = (int)bm->mask_kind;
+  L.mp = mp;
+  L.doc_len = doc_len;
+  L.Bm = bm->B;
+  L.Hm = bm->H;
+  L.Q_LEN = bm->Q_LEN;
+  L.KV_LEN = bm->KV_LEN;
+  L.NQB = nqb;
+  L.NKB = nkb;
+  L.kv_num = bm->kv_num_blocks;
+  L.kv_idx = bm->kv_indices;
+  L.full_num = bm->full_kv_num_blocks;
+  L.full_idx = bm->full_kv_indices;
+  L.schedule = bm->schedule;
+  L.separate_full = 1;
+  const bool with_q = bm->q_num_blocks && bm->q_indices && bm->full_q_num_blocks &&
+                      bm->full_q_indices;
+  L.q_num = with_q ? bm->q_num_blocks : nullptr;
+  L.q_idx = with_q ? bm->q_indices : nullptr;
+  L.full_q_num = with_q ? bm->full_q_num_blocks : nullptr;
+  L.full_q_idx = with_q ? bm->full_q_indices : nullptr;
+  hipError_t e = fa::launch_from_kv_blocks(L, status, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(FLEXATTN_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
 flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
                              const flexattn_tensor* v, const flexattn_block_mask* bm,
                              flexattn_score_kind score_kind, const flexattn_score_params* params,

@@ -314,7 +314,9 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int* kv_n
     running[c] = 0;
   }
   __syncthreads();
-  for (int i = t; i < n; i += kSchedThreads) atomicAdd(&hist[kv_num[i] + full_num[i]], 1);
+  // keys are clamped to the bins (caller-given lists may hold bad counts)
+  for (int i = t; i < n; i += kSchedThreads)
+    atomicAdd(&hist[min(max(kv_num[i] + full_num[i], 0), nbins - 1)], 1);
   __syncthreads();
   // offsets for descending keys: off[c] = sum_{c' > c} hist[c']. Thread t owns
   // the contiguous bins (hi_bin - seg, hi_bin], scanned from the top.
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int* kv_n
   __syncthreads();
   for (int base = 0; base < n; base += kSchedThreads) {
     const int i = base + t;
-    const int key = (i < n) ? kv_num[i] + full_num[i] : -1;
+    const int key = (i < n) ? min(max(kv_num[i] + full_num[i], 0), nbins - 1) : -1;
     keys[t] = key;
     __syncthreads();
     if (i < n) {
@@ -428,7 +430,64 @@ __global__ __launch_bounds__(kTransposeThreads) void transpose_kernel(
   }
 }
 
+// Checks of caller-given lists (from_kv_blocks): one 128-thread workgroup per
+// row. Flags OR-ed into *status: 1 a count outside [0, NKB]; 2 an index
+// outside [0, NKB); 4 a list not strictly ascending; 8 a tile in both lists;
+// 16 a full tile that is not entirely inside Q_LEN x KV_LEN (a full tile has
+// all BLOCK_SIZE^2 elements allowed, so it cannot cross a sequence end).
+__global__ void clear_status_kernel(int* status) { *status = 0; }
+
+__global__ __launch_bounds__(kRowThreads) void validate_kernel(const int* kv_num, const int* kv_idx,
+                                                             const int* full_num,
+                                                             const int* full_idx, int NQB, int NKB,
+                                                             int Q_LEN, int KV_LEN, int* status) {
+  const long long row = blockIdx.x;
+  const bool q_tail = (int)(row % NQB) * kBlock + kBlock > Q_LEN;
+  const int t = threadIdx.x;
+  const int np_raw = kv_num[row], nf_raw = full_num[row];
+  int flags = 0;
+  if (np_raw < 0 || np_raw > NKB || nf_raw < 0 || nf_raw > NKB) flags |= 1;
+  const int np = min(max(np_raw, 0), NKB), nf = min(max(nf_raw, 0), NKB);
+  const int* P = kv_idx + row * NKB;
+  const int* F = full_idx + row * NKB;
+  for (int u = t; u < np; u += kRowThreads) {
+    const int j = P[u];
+    if (j < 0 || j >= NKB) flags |= 2;
+    if (u > 0 && P[u - 1] >= j) flags |= 4;
+    if (sorted_contains(F, nf, j)) flags |= 8;
+  }
+  for (int u = t; u < nf; u += kRowThreads) {
+    const int j = F[u];
+    if (j < 0 || j >= NKB) flags |= 2;
+    if (u > 0 && F[u - 1] >= j) flags |= 4;
+    if (q_tail || j * kBlock + kBlock > KV_LEN) flags |= 16;
+  }
+  if (flags) atomicOr(status, flags);
+}
+
 }  // namespace
+
+hipError_t launch_from_kv_blocks(const BuildLaunch& L, int* status, hipStream_t stream) {
+  const int rows = L.Bm * L.Hm * L.NQB;
+  clear_status_kernel<<<1, 1, 0, stream>>>(status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  validate_kernel<<<rows, kRowThreads, 0, stream>>>(L.kv_num, L.kv_idx, L.full_num, L.full_idx,
+                                                    L.NQB, L.NKB, L.Q_LEN, L.KV_LEN, status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nbins = L.NKB + 1;
+  schedule_kernel<<<1, kSchedThreads, sizeof(int) * 2 * (size_t)nbins, stream>>>(
+      L.kv_num, L.full_num, rows, nbins, L.schedule);
+  if (L.q_num) {
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    transpose_kernel<<<L.Bm * L.Hm, kTransposeThreads, 0, stream>>>(
+        L.kv_num, L.kv_idx, L.full_num, L.full_idx, L.NQB, L.NKB, L.q_num, L.q_idx,
+        L.full_q_num, L.full_q_idx);
+  }
+  return hipGetLastError();
+}
 
 int max_build_kv_blocks() {
   // 2*NKB+1 ints of dynamic LDS for the classify kernel, two int arrays of

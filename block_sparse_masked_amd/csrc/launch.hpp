@@ -28,6 +28,8 @@ struct BuildLaunch {
 };
 
 hipError_t launch_build(const BuildLaunch& L, hipStream_t stream);
+// validation, schedule and backward lists of caller-given tile lists
+hipError_t launch_from_kv_blocks(const BuildLaunch& L, int* status, hipStream_t stream);
 int max_build_kv_blocks();
 
 struct FwdLaunch {

@@ -233,6 +233,28 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
                              float scale, flexattn_tensor* out, float* lse, void* stream);
 
 /*
+ * from_kv_blocks (page "tensorplay.nn.attention API", BlockMask.from_kv_blocks):
+ * completes a BlockMask whose tile lists the caller filled. On input the
+ * caller sets every field of `bm`: the extents, lengths, BLOCK_SIZE (128),
+ * num_q_blocks / num_kv_blocks, mask_kind / mask_params (the mask the
+ * partial tiles are evaluated with; NOOP makes every listed tile dense),
+ * the four list buffers (full counts may be all 0) and schedule; the q_*
+ * buffers are optional as in flexattn_create_block_mask. The call writes
+ * the schedule and, when the q_* buffers are set, the backward lists.
+ * It also checks the lists on the GPU and writes *status (device int32):
+ * 0 when they are valid, else the OR of 1 (a count outside [0, NKB]),
+ * 2 (an index outside [0, NKB)), 4 (a list not strictly ascending),
+ * 8 (a tile in both the partial and the full list of a row) and 16 (a full
+ * tile not entirely inside Q_LEN x KV_LEN: all BLOCK_SIZE^2 elements of a
+ * full tile are allowed, so a tail tile can only be partial). The schedule
+ * and backward lists of invalid lists are meaningless; read *status before
+ * using the BlockMask. Host-side argument errors return as for
+ * flexattn_create_block_mask. Asynchronous on `stream`.
+ */
+flexattn_status flexattn_block_mask_from_kv_blocks(flexattn_block_mask* bm, int32_t* status,
+                                                   void* stream);
+
+/*
  * Backward of flexattn_fwd: the gradients of the forward's output with
  * respect to q, k and v for an upstream gradient d_out (page
  * "tensorplay.nn.attention API", section BlockMask, "Details": dQ walks each

@@ -15,6 +15,7 @@ from .reference import (  # noqa: F401
     create_block_mask,
     create_mask,
     document_causal_mask,
+    from_kv_blocks_mask,
     noop_mask,
     or_masks,
     sink_mask,

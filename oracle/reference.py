@@ -273,6 +273,33 @@ def create_block_mask(mask_mod: MaskMod, B: int, H: int, Q_LEN: int, KV_LEN: int
     return BlockMask(Q_LEN, KV_LEN, blk, kv_num, kv_ind, full_num, full_ind, counts)
 
 
+def from_kv_blocks_mask(kv_num_blocks: np.ndarray, kv_indices: np.ndarray,
+                        full_kv_num_blocks: Optional[np.ndarray] = None,
+                        full_kv_indices: Optional[np.ndarray] = None, BLOCK_SIZE: int = 128,
+                        mask_mod: Optional[MaskMod] = None) -> MaskMod:
+    """The element mask that tile lists given directly stand for (page
+    "tensorplay.nn.attention API", BlockMask.from_kv_blocks, with "Details"
+    items 1 and 2): an element is computed only inside a listed tile; inside
+    a partial tile where mask_mod allows it, inside a full tile always.
+    Lists with extent 1 over batch or heads broadcast."""
+    mask_mod = noop_mask if mask_mod is None else mask_mod
+    blk = int(BLOCK_SIZE)
+    B, H, nqb, nkb = kv_indices.shape
+    cls = np.zeros((B, H, nqb, nkb), dtype=np.int8)
+    for pos in np.ndindex(B, H, nqb):
+        for t in range(int(kv_num_blocks[pos])):
+            cls[pos + (int(kv_indices[pos + (t,)]),)] = 1
+        if full_kv_num_blocks is not None:
+            for t in range(int(full_kv_num_blocks[pos])):
+                cls[pos + (int(full_kv_indices[pos + (t,)]),)] = 2
+
+    def mod(b, h, q_idx, kv_idx):
+        c = cls[b if B > 1 else 0, h if H > 1 else 0][np.asarray(q_idx) // blk,
+                                                       np.asarray(kv_idx) // blk]
+        return np.where(c == 2, True, np.where(c == 1, mask_mod(b, h, q_idx, kv_idx), False))
+    return mod
+
+
 def to_dense(num_blocks: np.ndarray, indices: np.ndarray, num_cols: int) -> np.ndarray:
     """The page's reconstruction loop: mark (row, indices[row, i]) for
     i < num_blocks[row]; leading dims are batch dims."""

@@ -211,3 +211,20 @@ def test_bwd_rejects_bad_arguments(L):
     bad[4] = tens(Lq=128)
     assert _bwd(L, bad, bm) == lib._INVALID
     assert b"shaped like q" in L.flexattn_last_error()
+
+
+def test_from_kv_blocks_rejects_bad_arguments(L):
+    """Host-side checks of from_kv_blocks (no launch happens)."""
+    fn = L.flexattn_block_mask_from_kv_blocks
+    bm = _bm_struct()
+    bm.B, bm.H, bm.Q_LEN, bm.KV_LEN, bm.BLOCK_SIZE = 1, 1, 256, 256, 128
+    bm.num_q_blocks, bm.num_kv_blocks, bm.mask_kind = 2, 2, 0
+    assert fn(ctypes.byref(bm), None, None) == lib._INVALID          # NULL status
+    assert b"status" in L.flexattn_last_error()
+    assert fn(None, ctypes.c_void_p(16), None) == lib._INVALID       # NULL bm
+    bm.num_kv_blocks = 3                                              # inconsistent tile count
+    assert fn(ctypes.byref(bm), ctypes.c_void_p(16), None) == lib._INVALID
+    bm.num_kv_blocks, bm.BLOCK_SIZE = 2, 64
+    assert fn(ctypes.byref(bm), ctypes.c_void_p(16), None) == lib._UNSUPPORTED
+    bm.BLOCK_SIZE, bm.mask_kind = 128, 2                              # sliding window, window 0
+    assert fn(ctypes.byref(bm), ctypes.c_void_p(16), None) == lib._INVALID

@@ -410,3 +410,36 @@ def test_row_subset_equals_full_computation():
         np.testing.assert_allclose(part[1][1, h, [0, 5, 63]], full[1][1, h, [0, 5, 63]],
                                    rtol=0, atol=1e-14)
     assert np.isnan(part[0][0]).all()
+
+
+# ------------------------------------------------------------ from_kv_blocks
+
+@pytest.mark.parametrize("kind", list(SCALAR_MASKS))
+def test_from_kv_blocks_round_trip(kind):
+    """Lists built from a mask_mod, read back through from_kv_blocks with the
+    same mask_mod on partial tiles, give the same element mask."""
+    doc = W.document_ids([5, 1, 20, 13, 61])
+    mm = _oracle_mask(kind, doc)
+    bm = oracle.create_block_mask(mm, 1, 1, 77, 90, 16)
+    back = oracle.from_kv_blocks_mask(bm.kv_num_blocks, bm.kv_indices, bm.full_kv_num_blocks,
+                                      bm.full_kv_indices, 16, mm)
+    assert np.array_equal(oracle.create_mask(back, 1, 1, 77, 90), oracle.create_mask(mm, 1, 1, 77, 90))
+
+
+def test_from_kv_blocks_hand_example():
+    """Block 2, 3 x 3 tiles: row 0 lists tile 1 partial (causal inside) and
+    tile 0 full; row 1 nothing; row 2 tile 2 full. Checked element by
+    element against the definition."""
+    kv_num = np.array([[[1, 0, 0]]])
+    kv_idx = np.array([[[[1, 0, 0], [0, 0, 0], [0, 0, 0]]]])
+    full_num = np.array([[[1, 0, 1]]])
+    full_idx = np.array([[[[0, 0, 0], [0, 0, 0], [2, 0, 0]]]])
+    mod = oracle.from_kv_blocks_mask(kv_num, kv_idx, full_num, full_idx, 2, oracle.causal_mask)
+    got = oracle.create_mask(mod, 1, 1, 6, 6)[0, 0]
+    exp = np.zeros((6, 6), dtype=bool)
+    exp[0:2, 0:2] = True                        # full tile (0, 0)
+    for q in range(2):
+        for kv in range(2, 4):
+            exp[q, kv] = kv <= q                # partial tile (0, 1): causal -> none
+    exp[4:6, 4:6] = True                        # full tile (2, 2)
+    assert np.array_equal(got, exp)

@@ -29,7 +29,7 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libflexattn.so")
 
-MASK_KINDS = {"noop": 0, "causal": 1, "sliding_sink": 2, "document_causal": 3}
+MASK_KINDS = {"noop": 0, "causal": 1, "sliding_sink": 2, "document_causal": 3, "prefix_lm": 4}
 SCORE_KINDS = {"none": 0, "alibi": 1, "softcap": 2, "softcap_alibi": 3}
 _F32, _BF16 = 0, 1
 _OK, _INVALID, _UNSUPPORTED, _HIP = 0, 1, 2, 3
@@ -42,7 +42,7 @@ class FlexAttnError(RuntimeError):
 class _MaskParams(ctypes.Structure):
     _fields_ = [("window", ctypes.c_int32), ("num_sinks", ctypes.c_int32),
                 ("doc_ids", ctypes.c_void_p), ("doc_batch", ctypes.c_int32),
-                ("doc_len", ctypes.c_int32)]
+                ("doc_len", ctypes.c_int32), ("prefix_len", ctypes.c_int32)]
 
 
 class _ScoreParams(ctypes.Structure):
@@ -191,7 +191,7 @@ def create_block_mask(kind: str, B: int, H: int, Q_LEN: int, KV_LEN: int, block:
                       window: int = 0, num_sinks: int = 0,
                       doc_ids: Optional[torch.Tensor] = None,
                       device="cuda", stream=None, separate_full_blocks: bool = True,
-                      backward_lists: bool = False) -> BlockMask:
+                      backward_lists: bool = False, prefix_len: int = 0) -> BlockMask:
     """Build the BlockMask of a mask kind on the GPU (the library's builder
     kernels). B and H may be 1 to broadcast over batch / query heads.
     separate_full_blocks=False lists every non-empty tile as partial, so the
@@ -211,7 +211,7 @@ def create_block_mask(kind: str, B: int, H: int, Q_LEN: int, KV_LEN: int, block:
     full_idx = torch.empty((B, H, nqb, nkb), dtype=torch.int32, device=device)
     sched = torch.empty((n_sched,), dtype=torch.int32, device=device)
     assert kv_num.numel() == n_num and kv_idx.numel() == n_idx
-    mp = _MaskParams(window, num_sinks, None, 0, 0)
+    mp = _MaskParams(window, num_sinks, None, 0, 0, prefix_len)
     if kind == "document_causal":
         if doc_ids is None:
             raise ValueError("document_causal needs doc_ids")
@@ -347,7 +347,7 @@ def block_mask_from_kv_blocks(kv_num_blocks: torch.Tensor, kv_indices: torch.Ten
                               kind: str = "noop", window: int = 0, num_sinks: int = 0,
                               doc_ids: Optional[torch.Tensor] = None,
                               backward_lists: bool = False, validate: bool = True,
-                              stream=None) -> BlockMask:
+                              stream=None, prefix_len: int = 0) -> BlockMask:
     """A BlockMask from caller-given tile lists (BlockMask.from_kv_blocks):
     kv_num_blocks [B, H, NQB] and kv_indices [B, H, NQB, NKB] list the
     partial tiles (evaluated with the mask `kind`; "noop" makes them dense),
@@ -384,7 +384,7 @@ def block_mask_from_kv_blocks(kv_num_blocks: torch.Tensor, kv_indices: torch.Ten
     c.full_kv_num_blocks, c.full_kv_indices = full_num.data_ptr(), full_idx.data_ptr()
     c.schedule = sched.data_ptr()
     c.mask_kind = MASK_KINDS[kind]
-    mp = _MaskParams(window, num_sinks, None, 0, 0)
+    mp = _MaskParams(window, num_sinks, None, 0, 0, prefix_len)
     if kind == "document_causal":
         if doc_ids is None:
             raise ValueError("document_causal needs doc_ids")

@@ -43,8 +43,9 @@ flexattn_status check_mask(flexattn_mask_kind kind, const flexattn_mask_params* 
   out->sinks = 0;
   out->doc = nullptr;
   out->doc_bstride = 0;
+  out->prefix = 0;
   *doc_len = 0;
-  if ((int)kind < FLEXATTN_MASK_NOOP || (int)kind > FLEXATTN_MASK_DOCUMENT_CAUSAL)
+  if ((int)kind < FLEXATTN_MASK_NOOP || (int)kind > FLEXATTN_MASK_PREFIX_LM)
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: mask_kind %d is not one of the supported kinds", who,
                 (int)kind);
   if (kind == FLEXATTN_MASK_SLIDING_SINK) {
@@ -57,6 +58,13 @@ flexattn_status check_mask(flexattn_mask_kind kind, const flexattn_mask_params* 
                   who, p->num_sinks);
     out->window = p->window;
     out->sinks = p->num_sinks;
+  }
+  if (kind == FLEXATTN_MASK_PREFIX_LM) {
+    if (!p) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: PREFIX_LM needs params", who);
+    if (p->prefix_len < 0)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: PREFIX_LM prefix_len must be >= 0 (got %d)", who,
+                  p->prefix_len);
+    out->prefix = p->prefix_len;
   }
   if (kind == FLEXATTN_MASK_DOCUMENT_CAUSAL) {
     if (!p) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: DOCUMENT_CAUSAL needs params", who);
@@ -168,7 +176,7 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
   if (params) {
     bm->mask_params = *params;
   } else {
-    bm->mask_params = flexattn_mask_params{0, 0, nullptr, 0, 0};
+    bm->mask_params = flexattn_mask_params{0, 0, nullptr, 0, 0, 0};
   }
 
   fa::BuildLaunch L;

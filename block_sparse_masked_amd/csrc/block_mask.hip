@@ -196,6 +196,10 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
   } else if constexpr (KIND == MASK_CAUSAL) {
     lo1 = 0;
     hi1 = q;
+  } else if constexpr (KIND == MASK_PREFIX_LM) {
+    // [0, q] u [0, prefix - 1] is one interval
+    lo1 = 0;
+    hi1 = max(q, a.mp.prefix - 1);
   } else {  // SLIDING_SINK
     lo1 = max(0, q - a.mp.window + 1);
     hi1 = q;
@@ -523,6 +527,9 @@ hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
       break;
     case MASK_SLIDING_SINK:
       classify_kernel<MASK_SLIDING_SINK><<<rows, kRowThreads, lds, stream>>>(a);
+      break;
+    case MASK_PREFIX_LM:
+      classify_kernel<MASK_PREFIX_LM><<<rows, kRowThreads, lds, stream>>>(a);
       break;
     default: {
       // sortedness flags of each document row (1 or Bm rows) in NQB chunks

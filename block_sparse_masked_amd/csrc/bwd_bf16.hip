@@ -145,6 +145,8 @@ __device__ __forceinline__ bool allowed_el(const MaskParams& mp, int q, int kv, 
     return kv <= q;
   } else if constexpr (MASK == MASK_SLIDING_SINK) {
     return kv <= q && ((q - kv) < mp.window || kv < mp.sinks);
+  } else if constexpr (MASK == MASK_PREFIX_LM) {
+    return kv <= q || kv < mp.prefix;
   } else {
     return kv <= q && dq == dkv;
   }
@@ -548,6 +550,7 @@ hipError_t dispatch_mask(const BwdArgs& a, int mask, int score, hipStream_t stre
     case MASK_NOOP: return dispatch_score<D, MASK_NOOP>(a, score, stream);
     case MASK_CAUSAL: return dispatch_score<D, MASK_CAUSAL>(a, score, stream);
     case MASK_SLIDING_SINK: return dispatch_score<D, MASK_SLIDING_SINK>(a, score, stream);
+    case MASK_PREFIX_LM: return dispatch_score<D, MASK_PREFIX_LM>(a, score, stream);
     default: return dispatch_score<D, MASK_DOCUMENT>(a, score, stream);
   }
 }

@@ -10,7 +10,13 @@ constexpr int kBlock = 128;  // BlockMask tile edge (queries and keys)
 
 // Kinds, mirrored from the C header's enums (kept numeric so kernels can be
 // templated on them).
-enum MaskKind : int { MASK_NOOP = 0, MASK_CAUSAL = 1, MASK_SLIDING_SINK = 2, MASK_DOCUMENT = 3 };
+enum MaskKind : int {
+  MASK_NOOP = 0,
+  MASK_CAUSAL = 1,
+  MASK_SLIDING_SINK = 2,
+  MASK_DOCUMENT = 3,
+  MASK_PREFIX_LM = 4
+};
 enum ScoreKind : int { SCORE_NONE = 0, SCORE_ALIBI = 1, SCORE_SOFTCAP = 2, SCORE_SOFTCAP_ALIBI = 3 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -23,6 +29,7 @@ struct MaskParams {
   int sinks;
   const int* doc;
   long long doc_bstride;
+  int prefix;  // PREFIX_LM: keys [0, prefix) are visible to every query
 };
 
 // The BlockMask as the forward reads it.
@@ -57,6 +64,13 @@ template <>
 struct Mask<MASK_SLIDING_SINK> {
   __device__ __forceinline__ static bool allowed(const MaskParams& p, const int*, int q, int kv) {
     return kv <= q && ((q - kv) < p.window || kv < p.sinks);
+  }
+};
+
+template <>
+struct Mask<MASK_PREFIX_LM> {
+  __device__ __forceinline__ static bool allowed(const MaskParams& p, const int*, int q, int kv) {
+    return kv <= q || kv < p.prefix;
   }
 };
 

@@ -281,7 +281,8 @@ __device__ __forceinline__ MaskLimits mask_limits(int kv0, const FwdArgs& a, con
   const int base = kv0 + 4 * ln.hh;
   MaskLimits m;
   m.hi = a.KV_LEN - 1 - base;
-  if constexpr (MASK != MASK_NOOP) m.hi = min(m.hi, ln.qc - base);
+  if constexpr (MASK == MASK_PREFIX_LM) m.hi = min(m.hi, max(ln.qc, a.mp.prefix - 1) - base);
+  else if constexpr (MASK != MASK_NOOP) m.hi = min(m.hi, ln.qc - base);
   m.win_lo = ln.qc - base - a.mp.window;
   m.sink_hi = a.mp.sinks - base;
   return m;
@@ -604,6 +605,8 @@ hipError_t dispatch_mask(const FwdArgs& args, int mask, int score, int grid, hip
       return dispatch_score<D, MASK_CAUSAL, HEADS>(args, score, grid, stream);
     case MASK_SLIDING_SINK:
       return dispatch_score<D, MASK_SLIDING_SINK, HEADS>(args, score, grid, stream);
+    case MASK_PREFIX_LM:
+      return dispatch_score<D, MASK_PREFIX_LM, HEADS>(args, score, grid, stream);
     default:
       return dispatch_score<D, MASK_DOCUMENT, HEADS>(args, score, grid, stream);
   }

@@ -220,6 +220,8 @@ hipError_t f32_dispatch_mask(const F32Args& args, int mask, int score, int grid,
       return f32_dispatch_score<D, MASK_CAUSAL>(args, score, grid, stream);
     case MASK_SLIDING_SINK:
       return f32_dispatch_score<D, MASK_SLIDING_SINK>(args, score, grid, stream);
+    case MASK_PREFIX_LM:
+      return f32_dispatch_score<D, MASK_PREFIX_LM>(args, score, grid, stream);
     default:
       return f32_dispatch_score<D, MASK_DOCUMENT>(args, score, grid, stream);
   }

@@ -54,12 +54,16 @@ typedef enum {
  *                    attention inside each packed document, the
  *                    block-diagonal mask of page "Attention Backends"
  *                    (section "Why care about Attention Kernels?").
+ *   PREFIX_LM        kv_idx < prefix_len OR kv_idx <= q_idx: every query sees
+ *                    the whole prefix, causal after it (PrefixLM, named on
+ *                    the same page and section).
  */
 typedef enum {
   FLEXATTN_MASK_NOOP = 0,
   FLEXATTN_MASK_CAUSAL = 1,
   FLEXATTN_MASK_SLIDING_SINK = 2,
-  FLEXATTN_MASK_DOCUMENT_CAUSAL = 3
+  FLEXATTN_MASK_DOCUMENT_CAUSAL = 3,
+  FLEXATTN_MASK_PREFIX_LM = 4
 } flexattn_mask_kind;
 
 typedef struct {
@@ -69,6 +73,7 @@ typedef struct {
                               read through both q_idx and kv_idx; any id values */
   int32_t doc_batch;       /* DOCUMENT_CAUSAL: 1 (shared by all batches) or B     */
   int32_t doc_len;         /* DOCUMENT_CAUSAL: >= max(Q_LEN, KV_LEN)              */
+  int32_t prefix_len;      /* PREFIX_LM: >= 0                                     */
 } flexattn_mask_params;
 
 /*

@@ -18,6 +18,7 @@ from .reference import (  # noqa: F401
     from_kv_blocks_mask,
     noop_mask,
     or_masks,
+    prefix_lm_mask,
     sink_mask,
     sliding_sink_mask,
     softcap_alibi_score,
@@ -34,7 +35,7 @@ from .backward import (  # noqa: F401
 )
 
 
-def mask_mod_for(kind: str, window: int = 0, sinks: int = 0, doc_ids=None):
+def mask_mod_for(kind: str, window: int = 0, sinks: int = 0, doc_ids=None, prefix: int = 0):
     """The oracle mask_mod for a mask kind name."""
     if kind == "noop":
         return noop_mask
@@ -46,6 +47,8 @@ def mask_mod_for(kind: str, window: int = 0, sinks: int = 0, doc_ids=None):
         if doc_ids is None:
             raise ValueError("document_causal needs doc_ids")
         return document_causal_mask(doc_ids)
+    if kind == "prefix_lm":
+        return prefix_lm_mask(prefix)
     raise ValueError(f"unknown mask kind {kind!r}")
 
 
@@ -66,6 +69,6 @@ def score_mod_for(kind: str, num_heads: int, softcap: float = 0.0, slopes=None):
 
 def for_workload(w, inputs):
     """(mask_mod, score_mod) of a ``workloads.Workload`` and its inputs."""
-    mask = mask_mod_for(w.mask, w.window, w.sinks, inputs.doc_ids)
+    mask = mask_mod_for(w.mask, w.window, w.sinks, inputs.doc_ids, w.prefix)
     score = score_mod_for(w.score, w.Hq, w.softcap)
     return mask, score

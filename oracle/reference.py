@@ -104,6 +104,17 @@ def sliding_sink_mask(window: int, num_sinks: int) -> MaskMod:
     return and_masks(causal_mask, or_masks(window_mask(window), sink_mask(num_sinks)))
 
 
+def prefix_lm_mask(prefix_len: int) -> MaskMod:
+    """PrefixLM (named on page "Attention Backends", section "Why care about
+    Attention Kernels?"): every query sees the first prefix_len keys, and
+    causally after them: or_masks(kv_idx < prefix_len, causal_mask)."""
+    prefix_len = int(prefix_len)
+
+    def in_prefix(b, h, q_idx, kv_idx):
+        return kv_idx < prefix_len
+    return or_masks(in_prefix, causal_mask)
+
+
 def document_causal_mask(doc_ids: np.ndarray) -> MaskMod:
     """Block-diagonal causal mask over packed documents.
 

@@ -26,7 +26,7 @@ def build_gpu_mask(lib, w: W.Workload, inputs: W.Inputs, B_mask=1, H_mask=1,
         doc = torch.from_numpy(inputs.doc_ids.astype(np.int32))
     return lib.create_block_mask(w.mask, B_mask, H_mask, w.Q_LEN, w.KV_LEN, 128,
                                  window=w.window, num_sinks=w.sinks, doc_ids=doc,
-                                 separate_full_blocks=separate_full_blocks)
+                                 separate_full_blocks=separate_full_blocks, prefix_len=w.prefix)
 
 
 def run_gpu(lib, w: W.Workload, inputs: W.Inputs, bm=None):

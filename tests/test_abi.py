@@ -83,6 +83,10 @@ def test_create_block_mask_rejects_bad_arguments(L):
     assert _create(L, 3, lib._MaskParams(0, 0, 64, 1, 100)) == lib._INVALID
     assert b"doc_len" in L.flexattn_last_error()
     assert _create(L, 3, lib._MaskParams(0, 0, 64, 3, 256), B=2) == lib._INVALID
+    # PrefixLM needs params with prefix_len >= 0
+    assert _create(L, 4, None) == lib._INVALID
+    assert _create(L, 4, lib._MaskParams(0, 0, None, 0, 0, -1)) == lib._INVALID
+    assert b"prefix_len" in L.flexattn_last_error()
     # builder limit on KV length
     assert _create(L, 1, mp, K=128 * 5000) == lib._UNSUPPORTED
 
@@ -160,7 +164,7 @@ def test_fwd_rejects_mismatched_block_mask(L):
 def test_python_wrapper_maps_errors():
     import torch
     with pytest.raises(NotImplementedError):
-        lib.create_block_mask("prefix_lm", 1, 1, 128, 128, device="cpu")
+        lib.create_block_mask("dilated", 1, 1, 128, 128, device="cpu")
     q = torch.zeros(1, 1, 128, 64)
     with pytest.raises(ValueError, match="GPU tensor"):
         lib._tensor(q, "q")

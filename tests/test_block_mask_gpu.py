@@ -139,3 +139,13 @@ def test_builder_deterministic(lib):
     torch.cuda.synchronize()
     for name in ("kv_num_blocks", "kv_indices", "full_kv_num_blocks", "full_kv_indices", "schedule"):
         assert torch.equal(getattr(a, name), getattr(b, name))
+
+
+@pytest.mark.parametrize("q_len,kv_len", SHAPES)
+@pytest.mark.parametrize("prefix", [0, 1, 100, 128, 200, 700])
+def test_builder_prefix_lm(lib, q_len, kv_len, prefix):
+    """PrefixLM lists (prefix shorter than, equal to and beyond a tile, and
+    beyond the keys), bit-exact against the oracle."""
+    ref = oracle.create_block_mask(oracle.prefix_lm_mask(prefix), 1, 1, q_len, kv_len, 128)
+    bm = lib.create_block_mask("prefix_lm", 1, 1, q_len, kv_len, 128, prefix_len=prefix)
+    check(bm, ref)

@@ -46,14 +46,15 @@ def tiny(D, mask, score, B=2, Hq=4, Hkv=2, Q_LEN=300, KV_LEN=300, seed=0, **kw):
                       window=kw.get("window", 100), sinks=kw.get("sinks", 3),
                       doc_seed=kw.get("doc_seed", 77),
                       doc_len_range=kw.get("doc_len_range", (20, 150)), score=score,
-                      softcap=kw.get("softcap", 20.0), value_scale=kw.get("value_scale", 1.0))
+                      softcap=kw.get("softcap", 20.0), value_scale=kw.get("value_scale", 1.0),
+                      prefix=kw.get("prefix", 170))
 
 
 def mask_of(lib, w, inp, B_mask=1, H_mask=1, separate_full_blocks=True):
     doc = torch.from_numpy(inp.doc_ids.astype(np.int32)) if w.mask == "document_causal" else None
     return lib.create_block_mask(w.mask, B_mask, H_mask, w.Q_LEN, w.KV_LEN, 128, window=w.window,
                                  num_sinks=w.sinks, doc_ids=doc, backward_lists=True,
-                                 separate_full_blocks=separate_full_blocks)
+                                 separate_full_blocks=separate_full_blocks, prefix_len=w.prefix)
 
 
 def run_bwd(lib, w, inp, d_out, bm):
@@ -156,7 +157,8 @@ def test_backward_lists_full_workload(lib):
 # ------------------------------------------------------------------ gradients
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal"])
+@pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal",
+                                  "prefix_lm"])
 @pytest.mark.parametrize("score", ["none", "alibi", "softcap", "softcap_alibi"])
 def test_bwd_tiny_grid(lib, D, mask, score):
     """Every head dim x mask x score kind, GQA (2 query heads per KV head),

@@ -27,7 +27,7 @@ def tiny(dtype, D, mask, score, B=2, Hq=4, Hkv=2, Q_LEN=300, KV_LEN=300, seed=0,
                       window=kw.get("window", 100), sinks=kw.get("sinks", 3),
                       doc_seed=kw.get("doc_seed", 77), doc_len_range=kw.get("doc_len_range", (20, 150)),
                       score=score, softcap=kw.get("softcap", 20.0),
-                      value_scale=kw.get("value_scale", 1.0))
+                      value_scale=kw.get("value_scale", 1.0), prefix=kw.get("prefix", 170))
 
 
 def check_full(lib, w, B_mask=1, H_mask=1):
@@ -42,7 +42,8 @@ def check_full(lib, w, B_mask=1, H_mask=1):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal"])
+@pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal",
+                                  "prefix_lm"])
 @pytest.mark.parametrize("score", ["none", "alibi", "softcap", "softcap_alibi"])
 @pytest.mark.parametrize("heads", ["auto", "2"])
 def test_fwd_tiny_grid(lib, dtype, D, mask, score, heads, monkeypatch):

@@ -28,11 +28,12 @@ SCALAR_MASKS = {
     "causal": lambda doc: (lambda b, h, q, kv: kv <= q),
     "sliding_sink": lambda doc: (lambda b, h, q, kv: kv <= q and (q - kv < 40 or kv < 3)),
     "document_causal": lambda doc: (lambda b, h, q, kv: doc[q] == doc[kv] and kv <= q),
+    "prefix_lm": lambda doc: (lambda b, h, q, kv: kv <= q or kv < 10),
 }
 
 
 def _oracle_mask(kind, doc):
-    return oracle.mask_mod_for(kind, window=40, sinks=3, doc_ids=doc)
+    return oracle.mask_mod_for(kind, window=40, sinks=3, doc_ids=doc, prefix=10)
 
 
 @pytest.mark.parametrize("kind", list(SCALAR_MASKS))

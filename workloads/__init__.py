@@ -54,6 +54,7 @@ class Workload:
     softcap: float = 0.0
     value_scale: float = 1.0
     block: int = 128
+    prefix: int = 0  # prefix_lm: keys [0, prefix) visible to every query
     extra: dict = field(default_factory=dict, compare=False)
 
     @property

@@ -117,6 +117,49 @@ def cpu_baseline(w: W.Workload, inp: W.Inputs, budget_s: float = 20.0):
                       f"fp64 NumPy, {dt:.1f} s"}
 
 
+def decode_leg(fa, torch, dev, stream, steps: int):
+    """Split-KV forward on the decode workload (few queries, long KV): HBM
+    bound, so reported as bytes moved per second against the HBM peak. Its
+    inputs are freed before returning."""
+    w = W.DECODE_GQA
+    inp = W.generate(w)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (inp.q, inp.k, inp.v))
+    del inp
+    bm = fa.create_block_mask(w.mask, 1, 1, w.Q_LEN, w.KV_LEN, 128, device=dev, stream=stream)
+    splits = fa.auto_splits(q, bm)
+    lib = fa.load_library()
+    need = lib.flexattn_fwd_splitkv_workspace_bytes(w.B, w.Hq, w.Q_LEN, w.D, splits)
+    ws = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def call():
+        fa.flex_attention(q, k, v, bm, scale=w.scale, out=out, lse=lse, stream=stream,
+                          num_splits=splits, workspace=ws)
+    for _ in range(5):
+        call()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    alg = algorithmic_bytes(w, bm.num_q_blocks, bm.num_kv_blocks)
+    rec = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Q_LEN": w.Q_LEN,
+           "KV_LEN": w.KV_LEN, "D": w.D, "mask": w.mask, "num_splits": splits,
+           "ms_median": round(ms, 4), "calls": steps,
+           "algorithmic_bytes": alg,
+           "achieved_gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+           "peak_gbs": HBM_PEAK_GBS,
+           "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "workspace_bytes": need,
+           "bound": "hbm"}
+    del q, k, v, ws, out, lse
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +176,9 @@ def main(argv=None):
     ap.add_argument("--backward-steps", type=int, default=10,
                     help="after the forward, time this many backward calls (bf16 workloads; "
                          "0 = skip)")
+    ap.add_argument("--decode-steps", type=int, default=20,
+                    help="after the forward, time this many split-KV forwards on the decode "
+                         "workload (%s; 0 = skip)" % W.DECODE_GQA.name)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB "
                          "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -268,6 +314,10 @@ def main(argv=None):
         bwd_ms = float(np.median([a.elapsed_time(b) for a, b in ev_b]))
         backward = {"ms_median": round(bwd_ms, 4), "calls": args.backward_steps}
 
+    decode = None
+    if args.decode_steps > 0:
+        decode = decode_leg(fa, torch, dev, stream, args.decode_steps)
+
     pairs = allowed_pairs_per_head(w, inp.doc_lengths)
     eff_flops = 4.0 * w.D * pairs * w.B * w.Hq
     dense_flops = 4.0 * w.D * w.Q_LEN * w.KV_LEN * w.B * w.Hq
@@ -333,6 +383,8 @@ def main(argv=None):
             "frac_of_peak": round(alg / t / 1e12 / BF16_PEAK_TFLOPS, 4),
             "flop_convention": "10*D per allowed (q, kv) pair and (b, h); executed 18*D"})
         rec["backward"] = backward
+    if decode is not None:
+        rec["decode_splitkv"] = decode
     if inp.doc_lengths is not None:
         rec["config"]["doc_lengths"] = [int(x) for x in inp.doc_lengths]
     if not args.no_cpu_baseline:

@@ -94,6 +94,14 @@ def load_library():
         ctypes.c_int, ctypes.POINTER(_MaskParams), ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.POINTER(_BlockMask), ctypes.c_void_p]
+    lib.flexattn_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.flexattn_fwd_splitkv_workspace_bytes.argtypes = [ctypes.c_int32] * 5
+    lib.flexattn_fwd_splitkv.restype = ctypes.c_int
+    lib.flexattn_fwd_splitkv.argtypes = [
+        ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+        ctypes.POINTER(_BlockMask), ctypes.c_int, ctypes.POINTER(_ScoreParams), ctypes.c_float,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(_Tensor),
+        ctypes.c_void_p, ctypes.c_void_p]
     lib.flexattn_block_mask_from_kv_blocks.restype = ctypes.c_int
     lib.flexattn_block_mask_from_kv_blocks.argtypes = [ctypes.POINTER(_BlockMask), ctypes.c_void_p,
                                                        ctypes.c_void_p]
@@ -259,13 +267,31 @@ def _tensor(t: torch.Tensor, name: str) -> _Tensor:
     return _Tensor(t.data_ptr(), dt, *t.shape, st)
 
 
+def auto_splits(q: torch.Tensor, block_mask: BlockMask, target_workgroups: int = 1024) -> int:
+    """Split count for a bf16 call: enough workgroups to fill the chip
+    (target_workgroups, four per CU) when there are few query tiles, at most
+    the number of KV tiles a row can list, and 1 (no split) otherwise."""
+    if q.dtype != torch.bfloat16:
+        return 1
+    items = q.shape[0] * q.shape[1] * block_mask.num_q_blocks
+    if items >= target_workgroups // 2:
+        return 1
+    return max(1, min(block_mask.num_kv_blocks, target_workgroups // items, 64))
+
+
 def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask,
                    score: str = "none", softcap: float = 0.0,
                    alibi_slopes: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                   stream=None):
+                   stream=None, num_splits: Optional[int] = 1,
+                   workspace: Optional[torch.Tensor] = None):
     """Block-sparse attention forward. q [B,Hq,M,D]; k, v [B,Hkv,N,D].
 
+    num_splits > 1 (bf16) cuts each query tile's KV tiles into that many
+    slices run by separate workgroups and merged afterwards (split-KV, for
+    decode-like calls with few query tiles); None picks a count from the
+    shapes. The workspace (fp32, flexattn_fwd_splitkv_workspace_bytes) is
+    allocated when not given.
     Returns (out [B,Hq,M,D] in q's dtype, lse [B,Hq,M] float32)."""
     lib = load_library()
     if score not in SCORE_KINDS:
@@ -283,6 +309,20 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask
         alibi_slopes = alibi_slopes.to(device=q.device, dtype=torch.float32).contiguous()
         sp.alibi_slopes = alibi_slopes.data_ptr()
     tq, tk, tv, to = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v"), _tensor(out, "out")
+    if num_splits is None:
+        num_splits = auto_splits(q, block_mask)
+    if num_splits > 1:
+        B, Hq, M, D = q.shape
+        need = lib.flexattn_fwd_splitkv_workspace_bytes(B, Hq, M, D, num_splits)
+        if workspace is None:
+            workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
+        st = lib.flexattn_fwd_splitkv(
+            ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(block_mask._c),
+            SCORE_KINDS[score], ctypes.byref(sp), float(scale), int(num_splits),
+            ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+            ctypes.byref(to), ctypes.c_void_p(lse.data_ptr()), _stream_handle(q.device, stream))
+        _check(st, "flexattn_fwd_splitkv")
+        return out, lse
     st = lib.flexattn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
                           ctypes.byref(block_mask._c), SCORE_KINDS[score], ctypes.byref(sp),
                           float(scale), ctypes.byref(to), ctypes.c_void_p(lse.data_ptr()),

@@ -263,11 +263,20 @@ flexattn_status flexattn_block_mask_from_kv_blocks(flexattn_block_mask* bm, int3
   return ok();
 }
 
-flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
-                             const flexattn_tensor* v, const flexattn_block_mask* bm,
-                             flexattn_score_kind score_kind, const flexattn_score_params* params,
-                             float scale, flexattn_tensor* out, float* lse, void* stream) {
-  static const char* who = "flexattn_fwd";
+}  // extern "C"
+
+namespace {
+
+// Bytes of split-KV workspace: fp32 O and LSE per slice, query row and head.
+size_t splitkv_bytes(long long B, long long Hq, long long Q_LEN, long long D, long long splits) {
+  return (size_t)(splits * B * Hq * Q_LEN * (D + 1) * 4);
+}
+
+flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
+                         const flexattn_tensor* v, const flexattn_block_mask* bm,
+                         flexattn_score_kind score_kind, const flexattn_score_params* params,
+                         float scale, flexattn_tensor* out, float* lse, int splits,
+                         void* workspace, size_t workspace_bytes, void* stream, const char* who) {
   flexattn_status st;
   if ((st = check_tensor(q, "q")) != FLEXATTN_OK) return st;
   if ((st = check_tensor(k, "k")) != FLEXATTN_OK) return st;
@@ -344,6 +353,19 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
       (k->stride[2] > fa::kMaxBf16RowStride || v->stride[2] > fa::kMaxBf16RowStride))
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: k/v row stride above %lld elements", who,
                 (long long)fa::kMaxBf16RowStride);
+  if (splits > 1) {
+    if (q->dtype != FLEXATTN_BF16)
+      return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: split-KV is a bf16 path", who);
+    if (splits > 256)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: num_splits %d above 256", who, splits);
+    if (!workspace || !aligned16(workspace))
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: workspace is NULL or not 16-byte aligned", who);
+    if (workspace_bytes < splitkv_bytes(q->B, q->H, q->L, q->D, splits))
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: workspace of %zu bytes is below the %zu needed",
+                  who, workspace_bytes, splitkv_bytes(q->B, q->H, q->L, q->D, splits));
+    if ((long long)q->B * q->H * bm->num_q_blocks * splits > 0x7fffffffLL)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: too many workgroups for one launch", who);
+  }
   fa::FwdLaunch L;
   L.q = q->data;
   L.k = k->data;
@@ -378,12 +400,49 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
   L.bm.Hm = bm->H;
   L.bm.NQB = bm->num_q_blocks;
   L.bm.NKB = bm->num_kv_blocks;
+  if (splits > 1) {
+    L.splits = splits;
+    L.part_o = static_cast<float*>(workspace);
+    L.part_lse = L.part_o + (size_t)splits * q->B * q->H * q->L * q->D;
+  }
   hipError_t e = (q->dtype == FLEXATTN_BF16)
                      ? fa::launch_fwd_bf16(L, static_cast<hipStream_t>(stream))
                      : fa::launch_fwd_f32(L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(FLEXATTN_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
+                             const flexattn_tensor* v, const flexattn_block_mask* bm,
+                             flexattn_score_kind score_kind, const flexattn_score_params* params,
+                             float scale, flexattn_tensor* out, float* lse, void* stream) {
+  return fwd_impl(q, k, v, bm, score_kind, params, scale, out, lse, 1, nullptr, 0, stream,
+                  "flexattn_fwd");
+}
+
+size_t flexattn_fwd_splitkv_workspace_bytes(int32_t B, int32_t Hq, int32_t Q_LEN, int32_t D,
+                                            int32_t num_splits) {
+  if (B < 1 || Hq < 1 || Q_LEN < 1 || D < 1 || num_splits < 1) return 0;
+  return splitkv_bytes(B, Hq, Q_LEN, D, num_splits);
+}
+
+flexattn_status flexattn_fwd_splitkv(const flexattn_tensor* q, const flexattn_tensor* k,
+                                     const flexattn_tensor* v, const flexattn_block_mask* bm,
+                                     flexattn_score_kind score_kind,
+                                     const flexattn_score_params* params, float scale,
+                                     int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                     flexattn_tensor* out, float* lse, void* stream) {
+  static const char* who = "flexattn_fwd_splitkv";
+  if (num_splits < 1)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: num_splits must be >= 1 (got %d)", who,
+                num_splits);
+  return fwd_impl(q, k, v, bm, score_kind, params, scale, out, lse, num_splits, workspace,
+                  workspace_bytes, stream, who);
 }
 
 flexattn_status flexattn_bwd(const flexattn_tensor* q, const flexattn_tensor* k,

@@ -84,6 +84,12 @@ struct FwdArgs {
   float c_scale, c_cap, cap2;
   const float* slopes;
   BlockMaskView bm;
+  // split-KV: each item's tile list is cut into `splits` contiguous slices,
+  // one workgroup each, writing fp32 partial results (O normalised by its
+  // slice's row sum, and the slice's LSE) that a combine pass merges
+  int splits;     // 1: no split, O and LSE written directly
+  float* part_o;  // [splits][B][Hq][Q_LEN][D]
+  float* part_lse;  // [splits][B][Hq][Q_LEN]
 };
 
 // 16-byte chunk swizzle of a K block [NK][D] in LDS: the 16 rows a 16-lane
@@ -411,6 +417,11 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
   // dispatch order -> item; rounds of equal tile count are remapped so the
   // heads sharing a KV head run on one XCD (workgroups go round-robin to XCDs)
   int x = blockIdx.x;
+  int split = 0;
+  if (a.splits > 1) {
+    split = x % a.splits;
+    x /= a.splits;
+  }
   if (a.xcd_round > 0) {
     const int R = a.xcd_round;
     const int r = x / R, u = x - r * R;
@@ -450,8 +461,11 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
   // the counts, so the first step's loads need not wait for the staging
   const int nfull = __builtin_amdgcn_readfirstlane(min(a.bm.full_num[it.mrow], a.bm.NKB));
   const int n = __builtin_amdgcn_readfirstlane(min(nfull + a.bm.kv_num[it.mrow], a.bm.NKB));
-  const int first_full = a.bm.full_idx[lrow];
-  const int first_part = a.bm.kv_idx[lrow];
+  // this workgroup's slice [t_begin, t_end) of the item's tiles
+  const int t_begin = (int)((long long)n * split / a.splits);
+  const int t_end = (int)((long long)n * (split + 1) / a.splits);
+  const int first_tile = t_begin < nfull ? a.bm.full_idx[lrow + t_begin]
+                                         : a.bm.kv_idx[lrow + min(t_begin - nfull, a.bm.NKB - 1)];
   // the item's tiles, full then partial, staged in LDS once
   for (int t = threadIdx.x; t < n; t += THREADS)
     tlist[t] = t < nfull ? a.bm.full_idx[lrow + t] : a.bm.kv_idx[lrow + (t - nfull)];
@@ -478,14 +492,14 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
   float m_ref = -INFINITY;
   float l = 0.0f;
 
-  if (n > 0) {
+  if (t_end > t_begin) {
     // tile indices are clamped into [0, NKB): a malformed BlockMask computes
     // garbage but never reads outside the KV tensors
     auto clamp_kv0 = [&](int idx) { return kBlock * min(max(idx, 0), a.bm.NKB - 1); };
     auto tile_kv0 = [&](int t) { return clamp_kv0(__builtin_amdgcn_readfirstlane(tlist[t])); };
     // prologue: step 0 -> buffer 0, Q^T fragments; then the tile list is
     // visible (barrier in wait_loads_and_sync)
-    int kv0 = clamp_kv0(__builtin_amdgcn_readfirstlane(nfull > 0 ? first_full : first_part));
+    int kv0 = clamp_kv0(__builtin_amdgcn_readfirstlane(first_tile));
     issue_doc(0, kv0);
     kload.issue(kv0, a.KV_LEN, k_lds[0]);
     vload.issue(kv0, a.KV_LEN, v_lds[0]);
@@ -502,14 +516,14 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
     // start it issues the loads of step g + 1 into the other buffer (read by
     // step g - 1, which every wave finished before the last barrier).
     int g = 0;
-    int t_next = 1;
-    int kv_tile_next = n > 1 ? tile_kv0(1) : 0;
+    int t_next = t_begin + 1;
+    int kv_tile_next = t_next < t_end ? tile_kv0(t_next) : 0;
     auto run_tile = [&](auto masked_tag) {
 #pragma unroll
       for (int sub = 0; sub < SPT; ++sub) {
         constexpr bool M = decltype(masked_tag)::value;
         const bool last_sub = sub == SPT - 1;
-        const bool has_next = !last_sub || t_next < n;
+        const bool has_next = !last_sub || t_next < t_end;
         const int kv_nxt = last_sub ? kv_tile_next : kv0 + NK;
         // buffer of this step: with two steps per tile the parity is the
         // sub-step (every tile starts on buffer 0)
@@ -532,20 +546,41 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
         wait_loads_and_sync();
       }
       ++t_next;
-      kv_tile_next = t_next < n ? tile_kv0(t_next) : 0;
+      kv_tile_next = t_next < t_end ? tile_kv0(t_next) : 0;
     };
     // full tiles that end inside KV_LEN take the unmasked path; a full tile
     // crossing KV_LEN (never listed by the builder) is masked on the key bound
     const int nfull_fast =
         (nfull > 0 && tile_kv0(nfull - 1) + kBlock > a.KV_LEN) ? nfull - 1 : nfull;
-    int j = 0;
-    for (; j < nfull_fast; ++j) run_tile(std::false_type{});
-    for (; j < n; ++j) run_tile(std::true_type{});
+    int j = t_begin;
+    for (; j < min(nfull_fast, t_end); ++j) run_tile(std::false_type{});
+    for (; j < t_end; ++j) run_tile(std::true_type{});
   }
 
   // epilogue: O = O_acc / l, LSE = ln(sum) + max
   const float l_tot = l + __shfl_xor(l, 32, 64);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (a.splits > 1) {
+    // this slice's normalised O and LSE (-inf for an empty slice), fp32
+    if (qvalid) {
+      const long long row = (((long long)split * a.B + b) * a.Hq + h) * a.Q_LEN + ln.q;
+      float* orow = a.part_o + row * D;
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float4 v4;
+          v4.x = o[db][4 * gq + 0] * inv;
+          v4.y = o[db][4 * gq + 1] * inv;
+          v4.z = o[db][4 * gq + 2] * inv;
+          v4.w = o[db][4 * gq + 3] * inv;
+          *reinterpret_cast<float4*>(orow + 32 * db + 8 * gq + 4 * ln.hh) = v4;
+        }
+      if (ln.hh == 0)
+        a.part_lse[row] = l_tot > 0.0f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   if (qvalid) {
     u16* orow = a.o + b * a.so0 + h * a.so1 + (long long)ln.q * a.so2;
 #pragma unroll
@@ -619,6 +654,47 @@ hipError_t dispatch_heads(const FwdArgs& args, int heads, int mask, int score, i
   return dispatch_mask<D, 1>(args, mask, score, grid, stream);
 }
 
+// Merge of the split-KV slices, one 64-lane wave per query row: with the
+// slices' LSE_s, LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s
+// (the rescaling of the online softmax, applied across slices).
+template <int D>
+__global__ __launch_bounds__(256) void splitkv_combine_kernel(FwdArgs a) {
+  constexpr int PER = D / 64;  // elements per lane
+  const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) m = fmaxf(m, a.part_lse[s * rows + row]);
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
+  float wsum = 0.0f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < a.splits; ++s) {
+      const float ls = a.part_lse[s * rows + row];
+      const float w = ls == -INFINITY ? 0.0f : fast_exp2((ls - m) * kLog2e);
+      wsum += w;
+      const float* src = a.part_o + (s * rows + row) * D + lane * PER;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, src[i], acc[i]);
+    }
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  const int qi = (int)(row % a.Q_LEN);
+  const long long bh = row / a.Q_LEN;
+  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  u16* orow = a.o + b * a.so0 + h * a.so1 + (long long)qi * a.so2 + lane * PER;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const __bf16 v = (__bf16)(acc[i] * inv);
+    __builtin_memcpy(orow + i, &v, 2);
+  }
+  if (lane == 0)
+    a.lse[((long long)b * a.Hq + h) * a.Q_LEN + qi] =
+        wsum > 0.0f ? m + fast_log2(wsum) * kLn2 : -INFINITY;
+}
+
 }  // namespace
 
 int fwd_bf16_lds_bytes(int D, int NKB) {
@@ -650,11 +726,14 @@ hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream) {
   a.cap2 = L.softcap * kLog2e;
   a.slopes = L.slopes;
   a.bm = L.bm;
+  a.splits = L.splits > 1 ? L.splits : 1;
+  a.part_o = L.part_o;
+  a.part_lse = L.part_lse;
   // Two query heads per workgroup are possible when they share a KV head and
   // a BlockMask row (mask broadcast over heads, even GQA group); one head per
   // workgroup is the default, FLEXATTN_BF16_HEADS=2 selects the pairs (only
   // where they apply).
-  const bool pair_ok = L.bm.Hm == 1 && a.G % 2 == 0;
+  const bool pair_ok = L.bm.Hm == 1 && a.G % 2 == 0 && a.splits == 1;
   int heads = 1;  // measured: two 4-wave workgroups per CU beat one 8-wave one
   if (const char* env = getenv("FLEXATTN_BF16_HEADS")) {
     if (env[0] == '1') heads = 1;
@@ -666,12 +745,18 @@ hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream) {
   const int R = L.B * L.Hq / heads;
   const int g_items = a.G / heads;  // items per KV group
   a.xcd_round = (L.bm.Bm == 1 && L.bm.Hm == 1 && R % 8 == 0 && (R / 8) % g_items == 0) ? R : 0;
-  const int grid = R * L.bm.NQB;
+  const int grid = R * L.bm.NQB * a.splits;
   if (grid == 0) return hipSuccess;
   // the unscaled fast path takes the row max before scaling: scale must be > 0
   const int score = (L.score_kind == SCORE_NONE && !(L.scale > 0.0f)) ? SCORE_SCALED : L.score_kind;
-  if (L.D == 128) return dispatch_heads<128>(a, heads, L.mask_kind, score, grid, stream);
-  return dispatch_heads<64>(a, heads, L.mask_kind, score, grid, stream);
+  hipError_t e = (L.D == 128) ? dispatch_heads<128>(a, heads, L.mask_kind, score, grid, stream)
+                              : dispatch_heads<64>(a, heads, L.mask_kind, score, grid, stream);
+  if (e != hipSuccess || a.splits == 1) return e;
+  const long long rows = (long long)L.B * L.Hq * L.Q_LEN;
+  const unsigned blocks = (unsigned)((rows + 3) / 4);
+  if (L.D == 128) splitkv_combine_kernel<128><<<blocks, 256, 0, stream>>>(a);
+  else splitkv_combine_kernel<64><<<blocks, 256, 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace fa

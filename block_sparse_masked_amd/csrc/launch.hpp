@@ -49,6 +49,9 @@ struct FwdLaunch {
   const float* slopes;  // device [Hq] or nullptr
   float scale;
   BlockMaskView bm;
+  int splits = 1;             // bf16 split-KV slices per item (1: none)
+  float* part_o = nullptr;    // workspace [splits][B][Hq][Q_LEN][D] fp32
+  float* part_lse = nullptr;  // workspace [splits][B][Hq][Q_LEN] fp32
 };
 
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream);

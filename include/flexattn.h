@@ -238,6 +238,30 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
                              float scale, flexattn_tensor* out, float* lse, void* stream);
 
 /*
+ * Split-KV forward for calls with few query tiles and long KV lists (decode
+ * and short prefills): each query tile's KV tile list is cut into
+ * num_splits contiguous slices, one workgroup each, so the launch fills the
+ * chip; each slice writes its normalised O and its LSE in fp32 to
+ * `workspace`, and a combine pass merges them (LSE = ln sum exp LSE_s,
+ * O = sum exp(LSE_s - LSE) O_s), which is the online softmax's rescaling
+ * applied across slices. Same method and outputs as flexattn_fwd (section
+ * "Details" of page "tensorplay.nn.attention API", items 1 and 2), bf16 only
+ * (UNSUPPORTED otherwise), 1 <= num_splits <= 256; num_splits = 1 is
+ * flexattn_fwd. workspace: device memory of at least
+ * flexattn_fwd_splitkv_workspace_bytes(B, Hq, Q_LEN, D, num_splits) bytes,
+ * 16-byte aligned, caller-allocated and overwritten. Asynchronous on
+ * `stream`.
+ */
+size_t flexattn_fwd_splitkv_workspace_bytes(int32_t B, int32_t Hq, int32_t Q_LEN, int32_t D,
+                                            int32_t num_splits);
+flexattn_status flexattn_fwd_splitkv(const flexattn_tensor* q, const flexattn_tensor* k,
+                                     const flexattn_tensor* v, const flexattn_block_mask* bm,
+                                     flexattn_score_kind score_kind,
+                                     const flexattn_score_params* params, float scale,
+                                     int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                     flexattn_tensor* out, float* lse, void* stream);
+
+/*
  * from_kv_blocks (page "tensorplay.nn.attention API", BlockMask.from_kv_blocks):
  * completes a BlockMask whose tile lists the caller filled. On input the
  * caller sets every field of `bm`: the extents, lengths, BLOCK_SIZE (128),

@@ -232,3 +232,44 @@ def test_from_kv_blocks_rejects_bad_arguments(L):
     assert fn(ctypes.byref(bm), ctypes.c_void_p(16), None) == lib._UNSUPPORTED
     bm.BLOCK_SIZE, bm.mask_kind = 128, 2                              # sliding window, window 0
     assert fn(ctypes.byref(bm), ctypes.c_void_p(16), None) == lib._INVALID
+
+
+def _fwd_split(L, splits, ws=4096, ws_bytes=1 << 30, q=None, k=None, v=None, o=None):
+    q = _tensor() if q is None else q
+    k = _tensor() if k is None else k
+    v = _tensor() if v is None else v
+    o = _tensor() if o is None else o
+    bm = _good_bm()
+    sp = lib._ScoreParams(0.0, None)
+    return L.flexattn_fwd_splitkv(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                  ctypes.byref(bm), 0, ctypes.byref(sp), 0.125, splits,
+                                  ctypes.c_void_p(ws), ws_bytes, ctypes.byref(o),
+                                  ctypes.c_void_p(4096), None)
+
+
+def test_splitkv_workspace_bytes(L):
+    fn = L.flexattn_fwd_splitkv_workspace_bytes
+    fn.restype = ctypes.c_size_t
+    # fp32 partial O [splits][B][Hq][Q_LEN][D] then partial LSE [splits][B][Hq][Q_LEN]
+    assert fn(2, 8, 16, 128, 4) == 4 * (4 * 2 * 8 * 16 * 128 + 4 * 2 * 8 * 16)
+    assert fn(1, 1, 1, 64, 1) == 4 * (64 + 1)
+    assert fn(0, 1, 1, 64, 2) == 0 and fn(1, 1, 1, 64, 0) == 0
+
+
+@pytest.mark.parametrize("case,expect,msg", [
+    (dict(splits=0), lib._INVALID, b"num_splits"),
+    (dict(splits=257), lib._INVALID, b"above 256"),
+    (dict(splits=2, ws=0), lib._INVALID, b"workspace"),
+    (dict(splits=2, ws=4100), lib._INVALID, b"16-byte"),
+    (dict(splits=2, ws_bytes=1000), lib._INVALID, b"below"),
+])
+def test_splitkv_rejects_bad_arguments(L, case, expect, msg):
+    # the default tensors are bf16 (dtype 1): the checks past the dtype run
+    assert _fwd_split(L, **case) == expect
+    assert msg in L.flexattn_last_error()
+
+
+def test_splitkv_is_bf16_only(L):
+    t = [_tensor(dtype=0) for _ in range(4)]
+    assert _fwd_split(L, 2, q=t[0], k=t[1], v=t[2], o=t[3]) == lib._UNSUPPORTED
+    assert b"bf16" in L.flexattn_last_error()

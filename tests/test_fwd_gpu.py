@@ -224,3 +224,60 @@ def test_full_workload_sampled(lib, w):
         results.append(G.compare(w, o, lse, o_ref, lse_ref))
     for r in results:
         assert r["ok"], (w.name, G.summary(r))
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7])
+@pytest.mark.parametrize("mask,score", [("noop", "none"), ("sliding_sink", "alibi"),
+                                        ("document_causal", "softcap_alibi"),
+                                        ("prefix_lm", "none")])
+@pytest.mark.parametrize("q_len,kv_len", [(1, 2000), (16, 1000), (130, 700)])
+def test_fwd_splitkv(lib, splits, mask, score, q_len, kv_len):
+    """Split-KV forward (slices of each row's KV tiles merged by LSE) against
+    the oracle: decode-like lengths, GQA, every slice count including slices
+    with no tiles (7 slices of 6 tiles)."""
+    w = tiny("bf16", 128, mask, score, B=2, Hq=4, Hkv=2, Q_LEN=q_len, KV_LEN=kv_len,
+             window=300, prefix=50, value_scale=2.0 if "softcap" in score else 1.0)
+    inp = W.generate(w)
+    bm = G.build_gpu_mask(lib, w, inp)
+    q, k, v = (G.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    out, lse = lib.flex_attention(q, k, v, bm, score=w.score, softcap=w.softcap, scale=w.scale,
+                                  num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = G.oracle_rows(w, inp)
+    res = G.compare(w, out.float().cpu().numpy().astype(np.float64),
+                    lse.cpu().numpy().astype(np.float64), o_ref, lse_ref)
+    assert res["ok"], G.summary(res)
+
+
+def test_fwd_splitkv_empty_rows_and_auto(lib):
+    """Rows with no allowed key stay O = 0, LSE = -inf through the merge; the
+    automatic split count gives the same result as the oracle."""
+    w = tiny("bf16", 64, "sliding_sink", "none", B=1, Hq=2, Hkv=1, Q_LEN=400, KV_LEN=150,
+             window=60, sinks=0)
+    inp = W.generate(w)
+    bm = G.build_gpu_mask(lib, w, inp)
+    q, k, v = (G.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    for splits in (4, None):
+        out, lse = lib.flex_attention(q, k, v, bm, scale=w.scale, num_splits=splits)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = G.oracle_rows(w, inp)
+        res = G.compare(w, out.float().cpu().numpy().astype(np.float64),
+                        lse.cpu().numpy().astype(np.float64), o_ref, lse_ref)
+        assert res["ok"] and res["dead_rows"] > 0 and res["dead_ok"], G.summary(res)
+
+
+def test_fwd_decode_workload_sampled(lib):
+    """The decode workload at full size (B=8, Hq=32, Hkv=8, 16 queries, 32768
+    keys) with the automatic split count, sampled heads against the oracle."""
+    w = W.DECODE_GQA
+    inp = W.generate(w)
+    bm = G.build_gpu_mask(lib, w, inp)
+    q, k, v = (G.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    out, lse = lib.flex_attention(q, k, v, bm, scale=w.scale, num_splits=None)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    l_ = lse.cpu().numpy().astype(np.float64)
+    for b, h in ((0, 0), (3, 17), (7, 31)):
+        o_ref, lse_ref = G.oracle_rows(w, inp, batches=[b], heads=[h])
+        res = G.compare(w, o, l_, o_ref, lse_ref)
+        assert res["ok"] and res["n_rows"] == w.Q_LEN, G.summary(res)

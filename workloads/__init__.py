@@ -81,6 +81,10 @@ DOCUMENT = Workload("document_causal_bf16", B=1, Hq=16, Hkv=16, Q_LEN=16384,
 ALIBI_SOFTCAP = Workload("alibi_softcap_bf16", B=2, Hq=16, Hkv=16, Q_LEN=8192,
                          KV_LEN=8192, D=128, dtype="bf16", seed=5, mask="causal",
                          score="softcap_alibi", softcap=50.0, value_scale=2.0)
+# Decode-shaped calls (few queries, long KV): not a headline configuration;
+# measured on the HBM roofline with the split-KV path.
+DECODE_GQA = Workload("decode_gqa_bf16", B=8, Hq=32, Hkv=8, Q_LEN=16, KV_LEN=32768, D=128,
+                      dtype="bf16", seed=6, mask="noop")
 
 WORKLOADS = (TINY_CAUSAL, DENSE_CAUSAL_GQA, SLIDING_SINKS, DOCUMENT, ALIBI_SOFTCAP)
 BY_NAME = {w.name: w for w in WORKLOADS}

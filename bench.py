@@ -126,7 +126,7 @@ def decode_leg(fa, torch, dev, stream, steps: int):
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (inp.q, inp.k, inp.v))
     del inp
     bm = fa.create_block_mask(w.mask, 1, 1, w.Q_LEN, w.KV_LEN, 128, device=dev, stream=stream)
-    splits = fa.auto_splits(q, bm)
+    splits = fa.auto_splits(q, k, bm)
     lib = fa.load_library()
     need = lib.flexattn_fwd_splitkv_workspace_bytes(w.B, w.Hq, w.Q_LEN, w.D, splits)
     ws = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)

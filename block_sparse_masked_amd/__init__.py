@@ -267,13 +267,25 @@ def _tensor(t: torch.Tensor, name: str) -> _Tensor:
     return _Tensor(t.data_ptr(), dt, *t.shape, st)
 
 
-def auto_splits(q: torch.Tensor, block_mask: BlockMask, target_workgroups: int = 1024) -> int:
+def auto_splits(q: torch.Tensor, k: torch.Tensor, block_mask: BlockMask,
+                target_workgroups: int = 1024) -> int:
     """Split count for a bf16 call: enough workgroups to fill the chip
     (target_workgroups, four per CU) when there are few query tiles, at most
     the number of KV tiles a row can list, and 1 (no split) otherwise."""
     if q.dtype != torch.bfloat16:
         return 1
-    items = q.shape[0] * q.shape[1] * block_mask.num_q_blocks
+    B, Hq, M = q.shape[0], q.shape[1], q.shape[2]
+    group = Hq // k.shape[1]
+    # a short query tile (M <= 64) with the mask broadcast over heads packs
+    # 4 / waves-per-head query heads of one KV group into a workgroup (the
+    # same rule as the kernel's launcher)
+    heads_per_wg = 1
+    if block_mask.H == 1 and M <= 64:
+        for wph in (1, 2):
+            if M <= 32 * wph and group % (4 // wph) == 0:
+                heads_per_wg = 4 // wph
+                break
+    items = B * (Hq // heads_per_wg) * block_mask.num_q_blocks
     if items >= target_workgroups // 2:
         return 1
     return max(1, min(block_mask.num_kv_blocks, target_workgroups // items, 64))
@@ -310,7 +322,7 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask
         sp.alibi_slopes = alibi_slopes.data_ptr()
     tq, tk, tv, to = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v"), _tensor(out, "out")
     if num_splits is None:
-        num_splits = auto_splits(q, block_mask)
+        num_splits = auto_splits(q, k, block_mask)
     if num_splits > 1:
         B, Hq, M, D = q.shape
         need = lib.flexattn_fwd_splitkv_workspace_bytes(B, Hq, M, D, num_splits)

@@ -79,6 +79,11 @@ struct FwdArgs {
   int sk2, sv2;  // key-row strides (elements, < 2^22)
   int B, Hq, Hkv, G, Q_LEN, KV_LEN;
   int xcd_round;  // > 0: items per schedule round, remapped so KV groups share an XCD
+  // waves per query head (one-head workgroups): 4 covers a 128-row query
+  // tile; 2 or 1 (Q_LEN <= 64 or <= 32, mask broadcast over heads) gives the
+  // other waves further heads of the same KV group, so short query tiles do
+  // not leave most MFMA rows idle and the group's K/V are read once
+  int wph;
   int doc_len;
   MaskParams mp;
   float c_scale, c_cap, cap2;
@@ -427,18 +432,21 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
     const int r = x / R, u = x - r * R;
     x = r * R + (u & 7) * (R >> 3) + (u >> 3);
   }
-  // with HEADS = 2 the item's head index counts head pairs (2p, 2p + 1)
-  const Item it = decode_item(x, a.bm, a.B, a.Hq / HEADS);
+  // the item's head index counts groups of HPW consecutive heads (HEADS = 2:
+  // pairs; one-head workgroups with wph < 4: 4 / wph heads of a KV group)
+  const int wph = (HEADS == 1) ? a.wph : kWavesPerHead;
+  const int HPW = WAVES / wph;
+  const Item it = decode_item(x, a.bm, a.B, a.Hq / HPW);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = it.b, h = it.h * HEADS + wave / kWavesPerHead;
-  const int hk = (it.h * HEADS) / a.G;
+  const int b = it.b, h = it.h * HPW + wave / wph;
+  const int hk = (it.h * HPW) / a.G;
   Lane<D> ln;
   ln.lane = threadIdx.x & 63;
   ln.l32 = ln.lane & 31;
   ln.hh = ln.lane >> 5;
   ln.vg = (ln.lane >> 4) & 1;
   ln.vi = ln.lane & 15;
-  ln.q = it.qb * kBlock + (wave % kWavesPerHead) * 32 + ln.l32;
+  ln.q = it.qb * kBlock + (wave % wph) * 32 + ln.l32;
   const bool qvalid = ln.q < a.Q_LEN;
   ln.qc = qvalid ? ln.q : a.Q_LEN - 1;
   const int* doc_row = (MASK == MASK_DOCUMENT) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
@@ -739,11 +747,22 @@ hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream) {
     if (env[0] == '1') heads = 1;
     if (env[0] == '2' && pair_ok) heads = 2;
   }
+  // Short query tiles (Q_LEN <= 64, one tile) with the mask broadcast over
+  // heads: fewest waves per head that cover Q_LEN and give a whole number of
+  // heads per workgroup inside one KV group.
+  a.wph = kWavesPerHead;
+  if (heads == 1 && L.bm.Hm == 1 && L.Q_LEN <= 64)
+    for (int w = 1; w < kWavesPerHead; w *= 2)
+      if (L.Q_LEN <= 32 * w && a.G % (kWavesPerHead / w) == 0) {
+        a.wph = w;
+        break;
+      }
+  const int hpw = heads * kWavesPerHead / a.wph;  // query heads per workgroup
   // XCD-aware order: with the mask broadcast over batch and heads every
-  // schedule round holds the B*Hq/heads items of one query tile; split each
+  // schedule round holds the B*Hq/hpw items of one query tile; split each
   // round into 8 contiguous chunks of whole KV groups, one per XCD.
-  const int R = L.B * L.Hq / heads;
-  const int g_items = a.G / heads;  // items per KV group
+  const int R = L.B * L.Hq / hpw;
+  const int g_items = a.G / hpw;  // items per KV group
   a.xcd_round = (L.bm.Bm == 1 && L.bm.Hm == 1 && R % 8 == 0 && (R / 8) % g_items == 0) ? R : 0;
   const int grid = R * L.bm.NQB * a.splits;
   if (grid == 0) return hipSuccess;

@@ -281,3 +281,43 @@ def test_fwd_decode_workload_sampled(lib):
         o_ref, lse_ref = G.oracle_rows(w, inp, batches=[b], heads=[h])
         res = G.compare(w, o, l_, o_ref, lse_ref)
         assert res["ok"] and res["n_rows"] == w.Q_LEN, G.summary(res)
+
+
+@pytest.mark.parametrize("q_len", [1, 16, 33, 64])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 2), (8, 1), (3, 3)])
+@pytest.mark.parametrize("mask,score", [("noop", "alibi"), ("sliding_sink", "softcap_alibi"),
+                                        ("prefix_lm", "alibi"), ("causal", "none")])
+@pytest.mark.parametrize("splits", [1, None])
+def test_fwd_short_query_heads_packed(lib, q_len, Hq, Hkv, mask, score, splits):
+    """Short query tiles (Q_LEN <= 64) put several query heads of one KV group
+    in a workgroup, one or two waves each; ALiBi's per-head slope checks that
+    every wave takes its own head. Group sizes 4, 2, 8 and 1 (no packing)."""
+    w = tiny("bf16", 128, mask, score, B=2, Hq=Hq, Hkv=Hkv, Q_LEN=q_len, KV_LEN=700,
+             window=200, prefix=40, value_scale=2.0 if "softcap" in score else 1.0)
+    inp = W.generate(w)
+    bm = G.build_gpu_mask(lib, w, inp)
+    q, k, v = (G.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    out, lse = lib.flex_attention(q, k, v, bm, score=w.score, softcap=w.softcap, scale=w.scale,
+                                  num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = G.oracle_rows(w, inp)
+    res = G.compare(w, out.float().cpu().numpy().astype(np.float64),
+                    lse.cpu().numpy().astype(np.float64), o_ref, lse_ref)
+    assert res["ok"], G.summary(res)
+
+
+def test_fwd_short_query_per_head_mask_not_packed(lib):
+    """A BlockMask built per head (H_mask = Hq) keeps one head per workgroup:
+    same results as the broadcast mask."""
+    w = tiny("bf16", 64, "sliding_sink", "alibi", B=1, Hq=8, Hkv=2, Q_LEN=16, KV_LEN=900,
+             window=300)
+    inp = W.generate(w)
+    q, k, v = (G.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    o_ref, lse_ref = G.oracle_rows(w, inp)
+    for H_mask in (1, 8):
+        bm = G.build_gpu_mask(lib, w, inp, 1, H_mask)
+        out, lse = lib.flex_attention(q, k, v, bm, score=w.score, scale=w.scale)
+        torch.cuda.synchronize()
+        res = G.compare(w, out.float().cpu().numpy().astype(np.float64),
+                        lse.cpu().numpy().astype(np.float64), o_ref, lse_ref)
+        assert res["ok"], (H_mask, G.summary(res))

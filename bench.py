@@ -65,7 +65,7 @@ def algorithmic_bytes(w: W.Workload, nqb: int, nkb: int) -> int:
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("fwd_bf16.hip", "common.hpp", "fwd_common.hpp")
+KERNEL_SOURCES = ("fwd_bf16.hip", "fwd_bf16_kernel.hpp", "common.hpp", "fwd_common.hpp")
 
 
 def measured_traffic(workload: str):

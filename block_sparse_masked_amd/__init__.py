@@ -67,6 +67,10 @@ class _BlockMask(ctypes.Structure):
                 ("full_q_num_blocks", ctypes.c_void_p), ("full_q_indices", ctypes.c_void_p)]
 
 
+class _PageTable(ctypes.Structure):
+    _fields_ = [("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -102,6 +106,12 @@ def load_library():
         ctypes.POINTER(_BlockMask), ctypes.c_int, ctypes.POINTER(_ScoreParams), ctypes.c_float,
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(_Tensor),
         ctypes.c_void_p, ctypes.c_void_p]
+    lib.flexattn_fwd_paged.restype = ctypes.c_int
+    lib.flexattn_fwd_paged.argtypes = [
+        ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+        ctypes.POINTER(_PageTable), ctypes.POINTER(_BlockMask), ctypes.c_int,
+        ctypes.POINTER(_ScoreParams), ctypes.c_float, ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_size_t, ctypes.POINTER(_Tensor), ctypes.c_void_p, ctypes.c_void_p]
     lib.flexattn_block_mask_from_kv_blocks.restype = ctypes.c_int
     lib.flexattn_block_mask_from_kv_blocks.argtypes = [ctypes.POINTER(_BlockMask), ctypes.c_void_p,
                                                        ctypes.c_void_p]
@@ -296,8 +306,14 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask
                    alibi_slopes: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                    stream=None, num_splits: Optional[int] = 1,
-                   workspace: Optional[torch.Tensor] = None):
+                   workspace: Optional[torch.Tensor] = None,
+                   page_table: Optional[torch.Tensor] = None):
     """Block-sparse attention forward. q [B,Hq,M,D]; k, v [B,Hkv,N,D].
+
+    With page_table (int32 [B, max_pages], bf16): k and v are paged caches
+    [num_pages, Hkv, page_size, D] (page_size a multiple of 128) and key j of
+    batch b is row j % page_size of page page_table[b, j // page_size]; the
+    sequence length is block_mask.KV_LEN.
 
     num_splits > 1 (bf16) cuts each query tile's KV tiles into that many
     slices run by separate workgroups and merged afterwards (split-KV, for
@@ -323,6 +339,26 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask
     tq, tk, tv, to = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v"), _tensor(out, "out")
     if num_splits is None:
         num_splits = auto_splits(q, k, block_mask)
+    if page_table is not None:
+        if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_cuda:
+            raise ValueError("page_table must be a GPU int32 tensor [B, max_pages]")
+        if page_table.shape[0] != q.shape[0]:
+            raise ValueError("page_table must have one row per batch")
+        page_table = page_table.contiguous()
+        pt = _PageTable(page_table.data_ptr(), page_table.shape[1])
+        B, Hq, M, D = q.shape
+        need = lib.flexattn_fwd_splitkv_workspace_bytes(B, Hq, M, D, max(num_splits, 1))
+        if num_splits > 1 and workspace is None:
+            workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
+        ws_ptr = workspace.data_ptr() if num_splits > 1 else None
+        ws_bytes = workspace.numel() * workspace.element_size() if num_splits > 1 else 0
+        st = lib.flexattn_fwd_paged(
+            ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(pt),
+            ctypes.byref(block_mask._c), SCORE_KINDS[score], ctypes.byref(sp), float(scale),
+            int(num_splits), ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.byref(to),
+            ctypes.c_void_p(lse.data_ptr()), _stream_handle(q.device, stream))
+        _check(st, "flexattn_fwd_paged")
+        return out, lse
     if num_splits > 1:
         B, Hq, M, D = q.shape
         need = lib.flexattn_fwd_splitkv_workspace_bytes(B, Hq, M, D, num_splits)

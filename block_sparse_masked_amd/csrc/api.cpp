@@ -276,12 +276,13 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
                          const flexattn_tensor* v, const flexattn_block_mask* bm,
                          flexattn_score_kind score_kind, const flexattn_score_params* params,
                          float scale, flexattn_tensor* out, float* lse, int splits,
-                         void* workspace, size_t workspace_bytes, void* stream, const char* who) {
+                         void* workspace, size_t workspace_bytes, void* stream, const char* who,
+                         const flexattn_page_table* pages = nullptr) {
   flexattn_status st;
-  if ((st = check_tensor(q, "q")) != FLEXATTN_OK) return st;
-  if ((st = check_tensor(k, "k")) != FLEXATTN_OK) return st;
-  if ((st = check_tensor(v, "v")) != FLEXATTN_OK) return st;
-  if ((st = check_tensor(out, "out")) != FLEXATTN_OK) return st;
+  if ((st = check_tensor(q, "q", who)) != FLEXATTN_OK) return st;
+  if ((st = check_tensor(k, "k", who)) != FLEXATTN_OK) return st;
+  if ((st = check_tensor(v, "v", who)) != FLEXATTN_OK) return st;
+  if ((st = check_tensor(out, "out", who)) != FLEXATTN_OK) return st;
   if (!lse) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: lse is NULL", who);
   if (!bm) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: bm is NULL", who);
   if (k->dtype != q->dtype || v->dtype != q->dtype || out->dtype != q->dtype)
@@ -290,14 +291,36 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: head dim %d is not 64 or 128", who, q->D);
   if (k->D != q->D || v->D != q->D || out->D != q->D)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: q, k, v, out head dims differ", who);
-  if (k->B != q->B || v->B != q->B || out->B != q->B)
+  if (out->B != q->B || (!pages && (k->B != q->B || v->B != q->B)))
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: batch sizes differ", who);
+  // keys per sequence: the tensors' length, or for a paged cache the
+  // BlockMask's KV_LEN (the cache's L is the page size)
+  int kv_len = k->L;
+  if (pages) {
+    if (!pages->page_table || reinterpret_cast<uintptr_t>(pages->page_table) % 4 != 0)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: page_table is NULL or not 4-byte aligned", who);
+    if (q->dtype != FLEXATTN_BF16)
+      return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: the paged forward is a bf16 path", who);
+    if (k->B != v->B || k->B < 1)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: k and v caches must hold the same pages", who);
+    if (k->L % fa::kBlock != 0)
+      return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: page size %d is not a multiple of 128", who,
+                  k->L);
+    if (!bm) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: bm is NULL", who);
+    kv_len = bm->KV_LEN;
+    if (kv_len < 1 || pages->max_pages < 1 ||
+        (long long)pages->max_pages * k->L < (long long)kv_len)
+      return fail(FLEXATTN_ERR_INVALID_ARG,
+                  "%s: max_pages=%d pages of %d keys do not cover KV_LEN=%d", who,
+                  pages->max_pages, k->L, kv_len);
+  }
   if (k->H != v->H || out->H != q->H)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: head counts of k/v or q/out differ", who);
   if (q->H % k->H != 0)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", who, q->H,
                 k->H);
   if (k->L != v->L) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: k and v lengths differ", who);
+  (void)kv_len;
   if (out->L != q->L) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: out and q lengths differ", who);
   if (!(std::isfinite(scale)))
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: scale is not finite", who);
@@ -305,12 +328,12 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   if (bm->BLOCK_SIZE != fa::kBlock)
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: BlockMask BLOCK_SIZE must be 128 (got %d)", who,
                 bm->BLOCK_SIZE);
-  if (bm->Q_LEN != q->L || bm->KV_LEN != k->L)
+  if (bm->Q_LEN != q->L || bm->KV_LEN != kv_len)
     return fail(FLEXATTN_ERR_INVALID_ARG,
                 "%s: BlockMask built for Q_LEN=%d KV_LEN=%d, tensors have %d and %d", who,
-                bm->Q_LEN, bm->KV_LEN, q->L, k->L);
+                bm->Q_LEN, bm->KV_LEN, q->L, kv_len);
   if (bm->num_q_blocks != ceil_div(q->L, fa::kBlock) ||
-      bm->num_kv_blocks != ceil_div(k->L, fa::kBlock))
+      bm->num_kv_blocks != ceil_div(kv_len, fa::kBlock))
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: BlockMask tile counts do not match its lengths",
                 who);
   if (!(bm->B == 1 || bm->B == q->B) || !(bm->H == 1 || bm->H == q->H))
@@ -322,7 +345,7 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: a BlockMask buffer pointer is NULL", who);
   fa::MaskParams mp;
   int doc_len = 0;
-  if ((st = check_mask(bm->mask_kind, &bm->mask_params, q->B, q->L, k->L, &mp, &doc_len, who)) !=
+  if ((st = check_mask(bm->mask_kind, &bm->mask_params, q->B, q->L, kv_len, &mp, &doc_len, who)) !=
       FLEXATTN_OK)
     return st;
   if (bm->mask_kind == FLEXATTN_MASK_DOCUMENT_CAUSAL && bm->mask_params.doc_batch > 1 &&
@@ -345,9 +368,10 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   if (score_kind == FLEXATTN_SCORE_ALIBI || score_kind == FLEXATTN_SCORE_SOFTCAP_ALIBI)
     slopes = params ? params->alibi_slopes : nullptr;
 
-  if (q->dtype == FLEXATTN_BF16 && fa::fwd_bf16_lds_bytes(q->D, bm->num_kv_blocks) > fa::kMaxLdsBytes)
+  if (q->dtype == FLEXATTN_BF16 && fa::fwd_bf16_lds_bytes(q->D, bm->num_kv_blocks, pages != nullptr) >
+                                        fa::kMaxLdsBytes)
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: KV_LEN %d needs more LDS than a workgroup has", who,
-                k->L);
+                kv_len);
   // the bf16 kernel addresses a block of up to 128 key rows with 32-bit offsets
   if (q->dtype == FLEXATTN_BF16 &&
       (k->stride[2] > fa::kMaxBf16RowStride || v->stride[2] > fa::kMaxBf16RowStride))
@@ -382,7 +406,7 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   L.Hq = q->H;
   L.Hkv = k->H;
   L.Q_LEN = q->L;
-  L.KV_LEN = k->L;
+  L.KV_LEN = kv_len;
   L.D = q->D;
   L.mask_kind = (int)bm->mask_kind;
   L.mp = mp;
@@ -400,6 +424,12 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   L.bm.Hm = bm->H;
   L.bm.NQB = bm->num_q_blocks;
   L.bm.NKB = bm->num_kv_blocks;
+  if (pages) {
+    L.page_table = pages->page_table;
+    L.page_size = k->L;
+    L.pt_stride = pages->max_pages;
+    L.num_pages = k->B;
+  }
   if (splits > 1) {
     L.splits = splits;
     L.part_o = static_cast<float*>(workspace);
@@ -443,6 +473,22 @@ flexattn_status flexattn_fwd_splitkv(const flexattn_tensor* q, const flexattn_te
                 num_splits);
   return fwd_impl(q, k, v, bm, score_kind, params, scale, out, lse, num_splits, workspace,
                   workspace_bytes, stream, who);
+}
+
+flexattn_status flexattn_fwd_paged(const flexattn_tensor* q, const flexattn_tensor* k_cache,
+                                   const flexattn_tensor* v_cache,
+                                   const flexattn_page_table* pages,
+                                   const flexattn_block_mask* bm, flexattn_score_kind score_kind,
+                                   const flexattn_score_params* params, float scale,
+                                   int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                   flexattn_tensor* out, float* lse, void* stream) {
+  static const char* who = "flexattn_fwd_paged";
+  if (!pages) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: pages is NULL", who);
+  if (num_splits < 1)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: num_splits must be >= 1 (got %d)", who,
+                num_splits);
+  return fwd_impl(q, k_cache, v_cache, bm, score_kind, params, scale, out, lse, num_splits,
+                  workspace, workspace_bytes, stream, who, pages);
 }
 
 flexattn_status flexattn_bwd(const flexattn_tensor* q, const flexattn_tensor* k,

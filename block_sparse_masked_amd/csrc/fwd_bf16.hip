@@ -1,781 +1,19 @@
-// Block-sparse attention forward, bf16 inputs, fp32 accumulation, gfx950.
-//
-// The forward of page "tensorplay.nn.attention API" (BlockMask "Details"
-// item 1: reduce along KV over each query row-tile's tile lists; item 2:
-// mask_mod only on partial tiles) computed tile by tile with an online
-// softmax, so the score matrix is never materialised (page "Attention
-// Backends", section "Why care about Attention Kernels?"; page
-// "FlagAttention", tiling with recomputation). GQA: query head h reads KV head
-// h / (Hq / Hkv) (page "FlagAttention", section "Operator overview").
-//
-// Work decomposition: one workgroup of 4 waves per (b, h, 128-row query
-// tile); wave w owns query rows [32w, 32w + 32). Two workgroups share a CU,
-// so each SIMD runs two waves and one wave's softmax (vector ALUs) overlaps
-// the other's matrix products. Both products use v_mfma_f32_32x32x16_bf16:
-//   S^T = K . Q^T    (A = K rows from LDS, B = Q^T held in registers)
-//   O^T += V^T . P^T (A = V^T read transposed from LDS, B = P^T in registers)
-// The MFMA result's lane index is the query column, so each lane holds the
-// scores of one query row (half of a step's keys); the row max needs one
-// exchange with lane ^ 32, the P^T operand is the converted score registers
-// and the O^T accumulator is rescaled per lane.
-//
-// MFMA 32x32 result layout: register r of lane l holds row
-// 8*(r/4) + 4*(l/32) + r%4 and column l%32. An operand register slot t of
-// lane l holds k = 8*(l/32) + t for both A and B, so the key order inside the
-// P.V contraction follows the S result layout directly.
-//
-// KV is walked in steps of NK = 8192 / D keys (64 for D = 128, 128 for D = 64;
-// a step's K or V block is 16 KiB), each BlockMask tile in 128 / NK steps.
-// K and V of step g + 1 are loaded straight from global memory into LDS
-// (double-buffered) while step g computes; one barrier per step.
-// Full tiles take a path with no mask code. The running max is applied
-// lazily: O and the row sum are rescaled only when a row's max grows by more
-// than 2^8 (exp2 units), which leaves the result unchanged (any reference
-// point gives the same normalised sums) while skipping most rescales.
-#include <stdlib.h>
-
-#include <type_traits>
-
-#include "common.hpp"
-#include "fwd_common.hpp"
-#include "launch.hpp"
+// Block-sparse attention forward, bf16, contiguous K/V (the kernel and its
+// design notes are in fwd_bf16_kernel.hpp); paged K/V dispatch to
+// fwd_bf16_paged.hip, a separate translation unit so both compile in
+// parallel.
+#include "fwd_bf16_kernel.hpp"
 
 namespace fa {
 
-namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16;
-
-constexpr int kWavesPerHead = 4;  // 4 x 32 query rows = one 128-row query tile
-constexpr float kRescaleSlack = 8.0f;  // exp2 units: p <= 256 between rescales
-constexpr int kStepBytes = 16384;      // one K (or V) step block in LDS
-
-// internal score kind: plain scaled score with the scale applied before the
-// row max (needed when scale < 0; SCORE_NONE folds the scale into exp2)
-constexpr int SCORE_SCALED = 4;
-
-template <int D>
-struct Geom {
-  static constexpr int NK = kStepBytes / (2 * D);  // keys per step
-  static constexpr int SPT = kBlock / NK;          // steps per BlockMask tile
-  static constexpr int NB = NK / 32;               // 32-key blocks per step
-  static constexpr int NE = NB * 16;               // scores per lane per step
-  static constexpr int PKS = NK / 16;              // P.V k-steps per step
-  static constexpr int KS = D / 16;                // S k-steps
-  static constexpr int DB = D / 32;                // O d-blocks
-};
-
-struct FwdArgs {
-  const u16* q;
-  const u16* k;
-  const u16* v;
-  u16* o;
-  float* lse;
-  long long sq0, sq1, sq2, sk0, sk1, sv0, sv1, so0, so1, so2;
-  int sk2, sv2;  // key-row strides (elements, < 2^22)
-  int B, Hq, Hkv, G, Q_LEN, KV_LEN;
-  int xcd_round;  // > 0: items per schedule round, remapped so KV groups share an XCD
-  // waves per query head (one-head workgroups): 4 covers a 128-row query
-  // tile; 2 or 1 (Q_LEN <= 64 or <= 32, mask broadcast over heads) gives the
-  // other waves further heads of the same KV group, so short query tiles do
-  // not leave most MFMA rows idle and the group's K/V are read once
-  int wph;
-  int doc_len;
-  MaskParams mp;
-  float c_scale, c_cap, cap2;
-  const float* slopes;
-  BlockMaskView bm;
-  // split-KV: each item's tile list is cut into `splits` contiguous slices,
-  // one workgroup each, writing fp32 partial results (O normalised by its
-  // slice's row sum, and the slice's LSE) that a combine pass merges
-  int splits;     // 1: no split, O and LSE written directly
-  float* part_o;  // [splits][B][Hq][Q_LEN][D]
-  float* part_lse;  // [splits][B][Hq][Q_LEN]
-};
-
-// 16-byte chunk swizzle of a K block [NK][D] in LDS: the 16 rows a 16-lane
-// phase of a fragment read touches land in distinct banks.
-template <int D>
-__device__ __forceinline__ int swz(int row, int col) {
-  if constexpr (D == 128) {
-    return col ^ (row & 15);
-  } else {
-    return col ^ ((row >> 1) & 7);
-  }
-}
-
-// V block swizzle for the transposed reads: two 16-lane groups read the same
-// 4 consecutive rows at chunk pairs c, c+1 and c+2, c+3 (c = 4 * d-block).
-// XOR-ing with 4*(row%4) (D = 128: 16 chunks per 256-byte row) or with
-// 4*((row/2)%2) (D = 64: 8 chunks per 128-byte row, two rows per bank sweep)
-// gives those 16 half-chunk pairs distinct banks.
-template <int D>
-__device__ __forceinline__ int swz_v(int row, int col) {
-  if constexpr (D == 128) {
-    return col ^ ((row & 3) << 2);
-  } else {
-    return col ^ (((row >> 1) & 1) << 2);
-  }
-}
-
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return (unsigned)(unsigned long long)(__attribute__((address_space(3))) const void*)p;
-}
-
-// Buffer resource for raw loads: 64-bit base, no stride, `bytes` in range
-// (loads past it read as zero). Built from wave-uniform values.
-__device__ __forceinline__ i32x4 make_rsrc(unsigned long long base, unsigned bytes) {
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)base);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(base >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// Direct global->LDS loads (16 and 4 bytes per lane). Written as one asm
-// block with its M0 setup and no register results: the LDS they fill is a
-// buffer no instruction reads until after the explicit vmcnt(0) + barrier
-// that ends the step, so the compiler need not (and does not) wait for them.
-// No memory clobber: the asm stays ordered against the barriers and waits
-// (all have side effects), while the LDS reads of the other buffer may be
-// scheduled around it. Each load takes the CU's vector-memory path for a few
-// cycles, so the step spreads them between its matrix instructions.
-// The LDS address is wave-uniform by construction; readfirstlane states that
-// to the compiler so the asm operand is always a scalar register.
-__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               : : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "m0");
-}
-__device__ __forceinline__ void dma4(i32x4 rsrc, unsigned lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               : : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "m0");
-}
-
-// Loads of one [NK][D] step block of K or V. Each wave-wide load fills one
-// contiguous KiB of LDS (lane l writes bytes [16 l, 16 l + 16)), so each lane
-// fetches the global chunk whose swizzled home is that slot; its byte offset
-// from the block's first row is fixed and computed once. Per step only the
-// resource moves; its range ends at KV_LEN, so rows past it read as zero
-// (their scores are masked: a tile crossing KV_LEN takes the masked path).
-template <int D, bool IS_V, int WAVES>
-struct BlockLoader {
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int ROWS_PER_KB = 1024 / (2 * D);
-  static constexpr int KB_PER_WAVE = kStepBytes / 1024 / WAVES;
-  static constexpr int NK = Geom<D>::NK;
-  int voff[KB_PER_WAVE];
-  unsigned long long base;  // byte address of key row 0 of this (b, kv head)
-  unsigned row_bytes;
-  unsigned lds0;            // LDS byte address of this wave's first KiB, buffer 0
-
-  __device__ void init(const u16* g, int stride, int wave, int lane, const u16* lds_buf0) {
-    base = reinterpret_cast<unsigned long long>(g);
-    row_bytes = 2u * (unsigned)stride;
-    const int r_in = lane / CPR;
-    const int pch = lane % CPR;
-#pragma unroll
-    for (int i = 0; i < KB_PER_WAVE; ++i) {
-      const int row = (wave * KB_PER_WAVE + i) * ROWS_PER_KB + r_in;
-      const int col = IS_V ? swz_v<D>(row, pch) : swz<D>(row, pch);
-      voff[i] = row * (int)row_bytes + col * 16;
-    }
-    lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_buf0) + wave * KB_PER_WAVE * 1024);
-  }
-
-  // loads of keys [kv0, kv0 + NK) into buffer `buf` (its LDS is lds0 + buf * 2 * kStepBytes
-  // when the two buffers of K (or V) are laid out [buf][K|V])
-  __device__ __forceinline__ i32x4 plan(int kv0, int kv_len) const {
-    const int rows = min(kv_len - kv0, NK);
-    return make_rsrc(base + (unsigned long long)kv0 * row_bytes,
-                     rows > 0 ? (unsigned)rows * row_bytes : 0u);
-  }
-  __device__ __forceinline__ void issue_one(i32x4 rsrc, unsigned lds_buf, int i) const {
-    dma16(rsrc, lds_buf + 1024 * i, voff[i]);
-  }
-  __device__ __forceinline__ void issue(int kv0, int kv_len, unsigned lds_buf) const {
-    const int rows = min(kv_len - kv0, NK);
-    const i32x4 rsrc = make_rsrc(base + (unsigned long long)kv0 * row_bytes,
-                                 rows > 0 ? (unsigned)rows * row_bytes : 0u);
-#pragma unroll
-    for (int i = 0; i < KB_PER_WAVE; ++i) dma16(rsrc, lds_buf + 1024 * i, voff[i]);
-  }
-};
-
-__device__ __forceinline__ void wait_loads_and_sync() {
-  // vmcnt(0), expcnt/lgkmcnt unconstrained, then the workgroup barrier
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &u, 16);
-  return r;
-}
-
-// Per-lane context of one work item, including the LDS element offsets of
-// this lane's fragments. The swizzles only XOR row bits that are the same
-// for every block / k-step a lane reads, so one offset per K k-step and one
-// per V d-block suffice; the rest of each address is a compile-time constant.
-template <int D>
-struct Lane {
-  int lane, l32, hh, vg, vi;
-  int q, qc;
-  float slope2;
-  int dq;            // document id of this lane's query row (document mask)
-  int kofs[D / 16];  // K fragment (row l32 of block 0, k-step ks)
-  int vofs[D / 32];  // V transposed-read piece (k-step 0, half 0, d-block db)
-
-  __device__ void init_offsets() {
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) kofs[ks] = l32 * D + swz<D>(l32, 2 * ks + hh) * 8;
-    // + 16*ks + 8*half: multiples of 4 leave row % 4 and (row / 2) % 2 alone
-    const int row = 4 * hh + (vi >> 2);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int d = 32 * db + 16 * vg + 4 * (vi & 3);
-      vofs[db] = row * D + swz_v<D>(row, d >> 3) * 8 + (d & 7);
-    }
-  }
-};
-
-// Row max across the two lanes that hold one query row (lane, lane ^ 32).
-__device__ __forceinline__ float pair_max(float x) {
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                   false, false);
-  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-}
-
-// V^T operand fragment for P.V MFMA (k-step ks, d-block db): lane row
-// d = 32*db + lane%32, slot t <-> key 16*ks + 8*(t/4) + 4*hh + t%4 (the key
-// order of pf), read from the row-major V block with two transposing reads:
-// in each 16-lane group lane j supplies the 8-byte piece (row j/4, columns
-// 4*(j%4)..+3) of a 4-key x 16-d block and receives column j of that block.
-template <int D>
-__device__ __forceinline__ bf16x8 v_frag(const u16* sV, const Lane<D>& ln, int ks, int db) {
-  bf16x4 part[2];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const u16* src = sV + ln.vofs[db] + (16 * ks + 8 * ht) * D;
-    part[ht] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) bf16x4*)(src));
-  }
-  return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// K operand fragment for S MFMA (k-step ks, key block blk): rows
-// 32*blk + lane%32 keep row % 16 (and (row/2) % 8), so one offset per k-step.
-template <int D>
-__device__ __forceinline__ bf16x8 k_frag(const u16* sK, const Lane<D>& ln, int ks, int blk) {
-  return as_bf16x8(*reinterpret_cast<const uint4*>(sK + ln.kofs[ks] + 32 * blk * D));
-}
-
-// Key offset (within the step, without 4*hh) of result register r of block blk.
-__device__ __forceinline__ constexpr int key_off(int blk, int r) {
-  return 32 * blk + 8 * (r >> 2) + (r & 3);
-}
-
-// Per-step mask limits: key offset c (see key_off) is allowed when c <= hi,
-// and for the sliding window also c > win_lo or c < sink_hi; for documents
-// the key's id (LDS) must equal the query row's.
-struct MaskLimits {
-  int hi, win_lo, sink_hi;
-};
-
-template <int D, int MASK>
-__device__ __forceinline__ MaskLimits mask_limits(int kv0, const FwdArgs& a, const Lane<D>& ln) {
-  const int base = kv0 + 4 * ln.hh;
-  MaskLimits m;
-  m.hi = a.KV_LEN - 1 - base;
-  if constexpr (MASK == MASK_PREFIX_LM) m.hi = min(m.hi, max(ln.qc, a.mp.prefix - 1) - base);
-  else if constexpr (MASK != MASK_NOOP) m.hi = min(m.hi, ln.qc - base);
-  m.win_lo = ln.qc - base - a.mp.window;
-  m.sink_hi = a.mp.sinks - base;
-  return m;
-}
-
-// Logit of one score: y = score_mod(x) in base-2 units (raw x for
-// SCORE_NONE, scaled later), -inf where masked on partial tiles.
-template <int D, int MASK, int SCORE, bool MASKED>
-__device__ __forceinline__ float elem_logit(float x, int blk, int r, int kv0, const MaskLimits& ml,
-                                            const int* step_doc, const FwdArgs& a,
-                                            const Lane<D>& ln) {
-  float y = x;
-  if constexpr (SCORE == SCORE_SCALED) {
-    y = x * a.c_scale;
-  } else if constexpr (SCORE != SCORE_NONE) {
-    const int key = kv0 + key_off(blk, r) + 4 * ln.hh;
-    y = ScoreMod<SCORE>::apply(x, a.c_scale, a.c_cap, a.cap2, ln.slope2, (float)(key - ln.q));
-  }
-  if constexpr (MASKED) {
-    const int c = key_off(blk, r);
-    bool ok = c <= ml.hi;
-    if constexpr (MASK == MASK_SLIDING_SINK) ok = ok && (c > ml.win_lo || c < ml.sink_hi);
-    if constexpr (MASK == MASK_DOCUMENT) ok = ok && step_doc[c + 4 * ln.hh] == ln.dq;
-    y = ok ? y : -INFINITY;
-  }
-  return y;
-}
-
-// One KV step: S = K . Q^T, online softmax, O += V . P. `dma(i)` issues the
-// i-th of the NDMA loads of the next step (called between S products).
-template <int D, int MASK, int SCORE, bool MASKED, int NDMA, typename DMA>
-__device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l,
-                                     const bf16x8 (&qf)[D / 16], const u16* sK, const u16* sV,
-                                     int kv0, const int* step_doc, const FwdArgs& a,
-                                     const Lane<D>& ln, DMA&& dma) {
-  using G = Geom<D>;
-  f32x16 s[G::NB];
-#pragma unroll
-  for (int b = 0; b < G::NB; ++b) s[b] = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < G::KS; ++ks)
-#pragma unroll
-    for (int b = 0; b < G::NB; ++b)
-    {
-      s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(sK, ln, ks, b), qf[ks], s[b], 0,
-                                                     0, 0);
-      // the next step's loads, spread over the S products
-      constexpr int NS = G::KS * G::NB;
-      static_assert(NS % NDMA == 0, "loads spread evenly");
-      const int i = ks * G::NB + b;
-      if (i % (NS / NDMA) == 0) dma(i / (NS / NDMA));
-    }
-
-  const MaskLimits ml = mask_limits<D, MASK>(kv0, a, ln);
-  float mx = -INFINITY;
-#pragma unroll
-  for (int b = 0; b < G::NB; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[b][r] = elem_logit<D, MASK, SCORE, MASKED>(s[b][r], b, r, kv0, ml, step_doc, a, ln);
-      mx = fmaxf(mx, s[b][r]);
-    }
-  mx = pair_max(mx);
-  if constexpr (SCORE == SCORE_NONE) mx *= a.c_scale;  // c_scale > 0 here
-
-  // lazy rescale (a real branch: rare)
-  if (__any(mx > m_ref + kRescaleSlack)) {
-    asm volatile("");
-    const float m_new = fmaxf(m_ref, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_ref - m_new);
-    l *= alpha;
-#pragma unroll
-    for (int i = 0; i < G::DB; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-    m_ref = m_new;
-  }
-  const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
-
-  bf16x8 pf[G::PKS];
-  float rs = 0.0f;
-#pragma unroll
-  for (int e = 0; e < G::NE; ++e) {
-    const float y = s[e >> 4][e & 15];
-    float p;
-    if constexpr (SCORE == SCORE_NONE) {
-      p = fast_exp2(fmaf(y, a.c_scale, -m_use));
-    } else {
-      p = fast_exp2(y - m_use);
-    }
-    rs += p;
-    pf[e >> 3][e & 7] = (__bf16)p;
-  }
-  l += rs;
-
-#pragma unroll
-  for (int ks = 0; ks < G::PKS; ++ks)
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db)
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D>(sV, ln, ks, db), pf[ks], o[db], 0,
-                                                      0, 0);
-}
-
-// HEADS query heads that share one KV head (and one BlockMask row) per
-// workgroup: 4 * HEADS waves read the same K/V step blocks, so HEADS = 2
-// halves the global->LDS traffic per flop. Two waves per SIMD either way.
-template <int D, int MASK, int SCORE, int HEADS>
-__global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf16_kernel(FwdArgs a) {
-  using G = Geom<D>;
-  constexpr int WAVES = kWavesPerHead * HEADS;
-  constexpr int THREADS = 64 * WAVES;
-  constexpr int NK = G::NK;
-  constexpr int SPT = G::SPT;
-  constexpr int STEP_ELEMS = kStepBytes / 2;
-  // LDS: K and V step blocks double-buffered (separate arrays, so the
-  // compiler can tell the buffer being filled from the one being read and does
-  // not wait for in-flight loads before LDS reads), two document-id buffers,
-  // and the item's tile list (NKB ints, dynamic)
-  __shared__ __attribute__((aligned(16))) u16 sK0[STEP_ELEMS];
-  __shared__ __attribute__((aligned(16))) u16 sK1[STEP_ELEMS];
-  __shared__ __attribute__((aligned(16))) u16 sV0[STEP_ELEMS];
-  __shared__ __attribute__((aligned(16))) u16 sV1[STEP_ELEMS];
-  __shared__ __attribute__((aligned(16))) int docbuf[(MASK == MASK_DOCUMENT) ? 2 * NK : 1];
-  extern __shared__ __attribute__((aligned(16))) int tlist[];
-
-  // dispatch order -> item; rounds of equal tile count are remapped so the
-  // heads sharing a KV head run on one XCD (workgroups go round-robin to XCDs)
-  int x = blockIdx.x;
-  int split = 0;
-  if (a.splits > 1) {
-    split = x % a.splits;
-    x /= a.splits;
-  }
-  if (a.xcd_round > 0) {
-    const int R = a.xcd_round;
-    const int r = x / R, u = x - r * R;
-    x = r * R + (u & 7) * (R >> 3) + (u >> 3);
-  }
-  // the item's head index counts groups of HPW consecutive heads (HEADS = 2:
-  // pairs; one-head workgroups with wph < 4: 4 / wph heads of a KV group)
-  const int wph = (HEADS == 1) ? a.wph : kWavesPerHead;
-  const int HPW = WAVES / wph;
-  const Item it = decode_item(x, a.bm, a.B, a.Hq / HPW);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = it.b, h = it.h * HPW + wave / wph;
-  const int hk = (it.h * HPW) / a.G;
-  Lane<D> ln;
-  ln.lane = threadIdx.x & 63;
-  ln.l32 = ln.lane & 31;
-  ln.hh = ln.lane >> 5;
-  ln.vg = (ln.lane >> 4) & 1;
-  ln.vi = ln.lane & 15;
-  ln.q = it.qb * kBlock + (wave % wph) * 32 + ln.l32;
-  const bool qvalid = ln.q < a.Q_LEN;
-  ln.qc = qvalid ? ln.q : a.Q_LEN - 1;
-  const int* doc_row = (MASK == MASK_DOCUMENT) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
-  ln.dq = (MASK == MASK_DOCUMENT) ? doc_row[ln.qc] : 0;
-  ln.init_offsets();
-  ln.slope2 = 0.0f;
-  if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
-    ln.slope2 = alibi_slope(a.slopes, h, a.Hq) * kLog2e;
-
-  BlockLoader<D, false, WAVES> kload;
-  BlockLoader<D, true, WAVES> vload;
-  kload.init(a.k + b * a.sk0 + hk * a.sk1, a.sk2, wave, ln.lane, sK0);
-  vload.init(a.v + b * a.sv0 + hk * a.sv1, a.sv2, wave, ln.lane, sV0);
-  const unsigned k_lds[2] = {kload.lds0, kload.lds0 + (lds_addr(sK1) - lds_addr(sK0))};
-  const unsigned v_lds[2] = {vload.lds0, vload.lds0 + (lds_addr(sV1) - lds_addr(sV0))};
-
-  const long long lrow = (long long)it.mrow * a.bm.NKB;
-  // counts are clamped to the list length so a malformed BlockMask cannot
-  // index past the staged list; the first entry of each list is read with
-  // the counts, so the first step's loads need not wait for the staging
-  const int nfull = __builtin_amdgcn_readfirstlane(min(a.bm.full_num[it.mrow], a.bm.NKB));
-  const int n = __builtin_amdgcn_readfirstlane(min(nfull + a.bm.kv_num[it.mrow], a.bm.NKB));
-  // this workgroup's slice [t_begin, t_end) of the item's tiles
-  const int t_begin = (int)((long long)n * split / a.splits);
-  const int t_end = (int)((long long)n * (split + 1) / a.splits);
-  const int first_tile = t_begin < nfull ? a.bm.full_idx[lrow + t_begin]
-                                         : a.bm.kv_idx[lrow + min(t_begin - nfull, a.bm.NKB - 1)];
-  // the item's tiles, full then partial, staged in LDS once
-  for (int t = threadIdx.x; t < n; t += THREADS)
-    tlist[t] = t < nfull ? a.bm.full_idx[lrow + t] : a.bm.kv_idx[lrow + (t - nfull)];
-  // document ids of a step's keys -> docbuf (rows past KV_LEN read as 0)
-  auto issue_doc = [&](int buf, int kv0) {
-    if constexpr (MASK == MASK_DOCUMENT) {
-      if (wave == 0) {
-        const int rows = min(a.KV_LEN, a.doc_len) - kv0;
-        const i32x4 rsrc = make_rsrc(reinterpret_cast<unsigned long long>(doc_row + kv0),
-                                     rows > 0 ? 4u * (unsigned)rows : 0u);
-#pragma unroll
-        for (int c = 0; c < NK / 64; ++c)
-          dma4(rsrc, __builtin_amdgcn_readfirstlane(lds_addr(docbuf + buf * NK + 64 * c)),
-               4 * ln.lane + 256 * c);
-      }
-    }
-  };
-
-  f32x16 o[G::DB];
-#pragma unroll
-  for (int i = 0; i < G::DB; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
-  float m_ref = -INFINITY;
-  float l = 0.0f;
-
-  if (t_end > t_begin) {
-    // tile indices are clamped into [0, NKB): a malformed BlockMask computes
-    // garbage but never reads outside the KV tensors
-    auto clamp_kv0 = [&](int idx) { return kBlock * min(max(idx, 0), a.bm.NKB - 1); };
-    auto tile_kv0 = [&](int t) { return clamp_kv0(__builtin_amdgcn_readfirstlane(tlist[t])); };
-    // prologue: step 0 -> buffer 0, Q^T fragments; then the tile list is
-    // visible (barrier in wait_loads_and_sync)
-    int kv0 = clamp_kv0(__builtin_amdgcn_readfirstlane(first_tile));
-    issue_doc(0, kv0);
-    kload.issue(kv0, a.KV_LEN, k_lds[0]);
-    vload.issue(kv0, a.KV_LEN, v_lds[0]);
-    bf16x8 qf[G::KS];
-    {
-      const u16* qrow = a.q + b * a.sq0 + h * a.sq1 + (long long)ln.qc * a.sq2;
-#pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks)
-        qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * ln.hh));
-    }
-    wait_loads_and_sync();
-
-    // Step g (global step counter over all tiles) reads buffer g % 2; at its
-    // start it issues the loads of step g + 1 into the other buffer (read by
-    // step g - 1, which every wave finished before the last barrier).
-    int g = 0;
-    int t_next = t_begin + 1;
-    int kv_tile_next = t_next < t_end ? tile_kv0(t_next) : 0;
-    auto run_tile = [&](auto masked_tag) {
-#pragma unroll
-      for (int sub = 0; sub < SPT; ++sub) {
-        constexpr bool M = decltype(masked_tag)::value;
-        const bool last_sub = sub == SPT - 1;
-        const bool has_next = !last_sub || t_next < t_end;
-        const int kv_nxt = last_sub ? kv_tile_next : kv0 + NK;
-        // buffer of this step: with two steps per tile the parity is the
-        // sub-step (every tile starts on buffer 0)
-        const int cur = (SPT == 2) ? sub : (g & 1);
-        const int nb = cur ^ 1;
-        if (has_next) issue_doc(nb, kv_nxt);
-        // without a next step the loads get an empty range (they fetch
-        // nothing; buffer nb was last read before the previous barrier)
-        constexpr int KPW = decltype(kload)::KB_PER_WAVE;
-        const i32x4 krs = kload.plan(has_next ? kv_nxt : a.KV_LEN, a.KV_LEN);
-        const i32x4 vrs = vload.plan(has_next ? kv_nxt : a.KV_LEN, a.KV_LEN);
-        auto dma = [&](int i) {
-          if (i < KPW) kload.issue_one(krs, k_lds[nb], i);
-          else vload.issue_one(vrs, v_lds[nb], i - KPW);
-        };
-        step<D, MASK, SCORE, M, 2 * KPW>(o, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
-                                (MASK == MASK_DOCUMENT) ? docbuf + cur * NK : nullptr, a, ln, dma);
-        kv0 = kv_nxt;
-        ++g;
-        wait_loads_and_sync();
-      }
-      ++t_next;
-      kv_tile_next = t_next < t_end ? tile_kv0(t_next) : 0;
-    };
-    // full tiles that end inside KV_LEN take the unmasked path; a full tile
-    // crossing KV_LEN (never listed by the builder) is masked on the key bound
-    const int nfull_fast =
-        (nfull > 0 && tile_kv0(nfull - 1) + kBlock > a.KV_LEN) ? nfull - 1 : nfull;
-    int j = t_begin;
-    for (; j < min(nfull_fast, t_end); ++j) run_tile(std::false_type{});
-    for (; j < t_end; ++j) run_tile(std::true_type{});
-  }
-
-  // epilogue: O = O_acc / l, LSE = ln(sum) + max
-  const float l_tot = l + __shfl_xor(l, 32, 64);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (a.splits > 1) {
-    // this slice's normalised O and LSE (-inf for an empty slice), fp32
-    if (qvalid) {
-      const long long row = (((long long)split * a.B + b) * a.Hq + h) * a.Q_LEN + ln.q;
-      float* orow = a.part_o + row * D;
-#pragma unroll
-      for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          float4 v4;
-          v4.x = o[db][4 * gq + 0] * inv;
-          v4.y = o[db][4 * gq + 1] * inv;
-          v4.z = o[db][4 * gq + 2] * inv;
-          v4.w = o[db][4 * gq + 3] * inv;
-          *reinterpret_cast<float4*>(orow + 32 * db + 8 * gq + 4 * ln.hh) = v4;
-        }
-      if (ln.hh == 0)
-        a.part_lse[row] = l_tot > 0.0f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
-    }
-    return;
-  }
-  if (qvalid) {
-    u16* orow = a.o + b * a.so0 + h * a.so1 + (long long)ln.q * a.so2;
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        bf16x4 pk;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pk[j] = (__bf16)(o[db][4 * gq + j] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * gq + 4 * ln.hh) = pk;
-      }
-    }
-    if (ln.hh == 0) {
-      const float lse = l_tot > 0.0f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
-      a.lse[((long long)b * a.Hq + h) * a.Q_LEN + ln.q] = lse;
-    }
-  }
-}
-
-template <int D, int MASK, int SCORE, int HEADS>
-hipError_t launch_one(const FwdArgs& args, int grid, hipStream_t stream) {
-  const int lds = 4 * ((args.bm.NKB + 3) & ~3);
-  static int attr_bytes = 0;
-  if (lds > attr_bytes) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&fwd_bf16_kernel<D, MASK, SCORE, HEADS>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_bytes = lds;
-  }
-  fwd_bf16_kernel<D, MASK, SCORE, HEADS><<<grid, 64 * kWavesPerHead * HEADS, lds, stream>>>(args);
-  return hipGetLastError();
-}
-
-template <int D, int MASK, int HEADS>
-hipError_t dispatch_score(const FwdArgs& args, int score, int grid, hipStream_t stream) {
-  switch (score) {
-    case SCORE_NONE:
-      return launch_one<D, MASK, SCORE_NONE, HEADS>(args, grid, stream);
-    case SCORE_ALIBI:
-      return launch_one<D, MASK, SCORE_ALIBI, HEADS>(args, grid, stream);
-    case SCORE_SOFTCAP:
-      return launch_one<D, MASK, SCORE_SOFTCAP, HEADS>(args, grid, stream);
-    case SCORE_SOFTCAP_ALIBI:
-      return launch_one<D, MASK, SCORE_SOFTCAP_ALIBI, HEADS>(args, grid, stream);
-    default:
-      return launch_one<D, MASK, SCORE_SCALED, HEADS>(args, grid, stream);
-  }
-}
-
-template <int D, int HEADS>
-hipError_t dispatch_mask(const FwdArgs& args, int mask, int score, int grid, hipStream_t stream) {
-  switch (mask) {
-    case MASK_NOOP:
-      return dispatch_score<D, MASK_NOOP, HEADS>(args, score, grid, stream);
-    case MASK_CAUSAL:
-      return dispatch_score<D, MASK_CAUSAL, HEADS>(args, score, grid, stream);
-    case MASK_SLIDING_SINK:
-      return dispatch_score<D, MASK_SLIDING_SINK, HEADS>(args, score, grid, stream);
-    case MASK_PREFIX_LM:
-      return dispatch_score<D, MASK_PREFIX_LM, HEADS>(args, score, grid, stream);
-    default:
-      return dispatch_score<D, MASK_DOCUMENT, HEADS>(args, score, grid, stream);
-  }
-}
-
-template <int D>
-hipError_t dispatch_heads(const FwdArgs& args, int heads, int mask, int score, int grid,
-                          hipStream_t stream) {
-  if (heads == 2) return dispatch_mask<D, 2>(args, mask, score, grid, stream);
-  return dispatch_mask<D, 1>(args, mask, score, grid, stream);
-}
-
-// Merge of the split-KV slices, one 64-lane wave per query row: with the
-// slices' LSE_s, LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s
-// (the rescaling of the online softmax, applied across slices).
-template <int D>
-__global__ __launch_bounds__(256) void splitkv_combine_kernel(FwdArgs a) {
-  constexpr int PER = D / 64;  // elements per lane
-  const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  float m = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) m = fmaxf(m, a.part_lse[s * rows + row]);
-  float acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
-  float wsum = 0.0f;
-  if (m != -INFINITY) {
-    for (int s = 0; s < a.splits; ++s) {
-      const float ls = a.part_lse[s * rows + row];
-      const float w = ls == -INFINITY ? 0.0f : fast_exp2((ls - m) * kLog2e);
-      wsum += w;
-      const float* src = a.part_o + (s * rows + row) * D + lane * PER;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, src[i], acc[i]);
-    }
-  }
-  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  const int qi = (int)(row % a.Q_LEN);
-  const long long bh = row / a.Q_LEN;
-  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
-  u16* orow = a.o + b * a.so0 + h * a.so1 + (long long)qi * a.so2 + lane * PER;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const __bf16 v = (__bf16)(acc[i] * inv);
-    __builtin_memcpy(orow + i, &v, 2);
-  }
-  if (lane == 0)
-    a.lse[((long long)b * a.Hq + h) * a.Q_LEN + qi] =
-        wsum > 0.0f ? m + fast_log2(wsum) * kLn2 : -INFINITY;
-}
-
-}  // namespace
-
-int fwd_bf16_lds_bytes(int D, int NKB) {
+int fwd_bf16_lds_bytes(int D, int NKB, bool paged) {
   (void)D;
-  return 4 * kStepBytes + 4 * ((NKB + 3) & ~3) + 2 * 128 * 4;
+  return 4 * kStepBytes + 4 * ((NKB + 3) & ~3) * (paged ? 2 : 1) + 2 * 128 * 4;
 }
 
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream) {
-  FwdArgs a;
-  a.q = static_cast<const u16*>(L.q);
-  a.k = static_cast<const u16*>(L.k);
-  a.v = static_cast<const u16*>(L.v);
-  a.o = static_cast<u16*>(L.o);
-  a.lse = L.lse;
-  a.sq0 = L.sq[0]; a.sq1 = L.sq[1]; a.sq2 = L.sq[2];
-  a.sk0 = L.sk[0]; a.sk1 = L.sk[1]; a.sk2 = (int)L.sk[2];
-  a.sv0 = L.sv[0]; a.sv1 = L.sv[1]; a.sv2 = (int)L.sv[2];
-  a.so0 = L.so[0]; a.so1 = L.so[1]; a.so2 = L.so[2];
-  a.B = L.B;
-  a.Hq = L.Hq;
-  a.Hkv = L.Hkv;
-  a.G = L.Hq / L.Hkv;
-  a.Q_LEN = L.Q_LEN;
-  a.KV_LEN = L.KV_LEN;
-  a.mp = L.mp;
-  a.doc_len = L.doc_len;
-  a.c_scale = L.scale * kLog2e;
-  a.c_cap = L.softcap > 0.0f ? 2.0f * L.scale * kLog2e / L.softcap : 0.0f;
-  a.cap2 = L.softcap * kLog2e;
-  a.slopes = L.slopes;
-  a.bm = L.bm;
-  a.splits = L.splits > 1 ? L.splits : 1;
-  a.part_o = L.part_o;
-  a.part_lse = L.part_lse;
-  // Two query heads per workgroup are possible when they share a KV head and
-  // a BlockMask row (mask broadcast over heads, even GQA group); one head per
-  // workgroup is the default, FLEXATTN_BF16_HEADS=2 selects the pairs (only
-  // where they apply).
-  const bool pair_ok = L.bm.Hm == 1 && a.G % 2 == 0 && a.splits == 1;
-  int heads = 1;  // measured: two 4-wave workgroups per CU beat one 8-wave one
-  if (const char* env = getenv("FLEXATTN_BF16_HEADS")) {
-    if (env[0] == '1') heads = 1;
-    if (env[0] == '2' && pair_ok) heads = 2;
-  }
-  // Short query tiles (Q_LEN <= 64, one tile) with the mask broadcast over
-  // heads: fewest waves per head that cover Q_LEN and give a whole number of
-  // heads per workgroup inside one KV group.
-  a.wph = kWavesPerHead;
-  if (heads == 1 && L.bm.Hm == 1 && L.Q_LEN <= 64)
-    for (int w = 1; w < kWavesPerHead; w *= 2)
-      if (L.Q_LEN <= 32 * w && a.G % (kWavesPerHead / w) == 0) {
-        a.wph = w;
-        break;
-      }
-  const int hpw = heads * kWavesPerHead / a.wph;  // query heads per workgroup
-  // XCD-aware order: with the mask broadcast over batch and heads every
-  // schedule round holds the B*Hq/hpw items of one query tile; split each
-  // round into 8 contiguous chunks of whole KV groups, one per XCD.
-  const int R = L.B * L.Hq / hpw;
-  const int g_items = a.G / hpw;  // items per KV group
-  a.xcd_round = (L.bm.Bm == 1 && L.bm.Hm == 1 && R % 8 == 0 && (R / 8) % g_items == 0) ? R : 0;
-  const int grid = R * L.bm.NQB * a.splits;
-  if (grid == 0) return hipSuccess;
-  // the unscaled fast path takes the row max before scaling: scale must be > 0
-  const int score = (L.score_kind == SCORE_NONE && !(L.scale > 0.0f)) ? SCORE_SCALED : L.score_kind;
-  hipError_t e = (L.D == 128) ? dispatch_heads<128>(a, heads, L.mask_kind, score, grid, stream)
-                              : dispatch_heads<64>(a, heads, L.mask_kind, score, grid, stream);
-  if (e != hipSuccess || a.splits == 1) return e;
-  const long long rows = (long long)L.B * L.Hq * L.Q_LEN;
-  const unsigned blocks = (unsigned)((rows + 3) / 4);
-  if (L.D == 128) splitkv_combine_kernel<128><<<blocks, 256, 0, stream>>>(a);
-  else splitkv_combine_kernel<64><<<blocks, 256, 0, stream>>>(a);
-  return hipGetLastError();
+  if (L.page_table) return launch_fwd_bf16_paged(L, stream);
+  return launch_impl<false>(L, stream);
 }
 
 }  // namespace fa

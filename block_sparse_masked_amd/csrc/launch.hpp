@@ -52,10 +52,15 @@ struct FwdLaunch {
   int splits = 1;             // bf16 split-KV slices per item (1: none)
   float* part_o = nullptr;    // workspace [splits][B][Hq][Q_LEN][D] fp32
   float* part_lse = nullptr;  // workspace [splits][B][Hq][Q_LEN] fp32
+  // bf16 paged KV (page_table != nullptr): k / v are page caches, sk[0] /
+  // sv[0] the page strides; page_table int32 [B][pt_stride]
+  const int* page_table = nullptr;
+  int page_size = 0, pt_stride = 0, num_pages = 0;
 };
 
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream);
-int fwd_bf16_lds_bytes(int D, int NKB);  // dynamic LDS of the bf16 forward
+hipError_t launch_fwd_bf16_paged(const FwdLaunch& L, hipStream_t stream);  // L.page_table set
+int fwd_bf16_lds_bytes(int D, int NKB, bool paged);  // LDS of the bf16 forward
 constexpr int kMaxLdsBytes = 160 * 1024;
 constexpr long long kMaxBf16RowStride = 1ll << 22;  // k/v row stride limit of the bf16 forward
 hipError_t launch_fwd_f32(const FwdLaunch& L, hipStream_t stream);

@@ -262,6 +262,39 @@ flexattn_status flexattn_fwd_splitkv(const flexattn_tensor* q, const flexattn_te
                                      flexattn_tensor* out, float* lse, void* stream);
 
 /*
+ * Paged KV cache (page "FlagAttention", operator overview: paged attention,
+ * queries over a KV cache kept in fixed-size pages). The cache holds
+ * num_pages pages of page_size key rows per KV head; a sequence's keys are
+ * laid out page by page through its row of the page table.
+ * page_table: device int32 [B][max_pages]; entry (b, p) is the cache page
+ * that holds keys [p * page_size, (p + 1) * page_size) of batch b. Entries
+ * past the pages KV_LEN needs are not read. An entry outside
+ * [0, num_pages) is clamped into it (wrong output, no out-of-bounds read).
+ */
+typedef struct {
+  const int32_t* page_table;
+  int32_t max_pages;  /* entries per batch row; max_pages * page_size >= KV_LEN */
+} flexattn_page_table;
+
+/*
+ * Forward over a paged KV cache: the same method and outputs as
+ * flexattn_fwd (and, with num_splits > 1, flexattn_fwd_splitkv, whose
+ * workspace rules apply) with keys read through the page table. k_cache and
+ * v_cache are flexattn_tensors with B = num_pages, H = Hkv, L = page_size
+ * (a multiple of 128, so a BlockMask tile never straddles pages), any
+ * 16-byte-multiple strides. The sequence length is bm->KV_LEN. bf16 only
+ * (UNSUPPORTED otherwise); page sizes that are not multiples of 128 are
+ * UNSUPPORTED. Asynchronous on `stream`.
+ */
+flexattn_status flexattn_fwd_paged(const flexattn_tensor* q, const flexattn_tensor* k_cache,
+                                   const flexattn_tensor* v_cache,
+                                   const flexattn_page_table* pages,
+                                   const flexattn_block_mask* bm, flexattn_score_kind score_kind,
+                                   const flexattn_score_params* params, float scale,
+                                   int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                   flexattn_tensor* out, float* lse, void* stream);
+
+/*
  * from_kv_blocks (page "tensorplay.nn.attention API", BlockMask.from_kv_blocks):
  * completes a BlockMask whose tile lists the caller filled. On input the
  * caller sets every field of `bm`: the extents, lengths, BLOCK_SIZE (128),

@@ -16,6 +16,7 @@ from .reference import (  # noqa: F401
     create_mask,
     document_causal_mask,
     from_kv_blocks_mask,
+    gather_paged,
     noop_mask,
     or_masks,
     prefix_lm_mask,

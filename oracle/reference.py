@@ -327,6 +327,18 @@ def to_dense(num_blocks: np.ndarray, indices: np.ndarray, num_cols: int) -> np.n
 # standard softmax; rows are independent, so they may be taken in chunks)
 # --------------------------------------------------------------------------
 
+def gather_paged(cache: np.ndarray, page_table: np.ndarray, kv_len: int) -> np.ndarray:
+    """Keys (or values) of each sequence from a paged KV cache: row j of
+    batch b is row j mod P of cache page page_table[b, j div P], P the page
+    size (page "FlagAttention", operator overview: a KV cache kept in pages).
+    cache [num_pages, H, P, D] -> [B, H, kv_len, D]."""
+    P = cache.shape[2]
+    j = np.arange(kv_len)
+    pages = np.asarray(page_table)[:, j // P]                    # [B, kv_len]
+    out = cache[pages, :, (j % P)[None, :], :]                   # [B, kv_len, H, D]
+    return np.ascontiguousarray(np.swapaxes(out, 1, 2))
+
+
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
               mask_mod: Optional[MaskMod] = None,
               score_mod: Optional[ScoreMod] = None,

@@ -273,3 +273,33 @@ def test_splitkv_is_bf16_only(L):
     t = [_tensor(dtype=0) for _ in range(4)]
     assert _fwd_split(L, 2, q=t[0], k=t[1], v=t[2], o=t[3]) == lib._UNSUPPORTED
     assert b"bf16" in L.flexattn_last_error()
+
+
+def _fwd_paged(L, pages=True, table=4096, max_pages=2, page=128, dtype=1, splits=1):
+    q = _tensor(dtype=dtype)
+    kc = _tensor(dtype=dtype, B=5, H=2, L_=page)
+    vc = _tensor(dtype=dtype, B=5, H=2, L_=page)
+    o = _tensor(dtype=dtype)
+    bm = _good_bm()
+    sp = lib._ScoreParams(0.0, None)
+    pt = lib._PageTable(table, max_pages)
+    return L.flexattn_fwd_paged(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(vc),
+                                ctypes.byref(pt) if pages else None, ctypes.byref(bm), 0,
+                                ctypes.byref(sp), 0.125, splits, None, 0, ctypes.byref(o),
+                                ctypes.c_void_p(4096), None)
+
+
+@pytest.mark.parametrize("case,expect,msg", [
+    (dict(pages=False), lib._INVALID, b"pages is NULL"),
+    (dict(table=0), lib._INVALID, b"page_table"),
+    (dict(table=4098), lib._INVALID, b"aligned"),
+    (dict(max_pages=1), lib._INVALID, b"do not cover"),
+    (dict(page=64), lib._UNSUPPORTED, b"multiple of 128"),
+    (dict(dtype=0), lib._UNSUPPORTED, b"bf16"),
+    (dict(splits=0), lib._INVALID, b"num_splits"),
+    (dict(splits=2), lib._INVALID, b"workspace"),
+])
+def test_fwd_paged_rejects_bad_arguments(L, case, expect, msg):
+    # the BlockMask is for KV_LEN 256: two pages of 128 keys cover it
+    assert _fwd_paged(L, **case) == expect
+    assert msg in L.flexattn_last_error()

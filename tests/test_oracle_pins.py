@@ -444,3 +444,24 @@ def test_from_kv_blocks_hand_example():
             exp[q, kv] = kv <= q                # partial tile (0, 1): causal -> none
     exp[4:6, 4:6] = True                        # full tile (2, 2)
     assert np.array_equal(got, exp)
+
+
+@pytest.mark.parametrize("N,page", [(300, 128), (256, 128), (1000, 256), (128, 512)])
+def test_gather_paged_round_trip(N, page):
+    """The oracle's paged gather undoes the generator's page-by-page scatter
+    (written separately, as a loop over pages) for full and partial last
+    pages; cache rows outside the sequences are NaN and never gathered."""
+    rng = np.random.default_rng(N + page)
+    k = rng.standard_normal((2, 3, N, 16)).astype(np.float32)
+    v = rng.standard_normal((2, 3, N, 16)).astype(np.float32)
+    kc, vc, table = W.paged_cache(k, v, page, seed=N)
+    assert np.array_equal(oracle.gather_paged(kc, table, N), k)
+    assert np.array_equal(oracle.gather_paged(vc, table, N), v)
+
+
+def test_gather_paged_identity_layout():
+    """One page per sequence holding it whole, page b for batch b: the cache
+    is the contiguous tensor itself."""
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((3, 2, 256, 8))
+    assert np.array_equal(oracle.gather_paged(k, np.arange(3, dtype=np.int32)[:, None], 256), k)

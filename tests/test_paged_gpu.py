@@ -1,0 +1,88 @@
+"""Forward over a paged KV cache on the GPU: against the fp64 oracle on the
+keys gathered through the page table, bit-identical to the contiguous
+forward on the same keys, with and without split-KV. Unused cache rows are
+NaN, so a read outside a sequence would show in the output."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_helpers as G
+from tests.test_fwd_gpu import tiny
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_masked_amd as m
+    m.load_library()
+    return m
+
+
+def paged_inputs(w, page, seed=11):
+    inp = W.generate(w)
+    kc, vc, table = W.paged_cache(inp.k, inp.v, page, seed=seed)
+    dev = lambda x: G.to_device(x, "bf16")  # noqa: E731
+    return inp, dev(inp.q), dev(kc), dev(vc), torch.from_numpy(table).cuda(), (kc, vc, table)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask,score", [("noop", "none"), ("causal", "alibi"),
+                                        ("sliding_sink", "softcap"),
+                                        ("document_causal", "softcap_alibi"),
+                                        ("prefix_lm", "none")])
+@pytest.mark.parametrize("q_len,kv_len,page", [(300, 300, 128), (16, 1000, 256),
+                                               (130, 900, 384)])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_paged_against_oracle(lib, D, mask, score, q_len, kv_len, page, splits):
+    w = tiny("bf16", D, mask, score, B=2, Hq=4, Hkv=2, Q_LEN=q_len, KV_LEN=kv_len,
+             window=150, prefix=60, value_scale=2.0 if "softcap" in score else 1.0)
+    inp, q, kc, vc, table, host = paged_inputs(w, page)
+    # the oracle reads the keys through the page table
+    kc_h, vc_h, table_h = host
+    assert np.array_equal(oracle.gather_paged(kc_h, table_h, kv_len), inp.k)
+    bm = G.build_gpu_mask(lib, w, inp)
+    out, lse = lib.flex_attention(q, kc, vc, bm, score=w.score, softcap=w.softcap, scale=w.scale,
+                                  num_splits=splits, page_table=table)
+    torch.cuda.synchronize()
+    mask_mod, score_mod = oracle.for_workload(w, inp)
+    o_ref, lse_ref = oracle.attention(inp.q, oracle.gather_paged(kc_h, table_h, kv_len),
+                                      oracle.gather_paged(vc_h, table_h, kv_len), mask_mod,
+                                      score_mod, w.scale)
+    res = G.compare(w, out.float().cpu().numpy().astype(np.float64),
+                    lse.cpu().numpy().astype(np.float64), o_ref, lse_ref)
+    assert res["ok"], G.summary(res)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_paged_matches_contiguous_bitwise(lib, splits):
+    """Same keys, same tiles, same arithmetic: the paged forward's O and LSE
+    equal the contiguous forward's bit for bit."""
+    w = tiny("bf16", 128, "sliding_sink", "alibi", B=3, Hq=8, Hkv=2, Q_LEN=200, KV_LEN=1500,
+             window=400)
+    inp, q, kc, vc, table, _ = paged_inputs(w, 256, seed=3)
+    k, v = G.to_device(inp.k, "bf16"), G.to_device(inp.v, "bf16")
+    bm = G.build_gpu_mask(lib, w, inp)
+    o1, l1 = lib.flex_attention(q, k, v, bm, score="alibi", scale=w.scale, num_splits=splits)
+    o2, l2 = lib.flex_attention(q, kc, vc, bm, score="alibi", scale=w.scale, num_splits=splits,
+                                page_table=table)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_paged_rejections(lib):
+    w = tiny("bf16", 64, "noop", "none", B=1, Hq=2, Hkv=1, Q_LEN=128, KV_LEN=300)
+    inp, q, kc, vc, table, _ = paged_inputs(w, 128)
+    bm = G.build_gpu_mask(lib, w, inp)
+    with pytest.raises(ValueError, match="do not cover"):
+        lib.flex_attention(q, kc, vc, bm, page_table=table[:, :2].contiguous())
+    k64 = torch.zeros((kc.shape[0] * 2, kc.shape[1], 64, kc.shape[3]), dtype=kc.dtype,
+                      device=kc.device)
+    with pytest.raises(NotImplementedError, match="multiple of 128"):
+        lib.flex_attention(q, k64, k64, bm, page_table=table)
+    with pytest.raises(NotImplementedError, match="bf16"):
+        lib.flex_attention(q.float(), kc.float(), vc.float(), bm, page_table=table)

@@ -182,6 +182,34 @@ def generate_upstream(w: Workload) -> np.ndarray:
     return round_to_bf16(g) if w.dtype == "bf16" else g
 
 
+def paged_cache(k: np.ndarray, v: np.ndarray, page_size: int, seed: int, spare_pages: int = 3,
+                extra_columns: int = 1):
+    """Lay k and v [B, H, N, D] out in a paged KV cache: pages of page_size
+    key rows per head, placed at a seeded random permutation of the cache's
+    pages, with `spare_pages` pages no sequence uses.
+
+    Returns (k_cache, v_cache [P, H, page_size, D], page_table int32
+    [B, ceil(N / page_size) + extra_columns]). Cache rows that hold no key
+    (spare pages, the rows past N in a sequence's last page) are NaN, and
+    the page table's extra columns hold an index past the cache, so a read
+    of anything outside the sequence shows up in the output."""
+    B, H, N, D = k.shape
+    per_seq = -(-N // page_size)
+    P = B * per_seq + spare_pages
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(P)[:B * per_seq].reshape(B, per_seq)
+    k_cache = np.full((P, H, page_size, D), np.nan, dtype=k.dtype)
+    v_cache = np.full((P, H, page_size, D), np.nan, dtype=v.dtype)
+    for b in range(B):
+        for j in range(per_seq):
+            rows = min(page_size, N - j * page_size)
+            k_cache[order[b, j], :, :rows] = k[b, :, j * page_size:j * page_size + rows]
+            v_cache[order[b, j], :, :rows] = v[b, :, j * page_size:j * page_size + rows]
+    table = np.full((B, per_seq + extra_columns), P + 1000, dtype=np.int32)
+    table[:, :per_seq] = order
+    return k_cache, v_cache, table
+
+
 def small(w: Workload, **kw) -> Workload:
     """A reduced copy of a workload (same kinds and dtype), for quick checks."""
     return w.with_(**kw)

@@ -31,7 +31,7 @@ _LIB_PATH = os.path.join(_HERE, "libflexattn.so")
 
 MASK_KINDS = {"noop": 0, "causal": 1, "sliding_sink": 2, "document_causal": 3, "prefix_lm": 4}
 SCORE_KINDS = {"none": 0, "alibi": 1, "softcap": 2, "softcap_alibi": 3}
-_F32, _BF16 = 0, 1
+_F32, _BF16, _F16 = 0, 1, 2
 _OK, _INVALID, _UNSUPPORTED, _HIP = 0, 1, 2, 3
 
 
@@ -269,8 +269,10 @@ def _tensor(t: torch.Tensor, name: str) -> _Tensor:
         dt = _F32
     elif t.dtype == torch.bfloat16:
         dt = _BF16
+    elif t.dtype == torch.float16:
+        dt = _F16
     else:
-        raise NotImplementedError(f"{name} dtype {t.dtype} is not float32 or bfloat16")
+        raise NotImplementedError(f"{name} dtype {t.dtype} is not float32, bfloat16 or float16")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     st = (ctypes.c_int64 * 4)(*t.stride())
@@ -282,7 +284,7 @@ def auto_splits(q: torch.Tensor, k: torch.Tensor, block_mask: BlockMask,
     """Split count for a bf16 call: enough workgroups to fill the chip
     (target_workgroups, four per CU) when there are few query tiles, at most
     the number of KV tiles a row can list, and 1 (no split) otherwise."""
-    if q.dtype != torch.bfloat16:
+    if q.dtype not in (torch.bfloat16, torch.float16):
         return 1
     B, Hq, M = q.shape[0], q.shape[1], q.shape[2]
     group = Hq // k.shape[1]

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libflexattn.so")
 
-SOURCES = ["api.cpp", "block_mask.hip", "fwd_bf16.hip", "fwd_bf16_paged.hip", "fwd_f32.hip",
+SOURCES = ["api.cpp", "block_mask.hip", "fwd_bf16.hip", "fwd_bf16_paged.hip", "fwd_f16.hip",
+           "fwd_f32.hip",
            "bwd_bf16.hip"]
 ARCH = "gfx950"
 

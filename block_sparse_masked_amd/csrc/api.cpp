@@ -88,8 +88,8 @@ flexattn_status check_tensor(const flexattn_tensor* t, const char* name,
                              const char* who = "flexattn_fwd") {
   if (!t) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: %s is NULL", who, name);
   if (!t->data) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: %s->data is NULL", who, name);
-  if (t->dtype != FLEXATTN_F32 && t->dtype != FLEXATTN_BF16)
-    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: %s dtype %d is not F32 or BF16", who, name,
+  if (t->dtype != FLEXATTN_F32 && t->dtype != FLEXATTN_BF16 && t->dtype != FLEXATTN_F16)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: %s dtype %d is not F32, BF16 or F16", who, name,
                 (int)t->dtype);
   if (t->B < 1 || t->H < 1 || t->L < 1 || t->D < 1)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: %s has a non-positive extent", who, name);
@@ -368,18 +368,19 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   if (score_kind == FLEXATTN_SCORE_ALIBI || score_kind == FLEXATTN_SCORE_SOFTCAP_ALIBI)
     slopes = params ? params->alibi_slopes : nullptr;
 
-  if (q->dtype == FLEXATTN_BF16 && fa::fwd_bf16_lds_bytes(q->D, bm->num_kv_blocks, pages != nullptr) >
+  const bool half = q->dtype == FLEXATTN_BF16 || q->dtype == FLEXATTN_F16;  // 16-bit kernel
+  if (half && fa::fwd_bf16_lds_bytes(q->D, bm->num_kv_blocks, pages != nullptr) >
                                         fa::kMaxLdsBytes)
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: KV_LEN %d needs more LDS than a workgroup has", who,
                 kv_len);
   // the bf16 kernel addresses a block of up to 128 key rows with 32-bit offsets
-  if (q->dtype == FLEXATTN_BF16 &&
+  if (half &&
       (k->stride[2] > fa::kMaxBf16RowStride || v->stride[2] > fa::kMaxBf16RowStride))
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: k/v row stride above %lld elements", who,
                 (long long)fa::kMaxBf16RowStride);
   if (splits > 1) {
-    if (q->dtype != FLEXATTN_BF16)
-      return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: split-KV is a bf16 path", who);
+    if (!half)
+      return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: split-KV is a bf16 / fp16 path", who);
     if (splits > 256)
       return fail(FLEXATTN_ERR_INVALID_ARG, "%s: num_splits %d above 256", who, splits);
     if (!workspace || !aligned16(workspace))
@@ -435,7 +436,8 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
     L.part_o = static_cast<float*>(workspace);
     L.part_lse = L.part_o + (size_t)splits * q->B * q->H * q->L * q->D;
   }
-  hipError_t e = (q->dtype == FLEXATTN_BF16)
+  L.f16 = q->dtype == FLEXATTN_F16;
+  hipError_t e = half
                      ? fa::launch_fwd_bf16(L, static_cast<hipStream_t>(stream))
                      : fa::launch_fwd_f32(L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)

@@ -12,8 +12,9 @@ int fwd_bf16_lds_bytes(int D, int NKB, bool paged) {
 }
 
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream) {
+  if (L.f16) return launch_fwd_f16(L, stream);
   if (L.page_table) return launch_fwd_bf16_paged(L, stream);
-  return launch_impl<false>(L, stream);
+  return launch_impl<false, false>(L, stream);
 }
 
 }  // namespace fa

@@ -51,7 +51,32 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// The 16-bit input element: bf16 (F16 = false) or fp16. Both have the same
+// register and LDS layouts and a 32x32x16 MFMA with fp32 accumulation; P is
+// rounded to the input type for the P.V product.
+template <bool F16>
+struct Elem {
+  using T = __bf16;
+  using V8 = bf16x8;
+  using V4 = bf16x4;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Elem<true> {
+  using T = _Float16;
+  using V8 = f16x8;
+  using V4 = f16x4;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 
@@ -223,8 +248,9 @@ __device__ __forceinline__ void wait_loads_and_sync() {
   __syncthreads();
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
-  bf16x8 r;
+template <bool F16>
+__device__ __forceinline__ typename Elem<F16>::V8 as_v8(uint4 u) {
+  typename Elem<F16>::V8 r;
   __builtin_memcpy(&r, &u, 16);
   return r;
 }
@@ -267,23 +293,26 @@ __device__ __forceinline__ float pair_max(float x) {
 // order of pf), read from the row-major V block with two transposing reads:
 // in each 16-lane group lane j supplies the 8-byte piece (row j/4, columns
 // 4*(j%4)..+3) of a 4-key x 16-d block and receives column j of that block.
-template <int D>
-__device__ __forceinline__ bf16x8 v_frag(const u16* sV, const Lane<D>& ln, int ks, int db) {
-  bf16x4 part[2];
+template <int D, bool F16>
+__device__ __forceinline__ typename Elem<F16>::V8 v_frag(const u16* sV, const Lane<D>& ln, int ks,
+                                                         int db) {
+  typename Elem<F16>::V4 part[2];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const u16* src = sV + ln.vofs[db] + (16 * ks + 8 * ht) * D;
-    part[ht] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) bf16x4*)(src));
+    const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(src));
+    __builtin_memcpy(&part[ht], &raw, 8);
   }
   return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // K operand fragment for S MFMA (k-step ks, key block blk): rows
 // 32*blk + lane%32 keep row % 16 (and (row/2) % 8), so one offset per k-step.
-template <int D>
-__device__ __forceinline__ bf16x8 k_frag(const u16* sK, const Lane<D>& ln, int ks, int blk) {
-  return as_bf16x8(*reinterpret_cast<const uint4*>(sK + ln.kofs[ks] + 32 * blk * D));
+template <int D, bool F16>
+__device__ __forceinline__ typename Elem<F16>::V8 k_frag(const u16* sK, const Lane<D>& ln, int ks,
+                                                         int blk) {
+  return as_v8<F16>(*reinterpret_cast<const uint4*>(sK + ln.kofs[ks] + 32 * blk * D));
 }
 
 // Key offset (within the step, without 4*hh) of result register r of block blk.
@@ -335,9 +364,10 @@ __device__ __forceinline__ float elem_logit(float x, int blk, int r, int kv0, co
 
 // One KV step: S = K . Q^T, online softmax, O += V . P. `dma(i)` issues the
 // i-th of the NDMA loads of the next step (called between S products).
-template <int D, int MASK, int SCORE, bool MASKED, int NDMA, typename DMA>
+template <int D, int MASK, int SCORE, bool MASKED, int NDMA, bool F16, typename DMA>
 __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l,
-                                     const bf16x8 (&qf)[D / 16], const u16* sK, const u16* sV,
+                                     const typename Elem<F16>::V8 (&qf)[D / 16], const u16* sK,
+                                     const u16* sV,
                                      int kv0, const int* step_doc, const FwdArgs& a,
                                      const Lane<D>& ln, DMA&& dma) {
   using G = Geom<D>;
@@ -349,8 +379,7 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
 #pragma unroll
     for (int b = 0; b < G::NB; ++b)
     {
-      s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(sK, ln, ks, b), qf[ks], s[b], 0,
-                                                     0, 0);
+      s[b] = Elem<F16>::mfma(k_frag<D, F16>(sK, ln, ks, b), qf[ks], s[b]);
       // the next step's loads, spread over the S products
       constexpr int NS = G::KS * G::NB;
       static_assert(NS % NDMA == 0, "loads spread evenly");
@@ -384,7 +413,7 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
   }
   const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
 
-  bf16x8 pf[G::PKS];
+  typename Elem<F16>::V8 pf[G::PKS];
   float rs = 0.0f;
 #pragma unroll
   for (int e = 0; e < G::NE; ++e) {
@@ -396,7 +425,7 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
       p = fast_exp2(y - m_use);
     }
     rs += p;
-    pf[e >> 3][e & 7] = (__bf16)p;
+    pf[e >> 3][e & 7] = (typename Elem<F16>::T)p;
   }
   l += rs;
 
@@ -404,15 +433,15 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
   for (int ks = 0; ks < G::PKS; ++ks)
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D>(sV, ln, ks, db), pf[ks], o[db], 0,
-                                                      0, 0);
+      o[db] = Elem<F16>::mfma(v_frag<D, F16>(sV, ln, ks, db), pf[ks], o[db]);
 }
 
 // HEADS query heads that share one KV head (and one BlockMask row) per
 // workgroup: 4 * HEADS waves read the same K/V step blocks, so HEADS = 2
 // halves the global->LDS traffic per flop. Two waves per SIMD either way.
-template <int D, int MASK, int SCORE, int HEADS, bool PAGED>
+template <int D, int MASK, int SCORE, int HEADS, bool PAGED, bool F16>
 __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf16_kernel(FwdArgs a) {
+  using E = Elem<F16>;
   using G = Geom<D>;
   constexpr int WAVES = kWavesPerHead * HEADS;
   constexpr int THREADS = 64 * WAVES;
@@ -543,12 +572,12 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
     issue_doc(0, kv0);
     kload.issue(kv0, a.KV_LEN, k_lds[0]);
     vload.issue(kv0, a.KV_LEN, v_lds[0]);
-    bf16x8 qf[G::KS];
+    typename E::V8 qf[G::KS];
     {
       const u16* qrow = a.q + b * a.sq0 + h * a.sq1 + (long long)ln.qc * a.sq2;
 #pragma unroll
       for (int ks = 0; ks < G::KS; ++ks)
-        qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * ln.hh));
+        qf[ks] = as_v8<F16>(*reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * ln.hh));
     }
     wait_loads_and_sync();
 
@@ -585,7 +614,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
           if (i < KPW) kload.issue_one(krs, k_lds[nb], i);
           else vload.issue_one(vrs, v_lds[nb], i - KPW);
         };
-        step<D, MASK, SCORE, M, 2 * KPW>(o, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
+        step<D, MASK, SCORE, M, 2 * KPW, F16>(o, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
                                 (MASK == MASK_DOCUMENT) ? docbuf + cur * NK : nullptr, a, ln, dma);
         kv0 = kv_nxt;
         ++g;
@@ -634,10 +663,10 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
     for (int db = 0; db < G::DB; ++db) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        bf16x4 pk;
+        typename E::V4 pk;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pk[j] = (__bf16)(o[db][4 * gq + j] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * gq + 4 * ln.hh) = pk;
+        for (int j = 0; j < 4; ++j) pk[j] = (typename E::T)(o[db][4 * gq + j] * inv);
+        *reinterpret_cast<typename E::V4*>(orow + 32 * db + 8 * gq + 4 * ln.hh) = pk;
       }
     }
     if (ln.hh == 0) {
@@ -647,66 +676,67 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
   }
 }
 
-template <int D, int MASK, int SCORE, int HEADS, bool PAGED>
+template <int D, int MASK, int SCORE, int HEADS, bool PAGED, bool F16>
 hipError_t launch_one(const FwdArgs& args, int grid, hipStream_t stream) {
   const int lds = 4 * ((args.bm.NKB + 3) & ~3) * (PAGED ? 2 : 1);
   static int attr_bytes = 0;
   if (lds > attr_bytes) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&fwd_bf16_kernel<D, MASK, SCORE, HEADS, PAGED>),
+        reinterpret_cast<const void*>(&fwd_bf16_kernel<D, MASK, SCORE, HEADS, PAGED, F16>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_bytes = lds;
   }
-  fwd_bf16_kernel<D, MASK, SCORE, HEADS, PAGED><<<grid, 64 * kWavesPerHead * HEADS, lds, stream>>>(args);
+  fwd_bf16_kernel<D, MASK, SCORE, HEADS, PAGED, F16><<<grid, 64 * kWavesPerHead * HEADS, lds, stream>>>(args);
   return hipGetLastError();
 }
 
-template <int D, int MASK, int HEADS, bool PAGED>
+template <int D, int MASK, int HEADS, bool PAGED, bool F16>
 hipError_t dispatch_score(const FwdArgs& args, int score, int grid, hipStream_t stream) {
   switch (score) {
     case SCORE_NONE:
-      return launch_one<D, MASK, SCORE_NONE, HEADS, PAGED>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_NONE, HEADS, PAGED, F16>(args, grid, stream);
     case SCORE_ALIBI:
-      return launch_one<D, MASK, SCORE_ALIBI, HEADS, PAGED>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_ALIBI, HEADS, PAGED, F16>(args, grid, stream);
     case SCORE_SOFTCAP:
-      return launch_one<D, MASK, SCORE_SOFTCAP, HEADS, PAGED>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_SOFTCAP, HEADS, PAGED, F16>(args, grid, stream);
     case SCORE_SOFTCAP_ALIBI:
-      return launch_one<D, MASK, SCORE_SOFTCAP_ALIBI, HEADS, PAGED>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_SOFTCAP_ALIBI, HEADS, PAGED, F16>(args, grid, stream);
     default:
-      return launch_one<D, MASK, SCORE_SCALED, HEADS, PAGED>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_SCALED, HEADS, PAGED, F16>(args, grid, stream);
   }
 }
 
-template <int D, int HEADS, bool PAGED>
+template <int D, int HEADS, bool PAGED, bool F16>
 hipError_t dispatch_mask(const FwdArgs& args, int mask, int score, int grid, hipStream_t stream) {
   switch (mask) {
     case MASK_NOOP:
-      return dispatch_score<D, MASK_NOOP, HEADS, PAGED>(args, score, grid, stream);
+      return dispatch_score<D, MASK_NOOP, HEADS, PAGED, F16>(args, score, grid, stream);
     case MASK_CAUSAL:
-      return dispatch_score<D, MASK_CAUSAL, HEADS, PAGED>(args, score, grid, stream);
+      return dispatch_score<D, MASK_CAUSAL, HEADS, PAGED, F16>(args, score, grid, stream);
     case MASK_SLIDING_SINK:
-      return dispatch_score<D, MASK_SLIDING_SINK, HEADS, PAGED>(args, score, grid, stream);
+      return dispatch_score<D, MASK_SLIDING_SINK, HEADS, PAGED, F16>(args, score, grid, stream);
     case MASK_PREFIX_LM:
-      return dispatch_score<D, MASK_PREFIX_LM, HEADS, PAGED>(args, score, grid, stream);
+      return dispatch_score<D, MASK_PREFIX_LM, HEADS, PAGED, F16>(args, score, grid, stream);
     default:
-      return dispatch_score<D, MASK_DOCUMENT, HEADS, PAGED>(args, score, grid, stream);
+      return dispatch_score<D, MASK_DOCUMENT, HEADS, PAGED, F16>(args, score, grid, stream);
   }
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool F16>
 hipError_t dispatch_heads(const FwdArgs& args, int heads, int mask, int score, int grid,
                           hipStream_t stream) {
-  if constexpr (!PAGED)
-    if (heads == 2) return dispatch_mask<D, 2, false>(args, mask, score, grid, stream);
-  return dispatch_mask<D, 1, PAGED>(args, mask, score, grid, stream);
+  if constexpr (!PAGED && !F16)
+    if (heads == 2) return dispatch_mask<D, 2, false, false>(args, mask, score, grid, stream);
+  return dispatch_mask<D, 1, PAGED, F16>(args, mask, score, grid, stream);
 }
 
 // Merge of the split-KV slices, one 64-lane wave per query row: with the
 // slices' LSE_s, LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s
 // (the rescaling of the online softmax, applied across slices).
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void splitkv_combine_kernel(FwdArgs a) {
+  using T = typename Elem<F16>::T;
   constexpr int PER = D / 64;  // elements per lane
   const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -735,7 +765,7 @@ __global__ __launch_bounds__(256) void splitkv_combine_kernel(FwdArgs a) {
   u16* orow = a.o + b * a.so0 + h * a.so1 + (long long)qi * a.so2 + lane * PER;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const __bf16 v = (__bf16)(acc[i] * inv);
+    const T v = (T)(acc[i] * inv);
     __builtin_memcpy(orow + i, &v, 2);
   }
   if (lane == 0)
@@ -746,7 +776,7 @@ __global__ __launch_bounds__(256) void splitkv_combine_kernel(FwdArgs a) {
 
 // Argument set-up, launch shape and dispatch of the forward (and the merge
 // of split-KV slices); PAGED selects the paged-KV instantiations.
-template <bool PAGED>
+template <bool PAGED, bool F16>
 hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
   FwdArgs a;
   a.q = static_cast<const u16*>(L.q);
@@ -782,7 +812,7 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
   // a BlockMask row (mask broadcast over heads, even GQA group); one head per
   // workgroup is the default, FLEXATTN_BF16_HEADS=2 selects the pairs (only
   // where they apply).
-  const bool pair_ok = !PAGED && L.bm.Hm == 1 && a.G % 2 == 0 && a.splits == 1;
+  const bool pair_ok = !PAGED && !F16 && L.bm.Hm == 1 && a.G % 2 == 0 && a.splits == 1;
   int heads = 1;  // measured: two 4-wave workgroups per CU beat one 8-wave one
   if (const char* env = getenv("FLEXATTN_BF16_HEADS")) {
     if (env[0] == '1') heads = 1;
@@ -809,13 +839,13 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   // the unscaled fast path takes the row max before scaling: scale must be > 0
   const int score = (L.score_kind == SCORE_NONE && !(L.scale > 0.0f)) ? SCORE_SCALED : L.score_kind;
-  hipError_t e = (L.D == 128) ? dispatch_heads<128, PAGED>(a, heads, L.mask_kind, score, grid, stream)
-                              : dispatch_heads<64, PAGED>(a, heads, L.mask_kind, score, grid, stream);
+  hipError_t e = (L.D == 128) ? dispatch_heads<128, PAGED, F16>(a, heads, L.mask_kind, score, grid, stream)
+                              : dispatch_heads<64, PAGED, F16>(a, heads, L.mask_kind, score, grid, stream);
   if (e != hipSuccess || a.splits == 1) return e;
   const long long rows = (long long)L.B * L.Hq * L.Q_LEN;
   const unsigned blocks = (unsigned)((rows + 3) / 4);
-  if (L.D == 128) splitkv_combine_kernel<128><<<blocks, 256, 0, stream>>>(a);
-  else splitkv_combine_kernel<64><<<blocks, 256, 0, stream>>>(a);
+  if (L.D == 128) splitkv_combine_kernel<128, F16><<<blocks, 256, 0, stream>>>(a);
+  else splitkv_combine_kernel<64, F16><<<blocks, 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -6,7 +6,7 @@
 namespace fa {
 
 hipError_t launch_fwd_bf16_paged(const FwdLaunch& L, hipStream_t stream) {
-  return launch_impl<true>(L, stream);
+  return launch_impl<true, false>(L, stream);
 }
 
 }  // namespace fa

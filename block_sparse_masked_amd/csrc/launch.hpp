@@ -56,10 +56,12 @@ struct FwdLaunch {
   // sv[0] the page strides; page_table int32 [B][pt_stride]
   const int* page_table = nullptr;
   int page_size = 0, pt_stride = 0, num_pages = 0;
+  bool f16 = false;  // 16-bit forward: fp16 inputs (else bf16)
 };
 
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream);
 hipError_t launch_fwd_bf16_paged(const FwdLaunch& L, hipStream_t stream);  // L.page_table set
+hipError_t launch_fwd_f16(const FwdLaunch& L, hipStream_t stream);  // L.f16 set
 int fwd_bf16_lds_bytes(int D, int NKB, bool paged);  // LDS of the bf16 forward
 constexpr int kMaxLdsBytes = 160 * 1024;
 constexpr long long kMaxBf16RowStride = 1ll << 22;  // k/v row stride limit of the bf16 forward

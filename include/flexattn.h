@@ -101,7 +101,7 @@ typedef struct {
   const float* alibi_slopes;  /* ALIBI kinds: device float [Hq], or NULL   */
 } flexattn_score_params;
 
-typedef enum { FLEXATTN_F32 = 0, FLEXATTN_BF16 = 1 } flexattn_dtype;
+typedef enum { FLEXATTN_F32 = 0, FLEXATTN_BF16 = 1, FLEXATTN_F16 = 2 } flexattn_dtype;
 
 /*
  * A 4-D attention tensor [B][H][L][D] in device memory. stride[] are element
@@ -210,18 +210,19 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
  * tiles, computes s = scale * q.k, applies the score_mod, applies the
  * mask_mod on partial tiles only, and accumulates the softmax-weighted sum of
  * V online, never materialising the score matrix.
- *   q     [B][Hq][Q_LEN][D]; k, v [B][Hkv][KV_LEN][D]; same dtype (F32 or
- *         BF16); D in {64, 128}; Hq a multiple of Hkv; query head h reads KV
+ *   q     [B][Hq][Q_LEN][D]; k, v [B][Hkv][KV_LEN][D]; same dtype (F32,
+ *         BF16 or F16); D in {64, 128}; Hq a multiple of Hkv; query head h reads KV
  *         head h / (Hq / Hkv).
  *   bm    a BlockMask with bm->Q_LEN == Q_LEN, bm->KV_LEN == KV_LEN,
  *         bm->B in {1, B}, bm->H in {1, Hq}, BLOCK_SIZE 128.
  *   out   [B][Hq][Q_LEN][D], same dtype as q (written).
  *   lse   device float [B][Hq][Q_LEN], contiguous (written): natural-log
  *         log-sum-exp of the modified, masked scores of each row.
- * A row with no allowed key gets out = 0 and lse = -inf. bf16 inputs are
- * contracted on bf16 MFMA with fp32 accumulation (softmax probabilities are
- * rounded to bf16 for the P.V product); fp32 inputs are computed in fp32
- * throughout. BF16 limits (FLEXATTN_ERR_UNSUPPORTED beyond them): k and v
+ * A row with no allowed key gets out = 0 and lse = -inf. bf16 (fp16) inputs
+ * are contracted on bf16 (fp16) MFMA with fp32 accumulation (softmax
+ * probabilities are rounded to the input type for the P.V product); fp32
+ * inputs are computed in fp32 throughout. BF16 / F16 limits
+ * (FLEXATTN_ERR_UNSUPPORTED beyond them): k and v
  * row strides (stride[2]) at most 2^22 elements, and the per-row tile list
  * (num_kv_blocks ints) must fit in LDS beside the K/V staging buffers.
  * Work split (bf16): one query head per workgroup by default; the
@@ -245,8 +246,8 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
  * `workspace`, and a combine pass merges them (LSE = ln sum exp LSE_s,
  * O = sum exp(LSE_s - LSE) O_s), which is the online softmax's rescaling
  * applied across slices. Same method and outputs as flexattn_fwd (section
- * "Details" of page "tensorplay.nn.attention API", items 1 and 2), bf16 only
- * (UNSUPPORTED otherwise), 1 <= num_splits <= 256; num_splits = 1 is
+ * "Details" of page "tensorplay.nn.attention API", items 1 and 2), bf16 and
+ * fp16 (UNSUPPORTED for fp32), 1 <= num_splits <= 256; num_splits = 1 is
  * flexattn_fwd. workspace: device memory of at least
  * flexattn_fwd_splitkv_workspace_bytes(B, Hq, Q_LEN, D, num_splits) bytes,
  * 16-byte aligned, caller-allocated and overwritten. Asynchronous on

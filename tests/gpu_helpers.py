@@ -15,7 +15,7 @@ F32_ATOL = 1e-5         # max |O_gpu - O_ref| and |LSE_gpu - LSE_ref| for fp32 i
 
 def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    t = t.to(torch.bfloat16) if dtype == "bf16" else t
+    t = {"bf16": t.to(torch.bfloat16), "f16": t.to(torch.float16)}.get(dtype, t)
     return t.to(device)
 
 
@@ -46,10 +46,10 @@ def oracle_rows(w: W.Workload, inputs: W.Inputs, batches=None, heads=None, rows=
                             batches=batches, heads=heads, rows=rows)
 
 
-def bf16_ulp(x: np.ndarray) -> np.ndarray:
-    """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
+def bf16_ulp(x: np.ndarray, bits: int = 8) -> np.ndarray:
+    """Spacing of bfloat16 numbers at |x| (8 significant bits; 11 for fp16)."""
     ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
-    return np.exp2(np.floor(np.log2(ax)) - 7)
+    return np.exp2(np.floor(np.log2(ax)) - (bits - 1))
 
 
 def compare(w: W.Workload, o_gpu, lse_gpu, o_ref, lse_ref, where=None):
@@ -78,7 +78,8 @@ def compare(w: W.Workload, o_gpu, lse_gpu, o_ref, lse_ref, where=None):
         res["ok"] = (res["finite"] and res["dead_ok"] and res["o_max_abs"] <= F32_ATOL
                      and res["lse_max_abs"] <= F32_ATOL)
     else:
-        slack = BF16_O_ATOL + 0.5 * bf16_ulp(orf[live])
+        # bf16 and fp16 share the bound; the output rounding is the dtype's
+        slack = BF16_O_ATOL + 0.5 * bf16_ulp(orf[live], 11 if w.dtype == "f16" else 8)
         res["o_ulp_ok"] = bool(np.all(do <= slack))
         res["o_strict_ok"] = res["o_max_abs"] <= BF16_O_ATOL
         res["ok"] = (res["finite"] and res["dead_ok"] and res["o_ulp_ok"]

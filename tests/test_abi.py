@@ -169,7 +169,7 @@ def test_python_wrapper_maps_errors():
     with pytest.raises(ValueError, match="GPU tensor"):
         lib._tensor(q, "q")
     with pytest.raises(NotImplementedError):
-        lib._tensor(q.half(), "q")
+        lib._tensor(q.double(), "q")
 
 
 def test_library_has_no_undefined_internal_symbols():
@@ -296,6 +296,7 @@ def _fwd_paged(L, pages=True, table=4096, max_pages=2, page=128, dtype=1, splits
     (dict(max_pages=1), lib._INVALID, b"do not cover"),
     (dict(page=64), lib._UNSUPPORTED, b"multiple of 128"),
     (dict(dtype=0), lib._UNSUPPORTED, b"bf16"),
+    (dict(dtype=2), lib._UNSUPPORTED, b"bf16"),
     (dict(splits=0), lib._INVALID, b"num_splits"),
     (dict(splits=2), lib._INVALID, b"workspace"),
 ])

@@ -40,7 +40,7 @@ def check_full(lib, w, B_mask=1, H_mask=1):
     return res
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal",
                                   "prefix_lm"])
@@ -50,10 +50,11 @@ def test_fwd_tiny_grid(lib, dtype, D, mask, score, heads, monkeypatch):
     """Every dtype x head dim x mask x score kind, with GQA, 3 query tiles and a
     ragged tail (300 = 2*128 + 44). bf16 softcap cases scale the inputs by 2
     (cap 20); fp32 cases keep unit-variance inputs, where the 1e-5 bound is
-    stated, and use cap 2 so tanh is far from linear. heads="2" runs the bf16
+    stated, and use cap 2 so tanh is far from linear. fp16 runs the 16-bit
+    kernel with fp16 MFMA under the bf16 bounds. heads="2" runs the bf16
     kernel with the two query heads of a KV group in one workgroup."""
     if heads == "2":
-        if dtype == "f32":
+        if dtype != "bf16":
             pytest.skip("the head-pair workgroup is a bf16 kernel variant")
         monkeypatch.setenv("FLEXATTN_BF16_HEADS", "2")
     if dtype == "f32":
@@ -321,3 +322,42 @@ def test_fwd_short_query_per_head_mask_not_packed(lib):
         res = G.compare(w, out.float().cpu().numpy().astype(np.float64),
                         lse.cpu().numpy().astype(np.float64), o_ref, lse_ref)
         assert res["ok"], (H_mask, G.summary(res))
+
+
+@pytest.mark.parametrize("splits", [3, None])
+@pytest.mark.parametrize("mask,score", [("noop", "alibi"), ("sliding_sink", "softcap_alibi"),
+                                        ("document_causal", "none")])
+def test_fwd_f16_splitkv(lib, splits, mask, score):
+    """fp16 through the split-KV path and the combine kernel (decode-like
+    lengths, packed heads)."""
+    w = tiny("f16", 128, mask, score, B=2, Hq=8, Hkv=2, Q_LEN=16, KV_LEN=1500, window=300,
+             value_scale=2.0 if "softcap" in score else 1.0)
+    check_splits(lib, w, splits)
+
+
+def check_splits(lib, w, splits):
+    inp = W.generate(w)
+    bm = G.build_gpu_mask(lib, w, inp)
+    q, k, v = (G.to_device(x, w.dtype) for x in (inp.q, inp.k, inp.v))
+    out, lse = lib.flex_attention(q, k, v, bm, score=w.score, softcap=w.softcap, scale=w.scale,
+                                  num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = G.oracle_rows(w, inp)
+    res = G.compare(w, out.float().cpu().numpy().astype(np.float64),
+                    lse.cpu().numpy().astype(np.float64), o_ref, lse_ref)
+    assert res["ok"], G.summary(res)
+
+
+def test_fwd_f16_dense_causal_sampled(lib):
+    """The dense causal GQA workload's shapes in fp16 (B=4, Hq=16, Hkv=4,
+    4096 x 4096, D=128), sampled query rows of three heads against the
+    oracle."""
+    w = W.DENSE_CAUSAL_GQA.with_(name="dense_causal_gqa_f16", dtype="f16")
+    inp = W.generate(w)
+    bm = G.build_gpu_mask(lib, w, inp)
+    o, lse, _ = G.run_gpu(lib, w, inp, bm)
+    rows = np.r_[0:3, 1000:1003, 4093:4096]
+    for b, h in ((0, 0), (2, 9), (3, 15)):
+        o_ref, lse_ref = G.oracle_rows(w, inp, batches=[b], heads=[h], rows=rows)
+        res = G.compare(w, o, lse, o_ref, lse_ref)
+        assert res["ok"] and res["n_rows"] == len(rows), G.summary(res)

@@ -14,7 +14,9 @@ synthetic):
   q, KV heads for k and v), multiplied by ``value_scale`` (2 for the softcap
   case, 1 otherwise).
 * bf16 workloads round each float32 draw to the nearest bfloat16, ties to
-  even; the rounded values (held exactly in float32) are what both sides use.
+  even, and f16 workloads to the nearest IEEE half (NumPy's conversion, ties
+  to even); the rounded values (held exactly in float32) are what both
+  sides use.
 * The document (packed varlen) workload draws document lengths uniformly in
   ``[lo, hi]`` until the remainder fits in one document, and lays the documents
   out as contiguous runs of ids, the packed layout the L-GATr "Attention
@@ -43,7 +45,7 @@ class Workload:
     Q_LEN: int
     KV_LEN: int
     D: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     seed: int
     mask: str = "causal"
     window: int = 0
@@ -160,6 +162,8 @@ def generate(w: Workload) -> Inputs:
         q, k, v = q * s, k * s, v * s
     if w.dtype == "bf16":
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    elif w.dtype == "f16":
+        q, k, v = (x.astype(np.float16).astype(np.float32) for x in (q, k, v))
     elif w.dtype != "f32":
         raise ValueError(f"unknown dtype {w.dtype!r}")
     doc_ids = doc_lengths = None

@@ -25,7 +25,7 @@ import numpy as np
 
 import workloads as W
 
-BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 (and fp16) MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 F32_PEAK_TFLOPS = 157.3     # MI355X fp32 (vector / matrix)
 HBM_PEAK_GBS = 8000.0
 
@@ -201,6 +201,9 @@ def main(argv=None):
     ap.add_argument("--decode-steps", type=int, default=20,
                     help="after the forward, time this many split-KV forwards on the decode "
                          "workload (%s; 0 = skip)" % W.DECODE_GQA.name)
+    ap.add_argument("--f16-steps", type=int, default=20,
+                    help="after the forward, time this many forwards of the same workload with "
+                         "fp16 inputs (bf16 workloads; 0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB "
                          "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -336,6 +339,33 @@ def main(argv=None):
         bwd_ms = float(np.median([a.elapsed_time(b) for a, b in ev_b]))
         backward = {"ms_median": round(bwd_ms, 4), "calls": args.backward_steps}
 
+    # fp16 (after the timed region, not part of `value`): the same workload
+    # drawn and rounded as fp16, forward only
+    f16 = None
+    if args.f16_steps > 0 and w.dtype == "bf16":
+        w16 = w.with_(name=w.name.replace("bf16", "f16"), dtype="f16")
+        inp16 = W.generate(w16)
+        q16, k16, v16 = (torch.from_numpy(x).to(torch.float16).to(dev)
+                         for x in (inp16.q, inp16.k, inp16.v))
+        del inp16
+        out16 = torch.empty_like(q16)
+        bm16 = fa.create_block_mask(w.mask, 1, 1, w.Q_LEN, w.KV_LEN, 128, window=w.window,
+                                    num_sinks=w.sinks, doc_ids=doc, device=dev, stream=stream)
+        for _ in range(3):
+            fa.flex_attention(q16, k16, v16, bm16, score=w.score, softcap=w.softcap,
+                              scale=w.scale, out=out16, lse=lse, stream=stream)
+        ev_h = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                for _ in range(args.f16_steps)]
+        for i in range(args.f16_steps):
+            ev_h[i][0].record(stream)
+            fa.flex_attention(q16, k16, v16, bm16, score=w.score, softcap=w.softcap,
+                              scale=w.scale, out=out16, lse=lse, stream=stream)
+            ev_h[i][1].record(stream)
+        torch.cuda.synchronize()
+        f16 = {"ms_median": round(float(np.median([a.elapsed_time(b) for a, b in ev_h])), 4),
+               "calls": args.f16_steps}
+        del q16, k16, v16, out16
+
     decode = None
     if args.decode_steps > 0:
         decode = decode_leg(fa, torch, dev, stream, args.decode_steps)
@@ -405,6 +435,12 @@ def main(argv=None):
             "frac_of_peak": round(alg / t / 1e12 / BF16_PEAK_TFLOPS, 4),
             "flop_convention": "10*D per allowed (q, kv) pair and (b, h); executed 18*D"})
         rec["backward"] = backward
+    if f16 is not None:
+        t = f16["ms_median"] * 1e-3
+        f16.update({"effective_tflops": round(eff_flops / t / 1e12, 2),
+                    "frac_of_peak": round(eff_flops / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+                    "peak": BF16_PEAK_TFLOPS})
+        rec["fwd_f16"] = f16
     if decode is not None:
         rec["decode_splitkv"] = decode
     if inp.doc_lengths is not None:

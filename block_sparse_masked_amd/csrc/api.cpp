@@ -287,8 +287,10 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   if (!bm) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: bm is NULL", who);
   if (k->dtype != q->dtype || v->dtype != q->dtype || out->dtype != q->dtype)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: q, k, v and out must share one dtype", who);
-  if (q->D != 64 && q->D != 128)
-    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: head dim %d is not 64 or 128", who, q->D);
+  // head dims: 64 and 128; the 16-bit kernel also 256
+  if (q->D != 64 && q->D != 128 && !(q->D == 256 && q->dtype != FLEXATTN_F32))
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: head dim %d is not 64 or 128 (or 256 for 16-bit "
+                "inputs)", who, q->D);
   if (k->D != q->D || v->D != q->D || out->D != q->D)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: q, k, v, out head dims differ", who);
   if (out->B != q->B || (!pages && (k->B != q->B || v->B != q->B)))

@@ -137,7 +137,7 @@ struct FwdArgs {
 // phase of a fragment read touches land in distinct banks.
 template <int D>
 __device__ __forceinline__ int swz(int row, int col) {
-  if constexpr (D == 128) {
+  if constexpr (D >= 128) {
     return col ^ (row & 15);
   } else {
     return col ^ ((row >> 1) & 7);
@@ -151,7 +151,7 @@ __device__ __forceinline__ int swz(int row, int col) {
 // gives those 16 half-chunk pairs distinct banks.
 template <int D>
 __device__ __forceinline__ int swz_v(int row, int col) {
-  if constexpr (D == 128) {
+  if constexpr (D >= 128) {
     return col ^ ((row & 3) << 2);
   } else {
     return col ^ (((row >> 1) & 1) << 2);
@@ -439,8 +439,11 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
 // HEADS query heads that share one KV head (and one BlockMask row) per
 // workgroup: 4 * HEADS waves read the same K/V step blocks, so HEADS = 2
 // halves the global->LDS traffic per flop. Two waves per SIMD either way.
+// D = 256 holds 128 accumulator and 64 Q registers per lane: one workgroup
+// per CU, with the accumulators in the matrix-core registers.
 template <int D, int MASK, int SCORE, int HEADS, bool PAGED, bool F16>
-__global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * kWavesPerHead * HEADS, (D > 128) ? 1 : 2 / HEADS) void
+fwd_bf16_kernel(FwdArgs a) {
   using E = Elem<F16>;
   using G = Geom<D>;
   constexpr int WAVES = kWavesPerHead * HEADS;
@@ -456,7 +459,10 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
   __shared__ __attribute__((aligned(16))) u16 sK1[STEP_ELEMS];
   __shared__ __attribute__((aligned(16))) u16 sV0[STEP_ELEMS];
   __shared__ __attribute__((aligned(16))) u16 sV1[STEP_ELEMS];
-  __shared__ __attribute__((aligned(16))) int docbuf[(MASK == MASK_DOCUMENT) ? 2 * NK : 1];
+  // document ids are fetched 64 at a time (one wave-wide 4-byte load), so a
+  // buffer holds at least 64 even when a step has fewer keys (D = 256)
+  constexpr int DOC_STRIDE = NK > 64 ? NK : 64;
+  __shared__ __attribute__((aligned(16))) int docbuf[(MASK == MASK_DOCUMENT) ? 2 * DOC_STRIDE : 1];
   extern __shared__ __attribute__((aligned(16))) int tlist[];
 
   // dispatch order -> item; rounds of equal tile count are remapped so the
@@ -545,8 +551,8 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
         const i32x4 rsrc = make_rsrc(reinterpret_cast<unsigned long long>(doc_row + kv0),
                                      rows > 0 ? 4u * (unsigned)rows : 0u);
 #pragma unroll
-        for (int c = 0; c < NK / 64; ++c)
-          dma4(rsrc, __builtin_amdgcn_readfirstlane(lds_addr(docbuf + buf * NK + 64 * c)),
+        for (int c = 0; c < DOC_STRIDE / 64; ++c)
+          dma4(rsrc, __builtin_amdgcn_readfirstlane(lds_addr(docbuf + buf * DOC_STRIDE + 64 * c)),
                4 * ln.lane + 256 * c);
       }
     }
@@ -615,7 +621,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, 2 / HEADS) void fwd_bf1
           else vload.issue_one(vrs, v_lds[nb], i - KPW);
         };
         step<D, MASK, SCORE, M, 2 * KPW, F16>(o, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
-                                (MASK == MASK_DOCUMENT) ? docbuf + cur * NK : nullptr, a, ln, dma);
+                                (MASK == MASK_DOCUMENT) ? docbuf + cur * DOC_STRIDE : nullptr, a, ln, dma);
         kv0 = kv_nxt;
         ++g;
         wait_loads_and_sync();
@@ -726,7 +732,7 @@ hipError_t dispatch_mask(const FwdArgs& args, int mask, int score, int grid, hip
 template <int D, bool PAGED, bool F16>
 hipError_t dispatch_heads(const FwdArgs& args, int heads, int mask, int score, int grid,
                           hipStream_t stream) {
-  if constexpr (!PAGED && !F16)
+  if constexpr (!PAGED && !F16 && D <= 128)
     if (heads == 2) return dispatch_mask<D, 2, false, false>(args, mask, score, grid, stream);
   return dispatch_mask<D, 1, PAGED, F16>(args, mask, score, grid, stream);
 }
@@ -812,7 +818,7 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
   // a BlockMask row (mask broadcast over heads, even GQA group); one head per
   // workgroup is the default, FLEXATTN_BF16_HEADS=2 selects the pairs (only
   // where they apply).
-  const bool pair_ok = !PAGED && !F16 && L.bm.Hm == 1 && a.G % 2 == 0 && a.splits == 1;
+  const bool pair_ok = !PAGED && !F16 && L.D <= 128 && L.bm.Hm == 1 && a.G % 2 == 0 && a.splits == 1;
   int heads = 1;  // measured: two 4-wave workgroups per CU beat one 8-wave one
   if (const char* env = getenv("FLEXATTN_BF16_HEADS")) {
     if (env[0] == '1') heads = 1;
@@ -839,12 +845,14 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   // the unscaled fast path takes the row max before scaling: scale must be > 0
   const int score = (L.score_kind == SCORE_NONE && !(L.scale > 0.0f)) ? SCORE_SCALED : L.score_kind;
-  hipError_t e = (L.D == 128) ? dispatch_heads<128, PAGED, F16>(a, heads, L.mask_kind, score, grid, stream)
+  hipError_t e = (L.D == 256) ? dispatch_heads<256, PAGED, F16>(a, heads, L.mask_kind, score, grid, stream)
+               : (L.D == 128) ? dispatch_heads<128, PAGED, F16>(a, heads, L.mask_kind, score, grid, stream)
                               : dispatch_heads<64, PAGED, F16>(a, heads, L.mask_kind, score, grid, stream);
   if (e != hipSuccess || a.splits == 1) return e;
   const long long rows = (long long)L.B * L.Hq * L.Q_LEN;
   const unsigned blocks = (unsigned)((rows + 3) / 4);
-  if (L.D == 128) splitkv_combine_kernel<128, F16><<<blocks, 256, 0, stream>>>(a);
+  if (L.D == 256) splitkv_combine_kernel<256, F16><<<blocks, 256, 0, stream>>>(a);
+  else if (L.D == 128) splitkv_combine_kernel<128, F16><<<blocks, 256, 0, stream>>>(a);
   else splitkv_combine_kernel<64, F16><<<blocks, 256, 0, stream>>>(a);
   return hipGetLastError();
 }

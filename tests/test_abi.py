@@ -122,6 +122,9 @@ def _fwd(L, q=None, k=None, v=None, o=None, bm=None, score=0, sp=None, scale=0.1
     (dict(k=_tensor(dtype=7)), lib._UNSUPPORTED, b"dtype"),
     (dict(q=_tensor(D=96), k=_tensor(D=96), v=_tensor(D=96), o=_tensor(D=96)),
      lib._UNSUPPORTED, b"head dim"),
+    # 256 is a 16-bit kernel head dim only
+    (dict(q=_tensor(dtype=0, D=256), k=_tensor(dtype=0, D=256), v=_tensor(dtype=0, D=256),
+          o=_tensor(dtype=0, D=256)), lib._UNSUPPORTED, b"head dim"),
     (dict(v=_tensor(D=128)), lib._INVALID, b"head dims differ"),
     (dict(k=_tensor(H=3), v=_tensor(H=3)), lib._INVALID, b"multiple"),
     (dict(k=_tensor(dtype=0)), lib._INVALID, b"one dtype"),

@@ -361,3 +361,21 @@ def test_fwd_f16_dense_causal_sampled(lib):
         o_ref, lse_ref = G.oracle_rows(w, inp, batches=[b], heads=[h], rows=rows)
         res = G.compare(w, o, lse, o_ref, lse_ref)
         assert res["ok"] and res["n_rows"] == len(rows), G.summary(res)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal",
+                                  "prefix_lm"])
+@pytest.mark.parametrize("score", ["none", "alibi", "softcap", "softcap_alibi"])
+def test_fwd_head_dim_256(lib, dtype, mask, score):
+    """Head dim 256 (16-bit kernel, 32-key steps, one workgroup per CU):
+    every mask and score kind, GQA, 3 query tiles with a ragged tail."""
+    w = tiny(dtype, 256, mask, score, value_scale=2.0 if "softcap" in score else 1.0)
+    check_full(lib, w)
+
+
+@pytest.mark.parametrize("splits", [1, 5])
+def test_fwd_head_dim_256_short_query_and_split(lib, splits):
+    w = tiny("bf16", 256, "sliding_sink", "softcap_alibi", B=2, Hq=8, Hkv=2, Q_LEN=16,
+             KV_LEN=1200, window=500, value_scale=2.0)
+    check_splits(lib, w, splits)

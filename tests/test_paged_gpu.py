@@ -30,7 +30,7 @@ def paged_inputs(w, page, seed=11):
     return inp, dev(inp.q), dev(kc), dev(vc), torch.from_numpy(table).cuda(), (kc, vc, table)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("mask,score", [("noop", "none"), ("causal", "alibi"),
                                         ("sliding_sink", "softcap"),
                                         ("document_causal", "softcap_alibi"),

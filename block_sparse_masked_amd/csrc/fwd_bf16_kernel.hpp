@@ -748,20 +748,38 @@ __global__ __launch_bounds__(256) void splitkv_combine_kernel(FwdArgs a) {
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
+  // slices are read in batches of 8 (indices clamped to the last slice, the
+  // extra ones weighted 0) so the batch's loads are in flight together
+  constexpr int BATCH = 8;
   float m = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) m = fmaxf(m, a.part_lse[s * rows + row]);
+  for (int s0 = 0; s0 < a.splits; s0 += BATCH) {
+    float ls[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) ls[u] = a.part_lse[min(s0 + u, a.splits - 1) * rows + row];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) m = fmaxf(m, ls[u]);
+  }
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
   float wsum = 0.0f;
   if (m != -INFINITY) {
-    for (int s = 0; s < a.splits; ++s) {
-      const float ls = a.part_lse[s * rows + row];
-      const float w = ls == -INFINITY ? 0.0f : fast_exp2((ls - m) * kLog2e);
-      wsum += w;
-      const float* src = a.part_o + (s * rows + row) * D + lane * PER;
+    for (int s0 = 0; s0 < a.splits; s0 += BATCH) {
+      float ls[BATCH], ov[BATCH][PER];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, src[i], acc[i]);
+      for (int u = 0; u < BATCH; ++u) {
+        const long long srow = (long long)min(s0 + u, a.splits - 1) * rows + row;
+        ls[u] = a.part_lse[srow];
+        __builtin_memcpy(ov[u], a.part_o + srow * D + lane * PER, PER * 4);
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const float w = (s0 + u >= a.splits || ls[u] == -INFINITY)
+                            ? 0.0f : fast_exp2((ls[u] - m) * kLog2e);
+        wsum += w;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, ov[u][i], acc[i]);
+      }
     }
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;

@@ -29,7 +29,10 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libflexattn.so")
 
-MASK_KINDS = {"noop": 0, "causal": 1, "sliding_sink": 2, "document_causal": 3, "prefix_lm": 4}
+MASK_KINDS = {"noop": 0, "causal": 1, "sliding_sink": 2, "document_causal": 3, "prefix_lm": 4,
+              "composite": 5}
+# primitives of a composite mask's terms (and_masks inside, or_masks across terms)
+MASK_PRIMS = {"causal": 1, "window": 2, "sink": 4, "prefix": 8, "document": 16}
 SCORE_KINDS = {"none": 0, "alibi": 1, "softcap": 2, "softcap_alibi": 3}
 _F32, _BF16, _F16 = 0, 1, 2
 _OK, _INVALID, _UNSUPPORTED, _HIP = 0, 1, 2, 3
@@ -42,7 +45,8 @@ class FlexAttnError(RuntimeError):
 class _MaskParams(ctypes.Structure):
     _fields_ = [("window", ctypes.c_int32), ("num_sinks", ctypes.c_int32),
                 ("doc_ids", ctypes.c_void_p), ("doc_batch", ctypes.c_int32),
-                ("doc_len", ctypes.c_int32), ("prefix_len", ctypes.c_int32)]
+                ("doc_len", ctypes.c_int32), ("prefix_len", ctypes.c_int32),
+                ("num_terms", ctypes.c_int32), ("terms", ctypes.c_int32 * 4)]
 
 
 class _ScoreParams(ctypes.Structure):
@@ -205,13 +209,34 @@ class BlockMask:
         return 100.0 * (1.0 - nonempty / total)
 
 
+def _mask_params(kind, window, num_sinks, prefix_len, terms) -> _MaskParams:
+    mp = _MaskParams(window, num_sinks, None, 0, 0, prefix_len)
+    if kind == "composite":
+        if not terms or len(terms) > 4:
+            raise ValueError("a composite mask needs 1 to 4 terms")
+        mp.num_terms = len(terms)
+        for i, term in enumerate(terms):
+            bits = 0
+            for name in term:
+                if name not in MASK_PRIMS:
+                    raise ValueError(f"unknown mask primitive {name!r} (one of {sorted(MASK_PRIMS)})")
+                bits |= MASK_PRIMS[name]
+            mp.terms[i] = bits
+    return mp
+
+
 def create_block_mask(kind: str, B: int, H: int, Q_LEN: int, KV_LEN: int, block: int = 128,
                       window: int = 0, num_sinks: int = 0,
                       doc_ids: Optional[torch.Tensor] = None,
                       device="cuda", stream=None, separate_full_blocks: bool = True,
-                      backward_lists: bool = False, prefix_len: int = 0) -> BlockMask:
+                      backward_lists: bool = False, prefix_len: int = 0,
+                      terms=None) -> BlockMask:
     """Build the BlockMask of a mask kind on the GPU (the library's builder
     kernels). B and H may be 1 to broadcast over batch / query heads.
+    kind="composite" takes `terms`: up to 4 iterables of primitive names
+    (MASK_PRIMS); the mask is the OR of the terms and each term the AND of
+    its primitives (an empty term allows every pair), with the primitives'
+    parameters window, num_sinks, prefix_len and doc_ids.
     separate_full_blocks=False lists every non-empty tile as partial, so the
     forward applies the mask on every tile. backward_lists=True also builds
     the per-KV-tile query lists (q_num_blocks, q_indices, full_q_*) that
@@ -229,10 +254,10 @@ def create_block_mask(kind: str, B: int, H: int, Q_LEN: int, KV_LEN: int, block:
     full_idx = torch.empty((B, H, nqb, nkb), dtype=torch.int32, device=device)
     sched = torch.empty((n_sched,), dtype=torch.int32, device=device)
     assert kv_num.numel() == n_num and kv_idx.numel() == n_idx
-    mp = _MaskParams(window, num_sinks, None, 0, 0, prefix_len)
-    if kind == "document_causal":
+    mp = _mask_params(kind, window, num_sinks, prefix_len, terms)
+    if kind == "document_causal" or (kind == "composite" and any(t & 16 for t in mp.terms)):
         if doc_ids is None:
-            raise ValueError("document_causal needs doc_ids")
+            raise ValueError(f"{kind} needs doc_ids")
         doc_ids = doc_ids.to(device=device, dtype=torch.int32)
         if doc_ids.dim() == 1:
             doc_ids = doc_ids.unsqueeze(0)
@@ -437,7 +462,7 @@ def block_mask_from_kv_blocks(kv_num_blocks: torch.Tensor, kv_indices: torch.Ten
                               kind: str = "noop", window: int = 0, num_sinks: int = 0,
                               doc_ids: Optional[torch.Tensor] = None,
                               backward_lists: bool = False, validate: bool = True,
-                              stream=None, prefix_len: int = 0) -> BlockMask:
+                              stream=None, prefix_len: int = 0, terms=None) -> BlockMask:
     """A BlockMask from caller-given tile lists (BlockMask.from_kv_blocks):
     kv_num_blocks [B, H, NQB] and kv_indices [B, H, NQB, NKB] list the
     partial tiles (evaluated with the mask `kind`; "noop" makes them dense),
@@ -474,10 +499,10 @@ def block_mask_from_kv_blocks(kv_num_blocks: torch.Tensor, kv_indices: torch.Ten
     c.full_kv_num_blocks, c.full_kv_indices = full_num.data_ptr(), full_idx.data_ptr()
     c.schedule = sched.data_ptr()
     c.mask_kind = MASK_KINDS[kind]
-    mp = _MaskParams(window, num_sinks, None, 0, 0, prefix_len)
-    if kind == "document_causal":
+    mp = _mask_params(kind, window, num_sinks, prefix_len, terms)
+    if kind == "document_causal" or (kind == "composite" and any(t & 16 for t in mp.terms)):
         if doc_ids is None:
-            raise ValueError("document_causal needs doc_ids")
+            raise ValueError(f"{kind} needs doc_ids")
         doc_ids = doc_ids.to(device=device, dtype=torch.int32)
         doc_ids = (doc_ids.unsqueeze(0) if doc_ids.dim() == 1 else doc_ids).contiguous()
         mp.doc_ids, mp.doc_batch, mp.doc_len = doc_ids.data_ptr(), doc_ids.shape[0], doc_ids.shape[1]

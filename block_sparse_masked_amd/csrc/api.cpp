@@ -44,8 +44,10 @@ flexattn_status check_mask(flexattn_mask_kind kind, const flexattn_mask_params* 
   out->doc = nullptr;
   out->doc_bstride = 0;
   out->prefix = 0;
+  out->nterms = 0;
+  for (int t = 0; t < fa::kMaxTerms; ++t) out->terms[t] = 0;
   *doc_len = 0;
-  if ((int)kind < FLEXATTN_MASK_NOOP || (int)kind > FLEXATTN_MASK_PREFIX_LM)
+  if ((int)kind < FLEXATTN_MASK_NOOP || (int)kind > FLEXATTN_MASK_COMPOSITE)
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: mask_kind %d is not one of the supported kinds", who,
                 (int)kind);
   if (kind == FLEXATTN_MASK_SLIDING_SINK) {
@@ -66,7 +68,36 @@ flexattn_status check_mask(flexattn_mask_kind kind, const flexattn_mask_params* 
                   p->prefix_len);
     out->prefix = p->prefix_len;
   }
-  if (kind == FLEXATTN_MASK_DOCUMENT_CAUSAL) {
+  bool needs_doc = kind == FLEXATTN_MASK_DOCUMENT_CAUSAL;
+  if (kind == FLEXATTN_MASK_COMPOSITE) {
+    if (!p) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: COMPOSITE needs params", who);
+    if (p->num_terms < 1 || p->num_terms > fa::kMaxTerms)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: COMPOSITE num_terms must be 1..4 (got %d)", who,
+                  p->num_terms);
+    int used = 0;
+    for (int t = 0; t < p->num_terms; ++t) {
+      if (p->terms[t] < 0 || p->terms[t] > 31)
+        return fail(FLEXATTN_ERR_INVALID_ARG, "%s: COMPOSITE term %d has bits outside 0..31", who,
+                    t);
+      used |= p->terms[t];
+      out->terms[t] = p->terms[t];
+    }
+    out->nterms = p->num_terms;
+    if ((used & FLEXATTN_PRIM_WINDOW) && p->window < 1)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: COMPOSITE window must be >= 1 (got %d)", who,
+                  p->window);
+    if ((used & FLEXATTN_PRIM_SINK) && p->num_sinks < 0)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: COMPOSITE num_sinks must be >= 0 (got %d)", who,
+                  p->num_sinks);
+    if ((used & FLEXATTN_PRIM_PREFIX) && p->prefix_len < 0)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: COMPOSITE prefix_len must be >= 0 (got %d)",
+                  who, p->prefix_len);
+    out->window = p->window;
+    out->sinks = p->num_sinks;
+    out->prefix = p->prefix_len;
+    needs_doc = (used & FLEXATTN_PRIM_DOCUMENT) != 0;
+  }
+  if (needs_doc) {
     if (!p) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: DOCUMENT_CAUSAL needs params", who);
     if (!p->doc_ids) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: doc_ids is NULL", who);
     const int need = Q_LEN > KV_LEN ? Q_LEN : KV_LEN;
@@ -350,8 +381,7 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   if ((st = check_mask(bm->mask_kind, &bm->mask_params, q->B, q->L, kv_len, &mp, &doc_len, who)) !=
       FLEXATTN_OK)
     return st;
-  if (bm->mask_kind == FLEXATTN_MASK_DOCUMENT_CAUSAL && bm->mask_params.doc_batch > 1 &&
-      bm->B != q->B)
+  if (mp.doc && bm->mask_params.doc_batch > 1 && bm->B != q->B)
     return fail(FLEXATTN_ERR_INVALID_ARG,
                 "%s: per-batch doc_ids need a BlockMask built per batch (B=%d)", who, q->B);
   // the fp32 kernel launches four workgroups per query tile
@@ -555,8 +585,7 @@ flexattn_status flexattn_bwd(const flexattn_tensor* q, const flexattn_tensor* k,
   if ((st = check_mask(bm->mask_kind, &bm->mask_params, q->B, q->L, k->L, &mp, &doc_len, who)) !=
       FLEXATTN_OK)
     return st;
-  if (bm->mask_kind == FLEXATTN_MASK_DOCUMENT_CAUSAL && bm->mask_params.doc_batch > 1 &&
-      bm->B != q->B)
+  if (mp.doc && bm->mask_params.doc_batch > 1 && bm->B != q->B)
     return fail(FLEXATTN_ERR_INVALID_ARG,
                 "%s: per-batch doc_ids need a BlockMask built per batch (B=%d)", who, q->B);
   if ((long long)q->B * q->H * bm->num_q_blocks > 0x7fffffffLL ||

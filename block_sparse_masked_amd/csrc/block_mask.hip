@@ -117,6 +117,25 @@ __device__ int run_start_of(const int* doc, int q0, int* lds) {
   return res;
 }
 
+// Run [first, last] of value doc[q] in a non-decreasing id row of n entries
+// (binary searches for the first entry >= and the first entry > the value).
+__device__ __forceinline__ void doc_run_of(const int* doc, int n, int q, int& first, int& last) {
+  const int v = doc[q];
+  int lo = 0, hi = q;  // first index with doc >= v lies in [0, q]
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (doc[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  first = lo;
+  lo = q;
+  hi = n - 1;  // last index with doc <= v lies in [q, n - 1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (doc[mid] > v) hi = mid - 1; else lo = mid;
+  }
+  last = lo;
+}
+
 // Sortedness of the document ids, in NQB chunks per document row: workgroup
 // (r, c) checks that doc row r never decreases across positions
 // [c * chunk, (c + 1) * chunk] and writes 1 (sorted) or 0 to flags[r * NQB + c].
@@ -171,7 +190,45 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
   int lo1 = 0, hi1 = -1, lo2 = 0, hi2 = -1;
   bool brute = false;
   const int* doc = nullptr;
-  if constexpr (KIND == MASK_DOCUMENT) {
+  // COMPOSITE: each term's allowed keys form one interval (its interval
+  // primitives, intersected with the query's document run when the term
+  // tests documents); the union of the terms' intervals is counted exactly
+  int clo[kMaxTerms], chi[kMaxTerms];
+  int nint = 0;
+  if constexpr (KIND == MASK_COMPOSITE) {
+    bool uses_doc = false;
+    for (int tt = 0; tt < a.mp.nterms; ++tt) uses_doc |= (a.mp.terms[tt] & PRIM_DOCUMENT) != 0;
+    int run_lo = 0, run_hi = a.KV_LEN - 1;
+    if (uses_doc) {
+      const int drow = a.mp.doc_bstride > 0 ? bm : 0;
+      doc = a.mp.doc + (long long)drow * a.mp.doc_bstride;
+      int bad = 0;
+      for (int c = t; c < a.NQB; c += kRowThreads) bad |= (a.sorted_flags[drow * a.NQB + c] == 0);
+      brute = __syncthreads_or(bad) != 0;
+      if (!brute && qvalid) doc_run_of(doc, max(a.Q_LEN, a.KV_LEN), q, run_lo, run_hi);
+    }
+    for (int tt = 0; tt < a.mp.nterms; ++tt) {
+      const int bits = a.mp.terms[tt];
+      int lo, hi;
+      term_interval(bits, q, a.mp, lo, hi);
+      if (bits & PRIM_DOCUMENT) {
+        lo = max(lo, run_lo);
+        hi = min(hi, run_hi);
+      }
+      lo = max(lo, 0);
+      hi = min(hi, a.KV_LEN - 1);
+      if (lo > hi) continue;
+      // insert in ascending order of lo
+      int i = nint++;
+      while (i > 0 && clo[i - 1] > lo) {
+        clo[i] = clo[i - 1];
+        chi[i] = chi[i - 1];
+        --i;
+      }
+      clo[i] = lo;
+      chi[i] = hi;
+    }
+  } else if constexpr (KIND == MASK_DOCUMENT) {
     const int drow = a.mp.doc_bstride > 0 ? bm : 0;
     doc = a.mp.doc + (long long)drow * a.mp.doc_bstride;
     // sorted unless a chunk flag of this document row says otherwise
@@ -211,7 +268,25 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
   __syncthreads();  // totals zeroed
 
   if (qvalid) {
-    if (KIND == MASK_DOCUMENT && brute) {
+    if (KIND == MASK_COMPOSITE && brute) {
+      // unsorted ids: evaluate every key of the row
+      const int dq = doc[q];
+      for (int j = 0; j < NKB; ++j) {
+        int cnt = 0;
+        const int c1 = min(j * kBlock + kBlock, a.KV_LEN);
+        for (int kv = j * kBlock; kv < c1; ++kv) cnt += composite_allowed(a.mp, q, kv, dq, doc[kv]);
+        if (cnt) atomicAdd(&tot[j], cnt);
+      }
+    } else if (KIND == MASK_COMPOSITE) {
+      // merge the sorted intervals into disjoint ones and count each once
+      int i = 0;
+      while (i < nint) {
+        int lo = clo[i], hi = chi[i];
+        ++i;
+        while (i < nint && clo[i] <= hi + 1) hi = max(hi, chi[i++]);
+        add_interval(tot, dif, lo, hi, 1);
+      }
+    } else if (KIND == MASK_DOCUMENT && brute) {
       // unsorted ids: compare every key <= q with this row's id
       const int dq = doc[q];
       const int e = min(q, a.KV_LEN - 1);
@@ -531,6 +606,19 @@ hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
     case MASK_PREFIX_LM:
       classify_kernel<MASK_PREFIX_LM><<<rows, kRowThreads, lds, stream>>>(a);
       break;
+    case MASK_COMPOSITE: {
+      if (L.mp.doc) {
+        const int drows = L.mp.doc_bstride > 0 ? L.Bm : 1;
+        const int n = L.Q_LEN > L.KV_LEN ? L.Q_LEN : L.KV_LEN;
+        const int chunk = (n + L.NQB - 1) / L.NQB;
+        doc_sorted_kernel<<<dim3(L.NQB, drows), 256, 0, stream>>>(L.mp.doc, L.mp.doc_bstride, n,
+                                                                 chunk, L.NQB, L.schedule);
+        hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) return e0;
+      }
+      classify_kernel<MASK_COMPOSITE><<<rows, kRowThreads, lds, stream>>>(a);
+      break;
+    }
     default: {
       // sortedness flags of each document row (1 or Bm rows) in NQB chunks
       const int drows = L.mp.doc_bstride > 0 ? L.Bm : 1;

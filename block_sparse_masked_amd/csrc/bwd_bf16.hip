@@ -147,6 +147,8 @@ __device__ __forceinline__ bool allowed_el(const MaskParams& mp, int q, int kv, 
     return kv <= q && ((q - kv) < mp.window || kv < mp.sinks);
   } else if constexpr (MASK == MASK_PREFIX_LM) {
     return kv <= q || kv < mp.prefix;
+  } else if constexpr (MASK == MASK_COMPOSITE) {
+    return composite_allowed(mp, q, kv, dq, dkv);
   } else {
     return kv <= q && dq == dkv;
   }
@@ -221,8 +223,9 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   float slope2 = 0.0f;
   if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
     slope2 = alibi_slope(a.slopes, h, a.Hq) * kLog2e;
-  const int* doc_row = (MASK == MASK_DOCUMENT) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
-  const int dq_id = (MASK == MASK_DOCUMENT) ? doc_row[qc] : 0;
+  const int* doc_row =
+      (mask_uses_doc(MASK) && a.mp.doc) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
+  const int dq_id = doc_row ? doc_row[qc] : 0;
 
   f32x16 acc[DB];
 #pragma unroll
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
         const int kl = 32 * blk + 8 * (r >> 2) + 4 * hh + (r & 3);
         float x, dm;
         logit_and_slope<MASK, SCORE, MASKED>(s[r], q, kv0 + kl, dq_id,
-                                             (MASK == MASK_DOCUMENT) ? sdoc[kl] : 0, slope2, a,
+                                             mask_uses_doc(MASK) ? sdoc[kl] : 0, slope2, a,
                                              x, dm);
         const float p = fast_exp2(x - lse2);
         if constexpr (DELTA) psum = fmaf(p, dp[r], psum);
@@ -279,9 +282,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     __syncthreads();  // the previous tile's reads are done
     stage_rows<D, 2>(sK, kbase, a.sk[2], kv0, a.KV_LEN, tid);
     stage_rows<D, 2>(sV, vbase, a.sv[2], kv0, a.KV_LEN, tid);
-    if constexpr (MASK == MASK_DOCUMENT) {
-      for (int i = tid; i < kBlock; i += kThreads)
-        sdoc[i] = (kv0 + i < a.KV_LEN) ? doc_row[kv0 + i] : -1;
+    if constexpr (mask_uses_doc(MASK)) {
+      if (doc_row)
+        for (int i = tid; i < kBlock; i += kThreads)
+          sdoc[i] = (kv0 + i < a.KV_LEN) ? doc_row[kv0 + i] : -1;
     }
     __syncthreads();
     if (full && kv0 + kBlock <= a.KV_LEN) tile(kv0, std::false_type{});
@@ -349,8 +353,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
       vf[ks] = ld_frag(vrow + 16 * ks + 8 * hh);
     }
   }
-  const int* doc_row = (MASK == MASK_DOCUMENT) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
-  const int dkv_id = (MASK == MASK_DOCUMENT) ? doc_row[kvc] : 0;
+  const int* doc_row =
+      (mask_uses_doc(MASK) && a.mp.doc) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
+  const int dkv_id = doc_row ? doc_row[kvc] : 0;
 
   f32x16 acck[DB], accv[DB];
 #pragma unroll
@@ -414,7 +419,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
       const long long lrow = ((long long)b * a.Hq + h) * a.Q_LEN + min(q0 + tid, a.Q_LEN - 1);
       pl = a.lse[lrow];
       pd = a.delta[lrow];
-      if constexpr (MASK == MASK_DOCUMENT) pdoc = doc_row[min(q0 + tid, a.Q_LEN - 1)];
+      if constexpr (mask_uses_doc(MASK))
+        if (doc_row) pdoc = doc_row[min(q0 + tid, a.Q_LEN - 1)];
     }
   };
   auto commit = [&](int q0) __attribute__((always_inline)) {
@@ -433,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
       const bool in = q0 + tid < a.Q_LEN;
       slse[tid] = in ? lse_base2(pl) : INFINITY;
       sdel[tid] = in ? pd : 0.0f;
-      if constexpr (MASK == MASK_DOCUMENT) sdoc[tid] = in ? pdoc : -2;
+      if constexpr (mask_uses_doc(MASK)) sdoc[tid] = in ? pdoc : -2;
     }
   };
 
@@ -463,7 +469,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
           const int ql = ql0 + j;
           float x, dm;
           logit_and_slope<MASK, SCORE, MASKED>(s[r], q0 + ql, kv,
-                                               (MASK == MASK_DOCUMENT) ? sdoc[ql] : 0, dkv_id,
+                                               mask_uses_doc(MASK) ? sdoc[ql] : 0, dkv_id,
                                                slope2, a, x, dm);
           const float p = fast_exp2(x - lv[j]);
           pf[r >> 3][r & 7] = (__bf16)p;
@@ -551,6 +557,7 @@ hipError_t dispatch_mask(const BwdArgs& a, int mask, int score, hipStream_t stre
     case MASK_CAUSAL: return dispatch_score<D, MASK_CAUSAL>(a, score, stream);
     case MASK_SLIDING_SINK: return dispatch_score<D, MASK_SLIDING_SINK>(a, score, stream);
     case MASK_PREFIX_LM: return dispatch_score<D, MASK_PREFIX_LM>(a, score, stream);
+    case MASK_COMPOSITE: return dispatch_score<D, MASK_COMPOSITE>(a, score, stream);
     default: return dispatch_score<D, MASK_DOCUMENT>(a, score, stream);
   }
 }

@@ -15,8 +15,22 @@ enum MaskKind : int {
   MASK_CAUSAL = 1,
   MASK_SLIDING_SINK = 2,
   MASK_DOCUMENT = 3,
-  MASK_PREFIX_LM = 4
+  MASK_PREFIX_LM = 4,
+  MASK_COMPOSITE = 5  // OR of up to 4 terms, each an AND of primitives
 };
+
+// Primitives of a composite mask term (bit set = the term requires it).
+enum MaskPrim : int {
+  PRIM_CAUSAL = 1,    // kv <= q
+  PRIM_WINDOW = 2,    // q - kv < window
+  PRIM_SINK = 4,      // kv < sinks
+  PRIM_PREFIX = 8,    // kv < prefix
+  PRIM_DOCUMENT = 16  // doc[q] == doc[kv]
+};
+constexpr int kMaxTerms = 4;
+
+// Kinds whose kernels read document ids.
+constexpr bool mask_uses_doc(int kind) { return kind == MASK_DOCUMENT || kind == MASK_COMPOSITE; }
 enum ScoreKind : int { SCORE_NONE = 0, SCORE_ALIBI = 1, SCORE_SOFTCAP = 2, SCORE_SOFTCAP_ALIBI = 3 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -30,7 +44,37 @@ struct MaskParams {
   const int* doc;
   long long doc_bstride;
   int prefix;  // PREFIX_LM: keys [0, prefix) are visible to every query
+  // COMPOSITE: allowed = OR over terms[0 .. nterms) of (AND of the term's
+  // primitives); a term with no bits allows everything
+  int nterms;
+  int terms[kMaxTerms];
 };
+
+// Keys [lo, hi] a composite term's interval primitives allow for query q
+// (the document primitive is tested separately; lo > hi when none).
+__device__ __forceinline__ void term_interval(int bits, int q, const MaskParams& p, int& lo,
+                                              int& hi) {
+  lo = 0;
+  hi = 0x7fffffff;
+  if (bits & PRIM_CAUSAL) hi = min(hi, q);
+  if (bits & PRIM_WINDOW) lo = max(lo, q - p.window + 1);
+  if (bits & PRIM_SINK) hi = min(hi, p.sinks - 1);
+  if (bits & PRIM_PREFIX) hi = min(hi, p.prefix - 1);
+}
+
+// Composite mask of one element; dq / dkv are the document ids of the query
+// and key (read only when a term has the document primitive).
+__device__ __forceinline__ bool composite_allowed(const MaskParams& p, int q, int kv, int dq,
+                                                  int dkv) {
+  bool any = false;
+  for (int t = 0; t < p.nterms; ++t) {
+    const int bits = p.terms[t];
+    int lo, hi;
+    term_interval(bits, q, p, lo, hi);
+    any = any || (kv >= lo && kv <= hi && (!(bits & PRIM_DOCUMENT) || dq == dkv));
+  }
+  return any;
+}
 
 // The BlockMask as the forward reads it.
 struct BlockMaskView {
@@ -71,6 +115,15 @@ template <>
 struct Mask<MASK_PREFIX_LM> {
   __device__ __forceinline__ static bool allowed(const MaskParams& p, const int*, int q, int kv) {
     return kv <= q || kv < p.prefix;
+  }
+};
+
+template <>
+struct Mask<MASK_COMPOSITE> {
+  // doc: this batch's document id row (nullptr when no term uses it)
+  __device__ __forceinline__ static bool allowed(const MaskParams& p, const int* doc, int q,
+                                                 int kv) {
+    return composite_allowed(p, q, kv, doc ? doc[q] : 0, doc ? doc[kv] : 0);
   }
 };
 

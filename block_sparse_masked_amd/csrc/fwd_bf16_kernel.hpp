@@ -325,6 +325,7 @@ __device__ __forceinline__ constexpr int key_off(int blk, int r) {
 // the key's id (LDS) must equal the query row's.
 struct MaskLimits {
   int hi, win_lo, sink_hi;
+  int tlo[kMaxTerms], thi[kMaxTerms];  // COMPOSITE: allowed offsets of each term
 };
 
 template <int D, int MASK>
@@ -333,9 +334,22 @@ __device__ __forceinline__ MaskLimits mask_limits(int kv0, const FwdArgs& a, con
   MaskLimits m;
   m.hi = a.KV_LEN - 1 - base;
   if constexpr (MASK == MASK_PREFIX_LM) m.hi = min(m.hi, max(ln.qc, a.mp.prefix - 1) - base);
-  else if constexpr (MASK != MASK_NOOP) m.hi = min(m.hi, ln.qc - base);
+  else if constexpr (MASK != MASK_NOOP && MASK != MASK_COMPOSITE) m.hi = min(m.hi, ln.qc - base);
   m.win_lo = ln.qc - base - a.mp.window;
   m.sink_hi = a.mp.sinks - base;
+  if constexpr (MASK == MASK_COMPOSITE) {
+#pragma unroll
+    for (int t = 0; t < kMaxTerms; ++t) {
+      int lo = 1, hi = 0;  // unused terms allow nothing
+      if (t < a.mp.nterms) {
+        term_interval(a.mp.terms[t], ln.qc, a.mp, lo, hi);
+        hi = min(hi, a.KV_LEN - 1) - base;
+        lo -= base;
+      }
+      m.tlo[t] = lo;
+      m.thi[t] = hi;
+    }
+  }
   return m;
 }
 
@@ -357,6 +371,16 @@ __device__ __forceinline__ float elem_logit(float x, int blk, int r, int kv0, co
     bool ok = c <= ml.hi;
     if constexpr (MASK == MASK_SLIDING_SINK) ok = ok && (c > ml.win_lo || c < ml.sink_hi);
     if constexpr (MASK == MASK_DOCUMENT) ok = ok && step_doc[c + 4 * ln.hh] == ln.dq;
+    if constexpr (MASK == MASK_COMPOSITE) {
+      bool any = false;
+#pragma unroll
+      for (int t = 0; t < kMaxTerms; ++t) {
+        bool in = c >= ml.tlo[t] && c <= ml.thi[t];
+        if (a.mp.terms[t] & PRIM_DOCUMENT) in = in && step_doc[c + 4 * ln.hh] == ln.dq;
+        any = any || in;
+      }
+      ok = ok && any;
+    }
     y = ok ? y : -INFINITY;
   }
   return y;
@@ -462,7 +486,7 @@ fwd_bf16_kernel(FwdArgs a) {
   // document ids are fetched 64 at a time (one wave-wide 4-byte load), so a
   // buffer holds at least 64 even when a step has fewer keys (D = 256)
   constexpr int DOC_STRIDE = NK > 64 ? NK : 64;
-  __shared__ __attribute__((aligned(16))) int docbuf[(MASK == MASK_DOCUMENT) ? 2 * DOC_STRIDE : 1];
+  __shared__ __attribute__((aligned(16))) int docbuf[mask_uses_doc(MASK) ? 2 * DOC_STRIDE : 1];
   extern __shared__ __attribute__((aligned(16))) int tlist[];
 
   // dispatch order -> item; rounds of equal tile count are remapped so the
@@ -495,8 +519,10 @@ fwd_bf16_kernel(FwdArgs a) {
   ln.q = it.qb * kBlock + (wave % wph) * 32 + ln.l32;
   const bool qvalid = ln.q < a.Q_LEN;
   ln.qc = qvalid ? ln.q : a.Q_LEN - 1;
-  const int* doc_row = (MASK == MASK_DOCUMENT) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
-  ln.dq = (MASK == MASK_DOCUMENT) ? doc_row[ln.qc] : 0;
+  // document ids (COMPOSITE: only when a term tests documents)
+  const int* doc_row =
+      (mask_uses_doc(MASK) && a.mp.doc) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
+  ln.dq = doc_row ? doc_row[ln.qc] : 0;
   ln.init_offsets();
   ln.slope2 = 0.0f;
   if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
@@ -545,8 +571,8 @@ fwd_bf16_kernel(FwdArgs a) {
   }
   // document ids of a step's keys -> docbuf (rows past KV_LEN read as 0)
   auto issue_doc = [&](int buf, int kv0) {
-    if constexpr (MASK == MASK_DOCUMENT) {
-      if (wave == 0) {
+    if constexpr (mask_uses_doc(MASK)) {
+      if (wave == 0 && doc_row) {
         const int rows = min(a.KV_LEN, a.doc_len) - kv0;
         const i32x4 rsrc = make_rsrc(reinterpret_cast<unsigned long long>(doc_row + kv0),
                                      rows > 0 ? 4u * (unsigned)rows : 0u);
@@ -621,7 +647,7 @@ fwd_bf16_kernel(FwdArgs a) {
           else vload.issue_one(vrs, v_lds[nb], i - KPW);
         };
         step<D, MASK, SCORE, M, 2 * KPW, F16>(o, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
-                                (MASK == MASK_DOCUMENT) ? docbuf + cur * DOC_STRIDE : nullptr, a, ln, dma);
+                                mask_uses_doc(MASK) ? docbuf + cur * DOC_STRIDE : nullptr, a, ln, dma);
         kv0 = kv_nxt;
         ++g;
         wait_loads_and_sync();
@@ -724,6 +750,8 @@ hipError_t dispatch_mask(const FwdArgs& args, int mask, int score, int grid, hip
       return dispatch_score<D, MASK_SLIDING_SINK, HEADS, PAGED, F16>(args, score, grid, stream);
     case MASK_PREFIX_LM:
       return dispatch_score<D, MASK_PREFIX_LM, HEADS, PAGED, F16>(args, score, grid, stream);
+    case MASK_COMPOSITE:
+      return dispatch_score<D, MASK_COMPOSITE, HEADS, PAGED, F16>(args, score, grid, stream);
     default:
       return dispatch_score<D, MASK_DOCUMENT, HEADS, PAGED, F16>(args, score, grid, stream);
   }

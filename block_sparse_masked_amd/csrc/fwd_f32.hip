@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
   float slope = 0.0f;
   if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
     slope = alibi_slope(a.slopes, h, a.Hq);
-  const int* doc = (MASK == MASK_DOCUMENT) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
+  const int* doc = (mask_uses_doc(MASK) && a.mp.doc) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
 
   const float* kbase = a.k + b * a.sk0 + hk * a.sk1;
   const float* vbase = a.v + b * a.sv0 + hk * a.sv1;
@@ -222,6 +222,8 @@ hipError_t f32_dispatch_mask(const F32Args& args, int mask, int score, int grid,
       return f32_dispatch_score<D, MASK_SLIDING_SINK>(args, score, grid, stream);
     case MASK_PREFIX_LM:
       return f32_dispatch_score<D, MASK_PREFIX_LM>(args, score, grid, stream);
+    case MASK_COMPOSITE:
+      return f32_dispatch_score<D, MASK_COMPOSITE>(args, score, grid, stream);
     default:
       return f32_dispatch_score<D, MASK_DOCUMENT>(args, score, grid, stream);
   }

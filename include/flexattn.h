@@ -57,14 +57,34 @@ typedef enum {
  *   PREFIX_LM        kv_idx < prefix_len OR kv_idx <= q_idx: every query sees
  *                    the whole prefix, causal after it (PrefixLM, named on
  *                    the same page and section).
+ *   COMPOSITE        runtime composition (page "tensorplay.nn.attention API":
+ *                    or_masks is the union, and_masks the intersection of
+ *                    mask_mods): the OR of num_terms (1..4) terms, each the
+ *                    AND of the primitives its bit set selects:
+ *                      FLEXATTN_PRIM_CAUSAL    kv_idx <= q_idx
+ *                      FLEXATTN_PRIM_WINDOW    q_idx - kv_idx < window
+ *                      FLEXATTN_PRIM_SINK      kv_idx < num_sinks
+ *                      FLEXATTN_PRIM_PREFIX    kv_idx < prefix_len
+ *                      FLEXATTN_PRIM_DOCUMENT  doc[q_idx] == doc[kv_idx]
+ *                    A term with no bits is noop_mask (every pair). The
+ *                    primitives share the parameters below.
  */
 typedef enum {
   FLEXATTN_MASK_NOOP = 0,
   FLEXATTN_MASK_CAUSAL = 1,
   FLEXATTN_MASK_SLIDING_SINK = 2,
   FLEXATTN_MASK_DOCUMENT_CAUSAL = 3,
-  FLEXATTN_MASK_PREFIX_LM = 4
+  FLEXATTN_MASK_PREFIX_LM = 4,
+  FLEXATTN_MASK_COMPOSITE = 5
 } flexattn_mask_kind;
+
+enum {
+  FLEXATTN_PRIM_CAUSAL = 1,
+  FLEXATTN_PRIM_WINDOW = 2,
+  FLEXATTN_PRIM_SINK = 4,
+  FLEXATTN_PRIM_PREFIX = 8,
+  FLEXATTN_PRIM_DOCUMENT = 16
+};
 
 typedef struct {
   int32_t window;          /* SLIDING_SINK: >= 1                                  */
@@ -74,6 +94,11 @@ typedef struct {
   int32_t doc_batch;       /* DOCUMENT_CAUSAL: 1 (shared by all batches) or B     */
   int32_t doc_len;         /* DOCUMENT_CAUSAL: >= max(Q_LEN, KV_LEN)              */
   int32_t prefix_len;      /* PREFIX_LM: >= 0                                     */
+  int32_t num_terms;       /* COMPOSITE: 1..4                                     */
+  int32_t terms[4];        /* COMPOSITE: FLEXATTN_PRIM_* bit set of each term;
+                              a primitive used by a term needs its parameter
+                              (window >= 1, num_sinks >= 0, prefix_len >= 0,
+                              doc_ids as for DOCUMENT_CAUSAL)               */
 } flexattn_mask_params;
 
 /*

@@ -16,6 +16,9 @@ from .reference import (  # noqa: F401
     create_mask,
     document_causal_mask,
     from_kv_blocks_mask,
+    composite_mask,
+    prefix_mask,
+    document_mask,
     gather_paged,
     noop_mask,
     or_masks,
@@ -36,7 +39,8 @@ from .backward import (  # noqa: F401
 )
 
 
-def mask_mod_for(kind: str, window: int = 0, sinks: int = 0, doc_ids=None, prefix: int = 0):
+def mask_mod_for(kind: str, window: int = 0, sinks: int = 0, doc_ids=None, prefix: int = 0,
+                 terms=None):
     """The oracle mask_mod for a mask kind name."""
     if kind == "noop":
         return noop_mask
@@ -50,6 +54,8 @@ def mask_mod_for(kind: str, window: int = 0, sinks: int = 0, doc_ids=None, prefi
         return document_causal_mask(doc_ids)
     if kind == "prefix_lm":
         return prefix_lm_mask(prefix)
+    if kind == "composite":
+        return composite_mask(terms, window, sinks, prefix, doc_ids)
     raise ValueError(f"unknown mask kind {kind!r}")
 
 
@@ -70,6 +76,6 @@ def score_mod_for(kind: str, num_heads: int, softcap: float = 0.0, slopes=None):
 
 def for_workload(w, inputs):
     """(mask_mod, score_mod) of a ``workloads.Workload`` and its inputs."""
-    mask = mask_mod_for(w.mask, w.window, w.sinks, inputs.doc_ids, w.prefix)
+    mask = mask_mod_for(w.mask, w.window, w.sinks, inputs.doc_ids, w.prefix, w.terms)
     score = score_mod_for(w.score, w.Hq, w.softcap)
     return mask, score

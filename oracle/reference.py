@@ -115,6 +115,38 @@ def prefix_lm_mask(prefix_len: int) -> MaskMod:
     return or_masks(in_prefix, causal_mask)
 
 
+def prefix_mask(prefix_len: int) -> MaskMod:
+    """The first ``prefix_len`` keys, whatever the query."""
+    prefix_len = int(prefix_len)
+
+    def mod(b, h, q_idx, kv_idx):
+        return kv_idx < prefix_len
+    return mod
+
+
+def document_mask(doc_ids: np.ndarray) -> MaskMod:
+    """Pairs whose positions carry the same document id (``doc_ids`` ``[L]``
+    or ``[B, L]``, indexed by q_idx and kv_idx), in either direction."""
+    doc = np.asarray(doc_ids)
+
+    def mod(b, h, q_idx, kv_idx):
+        d = doc if doc.ndim == 1 else doc[b]
+        return d[q_idx] == d[kv_idx]
+    return mod
+
+
+def composite_mask(terms, window: int = 0, num_sinks: int = 0, prefix_len: int = 0,
+                   doc_ids=None) -> MaskMod:
+    """Runtime composition (page "tensorplay.nn.attention API": or_masks is
+    the union and and_masks the intersection of mask_mods): or_masks over the
+    terms of and_masks over each term's primitives, named "causal",
+    "window", "sink", "prefix", "document"; an empty term is noop_mask."""
+    prims = {"causal": lambda: causal_mask, "window": lambda: window_mask(window),
+             "sink": lambda: sink_mask(num_sinks), "prefix": lambda: prefix_mask(prefix_len),
+             "document": lambda: document_mask(doc_ids)}
+    return or_masks(*[and_masks(*[prims[name]() for name in term]) for term in terms])
+
+
 def document_causal_mask(doc_ids: np.ndarray) -> MaskMod:
     """Block-diagonal causal mask over packed documents.
 

@@ -20,13 +20,14 @@ def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
 
 
 def build_gpu_mask(lib, w: W.Workload, inputs: W.Inputs, B_mask=1, H_mask=1,
-                   separate_full_blocks=True):
+                   separate_full_blocks=True, backward_lists=False):
     doc = None
-    if w.mask == "document_causal":
+    if inputs.doc_ids is not None:
         doc = torch.from_numpy(inputs.doc_ids.astype(np.int32))
     return lib.create_block_mask(w.mask, B_mask, H_mask, w.Q_LEN, w.KV_LEN, 128,
                                  window=w.window, num_sinks=w.sinks, doc_ids=doc,
-                                 separate_full_blocks=separate_full_blocks, prefix_len=w.prefix)
+                                 separate_full_blocks=separate_full_blocks, prefix_len=w.prefix,
+                                 terms=w.terms, backward_lists=backward_lists)
 
 
 def run_gpu(lib, w: W.Workload, inputs: W.Inputs, bm=None):

@@ -307,3 +307,32 @@ def test_fwd_paged_rejects_bad_arguments(L, case, expect, msg):
     # the BlockMask is for KV_LEN 256: two pages of 128 keys cover it
     assert _fwd_paged(L, **case) == expect
     assert msg in L.flexattn_last_error()
+
+
+def _composite_params(terms, window=0, sinks=0, prefix=0, doc=None, doc_len=0):
+    mp = lib._MaskParams(window, sinks, doc, 1 if doc else 0, doc_len, prefix)
+    mp.num_terms = len(terms)
+    for i, t in enumerate(terms):
+        mp.terms[i] = t
+    return mp
+
+
+def test_create_composite_rejects_bad_arguments(L):
+    """COMPOSITE: 1..4 terms of 5-bit primitive sets, each used primitive's
+    parameter present (all checked before any launch)."""
+    assert _create(L, 5, None) == lib._INVALID
+    assert _create(L, 5, _composite_params([])) == lib._INVALID
+    assert b"num_terms" in L.flexattn_last_error()
+    mp = _composite_params([1, 1, 1, 1])
+    mp.num_terms = 5
+    assert _create(L, 5, mp) == lib._INVALID
+    assert _create(L, 5, _composite_params([32])) == lib._INVALID
+    assert b"bits" in L.flexattn_last_error()
+    assert _create(L, 5, _composite_params([2], window=0)) == lib._INVALID
+    assert b"window" in L.flexattn_last_error()
+    assert _create(L, 5, _composite_params([4], sinks=-1)) == lib._INVALID
+    assert _create(L, 5, _composite_params([8], prefix=-1)) == lib._INVALID
+    assert _create(L, 5, _composite_params([16])) == lib._INVALID
+    assert b"doc_ids" in L.flexattn_last_error()
+    assert _create(L, 5, _composite_params([16], doc=4096, doc_len=100)) == lib._INVALID
+    assert b"doc_len" in L.flexattn_last_error()

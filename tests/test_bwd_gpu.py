@@ -47,14 +47,12 @@ def tiny(D, mask, score, B=2, Hq=4, Hkv=2, Q_LEN=300, KV_LEN=300, seed=0, **kw):
                       doc_seed=kw.get("doc_seed", 77),
                       doc_len_range=kw.get("doc_len_range", (20, 150)), score=score,
                       softcap=kw.get("softcap", 20.0), value_scale=kw.get("value_scale", 1.0),
-                      prefix=kw.get("prefix", 170))
+                      prefix=kw.get("prefix", 170), terms=kw.get("terms"))
 
 
 def mask_of(lib, w, inp, B_mask=1, H_mask=1, separate_full_blocks=True):
-    doc = torch.from_numpy(inp.doc_ids.astype(np.int32)) if w.mask == "document_causal" else None
-    return lib.create_block_mask(w.mask, B_mask, H_mask, w.Q_LEN, w.KV_LEN, 128, window=w.window,
-                                 num_sinks=w.sinks, doc_ids=doc, backward_lists=True,
-                                 separate_full_blocks=separate_full_blocks, prefix_len=w.prefix)
+    return G.build_gpu_mask(lib, w, inp, B_mask, H_mask, separate_full_blocks,
+                            backward_lists=True)
 
 
 def run_bwd(lib, w, inp, d_out, bm):

@@ -27,7 +27,8 @@ def tiny(dtype, D, mask, score, B=2, Hq=4, Hkv=2, Q_LEN=300, KV_LEN=300, seed=0,
                       window=kw.get("window", 100), sinks=kw.get("sinks", 3),
                       doc_seed=kw.get("doc_seed", 77), doc_len_range=kw.get("doc_len_range", (20, 150)),
                       score=score, softcap=kw.get("softcap", 20.0),
-                      value_scale=kw.get("value_scale", 1.0), prefix=kw.get("prefix", 170))
+                      value_scale=kw.get("value_scale", 1.0), prefix=kw.get("prefix", 170),
+                      terms=kw.get("terms"))
 
 
 def check_full(lib, w, B_mask=1, H_mask=1):

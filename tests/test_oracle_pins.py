@@ -465,3 +465,49 @@ def test_gather_paged_identity_layout():
     rng = np.random.default_rng(5)
     k = rng.standard_normal((3, 2, 256, 8))
     assert np.array_equal(oracle.gather_paged(k, np.arange(3, dtype=np.int32)[:, None], 256), k)
+
+
+def _prim_truth(name, q, kv, W_, S, P, doc):
+    """One primitive by its definition, for a single (q, kv) pair."""
+    return {"causal": kv <= q, "window": q - kv < W_, "sink": kv < S, "prefix": kv < P,
+            "document": doc[q] == doc[kv]}[name]
+
+
+@pytest.mark.parametrize("terms", [
+    [("causal", "window"), ("causal", "sink")], [("causal", "document", "window")],
+    [("prefix",), ("causal", "window")], [("document",)], [("window", "sink")], [()],
+    [("causal", "window"), ("sink",), ("prefix", "document"), ("causal", "document")]])
+def test_composite_mask_brute_force(terms):
+    """The composite oracle against a pure-Python truth table: any() over the
+    terms of all() over each term's primitives, pair by pair."""
+    L_, W_, S, P = 23, 5, 2, 4
+    doc = np.repeat(np.arange(5), [4, 6, 1, 7, 5])
+    mod = oracle.composite_mask(terms, W_, S, P, doc)
+    q = np.arange(L_)[:, None]
+    kv = np.arange(L_)[None, :]
+    got = np.broadcast_to(mod(0, 0, q, kv), (L_, L_))
+    want = np.array([[any(all(_prim_truth(n, i, j, W_, S, P, doc) for n in t) for t in terms)
+                      for j in range(L_)] for i in range(L_)])
+    assert np.array_equal(got, want)
+
+
+def test_composite_mask_reduces_to_the_fixed_kinds():
+    """Compositions that spell the fixed kinds give their element masks:
+    (causal AND window) OR (causal AND sink) is the sliding window with sinks
+    (distributivity), causal OR prefix is PrefixLM, causal AND document is the
+    causal document mask."""
+    L_ = 300
+    doc = np.repeat(np.arange(6), [40, 70, 10, 90, 50, 40])
+    q = np.arange(L_)[:, None]
+    kv = np.arange(L_)[None, :]
+    pairs = [
+        (oracle.composite_mask([("causal", "window"), ("causal", "sink")], 50, 3),
+         oracle.sliding_sink_mask(50, 3)),
+        (oracle.composite_mask([("causal",), ("prefix",)], prefix_len=70), oracle.prefix_lm_mask(70)),
+        (oracle.composite_mask([("causal", "document")], doc_ids=doc),
+         oracle.document_causal_mask(doc)),
+        (oracle.composite_mask([()]), oracle.noop_mask),
+    ]
+    for a, b in pairs:
+        assert np.array_equal(np.broadcast_to(a(0, 0, q, kv), (L_, L_)),
+                              np.broadcast_to(b(0, 0, q, kv), (L_, L_)))

@@ -30,7 +30,7 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-MASK_KINDS = ("noop", "causal", "sliding_sink", "document_causal")
+MASK_KINDS = ("noop", "causal", "sliding_sink", "document_causal", "prefix_lm", "composite")
 SCORE_KINDS = ("none", "alibi", "softcap", "softcap_alibi")
 
 
@@ -57,6 +57,7 @@ class Workload:
     value_scale: float = 1.0
     block: int = 128
     prefix: int = 0  # prefix_lm: keys [0, prefix) visible to every query
+    terms: Optional[tuple] = None  # composite: tuples of primitive names
     extra: dict = field(default_factory=dict, compare=False)
 
     @property
@@ -167,7 +168,8 @@ def generate(w: Workload) -> Inputs:
     elif w.dtype != "f32":
         raise ValueError(f"unknown dtype {w.dtype!r}")
     doc_ids = doc_lengths = None
-    if w.mask == "document_causal":
+    if w.mask == "document_causal" or (w.mask == "composite"
+                                       and any("document" in t for t in w.terms)):
         L = max(w.Q_LEN, w.KV_LEN)
         if w.doc_seed is None:
             raise ValueError("document workload needs doc_seed")

@@ -17,6 +17,7 @@ import os
 from dataclasses import dataclass
 from typing import Optional
 
+import numpy as np
 import torch
 
 __all__ = [
@@ -197,6 +198,56 @@ class BlockMask:
     @property
     def num_kv_blocks(self) -> int:
         return self.kv_indices.shape[-1]
+
+    # Inspection helpers (page "tensorplay.nn.attention API", BlockMask:
+    # to_dense, to_string, sparsity). They read the lists back to the host;
+    # nothing on the attention path uses them.
+
+    def to_dense(self) -> np.ndarray:
+        """Tile classes [B, H, NQB, NKB] on the host: 0 empty, 1 partial,
+        2 full."""
+        out = np.zeros(tuple(self.kv_indices.shape), dtype=np.int8)
+        for lists, cls in (((self.kv_num_blocks, self.kv_indices), 1),
+                           ((self.full_kv_num_blocks, self.full_kv_indices), 2)):
+            num, idx = (t.cpu().numpy() for t in lists)
+            for pos in np.ndindex(*num.shape):
+                out[pos + (idx[pos][:int(num[pos])],)] = cls
+        return out
+
+    def sparsity(self) -> float:
+        """Percentage of tiles that are not computed (empty), over all (b, h)."""
+        nonempty = int(self.kv_num_blocks.sum().item()) + int(self.full_kv_num_blocks.sum().item())
+        return 100.0 * (1.0 - nonempty / float(self.kv_indices.numel()))
+
+    def to_string(self, grid_size=(20, 20), limit: int = 4) -> str:
+        """A character picture of the tile grid of the first `limit` (b, h)
+        rows of the BlockMask: '#' full, '+' partial, '.' empty. The grid is
+        reduced to at most grid_size cells (rows, columns) by grouping
+        tiles; a cell is '#' when all its tiles are full, '.' when all are
+        empty, '+' otherwise. grid_size=-1 prints every tile."""
+        dense = self.to_dense()
+        B, H, nqb, nkb = dense.shape
+        if grid_size == -1:
+            gr, gc = nqb, nkb
+        else:
+            gr, gc = (grid_size, grid_size) if isinstance(grid_size, int) else grid_size
+            gr, gc = min(gr, nqb), min(gc, nkb)
+        rows = np.array_split(np.arange(nqb), gr)
+        cols = np.array_split(np.arange(nkb), gc)
+        out = [f"BlockMask(B={self.B}, H={self.H}, Q_LEN={self.Q_LEN}, KV_LEN={self.KV_LEN}, "
+               f"BLOCK_SIZE={self.BLOCK_SIZE}, kind={self.kind}, sparsity={self.sparsity():.2f}%)"]
+        for n, (b, h) in enumerate(np.ndindex(B, H)):
+            if n >= limit:
+                out.append(f"... {B * H - limit} more (b, h)")
+                break
+            out.append(f"(b={b}, h={h})")
+            for r in rows:
+                line = ""
+                for c in cols:
+                    cell = dense[b, h][np.ix_(r, c)]
+                    line += "#" if (cell == 2).all() else "." if (cell == 0).all() else "+"
+                out.append(line)
+        return "\n".join(out)
 
     def numel(self) -> int:
         """Dense element count of the mask (sparsity ignored)."""

@@ -120,6 +120,18 @@ def load_library():
     lib.flexattn_block_mask_from_kv_blocks.restype = ctypes.c_int
     lib.flexattn_block_mask_from_kv_blocks.argtypes = [ctypes.POINTER(_BlockMask), ctypes.c_void_p,
                                                        ctypes.c_void_p]
+    lib.flexattn_fwd_train.restype = ctypes.c_int
+    lib.flexattn_fwd_train.argtypes = [
+        ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+        ctypes.POINTER(_BlockMask), ctypes.c_int, ctypes.POINTER(_ScoreParams), ctypes.c_float,
+        ctypes.POINTER(_Tensor), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.flexattn_bwd_from_out.restype = ctypes.c_int
+    lib.flexattn_bwd_from_out.argtypes = [
+        ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Tensor),
+        ctypes.POINTER(_BlockMask), ctypes.c_int, ctypes.POINTER(_ScoreParams), ctypes.c_float,
+        ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+        ctypes.c_void_p, ctypes.c_void_p]
     lib.flexattn_bwd.restype = ctypes.c_int
     lib.flexattn_bwd.argtypes = [
         ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
@@ -457,15 +469,54 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask
     return out, lse
 
 
+def flex_attention_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask,
+                         score: str = "none", softcap: float = 0.0,
+                         alibi_slopes: Optional[torch.Tensor] = None,
+                         scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None,
+                         out_f32: Optional[torch.Tensor] = None, stream=None):
+    """flex_attention (16-bit inputs, no split) that also returns O in fp32
+    for flex_attention_backward(..., out_f32=...). Returns (out, lse,
+    out_f32)."""
+    lib = load_library()
+    if score not in SCORE_KINDS:
+        raise NotImplementedError(f"score kind {score!r} is not one of {sorted(SCORE_KINDS)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    out = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if out_f32 is None:
+        out_f32 = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if (out_f32.dtype != torch.float32 or not out_f32.is_contiguous()
+            or tuple(out_f32.shape) != tuple(q.shape)):
+        raise ValueError("out_f32 must be a contiguous float32 tensor shaped like q")
+    sp = _ScoreParams(float(softcap), None)
+    if alibi_slopes is not None:
+        alibi_slopes = alibi_slopes.to(device=q.device, dtype=torch.float32).contiguous()
+        sp.alibi_slopes = alibi_slopes.data_ptr()
+    tq, tk, tv, to = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v"), _tensor(out, "out")
+    st = lib.flexattn_fwd_train(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
+                                ctypes.byref(block_mask._c), SCORE_KINDS[score], ctypes.byref(sp),
+                                float(scale), ctypes.byref(to), ctypes.c_void_p(lse.data_ptr()),
+                                ctypes.c_void_p(out_f32.data_ptr()),
+                                _stream_handle(q.device, stream))
+    _check(st, "flexattn_fwd_train")
+    return out, lse, out_f32
+
+
 def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                             lse: torch.Tensor, d_out: torch.Tensor,
                             block_mask: BlockMask, score: str = "none", softcap: float = 0.0,
                             alibi_slopes: Optional[torch.Tensor] = None,
                             scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
                             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-                            workspace: Optional[torch.Tensor] = None, stream=None):
+                            workspace: Optional[torch.Tensor] = None, stream=None,
+                            out_f32: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv) of flex_attention's output for the upstream
-    gradient d_out. bf16 tensors; lse is the forward's and the BlockMask must
+    gradient d_out. With out_f32 (the fp32 O of flex_attention_train) the
+    row sums Delta = dO . O come from one pass over it instead of a
+    recompute. bf16 tensors; lse is the forward's and the BlockMask must
     carry the backward lists (create_block_mask(..., backward_lists=True)).
     dk / dv sum the query heads of each KV head."""
     lib = load_library()
@@ -490,12 +541,21 @@ def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         sp.alibi_slopes = alibi_slopes.data_ptr()
     t = {n: _tensor(x, n) for n, x in (("q", q), ("k", k), ("v", v), ("d_out", d_out),
                                        ("dq", dq), ("dk", dk), ("dv", dv))}
+    tail = (ctypes.byref(t["d_out"]), ctypes.byref(block_mask._c), SCORE_KINDS[score],
+            ctypes.byref(sp), float(scale), ctypes.byref(t["dq"]), ctypes.byref(t["dk"]),
+            ctypes.byref(t["dv"]), ctypes.c_void_p(workspace.data_ptr()),
+            _stream_handle(q.device, stream))
+    if out_f32 is not None:
+        if (out_f32.dtype != torch.float32 or not out_f32.is_contiguous()
+                or tuple(out_f32.shape) != tuple(q.shape)):
+            raise ValueError("out_f32 must be the contiguous float32 O of flex_attention_train")
+        st = lib.flexattn_bwd_from_out(ctypes.byref(t["q"]), ctypes.byref(t["k"]),
+                                       ctypes.byref(t["v"]), ctypes.c_void_p(lse.data_ptr()),
+                                       ctypes.c_void_p(out_f32.data_ptr()), *tail)
+        _check(st, "flexattn_bwd_from_out")
+        return dq, dk, dv
     st = lib.flexattn_bwd(ctypes.byref(t["q"]), ctypes.byref(t["k"]), ctypes.byref(t["v"]),
-                          ctypes.c_void_p(lse.data_ptr()),
-                          ctypes.byref(t["d_out"]), ctypes.byref(block_mask._c),
-                          SCORE_KINDS[score], ctypes.byref(sp), float(scale),
-                          ctypes.byref(t["dq"]), ctypes.byref(t["dk"]), ctypes.byref(t["dv"]),
-                          ctypes.c_void_p(workspace.data_ptr()), _stream_handle(q.device, stream))
+                          ctypes.c_void_p(lse.data_ptr()), *tail)
     _check(st, "flexattn_bwd")
     return dq, dk, dv
 

@@ -308,7 +308,7 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
                          flexattn_score_kind score_kind, const flexattn_score_params* params,
                          float scale, flexattn_tensor* out, float* lse, int splits,
                          void* workspace, size_t workspace_bytes, void* stream, const char* who,
-                         const flexattn_page_table* pages = nullptr) {
+                         const flexattn_page_table* pages = nullptr, float* out_f32 = nullptr) {
   flexattn_status st;
   if ((st = check_tensor(q, "q", who)) != FLEXATTN_OK) return st;
   if ((st = check_tensor(k, "k", who)) != FLEXATTN_OK) return st;
@@ -457,6 +457,13 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   L.bm.Hm = bm->H;
   L.bm.NQB = bm->num_q_blocks;
   L.bm.NKB = bm->num_kv_blocks;
+  if (out_f32) {
+    if (!half || splits > 1 || pages || !aligned16(out_f32))
+      return fail(FLEXATTN_ERR_INVALID_ARG,
+                  "%s: out_f32 needs a 16-bit, unsplit, contiguous-KV call and 16-byte alignment",
+                  who);
+    L.o32 = out_f32;
+  }
   if (pages) {
     L.page_table = pages->page_table;
     L.page_size = k->L;
@@ -509,6 +516,18 @@ flexattn_status flexattn_fwd_splitkv(const flexattn_tensor* q, const flexattn_te
                   workspace_bytes, stream, who);
 }
 
+flexattn_status flexattn_fwd_train(const flexattn_tensor* q, const flexattn_tensor* k,
+                                   const flexattn_tensor* v, const flexattn_block_mask* bm,
+                                   flexattn_score_kind score_kind,
+                                   const flexattn_score_params* params, float scale,
+                                   flexattn_tensor* out, float* lse, float* out_f32,
+                                   void* stream) {
+  static const char* who = "flexattn_fwd_train";
+  if (!out_f32) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: out_f32 is NULL", who);
+  return fwd_impl(q, k, v, bm, score_kind, params, scale, out, lse, 1, nullptr, 0, stream, who,
+                  nullptr, out_f32);
+}
+
 flexattn_status flexattn_fwd_paged(const flexattn_tensor* q, const flexattn_tensor* k_cache,
                                    const flexattn_tensor* v_cache,
                                    const flexattn_page_table* pages,
@@ -525,14 +544,13 @@ flexattn_status flexattn_fwd_paged(const flexattn_tensor* q, const flexattn_tens
                   workspace, workspace_bytes, stream, who, pages);
 }
 
-flexattn_status flexattn_bwd(const flexattn_tensor* q, const flexattn_tensor* k,
-                             const flexattn_tensor* v, const float* lse,
-                             const flexattn_tensor* d_out,
-                             const flexattn_block_mask* bm, flexattn_score_kind score_kind,
-                             const flexattn_score_params* params, float scale,
-                             flexattn_tensor* dq, flexattn_tensor* dk, flexattn_tensor* dv,
-                             float* workspace, void* stream) {
-  static const char* who = "flexattn_bwd";
+static flexattn_status bwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
+                                const flexattn_tensor* v, const float* lse, const float* out_f32,
+                                const flexattn_tensor* d_out, const flexattn_block_mask* bm,
+                                flexattn_score_kind score_kind,
+                                const flexattn_score_params* params, float scale,
+                                flexattn_tensor* dq, flexattn_tensor* dk, flexattn_tensor* dv,
+                                float* workspace, void* stream, const char* who) {
   flexattn_status st;
   const flexattn_tensor* all[7] = {q, k, v, d_out, dq, dk, dv};
   const char* names[7] = {"q", "k", "v", "d_out", "dq", "dk", "dv"};
@@ -612,6 +630,7 @@ flexattn_status flexattn_bwd(const flexattn_tensor* q, const flexattn_tensor* k,
   L.dout = d_out->data;
   L.lse = lse;
   L.delta = workspace;
+  L.o32 = out_f32;
   L.dq = dq->data;
   L.dk = dk->data;
   L.dv = dv->data;
@@ -653,6 +672,32 @@ flexattn_status flexattn_bwd(const flexattn_tensor* q, const flexattn_tensor* k,
   if (e != hipSuccess)
     return fail(FLEXATTN_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();
+}
+
+flexattn_status flexattn_bwd(const flexattn_tensor* q, const flexattn_tensor* k,
+                             const flexattn_tensor* v, const float* lse,
+                             const flexattn_tensor* d_out,
+                             const flexattn_block_mask* bm, flexattn_score_kind score_kind,
+                             const flexattn_score_params* params, float scale,
+                             flexattn_tensor* dq, flexattn_tensor* dk, flexattn_tensor* dv,
+                             float* workspace, void* stream) {
+  return bwd_impl(q, k, v, lse, nullptr, d_out, bm, score_kind, params, scale, dq, dk, dv,
+                  workspace, stream, "flexattn_bwd");
+}
+
+flexattn_status flexattn_bwd_from_out(const flexattn_tensor* q, const flexattn_tensor* k,
+                                      const flexattn_tensor* v, const float* lse,
+                                      const float* out_f32, const flexattn_tensor* d_out,
+                                      const flexattn_block_mask* bm,
+                                      flexattn_score_kind score_kind,
+                                      const flexattn_score_params* params, float scale,
+                                      flexattn_tensor* dq, flexattn_tensor* dk,
+                                      flexattn_tensor* dv, float* workspace, void* stream) {
+  static const char* who = "flexattn_bwd_from_out";
+  if (!out_f32 || reinterpret_cast<uintptr_t>(out_f32) % 4 != 0)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: out_f32 is NULL or not 4-byte aligned", who);
+  return bwd_impl(q, k, v, lse, out_f32, d_out, bm, score_kind, params, scale, dq, dk, dv,
+                  workspace, stream, who);
 }
 
 }  // extern "C"

@@ -60,6 +60,7 @@ struct BwdArgs {
   const u16* dout;
   const float* lse;  // [B][Hq][Q_LEN]
   float* delta;      // [B][Hq][Q_LEN]
+  const float* o32;  // fp32 O [B][Hq][Q_LEN][D] or nullptr
   u16* dq;
   u16* dk;
   u16* dv;
@@ -526,10 +527,41 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   }
 }
 
+// Delta = dO . O per query row from the forward's fp32 O (one wave per row):
+// sum_j P_ij dP_ij = dO_i . sum_j P_ij v_j = dO_i . O_i.
+template <int D>
+__global__ __launch_bounds__(256) void delta_from_out_kernel(BwdArgs a) {
+  constexpr int PER = D / 64;
+  const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int qi = (int)(row % a.Q_LEN);
+  const long long bh = row / a.Q_LEN;
+  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  const u16* g = a.dout + b * a.sdo[0] + h * a.sdo[1] + (long long)qi * a.sdo[2] + lane * PER;
+  const float* o = a.o32 + row * D + lane * PER;
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    __bf16 gv;
+    __builtin_memcpy(&gv, g + i, 2);
+    acc = fmaf((float)gv, o[i], acc);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) a.delta[row] = acc;
+}
+
 template <int D, int MASK, int SCORE>
 hipError_t launch_kernels(const BwdArgs& a, hipStream_t stream) {
   const long long nq = (long long)a.B * a.Hq * a.bm.NQB;
-  dq_kernel<D, MASK, SCORE, true><<<(unsigned)nq, kThreads, 0, stream>>>(a);
+  if (a.o32) {
+    const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
+    delta_from_out_kernel<D><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(a);
+  } else {
+    dq_kernel<D, MASK, SCORE, true><<<(unsigned)nq, kThreads, 0, stream>>>(a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dq_kernel<D, MASK, SCORE, false><<<(unsigned)nq, kThreads, 0, stream>>>(a);
@@ -572,6 +604,7 @@ hipError_t launch_bwd_bf16(const BwdLaunch& L, hipStream_t stream) {
   a.dout = static_cast<const u16*>(L.dout);
   a.lse = L.lse;
   a.delta = L.delta;
+  a.o32 = L.o32;
   a.dq = static_cast<u16*>(L.dq);
   a.dk = static_cast<u16*>(L.dk);
   a.dv = static_cast<u16*>(L.dv);

@@ -131,6 +131,9 @@ struct FwdArgs {
   // page_size is a multiple of 128, so a BlockMask tile lies in one page.
   const int* page_table;
   int page_size, pt_stride, num_pages;
+  // optional fp32 copy of O, contiguous [B][Hq][Q_LEN][D] (unsplit calls):
+  // the backward's row sums Delta = dO . O are then one pass over it
+  float* o32;
 };
 
 // 16-byte chunk swizzle of a K block [NK][D] in LDS: the 16 rows a 16-lane
@@ -689,6 +692,20 @@ fwd_bf16_kernel(FwdArgs a) {
     }
     return;
   }
+  if (qvalid && a.o32) {
+    float* orow = a.o32 + (((long long)b * a.Hq + h) * a.Q_LEN + ln.q) * D;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float4 v4;
+        v4.x = o[db][4 * gq + 0] * inv;
+        v4.y = o[db][4 * gq + 1] * inv;
+        v4.z = o[db][4 * gq + 2] * inv;
+        v4.w = o[db][4 * gq + 3] * inv;
+        *reinterpret_cast<float4*>(orow + 32 * db + 8 * gq + 4 * ln.hh) = v4;
+      }
+  }
   if (qvalid) {
     u16* orow = a.o + b * a.so0 + h * a.so1 + (long long)ln.q * a.so2;
 #pragma unroll
@@ -860,6 +877,7 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
   a.page_size = L.page_size;
   a.pt_stride = L.pt_stride;
   a.num_pages = L.num_pages;
+  a.o32 = L.o32;
   // Two query heads per workgroup are possible when they share a KV head and
   // a BlockMask row (mask broadcast over heads, even GQA group); one head per
   // workgroup is the default, FLEXATTN_BF16_HEADS=2 selects the pairs (only

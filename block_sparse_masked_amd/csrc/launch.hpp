@@ -57,6 +57,7 @@ struct FwdLaunch {
   const int* page_table = nullptr;
   int page_size = 0, pt_stride = 0, num_pages = 0;
   bool f16 = false;  // 16-bit forward: fp16 inputs (else bf16)
+  float* o32 = nullptr;  // 16-bit forward, unsplit: fp32 copy of O [B][Hq][Q_LEN][D]
 };
 
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream);
@@ -75,6 +76,7 @@ struct BwdLaunch {
   const void* dout;
   const float* lse;
   float* delta;  // workspace [B][Hq][Q_LEN]
+  const float* o32 = nullptr;  // fp32 O [B][Hq][Q_LEN][D]: Delta = dO . O (else recomputed)
   void* dq;
   void* dk;
   void* dv;

@@ -372,6 +372,34 @@ flexattn_status flexattn_bwd(const flexattn_tensor* q, const flexattn_tensor* k,
                              flexattn_tensor* dq, flexattn_tensor* dk, flexattn_tensor* dv,
                              float* workspace, void* stream);
 
+/*
+ * Training pair (the backward's row sums Delta_i = sum_j P_ij dP_ij equal
+ * dO_i . O_i, since O_i = sum_j P_ij v_j; the chain rule of the same
+ * forward as flexattn_bwd). flexattn_fwd_train is flexattn_fwd (16-bit
+ * inputs, no split, contiguous K/V) that also writes O in fp32 to out_f32,
+ * device float [B][Hq][Q_LEN][D] contiguous, 16-byte aligned, caller-
+ * allocated. flexattn_bwd_from_out is flexattn_bwd with Delta taken as
+ * dO . out_f32 in one pass over them instead of recomputing P and dP for
+ * it; out_f32 must come from flexattn_fwd_train on the same inputs (fp32
+ * O keeps Delta within the gradients' error bound, the rounded 16-bit O
+ * does not). Same errors as the calls they extend, plus INVALID_ARG for a
+ * NULL or misaligned out_f32. Asynchronous on `stream`.
+ */
+flexattn_status flexattn_fwd_train(const flexattn_tensor* q, const flexattn_tensor* k,
+                                   const flexattn_tensor* v, const flexattn_block_mask* bm,
+                                   flexattn_score_kind score_kind,
+                                   const flexattn_score_params* params, float scale,
+                                   flexattn_tensor* out, float* lse, float* out_f32,
+                                   void* stream);
+flexattn_status flexattn_bwd_from_out(const flexattn_tensor* q, const flexattn_tensor* k,
+                                      const flexattn_tensor* v, const float* lse,
+                                      const float* out_f32, const flexattn_tensor* d_out,
+                                      const flexattn_block_mask* bm,
+                                      flexattn_score_kind score_kind,
+                                      const flexattn_score_params* params, float scale,
+                                      flexattn_tensor* dq, flexattn_tensor* dk,
+                                      flexattn_tensor* dv, float* workspace, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). Host only. */
 const char* flexattn_last_error(void);
 

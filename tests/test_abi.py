@@ -336,3 +336,27 @@ def test_create_composite_rejects_bad_arguments(L):
     assert b"doc_ids" in L.flexattn_last_error()
     assert _create(L, 5, _composite_params([16], doc=4096, doc_len=100)) == lib._INVALID
     assert b"doc_len" in L.flexattn_last_error()
+
+
+def test_training_pair_rejects_bad_arguments(L):
+    q, k, v, o = _tensor(), _tensor(), _tensor(), _tensor()
+    bm = _good_bm()
+    sp = lib._ScoreParams(0.0, None)
+    assert L.flexattn_fwd_train(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(bm),
+                                0, ctypes.byref(sp), 0.125, ctypes.byref(o), ctypes.c_void_p(4096),
+                                None, None) == lib._INVALID
+    assert b"out_f32" in L.flexattn_last_error()
+    assert L.flexattn_fwd_train(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(bm),
+                                0, ctypes.byref(sp), 0.125, ctypes.byref(o), ctypes.c_void_p(4096),
+                                ctypes.c_void_p(4100), None) == lib._INVALID
+    f = [_tensor(dtype=0) for _ in range(4)]
+    assert L.flexattn_fwd_train(ctypes.byref(f[0]), ctypes.byref(f[1]), ctypes.byref(f[2]),
+                                ctypes.byref(bm), 0, ctypes.byref(sp), 0.125, ctypes.byref(f[3]),
+                                ctypes.c_void_p(4096), ctypes.c_void_p(8192), None) == lib._INVALID
+    assert b"16-bit" in L.flexattn_last_error()
+    t = [_tensor() for _ in range(7)]
+    assert L.flexattn_bwd_from_out(*(ctypes.byref(x) for x in t[:3]), ctypes.c_void_p(4096), None,
+                                   ctypes.byref(t[3]), ctypes.byref(bm), 0, ctypes.byref(sp),
+                                   0.125, *(ctypes.byref(x) for x in t[4:]),
+                                   ctypes.c_void_p(4096), None) == lib._INVALID
+    assert b"out_f32" in L.flexattn_last_error()

@@ -14,6 +14,16 @@ under 1.5% of the row RMS; the bound allows 4% of the row RMS, 2% of the
 element for the output rounding, 0.1% of the tensor RMS for rows whose
 reference is nearly zero, and 1e-5 for gradients that are exactly zero in
 the reference (a row with a single allowed key).
+
+The training pair (Delta = dO . O from the forward's fp32 O) adds one
+term. That O was formed with P rounded to bf16 for its P.V product, so
+Delta_i is off by at most 2^-9 sum_j P_ij |dP_ij| (bound used: 2^-8 times
+it, a_i), which reaches dQ_i through -scale * dmod * P_ij * k_j and dK_j
+through -scale * dmod * P_ij * q_i:
+    dQ_id += 2^-8 scale a_i sum_j P_ij |dmod_ij| |k_jd|
+    dK_jd += 2^-8 scale sum_i a_i P_ij |dmod_ij| |q_id|   (over the GQA group)
+(dV does not use Delta.) This error does not shrink with the row's
+gradient, which is why the training pair is opt-in.
 """
 import numpy as np
 import pytest
@@ -73,24 +83,53 @@ def oracle_bwd(w, inp, d_out, **sel):
     return oracle.attention_backward(inp.q, inp.k, inp.v, d_out, mask, score, grad, w.scale, **sel)
 
 
-def check(got, ref, name):
-    """Apply the bound above to the rows the reference computed; returns the
-    largest error over its bound."""
+def check(got, ref, name, extra=None):
+    """Apply the bound above (plus `extra`, elementwise) to the rows the
+    reference computed; returns the largest error over its bound."""
     rows = ~np.isnan(ref).any(axis=-1)
     g, r = got[rows], ref[rows]
+    ex = 0.0 if extra is None else extra[rows]
     assert np.all(np.isfinite(g)), f"{name}: non-finite values"
     if not r.size:
         return 0.0
     rms_all = float(np.sqrt(np.mean(r * r)))
     rms_row = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
     err = np.abs(g - r)
-    bound = BWD_ROW_RMS * rms_row + BWD_RTOL * np.abs(r) + BWD_FLOOR * rms_all + BWD_ABS
+    bound = BWD_ROW_RMS * rms_row + BWD_RTOL * np.abs(r) + BWD_FLOOR * rms_all + BWD_ABS + ex
     ratio = err / bound
     worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
     assert np.all(err <= bound), (f"{name}: err/bound {ratio[worst]:.3g} at {worst}: err "
                                   f"{err[worst]:.4g}, ref {r[worst]:.4g}, row rms "
                                   f"{float(rms_row[worst[:-1]][0]):.4g}, tensor rms {rms_all:.4g}")
     return float(ratio.max())
+
+
+def delta_rounding_terms(w, inp, d_out):
+    """The training pair's extra bound terms for dQ and dK (fp64, from the
+    oracle's probabilities; see the module docstring)."""
+    mask_mod, score_mod = oracle.for_workload(w, inp)
+    grad = oracle.score_grad_for(w.score, w.softcap)
+    _, lse = oracle.attention(inp.q, inp.k, inp.v, mask_mod, score_mod, w.scale)
+    q, k, v = (np.asarray(x, np.float64) for x in (inp.q, inp.k, inp.v))
+    g = np.asarray(d_out, np.float64)
+    ex_q = np.zeros(q.shape)
+    ex_k = np.zeros(k.shape)
+    qi = np.arange(w.Q_LEN)[:, None]
+    kj = np.arange(w.KV_LEN)[None, :]
+    for b in range(w.B):
+        for h in range(w.Hq):
+            hk = h // (w.Hq // w.Hkv)
+            s = w.scale * (q[b, h] @ k[b, hk].T)
+            sm = score_mod(s, b, h, qi, kj) if score_mod is not None else s
+            allowed = np.broadcast_to(mask_mod(b, h, qi, kj), s.shape)
+            lse_bh = np.where(np.isfinite(lse[b, h]), lse[b, h], np.inf)[:, None]
+            p = np.where(allowed, np.exp(np.where(allowed, sm, -np.inf) - lse_bh), 0.0)
+            dmod = np.abs(grad(s, b, h, qi, kj)) if grad is not None else 1.0
+            a = (p * np.abs(g[b, h] @ v[b, hk].T)).sum(axis=1)
+            c = 2.0 ** -8 * w.scale
+            ex_q[b, h] = c * a[:, None] * ((p * dmod) @ np.abs(k[b, hk]))
+            ex_k[b, hk] += c * ((p * dmod).T * a[None, :]) @ np.abs(q[b, h])
+    return ex_q, ex_k
 
 
 def full_check(lib, w, B_mask=1, H_mask=1, separate_full_blocks=True):
@@ -298,3 +337,50 @@ def test_bwd_sliding_sinks_unequal_lengths(lib, q_len, kv_len):
     w = tiny(128, "sliding_sink", "softcap_alibi", B=1, Hq=4, Hkv=1, Q_LEN=q_len, KV_LEN=kv_len,
              window=150, sinks=5, value_scale=2.0)
     full_check(lib, w)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal", "prefix_lm"])
+@pytest.mark.parametrize("score", ["none", "alibi", "softcap", "softcap_alibi"])
+def test_training_pair_fp32_out_delta(lib, D, mask, score):
+    """flex_attention_train writes the same bf16 O and LSE as flex_attention
+    plus an fp32 O; flex_attention_backward(out_f32=...) takes Delta from it
+    and meets the same gradient bound against the oracle."""
+    w = tiny(D, mask, score, value_scale=2.0 if "softcap" in score else 1.0)
+    inp = W.generate(w)
+    d_out = W.generate_upstream(w)
+    bm = mask_of(lib, w, inp)
+    q, k, v = (G.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    g = G.to_device(d_out, "bf16")
+    o1, l1 = lib.flex_attention(q, k, v, bm, score=w.score, softcap=w.softcap, scale=w.scale)
+    o2, l2, o32 = lib.flex_attention_train(q, k, v, bm, score=w.score, softcap=w.softcap,
+                                           scale=w.scale)
+    dq, dk, dv = lib.flex_attention_backward(q, k, v, l2, g, bm, score=w.score,
+                                             softcap=w.softcap, scale=w.scale, out_f32=o32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o32.to(torch.bfloat16), o2)  # the bf16 O is the fp32 O rounded
+    ref = oracle_bwd(w, inp, d_out)
+    ex_q, ex_k = delta_rounding_terms(w, inp, d_out)
+    for t, r, n, ex in zip((dq, dk, dv), ref, ("dq", "dk", "dv"), (ex_q, ex_k, None)):
+        check(t.float().cpu().numpy().astype(np.float64), r, n, ex)
+
+
+def test_training_pair_dense_causal_sampled(lib):
+    """The dense causal workload's shapes through the training pair: dQ rows
+    of two heads against the oracle."""
+    w = W.DENSE_CAUSAL_GQA
+    inp = W.generate(w)
+    d_out = W.generate_upstream(w)
+    bm = mask_of(lib, w, inp)
+    q, k, v = (G.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    g = G.to_device(d_out, "bf16")
+    _, lse, o32 = lib.flex_attention_train(q, k, v, bm, scale=w.scale)
+    dq, _, _ = lib.flex_attention_backward(q, k, v, lse, g, bm, scale=w.scale, out_f32=o32)
+    torch.cuda.synchronize()
+    rows = np.r_[0:2, 2047:2050, 4094:4096]
+    got = dq.float().cpu().numpy().astype(np.float64)
+    for b, h in ((0, 3), (3, 14)):
+        ref = oracle_bwd(w, inp, d_out, batches=[b], heads=[h], rows=rows)[0]
+        assert (~np.isnan(ref).any(axis=-1)).sum() == len(rows)
+        check(got, ref, "dq")

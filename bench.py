@@ -68,10 +68,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("fwd_bf16.hip", "fwd_bf16_kernel.hpp", "common.hpp", "fwd_common.hpp")
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per forward launch from the committed FETCH_SIZE/WRITE_SIZE
-    counter summary of this workload, or None when there is none or the
-    kernel sources changed since it was taken."""
+def measured_traffic(workload: str, field: str = "traffic_bytes_per_launch"):
+    """HBM bytes per forward launch (or another field: mfma_util_pct) from
+    the committed counter summary of this workload, or None when there is
+    none or the kernel sources changed since it was taken."""
     import hashlib
     path = os.path.join(HERE, "profiles", f"fwd_bf16_kernel.{workload}.counters.md")
     if not os.path.exists(path):
@@ -87,7 +87,7 @@ def measured_traffic(workload: str):
         if fields.get(f"source_sha256_{name}") != digest:
             return None
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        return float(fields[field]) if "." in fields[field] else int(fields[field])
     except (KeyError, ValueError):
         return None
 
@@ -437,6 +437,8 @@ def main(argv=None):
             "traffic": measured_traffic(w.name) if w.dtype == "bf16" else None,
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes": algorithmic_bytes(w, nqb, nkb),
+            "mfma_util_pct": (measured_traffic(w.name, "mfma_util_pct")
+                              if w.dtype == "bf16" else None),
         },
     }
     if ablation is not None:

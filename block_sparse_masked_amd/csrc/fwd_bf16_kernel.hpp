@@ -39,6 +39,7 @@
 
 #include <stdlib.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -728,13 +729,19 @@ fwd_bf16_kernel(FwdArgs a) {
 template <int D, int MASK, int SCORE, int HEADS, bool PAGED, bool F16>
 hipError_t launch_one(const FwdArgs& args, int grid, hipStream_t stream) {
   const int lds = 4 * ((args.bm.NKB + 3) & ~3) * (PAGED ? 2 : 1);
-  static int attr_bytes = 0;
-  if (lds > attr_bytes) {
-    hipError_t e = hipFuncSetAttribute(
+  // the dynamic-LDS limit is raised once per device and size (the attribute
+  // is per device; concurrent callers at worst set it twice)
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> attr_bytes[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= kMaxDevices || lds > attr_bytes[dev].load(std::memory_order_relaxed)) {
+    e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&fwd_bf16_kernel<D, MASK, SCORE, HEADS, PAGED, F16>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    attr_bytes = lds;
+    if (dev < kMaxDevices) attr_bytes[dev].store(lds, std::memory_order_relaxed);
   }
   fwd_bf16_kernel<D, MASK, SCORE, HEADS, PAGED, F16><<<grid, 64 * kWavesPerHead * HEADS, lds, stream>>>(args);
   return hipGetLastError();

@@ -385,7 +385,7 @@ def auto_splits(q: torch.Tensor, k: torch.Tensor, block_mask: BlockMask,
             if M <= 32 * wph and group % (4 // wph) == 0:
                 heads_per_wg = 4 // wph
                 break
-    items = B * (Hq // heads_per_wg) * block_mask.num_q_blocks
+    items = B * (Hq // heads_per_wg) * block_mask.num_q_blocks * (block_mask.BLOCK_SIZE // 128)
     if items >= target_workgroups // 2:
         return 1
     return max(1, min(block_mask.num_kv_blocks, target_workgroups // items, 64))

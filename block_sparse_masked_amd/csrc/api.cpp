@@ -35,6 +35,12 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// BLOCK_SIZE values the builder and the forwards take: multiples of the
+// kernels' 128 x 128 tile up to 512 (the backward and from_kv_blocks: 128)
+bool valid_block(int block) {
+  return block >= fa::kBlock && block <= 4 * fa::kBlock && block % fa::kBlock == 0;
+}
+
 // Validate mask kind + params; fill the kernel-side view.
 flexattn_status check_mask(flexattn_mask_kind kind, const flexattn_mask_params* p, int B_build,
                            int Q_LEN, int KV_LEN, fa::MaskParams* out, int* doc_len,
@@ -156,9 +162,9 @@ flexattn_status flexattn_block_mask_sizes(int32_t B, int32_t H, int32_t Q_LEN, i
     return fail(FLEXATTN_ERR_INVALID_ARG,
                 "flexattn_block_mask_sizes: B, H, Q_LEN, KV_LEN must be >= 1 (got %d %d %d %d)", B,
                 H, Q_LEN, KV_LEN);
-  if (block != fa::kBlock)
-    return fail(FLEXATTN_ERR_UNSUPPORTED, "flexattn_block_mask_sizes: block must be 128 (got %d)",
-                block);
+  if (!valid_block(block))
+    return fail(FLEXATTN_ERR_UNSUPPORTED,
+                "flexattn_block_mask_sizes: block must be 128, 256, 384 or 512 (got %d)", block);
   const size_t rows = (size_t)B * H * ceil_div(Q_LEN, block);
   *num_elems = rows;
   *idx_elems = rows * (size_t)ceil_div(KV_LEN, block);
@@ -176,8 +182,9 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
   if (B < 1 || H < 1 || Q_LEN < 1 || KV_LEN < 1)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: B, H, Q_LEN, KV_LEN must be >= 1 (got %d %d %d %d)",
                 who, B, H, Q_LEN, KV_LEN);
-  if (block != fa::kBlock)
-    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: block must be 128 (got %d)", who, block);
+  if (!valid_block(block))
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: block must be 128, 256, 384 or 512 (got %d)", who,
+                block);
   const int nkb = ceil_div(KV_LEN, block);
   if (nkb > fa::max_build_kv_blocks())
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: KV_LEN %d exceeds the builder limit of %d tiles",
@@ -226,6 +233,7 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
   L.full_idx = bm->full_kv_indices;
   L.schedule = bm->schedule;
   L.separate_full = separate_full_blocks != 0;
+  L.block = block;
   const bool with_q = bm->q_num_blocks && bm->q_indices && bm->full_q_num_blocks &&
                       bm->full_q_indices;
   L.q_num = with_q ? bm->q_num_blocks : nullptr;
@@ -358,15 +366,16 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   if (!(std::isfinite(scale)))
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: scale is not finite", who);
   // BlockMask consistency
-  if (bm->BLOCK_SIZE != fa::kBlock)
-    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: BlockMask BLOCK_SIZE must be 128 (got %d)", who,
+  if (!valid_block(bm->BLOCK_SIZE))
+    return fail(FLEXATTN_ERR_UNSUPPORTED,
+                "%s: BlockMask BLOCK_SIZE must be 128, 256, 384 or 512 (got %d)", who,
                 bm->BLOCK_SIZE);
+  const int BS = bm->BLOCK_SIZE;
   if (bm->Q_LEN != q->L || bm->KV_LEN != kv_len)
     return fail(FLEXATTN_ERR_INVALID_ARG,
                 "%s: BlockMask built for Q_LEN=%d KV_LEN=%d, tensors have %d and %d", who,
                 bm->Q_LEN, bm->KV_LEN, q->L, kv_len);
-  if (bm->num_q_blocks != ceil_div(q->L, fa::kBlock) ||
-      bm->num_kv_blocks != ceil_div(kv_len, fa::kBlock))
+  if (bm->num_q_blocks != ceil_div(q->L, BS) || bm->num_kv_blocks != ceil_div(kv_len, BS))
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: BlockMask tile counts do not match its lengths",
                 who);
   if (!(bm->B == 1 || bm->B == q->B) || !(bm->H == 1 || bm->H == q->H))
@@ -384,8 +393,9 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   if (mp.doc && bm->mask_params.doc_batch > 1 && bm->B != q->B)
     return fail(FLEXATTN_ERR_INVALID_ARG,
                 "%s: per-batch doc_ids need a BlockMask built per batch (B=%d)", who, q->B);
-  // the fp32 kernel launches four workgroups per query tile
-  if ((long long)q->B * q->H * bm->num_q_blocks * 4 > 0x7fffffffLL)
+  // the fp32 kernel launches BLOCK_SIZE / 32 workgroups per tile row, the
+  // 16-bit one BLOCK_SIZE / 128 per tile row and head
+  if ((long long)q->B * q->H * bm->num_q_blocks * (BS / 32) > 0x7fffffffLL)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: too many query tiles for one launch", who);
   if ((int)score_kind < FLEXATTN_SCORE_NONE || (int)score_kind > FLEXATTN_SCORE_SOFTCAP_ALIBI)
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: score_kind %d is not a supported kind", who,
@@ -401,7 +411,7 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
     slopes = params ? params->alibi_slopes : nullptr;
 
   const bool half = q->dtype == FLEXATTN_BF16 || q->dtype == FLEXATTN_F16;  // 16-bit kernel
-  if (half && fa::fwd_bf16_lds_bytes(q->D, bm->num_kv_blocks, pages != nullptr) >
+  if (half && fa::fwd_bf16_lds_bytes(q->D, bm->num_kv_blocks * (BS / fa::kBlock), pages != nullptr) >
                                         fa::kMaxLdsBytes)
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: KV_LEN %d needs more LDS than a workgroup has", who,
                 kv_len);
@@ -457,6 +467,7 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   L.bm.Hm = bm->H;
   L.bm.NQB = bm->num_q_blocks;
   L.bm.NKB = bm->num_kv_blocks;
+  L.bm.BS = BS;
   if (out_f32) {
     if (!half || splits > 1 || pages || !aligned16(out_f32))
       return fail(FLEXATTN_ERR_INVALID_ARG,

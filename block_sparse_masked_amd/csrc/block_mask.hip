@@ -33,6 +33,7 @@ struct BuildArgs {
   int doc_len;
   const int* sorted_flags;  // document kind: per-chunk sortedness (schedule buffer)
   int Bm, Hm, Q_LEN, KV_LEN, NQB, NKB;
+  int BS;  // BLOCK_SIZE: a multiple of 128 (rows are counted 128 at a time)
   int* kv_num;
   int* kv_idx;
   int* full_num;
@@ -156,18 +157,18 @@ __global__ __launch_bounds__(256) void doc_sorted_kernel(const int* doc, long lo
 // Adds the allowed count of the key interval [lo, hi] of one query row to the
 // per-tile totals: the two end tiles directly, the tiles in between (every
 // key allowed) through the difference array `dif` (prefix-summed later).
-__device__ __forceinline__ void add_interval(int* tot, int* dif, int lo, int hi, int sign) {
+__device__ __forceinline__ void add_interval(int* tot, int* dif, int lo, int hi, int sign, int bs) {
   if (hi < lo) return;
-  const int jl = lo / kBlock, jh = hi / kBlock;
+  const int jl = lo / bs, jh = hi / bs;
   if (jl == jh) {
     atomicAdd(&tot[jl], sign * (hi - lo + 1));
     return;
   }
-  atomicAdd(&tot[jl], sign * ((jl + 1) * kBlock - lo));
-  atomicAdd(&tot[jh], sign * (hi - jh * kBlock + 1));
+  atomicAdd(&tot[jl], sign * ((jl + 1) * bs - lo));
+  atomicAdd(&tot[jh], sign * (hi - jh * bs + 1));
   if (jh > jl + 1) {
-    atomicAdd(&dif[jl + 1], sign * kBlock);
-    atomicAdd(&dif[jh], -sign * kBlock);
+    atomicAdd(&dif[jl + 1], sign * bs);
+    atomicAdd(&dif[jh], -sign * bs);
   }
 }
 
@@ -179,13 +180,17 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
   const int qb = row % a.NQB;
   const int bm = row / (a.NQB * a.Hm);
   const int t = threadIdx.x;
-  const int q = qb * kBlock + t;
-  const bool qvalid = q < a.Q_LEN;
   const int NKB = a.NKB;
+  const int BS = a.BS;
   int* tot = smem;
   int* dif = smem + NKB;
   for (int j = t; j < 2 * NKB + 1; j += kRowThreads) smem[j] = 0;
 
+  // The tile row's BS query rows, 128 at a time (one per thread); each
+  // query row's allowed keys are counted into the per-tile totals.
+  for (int sb = 0; sb < BS / kBlock; ++sb) {
+  const int q = qb * BS + sb * kBlock + t;
+  const bool qvalid = q < a.Q_LEN;
   // Per-row allowed intervals: I1 = [lo1, hi1], I2 = [lo2, hi2] (may be empty).
   int lo1 = 0, hi1 = -1, lo2 = 0, hi2 = -1;
   bool brute = false;
@@ -236,7 +241,7 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
     for (int c = t; c < a.NQB; c += kRowThreads) bad |= (a.sorted_flags[drow * a.NQB + c] == 0);
     const bool sorted = __syncthreads_or(bad) == 0;
     if (sorted) {
-      const int q0 = qb * kBlock;
+      const int q0 = qb * BS + sb * kBlock;
       const int s0 = run_start_of(doc, min(q0, a.doc_len - 1), scratch);
       // run boundaries inside this tile, then the latest boundary <= q
       int bnd = (qvalid && q > q0 && doc[q] != doc[q - 1]) ? q : -1;
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
   }
   hi1 = min(hi1, a.KV_LEN - 1);
   hi2 = min(hi2, a.KV_LEN - 1);
-  __syncthreads();  // totals zeroed
+  __syncthreads();  // totals zeroed (first pass), scratch free
 
   if (qvalid) {
     if (KIND == MASK_COMPOSITE && brute) {
@@ -273,8 +278,8 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
       const int dq = doc[q];
       for (int j = 0; j < NKB; ++j) {
         int cnt = 0;
-        const int c1 = min(j * kBlock + kBlock, a.KV_LEN);
-        for (int kv = j * kBlock; kv < c1; ++kv) cnt += composite_allowed(a.mp, q, kv, dq, doc[kv]);
+        const int c1 = min(j * BS + BS, a.KV_LEN);
+        for (int kv = j * BS; kv < c1; ++kv) cnt += composite_allowed(a.mp, q, kv, dq, doc[kv]);
         if (cnt) atomicAdd(&tot[j], cnt);
       }
     } else if (KIND == MASK_COMPOSITE) {
@@ -284,28 +289,29 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
         int lo = clo[i], hi = chi[i];
         ++i;
         while (i < nint && clo[i] <= hi + 1) hi = max(hi, chi[i++]);
-        add_interval(tot, dif, lo, hi, 1);
+        add_interval(tot, dif, lo, hi, 1, BS);
       }
     } else if (KIND == MASK_DOCUMENT && brute) {
       // unsorted ids: compare every key <= q with this row's id
       const int dq = doc[q];
       const int e = min(q, a.KV_LEN - 1);
-      for (int j = 0; j * kBlock <= e; ++j) {
+      for (int j = 0; j * BS <= e; ++j) {
         int cnt = 0;
-        const int c1 = min(j * kBlock + kBlock - 1, e);
-        for (int kv = j * kBlock; kv <= c1; ++kv) cnt += (doc[kv] == dq);
+        const int c1 = min(j * BS + BS - 1, e);
+        for (int kv = j * BS; kv <= c1; ++kv) cnt += (doc[kv] == dq);
         if (cnt) atomicAdd(&tot[j], cnt);
       }
     } else {
-      add_interval(tot, dif, lo1, hi1, 1);
+      add_interval(tot, dif, lo1, hi1, 1, BS);
       if constexpr (KIND == MASK_SLIDING_SINK) {
         // |I1 u I2| = |I1| + |I2| - |I1 n I2|
-        add_interval(tot, dif, lo2, hi2, 1);
-        add_interval(tot, dif, max(lo1, lo2), min(hi1, hi2), -1);
+        add_interval(tot, dif, lo2, hi2, 1, BS);
+        add_interval(tot, dif, max(lo1, lo2), min(hi1, hi2), -1, BS);
       }
     }
   }
   __syncthreads();
+  }  // sub-blocks of the tile row
 
   // Totals (difference array prefix-summed in chunks of 128 tiles), then
   // classify and compact, keeping ascending order.
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
     int isP = 0, isF = 0;
     if (j < NKB) {
       const int cnt = tot[j] + run + incD;
-      isF = a.separate_full && (cnt == kBlock * kBlock);
+      isF = a.separate_full && (cnt == BS * BS);
       isP = (cnt > 0 && !isF);
     }
     const int incP = block_incl_scan128(isP, scratch);
@@ -591,6 +597,7 @@ hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
   a.full_num = L.full_num;
   a.full_idx = L.full_idx;
   a.separate_full = L.separate_full;
+  a.BS = L.block;
   const int rows = L.Bm * L.Hm * L.NQB;
   const size_t lds = sizeof(int) * (2 * (size_t)L.NKB + 1);
   switch (L.kind) {

@@ -84,6 +84,7 @@ struct BlockMaskView {
   const int* full_idx;  // [Bm][Hm][NQB][NKB]
   const int* schedule;  // [Bm*Hm*NQB]
   int Bm, Hm, NQB, NKB;
+  int BS = kBlock;  // BLOCK_SIZE of the lists (a multiple of kBlock)
 };
 
 // Element mask of each kind: allowed(b, q, kv) for in-range indices.

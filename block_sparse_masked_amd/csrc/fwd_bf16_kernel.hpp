@@ -501,6 +501,14 @@ fwd_bf16_kernel(FwdArgs a) {
     split = x % a.splits;
     x /= a.splits;
   }
+  // BLOCK_SIZE = mk * 128: a tile row holds mk 128-row query tiles (one item
+  // each) and a listed tile mk 128-key tiles (walked one after another)
+  const int mk = a.bm.BS / kBlock;
+  int qsub = 0;
+  if (mk > 1) {
+    qsub = x % mk;
+    x /= mk;
+  }
   if (a.xcd_round > 0) {
     const int R = a.xcd_round;
     const int r = x / R, u = x - r * R;
@@ -514,13 +522,15 @@ fwd_bf16_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = it.b, h = it.h * HPW + wave / wph;
   const int hk = (it.h * HPW) / a.G;
+  const int q_tile0 = it.qb * a.bm.BS + qsub * kBlock;
+  if (q_tile0 >= a.Q_LEN) return;  // a 128-row tile past Q_LEN (BLOCK_SIZE > 128)
   Lane<D> ln;
   ln.lane = threadIdx.x & 63;
   ln.l32 = ln.lane & 31;
   ln.hh = ln.lane >> 5;
   ln.vg = (ln.lane >> 4) & 1;
   ln.vi = ln.lane & 15;
-  ln.q = it.qb * kBlock + (wave % wph) * 32 + ln.l32;
+  ln.q = q_tile0 + (wave % wph) * 32 + ln.l32;
   const bool qvalid = ln.q < a.Q_LEN;
   ln.qc = qvalid ? ln.q : a.Q_LEN - 1;
   // document ids (COMPOSITE: only when a term tests documents)
@@ -543,7 +553,9 @@ fwd_bf16_kernel(FwdArgs a) {
   // base + kv0 * row_bytes, so the per-step address arithmetic is unchanged
   const unsigned long long kbase0 = kload.base, vbase0 = vload.base;
   auto phys_page = [&](int kv0) {
-    const int pp = a.page_table[(long long)b * a.pt_stride + kv0 / a.page_size];
+    // a key tile past KV_LEN (loads nothing) reads the last page's entry
+    const int lp = min(kv0, a.KV_LEN - 1) / a.page_size;
+    const int pp = a.page_table[(long long)b * a.pt_stride + lp];
     return min(max(pp, 0), a.num_pages - 1);
   };
   auto set_page = [&](int kv0, int pp) {
@@ -558,20 +570,28 @@ fwd_bf16_kernel(FwdArgs a) {
   // counts are clamped to the list length so a malformed BlockMask cannot
   // index past the staged list; the first entry of each list is read with
   // the counts, so the first step's loads need not wait for the staging
-  const int nfull = __builtin_amdgcn_readfirstlane(min(a.bm.full_num[it.mrow], a.bm.NKB));
-  const int n = __builtin_amdgcn_readfirstlane(min(nfull + a.bm.kv_num[it.mrow], a.bm.NKB));
+  const int nfull_c = __builtin_amdgcn_readfirstlane(min(a.bm.full_num[it.mrow], a.bm.NKB));
+  const int n_c = __builtin_amdgcn_readfirstlane(min(nfull_c + a.bm.kv_num[it.mrow], a.bm.NKB));
+  // in 128-key tiles: listed tile i covers 128-key tiles [i * mk, i * mk + mk)
+  const int nfull = nfull_c * mk, n = n_c * mk;
+  const int nlist = a.bm.NKB * mk;  // 128-key tiles the lists can name
   // this workgroup's slice [t_begin, t_end) of the item's tiles
   const int t_begin = (int)((long long)n * split / a.splits);
   const int t_end = (int)((long long)n * (split + 1) / a.splits);
-  const int first_tile = t_begin < nfull ? a.bm.full_idx[lrow + t_begin]
-                                         : a.bm.kv_idx[lrow + min(t_begin - nfull, a.bm.NKB - 1)];
+  auto listed = [&](int t) {
+    const int c = t / mk;
+    const int idx = c < nfull_c ? a.bm.full_idx[lrow + c]
+                                : a.bm.kv_idx[lrow + min(c - nfull_c, a.bm.NKB - 1)];
+    return idx * mk + (t - c * mk);
+  };
+  const int first_tile = listed(t_begin);
   // the item's tiles, full then partial, staged in LDS once (paged KV: and
-  // each tile's physical page, after the NKB-long tile list)
-  int* tpage = tlist + ((a.bm.NKB + 3) & ~3);
+  // each tile's physical page, after the tile list)
+  int* tpage = tlist + ((nlist + 3) & ~3);
   for (int t = threadIdx.x; t < n; t += THREADS) {
-    const int idx = t < nfull ? a.bm.full_idx[lrow + t] : a.bm.kv_idx[lrow + (t - nfull)];
+    const int idx = listed(t);
     tlist[t] = idx;
-    if constexpr (paged) tpage[t] = phys_page(kBlock * min(max(idx, 0), a.bm.NKB - 1));
+    if constexpr (paged) tpage[t] = phys_page(kBlock * min(max(idx, 0), nlist - 1));
   }
   // document ids of a step's keys -> docbuf (rows past KV_LEN read as 0)
   auto issue_doc = [&](int buf, int kv0) {
@@ -599,7 +619,7 @@ fwd_bf16_kernel(FwdArgs a) {
   if (t_end > t_begin) {
     // tile indices are clamped into [0, NKB): a malformed BlockMask computes
     // garbage but never reads outside the KV tensors
-    auto clamp_kv0 = [&](int idx) { return kBlock * min(max(idx, 0), a.bm.NKB - 1); };
+    auto clamp_kv0 = [&](int idx) { return kBlock * min(max(idx, 0), nlist - 1); };
     auto tile_kv0 = [&](int t) { return clamp_kv0(__builtin_amdgcn_readfirstlane(tlist[t])); };
     // prologue: step 0 -> buffer 0, Q^T fragments; then the tile list is
     // visible (barrier in wait_loads_and_sync)
@@ -728,7 +748,8 @@ fwd_bf16_kernel(FwdArgs a) {
 
 template <int D, int MASK, int SCORE, int HEADS, bool PAGED, bool F16>
 hipError_t launch_one(const FwdArgs& args, int grid, hipStream_t stream) {
-  const int lds = 4 * ((args.bm.NKB + 3) & ~3) * (PAGED ? 2 : 1);
+  const int nlist = args.bm.NKB * (args.bm.BS / kBlock);
+  const int lds = 4 * ((nlist + 3) & ~3) * (PAGED ? 2 : 1);
   // the dynamic-LDS limit is raised once per device and size (the attribute
   // is per device; concurrent callers at worst set it twice)
   constexpr int kMaxDevices = 64;
@@ -912,7 +933,7 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
   const int R = L.B * L.Hq / hpw;
   const int g_items = a.G / hpw;  // items per KV group
   a.xcd_round = (L.bm.Bm == 1 && L.bm.Hm == 1 && R % 8 == 0 && (R / 8) % g_items == 0) ? R : 0;
-  const int grid = R * L.bm.NQB * a.splits;
+  const int grid = R * L.bm.NQB * (L.bm.BS / kBlock) * a.splits;
   if (grid == 0) return hipSuccess;
   // the unscaled fast path takes the row max before scaling: scale must be > 0
   const int score = (L.score_kind == SCORE_NONE && !(L.scale > 0.0f)) ? SCORE_SCALED : L.score_kind;

@@ -19,7 +19,6 @@ namespace {
 constexpr int kTpr = 4;                        // threads per query row
 constexpr int kRowsPerWg = 32;                 // query rows per workgroup
 constexpr int kThreads = kTpr * kRowsPerWg;
-constexpr int kWgPerTile = kBlock / kRowsPerWg;
 constexpr int kChunk = 16;  // keys per online-softmax update
 constexpr int kSub = 64;    // keys staged in LDS at a time (half a tile)
 
@@ -80,10 +79,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
   float* sK = smem_f32;
   float* sV = smem_f32 + kSub * D;
 
-  const Item it = decode_item(blockIdx.x / kWgPerTile, a.bm, a.B, a.Hq);
+  // kRowsPerWg query rows per workgroup, BLOCK_SIZE / kRowsPerWg per tile row
+  const int wg_per_row = a.bm.BS / kRowsPerWg;
+  const Item it = decode_item(blockIdx.x / wg_per_row, a.bm, a.B, a.Hq);
   const int b = it.b, h = it.h, hk = h / a.G;
   const int half = threadIdx.x % kTpr;  // this thread's quarter of the head dimension
-  const int q = it.qb * kBlock + (blockIdx.x % kWgPerTile) * kRowsPerWg + threadIdx.x / kTpr;
+  const int q = it.qb * a.bm.BS + (blockIdx.x % wg_per_row) * kRowsPerWg + threadIdx.x / kTpr;
   const bool qvalid = q < a.Q_LEN;
   const int qc = qvalid ? q : a.Q_LEN - 1;
 
@@ -115,9 +116,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
   for (int t = 0; t < nfull + npart; ++t) {
     const bool partial = t >= nfull;
     const int kb = partial ? a.bm.kv_idx[lrow + (t - nfull)] : a.bm.full_idx[lrow + t];
-    const bool do_mask = partial || (kb * kBlock + kBlock > a.KV_LEN);
-   for (int sub = 0; sub < kBlock; sub += kSub) {
-    const int kv0 = kb * kBlock + sub;
+    const bool do_mask = partial || (kb * a.bm.BS + a.bm.BS > a.KV_LEN);
+   for (int sub = 0; sub < a.bm.BS; sub += kSub) {
+    const int kv0 = kb * a.bm.BS + sub;
     __syncthreads();
     load_tile_f32<D>(sK, kbase, a.sk2, kv0, a.KV_LEN);
     load_tile_f32<D>(sV, vbase, a.sv2, kv0, a.KV_LEN);
@@ -252,7 +253,7 @@ hipError_t launch_fwd_f32(const FwdLaunch& L, hipStream_t stream) {
   a.softcap = L.softcap;
   a.slopes = L.slopes;
   a.bm = L.bm;
-  const int grid = L.B * L.Hq * L.bm.NQB * kWgPerTile;
+  const int grid = L.B * L.Hq * L.bm.NQB * (L.bm.BS / kRowsPerWg);
   if (grid == 0) return hipSuccess;
   if (L.D == 128) return f32_dispatch_mask<128>(a, L.mask_kind, L.score_kind, grid, stream);
   return f32_dispatch_mask<64>(a, L.mask_kind, L.score_kind, grid, stream);

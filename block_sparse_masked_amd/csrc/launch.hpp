@@ -14,6 +14,7 @@ struct BuildLaunch {
   MaskParams mp;
   int doc_len;
   int Bm, Hm, Q_LEN, KV_LEN, NQB, NKB;
+  int block = 128;  // BLOCK_SIZE (a multiple of 128)
   int* kv_num;
   int* kv_idx;
   int* full_num;

@@ -48,6 +48,11 @@ def test_block_mask_sizes(L):
     assert lib.block_mask_sizes(1, 1, 300, 129) == (3, 3 * 2, 3)
     with pytest.raises(NotImplementedError, match="block must be 128"):
         lib.block_mask_sizes(1, 1, 256, 256, 64)
+    # multiples of 128 up to 512
+    assert lib.block_mask_sizes(2, 3, 1000, 700, 256) == (2 * 3 * 4, 2 * 3 * 4 * 3, 2 * 3 * 4)
+    for bad in (192, 640):
+        with pytest.raises(NotImplementedError, match="block must be 128"):
+            lib.block_mask_sizes(1, 1, 256, 256, bad)
     with pytest.raises(ValueError, match="must be >= 1"):
         lib.block_mask_sizes(0, 1, 256, 256)
 
@@ -360,3 +365,8 @@ def test_training_pair_rejects_bad_arguments(L):
                                    0.125, *(ctypes.byref(x) for x in t[4:]),
                                    ctypes.c_void_p(4096), None) == lib._INVALID
     assert b"out_f32" in L.flexattn_last_error()
+
+
+def test_create_rejects_block_sizes(L):
+    assert _create(L, 1, lib._MaskParams(0, 0, None, 0, 0), block=640) == lib._UNSUPPORTED
+    assert _create(L, 1, lib._MaskParams(0, 0, None, 0, 0), block=192) == lib._UNSUPPORTED

@@ -156,7 +156,9 @@ typedef struct {
  * Fields (all index tensors are caller-allocated device int32 buffers):
  *   B, H                 extents of the index tensors over batch and query
  *                        heads; 1 broadcasts over that dimension.
- *   Q_LEN, KV_LEN        sequence lengths; BLOCK_SIZE = 128.
+ *   Q_LEN, KV_LEN        sequence lengths; BLOCK_SIZE: the square tile edge,
+ *                        128, 256, 384 or 512 (the page's default is 128;
+ *                        the backward and from_kv_blocks take 128 only).
  *   num_q_blocks (NQB)   ceil(Q_LEN / BLOCK_SIZE); num_kv_blocks (NKB) likewise.
  *   kv_num_blocks        [B][H][NQB]
  *   kv_indices           [B][H][NQB][NKB]
@@ -218,7 +220,9 @@ flexattn_status flexattn_block_mask_sizes(int32_t B, int32_t H, int32_t Q_LEN, i
  * dimension; the enumerated kinds do not depend on b or h except through
  * per-batch doc_ids). On input the caller sets bm->kv_num_blocks,
  * kv_indices, full_kv_num_blocks, full_kv_indices and schedule; the call
- * fills every other field. block must be 128. Asynchronous on `stream`.
+ * fills every other field. block is the BLOCK_SIZE: 128, 256, 384 or 512
+ * (UNSUPPORTED otherwise; size the buffers with the same block through
+ * flexattn_block_mask_sizes). Asynchronous on `stream`.
  */
 flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
                                            const flexattn_mask_params* params, int32_t B,
@@ -239,7 +243,8 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
  *         BF16 or F16); D in {64, 128}; Hq a multiple of Hkv; query head h reads KV
  *         head h / (Hq / Hkv).
  *   bm    a BlockMask with bm->Q_LEN == Q_LEN, bm->KV_LEN == KV_LEN,
- *         bm->B in {1, B}, bm->H in {1, Hq}, BLOCK_SIZE 128.
+ *         bm->B in {1, B}, bm->H in {1, Hq}, BLOCK_SIZE 128, 256, 384 or 512
+ *         (the kernels walk 128 x 128 pieces of larger tiles).
  *   out   [B][Hq][Q_LEN][D], same dtype as q (written).
  *   lse   device float [B][Hq][Q_LEN], contiguous (written): natural-log
  *         log-sum-exp of the modified, masked scores of each row.
@@ -360,7 +365,8 @@ flexattn_status flexattn_block_mask_from_kv_blocks(flexattn_block_mask* bm, int3
  *         overwritten with Delta_i = sum_j P_ij dP_ij, which equals dO_i . O_i
  *         but is formed from fp32 P and dP, so the forward's output is not an
  *         input.
- * All tensors are BF16 with D in {64, 128} (UNSUPPORTED otherwise); strides
+ * All tensors are BF16 with D in {64, 128}, and the BlockMask has BLOCK_SIZE
+ * 128 (UNSUPPORTED otherwise); strides
  * and alignment as for flexattn_fwd. Rows with no allowed key (LSE = -inf)
  * get dq = 0. Asynchronous on `stream`; no host synchronisation.
  */

@@ -592,12 +592,13 @@ static flexattn_status bwd_impl(const flexattn_tensor* q, const flexattn_tensor*
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", who, q->H,
                 k->H);
   if (!std::isfinite(scale)) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: scale is not finite", who);
-  if (bm->BLOCK_SIZE != fa::kBlock)
-    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: BlockMask BLOCK_SIZE must be 128 (got %d)", who,
+  if (!valid_block(bm->BLOCK_SIZE))
+    return fail(FLEXATTN_ERR_UNSUPPORTED,
+                "%s: BlockMask BLOCK_SIZE must be 128, 256, 384 or 512 (got %d)", who,
                 bm->BLOCK_SIZE);
-  if (bm->Q_LEN != q->L || bm->KV_LEN != k->L ||
-      bm->num_q_blocks != ceil_div(q->L, fa::kBlock) ||
-      bm->num_kv_blocks != ceil_div(k->L, fa::kBlock))
+  const int BS = bm->BLOCK_SIZE;
+  if (bm->Q_LEN != q->L || bm->KV_LEN != k->L || bm->num_q_blocks != ceil_div(q->L, BS) ||
+      bm->num_kv_blocks != ceil_div(k->L, BS))
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: BlockMask lengths do not match the tensors", who);
   if (!(bm->B == 1 || bm->B == q->B) || !(bm->H == 1 || bm->H == q->H))
     return fail(FLEXATTN_ERR_INVALID_ARG,
@@ -617,8 +618,8 @@ static flexattn_status bwd_impl(const flexattn_tensor* q, const flexattn_tensor*
   if (mp.doc && bm->mask_params.doc_batch > 1 && bm->B != q->B)
     return fail(FLEXATTN_ERR_INVALID_ARG,
                 "%s: per-batch doc_ids need a BlockMask built per batch (B=%d)", who, q->B);
-  if ((long long)q->B * q->H * bm->num_q_blocks > 0x7fffffffLL ||
-      (long long)q->B * k->H * bm->num_kv_blocks > 0x7fffffffLL ||
+  if ((long long)q->B * q->H * bm->num_q_blocks * (BS / fa::kBlock) > 0x7fffffffLL ||
+      (long long)q->B * k->H * bm->num_kv_blocks * (BS / fa::kBlock) > 0x7fffffffLL ||
       (long long)q->B * q->H * q->L > 0x7fffffffLL)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: too many tiles or rows for one launch", who);
   if ((int)score_kind < FLEXATTN_SCORE_NONE || (int)score_kind > FLEXATTN_SCORE_SOFTCAP_ALIBI)
@@ -675,6 +676,7 @@ static flexattn_status bwd_impl(const flexattn_tensor* q, const flexattn_tensor*
   L.bm.Hm = bm->H;
   L.bm.NQB = bm->num_q_blocks;
   L.bm.NKB = bm->num_kv_blocks;
+  L.bm.BS = BS;
   L.q_num = bm->q_num_blocks;
   L.q_idx = bm->q_indices;
   L.full_q_num = bm->full_q_num_blocks;

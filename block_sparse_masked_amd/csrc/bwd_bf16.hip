@@ -199,11 +199,16 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) u16 sV[kBlock * LDR];
   __shared__ int sdoc[kBlock];
 
-  const Item it = decode_item(blockIdx.x, a.bm, a.B, a.Hq);
+  // BLOCK_SIZE = mk * 128: mk 128-row items per tile row, mk 128-key tiles
+  // per listed tile
+  const int mk = a.bm.BS / kBlock;
+  const Item it = decode_item(blockIdx.x / mk, a.bm, a.B, a.Hq);
   const int b = it.b, h = it.h, hk = h / a.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int q = it.qb * kBlock + wave * 32 + l32;
+  const int q_tile0 = it.qb * a.bm.BS + (blockIdx.x % mk) * kBlock;
+  if (q_tile0 >= a.Q_LEN) return;  // a 128-row piece past Q_LEN
+  const int q = q_tile0 + wave * 32 + l32;
   const bool qvalid = q < a.Q_LEN;
   const int qc = qvalid ? q : a.Q_LEN - 1;
 
@@ -275,11 +280,12 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     }
   };
 
-  for (int t = 0; t < nfull + npart; ++t) {
-    const bool full = t < nfull;
-    const int kb = min(max(full ? a.bm.full_idx[lrow + t] : a.bm.kv_idx[lrow + t - nfull], 0),
+  for (int t = 0; t < (nfull + npart) * mk; ++t) {
+    const int c = t / mk;  // listed tile; its 128-key piece t % mk
+    const bool full = c < nfull;
+    const int kb = min(max(full ? a.bm.full_idx[lrow + c] : a.bm.kv_idx[lrow + c - nfull], 0),
                        NKB - 1);
-    const int kv0 = kb * kBlock;
+    const int kv0 = kb * a.bm.BS + (t - c * mk) * kBlock;
     __syncthreads();  // the previous tile's reads are done
     stage_rows<D, 2>(sK, kbase, a.sk[2], kv0, a.KV_LEN, tid);
     stage_rows<D, 2>(sV, vbase, a.sv[2], kv0, a.KV_LEN, tid);
@@ -335,8 +341,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   // Under causal-like masks the early KV tiles have the longest query lists,
   // so the launch runs longest first (one workgroup per CU at this size).
   const int nbh = a.B * a.Hkv;
-  const int kb = blockIdx.x / nbh;
+  const int mk = a.bm.BS / kBlock;  // 128-key items per tile column
+  const int kb = blockIdx.x / nbh;  // in 128-key tiles
+  const int kbc = kb / mk;          // the BlockMask's tile column
   const int bh = blockIdx.x - kb * nbh;
+  if (kb * kBlock >= a.KV_LEN) return;  // a 128-key piece past KV_LEN
   const int hk = bh % a.Hkv, b = bh / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -377,24 +386,26 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
       const int h = hk * a.G + p.gi;
       const int bmi = a.bm.Bm == 1 ? 0 : b;
       const int hm = a.bm.Hm == 1 ? 0 : h;
-      p.mrow = ((long long)bmi * a.bm.Hm + hm) * NKB + kb;
+      p.mrow = ((long long)bmi * a.bm.Hm + hm) * NKB + kbc;
       p.nfull = min(max(a.fq_num[p.mrow], 0), NQB);
       p.npart = min(max(a.q_num[p.mrow], 0), NQB);
       if (p.nfull + p.npart > 0) break;
     }
     return p;
   };
+  // p.t counts 128-row pieces: listed tile p.t / mk, piece p.t % mk
   auto next_pos = [&](Pos p) __attribute__((always_inline)) {
-    if (p.t + 1 < p.nfull + p.npart) {
+    if (p.t + 1 < (p.nfull + p.npart) * mk) {
       ++p.t;
       return p;
     }
     return first_from(p.gi + 1);
   };
   auto tile_q0 = [&](const Pos& p) __attribute__((always_inline)) {
-    const bool full = p.t < p.nfull;
-    const int qb = full ? a.fq_idx[p.mrow * NQB + p.t] : a.q_idx[p.mrow * NQB + p.t - p.nfull];
-    return min(max(qb, 0), NQB - 1) * kBlock;
+    const int c = p.t / mk;
+    const bool full = c < p.nfull;
+    const int qb = full ? a.fq_idx[p.mrow * NQB + c] : a.q_idx[p.mrow * NQB + c - p.nfull];
+    return min(max(qb, 0), NQB - 1) * a.bm.BS + (p.t - c * mk) * kBlock;
   };
 
   // The next tile's Q / dO rows (and LSE, Delta, document ids) are loaded
@@ -494,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   if (cur.gi < a.G) fetch(cur);
   while (cur.gi < a.G) {
     const int q0 = tile_q0(cur);
-    const bool full = cur.t < cur.nfull;
+    const bool full = cur.t / mk < cur.nfull;
     float slope2 = 0.0f;
     if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
       slope2 = alibi_slope(a.slopes, hk * a.G + cur.gi, a.Hq) * kLog2e;
@@ -555,7 +566,7 @@ __global__ __launch_bounds__(256) void delta_from_out_kernel(BwdArgs a) {
 
 template <int D, int MASK, int SCORE>
 hipError_t launch_kernels(const BwdArgs& a, hipStream_t stream) {
-  const long long nq = (long long)a.B * a.Hq * a.bm.NQB;
+  const long long nq = (long long)a.B * a.Hq * a.bm.NQB * (a.bm.BS / kBlock);
   if (a.o32) {
     const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
     delta_from_out_kernel<D><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(a);
@@ -567,7 +578,7 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t stream) {
   dq_kernel<D, MASK, SCORE, false><<<(unsigned)nq, kThreads, 0, stream>>>(a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long nk = (long long)a.B * a.Hkv * a.bm.NKB;
+  const long long nk = (long long)a.B * a.Hkv * a.bm.NKB * (a.bm.BS / kBlock);
   dkdv_kernel<D, MASK, SCORE><<<(unsigned)nk, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }

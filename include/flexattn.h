@@ -158,7 +158,7 @@ typedef struct {
  *                        heads; 1 broadcasts over that dimension.
  *   Q_LEN, KV_LEN        sequence lengths; BLOCK_SIZE: the square tile edge,
  *                        128, 256, 384 or 512 (the page's default is 128;
- *                        the backward and from_kv_blocks take 128 only).
+ *                        from_kv_blocks takes 128 only).
  *   num_q_blocks (NQB)   ceil(Q_LEN / BLOCK_SIZE); num_kv_blocks (NKB) likewise.
  *   kv_num_blocks        [B][H][NQB]
  *   kv_indices           [B][H][NQB][NKB]
@@ -365,8 +365,7 @@ flexattn_status flexattn_block_mask_from_kv_blocks(flexattn_block_mask* bm, int3
  *         overwritten with Delta_i = sum_j P_ij dP_ij, which equals dO_i . O_i
  *         but is formed from fp32 P and dP, so the forward's output is not an
  *         input.
- * All tensors are BF16 with D in {64, 128}, and the BlockMask has BLOCK_SIZE
- * 128 (UNSUPPORTED otherwise); strides
+ * All tensors are BF16 with D in {64, 128} (UNSUPPORTED otherwise); strides
  * and alignment as for flexattn_fwd. Rows with no allowed key (LSE = -inf)
  * get dq = 0. Asynchronous on `stream`; no host synchronisation.
  */

@@ -1,7 +1,7 @@
 """BLOCK_SIZE 256, 384 and 512 (square tiles that are multiples of the
 kernels' 128): the builder's tensors bit-exact against the oracle's builder
 at that block size, and the forwards (fp32, bf16, fp16; split-KV and paged)
-against the fp64 oracle. The backward and from_kv_blocks take 128 only."""
+against the fp64 oracle, and the backward. from_kv_blocks takes 128 only."""
 import numpy as np
 import pytest
 import torch
@@ -96,8 +96,23 @@ def test_block_size_split_and_paged(lib, block, splits):
 def test_block_size_rejections(lib):
     with pytest.raises(NotImplementedError, match="block"):
         lib.create_block_mask("causal", 1, 1, 512, 512, 192)
-    bm = lib.create_block_mask("causal", 1, 1, 512, 512, 256, backward_lists=True)
-    q = torch.zeros((1, 2, 512, 64), dtype=torch.bfloat16, device="cuda")
-    out, lse = lib.flex_attention(q, q, q, bm)
-    with pytest.raises(NotImplementedError, match="BLOCK_SIZE"):
-        lib.flex_attention_backward(q, q, q, lse, out, bm)
+
+
+@pytest.mark.parametrize("block", [256, 512])
+@pytest.mark.parametrize("kind,score", [("causal", "softcap"), ("document_causal", "alibi"),
+                                        ("sliding_sink", "none"), ("composite", "softcap_alibi")])
+def test_block_size_backward(lib, block, kind, score):
+    """The backward walks the 128 x 128 pieces of the larger tiles (dQ over
+    each row's key pieces, dK/dV over each column's query pieces)."""
+    from tests.test_bwd_gpu import tiny as btiny, check, oracle_bwd, run_bwd
+    w = btiny(128 if block == 256 else 64, kind, score, Q_LEN=650, KV_LEN=700, window=250,
+              sinks=3, prefix=100, doc_seed=3, doc_len_range=(60, 300),
+              terms=TERMS if kind == "composite" else None,
+              value_scale=2.0 if "softcap" in score else 1.0)
+    inp = W.generate(w)
+    d_out = W.generate_upstream(w)
+    bm = build(lib, w, inp, block, backward_lists=True)
+    got = run_bwd(lib, w, inp, d_out, bm)
+    ref = oracle_bwd(w, inp, d_out)
+    for g, r, n in zip(got, ref, ("dq", "dk", "dv")):
+        check(g, r, n)

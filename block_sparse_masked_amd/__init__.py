@@ -69,7 +69,8 @@ class _BlockMask(ctypes.Structure):
                 ("schedule", ctypes.c_void_p), ("mask_kind", ctypes.c_int),
                 ("mask_params", _MaskParams),
                 ("q_num_blocks", ctypes.c_void_p), ("q_indices", ctypes.c_void_p),
-                ("full_q_num_blocks", ctypes.c_void_p), ("full_q_indices", ctypes.c_void_p)]
+                ("full_q_num_blocks", ctypes.c_void_p), ("full_q_indices", ctypes.c_void_p),
+                ("Q_BLOCK_SIZE", ctypes.c_int32)]
 
 
 class _PageTable(ctypes.Structure):
@@ -95,6 +96,9 @@ def load_library():
     lib = ctypes.CDLL(_LIB_PATH)
     lib.flexattn_last_error.restype = ctypes.c_char_p
     lib.flexattn_version.restype = ctypes.c_char_p
+    lib.flexattn_block_mask_sizes_2d.restype = ctypes.c_int
+    lib.flexattn_block_mask_sizes_2d.argtypes = [ctypes.c_int32] * 6 + [
+        ctypes.POINTER(ctypes.c_size_t)] * 3
     lib.flexattn_block_mask_sizes.restype = ctypes.c_int
     lib.flexattn_block_mask_sizes.argtypes = [ctypes.c_int32] * 5 + [
         ctypes.POINTER(ctypes.c_size_t)] * 3
@@ -169,12 +173,21 @@ def _stream_handle(device: torch.device, stream=None) -> int:
     return int(stream.cuda_stream)
 
 
-def block_mask_sizes(B: int, H: int, Q_LEN: int, KV_LEN: int, block: int = 128):
+def _blocks(block):
+    """(kv_block, q_block) from an int or the page's (KV_BLOCK_SIZE,
+    Q_BLOCK_SIZE) tuple."""
+    if isinstance(block, (tuple, list)):
+        return int(block[0]), int(block[1])
+    return int(block), int(block)
+
+
+def block_mask_sizes(B: int, H: int, Q_LEN: int, KV_LEN: int, block=128):
     """(num_elems, idx_elems, sched_elems) of the BlockMask buffers."""
     lib = load_library()
+    kb, qb = _blocks(block)
     a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
-    _check(lib.flexattn_block_mask_sizes(B, H, Q_LEN, KV_LEN, block, ctypes.byref(a),
-                                         ctypes.byref(b), ctypes.byref(c)),
+    _check(lib.flexattn_block_mask_sizes_2d(B, H, Q_LEN, KV_LEN, kb, qb, ctypes.byref(a),
+                                            ctypes.byref(b), ctypes.byref(c)),
            "flexattn_block_mask_sizes")
     return a.value, b.value, c.value
 
@@ -202,6 +215,11 @@ class BlockMask:
     full_q_num_blocks: Optional[torch.Tensor] = None  # int32 [B, H, NKB]
     full_q_indices: Optional[torch.Tensor] = None     # int32 [B, H, NKB, NQB]
     status: Optional[torch.Tensor] = None             # int32 [1]: from_kv_blocks check flags
+    Q_BLOCK_SIZE: int = 0  # query rows per tile (0: BLOCK_SIZE, square tiles)
+
+    @property
+    def q_block(self) -> int:
+        return self.Q_BLOCK_SIZE or self.BLOCK_SIZE
 
     @property
     def num_q_blocks(self) -> int:
@@ -247,7 +265,8 @@ class BlockMask:
         rows = np.array_split(np.arange(nqb), gr)
         cols = np.array_split(np.arange(nkb), gc)
         out = [f"BlockMask(B={self.B}, H={self.H}, Q_LEN={self.Q_LEN}, KV_LEN={self.KV_LEN}, "
-               f"BLOCK_SIZE={self.BLOCK_SIZE}, kind={self.kind}, sparsity={self.sparsity():.2f}%)"]
+               f"BLOCK_SIZE={self.BLOCK_SIZE if self.q_block == self.BLOCK_SIZE else (self.BLOCK_SIZE, self.q_block)}, "
+               f"kind={self.kind}, sparsity={self.sparsity():.2f}%)"]
         for n, (b, h) in enumerate(np.ndindex(B, H)):
             if n >= limit:
                 out.append(f"... {B * H - limit} more (b, h)")
@@ -309,7 +328,8 @@ def create_block_mask(kind: str, B: int, H: int, Q_LEN: int, KV_LEN: int, block:
         raise NotImplementedError(f"mask kind {kind!r} is not one of {sorted(MASK_KINDS)}")
     device = torch.device(device)
     n_num, n_idx, n_sched = block_mask_sizes(B, H, Q_LEN, KV_LEN, block)
-    nqb = -(-Q_LEN // block)
+    block, q_block = _blocks(block)
+    nqb = -(-Q_LEN // q_block)
     nkb = -(-KV_LEN // block)
     kv_num = torch.empty((B, H, nqb), dtype=torch.int32, device=device)
     kv_idx = torch.empty((B, H, nqb, nkb), dtype=torch.int32, device=device)
@@ -329,6 +349,7 @@ def create_block_mask(kind: str, B: int, H: int, Q_LEN: int, KV_LEN: int, block:
         mp.doc_batch = doc_ids.shape[0]
         mp.doc_len = doc_ids.shape[1]
     c = _BlockMask()
+    c.Q_BLOCK_SIZE = q_block
     c.kv_num_blocks = kv_num.data_ptr()
     c.kv_indices = kv_idx.data_ptr()
     c.full_kv_num_blocks = full_num.data_ptr()
@@ -347,7 +368,7 @@ def create_block_mask(kind: str, B: int, H: int, Q_LEN: int, KV_LEN: int, block:
                                         _stream_handle(device, stream))
     _check(st, "flexattn_create_block_mask")
     return BlockMask(kind, B, H, Q_LEN, KV_LEN, block, kv_num, kv_idx, full_num, full_idx, sched,
-                     doc_ids, c, *qlists)
+                     doc_ids, c, *qlists, Q_BLOCK_SIZE=q_block)
 
 
 def _tensor(t: torch.Tensor, name: str) -> _Tensor:
@@ -385,7 +406,7 @@ def auto_splits(q: torch.Tensor, k: torch.Tensor, block_mask: BlockMask,
             if M <= 32 * wph and group % (4 // wph) == 0:
                 heads_per_wg = 4 // wph
                 break
-    items = B * (Hq // heads_per_wg) * block_mask.num_q_blocks * (block_mask.BLOCK_SIZE // 128)
+    items = B * (Hq // heads_per_wg) * block_mask.num_q_blocks * (block_mask.q_block // 128)
     if items >= target_workgroups // 2:
         return 1
     return max(1, min(block_mask.num_kv_blocks, target_workgroups // items, 64))

@@ -156,16 +156,25 @@ const char* flexattn_version(void) { return "flexattn-gfx950 0.1.0"; }
 flexattn_status flexattn_block_mask_sizes(int32_t B, int32_t H, int32_t Q_LEN, int32_t KV_LEN,
                                           int32_t block, size_t* num_elems, size_t* idx_elems,
                                           size_t* sched_elems) {
+  return flexattn_block_mask_sizes_2d(B, H, Q_LEN, KV_LEN, block, block, num_elems, idx_elems,
+                                      sched_elems);
+}
+
+flexattn_status flexattn_block_mask_sizes_2d(int32_t B, int32_t H, int32_t Q_LEN, int32_t KV_LEN,
+                                             int32_t block, int32_t q_block,
+                                             size_t* num_elems, size_t* idx_elems,
+                                             size_t* sched_elems) {
   if (!num_elems || !idx_elems || !sched_elems)
     return fail(FLEXATTN_ERR_INVALID_ARG, "flexattn_block_mask_sizes: NULL output pointer");
   if (B < 1 || H < 1 || Q_LEN < 1 || KV_LEN < 1)
     return fail(FLEXATTN_ERR_INVALID_ARG,
                 "flexattn_block_mask_sizes: B, H, Q_LEN, KV_LEN must be >= 1 (got %d %d %d %d)", B,
                 H, Q_LEN, KV_LEN);
-  if (!valid_block(block))
+  if (!valid_block(block) || !valid_block(q_block))
     return fail(FLEXATTN_ERR_UNSUPPORTED,
-                "flexattn_block_mask_sizes: block must be 128, 256, 384 or 512 (got %d)", block);
-  const size_t rows = (size_t)B * H * ceil_div(Q_LEN, block);
+                "flexattn_block_mask_sizes: block must be 128, 256, 384 or 512 (got %d, %d)",
+                block, q_block);
+  const size_t rows = (size_t)B * H * ceil_div(Q_LEN, q_block);
   *num_elems = rows;
   *idx_elems = rows * (size_t)ceil_div(KV_LEN, block);
   *sched_elems = rows;
@@ -182,14 +191,16 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
   if (B < 1 || H < 1 || Q_LEN < 1 || KV_LEN < 1)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: B, H, Q_LEN, KV_LEN must be >= 1 (got %d %d %d %d)",
                 who, B, H, Q_LEN, KV_LEN);
-  if (!valid_block(block))
-    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: block must be 128, 256, 384 or 512 (got %d)", who,
-                block);
+  const int q_block = bm->Q_BLOCK_SIZE > 0 ? bm->Q_BLOCK_SIZE : block;
+  if (!valid_block(block) || !valid_block(q_block))
+    return fail(FLEXATTN_ERR_UNSUPPORTED,
+                "%s: block must be 128, 256, 384 or 512 (got %d, Q_BLOCK_SIZE %d)", who, block,
+                q_block);
   const int nkb = ceil_div(KV_LEN, block);
   if (nkb > fa::max_build_kv_blocks())
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: KV_LEN %d exceeds the builder limit of %d tiles",
                 who, KV_LEN, fa::max_build_kv_blocks());
-  if ((long long)B * H * ceil_div(Q_LEN, block) > 0x7fffffffLL / (nkb > 0 ? nkb : 1))
+  if ((long long)B * H * ceil_div(Q_LEN, q_block) > 0x7fffffffLL / (nkb > 0 ? nkb : 1))
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: index tensor too large", who);
   if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices ||
       !bm->schedule)
@@ -208,7 +219,8 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
   bm->Q_LEN = Q_LEN;
   bm->KV_LEN = KV_LEN;
   bm->BLOCK_SIZE = block;
-  bm->num_q_blocks = ceil_div(Q_LEN, block);
+  bm->Q_BLOCK_SIZE = q_block;
+  bm->num_q_blocks = ceil_div(Q_LEN, q_block);
   bm->num_kv_blocks = nkb;
   bm->mask_kind = kind;
   if (params) {
@@ -234,6 +246,7 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
   L.schedule = bm->schedule;
   L.separate_full = separate_full_blocks != 0;
   L.block = block;
+  L.q_block = q_block;
   const bool with_q = bm->q_num_blocks && bm->q_indices && bm->full_q_num_blocks &&
                       bm->full_q_indices;
   L.q_num = with_q ? bm->q_num_blocks : nullptr;
@@ -253,9 +266,9 @@ flexattn_status flexattn_block_mask_from_kv_blocks(flexattn_block_mask* bm, int3
   if (!status) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: status is NULL", who);
   if (bm->B < 1 || bm->H < 1 || bm->Q_LEN < 1 || bm->KV_LEN < 1)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: B, H, Q_LEN, KV_LEN must be >= 1", who);
-  if (bm->BLOCK_SIZE != fa::kBlock)
-    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: BLOCK_SIZE must be 128 (got %d)", who,
-                bm->BLOCK_SIZE);
+  if (bm->BLOCK_SIZE != fa::kBlock || (bm->Q_BLOCK_SIZE != 0 && bm->Q_BLOCK_SIZE != fa::kBlock))
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: BLOCK_SIZE must be 128 (got %d, Q_BLOCK_SIZE %d)",
+                who, bm->BLOCK_SIZE, bm->Q_BLOCK_SIZE);
   const int nqb = ceil_div(bm->Q_LEN, fa::kBlock), nkb = ceil_div(bm->KV_LEN, fa::kBlock);
   if (bm->num_q_blocks != nqb || bm->num_kv_blocks != nkb)
     return fail(FLEXATTN_ERR_INVALID_ARG,
@@ -371,11 +384,15 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
                 "%s: BlockMask BLOCK_SIZE must be 128, 256, 384 or 512 (got %d)", who,
                 bm->BLOCK_SIZE);
   const int BS = bm->BLOCK_SIZE;
+  const int QBS = bm->Q_BLOCK_SIZE > 0 ? bm->Q_BLOCK_SIZE : BS;
+  if (!valid_block(QBS))
+    return fail(FLEXATTN_ERR_UNSUPPORTED,
+                "%s: BlockMask Q_BLOCK_SIZE must be 128, 256, 384 or 512 (got %d)", who, QBS);
   if (bm->Q_LEN != q->L || bm->KV_LEN != kv_len)
     return fail(FLEXATTN_ERR_INVALID_ARG,
                 "%s: BlockMask built for Q_LEN=%d KV_LEN=%d, tensors have %d and %d", who,
                 bm->Q_LEN, bm->KV_LEN, q->L, kv_len);
-  if (bm->num_q_blocks != ceil_div(q->L, BS) || bm->num_kv_blocks != ceil_div(kv_len, BS))
+  if (bm->num_q_blocks != ceil_div(q->L, QBS) || bm->num_kv_blocks != ceil_div(kv_len, BS))
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: BlockMask tile counts do not match its lengths",
                 who);
   if (!(bm->B == 1 || bm->B == q->B) || !(bm->H == 1 || bm->H == q->H))
@@ -395,7 +412,7 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
                 "%s: per-batch doc_ids need a BlockMask built per batch (B=%d)", who, q->B);
   // the fp32 kernel launches BLOCK_SIZE / 32 workgroups per tile row, the
   // 16-bit one BLOCK_SIZE / 128 per tile row and head
-  if ((long long)q->B * q->H * bm->num_q_blocks * (BS / 32) > 0x7fffffffLL)
+  if ((long long)q->B * q->H * bm->num_q_blocks * (QBS / 32) > 0x7fffffffLL)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: too many query tiles for one launch", who);
   if ((int)score_kind < FLEXATTN_SCORE_NONE || (int)score_kind > FLEXATTN_SCORE_SOFTCAP_ALIBI)
     return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: score_kind %d is not a supported kind", who,
@@ -468,6 +485,7 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   L.bm.NQB = bm->num_q_blocks;
   L.bm.NKB = bm->num_kv_blocks;
   L.bm.BS = BS;
+  L.bm.QBS = QBS;
   if (out_f32) {
     if (!half || splits > 1 || pages || !aligned16(out_f32))
       return fail(FLEXATTN_ERR_INVALID_ARG,
@@ -597,7 +615,11 @@ static flexattn_status bwd_impl(const flexattn_tensor* q, const flexattn_tensor*
                 "%s: BlockMask BLOCK_SIZE must be 128, 256, 384 or 512 (got %d)", who,
                 bm->BLOCK_SIZE);
   const int BS = bm->BLOCK_SIZE;
-  if (bm->Q_LEN != q->L || bm->KV_LEN != k->L || bm->num_q_blocks != ceil_div(q->L, BS) ||
+  const int QBS = bm->Q_BLOCK_SIZE > 0 ? bm->Q_BLOCK_SIZE : BS;
+  if (!valid_block(QBS))
+    return fail(FLEXATTN_ERR_UNSUPPORTED,
+                "%s: BlockMask Q_BLOCK_SIZE must be 128, 256, 384 or 512 (got %d)", who, QBS);
+  if (bm->Q_LEN != q->L || bm->KV_LEN != k->L || bm->num_q_blocks != ceil_div(q->L, QBS) ||
       bm->num_kv_blocks != ceil_div(k->L, BS))
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: BlockMask lengths do not match the tensors", who);
   if (!(bm->B == 1 || bm->B == q->B) || !(bm->H == 1 || bm->H == q->H))
@@ -618,7 +640,7 @@ static flexattn_status bwd_impl(const flexattn_tensor* q, const flexattn_tensor*
   if (mp.doc && bm->mask_params.doc_batch > 1 && bm->B != q->B)
     return fail(FLEXATTN_ERR_INVALID_ARG,
                 "%s: per-batch doc_ids need a BlockMask built per batch (B=%d)", who, q->B);
-  if ((long long)q->B * q->H * bm->num_q_blocks * (BS / fa::kBlock) > 0x7fffffffLL ||
+  if ((long long)q->B * q->H * bm->num_q_blocks * (QBS / fa::kBlock) > 0x7fffffffLL ||
       (long long)q->B * k->H * bm->num_kv_blocks * (BS / fa::kBlock) > 0x7fffffffLL ||
       (long long)q->B * q->H * q->L > 0x7fffffffLL)
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: too many tiles or rows for one launch", who);
@@ -677,6 +699,7 @@ static flexattn_status bwd_impl(const flexattn_tensor* q, const flexattn_tensor*
   L.bm.NQB = bm->num_q_blocks;
   L.bm.NKB = bm->num_kv_blocks;
   L.bm.BS = BS;
+  L.bm.QBS = QBS;
   L.q_num = bm->q_num_blocks;
   L.q_idx = bm->q_indices;
   L.full_q_num = bm->full_q_num_blocks;

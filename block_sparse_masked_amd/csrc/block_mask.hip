@@ -33,7 +33,8 @@ struct BuildArgs {
   int doc_len;
   const int* sorted_flags;  // document kind: per-chunk sortedness (schedule buffer)
   int Bm, Hm, Q_LEN, KV_LEN, NQB, NKB;
-  int BS;  // BLOCK_SIZE: a multiple of 128 (rows are counted 128 at a time)
+  int BS;   // KV_BLOCK_SIZE: a multiple of 128
+  int QBS;  // Q_BLOCK_SIZE: a multiple of 128 (rows are counted 128 at a time)
   int* kv_num;
   int* kv_idx;
   int* full_num;
@@ -181,15 +182,15 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
   const int bm = row / (a.NQB * a.Hm);
   const int t = threadIdx.x;
   const int NKB = a.NKB;
-  const int BS = a.BS;
+  const int BS = a.BS, QBS = a.QBS;
   int* tot = smem;
   int* dif = smem + NKB;
   for (int j = t; j < 2 * NKB + 1; j += kRowThreads) smem[j] = 0;
 
   // The tile row's BS query rows, 128 at a time (one per thread); each
   // query row's allowed keys are counted into the per-tile totals.
-  for (int sb = 0; sb < BS / kBlock; ++sb) {
-  const int q = qb * BS + sb * kBlock + t;
+  for (int sb = 0; sb < QBS / kBlock; ++sb) {
+  const int q = qb * QBS + sb * kBlock + t;
   const bool qvalid = q < a.Q_LEN;
   // Per-row allowed intervals: I1 = [lo1, hi1], I2 = [lo2, hi2] (may be empty).
   int lo1 = 0, hi1 = -1, lo2 = 0, hi2 = -1;
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
     for (int c = t; c < a.NQB; c += kRowThreads) bad |= (a.sorted_flags[drow * a.NQB + c] == 0);
     const bool sorted = __syncthreads_or(bad) == 0;
     if (sorted) {
-      const int q0 = qb * BS + sb * kBlock;
+      const int q0 = qb * QBS + sb * kBlock;
       const int s0 = run_start_of(doc, min(q0, a.doc_len - 1), scratch);
       // run boundaries inside this tile, then the latest boundary <= q
       int bnd = (qvalid && q > q0 && doc[q] != doc[q - 1]) ? q : -1;
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(kRowThreads) void classify_kernel(BuildArgs a) {
     int isP = 0, isF = 0;
     if (j < NKB) {
       const int cnt = tot[j] + run + incD;
-      isF = a.separate_full && (cnt == BS * BS);
+      isF = a.separate_full && (cnt == QBS * BS);
       isP = (cnt > 0 && !isF);
     }
     const int incP = block_incl_scan128(isP, scratch);
@@ -598,6 +599,7 @@ hipError_t launch_build(const BuildLaunch& L, hipStream_t stream) {
   a.full_idx = L.full_idx;
   a.separate_full = L.separate_full;
   a.BS = L.block;
+  a.QBS = L.q_block;
   const int rows = L.Bm * L.Hm * L.NQB;
   const size_t lds = sizeof(int) * (2 * (size_t)L.NKB + 1);
   switch (L.kind) {

@@ -201,12 +201,12 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
 
   // BLOCK_SIZE = mk * 128: mk 128-row items per tile row, mk 128-key tiles
   // per listed tile
-  const int mk = a.bm.BS / kBlock;
-  const Item it = decode_item(blockIdx.x / mk, a.bm, a.B, a.Hq);
+  const int mk = a.bm.BS / kBlock, mq = a.bm.QBS / kBlock;
+  const Item it = decode_item(blockIdx.x / mq, a.bm, a.B, a.Hq);
   const int b = it.b, h = it.h, hk = h / a.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int q_tile0 = it.qb * a.bm.BS + (blockIdx.x % mk) * kBlock;
+  const int q_tile0 = it.qb * a.bm.QBS + (blockIdx.x % mq) * kBlock;
   if (q_tile0 >= a.Q_LEN) return;  // a 128-row piece past Q_LEN
   const int q = q_tile0 + wave * 32 + l32;
   const bool qvalid = q < a.Q_LEN;
@@ -341,7 +341,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   // Under causal-like masks the early KV tiles have the longest query lists,
   // so the launch runs longest first (one workgroup per CU at this size).
   const int nbh = a.B * a.Hkv;
-  const int mk = a.bm.BS / kBlock;  // 128-key items per tile column
+  const int mk = a.bm.BS / kBlock;   // 128-key items per tile column
+  const int mq = a.bm.QBS / kBlock;  // 128-row pieces per listed query tile
   const int kb = blockIdx.x / nbh;  // in 128-key tiles
   const int kbc = kb / mk;          // the BlockMask's tile column
   const int bh = blockIdx.x - kb * nbh;
@@ -393,19 +394,19 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     }
     return p;
   };
-  // p.t counts 128-row pieces: listed tile p.t / mk, piece p.t % mk
+  // p.t counts 128-row pieces: listed tile p.t / mq, piece p.t % mq
   auto next_pos = [&](Pos p) __attribute__((always_inline)) {
-    if (p.t + 1 < (p.nfull + p.npart) * mk) {
+    if (p.t + 1 < (p.nfull + p.npart) * mq) {
       ++p.t;
       return p;
     }
     return first_from(p.gi + 1);
   };
   auto tile_q0 = [&](const Pos& p) __attribute__((always_inline)) {
-    const int c = p.t / mk;
+    const int c = p.t / mq;
     const bool full = c < p.nfull;
     const int qb = full ? a.fq_idx[p.mrow * NQB + c] : a.q_idx[p.mrow * NQB + c - p.nfull];
-    return min(max(qb, 0), NQB - 1) * a.bm.BS + (p.t - c * mk) * kBlock;
+    return min(max(qb, 0), NQB - 1) * a.bm.QBS + (p.t - c * mq) * kBlock;
   };
 
   // The next tile's Q / dO rows (and LSE, Delta, document ids) are loaded
@@ -505,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   if (cur.gi < a.G) fetch(cur);
   while (cur.gi < a.G) {
     const int q0 = tile_q0(cur);
-    const bool full = cur.t / mk < cur.nfull;
+    const bool full = cur.t / mq < cur.nfull;
     float slope2 = 0.0f;
     if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
       slope2 = alibi_slope(a.slopes, hk * a.G + cur.gi, a.Hq) * kLog2e;
@@ -566,7 +567,7 @@ __global__ __launch_bounds__(256) void delta_from_out_kernel(BwdArgs a) {
 
 template <int D, int MASK, int SCORE>
 hipError_t launch_kernels(const BwdArgs& a, hipStream_t stream) {
-  const long long nq = (long long)a.B * a.Hq * a.bm.NQB * (a.bm.BS / kBlock);
+  const long long nq = (long long)a.B * a.Hq * a.bm.NQB * (a.bm.QBS / kBlock);
   if (a.o32) {
     const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
     delta_from_out_kernel<D><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(a);

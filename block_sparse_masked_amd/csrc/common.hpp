@@ -84,7 +84,8 @@ struct BlockMaskView {
   const int* full_idx;  // [Bm][Hm][NQB][NKB]
   const int* schedule;  // [Bm*Hm*NQB]
   int Bm, Hm, NQB, NKB;
-  int BS = kBlock;  // BLOCK_SIZE of the lists (a multiple of kBlock)
+  int BS = kBlock;   // KV_BLOCK_SIZE of the lists (a multiple of kBlock)
+  int QBS = kBlock;  // Q_BLOCK_SIZE of the lists (a multiple of kBlock)
 };
 
 // Element mask of each kind: allowed(b, q, kv) for in-range indices.

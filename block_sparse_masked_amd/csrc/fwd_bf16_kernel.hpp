@@ -503,11 +503,11 @@ fwd_bf16_kernel(FwdArgs a) {
   }
   // BLOCK_SIZE = mk * 128: a tile row holds mk 128-row query tiles (one item
   // each) and a listed tile mk 128-key tiles (walked one after another)
-  const int mk = a.bm.BS / kBlock;
+  const int mk = a.bm.BS / kBlock, mq = a.bm.QBS / kBlock;
   int qsub = 0;
-  if (mk > 1) {
-    qsub = x % mk;
-    x /= mk;
+  if (mq > 1) {
+    qsub = x % mq;
+    x /= mq;
   }
   if (a.xcd_round > 0) {
     const int R = a.xcd_round;
@@ -522,7 +522,7 @@ fwd_bf16_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = it.b, h = it.h * HPW + wave / wph;
   const int hk = (it.h * HPW) / a.G;
-  const int q_tile0 = it.qb * a.bm.BS + qsub * kBlock;
+  const int q_tile0 = it.qb * a.bm.QBS + qsub * kBlock;
   if (q_tile0 >= a.Q_LEN) return;  // a 128-row tile past Q_LEN (BLOCK_SIZE > 128)
   Lane<D> ln;
   ln.lane = threadIdx.x & 63;
@@ -933,7 +933,7 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
   const int R = L.B * L.Hq / hpw;
   const int g_items = a.G / hpw;  // items per KV group
   a.xcd_round = (L.bm.Bm == 1 && L.bm.Hm == 1 && R % 8 == 0 && (R / 8) % g_items == 0) ? R : 0;
-  const int grid = R * L.bm.NQB * (L.bm.BS / kBlock) * a.splits;
+  const int grid = R * L.bm.NQB * (L.bm.QBS / kBlock) * a.splits;
   if (grid == 0) return hipSuccess;
   // the unscaled fast path takes the row max before scaling: scale must be > 0
   const int score = (L.score_kind == SCORE_NONE && !(L.scale > 0.0f)) ? SCORE_SCALED : L.score_kind;

@@ -80,11 +80,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
   float* sV = smem_f32 + kSub * D;
 
   // kRowsPerWg query rows per workgroup, BLOCK_SIZE / kRowsPerWg per tile row
-  const int wg_per_row = a.bm.BS / kRowsPerWg;
+  const int wg_per_row = a.bm.QBS / kRowsPerWg;
   const Item it = decode_item(blockIdx.x / wg_per_row, a.bm, a.B, a.Hq);
   const int b = it.b, h = it.h, hk = h / a.G;
   const int half = threadIdx.x % kTpr;  // this thread's quarter of the head dimension
-  const int q = it.qb * a.bm.BS + (blockIdx.x % wg_per_row) * kRowsPerWg + threadIdx.x / kTpr;
+  const int q = it.qb * a.bm.QBS + (blockIdx.x % wg_per_row) * kRowsPerWg + threadIdx.x / kTpr;
   const bool qvalid = q < a.Q_LEN;
   const int qc = qvalid ? q : a.Q_LEN - 1;
 
@@ -253,7 +253,7 @@ hipError_t launch_fwd_f32(const FwdLaunch& L, hipStream_t stream) {
   a.softcap = L.softcap;
   a.slopes = L.slopes;
   a.bm = L.bm;
-  const int grid = L.B * L.Hq * L.bm.NQB * (L.bm.BS / kRowsPerWg);
+  const int grid = L.B * L.Hq * L.bm.NQB * (L.bm.QBS / kRowsPerWg);
   if (grid == 0) return hipSuccess;
   if (L.D == 128) return f32_dispatch_mask<128>(a, L.mask_kind, L.score_kind, grid, stream);
   return f32_dispatch_mask<64>(a, L.mask_kind, L.score_kind, grid, stream);

@@ -14,7 +14,8 @@ struct BuildLaunch {
   MaskParams mp;
   int doc_len;
   int Bm, Hm, Q_LEN, KV_LEN, NQB, NKB;
-  int block = 128;  // BLOCK_SIZE (a multiple of 128)
+  int block = 128;    // KV_BLOCK_SIZE (a multiple of 128)
+  int q_block = 128;  // Q_BLOCK_SIZE (a multiple of 128)
   int* kv_num;
   int* kv_idx;
   int* full_num;

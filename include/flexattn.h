@@ -195,6 +195,11 @@ typedef struct {
   int32_t* q_indices;
   int32_t* full_q_num_blocks;
   int32_t* full_q_indices;
+  /* Q_BLOCK_SIZE of non-square tiles (the page's BLOCK_SIZE tuple
+     (KV_BLOCK_SIZE, Q_BLOCK_SIZE), with BLOCK_SIZE the KV one): 0 means
+     square tiles (= BLOCK_SIZE); else 128, 256, 384 or 512. An input to
+     flexattn_create_block_mask, which writes the value it used. */
+  int32_t Q_BLOCK_SIZE;
 } flexattn_block_mask;
 
 /*
@@ -203,6 +208,11 @@ typedef struct {
  * idx_elems for each of kv_indices / full_kv_indices, sched_elems for
  * schedule. Host only. Output pointers must be non-NULL.
  */
+/* The same for non-square tiles: kv_block x q_block. */
+flexattn_status flexattn_block_mask_sizes_2d(int32_t B, int32_t H, int32_t Q_LEN, int32_t KV_LEN,
+                                             int32_t kv_block, int32_t q_block,
+                                             size_t* num_elems, size_t* idx_elems,
+                                             size_t* sched_elems);
 flexattn_status flexattn_block_mask_sizes(int32_t B, int32_t H, int32_t Q_LEN, int32_t KV_LEN,
                                           int32_t block, size_t* num_elems, size_t* idx_elems,
                                           size_t* sched_elems);

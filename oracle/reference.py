@@ -261,19 +261,21 @@ class BlockMask:
         return 100.0 * (1.0 - dense.sum() / dense.size)
 
 
-def classify_tiles(counts: np.ndarray, q_len: int, kv_len: int, block: int):
+def classify_tiles(counts: np.ndarray, q_len: int, kv_len: int, block):
     """Tile classes from per-tile allowed counts: 0 empty, 1 partial, 2 full.
 
-    A tile is full only when all block x block elements exist and are allowed;
-    a tail tile has fewer than block*block in-range elements, so it is never
-    full."""
-    cls = np.where(counts == 0, 0, np.where(counts == block * block, 2, 1))
+    `block` is an int or (kv_block, q_block). A tile is full only when all of
+    its q_block x kv_block elements exist and are allowed; a tail tile has
+    fewer in-range elements, so it is never full."""
+    kblk, qblk = (block, block) if np.isscalar(block) else block
+    cls = np.where(counts == 0, 0, np.where(counts == kblk * qblk, 2, 1))
     return cls.astype(np.int8)
 
 
 def create_block_mask(mask_mod: MaskMod, B: int, H: int, Q_LEN: int, KV_LEN: int,
                       BLOCK_SIZE: int = 128, separate_full_blocks: bool = True) -> BlockMask:
-    """Reduce the element mask to block x block tiles and list them.
+    """Reduce the element mask to tiles and list them. BLOCK_SIZE is one
+    int (square tiles) or the page's tuple (KV_BLOCK_SIZE, Q_BLOCK_SIZE).
 
     For each (b, h, q-tile) the element mask rows of that tile are evaluated
     over every key, allowed elements are counted per KV tile, and the tile is
@@ -283,21 +285,22 @@ def create_block_mask(mask_mod: MaskMod, B: int, H: int, Q_LEN: int, KV_LEN: int
     every non-empty tile is listed in ``kv_*`` and ``full_kv_*`` is empty
     (page "tensorplay.nn.attention API", create_block_mask parameters).
     """
-    blk = int(BLOCK_SIZE)
-    nqb = -(-Q_LEN // blk)
-    nkb = -(-KV_LEN // blk)
+    kblk, qblk = (BLOCK_SIZE, BLOCK_SIZE) if np.isscalar(BLOCK_SIZE) else BLOCK_SIZE
+    kblk, qblk = int(kblk), int(qblk)
+    nqb = -(-Q_LEN // qblk)
+    nkb = -(-KV_LEN // kblk)
     counts = np.zeros((B, H, nqb, nkb), dtype=np.int64)
     kv_idx = np.arange(KV_LEN, dtype=np.int64)[None, :]
     for b in range(B):
         for h in range(H):
             for i in range(nqb):
-                q_idx = np.arange(i * blk, min((i + 1) * blk, Q_LEN), dtype=np.int64)[:, None]
+                q_idx = np.arange(i * qblk, min((i + 1) * qblk, Q_LEN), dtype=np.int64)[:, None]
                 rows = np.broadcast_to(mask_mod(b, h, q_idx, kv_idx), (q_idx.shape[0], KV_LEN))
                 per_col = rows.sum(axis=0, dtype=np.int64)
-                padded = np.zeros(nkb * blk, dtype=np.int64)
+                padded = np.zeros(nkb * kblk, dtype=np.int64)
                 padded[:KV_LEN] = per_col
-                counts[b, h, i] = padded.reshape(nkb, blk).sum(axis=1)
-    cls = classify_tiles(counts, Q_LEN, KV_LEN, blk)
+                counts[b, h, i] = padded.reshape(nkb, kblk).sum(axis=1)
+    cls = classify_tiles(counts, Q_LEN, KV_LEN, (kblk, qblk))
     if not separate_full_blocks:
         cls = np.where(cls == 0, 0, 1).astype(np.int8)
     kv_num = np.zeros((B, H, nqb), dtype=np.int32)
@@ -313,6 +316,7 @@ def create_block_mask(mask_mod: MaskMod, B: int, H: int, Q_LEN: int, KV_LEN: int
                 kv_ind[b, h, i, :len(part)] = part
                 full_num[b, h, i] = len(full)
                 full_ind[b, h, i, :len(full)] = full
+    blk = kblk if kblk == qblk else (kblk, qblk)
     return BlockMask(Q_LEN, KV_LEN, blk, kv_num, kv_ind, full_num, full_ind, counts)
 
 

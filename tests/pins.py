@@ -14,12 +14,13 @@ import torch
 
 # ---------------------------------------------------------------- BlockMask
 
-def brute_force_tiles(allowed, B, H, Q_LEN, KV_LEN, blk):
+def brute_force_tiles(allowed, B, H, Q_LEN, KV_LEN, blk, q_blk=None):
     """Per-element pure-Python loop: class of every tile (0 empty, 1 partial,
     2 full) straight from the definitions (a tile is skipped only if every
     element is masked; full means every one of its blk*blk elements exists and
     is allowed)."""
-    nqb = -(-Q_LEN // blk)
+    qb_ = blk if q_blk is None else q_blk  # query rows per tile (blk: keys)
+    nqb = -(-Q_LEN // qb_)
     nkb = -(-KV_LEN // blk)
     cls = np.zeros((B, H, nqb, nkb), dtype=np.int8)
     for b in range(B):
@@ -27,13 +28,13 @@ def brute_force_tiles(allowed, B, H, Q_LEN, KV_LEN, blk):
             for i in range(nqb):
                 for j in range(nkb):
                     n_allowed = 0
-                    for q in range(i * blk, min((i + 1) * blk, Q_LEN)):
+                    for q in range(i * qb_, min((i + 1) * qb_, Q_LEN)):
                         for kv in range(j * blk, min((j + 1) * blk, KV_LEN)):
                             if allowed(b, h, q, kv):
                                 n_allowed += 1
                     if n_allowed == 0:
                         cls[b, h, i, j] = 0
-                    elif n_allowed == blk * blk:
+                    elif n_allowed == blk * qb_:
                         cls[b, h, i, j] = 2
                     else:
                         cls[b, h, i, j] = 1

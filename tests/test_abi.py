@@ -50,6 +50,8 @@ def test_block_mask_sizes(L):
         lib.block_mask_sizes(1, 1, 256, 256, 64)
     # multiples of 128 up to 512
     assert lib.block_mask_sizes(2, 3, 1000, 700, 256) == (2 * 3 * 4, 2 * 3 * 4 * 3, 2 * 3 * 4)
+    # the tuple form (KV_BLOCK_SIZE, Q_BLOCK_SIZE)
+    assert lib.block_mask_sizes(2, 3, 1000, 700, (256, 128)) == (2 * 3 * 8, 2 * 3 * 8 * 3, 2 * 3 * 8)
     for bad in (192, 640):
         with pytest.raises(NotImplementedError, match="block must be 128"):
             lib.block_mask_sizes(1, 1, 256, 256, bad)

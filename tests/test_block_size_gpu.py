@@ -116,3 +116,54 @@ def test_block_size_backward(lib, block, kind, score):
     ref = oracle_bwd(w, inp, d_out)
     for g, r, n in zip(got, ref, ("dq", "dk", "dv")):
         check(g, r, n)
+
+
+@pytest.mark.parametrize("blocks", [(256, 128), (128, 256), (512, 256), (128, 384)])
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("q_len,kv_len", [(300, 300), (1000, 700), (129, 1500)])
+def test_non_square_builder_bit_exact(lib, blocks, kind, q_len, kv_len):
+    """BLOCK_SIZE as the page's tuple (KV_BLOCK_SIZE, Q_BLOCK_SIZE)."""
+    w = tiny("bf16", 64, kind, "none", Q_LEN=q_len, KV_LEN=kv_len, window=300, sinks=3,
+             prefix=200, doc_seed=q_len, doc_len_range=(50, 400),
+             terms=TERMS if kind == "composite" else None)
+    inp = W.generate(w)
+    mask_mod, _ = oracle.for_workload(w, inp)
+    ref = oracle.create_block_mask(mask_mod, 1, 1, q_len, kv_len, blocks)
+    bm = build(lib, w, inp, blocks, backward_lists=True)
+    torch.cuda.synchronize()
+    assert bm.BLOCK_SIZE == blocks[0] and bm.q_block == blocks[1]
+    for got, want in ((bm.kv_num_blocks, ref.kv_num_blocks), (bm.kv_indices, ref.kv_indices),
+                      (bm.full_kv_num_blocks, ref.full_kv_num_blocks),
+                      (bm.full_kv_indices, ref.full_kv_indices)):
+        assert np.array_equal(got.cpu().numpy(), want)
+    for got, want in zip((bm.q_num_blocks, bm.q_indices, bm.full_q_num_blocks, bm.full_q_indices),
+                         oracle.transpose_block_mask(ref)):
+        assert np.array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("blocks", [(256, 128), (128, 384)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("f16", 256)])
+@pytest.mark.parametrize("kind", ["causal", "document_causal", "composite"])
+def test_non_square_forward(lib, blocks, dtype, D, kind):
+    w = tiny(dtype, D, kind, "alibi", Q_LEN=700, KV_LEN=900, window=300, sinks=3, prefix=200,
+             doc_seed=5, doc_len_range=(50, 400), terms=TERMS if kind == "composite" else None)
+    inp = W.generate(w)
+    bm = build(lib, w, inp, blocks)
+    o, lse, _ = G.run_gpu(lib, w, inp, bm)
+    o_ref, lse_ref = G.oracle_rows(w, inp)
+    res = G.compare(w, o, lse, o_ref, lse_ref)
+    assert res["ok"], G.summary(res)
+
+
+@pytest.mark.parametrize("blocks", [(256, 128), (128, 256)])
+def test_non_square_backward(lib, blocks):
+    from tests.test_bwd_gpu import tiny as btiny, check, oracle_bwd, run_bwd
+    w = btiny(64, "sliding_sink", "softcap", Q_LEN=650, KV_LEN=700, window=250, sinks=3,
+              value_scale=2.0)
+    inp = W.generate(w)
+    d_out = W.generate_upstream(w)
+    bm = build(lib, w, inp, blocks, backward_lists=True)
+    got = run_bwd(lib, w, inp, d_out, bm)
+    ref = oracle_bwd(w, inp, d_out)
+    for g, r, n in zip(got, ref, ("dq", "dk", "dv")):
+        check(g, r, n)

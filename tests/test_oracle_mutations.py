@@ -142,7 +142,7 @@ def test_unmutated_oracle_passes_every_pin():
     # tanh softcap without the outer factor
     ("return cap * np.tanh(score / cap)", "return np.tanh(score / cap)", "loop"),
     # full-tile threshold off by one element
-    ("counts == block * block", "counts >= block * block - 1", "brute_causal"),
+    ("counts == kblk * qblk", "counts >= kblk * qblk - 1", "brute_causal"),
     # tail tiles dropped from the count
     ("padded[:KV_LEN] = per_col", "padded[:KV_LEN - 1] = per_col[:-1]", "brute_causal"),
     # sink term lost

@@ -511,3 +511,15 @@ def test_composite_mask_reduces_to_the_fixed_kinds():
     for a, b in pairs:
         assert np.array_equal(np.broadcast_to(a(0, 0, q, kv), (L_, L_)),
                               np.broadcast_to(b(0, 0, q, kv), (L_, L_)))
+
+
+@pytest.mark.parametrize("kind", list(SCALAR_MASKS))
+@pytest.mark.parametrize("kblk,qblk", [(16, 8), (8, 24), (32, 16)])
+def test_block_mask_non_square_brute_force(kind, kblk, qblk):
+    """Non-square tiles (page "tensorplay.nn.attention API": BLOCK_SIZE may be
+    the tuple (KV_BLOCK_SIZE, Q_BLOCK_SIZE)) against the per-element loop."""
+    q_len, kv_len = 77, 50
+    doc = W.document_ids([5, 1, 20, 13, 61])[:max(q_len, kv_len)]
+    bm = oracle.create_block_mask(_oracle_mask(kind, doc), 1, 1, q_len, kv_len, (kblk, qblk))
+    cls = pins.brute_force_tiles(SCALAR_MASKS[kind](doc), 1, 1, q_len, kv_len, kblk, qblk)
+    assert pins.block_mask_matches(bm, pins.lists_from_classes(cls))

@@ -250,11 +250,13 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
  * mask_mod on partial tiles only, and accumulates the softmax-weighted sum of
  * V online, never materialising the score matrix.
  *   q     [B][Hq][Q_LEN][D]; k, v [B][Hkv][KV_LEN][D]; same dtype (F32,
- *         BF16 or F16); D in {64, 128}; Hq a multiple of Hkv; query head h reads KV
+ *         BF16 or F16); D in {64, 128}, or 256 for BF16 / F16; Hq a multiple
+ *         of Hkv; query head h reads KV
  *         head h / (Hq / Hkv).
  *   bm    a BlockMask with bm->Q_LEN == Q_LEN, bm->KV_LEN == KV_LEN,
- *         bm->B in {1, B}, bm->H in {1, Hq}, BLOCK_SIZE 128, 256, 384 or 512
- *         (the kernels walk 128 x 128 pieces of larger tiles).
+ *         bm->B in {1, B}, bm->H in {1, Hq}, BLOCK_SIZE (and Q_BLOCK_SIZE)
+ *         128, 256, 384 or 512 (the kernels walk 128 x 128 pieces of larger
+ *         tiles).
  *   out   [B][Hq][Q_LEN][D], same dtype as q (written).
  *   lse   device float [B][Hq][Q_LEN], contiguous (written): natural-log
  *         log-sum-exp of the modified, masked scores of each row.

@@ -447,7 +447,7 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
     if (workspace_bytes < splitkv_bytes(q->B, q->H, q->L, q->D, splits))
       return fail(FLEXATTN_ERR_INVALID_ARG, "%s: workspace of %zu bytes is below the %zu needed",
                   who, workspace_bytes, splitkv_bytes(q->B, q->H, q->L, q->D, splits));
-    if ((long long)q->B * q->H * bm->num_q_blocks * splits > 0x7fffffffLL)
+    if ((long long)q->B * q->H * bm->num_q_blocks * (QBS / fa::kBlock) * splits > 0x7fffffffLL)
       return fail(FLEXATTN_ERR_INVALID_ARG, "%s: too many workgroups for one launch", who);
   }
   fa::FwdLaunch L;

@@ -56,6 +56,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // The 16-bit input element: bf16 (F16 = false) or fp16. Both have the same
 // register and LDS layouts and a 32x32x16 MFMA with fp32 accumulation; P is
@@ -271,6 +272,10 @@ struct Lane {
   int dq;            // document id of this lane's query row (document mask)
   int kofs[D / 16];  // K fragment (row l32 of block 0, k-step ks)
   int vofs[D / 32];  // V transposed-read piece (k-step 0, half 0, d-block db)
+  // 16-row layout (v_mfma_f32_16x16x32): query lane % 16, key group lane / 16
+  int c16, g4;
+  int kofs16[D / 32];  // K fragment (row c16 of block 0, k-step ks: d 32 ks + 8 g4)
+  int vofs16[D / 16];  // V transposed-read piece (rows 4 g4 + c16 / 4, d-block db)
 
   __device__ void init_offsets() {
 #pragma unroll
@@ -281,6 +286,19 @@ struct Lane {
     for (int db = 0; db < D / 32; ++db) {
       const int d = 32 * db + 16 * vg + 4 * (vi & 3);
       vofs[db] = row * D + swz_v<D>(row, d >> 3) * 8 + (d & 7);
+    }
+  }
+
+  // 16-row layout: the swizzles only XOR row bits that adding 16 (K) or
+  // 16 / 32 (V) rows leaves alone, so one offset per k-step and d-block
+  __device__ void init_offsets16() {
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) kofs16[ks] = c16 * D + swz<D>(c16, 4 * ks + g4) * 8;
+    const int row = 4 * g4 + (c16 >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const int d = 16 * db + 4 * (c16 & 3);
+      vofs16[db] = row * D + swz_v<D>(row, d >> 3) * 8 + (d & 7);
     }
   }
 };
@@ -464,12 +482,179 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
       o[db] = Elem<F16>::mfma(v_frag<D, F16>(sV, ln, ks, db), pf[ks], o[db]);
 }
 
+// ---------------------------------------------------------------------------
+// 16-row step (query tiles of at most 16 rows, such as decode): per wave one
+// query head of 16 rows, v_mfma_f32_16x16x32 for both products, so no MFMA
+// rows are idle. Result layout: register r of lane l holds row 4*(l/16) + r,
+// column l%16; operand slot t of lane l holds k = 8*(l/16) + t. S^T = K.Q^T
+// puts keys 16*blk + 4*g4 + r of the step on the lane's registers (query
+// c16); in the P.V contraction slot t of pair j stands for key
+// 32*j + 16*(t/4) + 4*g4 + t%4, and V^T is read in that order.
+// ---------------------------------------------------------------------------
+template <int D, bool F16>
+__device__ __forceinline__ typename Elem<F16>::V8 k_frag16(const u16* sK, const Lane<D>& ln,
+                                                           int ks, int blk) {
+  return as_v8<F16>(*reinterpret_cast<const uint4*>(sK + ln.kofs16[ks] + 16 * blk * D));
+}
+
+template <int D, bool F16>
+__device__ __forceinline__ typename Elem<F16>::V8 v_frag16(const u16* sV, const Lane<D>& ln, int j,
+                                                           int db) {
+  typename Elem<F16>::V4 part[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const u16* src = sV + ln.vofs16[db] + (32 * j + 16 * ht) * D;
+    const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(src));
+    __builtin_memcpy(&part[ht], &raw, 8);
+  }
+  return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16(typename Elem<F16>::V8 a, typename Elem<F16>::V8 b,
+                                        f32x4 c) {
+  if constexpr (F16) return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Logit of score r of 16-key block blk (key kv0 + 16*blk + 4*g4 + r).
+template <int D, int MASK, int SCORE, bool MASKED>
+__device__ __forceinline__ float elem_logit16(float x, int blk, int r, int kv0,
+                                              const MaskLimits& ml, const int* step_doc,
+                                              const FwdArgs& a, const Lane<D>& ln) {
+  float y = x;
+  const int c = 16 * blk + r;  // offset within the step, without 4*g4
+  if constexpr (SCORE == SCORE_SCALED) {
+    y = x * a.c_scale;
+  } else if constexpr (SCORE != SCORE_NONE) {
+    const int key = kv0 + c + 4 * ln.g4;
+    y = ScoreMod<SCORE>::apply(x, a.c_scale, a.c_cap, a.cap2, ln.slope2, (float)(key - ln.q));
+  }
+  if constexpr (MASKED) {
+    bool ok = c <= ml.hi;
+    if constexpr (MASK == MASK_SLIDING_SINK) ok = ok && (c > ml.win_lo || c < ml.sink_hi);
+    if constexpr (MASK == MASK_DOCUMENT) ok = ok && step_doc[c + 4 * ln.g4] == ln.dq;
+    if constexpr (MASK == MASK_COMPOSITE) {
+      bool any = false;
+#pragma unroll
+      for (int t = 0; t < kMaxTerms; ++t) {
+        bool in = c >= ml.tlo[t] && c <= ml.thi[t];
+        if (a.mp.terms[t] & PRIM_DOCUMENT) in = in && step_doc[c + 4 * ln.g4] == ln.dq;
+        any = any || in;
+      }
+      ok = ok && any;
+    }
+    y = ok ? y : -INFINITY;
+  }
+  return y;
+}
+
+template <int D, int MASK, int SCORE, bool MASKED, int NDMA, bool F16, typename DMA>
+__device__ __forceinline__ void step16(f32x4 (&o)[D / 16], float& m_ref, float& l,
+                                       const typename Elem<F16>::V8 (&qf)[D / 16], const u16* sK,
+                                       const u16* sV, int kv0, const int* step_doc,
+                                       const FwdArgs& a, const Lane<D>& ln, DMA&& dma) {
+  constexpr int NK = Geom<D>::NK;
+  constexpr int NB = NK / 16;  // 16-key blocks per step
+  constexpr int KS = D / 32;   // S k-steps
+  constexpr int DB = D / 16;   // O d-blocks
+  f32x4 s[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) s[b] = f32x4{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      s[b] = mfma16<F16>(k_frag16<D, F16>(sK, ln, ks, b), qf[ks], s[b]);
+      constexpr int NS = KS * NB;
+      static_assert(NS % NDMA == 0, "loads spread evenly");
+      const int i = ks * NB + b;
+      if (i % (NS / NDMA) == 0) dma(i / (NS / NDMA));
+    }
+
+  // the mask limits relative to key kv0 + 4*g4
+  MaskLimits ml;
+  {
+    const int base = kv0 + 4 * ln.g4;
+    ml.hi = a.KV_LEN - 1 - base;
+    if constexpr (MASK == MASK_PREFIX_LM) ml.hi = min(ml.hi, max(ln.qc, a.mp.prefix - 1) - base);
+    else if constexpr (MASK != MASK_NOOP && MASK != MASK_COMPOSITE) ml.hi = min(ml.hi, ln.qc - base);
+    ml.win_lo = ln.qc - base - a.mp.window;
+    ml.sink_hi = a.mp.sinks - base;
+    if constexpr (MASK == MASK_COMPOSITE) {
+#pragma unroll
+      for (int t = 0; t < kMaxTerms; ++t) {
+        int lo = 1, hi = 0;
+        if (t < a.mp.nterms) {
+          term_interval(a.mp.terms[t], ln.qc, a.mp, lo, hi);
+          hi = min(hi, a.KV_LEN - 1) - base;
+          lo -= base;
+        }
+        ml.tlo[t] = lo;
+        ml.thi[t] = hi;
+      }
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s[b][r] = elem_logit16<D, MASK, SCORE, MASKED>(s[b][r], b, r, kv0, ml, step_doc, a, ln);
+      mx = fmaxf(mx, s[b][r]);
+    }
+  // a query's keys are spread over lanes c16, c16 + 16, c16 + 32, c16 + 48
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if constexpr (SCORE == SCORE_NONE) mx *= a.c_scale;  // c_scale > 0 here
+
+  if (__any(mx > m_ref + kRescaleSlack)) {
+    asm volatile("");
+    const float m_new = fmaxf(m_ref, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_ref - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[i][r] *= alpha;
+    m_ref = m_new;
+  }
+  const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+
+  typename Elem<F16>::V8 pf[NB / 2];
+  float rs = 0.0f;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float y = s[b][r];
+      float p;
+      if constexpr (SCORE == SCORE_NONE) {
+        p = fast_exp2(fmaf(y, a.c_scale, -m_use));
+      } else {
+        p = fast_exp2(y - m_use);
+      }
+      rs += p;
+      pf[b >> 1][4 * (b & 1) + r] = (typename Elem<F16>::T)p;
+    }
+  l += rs;  // this lane's keys; the four lanes of a query are summed at the end
+
+#pragma unroll
+  for (int j = 0; j < NB / 2; ++j)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      o[db] = mfma16<F16>(v_frag16<D, F16>(sV, ln, j, db), pf[j], o[db]);
+}
+
 // HEADS query heads that share one KV head (and one BlockMask row) per
 // workgroup: 4 * HEADS waves read the same K/V step blocks, so HEADS = 2
 // halves the global->LDS traffic per flop. Two waves per SIMD either way.
 // D = 256 holds 128 accumulator and 64 Q registers per lane: one workgroup
 // per CU, with the accumulators in the matrix-core registers.
-template <int D, int MASK, int SCORE, int HEADS, bool PAGED, bool F16>
+// R16: the 16-row step for query tiles of at most 16 rows (one query head
+// per wave, 4 heads of a KV group per workgroup).
+template <int D, int MASK, int SCORE, int HEADS, bool PAGED, bool F16, bool R16>
 __global__ __launch_bounds__(64 * kWavesPerHead * HEADS, (D > 128) ? 1 : 2 / HEADS) void
 fwd_bf16_kernel(FwdArgs a) {
   using E = Elem<F16>;
@@ -530,14 +715,17 @@ fwd_bf16_kernel(FwdArgs a) {
   ln.hh = ln.lane >> 5;
   ln.vg = (ln.lane >> 4) & 1;
   ln.vi = ln.lane & 15;
-  ln.q = q_tile0 + (wave % wph) * 32 + ln.l32;
+  ln.c16 = ln.lane & 15;
+  ln.g4 = ln.lane >> 4;
+  ln.q = R16 ? q_tile0 + ln.c16 : q_tile0 + (wave % wph) * 32 + ln.l32;
   const bool qvalid = ln.q < a.Q_LEN;
   ln.qc = qvalid ? ln.q : a.Q_LEN - 1;
   // document ids (COMPOSITE: only when a term tests documents)
   const int* doc_row =
       (mask_uses_doc(MASK) && a.mp.doc) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
   ln.dq = doc_row ? doc_row[ln.qc] : 0;
-  ln.init_offsets();
+  if constexpr (R16) ln.init_offsets16();
+  else ln.init_offsets();
   ln.slope2 = 0.0f;
   if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
     ln.slope2 = alibi_slope(a.slopes, h, a.Hq) * kLog2e;
@@ -608,11 +796,16 @@ fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  f32x16 o[G::DB];
+  f32x16 o[R16 ? 1 : G::DB];  // O^T accumulators, 32-row layout
+  f32x4 o16[R16 ? D / 16 : 1];  // 16-row layout
 #pragma unroll
-  for (int i = 0; i < G::DB; ++i)
+  for (int i = 0; i < (R16 ? 1 : G::DB); ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < (R16 ? D / 16 : 1); ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o16[i][r] = 0.0f;
   float m_ref = -INFINITY;
   float l = 0.0f;
 
@@ -631,9 +824,15 @@ fwd_bf16_kernel(FwdArgs a) {
     typename E::V8 qf[G::KS];
     {
       const u16* qrow = a.q + b * a.sq0 + h * a.sq1 + (long long)ln.qc * a.sq2;
+      if constexpr (R16) {
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks)
-        qf[ks] = as_v8<F16>(*reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * ln.hh));
+        for (int ks = 0; ks < D / 32; ++ks)
+          qf[ks] = as_v8<F16>(*reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * ln.g4));
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks)
+          qf[ks] = as_v8<F16>(*reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * ln.hh));
+      }
     }
     wait_loads_and_sync();
 
@@ -670,8 +869,14 @@ fwd_bf16_kernel(FwdArgs a) {
           if (i < KPW) kload.issue_one(krs, k_lds[nb], i);
           else vload.issue_one(vrs, v_lds[nb], i - KPW);
         };
-        step<D, MASK, SCORE, M, 2 * KPW, F16>(o, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
-                                mask_uses_doc(MASK) ? docbuf + cur * DOC_STRIDE : nullptr, a, ln, dma);
+        if constexpr (R16)
+          step16<D, MASK, SCORE, M, 2 * KPW, F16>(
+              o16, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
+              mask_uses_doc(MASK) ? docbuf + cur * DOC_STRIDE : nullptr, a, ln, dma);
+        else
+          step<D, MASK, SCORE, M, 2 * KPW, F16>(
+              o, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
+              mask_uses_doc(MASK) ? docbuf + cur * DOC_STRIDE : nullptr, a, ln, dma);
         kv0 = kv_nxt;
         ++g;
         wait_loads_and_sync();
@@ -687,6 +892,44 @@ fwd_bf16_kernel(FwdArgs a) {
     int j = t_begin;
     for (; j < min(nfull_fast, t_end); ++j) run_tile(std::false_type{});
     for (; j < t_end; ++j) run_tile(std::true_type{});
+  }
+
+  if constexpr (R16) {
+    // 16-row epilogue: a query's row sum is spread over four lanes; lane
+    // holds O^T rows 16*db + 4*g4 + r of query c16
+    const float l1 = l + __shfl_xor(l, 16, 64);
+    const float l_tot16 = l1 + __shfl_xor(l1, 32, 64);
+    const float inv16 = l_tot16 > 0.0f ? 1.0f / l_tot16 : 0.0f;
+    const float lse2 = l_tot16 > 0.0f ? (m_ref + fast_log2(l_tot16)) * kLn2 : -INFINITY;
+    if (!qvalid) return;
+    auto put_f32 = [&](float* orow) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        float4 v4;
+        v4.x = o16[db][0] * inv16;
+        v4.y = o16[db][1] * inv16;
+        v4.z = o16[db][2] * inv16;
+        v4.w = o16[db][3] * inv16;
+        *reinterpret_cast<float4*>(orow + 16 * db + 4 * ln.g4) = v4;
+      }
+    };
+    if (a.splits > 1) {
+      const long long row = (((long long)split * a.B + b) * a.Hq + h) * a.Q_LEN + ln.q;
+      put_f32(a.part_o + row * D);
+      if (ln.g4 == 0) a.part_lse[row] = lse2;
+      return;
+    }
+    if (a.o32) put_f32(a.o32 + (((long long)b * a.Hq + h) * a.Q_LEN + ln.q) * D);
+    u16* orow = a.o + b * a.so0 + h * a.so1 + (long long)ln.q * a.so2;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      typename E::V4 pk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pk[j] = (typename E::T)(o16[db][j] * inv16);
+      *reinterpret_cast<typename E::V4*>(orow + 16 * db + 4 * ln.g4) = pk;
+    }
+    if (ln.g4 == 0) a.lse[((long long)b * a.Hq + h) * a.Q_LEN + ln.q] = lse2;
+    return;
   }
 
   // epilogue: O = O_acc / l, LSE = ln(sum) + max
@@ -746,7 +989,7 @@ fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int MASK, int SCORE, int HEADS, bool PAGED, bool F16>
+template <int D, int MASK, int SCORE, int HEADS, bool PAGED, bool F16, bool R16>
 hipError_t launch_one(const FwdArgs& args, int grid, hipStream_t stream) {
   const int nlist = args.bm.NKB * (args.bm.BS / kBlock);
   const int lds = 4 * ((nlist + 3) & ~3) * (PAGED ? 2 : 1);
@@ -759,55 +1002,57 @@ hipError_t launch_one(const FwdArgs& args, int grid, hipStream_t stream) {
   if (e != hipSuccess) return e;
   if (dev >= kMaxDevices || lds > attr_bytes[dev].load(std::memory_order_relaxed)) {
     e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&fwd_bf16_kernel<D, MASK, SCORE, HEADS, PAGED, F16>),
+        reinterpret_cast<const void*>(&fwd_bf16_kernel<D, MASK, SCORE, HEADS, PAGED, F16, R16>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     if (dev < kMaxDevices) attr_bytes[dev].store(lds, std::memory_order_relaxed);
   }
-  fwd_bf16_kernel<D, MASK, SCORE, HEADS, PAGED, F16><<<grid, 64 * kWavesPerHead * HEADS, lds, stream>>>(args);
+  fwd_bf16_kernel<D, MASK, SCORE, HEADS, PAGED, F16, R16><<<grid, 64 * kWavesPerHead * HEADS, lds, stream>>>(args);
   return hipGetLastError();
 }
 
-template <int D, int MASK, int HEADS, bool PAGED, bool F16>
+template <int D, int MASK, int HEADS, bool PAGED, bool F16, bool R16>
 hipError_t dispatch_score(const FwdArgs& args, int score, int grid, hipStream_t stream) {
   switch (score) {
     case SCORE_NONE:
-      return launch_one<D, MASK, SCORE_NONE, HEADS, PAGED, F16>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_NONE, HEADS, PAGED, F16, R16>(args, grid, stream);
     case SCORE_ALIBI:
-      return launch_one<D, MASK, SCORE_ALIBI, HEADS, PAGED, F16>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_ALIBI, HEADS, PAGED, F16, R16>(args, grid, stream);
     case SCORE_SOFTCAP:
-      return launch_one<D, MASK, SCORE_SOFTCAP, HEADS, PAGED, F16>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_SOFTCAP, HEADS, PAGED, F16, R16>(args, grid, stream);
     case SCORE_SOFTCAP_ALIBI:
-      return launch_one<D, MASK, SCORE_SOFTCAP_ALIBI, HEADS, PAGED, F16>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_SOFTCAP_ALIBI, HEADS, PAGED, F16, R16>(args, grid, stream);
     default:
-      return launch_one<D, MASK, SCORE_SCALED, HEADS, PAGED, F16>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_SCALED, HEADS, PAGED, F16, R16>(args, grid, stream);
   }
 }
 
-template <int D, int HEADS, bool PAGED, bool F16>
+template <int D, int HEADS, bool PAGED, bool F16, bool R16>
 hipError_t dispatch_mask(const FwdArgs& args, int mask, int score, int grid, hipStream_t stream) {
   switch (mask) {
     case MASK_NOOP:
-      return dispatch_score<D, MASK_NOOP, HEADS, PAGED, F16>(args, score, grid, stream);
+      return dispatch_score<D, MASK_NOOP, HEADS, PAGED, F16, R16>(args, score, grid, stream);
     case MASK_CAUSAL:
-      return dispatch_score<D, MASK_CAUSAL, HEADS, PAGED, F16>(args, score, grid, stream);
+      return dispatch_score<D, MASK_CAUSAL, HEADS, PAGED, F16, R16>(args, score, grid, stream);
     case MASK_SLIDING_SINK:
-      return dispatch_score<D, MASK_SLIDING_SINK, HEADS, PAGED, F16>(args, score, grid, stream);
+      return dispatch_score<D, MASK_SLIDING_SINK, HEADS, PAGED, F16, R16>(args, score, grid, stream);
     case MASK_PREFIX_LM:
-      return dispatch_score<D, MASK_PREFIX_LM, HEADS, PAGED, F16>(args, score, grid, stream);
+      return dispatch_score<D, MASK_PREFIX_LM, HEADS, PAGED, F16, R16>(args, score, grid, stream);
     case MASK_COMPOSITE:
-      return dispatch_score<D, MASK_COMPOSITE, HEADS, PAGED, F16>(args, score, grid, stream);
+      return dispatch_score<D, MASK_COMPOSITE, HEADS, PAGED, F16, R16>(args, score, grid, stream);
     default:
-      return dispatch_score<D, MASK_DOCUMENT, HEADS, PAGED, F16>(args, score, grid, stream);
+      return dispatch_score<D, MASK_DOCUMENT, HEADS, PAGED, F16, R16>(args, score, grid, stream);
   }
 }
 
 template <int D, bool PAGED, bool F16>
-hipError_t dispatch_heads(const FwdArgs& args, int heads, int mask, int score, int grid,
+hipError_t dispatch_heads(const FwdArgs& args, int heads, bool r16, int mask, int score, int grid,
                           hipStream_t stream) {
   if constexpr (!PAGED && !F16 && D <= 128)
-    if (heads == 2) return dispatch_mask<D, 2, false, false>(args, mask, score, grid, stream);
-  return dispatch_mask<D, 1, PAGED, F16>(args, mask, score, grid, stream);
+    if (heads == 2) return dispatch_mask<D, 2, false, false, false>(args, mask, score, grid, stream);
+  if constexpr (D <= 128)
+    if (r16) return dispatch_mask<D, 1, PAGED, F16, true>(args, mask, score, grid, stream);
+  return dispatch_mask<D, 1, PAGED, F16, false>(args, mask, score, grid, stream);
 }
 
 // Merge of the split-KV slices, one 64-lane wave per query row: with the
@@ -926,6 +1171,12 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
         a.wph = w;
         break;
       }
+  // At most 16 query rows per head: the 16-row MFMA step (half the matrix
+  // work of a 32-row step that would carry 16 empty rows).
+  // FLEXATTN_R16=0 keeps the 32-row step.
+  bool r16 = a.wph == 1 && L.Q_LEN <= 16 && L.D <= 128;
+  if (const char* env = getenv("FLEXATTN_R16"))
+    if (env[0] == '0') r16 = false;
   const int hpw = heads * kWavesPerHead / a.wph;  // query heads per workgroup
   // XCD-aware order: with the mask broadcast over batch and heads every
   // schedule round holds the B*Hq/hpw items of one query tile; split each
@@ -937,9 +1188,9 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   // the unscaled fast path takes the row max before scaling: scale must be > 0
   const int score = (L.score_kind == SCORE_NONE && !(L.scale > 0.0f)) ? SCORE_SCALED : L.score_kind;
-  hipError_t e = (L.D == 256) ? dispatch_heads<256, PAGED, F16>(a, heads, L.mask_kind, score, grid, stream)
-               : (L.D == 128) ? dispatch_heads<128, PAGED, F16>(a, heads, L.mask_kind, score, grid, stream)
-                              : dispatch_heads<64, PAGED, F16>(a, heads, L.mask_kind, score, grid, stream);
+  hipError_t e = (L.D == 256) ? dispatch_heads<256, PAGED, F16>(a, heads, r16, L.mask_kind, score, grid, stream)
+               : (L.D == 128) ? dispatch_heads<128, PAGED, F16>(a, heads, r16, L.mask_kind, score, grid, stream)
+                              : dispatch_heads<64, PAGED, F16>(a, heads, r16, L.mask_kind, score, grid, stream);
   if (e != hipSuccess || a.splits == 1) return e;
   const long long rows = (long long)L.B * L.Hq * L.Q_LEN;
   const unsigned blocks = (unsigned)((rows + 3) / 4);

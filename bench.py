@@ -117,7 +117,20 @@ def cpu_baseline(w: W.Workload, inp: W.Inputs, budget_s: float = 20.0):
                       f"fp64 NumPy, {dt:.1f} s"}
 
 
-def decode_leg(fa, torch, dev, stream, steps: int):
+def settle(torch, fn, ms: float):
+    """Untimed calls of fn for at least ms of wall time: a leg that follows
+    host-side input generation starts on an idle GPU, whose clock climbs over
+    the first tens of milliseconds of load."""
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            return
+
+
+def decode_leg(fa, torch, dev, stream, steps: int, settle_ms: float):
     """Split-KV forward on the decode workload (few queries, long KV): HBM
     bound, so reported as bytes moved per second against the HBM peak. Its
     inputs are freed before returning."""
@@ -136,8 +149,7 @@ def decode_leg(fa, torch, dev, stream, steps: int):
     def call():
         fa.flex_attention(q, k, v, bm, scale=w.scale, out=out, lse=lse, stream=stream,
                           num_splits=splits, workspace=ws)
-    for _ in range(5):
-        call()
+    settle(torch, call, settle_ms)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
         ev[i][0].record(stream)
@@ -166,8 +178,7 @@ def decode_leg(fa, torch, dev, stream, steps: int):
     def call_paged():
         fa.flex_attention(q, kc, vc, bm, scale=w.scale, out=out, lse=lse, stream=stream,
                           num_splits=splits, workspace=ws, page_table=table)
-    for _ in range(5):
-        call_paged()
+    settle(torch, call_paged, settle_ms)
     for i in range(steps):
         ev[i][0].record(stream)
         call_paged()
@@ -293,9 +304,9 @@ def main(argv=None):
         bm_all = fa.create_block_mask(w.mask, 1, 1, w.Q_LEN, w.KV_LEN, 128, window=w.window,
                                       num_sinks=w.sinks, doc_ids=doc, device=dev, stream=stream,
                                       separate_full_blocks=False)
-        for _ in range(3):
-            fa.flex_attention(q, k, v, bm_all, score=w.score, softcap=w.softcap, scale=w.scale,
-                              out=out, lse=lse, stream=stream)
+        settle(torch, lambda: fa.flex_attention(q, k, v, bm_all, score=w.score,
+                                                softcap=w.softcap, scale=w.scale, out=out,
+                                                lse=lse, stream=stream), args.settle_ms)
         ev_a = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
                 for _ in range(args.ablation_steps)]
         for i in range(args.ablation_steps):
@@ -323,10 +334,9 @@ def main(argv=None):
                           out=out, lse=lse, stream=stream)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-        for _ in range(2):
-            fa.flex_attention_backward(q, k, v, lse, g, bm_b, score=w.score, softcap=w.softcap,
-                                       scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws,
-                                       stream=stream)
+        settle(torch, lambda: fa.flex_attention_backward(
+            q, k, v, lse, g, bm_b, score=w.score, softcap=w.softcap, scale=w.scale, dq=dq, dk=dk,
+            dv=dv, workspace=ws, stream=stream), args.settle_ms)
         ev_b = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
                 for _ in range(args.backward_steps)]
         for i in range(args.backward_steps):
@@ -370,9 +380,9 @@ def main(argv=None):
         out16 = torch.empty_like(q16)
         bm16 = fa.create_block_mask(w.mask, 1, 1, w.Q_LEN, w.KV_LEN, 128, window=w.window,
                                     num_sinks=w.sinks, doc_ids=doc, device=dev, stream=stream)
-        for _ in range(3):
-            fa.flex_attention(q16, k16, v16, bm16, score=w.score, softcap=w.softcap,
-                              scale=w.scale, out=out16, lse=lse, stream=stream)
+        settle(torch, lambda: fa.flex_attention(q16, k16, v16, bm16, score=w.score,
+                                                softcap=w.softcap, scale=w.scale, out=out16,
+                                                lse=lse, stream=stream), args.settle_ms)
         ev_h = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
                 for _ in range(args.f16_steps)]
         for i in range(args.f16_steps):
@@ -387,7 +397,7 @@ def main(argv=None):
 
     decode = None
     if args.decode_steps > 0:
-        decode = decode_leg(fa, torch, dev, stream, args.decode_steps)
+        decode = decode_leg(fa, torch, dev, stream, args.decode_steps, args.settle_ms)
 
     pairs = allowed_pairs_per_head(w, inp.doc_lengths)
     eff_flops = 4.0 * w.D * pairs * w.B * w.Hq

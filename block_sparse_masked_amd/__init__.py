@@ -389,10 +389,12 @@ def _tensor(t: torch.Tensor, name: str) -> _Tensor:
 
 
 def auto_splits(q: torch.Tensor, k: torch.Tensor, block_mask: BlockMask,
-                target_workgroups: int = 1024) -> int:
-    """Split count for a bf16 call: enough workgroups to fill the chip
-    (target_workgroups, four per CU) when there are few query tiles, at most
-    the number of KV tiles a row can list, and 1 (no split) otherwise."""
+                target_workgroups: int = 512) -> int:
+    """Split count for a bf16 call: enough workgroups to fill the chip once
+    (target_workgroups, two per CU, the forward's occupancy) when there are
+    few query tiles, at most the number of KV tiles a row can list, and 1 (no
+    split) otherwise. Measured on the decode shape (64 items): 8 slices (512
+    workgroups) beat 16 (two rounds) and the 10 and 12 of a ragged round."""
     if q.dtype not in (torch.bfloat16, torch.float16):
         return 1
     B, Hq, M = q.shape[0], q.shape[1], q.shape[2]

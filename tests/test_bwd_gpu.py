@@ -366,6 +366,35 @@ def test_training_pair_fp32_out_delta(lib, D, mask, score):
         check(t.float().cpu().numpy().astype(np.float64), r, n, ex)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask,score", [("causal", "softcap_alibi"), ("sliding_sink", "alibi"),
+                                        ("document_causal", "none")])
+@pytest.mark.parametrize("q_len", [5, 16])
+def test_training_pair_short_queries(lib, D, mask, score, q_len):
+    """At most 16 query rows with four query heads per KV head: the forward
+    runs the 16-row step, whose fp32 O feeds Delta; the gradients meet the
+    same bound against the oracle."""
+    w = tiny(D, mask, score, Hq=8, Hkv=2, Q_LEN=q_len, KV_LEN=700, window=200,
+             value_scale=2.0 if "softcap" in score else 1.0)
+    inp = W.generate(w)
+    d_out = W.generate_upstream(w)
+    bm = mask_of(lib, w, inp)
+    q, k, v = (G.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    g = G.to_device(d_out, "bf16")
+    o1, l1 = lib.flex_attention(q, k, v, bm, score=w.score, softcap=w.softcap, scale=w.scale)
+    o2, l2, o32 = lib.flex_attention_train(q, k, v, bm, score=w.score, softcap=w.softcap,
+                                           scale=w.scale)
+    dq, dk, dv = lib.flex_attention_backward(q, k, v, l2, g, bm, score=w.score,
+                                             softcap=w.softcap, scale=w.scale, out_f32=o32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o32.to(torch.bfloat16), o2)
+    ref = oracle_bwd(w, inp, d_out)
+    ex_q, ex_k = delta_rounding_terms(w, inp, d_out)
+    for t, r, n, ex in zip((dq, dk, dv), ref, ("dq", "dk", "dv"), (ex_q, ex_k, None)):
+        check(t.float().cpu().numpy().astype(np.float64), r, n, ex)
+
+
 def test_training_pair_dense_causal_sampled(lib):
     """The dense causal workload's shapes through the training pair: dQ rows
     of two heads against the oracle."""

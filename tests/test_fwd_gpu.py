@@ -41,27 +41,35 @@ def check_full(lib, w, B_mask=1, H_mask=1):
     return res
 
 
+TINY_MASKS = ["noop", "causal", "sliding_sink", "document_causal", "prefix_lm"]
+TINY_SCORES = ["none", "alibi", "softcap", "softcap_alibi"]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal",
-                                  "prefix_lm"])
-@pytest.mark.parametrize("score", ["none", "alibi", "softcap", "softcap_alibi"])
-@pytest.mark.parametrize("heads", ["auto", "2"])
-def test_fwd_tiny_grid(lib, dtype, D, mask, score, heads, monkeypatch):
+@pytest.mark.parametrize("mask", TINY_MASKS)
+@pytest.mark.parametrize("score", TINY_SCORES)
+def test_fwd_tiny_grid(lib, dtype, D, mask, score):
     """Every dtype x head dim x mask x score kind, with GQA, 3 query tiles and a
     ragged tail (300 = 2*128 + 44). bf16 softcap cases scale the inputs by 2
     (cap 20); fp32 cases keep unit-variance inputs, where the 1e-5 bound is
     stated, and use cap 2 so tanh is far from linear. fp16 runs the 16-bit
-    kernel with fp16 MFMA under the bf16 bounds. heads="2" runs the bf16
-    kernel with the two query heads of a KV group in one workgroup."""
-    if heads == "2":
-        if dtype != "bf16":
-            pytest.skip("the head-pair workgroup is a bf16 kernel variant")
-        monkeypatch.setenv("FLEXATTN_BF16_HEADS", "2")
+    kernel with fp16 MFMA under the bf16 bounds."""
     if dtype == "f32":
         w = tiny(dtype, D, mask, score, softcap=2.0)
     else:
         w = tiny(dtype, D, mask, score, value_scale=2.0 if "softcap" in score else 1.0)
+    check_full(lib, w)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", TINY_MASKS)
+@pytest.mark.parametrize("score", TINY_SCORES)
+def test_fwd_tiny_grid_head_pairs(lib, D, mask, score, monkeypatch):
+    """The bf16 grid again with FLEXATTN_BF16_HEADS=2: the two query heads of
+    a KV group in one 8-wave workgroup (a bf16 kernel variant)."""
+    monkeypatch.setenv("FLEXATTN_BF16_HEADS", "2")
+    w = tiny("bf16", D, mask, score, value_scale=2.0 if "softcap" in score else 1.0)
     check_full(lib, w)
 
 

@@ -75,8 +75,11 @@ def test_block_size_forward(lib, block, dtype, D, kind):
 
 @pytest.mark.parametrize("block", [256, 384])
 @pytest.mark.parametrize("splits", [1, 3])
-def test_block_size_split_and_paged(lib, block, splits):
-    w = tiny("bf16", 128, "sliding_sink", "alibi", B=2, Hq=8, Hkv=2, Q_LEN=40, KV_LEN=1700,
+@pytest.mark.parametrize("q_len", [40, 12])
+def test_block_size_split_and_paged(lib, block, splits, q_len):
+    """Q_LEN = 12 runs the 16-row step; the other 128-row pieces of the
+    query tile lie past Q_LEN and exit at once."""
+    w = tiny("bf16", 128, "sliding_sink", "alibi", B=2, Hq=8, Hkv=2, Q_LEN=q_len, KV_LEN=1700,
              window=600, sinks=3)
     inp = W.generate(w)
     bm = build(lib, w, inp, block)

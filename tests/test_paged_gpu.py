@@ -86,3 +86,28 @@ def test_paged_rejections(lib):
         lib.flex_attention(q, k64, k64, bm, page_table=table)
     with pytest.raises(NotImplementedError, match="bf16"):
         lib.flex_attention(q.float(), kc.float(), vc.float(), bm, page_table=table)
+
+
+def test_paged_decode_workload_sampled(lib):
+    """The decode workload at full size (B=8, Hq=32, Hkv=8, 16 queries, 32768
+    keys) read through a paged cache (pages of 256 keys at a seeded random
+    placement) with the automatic split count: sampled heads against the
+    oracle on the contiguous keys the pages hold."""
+    w = W.DECODE_GQA
+    inp = W.generate(w)
+    kc, vc, table = W.paged_cache(inp.k, inp.v, 256, seed=w.seed)
+    for b, j in ((0, 0), (5, 77), (7, 127)):  # a few pages hold the sequence's keys
+        assert np.array_equal(kc[table[b, j], :, :], inp.k[b, :, 256 * j:256 * j + 256])
+    q = G.to_device(inp.q, "bf16")
+    kd, vd = G.to_device(kc, "bf16"), G.to_device(vc, "bf16")
+    del kc, vc
+    bm = G.build_gpu_mask(lib, w, inp)
+    out, lse = lib.flex_attention(q, kd, vd, bm, scale=w.scale, num_splits=None,
+                                  page_table=torch.from_numpy(table).cuda())
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    l_ = lse.cpu().numpy().astype(np.float64)
+    for b, h in ((0, 0), (4, 9), (7, 31)):
+        o_ref, lse_ref = G.oracle_rows(w, inp, batches=[b], heads=[h])
+        res = G.compare(w, o, l_, o_ref, lse_ref)
+        assert res["ok"] and res["n_rows"] == w.Q_LEN, G.summary(res)

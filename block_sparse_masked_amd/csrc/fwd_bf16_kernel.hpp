@@ -22,6 +22,13 @@
 // exchange with lane ^ 32, the P^T operand is the converted score registers
 // and the O^T accumulator is rescaled per lane.
 //
+// Short query tiles (Q_LEN <= 64, mask broadcast over heads) give each query
+// head one or two waves and fill the workgroup with 4 or 2 heads of one KV
+// group, which then share the K/V stream. With one wave per head and at most
+// 16 query rows, both products use v_mfma_f32_16x16x32_bf16 instead (the
+// 16-row step: lane l holds query l % 16, lane group l / 16 a quarter of
+// each 16-key block), so no matrix work goes to empty rows.
+//
 // MFMA 32x32 result layout: register r of lane l holds row
 // 8*(r/4) + 4*(l/32) + r%4 and column l%32. An operand register slot t of
 // lane l holds k = 8*(l/32) + t for both A and B, so the key order inside the

@@ -408,7 +408,14 @@ def auto_splits(q: torch.Tensor, k: torch.Tensor, block_mask: BlockMask,
             if M <= 32 * wph and group % (4 // wph) == 0:
                 heads_per_wg = 4 // wph
                 break
-    items = B * (Hq // heads_per_wg) * block_mask.num_q_blocks * (block_mask.q_block // 128)
+        else:
+            # no exact packing: packs with a partial last one per KV group
+            wph = 1 if M <= 32 else 2
+            if 2 * group > 4 // wph:
+                heads_per_wg = 4 // wph
+    packs = -(-group // heads_per_wg)  # workgroups per KV group and query tile
+    items = (B * (Hq // group) * packs * block_mask.num_q_blocks
+             * (block_mask.q_block // 128))
     if items >= target_workgroups // 2:
         return 1
     return max(1, min(block_mask.num_kv_blocks, target_workgroups // items, 64))

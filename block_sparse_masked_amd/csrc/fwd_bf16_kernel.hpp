@@ -710,10 +710,15 @@ fwd_bf16_kernel(FwdArgs a) {
   // pairs; one-head workgroups with wph < 4: 4 / wph heads of a KV group)
   const int wph = (HEADS == 1) ? a.wph : kWavesPerHead;
   const int HPW = WAVES / wph;
-  const Item it = decode_item(x, a.bm, a.B, a.Hq / HPW);
+  // a KV group's heads in packs of HPW; when G is not a multiple of HPW the
+  // group's last pack is partial, and its spare waves take the group's last
+  // head, load and synchronise like the others, and store nothing
+  const int gpk = (a.G + HPW - 1) / HPW;  // packs per KV group
+  const Item it = decode_item(x, a.bm, a.B, (a.Hq / a.G) * gpk);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = it.b, h = it.h * HPW + wave / wph;
-  const int hk = (it.h * HPW) / a.G;
+  const int hk = it.h / gpk;
+  const int hlocal = (it.h - hk * gpk) * HPW + wave / wph;
+  const int b = it.b, h = hk * a.G + min(hlocal, a.G - 1);
   const int q_tile0 = it.qb * a.bm.QBS + qsub * kBlock;
   if (q_tile0 >= a.Q_LEN) return;  // a 128-row tile past Q_LEN (BLOCK_SIZE > 128)
   Lane<D> ln;
@@ -725,7 +730,7 @@ fwd_bf16_kernel(FwdArgs a) {
   ln.c16 = ln.lane & 15;
   ln.g4 = ln.lane >> 4;
   ln.q = R16 ? q_tile0 + ln.c16 : q_tile0 + (wave % wph) * 32 + ln.l32;
-  const bool qvalid = ln.q < a.Q_LEN;
+  const bool qvalid = hlocal < a.G && ln.q < a.Q_LEN;  // also gates every store
   ln.qc = qvalid ? ln.q : a.Q_LEN - 1;
   // document ids (COMPOSITE: only when a term tests documents)
   const int* doc_row =
@@ -1178,6 +1183,13 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
         a.wph = w;
         break;
       }
+  // No exact packing (G a multiple of neither 4 nor 2): packs of 4 / waves
+  // heads with a partial last pack per KV group, as long as real heads fill
+  // at least half of a group's slots (G = 3, 5, 7, ...).
+  if (heads == 1 && L.bm.Hm == 1 && L.Q_LEN <= 64 && a.wph == kWavesPerHead) {
+    const int w = L.Q_LEN <= 32 ? 1 : 2;
+    if (2 * a.G > kWavesPerHead / w) a.wph = w;
+  }
   // At most 16 query rows per head: the 16-row MFMA step (half the matrix
   // work of a 32-row step that would carry 16 empty rows).
   // FLEXATTN_R16=0 keeps the 32-row step.
@@ -1186,10 +1198,10 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
     if (env[0] == '0') r16 = false;
   const int hpw = heads * kWavesPerHead / a.wph;  // query heads per workgroup
   // XCD-aware order: with the mask broadcast over batch and heads every
-  // schedule round holds the B*Hq/hpw items of one query tile; split each
-  // round into 8 contiguous chunks of whole KV groups, one per XCD.
-  const int R = L.B * L.Hq / hpw;
-  const int g_items = a.G / hpw;  // items per KV group
+  // schedule round holds the B*Hkv*g_items items of one query tile; split
+  // each round into 8 contiguous chunks of whole KV groups, one per XCD.
+  const int g_items = (a.G + hpw - 1) / hpw;  // items (head packs) per KV group
+  const int R = L.B * (L.Hq / a.G) * g_items;
   a.xcd_round = (L.bm.Bm == 1 && L.bm.Hm == 1 && R % 8 == 0 && (R / 8) % g_items == 0) ? R : 0;
   const int grid = R * L.bm.NQB * (L.bm.QBS / kBlock) * a.splits;
   if (grid == 0) return hipSuccess;

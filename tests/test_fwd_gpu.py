@@ -294,14 +294,16 @@ def test_fwd_decode_workload_sampled(lib):
 
 
 @pytest.mark.parametrize("q_len", [1, 16, 33, 64])
-@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 2), (8, 1), (3, 3)])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 2), (8, 1), (3, 3), (14, 2), (6, 2), (5, 1)])
 @pytest.mark.parametrize("mask,score", [("noop", "alibi"), ("sliding_sink", "softcap_alibi"),
                                         ("prefix_lm", "alibi"), ("causal", "none")])
 @pytest.mark.parametrize("splits", [1, None])
 def test_fwd_short_query_heads_packed(lib, q_len, Hq, Hkv, mask, score, splits):
     """Short query tiles (Q_LEN <= 64) put several query heads of one KV group
     in a workgroup, one or two waves each; ALiBi's per-head slope checks that
-    every wave takes its own head. Group sizes 4, 2, 8 and 1 (no packing)."""
+    every wave takes its own head. Group sizes 4, 2, 8 and 1 (no packing);
+    7, 3 and 5 pack four (or two) heads with a partial last pack per KV
+    group, whose spare waves store nothing."""
     w = tiny("bf16", 128, mask, score, B=2, Hq=Hq, Hkv=Hkv, Q_LEN=q_len, KV_LEN=700,
              window=200, prefix=40, value_scale=2.0 if "softcap" in score else 1.0)
     inp = W.generate(w)

@@ -112,3 +112,16 @@ def test_r16_matches_32_row_step(lib, D, splits, monkeypatch):
     assert torch.equal(torch.isinf(l16), torch.isinf(l32))
     fin = torch.isfinite(l32)
     assert float(((l16 - l32)[fin].abs() / l32[fin].abs().clamp_min(1.0)).max()) < 1e-5
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_ragged_head_packs_paged(lib, D, splits):
+    """Seven query heads per KV head: packs of 4 + 3 on the 16-row step,
+    through a paged cache, with and without slices."""
+    w = tiny("bf16", D, "sliding_sink", "softcap_alibi", B=2, Hq=14, Hkv=2, Q_LEN=16,
+             KV_LEN=1100, window=300, value_scale=2.0)
+    inp = W.generate(w)
+    kc, vc, table = W.paged_cache(inp.k, inp.v, 256, seed=8)
+    out, lse = _run(lib, w, inp, splits, paged=(kc, vc, table))
+    _check(w, inp, out, lse)

@@ -409,8 +409,11 @@ def auto_splits(q: torch.Tensor, k: torch.Tensor, block_mask: BlockMask,
                 heads_per_wg = 4 // wph
                 break
         else:
-            # no exact packing: packs with a partial last one per KV group
+            # no exact packing (head dim <= 128): packs with a partial last
+            # one per KV group
             wph = 1 if M <= 32 else 2
+            if q.shape[-1] > 128:
+                wph = 4
             if 2 * group > 4 // wph:
                 heads_per_wg = 4 // wph
     packs = -(-group // heads_per_wg)  # workgroups per KV group and query tile

@@ -710,15 +710,28 @@ fwd_bf16_kernel(FwdArgs a) {
   // pairs; one-head workgroups with wph < 4: 4 / wph heads of a KV group)
   const int wph = (HEADS == 1) ? a.wph : kWavesPerHead;
   const int HPW = WAVES / wph;
-  // a KV group's heads in packs of HPW; when G is not a multiple of HPW the
-  // group's last pack is partial, and its spare waves take the group's last
-  // head, load and synchronise like the others, and store nothing
-  const int gpk = (a.G + HPW - 1) / HPW;  // packs per KV group
-  const Item it = decode_item(x, a.bm, a.B, (a.Hq / a.G) * gpk);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hk = it.h / gpk;
-  const int hlocal = (it.h - hk * gpk) * HPW + wave / wph;
-  const int b = it.b, h = hk * a.G + min(hlocal, a.G - 1);
+  // D <= 128: a KV group's heads in packs of HPW; when G is not a multiple
+  // of HPW the group's last pack is partial, and its spare waves take the
+  // group's last head, load and synchronise like the others, and store
+  // nothing. D = 256: whole packs only (G a multiple of HPW).
+  Item it;
+  int b, h, hk;
+  bool hvalid = true;
+  if constexpr (D <= 128) {
+    const int gpk = (a.G + HPW - 1) / HPW;  // packs per KV group
+    it = decode_item(x, a.bm, a.B, (a.Hq / a.G) * gpk);
+    hk = it.h / gpk;
+    const int hlocal = (it.h - hk * gpk) * HPW + wave / wph;
+    hvalid = hlocal < a.G;
+    b = it.b;
+    h = hk * a.G + min(hlocal, a.G - 1);
+  } else {
+    it = decode_item(x, a.bm, a.B, a.Hq / HPW);
+    b = it.b;
+    h = it.h * HPW + wave / wph;
+    hk = (it.h * HPW) / a.G;
+  }
   const int q_tile0 = it.qb * a.bm.QBS + qsub * kBlock;
   if (q_tile0 >= a.Q_LEN) return;  // a 128-row tile past Q_LEN (BLOCK_SIZE > 128)
   Lane<D> ln;
@@ -730,7 +743,7 @@ fwd_bf16_kernel(FwdArgs a) {
   ln.c16 = ln.lane & 15;
   ln.g4 = ln.lane >> 4;
   ln.q = R16 ? q_tile0 + ln.c16 : q_tile0 + (wave % wph) * 32 + ln.l32;
-  const bool qvalid = hlocal < a.G && ln.q < a.Q_LEN;  // also gates every store
+  const bool qvalid = hvalid && ln.q < a.Q_LEN;  // also gates every store
   ln.qc = qvalid ? ln.q : a.Q_LEN - 1;
   // document ids (COMPOSITE: only when a term tests documents)
   const int* doc_row =
@@ -1186,7 +1199,7 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
   // No exact packing (G a multiple of neither 4 nor 2): packs of 4 / waves
   // heads with a partial last pack per KV group, as long as real heads fill
   // at least half of a group's slots (G = 3, 5, 7, ...).
-  if (heads == 1 && L.bm.Hm == 1 && L.Q_LEN <= 64 && a.wph == kWavesPerHead) {
+  if (L.D <= 128 && heads == 1 && L.bm.Hm == 1 && L.Q_LEN <= 64 && a.wph == kWavesPerHead) {
     const int w = L.Q_LEN <= 32 ? 1 : 2;
     if (2 * a.G > kWavesPerHead / w) a.wph = w;
   }

@@ -23,6 +23,7 @@ import torch
 __all__ = [
     "BlockMask", "FlexAttnError", "MASK_KINDS", "SCORE_KINDS", "create_block_mask",
     "flex_attention", "flex_attention_backward", "block_mask_from_kv_blocks", "library_path",
+    "auto_splits", "fwd_plan", "flex_attention_train",
     "load_library",
     "block_mask_sizes", "version",
 ]
@@ -71,6 +72,12 @@ class _BlockMask(ctypes.Structure):
                 ("q_num_blocks", ctypes.c_void_p), ("q_indices", ctypes.c_void_p),
                 ("full_q_num_blocks", ctypes.c_void_p), ("full_q_indices", ctypes.c_void_p),
                 ("Q_BLOCK_SIZE", ctypes.c_int32)]
+
+
+class _FwdPlan(ctypes.Structure):
+    _fields_ = [("waves_per_head", ctypes.c_int32), ("heads_per_workgroup", ctypes.c_int32),
+                ("row16", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+                ("work_items", ctypes.c_int64)]
 
 
 class _PageTable(ctypes.Structure):
@@ -143,6 +150,9 @@ def load_library():
         ctypes.POINTER(_BlockMask), ctypes.c_int, ctypes.POINTER(_ScoreParams), ctypes.c_float,
         ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
         ctypes.c_void_p, ctypes.c_void_p]
+    lib.flexattn_fwd_make_plan.restype = ctypes.c_int
+    lib.flexattn_fwd_make_plan.argtypes = [ctypes.c_int32] * 5 + [
+        ctypes.c_int, ctypes.POINTER(_BlockMask), ctypes.c_int32, ctypes.POINTER(_FwdPlan)]
     lib.flexattn_fwd.restype = ctypes.c_int
     lib.flexattn_fwd.argtypes = [
         ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
@@ -244,11 +254,6 @@ class BlockMask:
                 out[pos + (idx[pos][:int(num[pos])],)] = cls
         return out
 
-    def sparsity(self) -> float:
-        """Percentage of tiles that are not computed (empty), over all (b, h)."""
-        nonempty = int(self.kv_num_blocks.sum().item()) + int(self.full_kv_num_blocks.sum().item())
-        return 100.0 * (1.0 - nonempty / float(self.kv_indices.numel()))
-
     def to_string(self, grid_size=(20, 20), limit: int = 4) -> str:
         """A character picture of the tile grid of the first `limit` (b, h)
         rows of the BlockMask: '#' full, '+' partial, '.' empty. The grid is
@@ -285,7 +290,8 @@ class BlockMask:
         return self.B * self.H * self.Q_LEN * self.KV_LEN
 
     def sparsity(self) -> float:
-        """Percentage of tiles that are not computed (reads the counts back)."""
+        """Percentage of tiles that are not computed (empty), over all (b, h)
+        (reads the counts back)."""
         nonempty = int(self.kv_num_blocks.sum().item()) + int(self.full_kv_num_blocks.sum().item())
         total = self.B * self.H * self.num_q_blocks * self.num_kv_blocks
         return 100.0 * (1.0 - nonempty / total)
@@ -388,40 +394,32 @@ def _tensor(t: torch.Tensor, name: str) -> _Tensor:
     return _Tensor(t.data_ptr(), dt, *t.shape, st)
 
 
+def fwd_plan(q: torch.Tensor, k: torch.Tensor, block_mask: BlockMask,
+             target_workgroups: int = 512) -> dict:
+    """The library's launch plan for a forward of these shapes
+    (flexattn_fwd_make_plan): waves_per_head, heads_per_workgroup, row16,
+    num_splits (slices that fill target_workgroups once when work items are
+    few) and work_items."""
+    lib = load_library()
+    dt = {torch.float32: _F32, torch.bfloat16: _BF16, torch.float16: _F16}.get(q.dtype)
+    if dt is None:
+        raise NotImplementedError(f"q dtype {q.dtype} is not float32, bfloat16 or float16")
+    B, Hq, M, D = q.shape
+    plan = _FwdPlan()
+    _check(lib.flexattn_fwd_make_plan(B, Hq, k.shape[1], M, D, dt, ctypes.byref(block_mask._c),
+                                      int(target_workgroups), ctypes.byref(plan)),
+           "flexattn_fwd_make_plan")
+    return {name: getattr(plan, name) for name, _ in _FwdPlan._fields_}
+
+
 def auto_splits(q: torch.Tensor, k: torch.Tensor, block_mask: BlockMask,
                 target_workgroups: int = 512) -> int:
-    """Split count for a bf16 call: enough workgroups to fill the chip once
+    """Split count for a call: enough workgroups to fill the chip once
     (target_workgroups, two per CU, the forward's occupancy) when there are
-    few query tiles, at most the number of KV tiles a row can list, and 1 (no
-    split) otherwise. Measured on the decode shape (64 items): 8 slices (512
-    workgroups) beat 16 (two rounds) and the 10 and 12 of a ragged round."""
-    if q.dtype not in (torch.bfloat16, torch.float16):
-        return 1
-    B, Hq, M = q.shape[0], q.shape[1], q.shape[2]
-    group = Hq // k.shape[1]
-    # a short query tile (M <= 64) with the mask broadcast over heads packs
-    # 4 / waves-per-head query heads of one KV group into a workgroup (the
-    # same rule as the kernel's launcher)
-    heads_per_wg = 1
-    if block_mask.H == 1 and M <= 64:
-        for wph in (1, 2):
-            if M <= 32 * wph and group % (4 // wph) == 0:
-                heads_per_wg = 4 // wph
-                break
-        else:
-            # no exact packing (head dim <= 128): packs with a partial last
-            # one per KV group
-            wph = 1 if M <= 32 else 2
-            if q.shape[-1] > 128:
-                wph = 4
-            if 2 * group > 4 // wph:
-                heads_per_wg = 4 // wph
-    packs = -(-group // heads_per_wg)  # workgroups per KV group and query tile
-    items = (B * (Hq // group) * packs * block_mask.num_q_blocks
-             * (block_mask.q_block // 128))
-    if items >= target_workgroups // 2:
-        return 1
-    return max(1, min(block_mask.num_kv_blocks, target_workgroups // items, 64))
+    few work items, and 1 (no split) otherwise; the library's plan decides.
+    Measured on the decode shape (64 items): 8 slices (512 workgroups) beat
+    16 (two rounds) and the 10 and 12 of a ragged round."""
+    return fwd_plan(q, k, block_mask, target_workgroups)["num_splits"]
 
 
 def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask,

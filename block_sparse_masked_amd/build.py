@@ -19,9 +19,10 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libflexattn.so")
 
-SOURCES = ["api.cpp", "block_mask.hip", "fwd_bf16.hip", "fwd_bf16_paged.hip", "fwd_f16.hip",
-           "fwd_f32.hip",
-           "bwd_bf16.hip"]
+SOURCES = ["api.cpp", "block_mask.hip", "fwd_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip"]
+# fwd_bf16_inst.hip is compiled once per kernel slice (head dim, paged K/V,
+# fp16 elements), so the slices build in parallel
+SLICES = [(d, paged, f16) for d in (64, 128, 256) for paged, f16 in ((0, 0), (1, 0), (0, 1))]
 ARCH = "gfx950"
 
 
@@ -41,11 +42,11 @@ def common_flags(debug: bool):
     return flags
 
 
-def compile_one(src: str, debug: bool, extra) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def compile_one(src: str, debug: bool, extra, defines=(), obj_name=None) -> str:
+    obj = os.path.join(BUILD, obj_name or os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") or src.endswith(".cpp") else []
-    cmd = [hipcc()] + common_flags(debug) + list(extra) + lang + ["-c", os.path.join(CSRC, src),
-                                                                   "-o", obj]
+    cmd = ([hipcc()] + common_flags(debug) + list(extra) + [f"-D{d}" for d in defines] + lang
+           + ["-c", os.path.join(CSRC, src), "-o", obj])
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in line)
@@ -56,10 +57,20 @@ def compile_one(src: str, debug: bool, extra) -> str:
     return obj
 
 
-def build(jobs: int = 4, debug: bool = False, extra=()) -> str:
+def _jobs():
+    """(source, defines, object name) of every object of the library."""
+    jobs = [(s, (), None) for s in SOURCES]
+    for d, paged, f16 in SLICES:
+        jobs.append(("fwd_bf16_inst.hip", (f"FA_D={d}", f"FA_PAGED={paged}", f"FA_F16={f16}"),
+                     f"fwd_bf16_inst_d{d}_p{paged}_h{f16}.o"))
+    # the longest compiles first
+    return sorted(jobs, key=lambda j: j[0] != "fwd_bf16_inst.hip")
+
+
+def build(jobs: int = 8, debug: bool = False, extra=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: compile_one(s, debug, extra), SOURCES))
+        objs = list(ex.map(lambda j: compile_one(j[0], debug, extra, j[1], j[2]), _jobs()))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -71,7 +82,7 @@ def build(jobs: int = 4, debug: bool = False, extra=()) -> str:
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--jobs", type=int, default=4)
+    ap.add_argument("--jobs", type=int, default=8)
     ap.add_argument("--debug", action="store_true")
     ap.add_argument("--save-temps", action="store_true",
                     help="keep the gfx950 assembly of our own kernels under _build/")

@@ -10,6 +10,7 @@
 #include <string>
 
 #include "../../include/flexattn.h"
+#include "fwd_plan.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -523,6 +524,46 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
                              float scale, flexattn_tensor* out, float* lse, void* stream) {
   return fwd_impl(q, k, v, bm, score_kind, params, scale, out, lse, 1, nullptr, 0, stream,
                   "flexattn_fwd");
+}
+
+flexattn_status flexattn_fwd_make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Q_LEN,
+                                       int32_t D, flexattn_dtype dtype,
+                                       const flexattn_block_mask* bm, int32_t target_workgroups,
+                                       flexattn_fwd_plan* plan) {
+  static const char* who = "flexattn_fwd_make_plan";
+  if (!bm || !plan) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: bm or plan is NULL", who);
+  if (B < 1 || Hq < 1 || Hkv < 1 || Q_LEN < 1 || D < 1)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: non-positive shape", who);
+  if (Hq % Hkv != 0)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", who, Hq, Hkv);
+  if (dtype != FLEXATTN_F32 && dtype != FLEXATTN_BF16 && dtype != FLEXATTN_F16)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: dtype %d is not F32, BF16 or F16", who,
+                (int)dtype);
+  if (!valid_block(bm->BLOCK_SIZE))
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: BlockMask BLOCK_SIZE %d", who, bm->BLOCK_SIZE);
+  const int QBS = bm->Q_BLOCK_SIZE > 0 ? bm->Q_BLOCK_SIZE : bm->BLOCK_SIZE;
+  if (!valid_block(QBS))
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: BlockMask Q_BLOCK_SIZE %d", who, QBS);
+  if (!(bm->B == 1 || bm->B == B) || !(bm->H == 1 || bm->H == Hq) || bm->Q_LEN != Q_LEN ||
+      bm->num_q_blocks != ceil_div(Q_LEN, QBS) || bm->num_kv_blocks < 1)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: BlockMask does not match the shapes", who);
+  const int target = target_workgroups > 0 ? target_workgroups : 512;
+  if (dtype == FLEXATTN_F32) {
+    plan->waves_per_head = 0;  // not the 16-bit kernel's layout: 32-row workgroups
+    plan->heads_per_workgroup = 1;
+    plan->row16 = 0;
+    plan->num_splits = 1;
+    plan->work_items = (int64_t)B * Hq * bm->num_q_blocks * (QBS / 32);
+    return ok();
+  }
+  const fa::FwdPlan p = fa::plan_fwd(B, Hq, Hkv, Q_LEN, D, bm->B, bm->H, bm->num_q_blocks, QBS,
+                                     bm->num_kv_blocks, target);
+  plan->waves_per_head = p.wph;
+  plan->heads_per_workgroup = p.hpw;
+  plan->row16 = p.r16 ? 1 : 0;
+  plan->num_splits = p.splits;
+  plan->work_items = p.items;
+  return ok();
 }
 
 size_t flexattn_fwd_splitkv_workspace_bytes(int32_t B, int32_t Hq, int32_t Q_LEN, int32_t D,

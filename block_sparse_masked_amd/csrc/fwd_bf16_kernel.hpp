@@ -39,23 +39,24 @@
 // K and V of step g + 1 are loaded straight from global memory into LDS
 // (double-buffered) while step g computes; one barrier per step.
 // Full tiles take a path with no mask code. The running max is applied
-// lazily: O and the row sum are rescaled only when a row's max grows by more
-// than 2^8 (exp2 units), which leaves the result unchanged (any reference
-// point gives the same normalised sums) while skipping most rescales.
+// lazily: O and the row sums are rescaled only when a row's max grows by more
+// than 8 (log2 units), which skips most rescales; any reference point gives
+// the same normalised sums in exact arithmetic. In rounded arithmetic the
+// row's largest probability can then be up to 2^8 instead of exactly 1, and
+// its rounding to the input type would go straight into O; so O is divided
+// by the fp32 sum of the rounded probabilities (the values the P.V product
+// multiplies), and LSE uses the sum of the unrounded ones.
 #pragma once
-
-#include <stdlib.h>
 
 #include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
 #include "fwd_common.hpp"
+#include "fwd_plan.hpp"
 #include "launch.hpp"
 
 namespace fa {
-
-namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -68,6 +69,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // The 16-bit input element: bf16 (F16 = false) or fp16. Both have the same
 // register and LDS layouts and a 32x32x16 MFMA with fp32 accumulation; P is
 // rounded to the input type for the P.V product.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// sum8: c + the 8 rounded probabilities of one P operand register set, in
+// fp32 (four two-element dot products with (1, 1)): the row sum of exactly
+// the values the P.V product multiplies.
 template <bool F16>
 struct Elem {
   using T = __bf16;
@@ -75,6 +82,13 @@ struct Elem {
   using V4 = bf16x4;
   static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float sum8(V8 p, float c) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, c, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, c, false);
   }
 };
 template <>
@@ -84,6 +98,13 @@ struct Elem<true> {
   using V4 = f16x4;
   static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float sum8(V8 p, float c) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    c = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 0, 1), one, c, false);
+    c = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 2, 3), one, c, false);
+    c = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 4, 5), one, c, false);
+    return __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 6, 7), one, c, false);
   }
 };
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -418,7 +439,7 @@ __device__ __forceinline__ float elem_logit(float x, int blk, int r, int kv0, co
 // One KV step: S = K . Q^T, online softmax, O += V . P. `dma(i)` issues the
 // i-th of the NDMA loads of the next step (called between S products).
 template <int D, int MASK, int SCORE, bool MASKED, int NDMA, bool F16, typename DMA>
-__device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l,
+__device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l, float& lp,
                                      const typename Elem<F16>::V8 (&qf)[D / 16], const u16* sK,
                                      const u16* sV,
                                      int kv0, const int* step_doc, const FwdArgs& a,
@@ -458,6 +479,7 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
     const float m_new = fmaxf(m_ref, mx);
     const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_ref - m_new);
     l *= alpha;
+    lp *= alpha;
 #pragma unroll
     for (int i = 0; i < G::DB; ++i)
 #pragma unroll
@@ -481,6 +503,8 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
     pf[e >> 3][e & 7] = (typename Elem<F16>::T)p;
   }
   l += rs;
+#pragma unroll
+  for (int ks = 0; ks < G::PKS; ++ks) lp = Elem<F16>::sum8(pf[ks], lp);
 
 #pragma unroll
   for (int ks = 0; ks < G::PKS; ++ks)
@@ -558,7 +582,7 @@ __device__ __forceinline__ float elem_logit16(float x, int blk, int r, int kv0,
 }
 
 template <int D, int MASK, int SCORE, bool MASKED, int NDMA, bool F16, typename DMA>
-__device__ __forceinline__ void step16(f32x4 (&o)[D / 16], float& m_ref, float& l,
+__device__ __forceinline__ void step16(f32x4 (&o)[D / 16], float& m_ref, float& l, float& lp,
                                        const typename Elem<F16>::V8 (&qf)[D / 16], const u16* sK,
                                        const u16* sV, int kv0, const int* step_doc,
                                        const FwdArgs& a, const Lane<D>& ln, DMA&& dma) {
@@ -621,6 +645,7 @@ __device__ __forceinline__ void step16(f32x4 (&o)[D / 16], float& m_ref, float& 
     const float m_new = fmaxf(m_ref, mx);
     const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_ref - m_new);
     l *= alpha;
+    lp *= alpha;
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
@@ -646,6 +671,8 @@ __device__ __forceinline__ void step16(f32x4 (&o)[D / 16], float& m_ref, float& 
       pf[b >> 1][4 * (b & 1) + r] = (typename Elem<F16>::T)p;
     }
   l += rs;  // this lane's keys; the four lanes of a query are summed at the end
+#pragma unroll
+  for (int j = 0; j < NB / 2; ++j) lp = Elem<F16>::sum8(pf[j], lp);
 
 #pragma unroll
   for (int j = 0; j < NB / 2; ++j)
@@ -654,19 +681,17 @@ __device__ __forceinline__ void step16(f32x4 (&o)[D / 16], float& m_ref, float& 
       o[db] = mfma16<F16>(v_frag16<D, F16>(sV, ln, j, db), pf[j], o[db]);
 }
 
-// HEADS query heads that share one KV head (and one BlockMask row) per
-// workgroup: 4 * HEADS waves read the same K/V step blocks, so HEADS = 2
-// halves the global->LDS traffic per flop. Two waves per SIMD either way.
+// Four waves per workgroup, two workgroups per CU (two waves per SIMD).
 // D = 256 holds 128 accumulator and 64 Q registers per lane: one workgroup
 // per CU, with the accumulators in the matrix-core registers.
 // R16: the 16-row step for query tiles of at most 16 rows (one query head
 // per wave, 4 heads of a KV group per workgroup).
-template <int D, int MASK, int SCORE, int HEADS, bool PAGED, bool F16, bool R16>
-__global__ __launch_bounds__(64 * kWavesPerHead * HEADS, (D > 128) ? 1 : 2 / HEADS) void
+template <int D, int MASK, int SCORE, bool PAGED, bool F16, bool R16>
+__global__ __launch_bounds__(64 * kWavesPerHead, (D > 128) ? 1 : 2) void
 fwd_bf16_kernel(FwdArgs a) {
   using E = Elem<F16>;
   using G = Geom<D>;
-  constexpr int WAVES = kWavesPerHead * HEADS;
+  constexpr int WAVES = kWavesPerHead;
   constexpr int THREADS = 64 * WAVES;
   constexpr int NK = G::NK;
   constexpr int SPT = G::SPT;
@@ -706,9 +731,9 @@ fwd_bf16_kernel(FwdArgs a) {
     const int r = x / R, u = x - r * R;
     x = r * R + (u & 7) * (R >> 3) + (u >> 3);
   }
-  // the item's head index counts groups of HPW consecutive heads (HEADS = 2:
-  // pairs; one-head workgroups with wph < 4: 4 / wph heads of a KV group)
-  const int wph = (HEADS == 1) ? a.wph : kWavesPerHead;
+  // the item's head index counts packs of HPW consecutive heads of one KV
+  // group (wph < 4: 4 / wph heads per workgroup)
+  const int wph = a.wph;
   const int HPW = WAVES / wph;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // D <= 128: a KV group's heads in packs of HPW; when G is not a multiple
@@ -721,11 +746,11 @@ fwd_bf16_kernel(FwdArgs a) {
   if constexpr (D <= 128) {
     const int gpk = (a.G + HPW - 1) / HPW;  // packs per KV group
     it = decode_item(x, a.bm, a.B, (a.Hq / a.G) * gpk);
-    hk = it.h / gpk;
-    const int hlocal = (it.h - hk * gpk) * HPW + wave / wph;
-    hvalid = hlocal < a.G;
+    const PackedHead ph = packed_head(it.h, a.G, HPW, wave / wph);
     b = it.b;
-    h = hk * a.G + min(hlocal, a.G - 1);
+    h = ph.h;
+    hk = ph.hk;
+    hvalid = ph.valid;
   } else {
     it = decode_item(x, a.bm, a.B, a.Hq / HPW);
     b = it.b;
@@ -832,7 +857,8 @@ fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) o16[i][r] = 0.0f;
   float m_ref = -INFINITY;
-  float l = 0.0f;
+  float l = 0.0f;   // row sum of the probabilities (fp32): the LSE
+  float lp = 0.0f;  // row sum of the rounded probabilities P.V multiplies: O's divisor
 
   if (t_end > t_begin) {
     // tile indices are clamped into [0, NKB): a malformed BlockMask computes
@@ -896,11 +922,11 @@ fwd_bf16_kernel(FwdArgs a) {
         };
         if constexpr (R16)
           step16<D, MASK, SCORE, M, 2 * KPW, F16>(
-              o16, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
+              o16, m_ref, l, lp, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
               mask_uses_doc(MASK) ? docbuf + cur * DOC_STRIDE : nullptr, a, ln, dma);
         else
           step<D, MASK, SCORE, M, 2 * KPW, F16>(
-              o, m_ref, l, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
+              o, m_ref, l, lp, qf, cur ? sK1 : sK0, cur ? sV1 : sV0, kv0,
               mask_uses_doc(MASK) ? docbuf + cur * DOC_STRIDE : nullptr, a, ln, dma);
         kv0 = kv_nxt;
         ++g;
@@ -924,7 +950,9 @@ fwd_bf16_kernel(FwdArgs a) {
     // holds O^T rows 16*db + 4*g4 + r of query c16
     const float l1 = l + __shfl_xor(l, 16, 64);
     const float l_tot16 = l1 + __shfl_xor(l1, 32, 64);
-    const float inv16 = l_tot16 > 0.0f ? 1.0f / l_tot16 : 0.0f;
+    const float lp1 = lp + __shfl_xor(lp, 16, 64);
+    const float lp_tot16 = lp1 + __shfl_xor(lp1, 32, 64);
+    const float inv16 = lp_tot16 > 0.0f ? 1.0f / lp_tot16 : 0.0f;
     const float lse2 = l_tot16 > 0.0f ? (m_ref + fast_log2(l_tot16)) * kLn2 : -INFINITY;
     if (!qvalid) return;
     auto put_f32 = [&](float* orow) {
@@ -958,8 +986,13 @@ fwd_bf16_kernel(FwdArgs a) {
   }
 
   // epilogue: O = O_acc / l, LSE = ln(sum) + max
+  // O is divided by the sum of the rounded probabilities it was accumulated
+  // from, so its weights sum to one whatever the rounding (with the lazy
+  // reference the largest probability of a row can be up to 2^8 and is not
+  // exact in the input type); LSE takes the exact fp32 sum
   const float l_tot = l + __shfl_xor(l, 32, 64);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lp_tot = lp + __shfl_xor(lp, 32, 64);
+  const float inv = lp_tot > 0.0f ? 1.0f / lp_tot : 0.0f;
   if (a.splits > 1) {
     // this slice's normalised O and LSE (-inf for an empty slice), fp32
     if (qvalid) {
@@ -1014,224 +1047,92 @@ fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int MASK, int SCORE, int HEADS, bool PAGED, bool F16, bool R16>
+template <int D, int MASK, int SCORE, bool PAGED, bool F16, bool R16>
 hipError_t launch_one(const FwdArgs& args, int grid, hipStream_t stream) {
   const int nlist = args.bm.NKB * (args.bm.BS / kBlock);
   const int lds = 4 * ((nlist + 3) & ~3) * (PAGED ? 2 : 1);
-  // the dynamic-LDS limit is raised once per device and size (the attribute
-  // is per device; concurrent callers at worst set it twice)
+  const void* fn = reinterpret_cast<const void*>(&fwd_bf16_kernel<D, MASK, SCORE, PAGED, F16, R16>);
+  // The kernel's dynamic-LDS limit is raised once per device to everything
+  // the CU has beside its static LDS; the value is the same for every call,
+  // so concurrent first calls at worst set it twice, never lower it.
   constexpr int kMaxDevices = 64;
-  static std::atomic<int> attr_bytes[kMaxDevices] = {};
+  static std::atomic<bool> raised[kMaxDevices] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= kMaxDevices || lds > attr_bytes[dev].load(std::memory_order_relaxed)) {
-    e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&fwd_bf16_kernel<D, MASK, SCORE, HEADS, PAGED, F16, R16>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (dev >= kMaxDevices || !raised[dev].load(std::memory_order_acquire)) {
+    hipFuncAttributes attr;
+    e = hipFuncGetAttributes(&attr, fn);
     if (e != hipSuccess) return e;
-    if (dev < kMaxDevices) attr_bytes[dev].store(lds, std::memory_order_relaxed);
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kMaxLdsBytes - (int)attr.sharedSizeBytes);
+    if (e != hipSuccess) return e;
+    if (dev < kMaxDevices) raised[dev].store(true, std::memory_order_release);
   }
-  fwd_bf16_kernel<D, MASK, SCORE, HEADS, PAGED, F16, R16><<<grid, 64 * kWavesPerHead * HEADS, lds, stream>>>(args);
+  fwd_bf16_kernel<D, MASK, SCORE, PAGED, F16, R16><<<grid, 64 * kWavesPerHead, lds, stream>>>(args);
   return hipGetLastError();
 }
 
-template <int D, int MASK, int HEADS, bool PAGED, bool F16, bool R16>
+template <int D, int MASK, bool PAGED, bool F16, bool R16>
 hipError_t dispatch_score(const FwdArgs& args, int score, int grid, hipStream_t stream) {
   switch (score) {
     case SCORE_NONE:
-      return launch_one<D, MASK, SCORE_NONE, HEADS, PAGED, F16, R16>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_NONE, PAGED, F16, R16>(args, grid, stream);
     case SCORE_ALIBI:
-      return launch_one<D, MASK, SCORE_ALIBI, HEADS, PAGED, F16, R16>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_ALIBI, PAGED, F16, R16>(args, grid, stream);
     case SCORE_SOFTCAP:
-      return launch_one<D, MASK, SCORE_SOFTCAP, HEADS, PAGED, F16, R16>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_SOFTCAP, PAGED, F16, R16>(args, grid, stream);
     case SCORE_SOFTCAP_ALIBI:
-      return launch_one<D, MASK, SCORE_SOFTCAP_ALIBI, HEADS, PAGED, F16, R16>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_SOFTCAP_ALIBI, PAGED, F16, R16>(args, grid, stream);
     default:
-      return launch_one<D, MASK, SCORE_SCALED, HEADS, PAGED, F16, R16>(args, grid, stream);
+      return launch_one<D, MASK, SCORE_SCALED, PAGED, F16, R16>(args, grid, stream);
   }
 }
 
-template <int D, int HEADS, bool PAGED, bool F16, bool R16>
+template <int D, bool PAGED, bool F16, bool R16>
 hipError_t dispatch_mask(const FwdArgs& args, int mask, int score, int grid, hipStream_t stream) {
   switch (mask) {
     case MASK_NOOP:
-      return dispatch_score<D, MASK_NOOP, HEADS, PAGED, F16, R16>(args, score, grid, stream);
+      return dispatch_score<D, MASK_NOOP, PAGED, F16, R16>(args, score, grid, stream);
     case MASK_CAUSAL:
-      return dispatch_score<D, MASK_CAUSAL, HEADS, PAGED, F16, R16>(args, score, grid, stream);
+      return dispatch_score<D, MASK_CAUSAL, PAGED, F16, R16>(args, score, grid, stream);
     case MASK_SLIDING_SINK:
-      return dispatch_score<D, MASK_SLIDING_SINK, HEADS, PAGED, F16, R16>(args, score, grid, stream);
+      return dispatch_score<D, MASK_SLIDING_SINK, PAGED, F16, R16>(args, score, grid, stream);
     case MASK_PREFIX_LM:
-      return dispatch_score<D, MASK_PREFIX_LM, HEADS, PAGED, F16, R16>(args, score, grid, stream);
+      return dispatch_score<D, MASK_PREFIX_LM, PAGED, F16, R16>(args, score, grid, stream);
     case MASK_COMPOSITE:
-      return dispatch_score<D, MASK_COMPOSITE, HEADS, PAGED, F16, R16>(args, score, grid, stream);
+      return dispatch_score<D, MASK_COMPOSITE, PAGED, F16, R16>(args, score, grid, stream);
     default:
-      return dispatch_score<D, MASK_DOCUMENT, HEADS, PAGED, F16, R16>(args, score, grid, stream);
+      return dispatch_score<D, MASK_DOCUMENT, PAGED, F16, R16>(args, score, grid, stream);
   }
 }
 
 template <int D, bool PAGED, bool F16>
-hipError_t dispatch_heads(const FwdArgs& args, int heads, bool r16, int mask, int score, int grid,
-                          hipStream_t stream) {
-  if constexpr (!PAGED && !F16 && D <= 128)
-    if (heads == 2) return dispatch_mask<D, 2, false, false, false>(args, mask, score, grid, stream);
+hipError_t dispatch_step(const FwdArgs& args, bool r16, int mask, int score, int grid,
+                         hipStream_t stream) {
   if constexpr (D <= 128)
-    if (r16) return dispatch_mask<D, 1, PAGED, F16, true>(args, mask, score, grid, stream);
-  return dispatch_mask<D, 1, PAGED, F16, false>(args, mask, score, grid, stream);
+    if (r16) return dispatch_mask<D, PAGED, F16, true>(args, mask, score, grid, stream);
+  return dispatch_mask<D, PAGED, F16, false>(args, mask, score, grid, stream);
 }
 
-// Merge of the split-KV slices, one 64-lane wave per query row: with the
-// slices' LSE_s, LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s
-// (the rescaling of the online softmax, applied across slices).
-template <int D, bool F16>
-__global__ __launch_bounds__(256) void splitkv_combine_kernel(FwdArgs a) {
-  using T = typename Elem<F16>::T;
-  constexpr int PER = D / 64;  // elements per lane
-  const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  // slices are read in batches of 8 (indices clamped to the last slice, the
-  // extra ones weighted 0) so the batch's loads are in flight together
-  constexpr int BATCH = 8;
-  float m = -INFINITY;
-  for (int s0 = 0; s0 < a.splits; s0 += BATCH) {
-    float ls[BATCH];
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) ls[u] = a.part_lse[min(s0 + u, a.splits - 1) * rows + row];
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) m = fmaxf(m, ls[u]);
-  }
-  float acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
-  float wsum = 0.0f;
-  if (m != -INFINITY) {
-    for (int s0 = 0; s0 < a.splits; s0 += BATCH) {
-      float ls[BATCH], ov[BATCH][PER];
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const long long srow = (long long)min(s0 + u, a.splits - 1) * rows + row;
-        ls[u] = a.part_lse[srow];
-        __builtin_memcpy(ov[u], a.part_o + srow * D + lane * PER, PER * 4);
-      }
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const float w = (s0 + u >= a.splits || ls[u] == -INFINITY)
-                            ? 0.0f : fast_exp2((ls[u] - m) * kLog2e);
-        wsum += w;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, ov[u][i], acc[i]);
-      }
-    }
-  }
-  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  const int qi = (int)(row % a.Q_LEN);
-  const long long bh = row / a.Q_LEN;
-  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
-  u16* orow = a.o + b * a.so0 + h * a.so1 + (long long)qi * a.so2 + lane * PER;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const T v = (T)(acc[i] * inv);
-    __builtin_memcpy(orow + i, &v, 2);
-  }
-  if (lane == 0)
-    a.lse[((long long)b * a.Hq + h) * a.Q_LEN + qi] =
-        wsum > 0.0f ? m + fast_log2(wsum) * kLn2 : -INFINITY;
+// One (head dim, KV layout, element type) slice of the kernel instantiations:
+// every mask kind x score kind x MFMA step. fwd_bf16_inst.hip holds the
+// explicit instantiations (one object file per slice, compiled in
+// parallel); the launcher only declares them.
+template <int D, bool PAGED, bool F16>
+hipError_t fwd16_launch(const FwdArgs& a, bool r16, int mask, int score, int grid,
+                        hipStream_t stream) {
+  return dispatch_step<D, PAGED, F16>(a, r16, mask, score, grid, stream);
 }
 
-
-// Argument set-up, launch shape and dispatch of the forward (and the merge
-// of split-KV slices); PAGED selects the paged-KV instantiations.
-template <bool PAGED, bool F16>
-hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
-  FwdArgs a;
-  a.q = static_cast<const u16*>(L.q);
-  a.k = static_cast<const u16*>(L.k);
-  a.v = static_cast<const u16*>(L.v);
-  a.o = static_cast<u16*>(L.o);
-  a.lse = L.lse;
-  a.sq0 = L.sq[0]; a.sq1 = L.sq[1]; a.sq2 = L.sq[2];
-  a.sk0 = L.sk[0]; a.sk1 = L.sk[1]; a.sk2 = (int)L.sk[2];
-  a.sv0 = L.sv[0]; a.sv1 = L.sv[1]; a.sv2 = (int)L.sv[2];
-  a.so0 = L.so[0]; a.so1 = L.so[1]; a.so2 = L.so[2];
-  a.B = L.B;
-  a.Hq = L.Hq;
-  a.Hkv = L.Hkv;
-  a.G = L.Hq / L.Hkv;
-  a.Q_LEN = L.Q_LEN;
-  a.KV_LEN = L.KV_LEN;
-  a.mp = L.mp;
-  a.doc_len = L.doc_len;
-  a.c_scale = L.scale * kLog2e;
-  a.c_cap = L.softcap > 0.0f ? 2.0f * L.scale * kLog2e / L.softcap : 0.0f;
-  a.cap2 = L.softcap * kLog2e;
-  a.slopes = L.slopes;
-  a.bm = L.bm;
-  a.splits = L.splits > 1 ? L.splits : 1;
-  a.part_o = L.part_o;
-  a.part_lse = L.part_lse;
-  a.page_table = L.page_table;
-  a.page_size = L.page_size;
-  a.pt_stride = L.pt_stride;
-  a.num_pages = L.num_pages;
-  a.o32 = L.o32;
-  // Two query heads per workgroup are possible when they share a KV head and
-  // a BlockMask row (mask broadcast over heads, even GQA group); one head per
-  // workgroup is the default, FLEXATTN_BF16_HEADS=2 selects the pairs (only
-  // where they apply).
-  const bool pair_ok = !PAGED && !F16 && L.D <= 128 && L.bm.Hm == 1 && a.G % 2 == 0 && a.splits == 1;
-  int heads = 1;  // measured: two 4-wave workgroups per CU beat one 8-wave one
-  if (const char* env = getenv("FLEXATTN_BF16_HEADS")) {
-    if (env[0] == '1') heads = 1;
-    if (env[0] == '2' && pair_ok) heads = 2;
-  }
-  // Short query tiles (Q_LEN <= 64, one tile) with the mask broadcast over
-  // heads: fewest waves per head that cover Q_LEN and give a whole number of
-  // heads per workgroup inside one KV group.
-  a.wph = kWavesPerHead;
-  if (heads == 1 && L.bm.Hm == 1 && L.Q_LEN <= 64)
-    for (int w = 1; w < kWavesPerHead; w *= 2)
-      if (L.Q_LEN <= 32 * w && a.G % (kWavesPerHead / w) == 0) {
-        a.wph = w;
-        break;
-      }
-  // No exact packing (G a multiple of neither 4 nor 2): packs of 4 / waves
-  // heads with a partial last pack per KV group, as long as real heads fill
-  // at least half of a group's slots (G = 3, 5, 7, ...).
-  if (L.D <= 128 && heads == 1 && L.bm.Hm == 1 && L.Q_LEN <= 64 && a.wph == kWavesPerHead) {
-    const int w = L.Q_LEN <= 32 ? 1 : 2;
-    if (2 * a.G > kWavesPerHead / w) a.wph = w;
-  }
-  // At most 16 query rows per head: the 16-row MFMA step (half the matrix
-  // work of a 32-row step that would carry 16 empty rows).
-  // FLEXATTN_R16=0 keeps the 32-row step.
-  bool r16 = a.wph == 1 && L.Q_LEN <= 16 && L.D <= 128;
-  if (const char* env = getenv("FLEXATTN_R16"))
-    if (env[0] == '0') r16 = false;
-  const int hpw = heads * kWavesPerHead / a.wph;  // query heads per workgroup
-  // XCD-aware order: with the mask broadcast over batch and heads every
-  // schedule round holds the B*Hkv*g_items items of one query tile; split
-  // each round into 8 contiguous chunks of whole KV groups, one per XCD.
-  const int g_items = (a.G + hpw - 1) / hpw;  // items (head packs) per KV group
-  const int R = L.B * (L.Hq / a.G) * g_items;
-  a.xcd_round = (L.bm.Bm == 1 && L.bm.Hm == 1 && R % 8 == 0 && (R / 8) % g_items == 0) ? R : 0;
-  const int grid = R * L.bm.NQB * (L.bm.QBS / kBlock) * a.splits;
-  if (grid == 0) return hipSuccess;
-  // the unscaled fast path takes the row max before scaling: scale must be > 0
-  const int score = (L.score_kind == SCORE_NONE && !(L.scale > 0.0f)) ? SCORE_SCALED : L.score_kind;
-  hipError_t e = (L.D == 256) ? dispatch_heads<256, PAGED, F16>(a, heads, r16, L.mask_kind, score, grid, stream)
-               : (L.D == 128) ? dispatch_heads<128, PAGED, F16>(a, heads, r16, L.mask_kind, score, grid, stream)
-                              : dispatch_heads<64, PAGED, F16>(a, heads, r16, L.mask_kind, score, grid, stream);
-  if (e != hipSuccess || a.splits == 1) return e;
-  const long long rows = (long long)L.B * L.Hq * L.Q_LEN;
-  const unsigned blocks = (unsigned)((rows + 3) / 4);
-  if (L.D == 256) splitkv_combine_kernel<256, F16><<<blocks, 256, 0, stream>>>(a);
-  else if (L.D == 128) splitkv_combine_kernel<128, F16><<<blocks, 256, 0, stream>>>(a);
-  else splitkv_combine_kernel<64, F16><<<blocks, 256, 0, stream>>>(a);
-  return hipGetLastError();
-}
-
-}  // namespace
+#define FA_FWD16_SLICE(D, PAGED, F16)                                                        \
+  template hipError_t fwd16_launch<D, PAGED, F16>(const FwdArgs&, bool, int, int, int,     \
+                                                  hipStream_t)
+#define FA_FWD16_SLICES(prefix)                                                              \
+  prefix FA_FWD16_SLICE(64, false, false); prefix FA_FWD16_SLICE(128, false, false);        \
+  prefix FA_FWD16_SLICE(256, false, false); prefix FA_FWD16_SLICE(64, true, false);         \
+  prefix FA_FWD16_SLICE(128, true, false); prefix FA_FWD16_SLICE(256, true, false);         \
+  prefix FA_FWD16_SLICE(64, false, true); prefix FA_FWD16_SLICE(128, false, true);          \
+  prefix FA_FWD16_SLICE(256, false, true)
 
 }  // namespace fa

@@ -62,9 +62,8 @@ struct FwdLaunch {
   float* o32 = nullptr;  // 16-bit forward, unsplit: fp32 copy of O [B][Hq][Q_LEN][D]
 };
 
+// the 16-bit forward: bf16 or fp16 (L.f16), contiguous or paged K/V (L.page_table)
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream);
-hipError_t launch_fwd_bf16_paged(const FwdLaunch& L, hipStream_t stream);  // L.page_table set
-hipError_t launch_fwd_f16(const FwdLaunch& L, hipStream_t stream);  // L.f16 set
 int fwd_bf16_lds_bytes(int D, int NKB, bool paged);  // LDS of the bf16 forward
 constexpr int kMaxLdsBytes = 160 * 1024;
 constexpr long long kMaxBf16RowStride = 1ll << 22;  // k/v row stride limit of the bf16 forward

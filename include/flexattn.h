@@ -31,6 +31,18 @@
 extern "C" {
 #endif
 
+/*
+ * Status of every entry point. The values are small positive integers (0 =
+ * success) so that a C caller can test `if (status)`; they are part of the
+ * ABI and do not change.
+ *   FLEXATTN_OK               the call was checked and its work enqueued.
+ *   FLEXATTN_ERR_INVALID_ARG  a pointer, shape, stride or alignment is wrong;
+ *                             nothing was launched.
+ *   FLEXATTN_ERR_UNSUPPORTED  a valid request outside the built set (dtype,
+ *                             head dim, block size, kind, size limit);
+ *                             nothing was launched.
+ *   FLEXATTN_ERR_HIP          a HIP call or kernel launch failed.
+ */
 typedef enum {
   FLEXATTN_OK = 0,
   FLEXATTN_ERR_INVALID_ARG = 1,
@@ -267,18 +279,54 @@ flexattn_status flexattn_create_block_mask(flexattn_mask_kind kind,
  * (FLEXATTN_ERR_UNSUPPORTED beyond them): k and v
  * row strides (stride[2]) at most 2^22 elements, and the per-row tile list
  * (num_kv_blocks ints) must fit in LDS beside the K/V staging buffers.
- * Work split (bf16): one query head per workgroup by default; the
- * environment variable FLEXATTN_BF16_HEADS=2 (read at each call) puts the
- * two query heads of one KV group in one workgroup (halving K/V loads)
- * where the BlockMask is broadcast over heads and the GQA group size is
- * even; =1 forces the default. Results do not depend on it beyond
- * floating-point summation order.
+ * Work split (16-bit): one query head per workgroup, except that short query
+ * tiles (Q_LEN <= 64, BlockMask broadcast over heads) pack several query
+ * heads of one KV group into a workgroup; flexattn_fwd_make_plan reports the
+ * packing a call gets. The split depends only on the shapes and the
+ * BlockMask's extents; nothing else (no environment variable) selects it.
  * Asynchronous on `stream`.
  */
 flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
                              const flexattn_tensor* v, const flexattn_block_mask* bm,
                              flexattn_score_kind score_kind, const flexattn_score_params* params,
                              float scale, flexattn_tensor* out, float* lse, void* stream);
+
+/*
+ * Launch plan of the forward for given shapes (host only; reads no device
+ * memory). It is the rule flexattn_fwd, flexattn_fwd_splitkv and
+ * flexattn_fwd_paged apply, reported so that a caller can size a split-KV
+ * call without restating it:
+ *   waves_per_head       4: one 128-row query tile per workgroup; 2 or 1:
+ *                        short query tiles, several heads per workgroup.
+ *   heads_per_workgroup  query heads of one KV group sharing a workgroup and
+ *                        its K/V stream (4 / waves_per_head).
+ *   row16                1 when the 16-row MFMA step runs (at most 16 query
+ *                        rows per head, one wave per head).
+ *   work_items           workgroups of one unsplit launch.
+ *   num_splits           KV slices per item that fill target_workgroups
+ *                        once when items are few (1 = do not split): at most
+ *                        num_kv_blocks and 64.
+ * Shapes: q [B][Hq][Q_LEN][D], KV heads Hkv, dtype as flexattn_tensor's;
+ * bm: the BlockMask of the call (its extents, tile counts and block sizes
+ * are read; its device buffers are not). target_workgroups <= 0 means 512
+ * (two workgroups on each of 256 CUs). fp32 calls get waves_per_head 0,
+ * heads_per_workgroup 1, row16 0, num_splits 1 (the fp32 path does not
+ * split) and the fp32 kernel's workgroup count (one per 32 query rows).
+ * Errors: INVALID_ARG for NULL pointers, non-positive shapes or a BlockMask
+ * that does not match them; UNSUPPORTED for other dtypes or block sizes.
+ */
+typedef struct {
+  int32_t waves_per_head;
+  int32_t heads_per_workgroup;
+  int32_t row16;
+  int32_t num_splits;
+  int64_t work_items;
+} flexattn_fwd_plan;
+
+flexattn_status flexattn_fwd_make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Q_LEN,
+                                       int32_t D, flexattn_dtype dtype,
+                                       const flexattn_block_mask* bm, int32_t target_workgroups,
+                                       flexattn_fwd_plan* plan);
 
 /*
  * Split-KV forward for calls with few query tiles and long KV lists (decode

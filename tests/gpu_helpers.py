@@ -93,3 +93,33 @@ def summary(res) -> str:
             "o_strict_ok", "dead_rows", "dead_ok", "finite")
     return ", ".join(f"{k}={res[k]:.3g}" if isinstance(res.get(k), float) else f"{k}={res.get(k)}"
                      for k in keys if k in res)
+
+
+def full_size_report(w: W.Workload, o16, o32, lse_gpu, o_ref, lse_ref):
+    """The stated bounds at full size, on the rows the reference computed
+    (NaN elsewhere). The kernel's fp32 O (the value before the output is
+    rounded to the input dtype) must meet the strict max-abs bound; the
+    16-bit O is reported strictly and ulp-aware, and each of its elements
+    over the strict bound is counted (they can only come from rounding the
+    fp32 O, which the caller checks bitwise)."""
+    sel = ~np.isnan(lse_ref)
+    live = sel & ~np.isneginf(lse_ref)
+    rep = {"workload": w.name, "rows": int(sel.sum()), "live_rows": int(live.sum())}
+    d32 = np.abs(o32[live] - o_ref[live])
+    d16 = np.abs(o16[live] - o_ref[live])
+    bits = 11 if w.dtype == "f16" else 8
+    slack = BF16_O_ATOL + 0.5 * bf16_ulp(o_ref[live], bits)
+    dl = np.abs(lse_gpu[live] - lse_ref[live])
+    rep.update({
+        "o_f32_max_abs": float(d32.max()),
+        "o_max_abs": float(d16.max()),
+        "o_over_strict": int((d16 > BF16_O_ATOL).sum()),
+        "o_ulp_aware_ok": bool(np.all(d16 <= slack)),
+        "lse_max_abs": float(dl.max()),
+        "lse_max_rel_guarded": float((dl / np.maximum(np.abs(lse_ref[live]), 1.0)).max()),
+        "lse_max_rel_strict": float((dl / np.abs(lse_ref[live])).max()),
+        "dead_rows_ok": bool(np.all(np.isneginf(lse_gpu[sel & np.isneginf(lse_ref)]))),
+    })
+    rep["ok"] = (rep["o_f32_max_abs"] <= BF16_O_ATOL and rep["o_ulp_aware_ok"]
+                 and rep["lse_max_rel_guarded"] <= BF16_LSE_RTOL and rep["dead_rows_ok"])
+    return rep

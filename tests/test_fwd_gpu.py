@@ -62,17 +62,6 @@ def test_fwd_tiny_grid(lib, dtype, D, mask, score):
     check_full(lib, w)
 
 
-@pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("mask", TINY_MASKS)
-@pytest.mark.parametrize("score", TINY_SCORES)
-def test_fwd_tiny_grid_head_pairs(lib, D, mask, score, monkeypatch):
-    """The bf16 grid again with FLEXATTN_BF16_HEADS=2: the two query heads of
-    a KV group in one 8-wave workgroup (a bf16 kernel variant)."""
-    monkeypatch.setenv("FLEXATTN_BF16_HEADS", "2")
-    w = tiny("bf16", D, mask, score, value_scale=2.0 if "softcap" in score else 1.0)
-    check_full(lib, w)
-
-
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal"])
 def test_fwd_unseparated_mask(lib, dtype, mask):
@@ -106,12 +95,6 @@ def test_fwd_nonpositive_scale(lib, dtype, scale, mask):
                                           (128, 128), (513, 200)])
 def test_fwd_ragged_lengths(lib, dtype, q_len, kv_len):
     check_full(lib, tiny(dtype, 64, "causal", "none", Q_LEN=q_len, KV_LEN=kv_len, B=1, Hq=2))
-
-
-@pytest.mark.parametrize("q_len,kv_len", [(1, 200), (200, 1), (129, 257), (513, 200)])
-def test_fwd_ragged_lengths_head_pairs(lib, q_len, kv_len, monkeypatch):
-    monkeypatch.setenv("FLEXATTN_BF16_HEADS", "2")
-    check_full(lib, tiny("bf16", 128, "causal", "none", Q_LEN=q_len, KV_LEN=kv_len, B=2, Hq=4))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -208,34 +191,6 @@ def test_tiny_causal_workload_full(lib):
     assert res["o_max_abs"] <= 1e-5 and res["lse_max_abs"] <= 1e-5
 
 
-def _sample_rows(L, rng, n=96):
-    fixed = [0, 1, 2, 127, 128, 129, 255, 256, L // 2, L - 129, L - 128, L - 2, L - 1]
-    rnd = rng.choice(L, size=n, replace=False)
-    return np.unique(np.concatenate([fixed, rnd]))
-
-
-@pytest.mark.slow
-@pytest.mark.parametrize("w", W.WORKLOADS[1:], ids=[w.name for w in W.WORKLOADS[1:]])
-def test_full_workload_sampled(lib, w):
-    """Full-size workloads in the bench's launch configuration: every row of
-    the first and last (b, h), and sampled rows of four more (b, h) pairs."""
-    inp = W.generate(w)
-    o, lse, _ = G.run_gpu(lib, w, inp)
-    rng = np.random.default_rng(2024)
-    results = []
-    pairs = [(0, 0), (w.B - 1, w.Hq - 1)]
-    for b, h in pairs:
-        o_ref, lse_ref = G.oracle_rows(w, inp, batches=[b], heads=[h])
-        results.append(G.compare(w, o, lse, o_ref, lse_ref))
-    extra = {(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(4)}
-    for b, h in sorted(extra):
-        rows = _sample_rows(w.Q_LEN, rng)
-        o_ref, lse_ref = G.oracle_rows(w, inp, batches=[b], heads=[h], rows=rows)
-        results.append(G.compare(w, o, lse, o_ref, lse_ref))
-    for r in results:
-        assert r["ok"], (w.name, G.summary(r))
-
-
 @pytest.mark.parametrize("splits", [2, 3, 7])
 @pytest.mark.parametrize("mask,score", [("noop", "none"), ("sliding_sink", "alibi"),
                                         ("document_causal", "softcap_alibi"),
@@ -316,6 +271,24 @@ def test_fwd_short_query_heads_packed(lib, q_len, Hq, Hkv, mask, score, splits):
     res = G.compare(w, out.float().cpu().numpy().astype(np.float64),
                     lse.cpu().numpy().astype(np.float64), o_ref, lse_ref)
     assert res["ok"], G.summary(res)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(6, 2), (14, 2), (5, 1)])
+@pytest.mark.parametrize("mask", ["document_causal", "composite"])
+@pytest.mark.parametrize("q_len", [16, 40])
+@pytest.mark.parametrize("splits", [1, None])
+def test_fwd_ragged_packs_dtypes(lib, dtype, D, Hq, Hkv, mask, q_len, splits):
+    """Partial head packs (group sizes 3, 7 and 5) for both 16-bit types and
+    head dims 64 and 128, on the masks that read document ids (document
+    causal; a composite of same-document-causal OR sinks): 16 queries take
+    the 16-row step with packs of four heads, 40 queries two waves a head
+    with packs of two."""
+    terms = (("causal", "document"), ("sink",)) if mask == "composite" else None
+    w = tiny(dtype, D, mask, "alibi", B=2, Hq=Hq, Hkv=Hkv, Q_LEN=q_len, KV_LEN=700,
+             doc_len_range=(40, 300), terms=terms)
+    check_splits(lib, w, splits)
 
 
 def test_fwd_short_query_per_head_mask_not_packed(lib):

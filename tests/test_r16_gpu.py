@@ -2,7 +2,7 @@
 broadcast over heads and four query heads per KV head or more) on the GPU:
 against the fp64 oracle for every mask and score kind, paged and split-KV,
 bf16 and fp16, head dims 64 and 128; and against the 32-row step on the same
-inputs (FLEXATTN_R16=0 selects that one)."""
+inputs (a BlockMask built per query head selects that one)."""
 import numpy as np
 import pytest
 import torch
@@ -24,9 +24,9 @@ def lib():
     return m
 
 
-def _run(lib, w, inp, splits, paged=None, f16=False):
+def _run(lib, w, inp, splits, paged=None, f16=False, H_mask=1):
     dt = "f16" if f16 else "bf16"
-    bm = G.build_gpu_mask(lib, w, inp)
+    bm = G.build_gpu_mask(lib, w, inp, 1, H_mask)
     q = G.to_device(inp.q, dt)
     if paged is None:
         k, v = G.to_device(inp.k, dt), G.to_device(inp.v, dt)
@@ -97,15 +97,16 @@ def test_r16_composite(lib, splits):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("splits", [1, 6])
-def test_r16_matches_32_row_step(lib, D, splits, monkeypatch):
+def test_r16_matches_32_row_step(lib, D, splits):
     """The two steps reorder the same fp32 sums: outputs agree to a few bf16
-    ulps and LSE to 1e-5 relative."""
+    ulps and LSE to 1e-5 relative. A BlockMask built per query head keeps
+    one head per workgroup and the 32-row step; the broadcast mask packs four
+    heads per workgroup on the 16-row step."""
     w = tiny("bf16", D, "sliding_sink", "softcap_alibi", B=3, Hq=16, Hkv=4, Q_LEN=16,
              KV_LEN=2500, window=900, value_scale=2.0)
     inp = W.generate(w)
     o16, l16 = _run(lib, w, inp, splits)
-    monkeypatch.setenv("FLEXATTN_R16", "0")
-    o32, l32 = _run(lib, w, inp, splits)
+    o32, l32 = _run(lib, w, inp, splits, H_mask=w.Hq)
     d = (o16.float() - o32.float()).abs()
     tol = 2.0 ** -7 * o32.float().abs() + 1e-3
     assert bool((d <= tol).all()), float(d.max())
@@ -116,10 +117,12 @@ def test_r16_matches_32_row_step(lib, D, splits, monkeypatch):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("splits", [1, 3])
-def test_ragged_head_packs_paged(lib, D, splits):
-    """Seven query heads per KV head: packs of 4 + 3 on the 16-row step,
-    through a paged cache, with and without slices."""
-    w = tiny("bf16", D, "sliding_sink", "softcap_alibi", B=2, Hq=14, Hkv=2, Q_LEN=16,
+@pytest.mark.parametrize("q_len", [16, 40, 64])
+def test_ragged_head_packs_paged(lib, D, splits, q_len):
+    """Seven query heads per KV head through a paged cache, with and without
+    slices: packs of 4 + 3 on the 16-row step (16 queries), packs of 2 with
+    two waves a head (40 and 64 queries)."""
+    w = tiny("bf16", D, "sliding_sink", "softcap_alibi", B=2, Hq=14, Hkv=2, Q_LEN=q_len,
              KV_LEN=1100, window=300, value_scale=2.0)
     inp = W.generate(w)
     kc, vc, table = W.paged_cache(inp.k, inp.v, 256, seed=8)

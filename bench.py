@@ -65,7 +65,8 @@ def algorithmic_bytes(w: W.Workload, nqb: int, nkb: int) -> int:
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("fwd_bf16.hip", "fwd_bf16_kernel.hpp", "common.hpp", "fwd_common.hpp")
+KERNEL_SOURCES = ("fwd_bf16.hip", "fwd_bf16_inst.hip", "fwd_bf16_kernel.hpp", "fwd_plan.hpp",
+                  "common.hpp", "fwd_common.hpp")
 
 
 def measured_traffic(workload: str, field: str = "traffic_bytes_per_launch"):
@@ -94,27 +95,117 @@ def measured_traffic(workload: str, field: str = "traffic_bytes_per_launch"):
 
 def cpu_baseline(w: W.Workload, inp: W.Inputs, budget_s: float = 20.0):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
-    workload: whole (b, h) heads, as many as fit the time budget."""
+    workload: whole (b, h) heads, as many as fit the time budget. Returns
+    the record and the oracle's O / LSE (NaN outside the heads done)."""
     import oracle  # noqa: E402  (CPU-baseline leg only)
     cores = len(os.sched_getaffinity(0))
     mask, score = oracle.for_workload(w, inp)
     pairs = allowed_pairs_per_head(w, inp.doc_lengths)
     done, t0 = 0, time.perf_counter()
-    heads = []
+    o_ref = np.full((w.B, w.Hq, w.Q_LEN, w.D), np.nan)
+    lse_ref = np.full((w.B, w.Hq, w.Q_LEN), np.nan)
     for b in range(w.B):
         for h in range(w.Hq):
-            oracle.attention(inp.q, inp.k, inp.v, mask, score, w.scale, batches=[b], heads=[h])
+            o, l = oracle.attention(inp.q, inp.k, inp.v, mask, score, w.scale, batches=[b],
+                                    heads=[h])
+            o_ref[b, h], lse_ref[b, h] = o[b, h], l[b, h]
             done += 1
-            heads.append((b, h))
             if time.perf_counter() - t0 > budget_s:
                 break
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     flops = 4.0 * w.D * pairs * done
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {w.B * w.Hq} (b, h) heads, all {w.Q_LEN} query rows each, "
-                      f"fp64 NumPy, {dt:.1f} s"}
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "sample": f"{done} of {w.B * w.Hq} (b, h) heads, all {w.Q_LEN} query rows each, "
+                     f"fp64 NumPy, {dt:.1f} s",
+           "cpu_model": cpu_model(), "blas": blas_vendor()}
+    return rec, o_ref, lse_ref
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_vendor() -> str:
+    try:
+        cfg = np.show_config(mode="dicts")
+        blas = cfg.get("Build Dependencies", {}).get("blas", {})
+        return f"{blas.get('name', '?')} {blas.get('version', '')}".strip()
+    except Exception:  # noqa: BLE001  (older NumPy: no dict mode)
+        return "unknown"
+
+
+def device_facts(torch):
+    """CU count and peak engine clock from rocminfo (the spec peak is
+    re-derived from them), plus the rate of a large library bf16 GEMM on
+    this device as a practical matrix-core reference."""
+    import subprocess
+    facts = {}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        gpu = out[out.index("gfx950"):] if "gfx950" in out else out
+        for line in gpu.splitlines():
+            line = line.strip()
+            if line.startswith("Compute Unit:") and "compute_units" not in facts:
+                facts["compute_units"] = int(line.split(":")[1])
+            if line.startswith("Max Clock Freq. (MHz):") and "max_clock_mhz" not in facts:
+                facts["max_clock_mhz"] = int(line.split(":")[1])
+    except Exception as e:  # noqa: BLE001
+        facts["rocminfo_error"] = str(e)[:200]
+    if "compute_units" in facts and "max_clock_mhz" in facts:
+        facts["bf16_peak_tflops_from_clock"] = round(
+            facts["compute_units"] * 4096 * facts["max_clock_mhz"] * 1e6 / 1e12, 1)
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(5):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    reps = 20
+    for _ in range(reps):
+        torch.matmul(a, b)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    facts["library_gemm_bf16_tflops"] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+    facts["library_gemm_shape"] = f"{n}x{n}x{n} torch.matmul"
+    del a, b
+    return facts
+
+
+def errors_vs_oracle(w: W.Workload, out, lse, o32, o_ref, lse_ref):
+    """Errors on the rows the oracle computed (NaN elsewhere): strict and
+    ulp-aware max-abs of the output, max-abs of the fp32 O the same kernel
+    writes before rounding, and relative LSE error (guarded by
+    max(|LSE|, 1), and strict)."""
+    sel = ~np.isnan(lse_ref)
+    live = sel & ~np.isneginf(lse_ref)
+    o = out.float().cpu().numpy().astype(np.float64)
+    l_ = lse.cpu().numpy().astype(np.float64)
+    do = np.abs(o[live] - o_ref[live])
+    dl = np.abs(l_[live] - lse_ref[live])
+    rec = {"heads_compared": int(sel.any(axis=-1).sum()), "rows_compared": int(sel.sum()),
+           "o_max_abs": float(do.max()),
+           "lse_max_rel_guarded": float((dl / np.maximum(np.abs(lse_ref[live]), 1.0)).max()),
+           "lse_max_rel_strict": float((dl / np.abs(lse_ref[live])).max()),
+           "lse_max_abs": float(dl.max())}
+    if w.dtype != "f32":
+        ax = np.maximum(np.abs(o_ref[live]), np.finfo(np.float32).tiny)
+        half_ulp = 0.5 * np.exp2(np.floor(np.log2(ax)) - (10 if w.dtype == "f16" else 7))
+        rec["o_over_2e-2"] = int((do > 2e-2).sum())
+        rec["o_ulp_aware_ok"] = bool(np.all(do <= 2e-2 + half_ulp))
+        if o32 is not None:
+            rec["o_f32_max_abs"] = float(np.abs(o32.cpu().numpy()[live] - o_ref[live]).max())
+    return rec
 
 
 def settle(torch, fn, ms: float):
@@ -193,6 +284,77 @@ def decode_leg(fa, torch, dev, stream, steps: int, settle_ms: float):
     return rec
 
 
+def config_leg(fa, torch, w: W.Workload, steps: int, settle_ms: float, dev, stream):
+    """A workload other than the headline one, timed on its own after the
+    headline's legs (not part of `value`): the forward alone on resident
+    inputs with a BlockMask built once, its effective and dense-equivalent
+    rates, its roofline fraction, and its errors against the oracle on whole
+    heads (all of them for the fp32 workload, the first and the last (b, h)
+    for the others). Inputs are freed before returning."""
+    import oracle  # noqa: E402  (error check only)
+    inp = W.generate(w)
+    tdtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x).to(tdtype).to(dev) for x in (inp.q, inp.k, inp.v))
+    doc = torch.from_numpy(inp.doc_ids).to(dev) if inp.doc_ids is not None else None
+    bm = fa.create_block_mask(w.mask, 1, 1, w.Q_LEN, w.KV_LEN, 128, window=w.window,
+                              num_sinks=w.sinks, doc_ids=doc, device=dev, stream=stream)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def call():
+        fa.flex_attention(q, k, v, bm, score=w.score, softcap=w.softcap, scale=w.scale, out=out,
+                          lse=lse, stream=stream)
+    settle(torch, call, settle_ms)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.median(times))
+    pairs = allowed_pairs_per_head(w, inp.doc_lengths)
+    eff = 4.0 * w.D * pairs * w.B * w.Hq
+    dense = 4.0 * w.D * w.Q_LEN * w.KV_LEN * w.B * w.Hq
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
+    alg = algorithmic_bytes(w, bm.num_q_blocks, bm.num_kv_blocks)
+    traffic = measured_traffic(w.name) if w.dtype == "bf16" else None
+    t = ms * 1e-3
+    rec = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Q_LEN": w.Q_LEN,
+           "KV_LEN": w.KV_LEN, "D": w.D, "dtype": w.dtype, "mask": w.mask, "score": w.score,
+           "seed": w.seed, "calls": steps,
+           "fwd_ms_median": round(ms, 4), "fwd_ms_min": round(float(np.min(times)), 4),
+           "effective_tflops": round(eff / t / 1e12, 2),
+           "dense_equivalent_tflops": round(dense / t / 1e12, 2),
+           "unmasked_fraction": round(pairs / (w.Q_LEN * w.KV_LEN), 4),
+           "peak": peak, "frac": round(eff / t / 1e12 / peak, 4),
+           "algorithmic_bytes": alg, "algorithmic_gbs": round(alg / t / 1e9, 1),
+           "traffic": traffic,
+           "traffic_gbs": round(traffic / t / 1e9, 1) if traffic else None,
+           "mfma_util_pct": measured_traffic(w.name, "mfma_util_pct") if w.dtype == "bf16"
+           else None}
+    if inp.doc_lengths is not None:
+        rec["doc_lengths"] = [int(x) for x in inp.doc_lengths]
+    o32 = None
+    if w.dtype != "f32":
+        o32 = fa.flex_attention_train(q, k, v, bm, score=w.score, softcap=w.softcap,
+                                      scale=w.scale, stream=stream)[2]
+    torch.cuda.synchronize()
+    pairs_bh = ([(b, h) for b in range(w.B) for h in range(w.Hq)] if w.dtype == "f32"
+                else [(0, 0), (w.B - 1, w.Hq - 1)])
+    mask, score = oracle.for_workload(w, inp)
+    o_ref = np.full(tuple(out.shape), np.nan)
+    lse_ref = np.full(tuple(lse.shape), np.nan)
+    for b, h in pairs_bh:
+        ob, lb = oracle.attention(inp.q, inp.k, inp.v, mask, score, w.scale, batches=[b],
+                                  heads=[h])
+        o_ref[b, h], lse_ref[b, h] = ob[b, h], lb[b, h]
+    rec["errors"] = errors_vs_oracle(w, out, lse, o32, o_ref, lse_ref)
+    del q, k, v, out, lse, o32, bm
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +377,9 @@ def main(argv=None):
     ap.add_argument("--f16-steps", type=int, default=20,
                     help="after the forward, time this many forwards of the same workload with "
                          "fp16 inputs (bf16 workloads; 0 = skip)")
+    ap.add_argument("--config-steps", type=int, default=20,
+                    help="after the headline legs, time this many forwards of each of the other "
+                         "workloads and check their errors against the oracle (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB "
                          "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -294,6 +459,14 @@ def main(argv=None):
     ms_step = total_ms / args.steps
     build_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
     fwd_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
+
+    # the headline's fp32 O (same kernel, written before rounding) for the
+    # error report
+    o32_main = None
+    if w.dtype != "f32":
+        o32_main = fa.flex_attention_train(q, k, v, bm, score=w.score, softcap=w.softcap,
+                                           scale=w.scale, stream=stream)[2].cpu()
+    out_main, lse_main = out.clone(), lse.clone()
 
     # Full-tile ablation (after the timed region, not part of `value`): the
     # same forward on a BlockMask built with separate_full_blocks=False, so
@@ -399,6 +572,14 @@ def main(argv=None):
     if args.decode_steps > 0:
         decode = decode_leg(fa, torch, dev, stream, args.decode_steps, args.settle_ms)
 
+    configs = {}
+    if args.config_steps > 0:
+        for other in W.WORKLOADS:
+            if other.name != w.name:
+                configs[other.name] = config_leg(fa, torch, other, args.config_steps,
+                                                 args.settle_ms, dev, stream)
+    facts = device_facts(torch)
+
     pairs = allowed_pairs_per_head(w, inp.doc_lengths)
     eff_flops = 4.0 * w.D * pairs * w.B * w.Hq
     dense_flops = 4.0 * w.D * w.Q_LEN * w.KV_LEN * w.B * w.Hq
@@ -450,7 +631,12 @@ def main(argv=None):
             "mfma_util_pct": (measured_traffic(w.name, "mfma_util_pct")
                               if w.dtype == "bf16" else None),
         },
+        "device": facts,
     }
+    tr = rec["roofline"]["traffic"]
+    rec["roofline"]["hbm_gbs"] = round(tr / (fwd_avg * 1e-3) / 1e9, 1) if tr else None
+    if configs:
+        rec["configs"] = configs
     if ablation is not None:
         rec["full_tile_ablation"] = ablation
     if backward is not None:
@@ -479,7 +665,8 @@ def main(argv=None):
     if inp.doc_lengths is not None:
         rec["config"]["doc_lengths"] = [int(x) for x in inp.doc_lengths]
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+        rec["cpu_baseline"], o_ref, lse_ref = cpu_baseline(w, inp, args.cpu_budget)
+        rec["errors"] = errors_vs_oracle(w, out_main, lse_main, o32_main, o_ref, lse_ref)
     print(json.dumps(rec), flush=True)
     return 0
 

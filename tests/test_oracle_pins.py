@@ -523,3 +523,30 @@ def test_block_mask_non_square_brute_force(kind, kblk, qblk):
     bm = oracle.create_block_mask(_oracle_mask(kind, doc), 1, 1, q_len, kv_len, (kblk, qblk))
     cls = pins.brute_force_tiles(SCALAR_MASKS[kind](doc), 1, 1, q_len, kv_len, kblk, qblk)
     assert pins.block_mask_matches(bm, pins.lists_from_classes(cls))
+
+
+@pytest.mark.parametrize("B,H", [(1, 1), (2, 3)])
+def test_unmasked_pairs_closed_forms(B, H):
+    """unmasked_pairs counts the allowed (q, kv) elements of every (b, h):
+    closed forms for noop (M N), causal (L (L + 1) / 2), the document mask
+    (sum over documents of n (n + 1) / 2) and the sliding window with sinks
+    (row q sees min(q + 1, W) window keys plus the sinks below the window),
+    and brute force over the dense mask on a ragged shape."""
+    L = 1000
+    scale = B * H
+    assert oracle.unmasked_pairs(oracle.create_block_mask(oracle.noop_mask, B, H, 300, 700,
+                                                          128)) == scale * 300 * 700
+    assert oracle.unmasked_pairs(oracle.create_block_mask(oracle.causal_mask, B, H, L, L,
+                                                          128)) == scale * L * (L + 1) // 2
+    lens = np.array([123, 1, 400, 476])
+    doc = W.document_ids(lens)
+    bm = oracle.create_block_mask(oracle.document_causal_mask(doc), B, H, L, L, 128)
+    assert oracle.unmasked_pairs(bm) == scale * int((lens * (lens + 1) // 2).sum())
+    Wn, S = 64, 4
+    bm = oracle.create_block_mask(oracle.sliding_sink_mask(Wn, S), B, H, L, L, 128)
+    q = np.arange(L)
+    per_row = np.minimum(q + 1, Wn) + np.clip(np.minimum(S, q - Wn + 1), 0, None)
+    assert oracle.unmasked_pairs(bm) == scale * int(per_row.sum())
+    dense = oracle.create_mask(oracle.prefix_lm_mask(37), B, H, 150, 211)
+    bm = oracle.create_block_mask(oracle.prefix_lm_mask(37), B, H, 150, 211, 128)
+    assert oracle.unmasked_pairs(bm) == int(dense.sum())

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "BlockMask", "FlexAttnError", "MASK_KINDS", "SCORE_KINDS", "create_block_mask",
     "flex_attention", "flex_attention_backward", "block_mask_from_kv_blocks", "library_path",
-    "auto_splits", "fwd_plan", "flex_attention_train",
+    "auto_splits", "fwd_plan", "flex_attention_noalloc", "flex_attention_train",
     "load_library",
     "block_mask_sizes", "version",
 ]
@@ -122,6 +122,11 @@ def load_library():
         ctypes.POINTER(_BlockMask), ctypes.c_int, ctypes.POINTER(_ScoreParams), ctypes.c_float,
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(_Tensor),
         ctypes.c_void_p, ctypes.c_void_p]
+    lib.flexattn_fwd_splitkv_noalloc.restype = ctypes.c_int
+    lib.flexattn_fwd_splitkv_noalloc.argtypes = [
+        ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+        ctypes.POINTER(_BlockMask), ctypes.c_int, ctypes.POINTER(_ScoreParams), ctypes.c_float,
+        ctypes.c_int32, ctypes.POINTER(_Tensor), ctypes.c_void_p, ctypes.c_void_p]
     lib.flexattn_fwd_paged.restype = ctypes.c_int
     lib.flexattn_fwd_paged.argtypes = [
         ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
@@ -497,6 +502,37 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask
                           float(scale), ctypes.byref(to), ctypes.c_void_p(lse.data_ptr()),
                           _stream_handle(q.device, stream))
     _check(st, "flexattn_fwd")
+    return out, lse
+
+
+def flex_attention_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           block_mask: BlockMask, out: torch.Tensor, lse: torch.Tensor,
+                           num_splits: int, score: str = "none", softcap: float = 0.0,
+                           alibi_slopes: Optional[torch.Tensor] = None,
+                           scale: Optional[float] = None, stream=None):
+    """The split-KV forward with its partials in the library's own scratch
+    (flexattn_fwd_splitkv_noalloc): nothing is allocated, so out, lse and (for
+    ALiBi with explicit slopes) a contiguous float32 alibi_slopes on the
+    device must be given. Calls that overlap on one GPU race on the scratch."""
+    lib = load_library()
+    if score not in SCORE_KINDS:
+        raise NotImplementedError(f"score kind {score!r} is not one of {sorted(SCORE_KINDS)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, Hq, M]")
+    sp = _ScoreParams(float(softcap), None)
+    if alibi_slopes is not None:
+        if (alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_contiguous()
+                or alibi_slopes.device != q.device):
+            raise ValueError("alibi_slopes must be a contiguous float32 tensor on q's device")
+        sp.alibi_slopes = alibi_slopes.data_ptr()
+    tq, tk, tv, to = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v"), _tensor(out, "out")
+    st = lib.flexattn_fwd_splitkv_noalloc(
+        ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(block_mask._c),
+        SCORE_KINDS[score], ctypes.byref(sp), float(scale), int(num_splits), ctypes.byref(to),
+        ctypes.c_void_p(lse.data_ptr()), _stream_handle(q.device, stream))
+    _check(st, "flexattn_fwd_splitkv_noalloc")
     return out, lse
 
 

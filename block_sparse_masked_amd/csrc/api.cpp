@@ -13,6 +13,9 @@
 #include "fwd_plan.hpp"
 #include "launch.hpp"
 
+static_assert(FLEXATTN_SCRATCH_BYTES == fa::kFwdScratchBytes,
+              "the header's scratch size is the library's");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -584,6 +587,46 @@ flexattn_status flexattn_fwd_splitkv(const flexattn_tensor* q, const flexattn_te
                 num_splits);
   return fwd_impl(q, k, v, bm, score_kind, params, scale, out, lse, num_splits, workspace,
                   workspace_bytes, stream, who);
+}
+
+flexattn_status flexattn_fwd_splitkv_noalloc(const flexattn_tensor* q, const flexattn_tensor* k,
+                                             const flexattn_tensor* v,
+                                             const flexattn_block_mask* bm,
+                                             flexattn_score_kind score_kind,
+                                             const flexattn_score_params* params, float scale,
+                                             int32_t num_splits, flexattn_tensor* out, float* lse,
+                                             void* stream) {
+  static const char* who = "flexattn_fwd_splitkv_noalloc";
+  if (num_splits < 1)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: num_splits must be >= 1 (got %d)", who,
+                num_splits);
+  if (!q) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: q is NULL", who);
+  const size_t need = num_splits > 1 ? splitkv_bytes(q->B, q->H, q->L, q->D, num_splits) : 0;
+  if (need > fa::kFwdScratchBytes)
+    return fail(FLEXATTN_ERR_INVALID_ARG,
+                "%s: %d slices of B=%d Hq=%d Q_LEN=%d D=%d need %zu bytes of scratch; the "
+                "library's scratch holds %zu (use flexattn_fwd_splitkv with a workspace, or "
+                "fewer slices)", who, num_splits, q->B, q->H, q->L, q->D, need,
+                fa::kFwdScratchBytes);
+  if (stream) {
+    int dev = 0, sdev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+      return fail(FLEXATTN_ERR_HIP, "%s: cannot query the stream's device", who);
+    if (dev != sdev)
+      return fail(FLEXATTN_ERR_INVALID_ARG,
+                  "%s: the stream belongs to device %d, the current device is %d", who, sdev,
+                  dev);
+  }
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (num_splits > 1) {
+    const hipError_t e = fa::fwd_scratch(&ws, &ws_bytes);
+    if (e != hipSuccess)
+      return fail(FLEXATTN_ERR_HIP, "%s: scratch lookup failed: %s", who, hipGetErrorString(e));
+  }
+  return fwd_impl(q, k, v, bm, score_kind, params, scale, out, lse, num_splits, ws, ws_bytes,
+                  stream, who);
 }
 
 flexattn_status flexattn_fwd_train(const flexattn_tensor* q, const flexattn_tensor* k,

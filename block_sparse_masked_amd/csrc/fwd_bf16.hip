@@ -2,6 +2,8 @@
 // design notes are in fwd_bf16_kernel.hpp): argument set-up, the launch plan
 // (fwd_plan.hpp), dispatch to the kernel instantiations of
 // fwd_bf16_inst.hip, and the merge of split-KV slices.
+#include <mutex>
+
 #include "fwd_bf16_kernel.hpp"
 
 namespace fa {
@@ -133,6 +135,33 @@ hipError_t launch_impl(const FwdLaunch& L, hipStream_t stream) {
 
 
 }  // namespace
+
+// Scratch of the allocation-free split-KV entry point: the slices' fp32
+// partial O and LSE. One copy per GPU, held until the process ends; every
+// call on a GPU reuses it (calls that overlap on one GPU race).
+__device__ __align__(256) float scratch[kFwdScratchBytes / sizeof(float)];
+
+hipError_t fwd_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // the array's device address on this GPU (its name is a host-side
+    // stand-in that must never reach a kernel)
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kFwdScratchBytes;
+  return hipSuccess;
+}
 
 int fwd_bf16_lds_bytes(int D, int NKB, bool paged) {
   (void)D;

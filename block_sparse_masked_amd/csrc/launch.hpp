@@ -64,6 +64,10 @@ struct FwdLaunch {
 
 // the 16-bit forward: bf16 or fp16 (L.f16), contiguous or paged K/V (L.page_table)
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream);
+// the library's split-KV scratch on the current device (a file-scope device
+// array; its address is looked up once per device): no allocation
+constexpr size_t kFwdScratchBytes = size_t(32) << 20;
+hipError_t fwd_scratch(void** ptr, size_t* bytes);
 int fwd_bf16_lds_bytes(int D, int NKB, bool paged);  // LDS of the bf16 forward
 constexpr int kMaxLdsBytes = 160 * 1024;
 constexpr long long kMaxBf16RowStride = 1ll << 22;  // k/v row stride limit of the bf16 forward

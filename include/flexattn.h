@@ -353,6 +353,31 @@ flexattn_status flexattn_fwd_splitkv(const flexattn_tensor* q, const flexattn_te
                                      flexattn_tensor* out, float* lse, void* stream);
 
 /*
+ * flexattn_fwd_splitkv without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The slices' fp32 partials go to a
+ * scratch array inside the library: one copy of FLEXATTN_SCRATCH_BYTES
+ * (32 MiB) per GPU, held until the process ends; the first call on a device
+ * looks up its address there (no allocation). The call allocates nothing
+ * and frees nothing. Same arguments, method and outputs as
+ * flexattn_fwd_splitkv minus the workspace; num_splits = 1 runs flexattn_fwd.
+ * INVALID_ARG when the partials need more than the scratch holds
+ * (flexattn_fwd_splitkv_workspace_bytes(B, Hq, Q_LEN, D, num_splits) >
+ * FLEXATTN_SCRATCH_BYTES) or when `stream` belongs to another device than
+ * the current one. Every call on one GPU shares its scratch, which keeps the
+ * last call's contents: calls that overlap in time on one GPU (several
+ * streams, several host threads) race and must be ordered by the caller.
+ */
+#define FLEXATTN_SCRATCH_BYTES (32u * 1024u * 1024u)
+flexattn_status flexattn_fwd_splitkv_noalloc(const flexattn_tensor* q, const flexattn_tensor* k,
+                                             const flexattn_tensor* v,
+                                             const flexattn_block_mask* bm,
+                                             flexattn_score_kind score_kind,
+                                             const flexattn_score_params* params, float scale,
+                                             int32_t num_splits, flexattn_tensor* out, float* lse,
+                                             void* stream);
+
+/*
  * Paged KV cache (page "FlagAttention", operator overview: paged attention,
  * queries over a KV cache kept in fixed-size pages). The cache holds
  * num_pages pages of page_size key rows per KV head; a sequence's keys are

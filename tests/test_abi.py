@@ -372,3 +372,25 @@ def test_training_pair_rejects_bad_arguments(L):
 def test_create_rejects_block_sizes(L):
     assert _create(L, 1, lib._MaskParams(0, 0, None, 0, 0), block=640) == lib._UNSUPPORTED
     assert _create(L, 1, lib._MaskParams(0, 0, None, 0, 0), block=192) == lib._UNSUPPORTED
+
+
+def test_noalloc_rejects_oversized_partials_on_the_host(L):
+    """The allocation-free split-KV entry point refuses, before any HIP call,
+    a request whose partials exceed the library's fixed scratch, and a slice
+    count below 1; the message names the scratch size."""
+    q = _tensor(B=8, H=32, L_=64, D=128)
+    k = _tensor(B=8, H=8, L_=4096, D=128)
+    bm = _good_bm()
+    sp = lib._ScoreParams(0.0, None)
+    o = _tensor(B=8, H=32, L_=64, D=128)
+    fn = L.flexattn_fwd_splitkv_noalloc
+    need = L.flexattn_fwd_splitkv_workspace_bytes(8, 32, 64, 128, 32)
+    assert need > 32 * 1024 * 1024
+    assert fn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(bm), 0,
+              ctypes.byref(sp), 0.125, 32, ctypes.byref(o), ctypes.c_void_p(4096),
+              None) == lib._INVALID
+    assert b"scratch" in L.flexattn_last_error() and str(32 * 1024 * 1024).encode() in \
+        L.flexattn_last_error()
+    assert fn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(bm), 0,
+              ctypes.byref(sp), 0.125, 0, ctypes.byref(o), ctypes.c_void_p(4096),
+              None) == lib._INVALID

@@ -151,7 +151,7 @@ __device__ __forceinline__ bool allowed_el(const MaskParams& mp, int q, int kv, 
   } else if constexpr (MASK == MASK_COMPOSITE) {
     return composite_allowed(mp, q, kv, dq, dkv);
   } else {
-    return kv <= q && dq == dkv;
+    return (kv <= q) & (dq == dkv);
   }
 }
 

@@ -64,14 +64,18 @@ __device__ __forceinline__ void term_interval(int bits, int q, const MaskParams&
 
 // Composite mask of one element; dq / dkv are the document ids of the query
 // and key (read only when a term has the document primitive).
+// Evaluated without branches: every term slot is tested and the unused ones
+// are masked out, so a per-element test compiles to compares and selects.
 __device__ __forceinline__ bool composite_allowed(const MaskParams& p, int q, int kv, int dq,
                                                   int dkv) {
   bool any = false;
-  for (int t = 0; t < p.nterms; ++t) {
+#pragma unroll
+  for (int t = 0; t < kMaxTerms; ++t) {
     const int bits = p.terms[t];
     int lo, hi;
     term_interval(bits, q, p, lo, hi);
-    any = any || (kv >= lo && kv <= hi && (!(bits & PRIM_DOCUMENT) || dq == dkv));
+    const bool in = (kv >= lo) & (kv <= hi) & ((bits & PRIM_DOCUMENT) == 0 | dq == dkv);
+    any = any | (in & (t < p.nterms));
   }
   return any;
 }
@@ -133,7 +137,7 @@ template <>
 struct Mask<MASK_DOCUMENT> {
   // doc: this batch's document id row.
   __device__ __forceinline__ static bool allowed(const MaskParams&, const int* doc, int q, int kv) {
-    return kv <= q && doc[q] == doc[kv];
+    return (kv <= q) & (doc[q] == doc[kv]);  // both ids in range: no short circuit needed
   }
 };
 

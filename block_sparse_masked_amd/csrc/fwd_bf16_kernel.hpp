@@ -417,19 +417,23 @@ __device__ __forceinline__ float elem_logit(float x, int blk, int r, int kv0, co
     y = ScoreMod<SCORE>::apply(x, a.c_scale, a.c_cap, a.cap2, ln.slope2, (float)(key - ln.q));
   }
   if constexpr (MASKED) {
+    // conditions combined with & and |, not && and ||: every operand is
+    // safe to evaluate (the document ids of the step are in LDS), and
+    // short-circuit forms turned each element's test into a branch
     const int c = key_off(blk, r);
     bool ok = c <= ml.hi;
-    if constexpr (MASK == MASK_SLIDING_SINK) ok = ok && (c > ml.win_lo || c < ml.sink_hi);
-    if constexpr (MASK == MASK_DOCUMENT) ok = ok && step_doc[c + 4 * ln.hh] == ln.dq;
+    if constexpr (MASK == MASK_SLIDING_SINK) ok = ok & ((c > ml.win_lo) | (c < ml.sink_hi));
+    if constexpr (MASK == MASK_DOCUMENT) ok = ok & (step_doc[c + 4 * ln.hh] == ln.dq);
     if constexpr (MASK == MASK_COMPOSITE) {
       bool any = false;
+      const bool same_doc = step_doc[c + 4 * ln.hh] == ln.dq;  // ids in LDS (composite)
 #pragma unroll
       for (int t = 0; t < kMaxTerms; ++t) {
-        bool in = c >= ml.tlo[t] && c <= ml.thi[t];
-        if (a.mp.terms[t] & PRIM_DOCUMENT) in = in && step_doc[c + 4 * ln.hh] == ln.dq;
-        any = any || in;
+        bool in = (c >= ml.tlo[t]) & (c <= ml.thi[t]);
+        if (a.mp.terms[t] & PRIM_DOCUMENT) in = in & same_doc;
+        any = any | in;
       }
-      ok = ok && any;
+      ok = ok & any;
     }
     y = ok ? y : -INFINITY;
   }
@@ -564,17 +568,18 @@ __device__ __forceinline__ float elem_logit16(float x, int blk, int r, int kv0,
   }
   if constexpr (MASKED) {
     bool ok = c <= ml.hi;
-    if constexpr (MASK == MASK_SLIDING_SINK) ok = ok && (c > ml.win_lo || c < ml.sink_hi);
-    if constexpr (MASK == MASK_DOCUMENT) ok = ok && step_doc[c + 4 * ln.g4] == ln.dq;
+    if constexpr (MASK == MASK_SLIDING_SINK) ok = ok & ((c > ml.win_lo) | (c < ml.sink_hi));
+    if constexpr (MASK == MASK_DOCUMENT) ok = ok & (step_doc[c + 4 * ln.g4] == ln.dq);
     if constexpr (MASK == MASK_COMPOSITE) {
       bool any = false;
+      const bool same_doc = step_doc[c + 4 * ln.g4] == ln.dq;  // ids in LDS (composite)
 #pragma unroll
       for (int t = 0; t < kMaxTerms; ++t) {
-        bool in = c >= ml.tlo[t] && c <= ml.thi[t];
-        if (a.mp.terms[t] & PRIM_DOCUMENT) in = in && step_doc[c + 4 * ln.g4] == ln.dq;
-        any = any || in;
+        bool in = (c >= ml.tlo[t]) & (c <= ml.thi[t]);
+        if (a.mp.terms[t] & PRIM_DOCUMENT) in = in & same_doc;
+        any = any | in;
       }
-      ok = ok && any;
+      ok = ok & any;
     }
     y = ok ? y : -INFINITY;
   }

@@ -216,14 +216,24 @@ __device__ __forceinline__ i32x4 make_rsrc(unsigned long long base, unsigned byt
 // cycles, so the step spreads them between its matrix instructions.
 // The LDS address is wave-uniform by construction; readfirstlane states that
 // to the compiler so the asm operand is always a scalar register.
+// The compiler's hazard recognizer does not look inside inline asm, so the
+// block keeps the CDNA wait states itself: an LDS DMA that reads M0 needs
+// one wait state after the scalar write of M0 (without it the load can take
+// the previous M0, i.e. land on the previous load's LDS slot), and a vector
+// memory instruction needs five after a vector instruction wrote one of its
+// scalar operands (the resource words come from readfirstlane). s_nop n
+// gives n + 1 wait states: 3 + 1 (the M0 move) + 1 = 5 before the load.
+#define FA_LDS_DMA(op)                                                          \
+  "s_nop 2\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\t" op " %1, %2, 0 offen lds"
 __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile(FA_LDS_DMA("buffer_load_dwordx4")
                : : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "m0");
 }
 __device__ __forceinline__ void dma4(i32x4 rsrc, unsigned lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  asm volatile(FA_LDS_DMA("buffer_load_dword")
                : : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "m0");
 }
+#undef FA_LDS_DMA
 
 // Loads of one [NK][D] step block of K or V. Each wave-wide load fills one
 // contiguous KiB of LDS (lane l writes bytes [16 l, 16 l + 16)), so each lane

@@ -375,6 +375,41 @@ __device__ __forceinline__ typename Elem<F16>::V8 k_frag(const u16* sK, const La
   return as_v8<F16>(*reinterpret_cast<const uint4*>(sK + ln.kofs[ks] + 32 * blk * D));
 }
 
+// Fragment reads from per-step LDS byte bases. With one step per BlockMask
+// tile (D = 64) a step's buffer is known only at run time, and the compiler
+// rebuilt every fragment address from the buffer's base (one vector OR per
+// V k-step and d-block, one per K k-step: 20 a step). A base per K k-step and
+// per V d-block, formed once a step in a register the compiler treats as
+// opaque, lets every read carry its constant part in the offset field.
+__device__ __forceinline__ unsigned opaque_lds(const void* p, int elem_ofs) {
+  unsigned a = lds_addr(p) + 2u * (unsigned)elem_ofs;
+  asm("" : "+v"(a));
+  return a;
+}
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int D, bool F16>
+__device__ __forceinline__ typename Elem<F16>::V8 k_frag_at(unsigned kbase, int blk) {
+  const u32x4 raw = *reinterpret_cast<lds_u32x4*>(kbase + 2u * (unsigned)(32 * blk * D));
+  typename Elem<F16>::V8 r;
+  __builtin_memcpy(&r, &raw, 16);
+  return r;
+}
+
+template <int D, bool F16>
+__device__ __forceinline__ typename Elem<F16>::V8 v_frag_at(unsigned vbase, int ks) {
+  typename Elem<F16>::V4 part[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_s16x4*>(vbase + 2u * (unsigned)((16 * ks + 8 * ht) * D)));
+    __builtin_memcpy(&part[ht], &raw, 8);
+  }
+  return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Key offset (within the step, without 4*hh) of result register r of block blk.
 __device__ __forceinline__ constexpr int key_off(int blk, int r) {
   return 32 * blk + 8 * (r >> 2) + (r & 3);
@@ -459,6 +494,14 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
                                      int kv0, const int* step_doc, const FwdArgs& a,
                                      const Lane<D>& ln, DMA&& dma) {
   using G = Geom<D>;
+  constexpr bool kOpaque = G::SPT == 1;  // run-time buffer: fixed per-step bases
+  unsigned kb[G::KS], vb[G::DB];
+  if constexpr (kOpaque) {
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) kb[ks] = opaque_lds(sK, ln.kofs[ks]);
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) vb[db] = opaque_lds(sV, ln.vofs[db]);
+  }
   f32x16 s[G::NB];
 #pragma unroll
   for (int b = 0; b < G::NB; ++b) s[b] = f32x16{};
@@ -467,7 +510,8 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
 #pragma unroll
     for (int b = 0; b < G::NB; ++b)
     {
-      s[b] = Elem<F16>::mfma(k_frag<D, F16>(sK, ln, ks, b), qf[ks], s[b]);
+      const auto kf = kOpaque ? k_frag_at<D, F16>(kb[ks], b) : k_frag<D, F16>(sK, ln, ks, b);
+      s[b] = Elem<F16>::mfma(kf, qf[ks], s[b]);
       // the next step's loads, spread over the S products
       constexpr int NS = G::KS * G::NB;
       static_assert(NS % NDMA == 0, "loads spread evenly");
@@ -523,8 +567,10 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
 #pragma unroll
   for (int ks = 0; ks < G::PKS; ++ks)
 #pragma unroll
-    for (int db = 0; db < G::DB; ++db)
-      o[db] = Elem<F16>::mfma(v_frag<D, F16>(sV, ln, ks, db), pf[ks], o[db]);
+    for (int db = 0; db < G::DB; ++db) {
+      const auto vf = kOpaque ? v_frag_at<D, F16>(vb[db], ks) : v_frag<D, F16>(sV, ln, ks, db);
+      o[db] = Elem<F16>::mfma(vf, pf[ks], o[db]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -751,27 +797,14 @@ fwd_bf16_kernel(FwdArgs a) {
   const int wph = a.wph;
   const int HPW = WAVES / wph;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // D <= 128: a KV group's heads in packs of HPW; when G is not a multiple
-  // of HPW the group's last pack is partial, and its spare waves take the
-  // group's last head, load and synchronise like the others, and store
-  // nothing. D = 256: whole packs only (G a multiple of HPW).
-  Item it;
-  int b, h, hk;
-  bool hvalid = true;
-  if constexpr (D <= 128) {
-    const int gpk = (a.G + HPW - 1) / HPW;  // packs per KV group
-    it = decode_item(x, a.bm, a.B, (a.Hq / a.G) * gpk);
-    const PackedHead ph = packed_head(it.h, a.G, HPW, wave / wph);
-    b = it.b;
-    h = ph.h;
-    hk = ph.hk;
-    hvalid = ph.valid;
-  } else {
-    it = decode_item(x, a.bm, a.B, a.Hq / HPW);
-    b = it.b;
-    h = it.h * HPW + wave / wph;
-    hk = (it.h * HPW) / a.G;
-  }
+  // a KV group's heads in packs of HPW; when G is not a multiple of HPW the
+  // group's last pack is partial, and its spare waves take the group's last
+  // head, load and synchronise like the others, and store nothing
+  const int gpk = (a.G + HPW - 1) / HPW;  // packs per KV group
+  const Item it = decode_item(x, a.bm, a.B, (a.Hq / a.G) * gpk);
+  const PackedHead ph = packed_head(it.h, a.G, HPW, wave / wph);
+  const int b = it.b, h = ph.h, hk = ph.hk;
+  const bool hvalid = ph.valid;
   const int q_tile0 = it.qb * a.bm.QBS + qsub * kBlock;
   if (q_tile0 >= a.Q_LEN) return;  // a 128-row tile past Q_LEN (BLOCK_SIZE > 128)
   Lane<D> ln;

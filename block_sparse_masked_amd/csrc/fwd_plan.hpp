@@ -43,7 +43,8 @@ inline FwdPlan plan_fwd(int B, int Hq, int Hkv, int Q_LEN, int D, int bm_B, int 
       }
   // No exact packing (G a multiple of neither 4 nor 2): packs of W / waves
   // heads with a partial last pack per KV group, as long as real heads fill
-  // at least half of a group's slots (G = 3, 5, 7, ...); head dims <= 128.
+  // at least half of a group's slots (G = 3, 5, 7, ...). Head dims <= 128
+  // only: head dim 256 keeps whole packs (one head per workgroup here).
   if (D <= 128 && bm_H == 1 && Q_LEN <= 64 && p.wph == W) {
     const int w = Q_LEN <= 32 ? 1 : 2;
     if (2 * G > W / w) p.wph = w;

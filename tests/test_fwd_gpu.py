@@ -274,7 +274,7 @@ def test_fwd_short_query_heads_packed(lib, q_len, Hq, Hkv, mask, score, splits):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("Hq,Hkv", [(6, 2), (14, 2), (5, 1)])
 @pytest.mark.parametrize("mask", ["document_causal", "composite"])
 @pytest.mark.parametrize("q_len", [16, 40])
@@ -284,7 +284,8 @@ def test_fwd_ragged_packs_dtypes(lib, dtype, D, Hq, Hkv, mask, q_len, splits):
     head dims 64 and 128, on the masks that read document ids (document
     causal; a composite of same-document-causal OR sinks): 16 queries take
     the 16-row step with packs of four heads, 40 queries two waves a head
-    with packs of two."""
+    with packs of two. Head dim 256 runs the same shapes one head a
+    workgroup."""
     terms = (("causal", "document"), ("sink",)) if mask == "composite" else None
     w = tiny(dtype, D, mask, "alibi", B=2, Hq=Hq, Hkv=Hkv, Q_LEN=q_len, KV_LEN=700,
              doc_len_range=(40, 300), terms=terms)

@@ -65,6 +65,11 @@ def algorithmic_bytes(w: W.Workload, nqb: int, nkb: int) -> int:
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def note(msg: str) -> None:
+    """A progress line on stderr as each leg ends (stdout keeps the one JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 KERNEL_SOURCES = ("fwd_bf16.hip", "fwd_bf16_inst.hip", "fwd_bf16_kernel.hpp", "fwd_plan.hpp",
                   "common.hpp", "fwd_common.hpp")
 
@@ -459,6 +464,7 @@ def main(argv=None):
     ms_step = total_ms / args.steps
     build_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
     fwd_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
+    note(f"{args.steps} timed steps of {w.name}: {ms_step:.4f} ms per step")
 
     # the headline's fp32 O (same kernel, written before rounding) for the
     # error report
@@ -493,6 +499,7 @@ def main(argv=None):
                     "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
                     "speedup_from_full_tiles": round(all_partial_ms / float(np.median(fwd_ms)), 4),
                     "calls": args.ablation_steps}
+        note("full-tile ablation done")
 
     # Backward (after the forward's timed region, not part of `value`): one
     # flexattn_bwd call per step on the same inputs with a seeded upstream
@@ -540,6 +547,7 @@ def main(argv=None):
         backward["ms_median_from_out"] = round(
             float(np.median([a.elapsed_time(b) for a, b in ev_b])), 4)
         del o32
+        note("backward done")
 
     # fp16 (after the timed region, not part of `value`): the same workload
     # drawn and rounded as fp16, forward only
@@ -567,10 +575,12 @@ def main(argv=None):
         f16 = {"ms_median": round(float(np.median([a.elapsed_time(b) for a, b in ev_h])), 4),
                "calls": args.f16_steps}
         del q16, k16, v16, out16
+        note("fp16 leg done")
 
     decode = None
     if args.decode_steps > 0:
         decode = decode_leg(fa, torch, dev, stream, args.decode_steps, args.settle_ms)
+        note("decode leg done")
 
     configs = {}
     if args.config_steps > 0:
@@ -578,6 +588,7 @@ def main(argv=None):
             if other.name != w.name:
                 configs[other.name] = config_leg(fa, torch, other, args.config_steps,
                                                  args.settle_ms, dev, stream)
+                note(f"{other.name} leg done")
     facts = device_facts(torch)
 
     pairs = allowed_pairs_per_head(w, inp.doc_lengths)
@@ -667,6 +678,7 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], o_ref, lse_ref = cpu_baseline(w, inp, args.cpu_budget)
         rec["errors"] = errors_vs_oracle(w, out_main, lse_main, o32_main, o_ref, lse_ref)
+        note("cpu baseline done")
     print(json.dumps(rec), flush=True)
     return 0
 

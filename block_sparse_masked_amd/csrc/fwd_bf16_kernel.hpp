@@ -423,9 +423,10 @@ struct MaskLimits {
   int tlo[kMaxTerms], thi[kMaxTerms];  // COMPOSITE: allowed offsets of each term
 };
 
+// base: the key the lane's offsets count from (kv0 + 4*hh in the 32-row
+// layout, kv0 + 4*g4 in the 16-row one).
 template <int D, int MASK>
-__device__ __forceinline__ MaskLimits mask_limits(int kv0, const FwdArgs& a, const Lane<D>& ln) {
-  const int base = kv0 + 4 * ln.hh;
+__device__ __forceinline__ MaskLimits mask_limits(int base, const FwdArgs& a, const Lane<D>& ln) {
   MaskLimits m;
   m.hi = a.KV_LEN - 1 - base;
   if constexpr (MASK == MASK_PREFIX_LM) m.hi = min(m.hi, max(ln.qc, a.mp.prefix - 1) - base);
@@ -448,18 +449,55 @@ __device__ __forceinline__ MaskLimits mask_limits(int kv0, const FwdArgs& a, con
   return m;
 }
 
+// Score-mod kinds (ALiBi, softcap, both) form each logit relative to the
+// reference max in use before the step, z = y - m_old, from one per-step,
+// per-lane constant
+//   zbase = [cap2] + [slope2 * (first key of the lane - q)] - m_old
+// and the register's compile-time key offset c:
+//   softcap:  z = cap2 * (1 - 2 / (exp(2 s / cap) + 1)) + ... = fma(r, -2 cap2, t)
+//   ALiBi:    t = fma(slope2, c, zbase), z = fma(s, scale, t) without softcap
+// so the bias costs one FMA per score and exp2(z) needs no subtraction (a
+// step that raises the reference shifts its z once, in the rare rescale).
+template <int SCORE>
+constexpr bool kRelLogit =
+    SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP || SCORE == SCORE_SOFTCAP_ALIBI;
+
+template <int SCORE>
+__device__ __forceinline__ float rel_logit(float x, float c, float zbase, const FwdArgs& a,
+                                           float slope2) {
+  constexpr bool kSoft = SCORE == SCORE_SOFTCAP || SCORE == SCORE_SOFTCAP_ALIBI;
+  constexpr bool kAlibi = SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI;
+  const float t = kAlibi ? fmaf(slope2, c, zbase) : zbase;
+  if constexpr (kSoft) {
+    const float e = fast_exp2(x * a.c_cap);
+    return fmaf(fast_rcp(e + 1.0f), -2.0f * a.cap2, t);
+  } else {
+    return fmaf(x, a.c_scale, t);
+  }
+}
+
+template <int SCORE>
+__device__ __forceinline__ float rel_logit_base(float m_old, int key0_minus_q, const FwdArgs& a,
+                                                float slope2) {
+  float z = -m_old;
+  if constexpr (SCORE == SCORE_SOFTCAP || SCORE == SCORE_SOFTCAP_ALIBI) z += a.cap2;
+  if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
+    z = fmaf(slope2, (float)key0_minus_q, z);
+  return z;
+}
+
 // Logit of one score: y = score_mod(x) in base-2 units (raw x for
-// SCORE_NONE, scaled later), -inf where masked on partial tiles.
+// SCORE_NONE, scaled later; z = y - m_old for the score-mod kinds), -inf
+// where masked on partial tiles.
 template <int D, int MASK, int SCORE, bool MASKED>
-__device__ __forceinline__ float elem_logit(float x, int blk, int r, int kv0, const MaskLimits& ml,
-                                            const int* step_doc, const FwdArgs& a,
-                                            const Lane<D>& ln) {
+__device__ __forceinline__ float elem_logit(float x, int blk, int r, float zbase,
+                                            const MaskLimits& ml, const int* step_doc,
+                                            const FwdArgs& a, const Lane<D>& ln) {
   float y = x;
   if constexpr (SCORE == SCORE_SCALED) {
     y = x * a.c_scale;
-  } else if constexpr (SCORE != SCORE_NONE) {
-    const int key = kv0 + key_off(blk, r) + 4 * ln.hh;
-    y = ScoreMod<SCORE>::apply(x, a.c_scale, a.c_cap, a.cap2, ln.slope2, (float)(key - ln.q));
+  } else if constexpr (kRelLogit<SCORE>) {
+    y = rel_logit<SCORE>(x, (float)key_off(blk, r), zbase, a, ln.slope2);
   }
   if constexpr (MASKED) {
     // conditions combined with & and |, not && and ||: every operand is
@@ -519,22 +557,29 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
       if (i % (NS / NDMA) == 0) dma(i / (NS / NDMA));
     }
 
-  const MaskLimits ml = mask_limits<D, MASK>(kv0, a, ln);
+  const MaskLimits ml = mask_limits<D, MASK>(kv0 + 4 * ln.hh, a, ln);
+  constexpr bool kRel = kRelLogit<SCORE>;
+  const float m_old = (m_ref == -INFINITY) ? 0.0f : m_ref;
+  const float zbase =
+      kRel ? rel_logit_base<SCORE>(m_old, kv0 + 4 * ln.hh - ln.q, a, ln.slope2) : 0.0f;
   float mx = -INFINITY;
 #pragma unroll
   for (int b = 0; b < G::NB; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s[b][r] = elem_logit<D, MASK, SCORE, MASKED>(s[b][r], b, r, kv0, ml, step_doc, a, ln);
+      s[b][r] = elem_logit<D, MASK, SCORE, MASKED>(s[b][r], b, r, zbase, ml, step_doc, a, ln);
       mx = fmaxf(mx, s[b][r]);
     }
   mx = pair_max(mx);
   if constexpr (SCORE == SCORE_NONE) mx *= a.c_scale;  // c_scale > 0 here
 
-  // lazy rescale (a real branch: rare)
-  if (__any(mx > m_ref + kRescaleSlack)) {
+  // lazy rescale (a real branch: rare); relative logits compare against the
+  // slack directly (any finite logit when there is no reference yet)
+  const float thr = kRel ? ((m_ref == -INFINITY) ? -INFINITY : kRescaleSlack)
+                         : m_ref + kRescaleSlack;
+  if (__any(mx > thr)) {
     asm volatile("");
-    const float m_new = fmaxf(m_ref, mx);
+    const float m_new = fmaxf(m_ref, kRel ? mx + m_old : mx);
     const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_ref - m_new);
     l *= alpha;
     lp *= alpha;
@@ -543,6 +588,13 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
     m_ref = m_new;
+    if constexpr (kRel) {
+      const float delta = ((m_new == -INFINITY) ? 0.0f : m_new) - m_old;
+#pragma unroll
+      for (int b = 0; b < G::NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[b][r] -= delta;
+    }
   }
   const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
 
@@ -554,6 +606,8 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
     float p;
     if constexpr (SCORE == SCORE_NONE) {
       p = fast_exp2(fmaf(y, a.c_scale, -m_use));
+    } else if constexpr (kRel) {
+      p = fast_exp2(y);
     } else {
       p = fast_exp2(y - m_use);
     }
@@ -611,16 +665,15 @@ __device__ __forceinline__ f32x4 mfma16(typename Elem<F16>::V8 a, typename Elem<
 
 // Logit of score r of 16-key block blk (key kv0 + 16*blk + 4*g4 + r).
 template <int D, int MASK, int SCORE, bool MASKED>
-__device__ __forceinline__ float elem_logit16(float x, int blk, int r, int kv0,
+__device__ __forceinline__ float elem_logit16(float x, int blk, int r, float zbase,
                                               const MaskLimits& ml, const int* step_doc,
                                               const FwdArgs& a, const Lane<D>& ln) {
   float y = x;
   const int c = 16 * blk + r;  // offset within the step, without 4*g4
   if constexpr (SCORE == SCORE_SCALED) {
     y = x * a.c_scale;
-  } else if constexpr (SCORE != SCORE_NONE) {
-    const int key = kv0 + c + 4 * ln.g4;
-    y = ScoreMod<SCORE>::apply(x, a.c_scale, a.c_cap, a.cap2, ln.slope2, (float)(key - ln.q));
+  } else if constexpr (kRelLogit<SCORE>) {
+    y = rel_logit<SCORE>(x, (float)c, zbase, a, ln.slope2);
   }
   if constexpr (MASKED) {
     bool ok = c <= ml.hi;
@@ -666,34 +719,17 @@ __device__ __forceinline__ void step16(f32x4 (&o)[D / 16], float& m_ref, float& 
     }
 
   // the mask limits relative to key kv0 + 4*g4
-  MaskLimits ml;
-  {
-    const int base = kv0 + 4 * ln.g4;
-    ml.hi = a.KV_LEN - 1 - base;
-    if constexpr (MASK == MASK_PREFIX_LM) ml.hi = min(ml.hi, max(ln.qc, a.mp.prefix - 1) - base);
-    else if constexpr (MASK != MASK_NOOP && MASK != MASK_COMPOSITE) ml.hi = min(ml.hi, ln.qc - base);
-    ml.win_lo = ln.qc - base - a.mp.window;
-    ml.sink_hi = a.mp.sinks - base;
-    if constexpr (MASK == MASK_COMPOSITE) {
-#pragma unroll
-      for (int t = 0; t < kMaxTerms; ++t) {
-        int lo = 1, hi = 0;
-        if (t < a.mp.nterms) {
-          term_interval(a.mp.terms[t], ln.qc, a.mp, lo, hi);
-          hi = min(hi, a.KV_LEN - 1) - base;
-          lo -= base;
-        }
-        ml.tlo[t] = lo;
-        ml.thi[t] = hi;
-      }
-    }
-  }
+  const MaskLimits ml = mask_limits<D, MASK>(kv0 + 4 * ln.g4, a, ln);
+  constexpr bool kRel = kRelLogit<SCORE>;
+  const float m_old = (m_ref == -INFINITY) ? 0.0f : m_ref;
+  const float zbase =
+      kRel ? rel_logit_base<SCORE>(m_old, kv0 + 4 * ln.g4 - ln.q, a, ln.slope2) : 0.0f;
   float mx = -INFINITY;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      s[b][r] = elem_logit16<D, MASK, SCORE, MASKED>(s[b][r], b, r, kv0, ml, step_doc, a, ln);
+      s[b][r] = elem_logit16<D, MASK, SCORE, MASKED>(s[b][r], b, r, zbase, ml, step_doc, a, ln);
       mx = fmaxf(mx, s[b][r]);
     }
   // a query's keys are spread over lanes c16, c16 + 16, c16 + 32, c16 + 48
@@ -701,9 +737,11 @@ __device__ __forceinline__ void step16(f32x4 (&o)[D / 16], float& m_ref, float& 
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   if constexpr (SCORE == SCORE_NONE) mx *= a.c_scale;  // c_scale > 0 here
 
-  if (__any(mx > m_ref + kRescaleSlack)) {
+  const float thr = kRel ? ((m_ref == -INFINITY) ? -INFINITY : kRescaleSlack)
+                         : m_ref + kRescaleSlack;
+  if (__any(mx > thr)) {
     asm volatile("");
-    const float m_new = fmaxf(m_ref, mx);
+    const float m_new = fmaxf(m_ref, kRel ? mx + m_old : mx);
     const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_ref - m_new);
     l *= alpha;
     lp *= alpha;
@@ -712,6 +750,13 @@ __device__ __forceinline__ void step16(f32x4 (&o)[D / 16], float& m_ref, float& 
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[i][r] *= alpha;
     m_ref = m_new;
+    if constexpr (kRel) {
+      const float delta = ((m_new == -INFINITY) ? 0.0f : m_new) - m_old;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[b][r] -= delta;
+    }
   }
   const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
 
@@ -725,6 +770,8 @@ __device__ __forceinline__ void step16(f32x4 (&o)[D / 16], float& m_ref, float& 
       float p;
       if constexpr (SCORE == SCORE_NONE) {
         p = fast_exp2(fmaf(y, a.c_scale, -m_use));
+      } else if constexpr (kRel) {
+        p = fast_exp2(y);
       } else {
         p = fast_exp2(y - m_use);
       }
@@ -864,15 +911,33 @@ fwd_bf16_kernel(FwdArgs a) {
   // this workgroup's slice [t_begin, t_end) of the item's tiles
   const int t_begin = (int)((long long)n * split / a.splits);
   const int t_end = (int)((long long)n * (split + 1) / a.splits);
+  // Walk order (position t -> 128-key tile index). ALiBi scores grow toward
+  // the diagonal, so an ascending walk raised the reference max (a rescale
+  // of O) on almost every step of a steep head; the ALiBi kinds walk the
+  // partial tiles, then the full ones, each by descending key, so causal rows
+  // start on their diagonal tile and the maximum is known from the first
+  // step. The other kinds walk the full tiles, then the partial ones, by
+  // ascending key.
+  constexpr bool kDesc = SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI;
+  const int npart = n - nfull;
   auto listed = [&](int t) {
-    const int c = t / mk;
-    const int idx = c < nfull_c ? a.bm.full_idx[lrow + c]
-                                : a.bm.kv_idx[lrow + min(c - nfull_c, a.bm.NKB - 1)];
-    return idx * mk + (t - c * mk);
+    if constexpr (kDesc) {
+      const bool part = t < npart;
+      const int u = part ? npart - 1 - t : n - 1 - t;  // ascending piece of its list
+      const int c = u / mk;
+      const int idx =
+          part ? a.bm.kv_idx[lrow + min(c, a.bm.NKB - 1)] : a.bm.full_idx[lrow + c];
+      return idx * mk + (u - c * mk);
+    } else {
+      const int c = t / mk;
+      const int idx = c < nfull_c ? a.bm.full_idx[lrow + c]
+                                  : a.bm.kv_idx[lrow + min(c - nfull_c, a.bm.NKB - 1)];
+      return idx * mk + (t - c * mk);
+    }
   };
   const int first_tile = listed(t_begin);
-  // the item's tiles, full then partial, staged in LDS once (paged KV: and
-  // each tile's physical page, after the tile list)
+  // the item's tiles in walk order, staged in LDS once (paged KV: and each
+  // tile's physical page, after the tile list)
   int* tpage = tlist + ((nlist + 3) & ~3);
   for (int t = threadIdx.x; t < n; t += THREADS) {
     const int idx = listed(t);
@@ -984,13 +1049,21 @@ fwd_bf16_kernel(FwdArgs a) {
       kv_tile_next = t_next < t_end ? tile_kv0(t_next) : 0;
       pg_next = tile_page(t_next);
     };
-    // full tiles that end inside KV_LEN take the unmasked path; a full tile
-    // crossing KV_LEN (never listed by the builder) is masked on the key bound
-    const int nfull_fast =
-        (nfull > 0 && tile_kv0(nfull - 1) + kBlock > a.KV_LEN) ? nfull - 1 : nfull;
+    // partial tiles take the masked path, full tiles the unmasked one; a
+    // full tile crossing KV_LEN (never listed by the builder; the highest
+    // full tile) is masked on the key bound
     int j = t_begin;
-    for (; j < min(nfull_fast, t_end); ++j) run_tile(std::false_type{});
-    for (; j < t_end; ++j) run_tile(std::true_type{});
+    if constexpr (kDesc) {
+      const int mask_end =
+          (nfull > 0 && tile_kv0(npart) + kBlock > a.KV_LEN) ? npart + 1 : npart;
+      for (; j < min(mask_end, t_end); ++j) run_tile(std::true_type{});
+      for (; j < t_end; ++j) run_tile(std::false_type{});
+    } else {
+      const int nfull_fast =
+          (nfull > 0 && tile_kv0(nfull - 1) + kBlock > a.KV_LEN) ? nfull - 1 : nfull;
+      for (; j < min(nfull_fast, t_end); ++j) run_tile(std::false_type{});
+      for (; j < t_end; ++j) run_tile(std::true_type{});
+    }
   }
 
   if constexpr (R16) {

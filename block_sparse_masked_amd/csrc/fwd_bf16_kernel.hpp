@@ -449,6 +449,25 @@ __device__ __forceinline__ MaskLimits mask_limits(int base, const FwdArgs& a, co
   return m;
 }
 
+// Whether any key of a step can be allowed for this lane's query row, from
+// the step's mask limits over the offsets [0, nk) (a superset of the lane's
+// keys; document ids are not consulted, so a document test never rules a
+// step out).
+template <int MASK>
+__device__ __forceinline__ bool step_may_attend(const MaskLimits& ml, int nk) {
+  const int top = min(ml.hi, nk - 1);
+  bool any = top >= 0;
+  if constexpr (MASK == MASK_SLIDING_SINK)
+    any = any & ((max(ml.win_lo + 1, 0) <= top) | (min(ml.sink_hi - 1, top) >= 0));
+  if constexpr (MASK == MASK_COMPOSITE) {
+    bool t_any = false;
+#pragma unroll
+    for (int t = 0; t < kMaxTerms; ++t) t_any = t_any | (max(ml.tlo[t], 0) <= min(ml.thi[t], top));
+    any = any & t_any;
+  }
+  return any;
+}
+
 // Score-mod kinds (ALiBi, softcap, both) form each logit relative to the
 // reference max in use before the step, z = y - m_old, from one per-step,
 // per-lane constant
@@ -917,13 +936,25 @@ fwd_bf16_kernel(FwdArgs a) {
   // partial tiles, then the full ones, each by descending key, so causal rows
   // start on their diagonal tile and the maximum is known from the first
   // step. The other kinds walk the full tiles, then the partial ones, by
-  // ascending key.
+  // ascending key; masks whose lowest partial tile can leave a whole 64-key
+  // step unattended (a sliding window's sink tile, a PrefixLM prefix tile)
+  // walk their partial tiles by descending key instead, so that tile comes
+  // last and its second step can be cut (see the half tile below).
   constexpr bool kDesc = SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI;
+  constexpr bool kHalfLast = SPT == 2 && !kDesc &&
+      (MASK == MASK_SLIDING_SINK || MASK == MASK_PREFIX_LM || MASK == MASK_COMPOSITE);
   const int npart = n - nfull;
   auto listed = [&](int t) {
     if constexpr (kDesc) {
       const bool part = t < npart;
       const int u = part ? npart - 1 - t : n - 1 - t;  // ascending piece of its list
+      const int c = u / mk;
+      const int idx =
+          part ? a.bm.kv_idx[lrow + min(c, a.bm.NKB - 1)] : a.bm.full_idx[lrow + c];
+      return idx * mk + (u - c * mk);
+    } else if constexpr (kHalfLast) {
+      const bool part = t >= nfull;
+      const int u = part ? n - 1 - t : t;  // ascending piece of its list
       const int c = u / mk;
       const int idx =
           part ? a.bm.kv_idx[lrow + min(c, a.bm.NKB - 1)] : a.bm.full_idx[lrow + c];
@@ -1010,10 +1041,26 @@ fwd_bf16_kernel(FwdArgs a) {
       return (paged && t < t_end) ? __builtin_amdgcn_readfirstlane(tpage[t]) : 0;
     };
     int pg_next = tile_page(t_next);
+    // The walk's last tile, when partial, may have a second step that no
+    // row of the workgroup attends (a sliding window's sink tile for rows
+    // past the window): a workgroup-wide vote before the walk.
+    bool half_last = false;
+    if constexpr (kHalfLast) {
+      const int tl = t_end - 1;
+      const int kv_half = tile_kv0(tl) + NK;
+      const bool may = step_may_attend<MASK>(
+          mask_limits<D, MASK>(kv_half + 4 * (R16 ? ln.g4 : ln.hh), a, ln), NK);
+      half_last = (tl >= nfull) && !__syncthreads_or(may);
+    }
     auto run_tile = [&](auto masked_tag) {
 #pragma unroll
       for (int sub = 0; sub < SPT; ++sub) {
         constexpr bool M = decltype(masked_tag)::value;
+        // the item's last tile when its second step is masked for every row
+        // of the workgroup (say a sliding window's sink tile): skip that
+        // step; nothing follows it, so the buffer parity does not matter
+        if constexpr (M && kHalfLast)
+          if (sub == 1 && half_last && t_next == t_end) break;
         const bool last_sub = sub == SPT - 1;
         const bool has_next = !last_sub || t_next < t_end;
         const int kv_nxt = last_sub ? kv_tile_next : kv0 + NK;

@@ -364,3 +364,23 @@ def test_fwd_head_dim_256_short_query_and_split(lib, splits):
     w = tiny("bf16", 256, "sliding_sink", "softcap_alibi", B=2, Hq=8, Hkv=2, Q_LEN=16,
              KV_LEN=1200, window=500, value_scale=2.0)
     check_splits(lib, w, splits)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 128), ("bf16", 64)])
+@pytest.mark.parametrize("case", ["sink_tile", "prefix_tile", "kv_tail"])
+@pytest.mark.parametrize("splits", [1, None])
+def test_fwd_last_tile_half_step(lib, dtype, D, case, splits):
+    """The walk's last tile (a row's lowest partial tile) with a second
+    64-key step that no row of the workgroup attends is cut to its first
+    step: a sliding window's sink tile for rows past the window, a PrefixLM
+    prefix tile for rows past the diagonal band, and a key tail of fewer
+    than 64 keys. Head dim 64 has one step per tile (nothing to cut)."""
+    if case == "sink_tile":
+        w = tiny(dtype, D, "sliding_sink", "none", B=2, Hq=4, Hkv=2, Q_LEN=1100, KV_LEN=1100,
+                 window=128, sinks=4)
+    elif case == "prefix_tile":
+        w = tiny(dtype, D, "prefix_lm", "none", B=1, Hq=4, Hkv=1, Q_LEN=900, KV_LEN=900,
+                 prefix=40)
+    else:
+        w = tiny(dtype, D, "noop", "softcap", B=2, Hq=4, Hkv=2, Q_LEN=200, KV_LEN=950)
+    check_splits(lib, w, splits)

@@ -184,7 +184,48 @@ def device_facts(torch):
     facts["library_gemm_bf16_tflops"] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
     facts["library_gemm_shape"] = f"{n}x{n}x{n} torch.matmul"
     del a, b
+    facts.update(mfma_probe(torch, facts.get("compute_units", 256)))
     return facts
+
+
+def mfma_probe(torch, cus: int):
+    """Sustained dense bf16 MFMA rate on this device: libfaprobe.so's kernel
+    (every wave issuing 32x32x16 MFMAs back to back, two workgroups of four
+    waves per CU) timed with HIP events on the current stream; the clock it
+    implies is that rate over 4096 flop/clk per CU."""
+    import ctypes
+    path = os.path.join(HERE, "block_sparse_masked_amd", "libfaprobe.so")
+    if not os.path.exists(path):
+        return {"mfma_probe_error": "libfaprobe.so not built"}
+    probe = ctypes.CDLL(path)
+    probe.faprobe_mfma_bf16.restype = ctypes.c_int
+    probe.faprobe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    blocks, iters = 2 * cus, 20000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        rc = probe.faprobe_mfma_bf16(iters, blocks, out.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"faprobe_mfma_bf16 failed: HIP error {rc}")
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
+    flops = blocks * 4 * 4 * iters * 32768.0
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"mfma_probe_bf16_tflops": round(tflops, 1),
+            "mfma_probe_implied_clock_mhz": round(tflops * 1e12 / (cus * 4096) / 1e6),
+            "mfma_probe": f"{blocks} workgroups x 4 waves x {4 * iters} v_mfma_f32_32x32x16_bf16"}
 
 
 def errors_vs_oracle(w: W.Workload, out, lse, o32, o_ref, lse_ref):
@@ -646,6 +687,11 @@ def main(argv=None):
     }
     tr = rec["roofline"]["traffic"]
     rec["roofline"]["hbm_gbs"] = round(tr / (fwd_avg * 1e-3) / 1e9, 1) if tr else None
+    probe = facts.get("mfma_probe_bf16_tflops")
+    if probe and w.dtype == "bf16":
+        # beside the published peak: the fraction of the rate the matrix
+        # cores sustain on this device at the clock a full matrix load runs at
+        rec["roofline"]["frac_of_measured_mfma"] = round(fwd_tflops / probe, 4)
     if configs:
         rec["configs"] = configs
     if ablation is not None:

@@ -18,6 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libflexattn.so")
+# matrix-core throughput probe, a library of its own that only bench.py loads
+PROBE_SRC = "probe_mfma.hip"
+PROBE_LIB = os.path.join(HERE, "libfaprobe.so")
 
 SOURCES = ["api.cpp", "block_mask.hip", "fwd_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip"]
 # fwd_bf16_inst.hip is compiled once per kernel slice (head dim, paged K/V,
@@ -77,7 +80,21 @@ def build(jobs: int = 8, debug: bool = False, extra=()) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
     os.replace(tmp, LIB)
+    build_probe(debug)
     return LIB
+
+
+def build_probe(debug: bool = False) -> str:
+    """libfaprobe.so: the benchmark's matrix-core throughput probe."""
+    os.makedirs(BUILD, exist_ok=True)
+    obj = compile_one(PROBE_SRC, debug, ())
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def main(argv=None):

@@ -206,32 +206,31 @@ __device__ __forceinline__ i32x4 make_rsrc(unsigned long long base, unsigned byt
   return r;
 }
 
-// Direct global->LDS loads (16 and 4 bytes per lane). Written as one asm
-// block with its M0 setup and no register results: the LDS they fill is a
-// buffer no instruction reads until after the explicit vmcnt(0) + barrier
-// that ends the step, so the compiler need not (and does not) wait for them.
-// No memory clobber: the asm stays ordered against the barriers and waits
-// (all have side effects), while the LDS reads of the other buffer may be
-// scheduled around it. Each load takes the CU's vector-memory path for a few
-// cycles, so the step spreads them between its matrix instructions.
-// The LDS address is wave-uniform by construction; readfirstlane states that
-// to the compiler so the asm operand is always a scalar register.
-// The compiler's hazard recognizer does not look inside inline asm, so the
-// block keeps the CDNA wait states itself: an LDS DMA that reads M0 needs
-// one wait state after the scalar write of M0 (without it the load can take
-// the previous M0, i.e. land on the previous load's LDS slot), and a vector
-// memory instruction needs five after a vector instruction wrote one of its
-// scalar operands (the resource words come from readfirstlane). s_nop n
-// gives n + 1 wait states: 3 + 1 (the M0 move) + 1 = 5 before the load.
-#define FA_LDS_DMA(op)                                                          \
-  "s_nop 2\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\t" op " %1, %2, 0 offen lds"
+// Direct global->LDS loads (16 and 4 bytes per lane). Written as asm with
+// no register results: the LDS they fill is a buffer no instruction reads
+// until after the explicit vmcnt(0) + barrier that ends the step, so the
+// compiler need not (and does not) wait for them. No memory clobber: the asm
+// stays ordered against the barriers and waits (all have side effects),
+// while the LDS reads of the other buffer may be scheduled around it. Each
+// load takes the CU's vector-memory path for a few cycles, so the step
+// spreads them between its matrix instructions.
+// The load's LDS address is M0, passed as an operand bound to M0 (the
+// compiler writes it and knows it is used); the address is wave-uniform by
+// construction and readfirstlane states that to the compiler. The
+// compiler's hazard recognizer does not look inside inline asm, so the
+// block keeps the CDNA wait states itself: an LDS DMA needs one wait state
+// after a scalar write of M0 (without it the load can take the previous M0,
+// i.e. land on the previous load's LDS slot), and a vector memory
+// instruction five after a vector instruction wrote one of its scalar
+// operands (the resource words come from readfirstlane): s_nop 4 gives five.
+#define FA_LDS_DMA(op) "s_nop 4\n\t" op " %0, %1, 0 offen lds"
 __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned lds, int voff) {
   asm volatile(FA_LDS_DMA("buffer_load_dwordx4")
-               : : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "m0");
+               : : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds)));
 }
 __device__ __forceinline__ void dma4(i32x4 rsrc, unsigned lds, int voff) {
   asm volatile(FA_LDS_DMA("buffer_load_dword")
-               : : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "m0");
+               : : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds)));
 }
 #undef FA_LDS_DMA
 
@@ -306,6 +305,9 @@ template <int D>
 struct Lane {
   int lane, l32, hh, vg, vi;
   int q, qc;
+  // the wave's query rows (32-row layout, wave-uniform): qc of its first
+  // and last lane
+  int qw_lo, qw_hi;
   float slope2;
   int dq;            // document id of this lane's query row (document mask)
   int kofs[D / 16];  // K fragment (row l32 of block 0, k-step ks)
@@ -457,8 +459,11 @@ template <int MASK>
 __device__ __forceinline__ bool step_may_attend(const MaskLimits& ml, int nk) {
   const int top = min(ml.hi, nk - 1);
   bool any = top >= 0;
-  if constexpr (MASK == MASK_SLIDING_SINK)
-    any = any & ((max(ml.win_lo + 1, 0) <= top) | (min(ml.sink_hi - 1, top) >= 0));
+  if constexpr (MASK == MASK_SLIDING_SINK) {
+    const bool in_window = max(ml.win_lo + 1, 0) <= top;
+    const bool in_sinks = min(ml.sink_hi - 1, top) >= 0;
+    any = any & (in_window | in_sinks);
+  }
   if constexpr (MASK == MASK_COMPOSITE) {
     bool t_any = false;
 #pragma unroll
@@ -466,6 +471,30 @@ __device__ __forceinline__ bool step_may_attend(const MaskLimits& ml, int nk) {
     any = any & t_any;
   }
   return any;
+}
+
+// Mask test of one 32-key block of a step, keys [k0, k0 + 31], for every
+// row of the wave at once (interval masks: causal, sliding window with
+// sinks, PrefixLM): 0 when every key is allowed for every row, 1 when none
+// is, 2 when the elements must be tested one by one. Decided from the wave's
+// row range, conservatively (a block that is neither all allowed nor all
+// masked for certain is tested per element); wave-uniform.
+template <int D, int MASK>
+__device__ __forceinline__ int block_mode(int k0, const FwdArgs& a, const Lane<D>& ln) {
+  const int k1 = k0 + 31;
+  bool all = k1 < a.KV_LEN;
+  bool none = k0 >= a.KV_LEN;
+  if constexpr (MASK == MASK_CAUSAL) {
+    all = all & (k1 <= ln.qw_lo);
+    none = none | (k0 > ln.qw_hi);
+  } else if constexpr (MASK == MASK_SLIDING_SINK) {
+    all = all & (k1 <= ln.qw_lo) & ((ln.qw_hi - k0 < a.mp.window) | (k1 < a.mp.sinks));
+    none = none | (k0 > ln.qw_hi) | ((ln.qw_lo - k1 >= a.mp.window) & (k0 >= a.mp.sinks));
+  } else if constexpr (MASK == MASK_PREFIX_LM) {
+    all = all & ((k1 < a.mp.prefix) | (k1 <= ln.qw_lo));
+    none = none | ((k0 >= a.mp.prefix) & (k0 > ln.qw_hi));
+  }
+  return __builtin_amdgcn_readfirstlane(all ? 0 : (none ? 1 : 2));
 }
 
 // Score-mod kinds (ALiBi, softcap, both) form each logit relative to the
@@ -505,6 +534,32 @@ __device__ __forceinline__ float rel_logit_base(float m_old, int key0_minus_q, c
   return z;
 }
 
+// Mask test of one score of a partial tile (32-row layout).
+template <int D, int MASK>
+__device__ __forceinline__ bool elem_allowed(int blk, int r, const MaskLimits& ml,
+                                             const int* step_doc, const FwdArgs& a,
+                                             const Lane<D>& ln) {
+  // conditions combined with & and |, not && and ||: every operand is
+  // safe to evaluate (the document ids of the step are in LDS), and
+  // short-circuit forms turned each element's test into a branch
+  const int c = key_off(blk, r);
+  bool ok = c <= ml.hi;
+  if constexpr (MASK == MASK_SLIDING_SINK) ok = ok & ((c > ml.win_lo) | (c < ml.sink_hi));
+  if constexpr (MASK == MASK_DOCUMENT) ok = ok & (step_doc[c + 4 * ln.hh] == ln.dq);
+  if constexpr (MASK == MASK_COMPOSITE) {
+    bool any = false;
+    const bool same_doc = step_doc[c + 4 * ln.hh] == ln.dq;  // ids in LDS (composite)
+#pragma unroll
+    for (int t = 0; t < kMaxTerms; ++t) {
+      bool in = (c >= ml.tlo[t]) & (c <= ml.thi[t]);
+      if (a.mp.terms[t] & PRIM_DOCUMENT) in = in & same_doc;
+      any = any | in;
+    }
+    ok = ok & any;
+  }
+  return ok;
+}
+
 // Logit of one score: y = score_mod(x) in base-2 units (raw x for
 // SCORE_NONE, scaled later; z = y - m_old for the score-mod kinds), -inf
 // where masked on partial tiles.
@@ -518,27 +573,7 @@ __device__ __forceinline__ float elem_logit(float x, int blk, int r, float zbase
   } else if constexpr (kRelLogit<SCORE>) {
     y = rel_logit<SCORE>(x, (float)key_off(blk, r), zbase, a, ln.slope2);
   }
-  if constexpr (MASKED) {
-    // conditions combined with & and |, not && and ||: every operand is
-    // safe to evaluate (the document ids of the step are in LDS), and
-    // short-circuit forms turned each element's test into a branch
-    const int c = key_off(blk, r);
-    bool ok = c <= ml.hi;
-    if constexpr (MASK == MASK_SLIDING_SINK) ok = ok & ((c > ml.win_lo) | (c < ml.sink_hi));
-    if constexpr (MASK == MASK_DOCUMENT) ok = ok & (step_doc[c + 4 * ln.hh] == ln.dq);
-    if constexpr (MASK == MASK_COMPOSITE) {
-      bool any = false;
-      const bool same_doc = step_doc[c + 4 * ln.hh] == ln.dq;  // ids in LDS (composite)
-#pragma unroll
-      for (int t = 0; t < kMaxTerms; ++t) {
-        bool in = (c >= ml.tlo[t]) & (c <= ml.thi[t]);
-        if (a.mp.terms[t] & PRIM_DOCUMENT) in = in & same_doc;
-        any = any | in;
-      }
-      ok = ok & any;
-    }
-    y = ok ? y : -INFINITY;
-  }
+  if constexpr (MASKED) y = elem_allowed<D, MASK>(blk, r, ml, step_doc, a, ln) ? y : -INFINITY;
   return y;
 }
 
@@ -581,14 +616,35 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
   const float m_old = (m_ref == -INFINITY) ? 0.0f : m_ref;
   const float zbase =
       kRel ? rel_logit_base<SCORE>(m_old, kv0 + 4 * ln.hh - ln.q, a, ln.slope2) : 0.0f;
+  // logits; on partial tiles a 32-key block is tested per element only
+  // when the wave's rows do not all agree on it (a wave-uniform branch)
   float mx = -INFINITY;
 #pragma unroll
-  for (int b = 0; b < G::NB; ++b)
+  for (int b = 0; b < G::NB; ++b) {
+    // (only for the interval masks without a score mod: the score-mod
+    // kinds' logits need more registers and the branches made the compiler
+    // spill; a document block would need its key ids read and compared,
+    // which cost more than the tests it saved)
+    constexpr bool kElide = MASKED && !kRel &&
+        (MASK == MASK_CAUSAL || MASK == MASK_SLIDING_SINK || MASK == MASK_PREFIX_LM);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[b][r] = elem_logit<D, MASK, SCORE, MASKED>(s[b][r], b, r, zbase, ml, step_doc, a, ln);
-      mx = fmaxf(mx, s[b][r]);
+    for (int r = 0; r < 16; ++r)
+      s[b][r] = elem_logit<D, MASK, SCORE, MASKED && !kElide>(s[b][r], b, r, zbase, ml, step_doc,
+                                                              a, ln);
+    if constexpr (kElide) {
+      const int mode = block_mode<D, MASK>(kv0 + 32 * b, a, ln);
+      if (mode == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[b][r] = -INFINITY;
+      } else if (mode == 2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[b][r] = elem_allowed<D, MASK>(b, r, ml, step_doc, a, ln) ? s[b][r] : -INFINITY;
+      }
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+  }
   mx = pair_max(mx);
   if constexpr (SCORE == SCORE_NONE) mx *= a.c_scale;  // c_scale > 0 here
 
@@ -888,6 +944,8 @@ fwd_bf16_kernel(FwdArgs a) {
   const int* doc_row =
       (mask_uses_doc(MASK) && a.mp.doc) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
   ln.dq = doc_row ? doc_row[ln.qc] : 0;
+  ln.qw_lo = __builtin_amdgcn_readfirstlane(ln.qc);
+  ln.qw_hi = __builtin_amdgcn_readlane(ln.qc, 31);
   if constexpr (R16) ln.init_offsets16();
   else ln.init_offsets();
   ln.slope2 = 0.0f;

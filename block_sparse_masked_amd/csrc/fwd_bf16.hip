@@ -164,8 +164,8 @@ hipError_t fwd_scratch(void** ptr, size_t* bytes) {
 }
 
 int fwd_bf16_lds_bytes(int D, int NKB, bool paged) {
-  (void)D;
-  return 4 * kStepBytes + 4 * ((NKB + 3) & ~3) * (paged ? 2 : 1) + 2 * 128 * 4;
+  const int step = D == 64 ? step_bytes<64>() : kStepBytes;
+  return 4 * step + 4 * ((NKB + 3) & ~3) * (paged ? 2 : 1) + 2 * 128 * 4;
 }
 
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream) {

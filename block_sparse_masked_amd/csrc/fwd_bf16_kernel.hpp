@@ -12,9 +12,9 @@
 // h / (Hq / Hkv) (page "FlagAttention", section "Operator overview").
 //
 // Work decomposition: one workgroup of 4 waves per (b, h, 128-row query
-// tile); wave w owns query rows [32w, 32w + 32). Two workgroups share a CU,
-// so each SIMD runs two waves and one wave's softmax (vector ALUs) overlaps
-// the other's matrix products. Both products use v_mfma_f32_32x32x16_bf16:
+// tile); wave w owns query rows [32w, 32w + 32). Two workgroups share a CU
+// (three at head dim 64), so each SIMD runs two (three) waves and one wave's
+// softmax (vector ALUs) overlaps another's matrix products. Both products use v_mfma_f32_32x32x16_bf16:
 //   S^T = K . Q^T    (A = K rows from LDS, B = Q^T held in registers)
 //   O^T += V^T . P^T (A = V^T read transposed from LDS, B = P^T in registers)
 // The MFMA result's lane index is the query column, so each lane holds the
@@ -34,8 +34,9 @@
 // lane l holds k = 8*(l/32) + t for both A and B, so the key order inside the
 // P.V contraction follows the S result layout directly.
 //
-// KV is walked in steps of NK = 8192 / D keys (64 for D = 128, 128 for D = 64;
-// a step's K or V block is 16 KiB), each BlockMask tile in 128 / NK steps.
+// KV is walked in steps of 64 keys at D = 64 and 128 (a step's K or V block
+// is 8 or 16 KiB) and 32 keys at D = 256, each BlockMask tile in 128 / NK
+// steps.
 // K and V of step g + 1 are loaded straight from global memory into LDS
 // (double-buffered) while step g computes; one barrier per step.
 // Full tiles take a path with no mask code. The running max is applied
@@ -112,7 +113,15 @@ typedef unsigned short u16;
 
 constexpr int kWavesPerHead = 4;  // 4 x 32 query rows = one 128-row query tile
 constexpr float kRescaleSlack = 8.0f;  // exp2 units: p <= 256 between rescales
-constexpr int kStepBytes = 16384;      // one K (or V) step block in LDS
+constexpr int kStepBytes = 16384;      // one K (or V) step block in LDS (D >= 128)
+// Step block bytes per head dim. D = 64 takes 8 KiB blocks (64-key steps):
+// the kernel then needs at most 166 VGPRs and 32 KiB of step buffers, so
+// three workgroups share a CU (three waves per SIMD), which keeps the matrix
+// cores busier while the vector units bound the head dim's softmax.
+template <int D>
+constexpr int step_bytes() { return D == 64 ? 8192 : kStepBytes; }
+template <int D>
+constexpr int wg_per_cu() { return D > 128 ? 1 : (D == 64 ? 3 : 2); }
 
 // internal score kind: plain scaled score with the scale applied before the
 // row max (needed when scale < 0; SCORE_NONE folds the scale into exp2)
@@ -120,7 +129,7 @@ constexpr int SCORE_SCALED = 4;
 
 template <int D>
 struct Geom {
-  static constexpr int NK = kStepBytes / (2 * D);  // keys per step
+  static constexpr int NK = step_bytes<D>() / (2 * D);  // keys per step
   static constexpr int SPT = kBlock / NK;          // steps per BlockMask tile
   static constexpr int NB = NK / 32;               // 32-key blocks per step
   static constexpr int NE = NB * 16;               // scores per lane per step
@@ -244,7 +253,7 @@ template <int D, bool IS_V, int WAVES>
 struct BlockLoader {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int ROWS_PER_KB = 1024 / (2 * D);
-  static constexpr int KB_PER_WAVE = kStepBytes / 1024 / WAVES;
+  static constexpr int KB_PER_WAVE = step_bytes<D>() / 1024 / WAVES;
   static constexpr int NK = Geom<D>::NK;
   int voff[KB_PER_WAVE];
   unsigned long long base;  // byte address of key row 0 of this (b, kv head)
@@ -375,41 +384,6 @@ template <int D, bool F16>
 __device__ __forceinline__ typename Elem<F16>::V8 k_frag(const u16* sK, const Lane<D>& ln, int ks,
                                                          int blk) {
   return as_v8<F16>(*reinterpret_cast<const uint4*>(sK + ln.kofs[ks] + 32 * blk * D));
-}
-
-// Fragment reads from per-step LDS byte bases. With one step per BlockMask
-// tile (D = 64) a step's buffer is known only at run time, and the compiler
-// rebuilt every fragment address from the buffer's base (one vector OR per
-// V k-step and d-block, one per K k-step: 20 a step). A base per K k-step and
-// per V d-block, formed once a step in a register the compiler treats as
-// opaque, lets every read carry its constant part in the offset field.
-__device__ __forceinline__ unsigned opaque_lds(const void* p, int elem_ofs) {
-  unsigned a = lds_addr(p) + 2u * (unsigned)elem_ofs;
-  asm("" : "+v"(a));
-  return a;
-}
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-template <int D, bool F16>
-__device__ __forceinline__ typename Elem<F16>::V8 k_frag_at(unsigned kbase, int blk) {
-  const u32x4 raw = *reinterpret_cast<lds_u32x4*>(kbase + 2u * (unsigned)(32 * blk * D));
-  typename Elem<F16>::V8 r;
-  __builtin_memcpy(&r, &raw, 16);
-  return r;
-}
-
-template <int D, bool F16>
-__device__ __forceinline__ typename Elem<F16>::V8 v_frag_at(unsigned vbase, int ks) {
-  typename Elem<F16>::V4 part[2];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        reinterpret_cast<lds_s16x4*>(vbase + 2u * (unsigned)((16 * ks + 8 * ht) * D)));
-    __builtin_memcpy(&part[ht], &raw, 8);
-  }
-  return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Key offset (within the step, without 4*hh) of result register r of block blk.
@@ -586,14 +560,6 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
                                      int kv0, const int* step_doc, const FwdArgs& a,
                                      const Lane<D>& ln, DMA&& dma) {
   using G = Geom<D>;
-  constexpr bool kOpaque = G::SPT == 1;  // run-time buffer: fixed per-step bases
-  unsigned kb[G::KS], vb[G::DB];
-  if constexpr (kOpaque) {
-#pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) kb[ks] = opaque_lds(sK, ln.kofs[ks]);
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db) vb[db] = opaque_lds(sV, ln.vofs[db]);
-  }
   f32x16 s[G::NB];
 #pragma unroll
   for (int b = 0; b < G::NB; ++b) s[b] = f32x16{};
@@ -602,7 +568,7 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
 #pragma unroll
     for (int b = 0; b < G::NB; ++b)
     {
-      const auto kf = kOpaque ? k_frag_at<D, F16>(kb[ks], b) : k_frag<D, F16>(sK, ln, ks, b);
+      const auto kf = k_frag<D, F16>(sK, ln, ks, b);
       s[b] = Elem<F16>::mfma(kf, qf[ks], s[b]);
       // the next step's loads, spread over the S products
       constexpr int NS = G::KS * G::NB;
@@ -697,7 +663,7 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
   for (int ks = 0; ks < G::PKS; ++ks)
 #pragma unroll
     for (int db = 0; db < G::DB; ++db) {
-      const auto vf = kOpaque ? v_frag_at<D, F16>(vb[db], ks) : v_frag<D, F16>(sV, ln, ks, db);
+      const auto vf = v_frag<D, F16>(sV, ln, ks, db);
       o[db] = Elem<F16>::mfma(vf, pf[ks], o[db]);
     }
 }
@@ -864,13 +830,14 @@ __device__ __forceinline__ void step16(f32x4 (&o)[D / 16], float& m_ref, float& 
       o[db] = mfma16<F16>(v_frag16<D, F16>(sV, ln, j, db), pf[j], o[db]);
 }
 
-// Four waves per workgroup, two workgroups per CU (two waves per SIMD).
+// Four waves per workgroup, two workgroups per CU (two waves per SIMD);
+// three at D = 64.
 // D = 256 holds 128 accumulator and 64 Q registers per lane: one workgroup
 // per CU, with the accumulators in the matrix-core registers.
 // R16: the 16-row step for query tiles of at most 16 rows (one query head
 // per wave, 4 heads of a KV group per workgroup).
 template <int D, int MASK, int SCORE, bool PAGED, bool F16, bool R16>
-__global__ __launch_bounds__(64 * kWavesPerHead, (D > 128) ? 1 : 2) void
+__global__ __launch_bounds__(64 * kWavesPerHead, wg_per_cu<D>()) void
 fwd_bf16_kernel(FwdArgs a) {
   using E = Elem<F16>;
   using G = Geom<D>;
@@ -878,7 +845,7 @@ fwd_bf16_kernel(FwdArgs a) {
   constexpr int THREADS = 64 * WAVES;
   constexpr int NK = G::NK;
   constexpr int SPT = G::SPT;
-  constexpr int STEP_ELEMS = kStepBytes / 2;
+  constexpr int STEP_ELEMS = step_bytes<D>() / 2;
   // LDS: K and V step blocks double-buffered (separate arrays, so the
   // compiler can tell the buffer being filled from the one being read and does
   // not wait for in-flight loads before LDS reads), two document-id buffers,

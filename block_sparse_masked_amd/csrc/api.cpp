@@ -552,11 +552,11 @@ flexattn_status flexattn_fwd_make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32
     return fail(FLEXATTN_ERR_INVALID_ARG, "%s: BlockMask does not match the shapes", who);
   const int target = target_workgroups > 0 ? target_workgroups : 512;
   if (dtype == FLEXATTN_F32) {
-    plan->waves_per_head = 0;  // not the 16-bit kernel's layout: 32-row workgroups
+    plan->waves_per_head = 0;  // not the 16-bit kernel's layout: 8-row workgroups
     plan->heads_per_workgroup = 1;
     plan->row16 = 0;
     plan->num_splits = 1;
-    plan->work_items = (int64_t)B * Hq * bm->num_q_blocks * (QBS / 32);
+    plan->work_items = (int64_t)B * Hq * bm->num_q_blocks * (QBS / fa::kF32RowsPerWorkgroup);
     return ok();
   }
   const fa::FwdPlan p = fa::plan_fwd(B, Hq, Hkv, Q_LEN, D, bm->B, bm->H, bm->num_q_blocks, QBS,

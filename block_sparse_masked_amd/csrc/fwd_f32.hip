@@ -26,7 +26,7 @@ namespace {
 
 constexpr int kTpr = 4;         // threads per (row, key group): head-dim quarters
 constexpr int kGroups = 8;      // key groups per row
-constexpr int kRowsPerWg = 8;   // query rows per workgroup
+constexpr int kRowsPerWg = kF32RowsPerWorkgroup;  // query rows per workgroup
 constexpr int kThreads = kTpr * kGroups * kRowsPerWg;
 
 // keys staged in LDS at a time, and the LDS row stride (floats): 4 floats of

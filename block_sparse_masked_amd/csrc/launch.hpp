@@ -70,6 +70,8 @@ constexpr size_t kFwdScratchBytes = size_t(32) << 20;
 hipError_t fwd_scratch(void** ptr, size_t* bytes);
 int fwd_bf16_lds_bytes(int D, int NKB, bool paged);  // LDS of the bf16 forward
 constexpr int kMaxLdsBytes = 160 * 1024;
+// query rows per workgroup of the fp32 forward (fwd_f32.hip)
+constexpr int kF32RowsPerWorkgroup = 8;
 constexpr long long kMaxBf16RowStride = 1ll << 22;  // k/v row stride limit of the bf16 forward
 hipError_t launch_fwd_f32(const FwdLaunch& L, hipStream_t stream);
 

@@ -311,7 +311,7 @@ flexattn_status flexattn_fwd(const flexattn_tensor* q, const flexattn_tensor* k,
  * are read; its device buffers are not). target_workgroups <= 0 means 512
  * (two workgroups on each of 256 CUs). fp32 calls get waves_per_head 0,
  * heads_per_workgroup 1, row16 0, num_splits 1 (the fp32 path does not
- * split) and the fp32 kernel's workgroup count (one per 32 query rows).
+ * split) and the fp32 kernel's workgroup count (one per 8 query rows).
  * Errors: INVALID_ARG for NULL pointers, non-positive shapes or a BlockMask
  * that does not match them; UNSUPPORTED for other dtypes or block sizes.
  */

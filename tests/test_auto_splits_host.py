@@ -73,3 +73,12 @@ def test_plan_rejects_mismatched_mask():
     k = torch.empty(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fwd_plan(q, k, _bm(32, 4096))
+
+
+def test_plan_fp32_workgroups():
+    """The fp32 forward runs one workgroup per 8 query rows of each (b, h)
+    and does not split."""
+    q = torch.empty(2, 3, 300, 64)
+    k = torch.empty(2, 3, 1, 64)
+    p = fa.fwd_plan(q, k, _bm(300, 4096))
+    assert (p["waves_per_head"], p["num_splits"], p["work_items"]) == (0, 1, 2 * 3 * 3 * 128 // 8)

@@ -436,7 +436,7 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask
                    page_table: Optional[torch.Tensor] = None):
     """Block-sparse attention forward. q [B,Hq,M,D]; k, v [B,Hkv,N,D].
 
-    With page_table (int32 [B, max_pages], bf16): k and v are paged caches
+    With page_table (int32 [B, max_pages]; bf16 or fp16): k and v are paged caches
     [num_pages, Hkv, page_size, D] (page_size a multiple of 128) and key j of
     batch b is row j % page_size of page page_table[b, j // page_size]; the
     sequence length is block_mask.KV_LEN.

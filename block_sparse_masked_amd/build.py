@@ -25,7 +25,7 @@ PROBE_LIB = os.path.join(HERE, "libfaprobe.so")
 SOURCES = ["api.cpp", "block_mask.hip", "fwd_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip"]
 # fwd_bf16_inst.hip is compiled once per kernel slice (head dim, paged K/V,
 # fp16 elements), so the slices build in parallel
-SLICES = [(d, paged, f16) for d in (64, 128, 256) for paged, f16 in ((0, 0), (1, 0), (0, 1))]
+SLICES = [(d, paged, f16) for d in (64, 128, 256) for paged, f16 in ((0, 0), (1, 0), (0, 1), (1, 1))]
 ARCH = "gfx950"
 
 

@@ -357,8 +357,9 @@ flexattn_status fwd_impl(const flexattn_tensor* q, const flexattn_tensor* k,
   if (pages) {
     if (!pages->page_table || reinterpret_cast<uintptr_t>(pages->page_table) % 4 != 0)
       return fail(FLEXATTN_ERR_INVALID_ARG, "%s: page_table is NULL or not 4-byte aligned", who);
-    if (q->dtype != FLEXATTN_BF16)
-      return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: the paged forward is a bf16 path", who);
+    if (q->dtype != FLEXATTN_BF16 && q->dtype != FLEXATTN_F16)
+      return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: the paged forward is a 16-bit path (bf16 or "
+                  "fp16)", who);
     if (k->B != v->B || k->B < 1)
       return fail(FLEXATTN_ERR_INVALID_ARG, "%s: k and v caches must hold the same pages", who);
     if (k->L % fa::kBlock != 0)

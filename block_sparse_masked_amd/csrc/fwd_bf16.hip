@@ -169,7 +169,8 @@ int fwd_bf16_lds_bytes(int D, int NKB, bool paged) {
 }
 
 hipError_t launch_fwd_bf16(const FwdLaunch& L, hipStream_t stream) {
-  if (L.f16) return launch_impl<false, true>(L, stream);
+  if (L.f16) return L.page_table ? launch_impl<true, true>(L, stream)
+                                  : launch_impl<false, true>(L, stream);
   if (L.page_table) return launch_impl<true, false>(L, stream);
   return launch_impl<false, false>(L, stream);
 }

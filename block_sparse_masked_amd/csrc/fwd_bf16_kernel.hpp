@@ -1326,6 +1326,7 @@ hipError_t fwd16_launch(const FwdArgs& a, bool r16, int mask, int score, int gri
   prefix FA_FWD16_SLICE(256, false, false); prefix FA_FWD16_SLICE(64, true, false);         \
   prefix FA_FWD16_SLICE(128, true, false); prefix FA_FWD16_SLICE(256, true, false);         \
   prefix FA_FWD16_SLICE(64, false, true); prefix FA_FWD16_SLICE(128, false, true);          \
-  prefix FA_FWD16_SLICE(256, false, true)
+  prefix FA_FWD16_SLICE(256, false, true); prefix FA_FWD16_SLICE(64, true, true);           \
+  prefix FA_FWD16_SLICE(128, true, true); prefix FA_FWD16_SLICE(256, true, true)
 
 }  // namespace fa

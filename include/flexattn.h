@@ -398,8 +398,8 @@ typedef struct {
  * workspace rules apply) with keys read through the page table. k_cache and
  * v_cache are flexattn_tensors with B = num_pages, H = Hkv, L = page_size
  * (a multiple of 128, so a BlockMask tile never straddles pages), any
- * 16-byte-multiple strides. The sequence length is bm->KV_LEN. bf16 only
- * (UNSUPPORTED otherwise); page sizes that are not multiples of 128 are
+ * 16-byte-multiple strides. The sequence length is bm->KV_LEN. bf16 or
+ * fp16 (UNSUPPORTED otherwise); page sizes that are not multiples of 128 are
  * UNSUPPORTED. Asynchronous on `stream`.
  */
 flexattn_status flexattn_fwd_paged(const flexattn_tensor* q, const flexattn_tensor* k_cache,

@@ -111,3 +111,33 @@ def test_paged_decode_workload_sampled(lib):
         o_ref, lse_ref = G.oracle_rows(w, inp, batches=[b], heads=[h])
         res = G.compare(w, o, l_, o_ref, lse_ref)
         assert res["ok"] and res["n_rows"] == w.Q_LEN, G.summary(res)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("mask,score", [("causal", "alibi"), ("sliding_sink", "softcap")])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_paged_fp16_against_oracle(lib, D, mask, score, splits):
+    """fp16 inputs through the paged cache: against the oracle on the
+    gathered keys, and bit-identical to the contiguous fp16 forward."""
+    w = tiny("f16", D, mask, score, B=2, Hq=4, Hkv=2, Q_LEN=300, KV_LEN=900, window=150,
+             value_scale=2.0 if "softcap" in score else 1.0)
+    inp = W.generate(w)
+    kc_h, vc_h, table_h = W.paged_cache(inp.k, inp.v, 256, seed=5)
+    q = G.to_device(inp.q, "f16")
+    kc, vc = G.to_device(kc_h, "f16"), G.to_device(vc_h, "f16")
+    table = torch.from_numpy(table_h).cuda()
+    bm = G.build_gpu_mask(lib, w, inp)
+    out, lse = lib.flex_attention(q, kc, vc, bm, score=w.score, softcap=w.softcap, scale=w.scale,
+                                  num_splits=splits, page_table=table)
+    k, v = G.to_device(inp.k, "f16"), G.to_device(inp.v, "f16")
+    o2, l2 = lib.flex_attention(q, k, v, bm, score=w.score, softcap=w.softcap, scale=w.scale,
+                                num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+    mask_mod, score_mod = oracle.for_workload(w, inp)
+    o_ref, lse_ref = oracle.attention(inp.q, oracle.gather_paged(kc_h, table_h, w.KV_LEN),
+                                      oracle.gather_paged(vc_h, table_h, w.KV_LEN), mask_mod,
+                                      score_mod, w.scale)
+    res = G.compare(w, out.float().cpu().numpy().astype(np.float64),
+                    lse.cpu().numpy().astype(np.float64), o_ref, lse_ref)
+    assert res["ok"], G.summary(res)

@@ -305,10 +305,10 @@ def _fwd_paged(L, pages=True, table=4096, max_pages=2, page=128, dtype=1, splits
     (dict(table=4098), lib._INVALID, b"aligned"),
     (dict(max_pages=1), lib._INVALID, b"do not cover"),
     (dict(page=64), lib._UNSUPPORTED, b"multiple of 128"),
-    (dict(dtype=0), lib._UNSUPPORTED, b"bf16"),
-    (dict(dtype=2), lib._UNSUPPORTED, b"bf16"),
+    (dict(dtype=0), lib._UNSUPPORTED, b"16-bit"),
     (dict(splits=0), lib._INVALID, b"num_splits"),
     (dict(splits=2), lib._INVALID, b"workspace"),
+    (dict(dtype=2, splits=0), lib._INVALID, b"num_splits"),
 ])
 def test_fwd_paged_rejects_bad_arguments(L, case, expect, msg):
     # the BlockMask is for KV_LEN 256: two pages of 128 keys cover it

@@ -583,7 +583,8 @@ def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """Gradients (dq, dk, dv) of flex_attention's output for the upstream
     gradient d_out. With out_f32 (the fp32 O of flex_attention_train) the
     row sums Delta = dO . O come from one pass over it instead of a
-    recompute. bf16 tensors; lse is the forward's and the BlockMask must
+    recompute. bf16 or fp16 tensors (one dtype for all; the gradients come
+    back in it); lse is the forward's and the BlockMask must
     carry the backward lists (create_block_mask(..., backward_lists=True)).
     dk / dv sum the query heads of each KV head."""
     lib = load_library()

@@ -22,7 +22,9 @@ LIB = os.path.join(HERE, "libflexattn.so")
 PROBE_SRC = "probe_mfma.hip"
 PROBE_LIB = os.path.join(HERE, "libfaprobe.so")
 
-SOURCES = ["api.cpp", "block_mask.hip", "fwd_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip"]
+SOURCES = ["api.cpp", "block_mask.hip", "fwd_bf16.hip", "fwd_f32.hip"]
+# bwd_bf16.hip is compiled once per 16-bit element type (0: bf16, 1: fp16)
+BWD_ELEMS = (0, 1)
 # fwd_bf16_inst.hip is compiled once per kernel slice (head dim, paged K/V,
 # fp16 elements), so the slices build in parallel
 SLICES = [(d, paged, f16) for d in (64, 128, 256) for paged, f16 in ((0, 0), (1, 0), (0, 1), (1, 1))]
@@ -66,8 +68,10 @@ def _jobs():
     for d, paged, f16 in SLICES:
         jobs.append(("fwd_bf16_inst.hip", (f"FA_D={d}", f"FA_PAGED={paged}", f"FA_F16={f16}"),
                      f"fwd_bf16_inst_d{d}_p{paged}_h{f16}.o"))
+    for f16 in BWD_ELEMS:
+        jobs.append(("bwd_bf16.hip", (f"FA_BWD_F16={f16}",), f"bwd_bf16_h{f16}.o"))
     # the longest compiles first
-    return sorted(jobs, key=lambda j: j[0] != "fwd_bf16_inst.hip")
+    return sorted(jobs, key=lambda j: j[0] not in ("fwd_bf16_inst.hip", "bwd_bf16.hip"))
 
 
 def build(jobs: int = 8, debug: bool = False, extra=()) -> str:

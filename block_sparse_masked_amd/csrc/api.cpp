@@ -670,10 +670,12 @@ static flexattn_status bwd_impl(const flexattn_tensor* q, const flexattn_tensor*
   const char* names[7] = {"q", "k", "v", "d_out", "dq", "dk", "dv"};
   for (int i = 0; i < 7; ++i)
     if ((st = check_tensor(all[i], names[i], who)) != FLEXATTN_OK) return st;
-  for (int i = 0; i < 7; ++i)
-    if (all[i]->dtype != FLEXATTN_BF16)
-      return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: %s must be BF16 (the backward is bf16 only)",
-                  who, names[i]);
+  if (q->dtype != FLEXATTN_BF16 && q->dtype != FLEXATTN_F16)
+    return fail(FLEXATTN_ERR_UNSUPPORTED,
+                "%s: q must be BF16 or F16 (the backward is a 16-bit path)", who);
+  for (int i = 1; i < 7; ++i)
+    if (all[i]->dtype != q->dtype)
+      return fail(FLEXATTN_ERR_INVALID_ARG, "%s: %s dtype differs from q", who, names[i]);
   if (!lse) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: lse is NULL", who);
   if (!workspace) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: workspace is NULL", who);
   if (!bm) return fail(FLEXATTN_ERR_INVALID_ARG, "%s: bm is NULL", who);
@@ -789,7 +791,9 @@ static flexattn_status bwd_impl(const flexattn_tensor* q, const flexattn_tensor*
   L.q_idx = bm->q_indices;
   L.full_q_num = bm->full_q_num_blocks;
   L.full_q_idx = bm->full_q_indices;
-  hipError_t e = fa::launch_bwd_bf16(L, static_cast<hipStream_t>(stream));
+  hipError_t e = q->dtype == FLEXATTN_F16
+                     ? fa::launch_bwd_f16(L, static_cast<hipStream_t>(stream))
+                     : fa::launch_bwd_bf16(L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(FLEXATTN_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();

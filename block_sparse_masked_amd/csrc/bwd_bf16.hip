@@ -1,4 +1,6 @@
-// Block-sparse attention backward, bf16 inputs, fp32 accumulation, gfx950.
+// Block-sparse attention backward, bf16 or fp16 inputs, fp32 accumulation,
+// gfx950. The build compiles this file once per element type (FA_BWD_F16 = 0
+// for bf16, 1 for fp16), each object defining its launcher.
 //
 // Gradients of the forward in fwd_bf16.hip for an upstream dO, visiting only
 // the tiles a BlockMask lists and applying mask_mod on partial tiles only
@@ -15,8 +17,8 @@
 //   dq_kernel<DELTA>  one workgroup per (b, h, query tile), in the forward's
 //                 schedule order, walking the KV tiles of the forward lists:
 //                 Delta_i = sum_j P_ij dP_ij from fp32 P and dP. Delta equals
-//                 dO_i . O_i, but O is stored in bf16 and the difference
-//                 dP - Delta cancels: taken from the bf16 O, Delta's rounding
+//                 dO_i . O_i, but O is stored in 16 bits and the difference
+//                 dP - Delta cancels: taken from that O, Delta's rounding
 //                 reaches tens of percent of some rows' dQ, taken this way
 //                 it stays at the fp32 level;
 //   dq_kernel     the same walk again for dQ;
@@ -25,15 +27,15 @@
 //                 GQA group, so dK / dV are summed in registers with a fixed
 //                 order (deterministic, no atomics).
 //
-// MFMA layout (v_mfma_f32_32x32x16_bf16): an operand fragment is 8 bf16 per
-// lane, lane l holding row/column l%32 and k = 8*(l/32) .. +7; a result is 16
+// MFMA layout (v_mfma_f32_32x32x16_bf16, or _f16): an operand fragment is 8
+// elements per lane, lane l holding row/column l%32 and k = 8*(l/32) .. +7; a result is 16
 // fp32 per lane, register r holding row 8*(r/4) + 4*(l/32) + r%4 and column
 // l%32. The 32x32 score tiles are produced with the key (dQ) or the query
 // (dK/dV) on the lane axis, so P and dS pack straight into the B operand of
 // the next product, whose A operand is read transposed from LDS
 // (ds_read_b64_tr_b16) in the matching row order.
 //
-// Tiles are staged in LDS as row-major blocks with 8 bf16 of padding per row
+// Tiles are staged in LDS as row-major blocks with 8 elements of padding per row
 // (272-byte rows at D = 128), which spreads both the 16-byte row reads and
 // the transposed 8-byte reads over the banks without a swizzle.
 #include <cmath>
@@ -42,6 +44,10 @@
 #include "fwd_common.hpp"
 #include "launch.hpp"
 
+#if !defined(FA_BWD_F16)
+#error "compile bwd_bf16.hip with -DFA_BWD_F16=<0|1>"
+#endif
+
 namespace fa {
 namespace {
 
@@ -49,9 +55,34 @@ typedef unsigned short u16;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// The 16-bit element (bf16 for F16 = false, else fp16): both take the same
+// fragment layouts and a 32x32x16 MFMA with fp32 accumulation; P and dS are
+// rounded to it for the second products, dQ / dK / dV are stored in it.
+template <bool F16>
+struct BElem {
+  using T = __bf16;
+  using V8 = bf16x8;
+  using V4 = bf16x4;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct BElem<true> {
+  using T = _Float16;
+  using V8 = f16x8;
+  using V4 = f16x4;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
 
 constexpr int kThreads = 256;  // four waves
-constexpr int kPad = 8;        // bf16 elements of padding per LDS row
+constexpr int kPad = 8;        // elements of padding per LDS row
 
 struct BwdArgs {
   const u16* q;
@@ -76,9 +107,10 @@ struct BwdArgs {
   const int* fq_idx;
 };
 
-__device__ __forceinline__ bf16x8 ld_frag(const u16* p) {
+template <bool F16>
+__device__ __forceinline__ typename BElem<F16>::V8 ld_frag(const u16* p) {
   const uint4 u = *reinterpret_cast<const uint4*>(p);
-  bf16x8 r;
+  typename BElem<F16>::V8 r;
   __builtin_memcpy(&r, &u, 16);
   return r;
 }
@@ -88,20 +120,23 @@ __device__ __forceinline__ bf16x8 ld_frag(const u16* p) {
 // Each 16-lane group of a ds_read_b64_tr_b16 supplies the 8-byte pieces (row
 // j/4, columns 4*(j%4) .. +3) of a 4-row x 16-column block and lane j gets
 // column j of it.
-template <int LDR>
-__device__ __forceinline__ bf16x8 tr_frag(const u16* blk, int lane, int ks, int db) {
+template <int LDR, bool F16>
+__device__ __forceinline__ typename BElem<F16>::V8 tr_frag(const u16* blk, int lane, int ks,
+                                                          int db) {
   const int hh = lane >> 5, vg = (lane >> 4) & 1, vi = lane & 15;
   const int row = 16 * ks + 4 * hh + (vi >> 2);
   const int col = 32 * db + 16 * vg + 4 * (vi & 3);
-  bf16x4 part[2];
+  typename BElem<F16>::V4 part[2];
 #pragma unroll
-  for (int ht = 0; ht < 2; ++ht)
-    part[ht] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) bf16x4*)(blk + (row + 8 * ht) * LDR + col));
+  for (int ht = 0; ht < 2; ++ht) {
+    const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(blk + (row + 8 * ht) * LDR + col));
+    __builtin_memcpy(&part[ht], &raw, 8);
+  }
   return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Rows [r0, r0 + 128) of a [len][D] bf16 matrix (row stride `ld` elements)
+// Rows [r0, r0 + 128) of a [len][D] 16-bit matrix (row stride `ld` elements)
 // into a padded LDS block; rows at or past `len` are zero. Branch-free (the
 // row is clamped and the value zeroed) so each thread's loads are issued
 // back to back, NB at a time, before any of them is waited for.
@@ -191,8 +226,10 @@ __device__ __forceinline__ float lse_base2(float lse) {
 // dQ^T += K^T . dS^T with K read transposed from LDS. With DELTA the walk
 // only sums P dP per query row and writes Delta.
 // ---------------------------------------------------------------------------
-template <int D, int MASK, int SCORE, bool DELTA>
+template <int D, int MASK, int SCORE, bool DELTA, bool F16>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
+  using E = BElem<F16>;
+  using T = typename E::T;
   constexpr int LDR = D + kPad;
   constexpr int KS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) u16 sK[kBlock * LDR];
@@ -212,14 +249,14 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   const bool qvalid = q < a.Q_LEN;
   const int qc = qvalid ? q : a.Q_LEN - 1;
 
-  bf16x8 qf[KS], dof[KS];
+  typename E::V8 qf[KS], dof[KS];
   {
     const u16* qrow = a.q + b * a.sq[0] + h * a.sq[1] + (long long)qc * a.sq[2];
     const u16* grow = a.dout + b * a.sdo[0] + h * a.sdo[1] + (long long)qc * a.sdo[2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qf[ks] = ld_frag(qrow + 16 * ks + 8 * hh);
-      dof[ks] = ld_frag(grow + 16 * ks + 8 * hh);
+      qf[ks] = ld_frag<F16>(qrow + 16 * ks + 8 * hh);
+      dof[ks] = ld_frag<F16>(grow + 16 * ks + 8 * hh);
     }
   }
   const long long rowid = ((long long)b * a.Hq + h) * a.Q_LEN + qc;
@@ -253,11 +290,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
       const u16* vrow = sV + (32 * blk + l32) * LDR + 8 * hh;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(krow + 16 * ks), qf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(vrow + 16 * ks), dof[ks], dp, 0, 0,
-                                                     0);
+        s = E::mfma(ld_frag<F16>(krow + 16 * ks), qf[ks], s);
+        dp = E::mfma(ld_frag<F16>(vrow + 16 * ks), dof[ks], dp);
       }
-      bf16x8 dsf[2];
+      typename E::V8 dsf[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kl = 32 * blk + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -267,15 +303,14 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
                                              x, dm);
         const float p = fast_exp2(x - lse2);
         if constexpr (DELTA) psum = fmaf(p, dp[r], psum);
-        else dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dlt) * dm);
+        else dsf[r >> 3][r & 7] = (T)(p * (dp[r] - dlt) * dm);
       }
       if constexpr (!DELTA) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                tr_frag<LDR>(sK, lane, 2 * blk + k2, db), dsf[k2], acc[db], 0, 0, 0);
+            acc[db] = E::mfma(tr_frag<LDR, F16>(sK, lane, 2 * blk + k2, db), dsf[k2], acc[db]);
       }
     }
   };
@@ -311,10 +346,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        bf16x4 pk;
+        typename E::V4 pk;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pk[j] = (__bf16)(acc[db][4 * gq + j] * a.scale);
-        *reinterpret_cast<bf16x4*>(out + 32 * db + 8 * gq + 4 * hh) = pk;
+        for (int j = 0; j < 4; ++j) pk[j] = (T)(acc[db][4 * gq + j] * a.scale);
+        *reinterpret_cast<typename E::V4*>(out + 32 * db + 8 * gq + 4 * hh) = pk;
       }
   }
 }
@@ -326,8 +361,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
 // rows on the register axis, key on the lane axis), then dV^T += dO^T . P^T
 // and dK^T += Q^T . dS^T with dO and Q read transposed from LDS.
 // ---------------------------------------------------------------------------
-template <int D, int MASK, int SCORE>
+template <int D, int MASK, int SCORE, bool F16>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
+  using E = BElem<F16>;
+  using T = typename E::T;
   constexpr int LDR = D + kPad;
   constexpr int KS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) u16 sQ[kBlock * LDR];
@@ -354,14 +391,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   const bool kvalid = kv < a.KV_LEN;
   const int kvc = kvalid ? kv : a.KV_LEN - 1;
 
-  bf16x8 kf[KS], vf[KS];
+  typename E::V8 kf[KS], vf[KS];
   {
     const u16* krow = a.k + b * a.sk[0] + hk * a.sk[1] + (long long)kvc * a.sk[2];
     const u16* vrow = a.v + b * a.sv[0] + hk * a.sv[1] + (long long)kvc * a.sv[2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = ld_frag(krow + 16 * ks + 8 * hh);
-      vf[ks] = ld_frag(vrow + 16 * ks + 8 * hh);
+      kf[ks] = ld_frag<F16>(krow + 16 * ks + 8 * hh);
+      vf[ks] = ld_frag<F16>(vrow + 16 * ks + 8 * hh);
     }
   }
   const int* doc_row =
@@ -465,11 +502,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
       const u16* grow = sG + (32 * qs + l32) * LDR + 8 * hh;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(qrow + 16 * ks), kf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(grow + 16 * ks), vf[ks], dp, 0, 0,
-                                                     0);
+        s = E::mfma(ld_frag<F16>(qrow + 16 * ks), kf[ks], s);
+        dp = E::mfma(ld_frag<F16>(grow + 16 * ks), vf[ks], dp);
       }
-      bf16x8 pf[2], dsf[2];
+      typename E::V8 pf[2], dsf[2];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int ql0 = 32 * qs + 8 * g4 + 4 * hh;
@@ -485,18 +521,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
                                                mask_uses_doc(MASK) ? sdoc[ql] : 0, dkv_id,
                                                slope2, a, x, dm);
           const float p = fast_exp2(x - lv[j]);
-          pf[r >> 3][r & 7] = (__bf16)p;
-          dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl[j]) * dm);
+          pf[r >> 3][r & 7] = (T)p;
+          dsf[r >> 3][r & 7] = (T)(p * (dp[r] - dl[j]) * dm);
         }
       }
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_frag<LDR>(sG, lane, 2 * qs + k2, db), pf[k2], accv[db], 0, 0, 0);
-          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_frag<LDR>(sQ, lane, 2 * qs + k2, db), dsf[k2], acck[db], 0, 0, 0);
+          accv[db] = E::mfma(tr_frag<LDR, F16>(sG, lane, 2 * qs + k2, db), pf[k2], accv[db]);
+          acck[db] = E::mfma(tr_frag<LDR, F16>(sQ, lane, 2 * qs + k2, db), dsf[k2], acck[db]);
         }
     }
   };
@@ -527,21 +561,21 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        bf16x4 pk, pv;
+        typename E::V4 pk, pv;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          pk[j] = (__bf16)(acck[db][4 * gq + j] * a.scale);
-          pv[j] = (__bf16)accv[db][4 * gq + j];
+          pk[j] = (T)(acck[db][4 * gq + j] * a.scale);
+          pv[j] = (T)accv[db][4 * gq + j];
         }
-        *reinterpret_cast<bf16x4*>(ok + 32 * db + 8 * gq + 4 * hh) = pk;
-        *reinterpret_cast<bf16x4*>(ov + 32 * db + 8 * gq + 4 * hh) = pv;
+        *reinterpret_cast<typename E::V4*>(ok + 32 * db + 8 * gq + 4 * hh) = pk;
+        *reinterpret_cast<typename E::V4*>(ov + 32 * db + 8 * gq + 4 * hh) = pv;
       }
   }
 }
 
 // Delta = dO . O per query row from the forward's fp32 O (one wave per row):
 // sum_j P_ij dP_ij = dO_i . sum_j P_ij v_j = dO_i . O_i.
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void delta_from_out_kernel(BwdArgs a) {
   constexpr int PER = D / 64;
   const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
@@ -556,7 +590,7 @@ __global__ __launch_bounds__(256) void delta_from_out_kernel(BwdArgs a) {
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    __bf16 gv;
+    typename BElem<F16>::T gv;
     __builtin_memcpy(&gv, g + i, 2);
     acc = fmaf((float)gv, o[i], acc);
   }
@@ -565,50 +599,49 @@ __global__ __launch_bounds__(256) void delta_from_out_kernel(BwdArgs a) {
   if (lane == 0) a.delta[row] = acc;
 }
 
-template <int D, int MASK, int SCORE>
+template <int D, int MASK, int SCORE, bool F16>
 hipError_t launch_kernels(const BwdArgs& a, hipStream_t stream) {
   const long long nq = (long long)a.B * a.Hq * a.bm.NQB * (a.bm.QBS / kBlock);
   if (a.o32) {
     const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
-    delta_from_out_kernel<D><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(a);
+    delta_from_out_kernel<D, F16><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(a);
   } else {
-    dq_kernel<D, MASK, SCORE, true><<<(unsigned)nq, kThreads, 0, stream>>>(a);
+    dq_kernel<D, MASK, SCORE, true, F16><<<(unsigned)nq, kThreads, 0, stream>>>(a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dq_kernel<D, MASK, SCORE, false><<<(unsigned)nq, kThreads, 0, stream>>>(a);
+  dq_kernel<D, MASK, SCORE, false, F16><<<(unsigned)nq, kThreads, 0, stream>>>(a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long nk = (long long)a.B * a.Hkv * a.bm.NKB * (a.bm.BS / kBlock);
-  dkdv_kernel<D, MASK, SCORE><<<(unsigned)nk, kThreads, 0, stream>>>(a);
+  dkdv_kernel<D, MASK, SCORE, F16><<<(unsigned)nk, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <int D, int MASK>
+template <int D, int MASK, bool F16>
 hipError_t dispatch_score(const BwdArgs& a, int score, hipStream_t stream) {
   switch (score) {
-    case SCORE_NONE: return launch_kernels<D, MASK, SCORE_NONE>(a, stream);
-    case SCORE_ALIBI: return launch_kernels<D, MASK, SCORE_ALIBI>(a, stream);
-    case SCORE_SOFTCAP: return launch_kernels<D, MASK, SCORE_SOFTCAP>(a, stream);
-    default: return launch_kernels<D, MASK, SCORE_SOFTCAP_ALIBI>(a, stream);
+    case SCORE_NONE: return launch_kernels<D, MASK, SCORE_NONE, F16>(a, stream);
+    case SCORE_ALIBI: return launch_kernels<D, MASK, SCORE_ALIBI, F16>(a, stream);
+    case SCORE_SOFTCAP: return launch_kernels<D, MASK, SCORE_SOFTCAP, F16>(a, stream);
+    default: return launch_kernels<D, MASK, SCORE_SOFTCAP_ALIBI, F16>(a, stream);
   }
 }
 
-template <int D>
+template <int D, bool F16>
 hipError_t dispatch_mask(const BwdArgs& a, int mask, int score, hipStream_t stream) {
   switch (mask) {
-    case MASK_NOOP: return dispatch_score<D, MASK_NOOP>(a, score, stream);
-    case MASK_CAUSAL: return dispatch_score<D, MASK_CAUSAL>(a, score, stream);
-    case MASK_SLIDING_SINK: return dispatch_score<D, MASK_SLIDING_SINK>(a, score, stream);
-    case MASK_PREFIX_LM: return dispatch_score<D, MASK_PREFIX_LM>(a, score, stream);
-    case MASK_COMPOSITE: return dispatch_score<D, MASK_COMPOSITE>(a, score, stream);
-    default: return dispatch_score<D, MASK_DOCUMENT>(a, score, stream);
+    case MASK_NOOP: return dispatch_score<D, MASK_NOOP, F16>(a, score, stream);
+    case MASK_CAUSAL: return dispatch_score<D, MASK_CAUSAL, F16>(a, score, stream);
+    case MASK_SLIDING_SINK: return dispatch_score<D, MASK_SLIDING_SINK, F16>(a, score, stream);
+    case MASK_PREFIX_LM: return dispatch_score<D, MASK_PREFIX_LM, F16>(a, score, stream);
+    case MASK_COMPOSITE: return dispatch_score<D, MASK_COMPOSITE, F16>(a, score, stream);
+    default: return dispatch_score<D, MASK_DOCUMENT, F16>(a, score, stream);
   }
 }
 
-}  // namespace
-
-hipError_t launch_bwd_bf16(const BwdLaunch& L, hipStream_t stream) {
+template <bool F16>
+hipError_t launch_elem(const BwdLaunch& L, hipStream_t stream) {
   BwdArgs a;
   a.q = static_cast<const u16*>(L.q);
   a.k = static_cast<const u16*>(L.k);
@@ -646,8 +679,20 @@ hipError_t launch_bwd_bf16(const BwdLaunch& L, hipStream_t stream) {
   a.q_idx = L.q_idx;
   a.fq_num = L.full_q_num;
   a.fq_idx = L.full_q_idx;
-  if (L.D == 64) return dispatch_mask<64>(a, L.mask_kind, L.score_kind, stream);
-  return dispatch_mask<128>(a, L.mask_kind, L.score_kind, stream);
+  if (L.D == 64) return dispatch_mask<64, F16>(a, L.mask_kind, L.score_kind, stream);
+  return dispatch_mask<128, F16>(a, L.mask_kind, L.score_kind, stream);
 }
+
+}  // namespace
+
+#if FA_BWD_F16
+hipError_t launch_bwd_f16(const BwdLaunch& L, hipStream_t stream) {
+  return launch_elem<true>(L, stream);
+}
+#else
+hipError_t launch_bwd_bf16(const BwdLaunch& L, hipStream_t stream) {
+  return launch_elem<false>(L, stream);
+}
+#endif
 
 }  // namespace fa

@@ -102,6 +102,8 @@ struct BwdLaunch {
   const int* full_q_idx;
 };
 
+// the 16-bit backward, one object per element type: bf16 or fp16 inputs
 hipError_t launch_bwd_bf16(const BwdLaunch& L, hipStream_t stream);
+hipError_t launch_bwd_f16(const BwdLaunch& L, hipStream_t stream);
 
 }  // namespace fa

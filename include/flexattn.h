@@ -450,9 +450,13 @@ flexattn_status flexattn_block_mask_from_kv_blocks(flexattn_block_mask* bm, int3
  *         overwritten with Delta_i = sum_j P_ij dP_ij, which equals dO_i . O_i
  *         but is formed from fp32 P and dP, so the forward's output is not an
  *         input.
- * All tensors are BF16 with D in {64, 128} (UNSUPPORTED otherwise); strides
- * and alignment as for flexattn_fwd. Rows with no allowed key (LSE = -inf)
- * get dq = 0. Asynchronous on `stream`; no host synchronisation.
+ * All seven tensors share one dtype, BF16 or F16 (q of another dtype is
+ * UNSUPPORTED, a tensor differing from q INVALID_ARG); D in {64, 128}
+ * (UNSUPPORTED otherwise). The products run on the matching MFMA with fp32
+ * accumulation; P and dS are rounded to the input type for the second
+ * products and the gradients are stored in it. Strides and alignment as for
+ * flexattn_fwd. Rows with no allowed key (LSE = -inf) get dq = 0.
+ * Asynchronous on `stream`; no host synchronisation.
  */
 flexattn_status flexattn_bwd(const flexattn_tensor* q, const flexattn_tensor* k,
                              const flexattn_tensor* v, const float* lse,

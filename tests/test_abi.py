@@ -216,7 +216,13 @@ def test_bwd_rejects_bad_arguments(L):
     # fp32 tensors are not supported by the backward
     f32 = [tens(dtype=0) for _ in range(7)]
     assert _bwd(L, f32, bm) == lib._UNSUPPORTED
-    assert b"BF16" in L.flexattn_last_error()
+    assert b"16-bit" in L.flexattn_last_error()
+    # fp16 is accepted, but every tensor must share q's dtype
+    mixed = [tens(dtype=2)] + good[1:]
+    assert _bwd(L, mixed, bm) == lib._INVALID
+    assert b"dtype differs" in L.flexattn_last_error()
+    assert _bwd(L, [tens(dtype=2) for _ in range(7)], bm, ws=0) == lib._INVALID
+    assert b"workspace" in L.flexattn_last_error()
     # head dim, NULL workspace, NULL tensor, mismatched shapes
     assert _bwd(L, [tens(D=96) for _ in range(7)], bm) == lib._UNSUPPORTED
     assert _bwd(L, good, bm, ws=0) == lib._INVALID

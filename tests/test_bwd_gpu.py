@@ -50,9 +50,9 @@ def lib():
     return m
 
 
-def tiny(D, mask, score, B=2, Hq=4, Hkv=2, Q_LEN=300, KV_LEN=300, seed=0, **kw):
+def tiny(D, mask, score, B=2, Hq=4, Hkv=2, Q_LEN=300, KV_LEN=300, seed=0, dtype="bf16", **kw):
     return W.Workload(f"bwd_{D}_{mask}_{score}", B=B, Hq=Hq, Hkv=Hkv, Q_LEN=Q_LEN,
-                      KV_LEN=KV_LEN, D=D, dtype="bf16", seed=seed, mask=mask,
+                      KV_LEN=KV_LEN, D=D, dtype=dtype, seed=seed, mask=mask,
                       window=kw.get("window", 100), sinks=kw.get("sinks", 3),
                       doc_seed=kw.get("doc_seed", 77),
                       doc_len_range=kw.get("doc_len_range", (20, 150)), score=score,
@@ -66,14 +66,15 @@ def mask_of(lib, w, inp, B_mask=1, H_mask=1, separate_full_blocks=True):
 
 
 def run_bwd(lib, w, inp, d_out, bm):
-    q = G.to_device(inp.q, "bf16")
-    k = G.to_device(inp.k, "bf16")
-    v = G.to_device(inp.v, "bf16")
-    g = G.to_device(d_out, "bf16")
+    q = G.to_device(inp.q, w.dtype)
+    k = G.to_device(inp.k, w.dtype)
+    v = G.to_device(inp.v, w.dtype)
+    g = G.to_device(d_out, w.dtype)
     out, lse = lib.flex_attention(q, k, v, bm, score=w.score, softcap=w.softcap, scale=w.scale)
     dq, dk, dv = lib.flex_attention_backward(q, k, v, lse, g, bm, score=w.score,
                                              softcap=w.softcap, scale=w.scale)
     torch.cuda.synchronize()
+    assert dq.dtype == dk.dtype == dv.dtype == q.dtype
     return [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
 
 
@@ -413,3 +414,96 @@ def test_training_pair_dense_causal_sampled(lib):
         ref = oracle_bwd(w, inp, d_out, batches=[b], heads=[h], rows=rows)[0]
         assert (~np.isnan(ref).any(axis=-1)).sum() == len(rows)
         check(got, ref, "dq")
+
+
+# ------------------------------------------------------------- fp16 inputs
+# The same kernels with fp16 elements: P and dS are rounded to fp16 (2^-11
+# relative) instead of bf16 (2^-8) and the gradients are stored in fp16, so
+# the bf16-derived bound above holds with room to spare.
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", ["noop", "causal", "sliding_sink", "document_causal",
+                                  "prefix_lm"])
+@pytest.mark.parametrize("score", ["none", "softcap_alibi"])
+def test_bwd_f16_grid(lib, D, mask, score):
+    """fp16 q, k, v and dO: every head dim x mask kind, with and without
+    score mods, GQA, ragged tail tiles; gradients come back in fp16."""
+    w = tiny(D, mask, score, dtype="f16", value_scale=2.0 if "softcap" in score else 1.0)
+    full_check(lib, w)
+
+
+@pytest.mark.parametrize("q_len,kv_len", [(1, 200), (257, 129), (513, 200)])
+def test_bwd_f16_ragged_lengths(lib, q_len, kv_len):
+    """fp16 with lengths off the tile grid and Q_LEN != KV_LEN."""
+    w = tiny(128, "causal", "alibi", B=1, Hq=4, Hkv=1, Q_LEN=q_len, KV_LEN=kv_len, dtype="f16")
+    full_check(lib, w)
+
+
+def test_bwd_f16_matches_bf16_structure(lib):
+    """The fp16 and bf16 backward of inputs exact in both types (small
+    integers over 8) agree to the rounding of their stored gradients."""
+    w = tiny(128, "sliding_sink", "alibi", B=1, Hq=4, Hkv=2, Q_LEN=384, KV_LEN=384)
+    inp = W.generate(w)
+    rng = np.random.default_rng(5)
+    q, k, v, g = (rng.integers(-8, 9, size=x.shape).astype(np.float32) / 8
+                  for x in (inp.q, inp.k, inp.v, inp.q))
+    bm = mask_of(lib, w, inp)
+    res = {}
+    for dt in ("bf16", "f16"):
+        tq, tk, tv, tg = (G.to_device(x, dt) for x in (q, k, v, g))
+        out, lse = lib.flex_attention(tq, tk, tv, bm, score="alibi", scale=w.scale)
+        grads = lib.flex_attention_backward(tq, tk, tv, lse, tg, bm, score="alibi",
+                                            scale=w.scale)
+        torch.cuda.synchronize()
+        res[dt] = [t.float().cpu().numpy().astype(np.float64) for t in grads]
+    ref = oracle.attention_backward(q, k, v, g, *oracle.for_workload(w, inp),
+                                    oracle.score_grad_for("alibi", 0.0), w.scale)
+    for n, a, b, r in zip(("dq", "dk", "dv"), res["bf16"], res["f16"], ref):
+        # fp16 keeps 3 more mantissa bits at every rounding: its error is the smaller
+        ea, eb = np.abs(a - r).max(), np.abs(b - r).max()
+        assert eb <= ea, (n, ea, eb)
+        check(b, r, n)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask,score", [("causal", "softcap_alibi"), ("document_causal", "none")])
+def test_training_pair_f16(lib, D, mask, score):
+    """The fp16 training pair: flex_attention_train's fp32 O rounds to its
+    fp16 O, and the backward that takes Delta from it meets the bound."""
+    w = tiny(D, mask, score, dtype="f16", value_scale=2.0 if "softcap" in score else 1.0)
+    inp = W.generate(w)
+    d_out = W.generate_upstream(w)
+    bm = mask_of(lib, w, inp)
+    q, k, v = (G.to_device(x, "f16") for x in (inp.q, inp.k, inp.v))
+    g = G.to_device(d_out, "f16")
+    o1, l1 = lib.flex_attention(q, k, v, bm, score=w.score, softcap=w.softcap, scale=w.scale)
+    o2, l2, o32 = lib.flex_attention_train(q, k, v, bm, score=w.score, softcap=w.softcap,
+                                           scale=w.scale)
+    dq, dk, dv = lib.flex_attention_backward(q, k, v, l2, g, bm, score=w.score,
+                                             softcap=w.softcap, scale=w.scale, out_f32=o32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o32.to(torch.float16), o2)
+    ref = oracle_bwd(w, inp, d_out)
+    ex_q, ex_k = delta_rounding_terms(w, inp, d_out)
+    for t, r, n, ex in zip((dq, dk, dv), ref, ("dq", "dk", "dv"), (ex_q, ex_k, None)):
+        assert t.dtype == torch.float16
+        check(t.float().cpu().numpy().astype(np.float64), r, n, ex)
+
+
+def test_bwd_f16_dense_causal_full_size_sampled(lib):
+    """The dense causal workload's shapes (B=4, Hq=16, Hkv=4, L=4096, D=128)
+    in fp16: sampled dQ rows of two heads and dK / dV of one KV head of
+    b = 0 against the oracle."""
+    w = W.DENSE_CAUSAL_GQA.with_(dtype="f16", name="dense_causal_gqa_f16")
+    inp = W.generate(w)
+    d_out = W.generate_upstream(w)
+    bm = mask_of(lib, w, inp)
+    dq, dk, dv = run_bwd(lib, w, inp, d_out, bm)
+    rows = np.array([0, 1, 128, 2047, 4095])
+    for b, h in ((0, 0), (2, 9)):
+        ref_dq, _, _ = oracle_bwd(w, inp, d_out, batches=[b], heads=[h], rows=rows)
+        check(dq[b, h, rows], ref_dq[b, h, rows], f"dq[{b},{h}]")
+    _, ref_dk, ref_dv = oracle_bwd(w, inp, d_out, batches=[0], heads=[8, 9, 10, 11])
+    check(dk[0, 2], ref_dk[0, 2], "dk[0,2]")
+    check(dv[0, 2], ref_dv[0, 2], "dv[0,2]")

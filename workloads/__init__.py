@@ -182,10 +182,15 @@ def generate(w: Workload) -> Inputs:
 def generate_upstream(w: Workload) -> np.ndarray:
     """Upstream gradient dO for the backward: standard normal, shaped like
     the output [B, Hq, Q_LEN, D], from its own stream (seed + 7919) so the
-    forward's inputs do not change; rounded to bf16 for bf16 workloads."""
+    forward's inputs do not change; rounded to the workload's 16-bit type
+    (bf16 or IEEE half) as its inputs are."""
     rng = np.random.default_rng(w.seed + 7919)
     g = rng.standard_normal((w.B, w.Hq, w.Q_LEN, w.D), dtype=np.float32)
-    return round_to_bf16(g) if w.dtype == "bf16" else g
+    if w.dtype == "bf16":
+        return round_to_bf16(g)
+    if w.dtype == "f16":
+        return g.astype(np.float16).astype(np.float32)
+    return g
 
 
 def paged_cache(k: np.ndarray, v: np.ndarray, page_size: int, seed: int, spare_pages: int = 3,

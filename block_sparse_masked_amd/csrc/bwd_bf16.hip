@@ -53,6 +53,7 @@ namespace {
 
 typedef unsigned short u16;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -355,18 +356,58 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (b, KV head, KV tile); wave w owns key rows
-// 32w .. 32w+31. For every query head of the group and every query tile of
-// the backward lists, per 32-query block: S = Q.K^T and dP = dO.V^T (query
-// rows on the register axis, key on the lane axis), then dV^T += dO^T . P^T
-// and dK^T += Q^T . dS^T with dO and Q read transposed from LDS.
+// dK, dV: one workgroup of eight waves per (b, KV head, 128-key tile); wave w
+// owns keys 16w .. 16w+15 and uses v_mfma_f32_16x16x32 products, so a wave
+// holds half the accumulators of a 32-key wave and two waves share each SIMD
+// (one runs its matrix products while the other computes P and dS). For
+// every query head of the group and every query tile of the backward lists,
+// per 32-query block: S = Q.K^T and dP = dO.V^T as two 16-query tiles each
+// (query on the register axis, key on the lane axis), then dV^T += dO^T . P
+// and dK^T += Q^T . dS over the block's 32 queries, with dO and Q read
+// transposed from LDS.
+// 16x16x32 layout: operand slot t of lane l holds k = 8*(l/16) + t of
+// row / column l%16; result register r of lane l holds row 4*(l/16) + r,
+// column l%16. In the P and dS operands slot t stands for query
+// 16*(t/4) + 4*(l/16) + t%4 of the block (the two S tiles' registers in
+// order), and the transposed reads take the dO and Q rows in that order.
 // ---------------------------------------------------------------------------
+constexpr int kKvWaves = 8;
+
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16(typename BElem<F16>::V8 a, typename BElem<F16>::V8 b,
+                                        f32x4 c) {
+  if constexpr (F16) return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed 16x16x32 operand of a row-major LDS block [row][LDR]: lane row
+// d = 16*dt + lane%16, slot t <-> block row r0 + 16*(t/4) + 4*(lane/16) + t%4.
+// In each 16-lane group lane j supplies the 8-byte piece (row j/4, columns
+// 4*(j%4) .. +3) of a 4-row x 16-column block and receives column j.
+template <int LDR, bool F16>
+__device__ __forceinline__ typename BElem<F16>::V8 tr_frag16(const u16* blk, int lane, int r0,
+                                                            int dt) {
+  const int g4 = lane >> 4, j = lane & 15;
+  const int row = r0 + 4 * g4 + (j >> 2);
+  const int col = 16 * dt + 4 * (j & 3);
+  typename BElem<F16>::V4 part[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(blk + (row + 16 * ht) * LDR + col));
+    __builtin_memcpy(&part[ht], &raw, 8);
+  }
+  return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 template <int D, int MASK, int SCORE, bool F16>
-__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kKvWaves, 1) void dkdv_kernel(BwdArgs a) {
   using E = BElem<F16>;
   using T = typename E::T;
+  constexpr int THREADS = 64 * kKvWaves;
   constexpr int LDR = D + kPad;
-  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int KS = D / 32;  // k-steps of the S and dP products
+  constexpr int DT = D / 16;  // 16-row d tiles of dK^T and dV^T
   __shared__ __attribute__((aligned(16))) u16 sQ[kBlock * LDR];
   __shared__ __attribute__((aligned(16))) u16 sG[kBlock * LDR];  // dO
   __shared__ __attribute__((aligned(16))) float slse[kBlock];
@@ -386,8 +427,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   if (kb * kBlock >= a.KV_LEN) return;  // a 128-key piece past KV_LEN
   const int hk = bh % a.Hkv, b = bh / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int kv = kb * kBlock + wave * 32 + l32;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int kv = kb * kBlock + wave * 16 + c16;
   const bool kvalid = kv < a.KV_LEN;
   const int kvc = kvalid ? kv : a.KV_LEN - 1;
 
@@ -397,19 +438,19 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     const u16* vrow = a.v + b * a.sv[0] + hk * a.sv[1] + (long long)kvc * a.sv[2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = ld_frag<F16>(krow + 16 * ks + 8 * hh);
-      vf[ks] = ld_frag<F16>(vrow + 16 * ks + 8 * hh);
+      kf[ks] = ld_frag<F16>(krow + 32 * ks + 8 * g4);
+      vf[ks] = ld_frag<F16>(vrow + 32 * ks + 8 * g4);
     }
   }
   const int* doc_row =
       (mask_uses_doc(MASK) && a.mp.doc) ? a.mp.doc + b * a.mp.doc_bstride : nullptr;
   const int dkv_id = doc_row ? doc_row[kvc] : 0;
 
-  f32x16 acck[DB], accv[DB];
+  f32x4 acck[DT], accv[DT];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) {
-    acck[i] = f32x16{};
-    accv[i] = f32x16{};
+  for (int i = 0; i < DT; ++i) {
+    acck[i] = f32x4{};
+    accv[i] = f32x4{};
   }
 
   // The walk: for each query head of the group, its full then partial query
@@ -449,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   // The next tile's Q / dO rows (and LSE, Delta, document ids) are loaded
   // into registers while the current tile computes, then written to LDS.
   constexpr int CH = D / 8;                    // 16-byte chunks per row
-  constexpr int PER = kBlock * CH / kThreads;  // chunks per thread
+  constexpr int PER = kBlock * CH / THREADS;  // chunks per thread
   uint4 pq[PER], pg[PER];
   float pl = 0.0f, pd = 0.0f;
   int pdoc = 0;
@@ -460,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     const u16* gbase = a.dout + b * a.sdo[0] + h * a.sdo[1];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * kThreads;
+      const int c = tid + i * THREADS;
       const int rr = min(q0 + c / CH, a.Q_LEN - 1);
       pq[i] = *reinterpret_cast<const uint4*>(qbase + (long long)rr * a.sq[2] + (c % CH) * 8);
       pg[i] = *reinterpret_cast<const uint4*>(gbase + (long long)rr * a.sdo[2] + (c % CH) * 8);
@@ -476,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   auto commit = [&](int q0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * kThreads;
+      const int c = tid + i * THREADS;
       const int r = c / CH;
       const bool in = q0 + r < a.Q_LEN;
       uint4 wq = pq[i], wg = pg[i];
@@ -497,44 +538,44 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll 1
     for (int qs = 0; qs < kBlock / 32; ++qs) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-      const u16* qrow = sQ + (32 * qs + l32) * LDR + 8 * hh;
-      const u16* grow = sG + (32 * qs + l32) * LDR + 8 * hh;
+      f32x4 s[2], dp[2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = E::mfma(ld_frag<F16>(qrow + 16 * ks), kf[ks], s);
-        dp = E::mfma(ld_frag<F16>(grow + 16 * ks), vf[ks], dp);
+      for (int hq = 0; hq < 2; ++hq) {
+        s[hq] = f32x4{};
+        dp[hq] = f32x4{};
+        const u16* qrow = sQ + (32 * qs + 16 * hq + c16) * LDR + 8 * g4;
+        const u16* grow = sG + (32 * qs + 16 * hq + c16) * LDR + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s[hq] = mfma16<F16>(ld_frag<F16>(qrow + 32 * ks), kf[ks], s[hq]);
+          dp[hq] = mfma16<F16>(ld_frag<F16>(grow + 32 * ks), vf[ks], dp[hq]);
+        }
       }
-      typename E::V8 pf[2], dsf[2];
+      typename E::V8 pf, dsf;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int ql0 = 32 * qs + 8 * g4 + 4 * hh;
+      for (int hq = 0; hq < 2; ++hq) {
+        const int ql0 = 32 * qs + 16 * hq + 4 * g4;
         const float4 l4 = *reinterpret_cast<const float4*>(slse + ql0);
         const float4 d4 = *reinterpret_cast<const float4*>(sdel + ql0);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * g4 + j;
-          const int ql = ql0 + j;
+        for (int r = 0; r < 4; ++r) {
           float x, dm;
-          logit_and_slope<MASK, SCORE, MASKED>(s[r], q0 + ql, kv,
-                                               mask_uses_doc(MASK) ? sdoc[ql] : 0, dkv_id,
+          logit_and_slope<MASK, SCORE, MASKED>(s[hq][r], q0 + ql0 + r, kv,
+                                               mask_uses_doc(MASK) ? sdoc[ql0 + r] : 0, dkv_id,
                                                slope2, a, x, dm);
-          const float p = fast_exp2(x - lv[j]);
-          pf[r >> 3][r & 7] = (T)p;
-          dsf[r >> 3][r & 7] = (T)(p * (dp[r] - dl[j]) * dm);
+          const float p = fast_exp2(x - lv[r]);
+          pf[4 * hq + r] = (T)p;
+          dsf[4 * hq + r] = (T)(p * (dp[hq][r] - dl[r]) * dm);
         }
       }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          accv[db] = E::mfma(tr_frag<LDR, F16>(sG, lane, 2 * qs + k2, db), pf[k2], accv[db]);
-          acck[db] = E::mfma(tr_frag<LDR, F16>(sQ, lane, 2 * qs + k2, db), dsf[k2], acck[db]);
-        }
+      for (int dt = 0; dt < DT; ++dt) {
+        accv[dt] = mfma16<F16>(tr_frag16<LDR, F16>(sG, lane, 32 * qs, dt), pf, accv[dt]);
+        acck[dt] = mfma16<F16>(tr_frag16<LDR, F16>(sQ, lane, 32 * qs, dt), dsf, acck[dt]);
+      }
     }
   };
-
 
   Pos cur = first_from(0);
   if (cur.gi < a.G) fetch(cur);
@@ -555,21 +596,20 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   }
 
   if (kvalid) {
+    // result register r of lane l: d = 16*dt + 4*(l/16) + r of key l%16
     u16* ok = a.dk + b * a.sdk[0] + hk * a.sdk[1] + (long long)kv * a.sdk[2];
     u16* ov = a.dv + b * a.sdv[0] + hk * a.sdv[1] + (long long)kv * a.sdv[2];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int dt = 0; dt < DT; ++dt) {
+      typename E::V4 pk, pv;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        typename E::V4 pk, pv;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pk[j] = (T)(acck[db][4 * gq + j] * a.scale);
-          pv[j] = (T)accv[db][4 * gq + j];
-        }
-        *reinterpret_cast<typename E::V4*>(ok + 32 * db + 8 * gq + 4 * hh) = pk;
-        *reinterpret_cast<typename E::V4*>(ov + 32 * db + 8 * gq + 4 * hh) = pv;
+      for (int r = 0; r < 4; ++r) {
+        pk[r] = (T)(acck[dt][r] * a.scale);
+        pv[r] = (T)accv[dt][r];
       }
+      *reinterpret_cast<typename E::V4*>(ok + 16 * dt + 4 * g4) = pk;
+      *reinterpret_cast<typename E::V4*>(ov + 16 * dt + 4 * g4) = pv;
+    }
   }
 }
 
@@ -614,7 +654,7 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long nk = (long long)a.B * a.Hkv * a.bm.NKB * (a.bm.BS / kBlock);
-  dkdv_kernel<D, MASK, SCORE, F16><<<(unsigned)nk, kThreads, 0, stream>>>(a);
+  dkdv_kernel<D, MASK, SCORE, F16><<<(unsigned)nk, 64 * kKvWaves, 0, stream>>>(a);
   return hipGetLastError();
 }
 

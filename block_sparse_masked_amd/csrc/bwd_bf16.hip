@@ -38,6 +38,7 @@
 // Tiles are staged in LDS as row-major blocks with 8 elements of padding per row
 // (272-byte rows at D = 128), which spreads both the 16-byte row reads and
 // the transposed 8-byte reads over the banks without a swizzle.
+#include <atomic>
 #include <cmath>
 
 #include "common.hpp"
@@ -59,6 +60,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // The 16-bit element (bf16 for F16 = false, else fp16): both take the same
 // fragment layouts and a 32x32x16 MFMA with fp32 accumulation; P and dS are
@@ -218,6 +220,30 @@ __device__ __forceinline__ void logit_and_slope(float s, int q, int kv, int dq, 
 // lse in base 2; +inf for rows with no allowed key (P = 0 there)
 __device__ __forceinline__ float lse_base2(float lse) {
   return lse == -INFINITY ? INFINITY : lse * kLog2e;
+}
+
+// Direct global->LDS loads for the dK/dV walk's query tiles. A buffer
+// resource covers [base, base + bytes); loads past it read as zero. Each
+// wave-wide buffer_load_dwordx4 ... lds writes 1 KiB of LDS: lane l's 16
+// bytes land at M0 + 16 l. M0 is an operand bound to M0; the asm keeps the
+// CDNA wait states itself (one after a scalar write of M0, five after a
+// vector instruction wrote a scalar operand of a vector memory instruction),
+// since the compiler's hazard recognizer does not look inside inline asm.
+__device__ __forceinline__ unsigned lds_u32(const void* p) {
+  return (unsigned)(unsigned long long)(__attribute__((address_space(3))) const void*)p;
+}
+__device__ __forceinline__ i32x4 buf_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, unsigned lds, int voff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               : : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds)));
 }
 
 // ---------------------------------------------------------------------------
@@ -404,12 +430,16 @@ template <int D, int MASK, int SCORE, bool F16>
 __global__ __launch_bounds__(64 * kKvWaves, 1) void dkdv_kernel(BwdArgs a) {
   using E = BElem<F16>;
   using T = typename E::T;
-  constexpr int THREADS = 64 * kKvWaves;
   constexpr int LDR = D + kPad;
   constexpr int KS = D / 32;  // k-steps of the S and dP products
   constexpr int DT = D / 16;  // 16-row d tiles of dK^T and dV^T
-  __shared__ __attribute__((aligned(16))) u16 sQ[kBlock * LDR];
-  __shared__ __attribute__((aligned(16))) u16 sG[kBlock * LDR];  // dO
+  // The query tiles (Q and dO) are double-buffered in dynamic LDS and
+  // filled by direct global->LDS loads while the previous tile computes, so
+  // no registers are held for them.
+  static_assert(D <= 128, "two query-tile buffers fit the CU's LDS up to D = 128");
+  extern __shared__ __attribute__((aligned(16))) u16 dyn_lds[];  // [buf][Q | dO][kBlock][LDR]
+  const u16* sQ = dyn_lds;
+  const u16* sG = dyn_lds + kBlock * LDR;
   __shared__ __attribute__((aligned(16))) float slse[kBlock];
   __shared__ __attribute__((aligned(16))) float sdel[kBlock];
   __shared__ int sdoc[kBlock];
@@ -487,25 +517,14 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void dkdv_kernel(BwdArgs a) {
     return min(max(qb, 0), NQB - 1) * a.bm.QBS + (p.t - c * mq) * kBlock;
   };
 
-  // The next tile's Q / dO rows (and LSE, Delta, document ids) are loaded
-  // into registers while the current tile computes, then written to LDS.
-  constexpr int CH = D / 8;                    // 16-byte chunks per row
-  constexpr int PER = kBlock * CH / THREADS;  // chunks per thread
-  uint4 pq[PER], pg[PER];
+  // The next tile's LSE, Delta and document ids are loaded into registers
+  // while the current tile computes, then written to LDS (its Q and dO rows
+  // go straight to LDS, see dma_tile).
   float pl = 0.0f, pd = 0.0f;
   int pdoc = 0;
   auto fetch = [&](const Pos& p) __attribute__((always_inline)) {
     const int h = hk * a.G + p.gi;
     const int q0 = tile_q0(p);
-    const u16* qbase = a.q + b * a.sq[0] + h * a.sq[1];
-    const u16* gbase = a.dout + b * a.sdo[0] + h * a.sdo[1];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * THREADS;
-      const int rr = min(q0 + c / CH, a.Q_LEN - 1);
-      pq[i] = *reinterpret_cast<const uint4*>(qbase + (long long)rr * a.sq[2] + (c % CH) * 8);
-      pg[i] = *reinterpret_cast<const uint4*>(gbase + (long long)rr * a.sdo[2] + (c % CH) * 8);
-    }
     if (tid < kBlock) {
       const long long lrow = ((long long)b * a.Hq + h) * a.Q_LEN + min(q0 + tid, a.Q_LEN - 1);
       pl = a.lse[lrow];
@@ -515,17 +534,6 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void dkdv_kernel(BwdArgs a) {
     }
   };
   auto commit = [&](int q0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * THREADS;
-      const int r = c / CH;
-      const bool in = q0 + r < a.Q_LEN;
-      uint4 wq = pq[i], wg = pg[i];
-      wq.x = in ? wq.x : 0u; wq.y = in ? wq.y : 0u; wq.z = in ? wq.z : 0u; wq.w = in ? wq.w : 0u;
-      wg.x = in ? wg.x : 0u; wg.y = in ? wg.y : 0u; wg.z = in ? wg.z : 0u; wg.w = in ? wg.w : 0u;
-      *reinterpret_cast<uint4*>(sQ + r * LDR + (c % CH) * 8) = wq;
-      *reinterpret_cast<uint4*>(sG + r * LDR + (c % CH) * 8) = wg;
-    }
     if (tid < kBlock) {
       const bool in = q0 + tid < a.Q_LEN;
       slse[tid] = in ? lse_base2(pl) : INFINITY;
@@ -534,65 +542,157 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void dkdv_kernel(BwdArgs a) {
     }
   };
 
+  // Per 32-query block the products run in batches of four: first the S and
+  // dP products of each 16-query tile, two k-steps a batch, then the dV and
+  // dK products, two d tiles a batch. The operand fragments of each batch
+  // are read from LDS two batches ahead of its products (scheduling
+  // barriers keep that order), so the products do not wait on an LDS round
+  // trip one by one. The accumulation order is that of the plain loops.
   auto tile = [&](int q0, float slope2, auto masked_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    using V8 = typename E::V8;
+    constexpr int NSB = KS;          // S / dP batches: 2 tiles x KS / 2 k-step pairs
+    constexpr int NBT = NSB + DT / 2;  // all batches
+    static_assert(KS % 2 == 0 && DT % 2 == 0, "pairs of k-steps and d tiles");
 #pragma unroll 1
     for (int qs = 0; qs < kBlock / 32; ++qs) {
       f32x4 s[2], dp[2];
-#pragma unroll
-      for (int hq = 0; hq < 2; ++hq) {
-        s[hq] = f32x4{};
-        dp[hq] = f32x4{};
-        const u16* qrow = sQ + (32 * qs + 16 * hq + c16) * LDR + 8 * g4;
-        const u16* grow = sG + (32 * qs + 16 * hq + c16) * LDR + 8 * g4;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s[hq] = mfma16<F16>(ld_frag<F16>(qrow + 32 * ks), kf[ks], s[hq]);
-          dp[hq] = mfma16<F16>(ld_frag<F16>(grow + 32 * ks), vf[ks], dp[hq]);
+      V8 pf, dsf;
+      V8 fb[3][4];
+      auto load_b = [&](int k, V8 (&f)[4]) __attribute__((always_inline)) {
+        if (k < NSB) {
+          const int hq = k / (KS / 2), ks0 = 2 * (k % (KS / 2));
+          const u16* qrow = sQ + (32 * qs + 16 * hq + c16) * LDR + 8 * g4 + 32 * ks0;
+          const u16* grow = sG + (32 * qs + 16 * hq + c16) * LDR + 8 * g4 + 32 * ks0;
+          f[0] = ld_frag<F16>(qrow);
+          f[1] = ld_frag<F16>(grow);
+          f[2] = ld_frag<F16>(qrow + 32);
+          f[3] = ld_frag<F16>(grow + 32);
+        } else {
+          const int j0 = 2 * (k - NSB);
+          f[0] = tr_frag16<LDR, F16>(sG, lane, 32 * qs, j0);
+          f[1] = tr_frag16<LDR, F16>(sQ, lane, 32 * qs, j0);
+          f[2] = tr_frag16<LDR, F16>(sG, lane, 32 * qs, j0 + 1);
+          f[3] = tr_frag16<LDR, F16>(sQ, lane, 32 * qs, j0 + 1);
         }
-      }
-      typename E::V8 pf, dsf;
-#pragma unroll
-      for (int hq = 0; hq < 2; ++hq) {
-        const int ql0 = 32 * qs + 16 * hq + 4 * g4;
-        const float4 l4 = *reinterpret_cast<const float4*>(slse + ql0);
-        const float4 d4 = *reinterpret_cast<const float4*>(sdel + ql0);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x, dm;
-          logit_and_slope<MASK, SCORE, MASKED>(s[hq][r], q0 + ql0 + r, kv,
-                                               mask_uses_doc(MASK) ? sdoc[ql0 + r] : 0, dkv_id,
-                                               slope2, a, x, dm);
-          const float p = fast_exp2(x - lv[r]);
-          pf[4 * hq + r] = (T)p;
-          dsf[4 * hq + r] = (T)(p * (dp[hq][r] - dl[r]) * dm);
+      };
+      auto mfma_b = [&](int k, V8 (&f)[4]) __attribute__((always_inline)) {
+        if (k < NSB) {
+          const int hq = k / (KS / 2), ks0 = 2 * (k % (KS / 2));
+          if (ks0 == 0) {
+            s[hq] = f32x4{};
+            dp[hq] = f32x4{};
+          }
+          s[hq] = mfma16<F16>(f[0], kf[ks0], s[hq]);
+          dp[hq] = mfma16<F16>(f[1], vf[ks0], dp[hq]);
+          s[hq] = mfma16<F16>(f[2], kf[ks0 + 1], s[hq]);
+          dp[hq] = mfma16<F16>(f[3], vf[ks0 + 1], dp[hq]);
+        } else {
+          const int j0 = 2 * (k - NSB);
+          accv[j0] = mfma16<F16>(f[0], pf, accv[j0]);
+          acck[j0] = mfma16<F16>(f[1], dsf, acck[j0]);
+          accv[j0 + 1] = mfma16<F16>(f[2], pf, accv[j0 + 1]);
+          acck[j0 + 1] = mfma16<F16>(f[3], dsf, acck[j0 + 1]);
         }
-      }
+      };
+      load_b(0, fb[0]);
+      load_b(1, fb[1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        accv[dt] = mfma16<F16>(tr_frag16<LDR, F16>(sG, lane, 32 * qs, dt), pf, accv[dt]);
-        acck[dt] = mfma16<F16>(tr_frag16<LDR, F16>(sQ, lane, 32 * qs, dt), dsf, acck[dt]);
+      for (int k = 0; k < NBT; ++k) {
+        if (k == NSB) {
+          // P and dS of the block (the S / dP products are done)
+#pragma unroll
+          for (int hq = 0; hq < 2; ++hq) {
+            const int ql0 = 32 * qs + 16 * hq + 4 * g4;
+            const float4 l4 = *reinterpret_cast<const float4*>(slse + ql0);
+            const float4 d4 = *reinterpret_cast<const float4*>(sdel + ql0);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float x, dm;
+              logit_and_slope<MASK, SCORE, MASKED>(s[hq][r], q0 + ql0 + r, kv,
+                                                   mask_uses_doc(MASK) ? sdoc[ql0 + r] : 0,
+                                                   dkv_id, slope2, a, x, dm);
+              const float p = fast_exp2(x - lv[r]);
+              pf[4 * hq + r] = (T)p;
+              dsf[4 * hq + r] = (T)(p * (dp[hq][r] - dl[r]) * dm);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_b(k, fb[k % 3]);
+        if (k + 2 < NBT) load_b(k + 2, fb[(k + 2) % 3]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // Direct loads of one query tile's Q and dO rows into LDS buffer `buf`
+  // (D <= 128). The padded block is SPR 16-byte slots per row (D / 8 of data
+  // and one of padding); wave-wide load I fills slots [64 I, 64 I + 64), lane
+  // l slot 64 I + l, from that slot's row and chunk (a padding slot repeats
+  // the row's last chunk). Rows at or past Q_LEN are outside the resource
+  // and read as zero.
+  constexpr int SPR = 2 * LDR / 16;
+  constexpr int NINS = kBlock * SPR / 64;
+  static_assert(kBlock * SPR % 64 == 0, "whole wave-wide loads");
+  constexpr int IPW = (NINS + kKvWaves - 1) / kKvWaves;
+  auto dma_tile = [&](const Pos& p, int buf) __attribute__((always_inline)) {
+    {  // (scope of the tile's resources)
+      const int h = hk * a.G + p.gi;
+      const int q0 = tile_q0(p);
+      const int rows = max(min(a.Q_LEN - q0, kBlock), 0);
+      const long long rq = 2 * a.sq[2], rg = 2 * a.sdo[2];  // row bytes
+      const i32x4 rsq = buf_rsrc(a.q + b * a.sq[0] + h * a.sq[1] + (long long)q0 * a.sq[2],
+                                 (unsigned)(rows * rq));
+      const i32x4 rsg = buf_rsrc(a.dout + b * a.sdo[0] + h * a.sdo[1] + (long long)q0 * a.sdo[2],
+                                 (unsigned)(rows * rg));
+      const unsigned lq = lds_u32(dyn_lds + buf * 2 * kBlock * LDR);
+      const unsigned lg = lq + 2 * kBlock * LDR;
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int I = wave + kKvWaves * i;
+        if (I < NINS) {
+          const int slot = 64 * I + lane;
+          const int row = slot / SPR, ch = min(slot % SPR, SPR - 2);
+          lds_dma16(rsq, lq + 1024 * I, row * (int)rq + 16 * ch);
+          lds_dma16(rsg, lg + 1024 * I, row * (int)rg + 16 * ch);
+        }
       }
     }
   };
 
   Pos cur = first_from(0);
-  if (cur.gi < a.G) fetch(cur);
+  if (cur.gi < a.G) {
+    fetch(cur);
+    dma_tile(cur, 0);
+  }
+  int buf = 0;
   while (cur.gi < a.G) {
     const int q0 = tile_q0(cur);
     const bool full = cur.t / mq < cur.nfull;
     float slope2 = 0.0f;
     if constexpr (SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI)
       slope2 = alibi_slope(a.slopes, hk * a.G + cur.gi, a.Hq) * kLog2e;
-    __syncthreads();  // the previous tile's reads are done
-    commit(q0);
+    // this tile's loads (LDS and registers) have landed; after the barrier
+    // every wave has them and is done with the previous tile, whose buffer
+    // the next tile's loads then fill
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+    sQ = dyn_lds + buf * 2 * kBlock * LDR;
+    sG = sQ + kBlock * LDR;
+    commit(q0);
     const Pos nxt = next_pos(cur);
-    if (nxt.gi < a.G) fetch(nxt);
+    if (nxt.gi < a.G) {
+      fetch(nxt);
+      dma_tile(nxt, buf ^ 1);
+    }
+    __syncthreads();  // the tile's LSE, Delta and document ids
     if (full && q0 + kBlock <= a.Q_LEN) tile(q0, slope2, std::false_type{});
     else tile(q0, slope2, std::true_type{});
     cur = nxt;
+    buf ^= 1;
   }
 
   if (kvalid) {
@@ -654,7 +754,24 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long nk = (long long)a.B * a.Hkv * a.bm.NKB * (a.bm.BS / kBlock);
-  dkdv_kernel<D, MASK, SCORE, F16><<<(unsigned)nk, 64 * kKvWaves, 0, stream>>>(a);
+  // two query-tile buffers (Q and dO) in dynamic LDS, above the 64 KiB a
+  // launch gets by default; the kernel's limit is raised once per
+  // device to that fixed size (concurrent first calls set the same value)
+  constexpr int kDynLds = 2 * 2 * kBlock * (D + kPad) * 2;
+  const void* fn = reinterpret_cast<const void*>(&dkdv_kernel<D, MASK, SCORE, F16>);
+  {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<bool> raised[kMaxDevices] = {};
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= kMaxDevices || !raised[dev].load(std::memory_order_acquire)) {
+      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);
+      if (e != hipSuccess) return e;
+      if (dev < kMaxDevices) raised[dev].store(true, std::memory_order_release);
+    }
+  }
+  dkdv_kernel<D, MASK, SCORE, F16><<<(unsigned)nk, 64 * kKvWaves, kDynLds, stream>>>(a);
   return hipGetLastError();
 }
 

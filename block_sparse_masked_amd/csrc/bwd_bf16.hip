@@ -406,15 +406,27 @@ __device__ __forceinline__ f32x4 mfma16(typename BElem<F16>::V8 a, typename BEle
   else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Query order of the dK/dV walk inside a 16-query tile: tile row i (the S
+// product's A-operand row, and result row 4*(lane/16) + r) is query
+// pi16(i) of the tile: rows 0..7 the even queries, rows 8..15 the odd ones.
+// The padded LDS rows are 272 bytes (D = 128; 144 at D = 64) apart, so the
+// 16 rows of a row read still fall in distinct banks, and each pair of
+// 16-lane groups of a transposed read (eight rows, 32 bytes each) takes
+// eight queries of one parity, whose 32-byte pieces then fill the 256 bytes
+// of LDS banks once instead of overlapping pairwise as consecutive rows do.
+__device__ __forceinline__ constexpr int pi16(int i) { return ((i & 7) << 1) | (i >> 3); }
+__device__ __forceinline__ constexpr int pi16_inv(int r) { return (r >> 1) | ((r & 1) << 3); }
+
 // Transposed 16x16x32 operand of a row-major LDS block [row][LDR]: lane row
-// d = 16*dt + lane%16, slot t <-> block row r0 + 16*(t/4) + 4*(lane/16) + t%4.
+// d = 16*dt + lane%16, slot t <-> block row r0 + 16*(t/4) + pi16(4*(lane/16) + t%4),
+// the query order of the P and dS operands.
 // In each 16-lane group lane j supplies the 8-byte piece (row j/4, columns
 // 4*(j%4) .. +3) of a 4-row x 16-column block and receives column j.
 template <int LDR, bool F16>
 __device__ __forceinline__ typename BElem<F16>::V8 tr_frag16(const u16* blk, int lane, int r0,
                                                             int dt) {
   const int g4 = lane >> 4, j = lane & 15;
-  const int row = r0 + 4 * g4 + (j >> 2);
+  const int row = r0 + pi16(4 * g4 + (j >> 2));
   const int col = 16 * dt + 4 * (j & 3);
   typename BElem<F16>::V4 part[2];
 #pragma unroll
@@ -535,35 +547,41 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void dkdv_kernel(BwdArgs a) {
   };
   auto commit = [&](int q0) __attribute__((always_inline)) {
     if (tid < kBlock) {
+      // query tid of the tile at its tile-row position (see pi16)
       const bool in = q0 + tid < a.Q_LEN;
-      slse[tid] = in ? lse_base2(pl) : INFINITY;
-      sdel[tid] = in ? pd : 0.0f;
-      if constexpr (mask_uses_doc(MASK)) sdoc[tid] = in ? pdoc : -2;
+      const int at = (tid & ~15) | pi16_inv(tid & 15);
+      slse[at] = in ? lse_base2(pl) : INFINITY;
+      sdel[at] = in ? pd : 0.0f;
+      if constexpr (mask_uses_doc(MASK)) sdoc[at] = in ? pdoc : -2;
     }
   };
 
   // Per 32-query block the products run in batches of four: first the S and
   // dP products of each 16-query tile, two k-steps a batch, then the dV and
   // dK products, two d tiles a batch. The operand fragments of each batch
-  // are read from LDS two batches ahead of its products (scheduling
+  // are read from LDS one or two batches ahead of its products (scheduling
   // barriers keep that order), so the products do not wait on an LDS round
-  // trip one by one. The accumulation order is that of the plain loops.
+  // trip one by one.
   auto tile = [&](int q0, float slope2, auto masked_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     using V8 = typename E::V8;
+    const int qlane = q0 + 8 * (g4 & 1) + (g4 >> 1);
     constexpr int NSB = KS;          // S / dP batches: 2 tiles x KS / 2 k-step pairs
     constexpr int NBT = NSB + DT / 2;  // all batches
+    // batches read ahead: two, or one for the score-mod kinds, whose P and
+    // dS arithmetic needs the registers
+    constexpr int AHEAD = SCORE == SCORE_NONE ? 2 : 1;
     static_assert(KS % 2 == 0 && DT % 2 == 0, "pairs of k-steps and d tiles");
 #pragma unroll 1
     for (int qs = 0; qs < kBlock / 32; ++qs) {
       f32x4 s[2], dp[2];
       V8 pf, dsf;
-      V8 fb[3][4];
+      V8 fb[AHEAD + 1][4];
       auto load_b = [&](int k, V8 (&f)[4]) __attribute__((always_inline)) {
         if (k < NSB) {
           const int hq = k / (KS / 2), ks0 = 2 * (k % (KS / 2));
-          const u16* qrow = sQ + (32 * qs + 16 * hq + c16) * LDR + 8 * g4 + 32 * ks0;
-          const u16* grow = sG + (32 * qs + 16 * hq + c16) * LDR + 8 * g4 + 32 * ks0;
+          const u16* qrow = sQ + (32 * qs + 16 * hq + pi16(c16)) * LDR + 8 * g4 + 32 * ks0;
+          const u16* grow = sG + (32 * qs + 16 * hq + pi16(c16)) * LDR + 8 * g4 + 32 * ks0;
           f[0] = ld_frag<F16>(qrow);
           f[1] = ld_frag<F16>(grow);
           f[2] = ld_frag<F16>(qrow + 32);
@@ -595,8 +613,8 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void dkdv_kernel(BwdArgs a) {
           acck[j0 + 1] = mfma16<F16>(f[3], dsf, acck[j0 + 1]);
         }
       };
-      load_b(0, fb[0]);
-      load_b(1, fb[1]);
+#pragma unroll
+      for (int k = 0; k < AHEAD; ++k) load_b(k, fb[k]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < NBT; ++k) {
@@ -611,7 +629,8 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               float x, dm;
-              logit_and_slope<MASK, SCORE, MASKED>(s[hq][r], q0 + ql0 + r, kv,
+              // query pi16(4 g4 + r) = 8 (g4 & 1) + (g4 >> 1) + 2 r of the tile
+              logit_and_slope<MASK, SCORE, MASKED>(s[hq][r], qlane + 32 * qs + 16 * hq + 2 * r, kv,
                                                    mask_uses_doc(MASK) ? sdoc[ql0 + r] : 0,
                                                    dkv_id, slope2, a, x, dm);
               const float p = fast_exp2(x - lv[r]);
@@ -621,8 +640,8 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void dkdv_kernel(BwdArgs a) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        mfma_b(k, fb[k % 3]);
-        if (k + 2 < NBT) load_b(k + 2, fb[(k + 2) % 3]);
+        mfma_b(k, fb[k % (AHEAD + 1)]);
+        if (k + AHEAD < NBT) load_b(k + AHEAD, fb[(k + AHEAD) % (AHEAD + 1)]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -743,10 +743,11 @@ static flexattn_status bwd_impl(const flexattn_tensor* q, const flexattn_tensor*
   }
   if (score_kind == FLEXATTN_SCORE_ALIBI || score_kind == FLEXATTN_SCORE_SOFTCAP_ALIBI)
     slopes = params ? params->alibi_slopes : nullptr;
-  // the dK/dV kernel addresses a tile of up to 128 query rows of q and d_out
-  // with 32-bit offsets
-  if (q->stride[2] > fa::kMaxBf16RowStride || d_out->stride[2] > fa::kMaxBf16RowStride)
-    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: q/d_out row stride above %lld elements", who,
+  // the backward kernels address a tile of up to 128 rows of q, k, v and
+  // d_out with 32-bit offsets
+  if (q->stride[2] > fa::kMaxBf16RowStride || d_out->stride[2] > fa::kMaxBf16RowStride ||
+      k->stride[2] > fa::kMaxBf16RowStride || v->stride[2] > fa::kMaxBf16RowStride)
+    return fail(FLEXATTN_ERR_UNSUPPORTED, "%s: q/k/v/d_out row stride above %lld elements", who,
                 (long long)fa::kMaxBf16RowStride);
 
   fa::BwdLaunch L;

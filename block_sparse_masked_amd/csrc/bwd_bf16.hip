@@ -85,6 +85,11 @@ struct BElem<true> {
 };
 
 constexpr int kThreads = 256;  // four waves
+// keys per dQ step (one LDS buffer): 64 at D = 128, a whole 128-key tile at
+// D = 64, whose steps would otherwise be barrier-bound; two step buffers of
+// K and V then take 68 or 72 KiB, so two workgroups share a CU
+template <int D>
+constexpr int dq_step_keys() { return D == 64 ? 128 : 64; }
 constexpr int kPad = 8;        // elements of padding per LDS row
 
 struct BwdArgs {
@@ -245,6 +250,42 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, unsigned lds, int voff) {
   asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                : : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds)));
 }
+__device__ __forceinline__ void lds_dma4(i32x4 rsrc, unsigned lds, int voff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               : : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds)));
+}
+
+// Key order of the dQ walk inside a 32-key block: block row m = 16 a + 8 b +
+// 4 c + i (a, b, c in {0, 1}, i < 4) is key sigma32(m) = 16 a + 4 i + 2 b + c.
+// The S^T product's A operand takes key sigma32(lane % 32) in row lane % 32,
+// so result register r of lane l (row 8 (r / 4) + 4 (l / 32) + r % 4) is key
+// 16 (r / 8) + 4 (r % 4) + 2 ((r / 4) % 2) + l / 32, and the transposed K
+// reads take the keys in that order. Each 32-lane half of a transposed read
+// then touches four keys whose 272-byte (D = 128) rows are 4 rows apart: their
+// 64-byte pieces fall in disjoint LDS banks, where consecutive rows overlap.
+// The 16 keys of a row read stay distinct modulo 16, as before.
+__device__ __forceinline__ constexpr int sigma32(int m) {
+  return (m & 16) | ((m & 3) << 2) | (((m >> 3) & 1) << 1) | ((m >> 2) & 1);
+}
+
+// dQ operand K^T (32x32x16, read transposed from the key-major LDS block):
+// lane row d = 32 db + lane % 32, slot t <-> block row sigma32(16 (ks % 2) + 8 (t / 4)
+// + 4 (lane / 32) + t % 4) of the 32-key block ks / 2.
+template <int LDR, bool F16>
+__device__ __forceinline__ typename BElem<F16>::V8 tr_frag_keys(const u16* blk, int lane, int ks,
+                                                               int db) {
+  const int hh = lane >> 5, vg = (lane >> 4) & 1, vi = lane & 15;
+  const int row = 16 * ks + 4 * (vi >> 2) + hh;  // + 2 ht
+  const int col = 32 * db + 16 * vg + 4 * (vi & 3);
+  typename BElem<F16>::V4 part[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(blk + (row + 2 * ht) * LDR + col));
+    __builtin_memcpy(&part[ht], &raw, 8);
+  }
+  return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (b, h, query tile); wave w owns query rows
@@ -259,9 +300,13 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   using T = typename E::T;
   constexpr int LDR = D + kPad;
   constexpr int KS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) u16 sK[kBlock * LDR];
-  __shared__ __attribute__((aligned(16))) u16 sV[kBlock * LDR];
-  __shared__ int sdoc[kBlock];
+  // K and V in steps of 64 (D = 128) or 128 keys, double-buffered in dynamic LDS
+  // ([buf][K | V][64][LDR]) and filled by direct global->LDS loads while the
+  // previous step computes; the steps' document ids likewise ([buf][64]).
+  constexpr int kStepKeys = dq_step_keys<D>();
+  constexpr int SPT = kBlock / kStepKeys;  // steps per tile
+  extern __shared__ __attribute__((aligned(16))) u16 dq_lds[];
+  __shared__ __attribute__((aligned(16))) int sdoc[2][kStepKeys];
 
   // BLOCK_SIZE = mk * 128: mk 128-row items per tile row, mk 128-key tiles
   // per listed tile
@@ -308,13 +353,19 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   const u16* kbase = a.k + b * a.sk[0] + hk * a.sk[1];
   const u16* vbase = a.v + b * a.sv[0] + hk * a.sv[1];
 
-  auto tile = [&](int kv0, auto masked_tag) __attribute__((always_inline)) {
+  // one step from buffer `buf` (keys kv0 ..): S^T, dP^T, dS^T, then
+  // dQ^T += K^T . dS^T, per 32-key block
+  auto step = [&](int kv0, int buf, auto masked_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-#pragma unroll 1
-    for (int blk = 0; blk < kBlock / 32; ++blk) {
+    const u16* sK = dq_lds + buf * 2 * kStepKeys * LDR;
+    const u16* sV = sK + kStepKeys * LDR;
+    // (two 32-key blocks unrolled at D = 128; the four of a D = 64 step in a
+    // loop, which keeps the D = 64 kernels at their old register use)
+#pragma unroll(kStepKeys == 64 ? 2 : 1)
+    for (int blk = 0; blk < kStepKeys / 32; ++blk) {
       f32x16 s = f32x16{}, dp = f32x16{};
-      const u16* krow = sK + (32 * blk + l32) * LDR + 8 * hh;
-      const u16* vrow = sV + (32 * blk + l32) * LDR + 8 * hh;
+      const u16* krow = sK + (32 * blk + sigma32(l32)) * LDR + 8 * hh;
+      const u16* vrow = sV + (32 * blk + sigma32(l32)) * LDR + 8 * hh;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = E::mfma(ld_frag<F16>(krow + 16 * ks), qf[ks], s);
@@ -323,10 +374,11 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
       typename E::V8 dsf[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kl = 32 * blk + 8 * (r >> 2) + 4 * hh + (r & 3);
+        // key sigma32(8 (r / 4) + 4 hh + r % 4) of the block
+        const int kl = 32 * blk + 16 * (r >> 3) + 4 * (r & 3) + 2 * ((r >> 2) & 1) + hh;
         float x, dm;
         logit_and_slope<MASK, SCORE, MASKED>(s[r], q, kv0 + kl, dq_id,
-                                             mask_uses_doc(MASK) ? sdoc[kl] : 0, slope2, a,
+                                             mask_uses_doc(MASK) ? sdoc[buf][kl] : 0, slope2, a,
                                              x, dm);
         const float p = fast_exp2(x - lse2);
         if constexpr (DELTA) psum = fmaf(p, dp[r], psum);
@@ -337,28 +389,83 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            acc[db] = E::mfma(tr_frag<LDR, F16>(sK, lane, 2 * blk + k2, db), dsf[k2], acc[db]);
+            acc[db] = E::mfma(tr_frag_keys<LDR, F16>(sK, lane, 2 * blk + k2, db), dsf[k2],
+                              acc[db]);
       }
     }
   };
 
-  for (int t = 0; t < (nfull + npart) * mk; ++t) {
-    const int c = t / mk;  // listed tile; its 128-key piece t % mk
+  // Loads of a step's keys [kv0, kv0 + kStepKeys) into buffer `buf`: the padded block is
+  // SPR 16-byte slots per row (D / 8 of data and one of padding); wave-wide
+  // load I fills slots [64 I, 64 I + 64), lane l slot 64 I + l from that
+  // slot's row and chunk (a padding slot repeats the row's last chunk). Keys
+  // at or past KV_LEN are outside the resources and read as zero.
+  constexpr int SPR = 2 * LDR / 16;
+  constexpr int NINS = kStepKeys * SPR / 64;
+  static_assert(kStepKeys * SPR % 64 == 0, "whole wave-wide loads");
+  constexpr int IPW = (NINS + kThreads / 64 - 1) / (kThreads / 64);
+  auto dma_step = [&](int kv0, int buf) __attribute__((always_inline)) {
+    const int rows = max(min(a.KV_LEN - kv0, kStepKeys), 0);
+    const long long rk = 2 * a.sk[2], rv = 2 * a.sv[2];  // row bytes
+    const i32x4 rsk = buf_rsrc(kbase + (long long)kv0 * a.sk[2], (unsigned)(rows * rk));
+    const i32x4 rsv = buf_rsrc(vbase + (long long)kv0 * a.sv[2], (unsigned)(rows * rv));
+    const unsigned lk = lds_u32(dq_lds + buf * 2 * kStepKeys * LDR);
+    const unsigned lv = lk + 2 * kStepKeys * LDR;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int I = wave + (kThreads / 64) * i;
+      if (I < NINS) {
+        const int slot = 64 * I + lane;
+        const int row = slot / SPR, ch = min(slot % SPR, SPR - 2);
+        lds_dma16(rsk, lk + 1024 * I, row * (int)rk + 16 * ch);
+        lds_dma16(rsv, lv + 1024 * I, row * (int)rv + 16 * ch);
+      }
+    }
+    if constexpr (mask_uses_doc(MASK)) {
+      if (doc_row && wave == 0) {
+        const i32x4 rsd = buf_rsrc(doc_row + kv0, 4u * (unsigned)rows);
+#pragma unroll
+        for (int c = 0; c < kStepKeys / 64; ++c)
+          lds_dma4(rsd, lds_u32(&sdoc[buf][64 * c]), 4 * lane + 256 * c);
+      }
+    }
+  };
+
+  // Tile t of the walk: 128-key piece t % mk of listed tile t / mk.
+  const int ntile = (nfull + npart) * mk;
+  auto tile_kv0 = [&](int t) __attribute__((always_inline)) {
+    const int c = t / mk;
     const bool full = c < nfull;
     const int kb = min(max(full ? a.bm.full_idx[lrow + c] : a.bm.kv_idx[lrow + c - nfull], 0),
                        NKB - 1);
-    const int kv0 = kb * a.bm.BS + (t - c * mk) * kBlock;
-    __syncthreads();  // the previous tile's reads are done
-    stage_rows<D, 2>(sK, kbase, a.sk[2], kv0, a.KV_LEN, tid);
-    stage_rows<D, 2>(sV, vbase, a.sv[2], kv0, a.KV_LEN, tid);
-    if constexpr (mask_uses_doc(MASK)) {
-      if (doc_row)
-        for (int i = tid; i < kBlock; i += kThreads)
-          sdoc[i] = (kv0 + i < a.KV_LEN) ? doc_row[kv0 + i] : -1;
-    }
+    return kb * a.bm.BS + (t - c * mk) * kBlock;
+  };
+  if (ntile > 0) {
+    int kv0 = tile_kv0(0);
+    dma_step(kv0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (full && kv0 + kBlock <= a.KV_LEN) tile(kv0, std::false_type{});
-    else tile(kv0, std::true_type{});
+    // Step g reads buffer g % 2 (with two steps per tile every tile starts on
+    // buffer 0); at its start it issues the next step's loads into the other
+    // buffer (read by step g - 1, which every wave finished before the last
+    // barrier).
+    int g = 0;
+    for (int t = 0; t < ntile; ++t) {
+      const bool full = t / mk < nfull && kv0 + kBlock <= a.KV_LEN;
+      const int kv_next = t + 1 < ntile ? tile_kv0(t + 1) : 0;
+#pragma unroll
+      for (int sub = 0; sub < SPT; ++sub) {
+        const int cur = SPT == 2 ? sub : (g & 1);
+        if (sub + 1 < SPT) dma_step(kv0 + kStepKeys * (sub + 1), cur ^ 1);
+        else if (t + 1 < ntile) dma_step(kv_next, cur ^ 1);
+        if (full) step(kv0 + kStepKeys * sub, cur, std::false_type{});
+        else step(kv0 + kStepKeys * sub, cur, std::true_type{});
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+        ++g;
+      }
+      kv0 = kv_next;
+    }
   }
 
   if constexpr (DELTA) {
@@ -758,39 +865,50 @@ __global__ __launch_bounds__(256) void delta_from_out_kernel(BwdArgs a) {
   if (lane == 0) a.delta[row] = acc;
 }
 
+// A kernel's dynamic-LDS limit is raised once per device to the fixed size
+// its launches use (above the 64 KiB a launch gets by default); concurrent
+// first calls set the same value.
+template <typename K>
+hipError_t raise_lds_limit(K* kernel, int bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> raised[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < kMaxDevices && raised[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  if (dev < kMaxDevices) raised[dev].store(true, std::memory_order_release);
+  return hipSuccess;
+}
+
 template <int D, int MASK, int SCORE, bool F16>
 hipError_t launch_kernels(const BwdArgs& a, hipStream_t stream) {
   const long long nq = (long long)a.B * a.Hq * a.bm.NQB * (a.bm.QBS / kBlock);
+  // dQ: two 64-key K / V step buffers; dK/dV: two query-tile buffers (Q, dO)
+  constexpr int kDqLds = 2 * 2 * dq_step_keys<D>() * (D + kPad) * 2;
+  constexpr int kKvLds = 2 * 2 * kBlock * (D + kPad) * 2;
+  hipError_t e;
   if (a.o32) {
     const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
     delta_from_out_kernel<D, F16><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(a);
   } else {
-    dq_kernel<D, MASK, SCORE, true, F16><<<(unsigned)nq, kThreads, 0, stream>>>(a);
+    e = raise_lds_limit(&dq_kernel<D, MASK, SCORE, true, F16>, kDqLds);
+    if (e != hipSuccess) return e;
+    dq_kernel<D, MASK, SCORE, true, F16><<<(unsigned)nq, kThreads, kDqLds, stream>>>(a);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dq_kernel<D, MASK, SCORE, false, F16><<<(unsigned)nq, kThreads, 0, stream>>>(a);
+  e = raise_lds_limit(&dq_kernel<D, MASK, SCORE, false, F16>, kDqLds);
+  if (e != hipSuccess) return e;
+  dq_kernel<D, MASK, SCORE, false, F16><<<(unsigned)nq, kThreads, kDqLds, stream>>>(a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long nk = (long long)a.B * a.Hkv * a.bm.NKB * (a.bm.BS / kBlock);
-  // two query-tile buffers (Q and dO) in dynamic LDS, above the 64 KiB a
-  // launch gets by default; the kernel's limit is raised once per
-  // device to that fixed size (concurrent first calls set the same value)
-  constexpr int kDynLds = 2 * 2 * kBlock * (D + kPad) * 2;
-  const void* fn = reinterpret_cast<const void*>(&dkdv_kernel<D, MASK, SCORE, F16>);
-  {
-    constexpr int kMaxDevices = 64;
-    static std::atomic<bool> raised[kMaxDevices] = {};
-    int dev = 0;
-    e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev >= kMaxDevices || !raised[dev].load(std::memory_order_acquire)) {
-      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);
-      if (e != hipSuccess) return e;
-      if (dev < kMaxDevices) raised[dev].store(true, std::memory_order_release);
-    }
-  }
-  dkdv_kernel<D, MASK, SCORE, F16><<<(unsigned)nk, 64 * kKvWaves, kDynLds, stream>>>(a);
+  e = raise_lds_limit(&dkdv_kernel<D, MASK, SCORE, F16>, kKvLds);
+  if (e != hipSuccess) return e;
+  dkdv_kernel<D, MASK, SCORE, F16><<<(unsigned)nk, 64 * kKvWaves, kKvLds, stream>>>(a);
   return hipGetLastError();
 }
 

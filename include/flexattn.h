@@ -455,7 +455,9 @@ flexattn_status flexattn_block_mask_from_kv_blocks(flexattn_block_mask* bm, int3
  * (UNSUPPORTED otherwise). The products run on the matching MFMA with fp32
  * accumulation; P and dS are rounded to the input type for the second
  * products and the gradients are stored in it. Strides and alignment as for
- * flexattn_fwd. Rows with no allowed key (LSE = -inf) get dq = 0.
+ * flexattn_fwd; a row stride (stride[2]) of q, k, v or d_out above 2^22
+ * elements is UNSUPPORTED (the kernels address a tile of up to 128 rows with
+ * 32-bit offsets). Rows with no allowed key (LSE = -inf) get dq = 0.
  * Asynchronous on `stream`; no host synchronisation.
  */
 flexattn_status flexattn_bwd(const flexattn_tensor* q, const flexattn_tensor* k,

@@ -231,6 +231,14 @@ def test_bwd_rejects_bad_arguments(L):
     bad[4] = tens(Lq=128)
     assert _bwd(L, bad, bm) == lib._INVALID
     assert b"shaped like q" in L.flexattn_last_error()
+    # row strides past 2^22 elements (32-bit tile offsets) for q, k, v, d_out
+    big = (1 << 22) + 128
+    wide = lib._Tensor(16, 1, 1, 2, 256, 128, (ctypes.c_int64 * 4)(2 * 256 * big, 256 * big, big, 1))
+    for i in (0, 1, 2, 3):
+        bad = list(good)
+        bad[i] = wide
+        assert _bwd(L, bad, bm) == lib._UNSUPPORTED, i
+        assert b"row stride" in L.flexattn_last_error()
 
 
 def test_from_kv_blocks_rejects_bad_arguments(L):

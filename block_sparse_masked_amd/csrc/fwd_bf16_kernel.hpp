@@ -44,9 +44,10 @@
 // than 8 (log2 units), which skips most rescales; any reference point gives
 // the same normalised sums in exact arithmetic. In rounded arithmetic the
 // row's largest probability can then be up to 2^8 instead of exactly 1, and
-// its rounding to the input type would go straight into O; so O is divided
-// by the fp32 sum of the rounded probabilities (the values the P.V product
-// multiplies), and LSE uses the sum of the unrounded ones.
+// its rounding to the input type would go straight into O; so for the
+// score-mod kinds O is divided by the fp32 sum of the rounded probabilities
+// (the values the P.V product multiplies), and LSE uses the sum of the
+// unrounded ones, which the plain kinds also divide O by (kRoundedSum).
 #pragma once
 
 #include <atomic>
@@ -484,6 +485,16 @@ template <int SCORE>
 constexpr bool kRelLogit =
     SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP || SCORE == SCORE_SOFTCAP_ALIBI;
 
+// O's divisor. With the lazy reference a row's largest probability can be up
+// to 2^8 and is then not exact in the input type; where it dominates the row,
+// its rounding would reach O by up to 2^-9 of |V|. The score-mod kinds (whose
+// biases and caps make such rows common) divide by the fp32 sum of the
+// rounded probabilities P.V multiplies, so the weights sum to one whatever
+// the rounding; the plain kinds divide by the fp32 sum of the probabilities
+// (the LSE's sum), which saves a quarter of an instruction per score.
+template <int SCORE>
+constexpr bool kRoundedSum = kRelLogit<SCORE>;
+
 template <int SCORE>
 __device__ __forceinline__ float rel_logit(float x, float c, float zbase, const FwdArgs& a,
                                            float slope2) {
@@ -656,8 +667,12 @@ __device__ __forceinline__ void step(f32x16 (&o)[D / 32], float& m_ref, float& l
     pf[e >> 3][e & 7] = (typename Elem<F16>::T)p;
   }
   l += rs;
+  // the rounded sum only where a score mod can make one probability
+  // dominate a row with a value the input type does not hold exactly
+  if constexpr (kRoundedSum<SCORE>) {
 #pragma unroll
-  for (int ks = 0; ks < G::PKS; ++ks) lp = Elem<F16>::sum8(pf[ks], lp);
+    for (int ks = 0; ks < G::PKS; ++ks) lp = Elem<F16>::sum8(pf[ks], lp);
+  }
 
 #pragma unroll
   for (int ks = 0; ks < G::PKS; ++ks)
@@ -820,8 +835,10 @@ __device__ __forceinline__ void step16(f32x4 (&o)[D / 16], float& m_ref, float& 
       pf[b >> 1][4 * (b & 1) + r] = (typename Elem<F16>::T)p;
     }
   l += rs;  // this lane's keys; the four lanes of a query are summed at the end
+  if constexpr (kRoundedSum<SCORE>) {
 #pragma unroll
-  for (int j = 0; j < NB / 2; ++j) lp = Elem<F16>::sum8(pf[j], lp);
+    for (int j = 0; j < NB / 2; ++j) lp = Elem<F16>::sum8(pf[j], lp);
+  }
 
 #pragma unroll
   for (int j = 0; j < NB / 2; ++j)
@@ -1143,7 +1160,8 @@ fwd_bf16_kernel(FwdArgs a) {
     // holds O^T rows 16*db + 4*g4 + r of query c16
     const float l1 = l + __shfl_xor(l, 16, 64);
     const float l_tot16 = l1 + __shfl_xor(l1, 32, 64);
-    const float lp1 = lp + __shfl_xor(lp, 16, 64);
+    const float lp0 = kRoundedSum<SCORE> ? lp : l;
+    const float lp1 = lp0 + __shfl_xor(lp0, 16, 64);
     const float lp_tot16 = lp1 + __shfl_xor(lp1, 32, 64);
     const float inv16 = lp_tot16 > 0.0f ? 1.0f / lp_tot16 : 0.0f;
     const float lse2 = l_tot16 > 0.0f ? (m_ref + fast_log2(l_tot16)) * kLn2 : -INFINITY;
@@ -1180,11 +1198,10 @@ fwd_bf16_kernel(FwdArgs a) {
 
   // epilogue: O = O_acc / l, LSE = ln(sum) + max
   // O is divided by the sum of the rounded probabilities it was accumulated
-  // from, so its weights sum to one whatever the rounding (with the lazy
-  // reference the largest probability of a row can be up to 2^8 and is not
-  // exact in the input type); LSE takes the exact fp32 sum
+  // from for the score-mod kinds (see kRoundedSum), else by the fp32 sum;
+  // LSE takes the fp32 sum
   const float l_tot = l + __shfl_xor(l, 32, 64);
-  const float lp_tot = lp + __shfl_xor(lp, 32, 64);
+  const float lp_tot = kRoundedSum<SCORE> ? lp + __shfl_xor(lp, 32, 64) : l_tot;
   const float inv = lp_tot > 0.0f ? 1.0f / lp_tot : 0.0f;
   if (a.splits > 1) {
     // this slice's normalised O and LSE (-inf for an empty slice), fp32

@@ -35,9 +35,12 @@
 // the next product, whose A operand is read transposed from LDS
 // (ds_read_b64_tr_b16) in the matching row order.
 //
-// Tiles are staged in LDS as row-major blocks with 8 elements of padding per row
-// (272-byte rows at D = 128), which spreads both the 16-byte row reads and
-// the transposed 8-byte reads over the banks without a swizzle.
+// Tiles are staged in LDS as row-major blocks with 8 elements of padding per
+// row (272-byte rows at D = 128), double-buffered and filled by direct
+// global->LDS loads while the previous block computes. The padding spreads
+// the 16-byte row reads over the banks; the transposed 8-byte reads take the
+// block's rows in an order (sigma32 for the keys of dQ, pi16 for the queries
+// of dK/dV) whose rows read together fall in disjoint banks.
 #include <atomic>
 #include <cmath>
 
@@ -227,7 +230,7 @@ __device__ __forceinline__ float lse_base2(float lse) {
   return lse == -INFINITY ? INFINITY : lse * kLog2e;
 }
 
-// Direct global->LDS loads for the dK/dV walk's query tiles. A buffer
+// Direct global->LDS loads for the backward's K/V and Q/dO tiles. A buffer
 // resource covers [base, base + bytes); loads past it read as zero. Each
 // wave-wide buffer_load_dwordx4 ... lds writes 1 KiB of LDS: lane l's 16
 // bytes land at M0 + 16 l. M0 is an operand bound to M0; the asm keeps the
@@ -300,9 +303,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   using T = typename E::T;
   constexpr int LDR = D + kPad;
   constexpr int KS = D / 16, DB = D / 32;
-  // K and V in steps of 64 (D = 128) or 128 keys, double-buffered in dynamic LDS
-  // ([buf][K | V][64][LDR]) and filled by direct global->LDS loads while the
-  // previous step computes; the steps' document ids likewise ([buf][64]).
+  // K and V in steps of 64 (D = 128) or 128 keys, double-buffered in dynamic
+  // LDS ([buf][K | V][kStepKeys][LDR]) and filled by direct global->LDS loads
+  // while the previous step computes; the steps' document ids likewise
+  // ([buf][kStepKeys]).
   constexpr int kStepKeys = dq_step_keys<D>();
   constexpr int SPT = kBlock / kStepKeys;  // steps per tile
   extern __shared__ __attribute__((aligned(16))) u16 dq_lds[];
@@ -361,7 +365,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     const u16* sV = sK + kStepKeys * LDR;
     // (two 32-key blocks unrolled at D = 128; the four of a D = 64 step in a
     // loop, which keeps the D = 64 kernels at their old register use)
-#pragma unroll(kStepKeys == 64 ? 2 : 1)
+    constexpr int kBlkUnroll = kStepKeys == 64 ? 2 : 1;
+#pragma unroll kBlkUnroll
     for (int blk = 0; blk < kStepKeys / 32; ++blk) {
       f32x16 s = f32x16{}, dp = f32x16{};
       const u16* krow = sK + (32 * blk + sigma32(l32)) * LDR + 8 * hh;

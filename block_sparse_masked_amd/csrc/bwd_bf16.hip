@@ -249,6 +249,14 @@ __device__ __forceinline__ i32x4 buf_rsrc(const void* base, unsigned bytes) {
   r[3] = 0x00020000;
   return r;
 }
+// Bytes a resource must cover for `rows` rows of `row_bytes` stride and D
+// 16-bit elements: up to the last valid row's data, so a row stride below
+// the row length (0 for rows broadcast along the sequence) still reads every
+// valid row; rows past the last read as zero when the stride is the row
+// length or more, else other valid rows (their scores are masked either way).
+__device__ __forceinline__ unsigned range_bytes(int rows, long long row_bytes, int D) {
+  return rows > 0 ? (unsigned)((rows - 1) * row_bytes + 2 * D) : 0u;
+}
 __device__ __forceinline__ void lds_dma16(i32x4 rsrc, unsigned lds, int voff) {
   asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                : : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds)));
@@ -412,8 +420,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   auto dma_step = [&](int kv0, int buf) __attribute__((always_inline)) {
     const int rows = max(min(a.KV_LEN - kv0, kStepKeys), 0);
     const long long rk = 2 * a.sk[2], rv = 2 * a.sv[2];  // row bytes
-    const i32x4 rsk = buf_rsrc(kbase + (long long)kv0 * a.sk[2], (unsigned)(rows * rk));
-    const i32x4 rsv = buf_rsrc(vbase + (long long)kv0 * a.sv[2], (unsigned)(rows * rv));
+    const i32x4 rsk = buf_rsrc(kbase + (long long)kv0 * a.sk[2], range_bytes(rows, rk, D));
+    const i32x4 rsv = buf_rsrc(vbase + (long long)kv0 * a.sv[2], range_bytes(rows, rv, D));
     const unsigned lk = lds_u32(dq_lds + buf * 2 * kStepKeys * LDR);
     const unsigned lv = lk + 2 * kStepKeys * LDR;
 #pragma unroll
@@ -776,9 +784,9 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void dkdv_kernel(BwdArgs a) {
       const int rows = max(min(a.Q_LEN - q0, kBlock), 0);
       const long long rq = 2 * a.sq[2], rg = 2 * a.sdo[2];  // row bytes
       const i32x4 rsq = buf_rsrc(a.q + b * a.sq[0] + h * a.sq[1] + (long long)q0 * a.sq[2],
-                                 (unsigned)(rows * rq));
+                                 range_bytes(rows, rq, D));
       const i32x4 rsg = buf_rsrc(a.dout + b * a.sdo[0] + h * a.sdo[1] + (long long)q0 * a.sdo[2],
-                                 (unsigned)(rows * rg));
+                                 range_bytes(rows, rg, D));
       const unsigned lq = lds_u32(dyn_lds + buf * 2 * kBlock * LDR);
       const unsigned lg = lq + 2 * kBlock * LDR;
 #pragma unroll

@@ -248,8 +248,9 @@ __device__ __forceinline__ void dma4(i32x4 rsrc, unsigned lds, int voff) {
 // contiguous KiB of LDS (lane l writes bytes [16 l, 16 l + 16)), so each lane
 // fetches the global chunk whose swizzled home is that slot; its byte offset
 // from the block's first row is fixed and computed once. Per step only the
-// resource moves; its range ends at KV_LEN, so rows past it read as zero
-// (their scores are masked: a tile crossing KV_LEN takes the masked path).
+// resource moves; its range ends with key KV_LEN - 1 (see range_bytes), and
+// the scores of rows past it are masked: a tile crossing KV_LEN takes the
+// masked path.
 template <int D, bool IS_V, int WAVES>
 struct BlockLoader {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -277,18 +278,24 @@ struct BlockLoader {
 
   // loads of keys [kv0, kv0 + NK) into buffer `buf` (its LDS is lds0 + buf * 2 * kStepBytes
   // when the two buffers of K (or V) are laid out [buf][K|V])
+  // The range ends with the last valid row's data, not at rows * row_bytes,
+  // so a row stride below the row length (0 for keys broadcast along the
+  // sequence) still reads every valid row; rows past it read as zero when
+  // the stride is the row length or more, else other valid rows (their
+  // scores are masked either way).
+  __device__ __forceinline__ unsigned range_bytes(int rows) const {
+    return rows > 0 ? (unsigned)(rows - 1) * row_bytes + 2u * D : 0u;
+  }
   __device__ __forceinline__ i32x4 plan(int kv0, int kv_len) const {
     const int rows = min(kv_len - kv0, NK);
-    return make_rsrc(base + (unsigned long long)kv0 * row_bytes,
-                     rows > 0 ? (unsigned)rows * row_bytes : 0u);
+    return make_rsrc(base + (unsigned long long)kv0 * row_bytes, range_bytes(rows));
   }
   __device__ __forceinline__ void issue_one(i32x4 rsrc, unsigned lds_buf, int i) const {
     dma16(rsrc, lds_buf + 1024 * i, voff[i]);
   }
   __device__ __forceinline__ void issue(int kv0, int kv_len, unsigned lds_buf) const {
     const int rows = min(kv_len - kv0, NK);
-    const i32x4 rsrc = make_rsrc(base + (unsigned long long)kv0 * row_bytes,
-                                 rows > 0 ? (unsigned)rows * row_bytes : 0u);
+    const i32x4 rsrc = make_rsrc(base + (unsigned long long)kv0 * row_bytes, range_bytes(rows));
 #pragma unroll
     for (int i = 0; i < KB_PER_WAVE; ++i) dma16(rsrc, lds_buf + 1024 * i, voff[i]);
   }

@@ -507,3 +507,32 @@ def test_bwd_f16_dense_causal_full_size_sampled(lib):
     _, ref_dk, ref_dv = oracle_bwd(w, inp, d_out, batches=[0], heads=[8, 9, 10, 11])
     check(dk[0, 2], ref_dk[0, 2], "dk[0,2]")
     check(dv[0, 2], ref_dv[0, 2], "dv[0,2]")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("which", ["k", "v", "q_dout"])
+def test_rows_broadcast_with_zero_stride(lib, D, which):
+    """A tensor broadcast along the sequence (row stride 0, as torch's expand
+    gives) reads its one row for every position: the forward and the backward
+    match the same call on a contiguous copy, bit for bit."""
+    w = tiny(D, "causal", "none", B=1, Hq=4, Hkv=2, Q_LEN=300, KV_LEN=300)
+    inp = W.generate(w)
+    g = W.generate_upstream(w)
+    dev = lambda x: G.to_device(x, "bf16")  # noqa: E731
+    q, k, v, gd = dev(inp.q), dev(inp.k), dev(inp.v), dev(g)
+    bcast = lambda t: t[:, :, :1].expand(-1, -1, t.shape[2], -1)  # noqa: E731
+    if which == "k":
+        k = bcast(k)
+    elif which == "v":
+        v = bcast(v)
+    else:
+        q, gd = bcast(q), bcast(gd)
+    bm = mask_of(lib, w, inp)
+    got = [lib.flex_attention(q, k, v, bm)]
+    got.append(lib.flex_attention_backward(q, k, v, got[0][1], gd, bm))
+    qc, kc, vc, gc = (t.contiguous() for t in (q, k, v, gd))
+    ref = [lib.flex_attention(qc, kc, vc, bm)]
+    ref.append(lib.flex_attention_backward(qc, kc, vc, ref[0][1], gc, bm))
+    torch.cuda.synchronize()
+    for a, b, n in zip(got[0] + got[1], ref[0] + ref[1], ("out", "lse", "dq", "dk", "dv")):
+        assert torch.equal(a, b), n

@@ -879,17 +879,18 @@ __global__ __launch_bounds__(256) void delta_from_out_kernel(BwdArgs a) {
 }
 
 // A kernel's dynamic-LDS limit is raised once per device to the fixed size
-// its launches use (above the 64 KiB a launch gets by default); concurrent
-// first calls set the same value.
-template <typename K>
-hipError_t raise_lds_limit(K* kernel, int bytes) {
+// its launches use (above the 64 KiB a launch gets by default); the flag is
+// per kernel (one instantiation each), and concurrent first calls set the
+// same value.
+template <auto Kernel>
+hipError_t raise_lds_limit(int bytes) {
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> raised[kMaxDevices] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < kMaxDevices && raised[dev].load(std::memory_order_acquire)) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
   if (dev < kMaxDevices) raised[dev].store(true, std::memory_order_release);
@@ -907,19 +908,19 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t stream) {
     const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
     delta_from_out_kernel<D, F16><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(a);
   } else {
-    e = raise_lds_limit(&dq_kernel<D, MASK, SCORE, true, F16>, kDqLds);
+    e = raise_lds_limit<&dq_kernel<D, MASK, SCORE, true, F16>>(kDqLds);
     if (e != hipSuccess) return e;
     dq_kernel<D, MASK, SCORE, true, F16><<<(unsigned)nq, kThreads, kDqLds, stream>>>(a);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = raise_lds_limit(&dq_kernel<D, MASK, SCORE, false, F16>, kDqLds);
+  e = raise_lds_limit<&dq_kernel<D, MASK, SCORE, false, F16>>(kDqLds);
   if (e != hipSuccess) return e;
   dq_kernel<D, MASK, SCORE, false, F16><<<(unsigned)nq, kThreads, kDqLds, stream>>>(a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long nk = (long long)a.B * a.Hkv * a.bm.NKB * (a.bm.BS / kBlock);
-  e = raise_lds_limit(&dkdv_kernel<D, MASK, SCORE, F16>, kKvLds);
+  e = raise_lds_limit<&dkdv_kernel<D, MASK, SCORE, F16>>(kKvLds);
   if (e != hipSuccess) return e;
   dkdv_kernel<D, MASK, SCORE, F16><<<(unsigned)nk, 64 * kKvWaves, kKvLds, stream>>>(a);
   return hipGetLastError();

@@ -825,8 +825,8 @@ flexattn_status flexattn_bwd_from_out(const flexattn_tensor* q, const flexattn_t
                                       flexattn_tensor* dq, flexattn_tensor* dk,
                                       flexattn_tensor* dv, float* workspace, void* stream) {
   static const char* who = "flexattn_bwd_from_out";
-  if (!out_f32 || reinterpret_cast<uintptr_t>(out_f32) % 4 != 0)
-    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: out_f32 is NULL or not 4-byte aligned", who);
+  if (!out_f32 || reinterpret_cast<uintptr_t>(out_f32) % 16 != 0)
+    return fail(FLEXATTN_ERR_INVALID_ARG, "%s: out_f32 is NULL or not 16-byte aligned", who);
   return bwd_impl(q, k, v, lse, out_f32, d_out, bm, score_kind, params, scale, dq, dk, dv,
                   workspace, stream, who);
 }

@@ -852,30 +852,36 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void dkdv_kernel(BwdArgs a) {
   }
 }
 
-// Delta = dO . O per query row from the forward's fp32 O (one wave per row):
-// sum_j P_ij dP_ij = dO_i . sum_j P_ij v_j = dO_i . O_i.
+// Delta = dO . O per query row from the forward's fp32 O:
+// sum_j P_ij dP_ij = dO_i . sum_j P_ij v_j = dO_i . O_i. D / 8 lanes per row,
+// each reading 8 consecutive elements (two 16-byte loads of O, one of dO),
+// then a butterfly sum over the row's lanes; a 256-thread block takes
+// 2048 / D rows.
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void delta_from_out_kernel(BwdArgs a) {
-  constexpr int PER = D / 64;
+  constexpr int LPR = D / 8;  // lanes per row
+  constexpr int RPB = 256 / LPR;
   const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const int qi = (int)(row % a.Q_LEN);
-  const long long bh = row / a.Q_LEN;
-  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
-  const u16* g = a.dout + b * a.sdo[0] + h * a.sdo[1] + (long long)qi * a.sdo[2] + lane * PER;
-  const float* o = a.o32 + row * D + lane * PER;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int j = threadIdx.x % LPR;
   float acc = 0.0f;
+  if (row < rows) {
+    const int qi = (int)(row % a.Q_LEN);
+    const long long bh = row / a.Q_LEN;
+    const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+    const uint4 gv = *reinterpret_cast<const uint4*>(a.dout + b * a.sdo[0] + h * a.sdo[1] +
+                                                     (long long)qi * a.sdo[2] + 8 * j);
+    const float4 o0 = *reinterpret_cast<const float4*>(a.o32 + row * D + 8 * j);
+    const float4 o1 = *reinterpret_cast<const float4*>(a.o32 + row * D + 8 * j + 4);
+    typename BElem<F16>::T g[8];
+    __builtin_memcpy(g, &gv, 16);
+    const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    typename BElem<F16>::T gv;
-    __builtin_memcpy(&gv, g + i, 2);
-    acc = fmaf((float)gv, o[i], acc);
+    for (int i = 0; i < 8; ++i) acc = fmaf((float)g[i], o[i], acc);
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) a.delta[row] = acc;
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && j == 0) a.delta[row] = acc;
 }
 
 // A kernel's dynamic-LDS limit is raised once per device to the fixed size
@@ -906,7 +912,9 @@ hipError_t launch_kernels(const BwdArgs& a, hipStream_t stream) {
   hipError_t e;
   if (a.o32) {
     const long long rows = (long long)a.B * a.Hq * a.Q_LEN;
-    delta_from_out_kernel<D, F16><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(a);
+    constexpr int kRowsPerBlock = 256 / (D / 8);
+    delta_from_out_kernel<D, F16>
+        <<<(unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock), 256, 0, stream>>>(a);
   } else {
     e = raise_lds_limit<&dq_kernel<D, MASK, SCORE, true, F16>>(kDqLds);
     if (e != hipSuccess) return e;

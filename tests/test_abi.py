@@ -381,6 +381,12 @@ def test_training_pair_rejects_bad_arguments(L):
                                    0.125, *(ctypes.byref(x) for x in t[4:]),
                                    ctypes.c_void_p(4096), None) == lib._INVALID
     assert b"out_f32" in L.flexattn_last_error()
+    # out_f32 must be 16-byte aligned (Delta reads it in 16-byte pieces)
+    assert L.flexattn_bwd_from_out(*(ctypes.byref(x) for x in t[:3]), ctypes.c_void_p(4096),
+                                   ctypes.c_void_p(4100), ctypes.byref(t[3]), ctypes.byref(bm), 0,
+                                   ctypes.byref(sp), 0.125, *(ctypes.byref(x) for x in t[4:]),
+                                   ctypes.c_void_p(4096), None) == lib._INVALID
+    assert b"16-byte aligned" in L.flexattn_last_error()
 
 
 def test_create_rejects_block_sizes(L):
